@@ -1,0 +1,455 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test ties one oracle stage to a closed form, an invariant, a brute-force
+search, a hand-derived example or a printed worked example, chosen so that a
+plausible slip (dropped term, wrong sign or side, transposed operand, wrong
+exponent) fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as o
+from synthetic import bf16_bits_to_f32, f32_to_bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def spd(rng, n, cond_scale=1.0):
+    A = rng.standard_normal((3 * n, n)) * np.exp(cond_scale * rng.standard_normal(n))[None, :]
+    return A.T @ A
+
+
+# ---------------------------------------------------------------------------
+# Hessian factors and sensitivity
+# ---------------------------------------------------------------------------
+def test_hessian_matches_triple_loop():
+    rng = np.random.default_rng(1)
+    A = rng.standard_normal((7, 5))
+    H = o.hessian_factor(A)
+    for i in range(5):
+        for j in range(5):
+            s = 0.0
+            for t in range(7):
+                s += A[t, i] * A[t, j]
+            assert H[i, j] == pytest.approx(s, rel=1e-14, abs=1e-14)
+
+
+def test_hessian_symmetric_psd_and_trace_is_frobenius():
+    rng = np.random.default_rng(2)
+    A = rng.standard_normal((50, 12)) * np.exp(rng.standard_normal(12))
+    H = o.hessian_factor(A)
+    assert np.array_equal(H, H.T) or np.allclose(H, H.T, rtol=0, atol=1e-12)
+    assert np.linalg.eigvalsh(H).min() > -1e-9 * np.abs(H).max()
+    assert o.trace(H) == pytest.approx(float(np.sum(A * A)), rel=1e-13)
+    assert o.stream_sq_norm(A) == pytest.approx(o.trace(H), rel=1e-13)
+
+
+def test_sampled_entries_match_full_factor():
+    rng = np.random.default_rng(3)
+    A = rng.standard_normal((40, 9))
+    H = o.hessian_factor(A)
+    i = np.array([0, 3, 8, 5])
+    j = np.array([0, 7, 2, 5])
+    np.testing.assert_allclose(o.hessian_factor_entry(A[:, i], A[:, j]), H[i, j], rtol=1e-12, atol=1e-12)
+
+
+def test_bf16_decoding_known_bit_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0000, 0x4049], dtype=np.uint16)
+    # 1.0, -2.0, 1 + 2^-7, 0, 3.140625 (0x4049 -> sign 0, exp 128, mantissa 0x49)
+    np.testing.assert_array_equal(o.bf16_bits_to_f64(bits), [1.0, -2.0, 1.0078125, 0.0, 3.140625])
+
+
+def test_bf16_generator_rounds_to_nearest_even():
+    # 1 + 2^-8 lies exactly between bf16 neighbours 1 and 1 + 2^-7: ties to even (1.0);
+    # 1 + 3*2^-8 lies between 1+2^-7 and 1+2^-6: ties to even (1 + 2^-6).
+    x = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20], dtype=np.float32)
+    y = bf16_bits_to_f32(f32_to_bf16_bits(x))
+    np.testing.assert_array_equal(y, np.array([1.0, 1 + 2 ** -6, 1 + 2 ** -7], dtype=np.float32))
+
+
+def test_sensitivity_is_product_of_stream_norms():
+    rng = np.random.default_rng(4)
+    X = rng.standard_normal((30, 6)) * 2.0
+    G = rng.standard_normal((30, 4)) * 0.5
+    tx, tg, s = o.sensitivity(o.hessian_factor(X), o.hessian_factor(G))
+    assert s == pytest.approx(float(np.sum(X * X)) * float(np.sum(G * G)), rel=1e-13)
+    assert tx == pytest.approx(float(np.sum(X * X)), rel=1e-13)
+    assert tg == pytest.approx(float(np.sum(G * G)), rel=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Hadamard and rotation
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("b", [1, 2, 4, 16, 64, 256])
+def test_sylvester_orthogonality_and_recursive_construction(b):
+    H = o.sylvester_hadamard(b)
+    np.testing.assert_array_equal(H @ H.T, b * np.eye(b))
+    np.testing.assert_array_equal(H, H.T)
+    # Sylvester's recursive construction H_2m = [[H_m, H_m], [H_m, -H_m]]
+    R = np.array([[1.0]])
+    while R.shape[0] < b:
+        R = np.block([[R, R], [R, -R]])
+    np.testing.assert_array_equal(H, R)
+
+
+def test_hadamard_block_rule():
+    assert o.hadamard_block_size(11008) == 256
+    assert o.hadamard_block_size(28672) == 4096
+    assert o.hadamard_block_size(4096) == 4096
+    assert o.hadamard_block_size(8192, 4096) == 4096
+    with pytest.raises(ValueError):
+        o.hadamard_block_size(96, 64)
+
+
+@pytest.mark.parametrize("n,b", [(64, 0), (96, 32), (48, 16)])
+def test_rotation_is_orthogonal_and_matches_dense(n, b):
+    rng = np.random.default_rng(5)
+    s = rng.choice([-1, 1], size=n)
+    P = o.rotation_matrix(s, b)
+    np.testing.assert_allclose(P @ P.T, np.eye(n), atol=1e-13)
+    M = rng.standard_normal((5, n))
+    np.testing.assert_allclose(o.rotate_rows(M, s, b), M @ P.T, atol=1e-13)
+    np.testing.assert_allclose(o.rotate_cols(M.T, s, b), P @ M.T, atol=1e-13)
+
+
+def _map_like_w(dW, d_in, d_out, s_in, s_out, had_in, had_out, mode):
+    M = dW * d_out[:, None] * d_in[None, :]
+    if mode != o.BIIP_OUT_ONLY:
+        M = o.rotate_rows(M, s_in, had_in)
+    if mode != o.BIIP_IN_ONLY:
+        M = o.rotate_cols(M, s_out, had_out)
+    return M
+
+
+@pytest.mark.parametrize("mode", [o.BIIP_FULL, o.BIIP_NO_RESCALE, o.BIIP_IN_ONLY, o.BIIP_OUT_ONLY])
+def test_biip_keeps_kfac_loss_invariant(mode):
+    rng = np.random.default_rng(6)
+    out_n, in_n = 24, 32
+    W = rng.standard_normal((out_n, in_n)) * 0.02
+    W[:, 3] *= 20
+    HX, HG = spd(rng, in_n), spd(rng, out_n)
+    s_in, s_out = rng.choice([-1, 1], in_n), rng.choice([-1, 1], out_n)
+    Wt, HXt, HGt, d_in, d_out = o.biip(W, HX, HG, s_in, s_out, 0.25, mode, 16, 8)
+    for k in range(3):
+        dW = rng.standard_normal((out_n, in_n))
+        dWt = _map_like_w(dW, d_in, d_out, s_in, s_out, 16, 8, mode)
+        assert o.proxy_loss(dWt, HXt, HGt) == pytest.approx(o.proxy_loss(dW, HX, HG), rel=1e-11)
+    # W itself is mapped the same way
+    np.testing.assert_allclose(Wt, _map_like_w(W, d_in, d_out, s_in, s_out, 16, 8, mode), atol=1e-14)
+    # traces change only through the rescale; rotation alone keeps them
+    if mode == o.BIIP_NO_RESCALE:
+        assert o.trace(HXt) == pytest.approx(o.trace(HX), rel=1e-12)
+        assert o.trace(HGt) == pytest.approx(o.trace(HG), rel=1e-12)
+
+
+def test_rescale_quarter_power_minimizes_proxy_bound():
+    """With alpha = 1/4 each side's d minimizes tr(D^-1 H D^-1) * ||W D||_F^2 over
+    positive diagonals (Cauchy-Schwarz); random perturbations only increase it."""
+    rng = np.random.default_rng(7)
+    W = rng.standard_normal((10, 12))
+    W[:, 2] *= 15
+    HX, HG = spd(rng, 12, 1.0), spd(rng, 10, 1.0)
+    d_in, d_out = o.rescale_vectors(W, HX, HG, 0.25, o.BIIP_FULL)
+
+    def f_in(d):
+        return np.sum(np.diag(HX) / d ** 2) * np.sum((W * d[None, :]) ** 2)
+
+    def f_out(d):
+        return np.sum(np.diag(HG) / d ** 2) * np.sum((W * d[:, None]) ** 2)
+
+    base_in, base_out = f_in(d_in), f_out(d_out)
+    for _ in range(50):
+        assert f_in(d_in * np.exp(0.1 * rng.standard_normal(12))) >= base_in * (1 - 1e-12)
+        assert f_out(d_out * np.exp(0.1 * rng.standard_normal(10))) >= base_out * (1 - 1e-12)
+    # alpha = 1/2 (or the reciprocal rule) is not the minimizer
+    d_half, _ = o.rescale_vectors(W, HX, HG, 0.5, o.BIIP_FULL)
+    assert f_in(d_half) > base_in
+    assert f_in(1.0 / d_in) > base_in
+
+
+def test_rescale_degenerate_entries_give_unit_factor():
+    W = np.zeros((3, 4))
+    W[:, 1:] = 1.0
+    HX = np.diag([1.0, 2.0, 0.0, 4.0])
+    HG = np.eye(3)
+    d_in, d_out = o.rescale_vectors(W, HX, HG, 0.25)
+    assert d_in[0] == 1.0 and d_in[2] == 1.0
+    assert d_in[1] == pytest.approx((2.0 / 3.0) ** 0.25)
+
+
+# ---------------------------------------------------------------------------
+# Grid, GPTQ and losses
+# ---------------------------------------------------------------------------
+def test_minmax_grid_hand_example():
+    # group values (-1, 0.5, 2) at 2 bits: xmin -1, xmax 2, s = 1, z = 1;
+    # codes rint(w/s) + z = (0, rint(0.5) + 1 = 1 [half to even], 3); dequant (-1, 0, 2)
+    g = o.AsymMinMaxGrid(2, 3)
+    blk = np.array([[-1.0, 0.5, 2.0]])
+    g.set_params(blk)
+    assert g.scale[0] == 1.0 and g.zero[0] == 1.0
+    q = g.code(g.unrounded(blk[0]))
+    np.testing.assert_array_equal(q, [0, 1, 3])
+    np.testing.assert_array_equal(g.dequant(q), [-1.0, 0.0, 2.0])
+    # all-positive group: range forced to include 0 -> xmin 0, z 0; (0.3, 0.6, 0.9) at 2 bits: s = 0.3
+    g.set_params(np.array([[0.3, 0.6, 0.9]]))
+    assert g.zero[0] == 0.0 and g.scale[0] == pytest.approx(0.3)
+    # all-zero group: s = 1, z = 0
+    g.set_params(np.zeros((1, 3)))
+    assert g.scale[0] == 1.0 and g.zero[0] == 0.0
+
+
+def _textbook_rtn(W, bits, group):
+    """Round-to-nearest on an asymmetric min-max grid per (row, group), no feedback."""
+    maxq = 2 ** bits - 1
+    Q = np.empty_like(W)
+    codes = np.empty(W.shape, dtype=np.int64)
+    for g0 in range(0, W.shape[1], group):
+        blk = W[:, g0:g0 + group]
+        lo = np.minimum(blk.min(1), 0)
+        hi = np.maximum(blk.max(1), 0)
+        step = np.where(hi > lo, (hi - lo) / maxq, 1.0)
+        zp = np.rint(-lo / step)
+        c = np.clip(np.rint(blk / step[:, None]) + zp[:, None], 0, maxq)
+        codes[:, g0:g0 + group] = c
+        Q[:, g0:g0 + group] = step[:, None] * (c - zp[:, None])
+    return codes, Q
+
+
+@pytest.mark.parametrize("bits,group", [(2, 8), (3, 16), (4, 32)])
+def test_gptq_with_diagonal_hessian_is_rtn(bits, group):
+    rng = np.random.default_rng(8)
+    W = rng.standard_normal((16, 32)) * 0.05
+    HX = np.diag(np.exp(rng.standard_normal(32)))
+    r = o.quantize_layer(W, HX, None, bits, group, 0.01)
+    codes, Q = _textbook_rtn(W, bits, group)
+    np.testing.assert_array_equal(r["gptq"].codes, codes)
+    np.testing.assert_allclose(r["gptq"].qhat, Q, atol=1e-15)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_gptq_single_column_is_rtn(bits):
+    rng = np.random.default_rng(9)
+    W = rng.standard_normal((64, 1))
+    HX = np.array([[2.5]])
+    r = o.quantize_layer(W, HX, None, bits, 1, 0.01)
+    codes, Q = _textbook_rtn(W, bits, 1)
+    np.testing.assert_array_equal(r["gptq"].codes, codes)
+
+
+@pytest.mark.parametrize("bits,group,with_hg", [(2, 8, False), (2, 8, True), (3, 16, True), (4, 32, False)])
+def test_gptq_predicted_loss_equals_direct_loss(bits, group, with_hg):
+    """W0 - Qhat = E U and U H_d U^T = I, so sum_j e_j^T H_G e_j = tr(H_G dW H_d dW^T)."""
+    rng = np.random.default_rng(10)
+    n, m = 32, 12
+    W = rng.standard_normal((m, n)) * 0.02
+    W[:, 5] *= 20
+    HX = spd(rng, n, 1.0)
+    HG = spd(rng, m) if with_hg else None
+    r = o.quantize_layer(W, HX, HG, bits, group, 0.01)
+    res, U, lam = r["gptq"], r["U"], r["lam"]
+    dW = W - res.qhat
+    np.testing.assert_allclose(dW, res.E @ U, atol=1e-12)
+    Hd = HX + lam * np.eye(n)
+    np.testing.assert_allclose(U @ Hd @ U.T, np.eye(n), atol=1e-9)
+    assert r["loss_pred"] == pytest.approx(o.proxy_loss(dW, Hd, HG), rel=1e-10)
+    # the direct loss (undamped) is the predicted loss minus lam * tr(H_G dW dW^T)
+    assert r["loss_direct"] == pytest.approx(
+        r["loss_pred"] - lam * o.proxy_loss(dW, np.eye(n), HG), rel=1e-9)
+
+
+def test_gptq_rows_are_independent():
+    rng = np.random.default_rng(11)
+    W = rng.standard_normal((20, 24))
+    HX = spd(rng, 24)
+    full = o.quantize_layer(W, HX, None, 2, 8, 0.01)
+    rows = np.array([3, 17, 0])
+    sub = o.quantize_layer(W, HX, None, 2, 8, 0.01, rows=rows)
+    np.testing.assert_array_equal(sub["gptq"].codes, full["gptq"].codes[rows])
+
+
+def test_gptq_whitened_errors_within_babai_box():
+    """Unclamped columns: |w_j - qhat_j| <= s/2, i.e. |e_j| <= s / (2 U_jj)."""
+    rng = np.random.default_rng(12)
+    W = rng.standard_normal((16, 32))
+    HX = spd(rng, 32)
+    r = o.quantize_layer(W, HX, None, 4, 32, 0.01)
+    res, U = r["gptq"], r["U"]
+    s = np.repeat(res.scales, 32, axis=1)
+    u = res.unrounded
+    unclamped = (res.codes > 0) & (res.codes < 15)
+    bound = s / (2 * np.diag(U))[None, :]
+    assert np.all(np.abs(res.E)[unclamped] <= bound[unclamped] * (1 + 1e-12))
+    assert unclamped.mean() > 0.5
+    assert np.all((res.codes >= 0) & (res.codes <= 15))
+    del u
+
+
+def test_gptq_brute_force_bounds_2x4_w2():
+    """Exhaustive search over all 4^8 W2 codes of a 2x4 weight bounds GPTQ's loss from below."""
+    rng = np.random.default_rng(13)
+    for trial in range(3):
+        W = rng.standard_normal((2, 4))
+        HX = spd(rng, 4, 0.5)
+        HG = spd(rng, 2) if trial else None
+        r = o.quantize_layer(W, HX, HG, 2, 4, 0.0)
+        res = r["gptq"]
+        # the grid of the one group per row is set from the original W at column 0
+        g = o.AsymMinMaxGrid(2, 4)
+        g.set_params(W)
+        np.testing.assert_allclose(res.scales[:, 0], g.scale)
+        best = o.brute_force_min_loss(W, HX, HG, g.scale, g.zero, 2)
+        gl = o.proxy_loss(W - res.qhat, HX, HG)
+        assert best <= gl * (1 + 1e-12)
+        assert best > 0
+
+
+def test_babai_fig1_worked_example():
+    """[WaterKron] Figure 1: GPTQ on H = L^T L is Babai rounding on the lattice L diag(alpha) Z^2."""
+    with open(os.path.join(GOLDEN, "babai_fig1.json")) as f:
+        gold = json.load(f)
+    L = np.array(gold["L"])
+    H = L.T @ L
+    np.testing.assert_array_equal(H, np.array(gold["derived_by_hand"]["H = L^T L"]))
+    U, lam, dead, _ = o.damp_and_factor(H, 0.0)
+    np.testing.assert_allclose(U, np.array(gold["derived_by_hand"]["U = chol_upper(H^-1) = L^-T"]), atol=1e-15)
+    assert -U[0, 1] / U[0, 0] == pytest.approx(gold["derived_by_hand"]["feedback coefficient -U12/U11"])
+    rng = np.random.default_rng(14)
+    for key in ("alpha_rect", "alpha_square"):
+        alpha = np.array(gold[key])
+        half = 0.5 * np.diag(L) * alpha          # half-sides of the error cell
+        w = rng.standard_normal((400, 2))        # targets L w, w ~ N(0, I_2)
+        res = o.gptq(w, U, o.FixedUniformGrid(alpha))
+        q = res.qhat
+        e = (w - q) @ L.T                        # lattice-coordinate error L (w - q)
+        np.testing.assert_allclose(res.E, e, atol=1e-12)
+        assert np.all(np.abs(e) <= half * (1 + 1e-12))
+        # Babai's cell is a fundamental region: exactly one lattice point per target lands in it
+        for t in range(0, 400, 40):
+            base = np.rint(w[t] / alpha)
+            hits = []
+            for a, b in itertools.product(range(-3, 4), repeat=2):
+                cand = (base + np.array([a, b])) * alpha
+                err = L @ (w[t] - cand)
+                if np.all(np.abs(err) < half):
+                    hits.append(cand)
+            assert len(hits) == 1
+            np.testing.assert_allclose(hits[0], q[t], atol=1e-12)
+    sides = np.diag(L) * np.array(gold["alpha_square"])
+    np.testing.assert_allclose(sides, gold["derived_by_hand"]["cell sides (L11 alpha1, L22 alpha2) at alpha_square"])
+    assert np.prod(sides) == pytest.approx(gold["derived_by_hand"]["cell area = det L * alpha1 * alpha2"])
+    assert np.prod(sides) == pytest.approx(np.linalg.det(L))
+
+
+def test_not_spd_raises():
+    with pytest.raises(o.NotSPDError):
+        o.damp_and_factor(np.array([[1.0, 2.0], [2.0, 1.0]]), 0.01)
+
+
+def test_dead_channel_rule():
+    rng = np.random.default_rng(15)
+    HX = spd(rng, 8)
+    HX[3, :] = 0
+    HX[:, 3] = 0
+    W = rng.standard_normal((4, 8))
+    r = o.quantize_layer(W, HX, None, 2, 8, 0.01)
+    assert r["dead"][3] and r["dead"].sum() == 1
+    assert np.all(r["gptq"].qhat[:, 3] == 0)
+
+
+def test_replay_accepts_only_near_ties():
+    rng = np.random.default_rng(16)
+    W = rng.standard_normal((8, 16))
+    HX = spd(rng, 16)
+    r = o.quantize_layer(W, HX, None, 2, 16, 0.01)
+    codes = r["gptq"].codes.copy()
+    same = o.quantize_layer(W, HX, None, 2, 16, 0.01, replay_codes=codes)["gptq"]
+    assert same.hard_mismatches == 0 and same.accepted_ties == 0
+    bad = codes.copy()
+    u = r["gptq"].unrounded
+    far = np.abs((u - np.floor(u)) - 0.5) > 0.1
+    rr, cc = np.argwhere(far & (codes > 0))[0]
+    bad[rr, cc] -= 1
+    out = o.quantize_layer(W, HX, None, 2, 16, 0.01, replay_codes=bad)["gptq"]
+    assert out.hard_mismatches >= 1 and (int(rr), int(cc)) in out.mismatch_positions
+
+
+# ---------------------------------------------------------------------------
+# Packing
+# ---------------------------------------------------------------------------
+def test_pack_hand_examples():
+    c = np.zeros((1, 16), dtype=np.int64)
+    c[0, :4] = [1, 2, 3, 0]
+    assert o.pack_codes(c, 2)[0, 0] == 1 + 2 * 4 + 3 * 16          # 57
+    c4 = np.zeros((1, 8), dtype=np.int64)
+    c4[0, :2] = [0xF, 0x1]
+    assert o.pack_codes(c4, 4)[0, 0] == 0x1F
+    c4[0, 7] = 0xA
+    assert o.pack_codes(c4, 4)[0, 0] == 0xA000001F
+    # W3: code 10 occupies stream bits 30..32 and straddles words 0 and 1
+    c3 = np.zeros((1, 32), dtype=np.int64)
+    c3[0, 10] = 7
+    w = o.pack_codes(c3, 3)
+    assert w.shape == (1, 3)
+    assert w[0, 0] == 0xC0000000 and w[0, 1] == 1 and w[0, 2] == 0
+    c3[0, 31] = 5                                                 # bits 93..95 -> word 2 bits 29..31
+    assert o.pack_codes(c3, 3)[0, 2] == 5 << 29
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_pack_round_trip_and_size(bits):
+    rng = np.random.default_rng(17)
+    codes = rng.integers(0, 2 ** bits, size=(5, 64))
+    w = o.pack_codes(codes, bits)
+    assert w.shape == (5, 64 * bits // 32)
+    np.testing.assert_array_equal(o.unpack_codes(w, bits, 64), codes)
+    # independent unpack through numpy's bit unpacking of little-endian words
+    stream = np.unpackbits(w.astype("<u4").view(np.uint8), axis=1, bitorder="little")
+    back = (stream.reshape(5, 64, bits) * (1 << np.arange(bits))).sum(-1)
+    np.testing.assert_array_equal(back, codes)
+
+
+# ---------------------------------------------------------------------------
+# Bit allocation
+# ---------------------------------------------------------------------------
+def test_allocator_worked_examples():
+    # gains at 2 bits are s*3/64: (3, .75, .1875, .047); after 64 -> 3 bits its gain is
+    # 64*3/256 = .75, tied with 16 at 2 bits: the smallest index wins -> (4, 2, 2, 2)
+    assert o.allocate_bits([64, 16, 4, 1], [1, 1, 1, 1]) == [4, 2, 2, 2]
+    assert o.allocate_bits([100, 10, 1, 0.1], [1, 1, 1, 1]) == [4, 2, 2, 2]
+    # budget 10 of 4 unit layers, equal sensitivities: ties go to the lowest indices
+    assert o.allocate_bits([1, 1, 1, 1], [1, 1, 1, 1]) == [3, 3, 2, 2]
+
+
+def test_allocator_greedy_is_optimal_for_equal_sizes():
+    """For equal sizes the objective sum_l s_l 4^-b_l is separable convex with unit
+    costs, so the greedy result attains the brute-force optimum under the budget."""
+    rng = np.random.default_rng(18)
+    for trial in range(20):
+        L = int(rng.integers(2, 7))
+        s = np.exp(3 * rng.standard_normal(L))
+        bits = o.allocate_bits(s, [7] * L)
+        budget = (7 * L * 5) // 2
+        assert sum(b * 7 for b in bits) <= budget
+        best = min(sum(si * 4.0 ** -bi for si, bi in zip(s, bb))
+                   for bb in itertools.product((2, 3, 4), repeat=L) if 7 * sum(bb) <= budget)
+        got = sum(si * 4.0 ** -bi for si, bi in zip(s, bits))
+        assert got == pytest.approx(best, rel=1e-12)
+
+
+def test_allocator_budget_and_monotonicity():
+    rng = np.random.default_rng(19)
+    numel = [4096 * 4096] * 4 + [11008 * 4096] * 3
+    for trial in range(10):
+        s = np.exp(2 * rng.standard_normal(7))
+        bits = o.allocate_bits(s, numel)
+        assert all(b in (2, 3, 4) for b in bits)
+        assert sum(b * n for b, n in zip(bits, numel)) <= (sum(numel) * 5) // 2
+        for a in range(4):
+            for b in range(4):
+                if s[a] > s[b]:
+                    assert bits[a] >= bits[b]
