@@ -1,0 +1,222 @@
+/*
+ * kq.h -- C ABI of the KronQ per-layer quantization engine for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * What the engine computes, per linear layer (W is out x in, rows = output
+ * channels; X is tokens x in calibration activations, G is tokens x out output
+ * gradients):
+ *   1. the Kronecker Hessian factors H_X = X^T X and H_G = G^T G
+ *      (KronQ README, opening section: H ~ H_X (x) H_G; WaterKron and FlipFlop
+ *      Hessian, Table 1, row "Marginal");
+ *   2. the sensitivity tr(H_G) tr(H_X) that drives inter-layer bit allocation
+ *      (KronQ README, opening section; KronQ arXiv abstract, point 2);
+ *   3. bidirectional incoherence processing (BiIP): rescale plus randomized
+ *      Hadamard rotation on the input and the output side (KronQ README,
+ *      opening section and flags table; KronQ arXiv abstract, point 1);
+ *   4. GPTQ error-feedback quantization through a damped Cholesky factor of
+ *      H_X^-1, to packed 2/3/4-bit codes, minimizing tr(H_G dW H_X dW^T)
+ *      (KronQ README, opening section and "Mapping paper results to flags");
+ *   5. the per-sublayer bit allocation to an average bit budget.
+ *
+ * Conventions for every entry point:
+ *   - Matrix arguments are row-major with the stated leading dimension (in
+ *     elements).  Pointers are device pointers (memory from hipMalloc or a
+ *     PyTorch CUDA/HIP tensor) unless the argument says "host".
+ *   - The caller owns every buffer.  Entry points never keep a pointer after
+ *     they return and never free caller memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is enqueued on it and the call returns without waiting, except where an
+ *     entry point says it synchronizes.
+ *   - All argument checks run on the host before anything is enqueued.  A
+ *     non-OK status means nothing was enqueued, except KQ_EHIP (a launch or
+ *     runtime call failed) and KQ_ENOTSPD (reported after the work ran).
+ *   - kq_last_error() returns a thread-local message for the last non-OK
+ *     status of the calling thread.
+ */
+#ifndef KQ_H
+#define KQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kq_status {
+  KQ_OK = 0,
+  KQ_EINVAL = 1,      /* NULL pointer, bad enum value, bits outside {2,3,4}, ... */
+  KQ_ESHAPE = 2,      /* sizes that the operation does not accept */
+  KQ_ENOTSPD = 3,     /* damped H_X has a non-positive pivot (no Cholesky factor) */
+  KQ_EWORKSPACE = 4,  /* workspace NULL or smaller than the queried size */
+  KQ_ENOTIMPL = 5,    /* option not implemented */
+  KQ_EHIP = 6         /* a HIP runtime call or kernel launch failed */
+} kq_status;
+
+/* Incoherence-processing modes (KronQ README, "Mapping paper results to flags":
+ * --incoh_mode {full, no_rescale, su_only, sv_only}; the one-sided modes are
+ * read here as input-side-only and output-side-only processing). */
+enum {
+  KQ_BIIP_FULL = 0,       /* rescale + rotate, both sides */
+  KQ_BIIP_NO_RESCALE = 1, /* rotate both sides, no rescale */
+  KQ_BIIP_IN_ONLY = 2,    /* rescale + rotate the input side only */
+  KQ_BIIP_OUT_ONLY = 3    /* rescale + rotate the output side only */
+};
+
+/* Quantizer parameters (KronQ README flags: --w_bits, --w_groupsize, --w_asym;
+ * GPTQ's lazy block size and damping).  Defaults: bits 2, group 128,
+ * block 128, damp 0.01, asym 1, act_order 0. */
+typedef struct kq_quant_params {
+  int bits;       /* 2, 3 or 4 */
+  int group;      /* columns per (row, group) scale/zero; 0 < group, in % group == 0 */
+  int block;      /* GPTQ block width: 64 or 128; block % group == 0 or group % block == 0 */
+  float damp;     /* lambda = damp * mean(diag H_X), damp >= 0 */
+  int asym;       /* must be 1 (asymmetric min-max grid) */
+  int act_order;  /* must be 0 (natural column order) */
+} kq_quant_params;
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int kq_version(void);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* kq_last_error(void);
+
+/*
+ * kq_accumulate_hessian -- one Kronecker factor, H = A^T A or H += A^T A.
+ *
+ * Follows: KronQ README, opening section (K-FAC factorization H ~ H_X (x) H_G);
+ * WaterKron and FlipFlop Hessian, Table 1, "Marginal" (input factor E[x x^T],
+ * output factor E[g g^T]).  Sums are not normalized by the token count.
+ *
+ *   A_bf16      device, bf16 bit patterns, T x n, row-major, leading dim lda >= n
+ *               (token-major: row t holds token t's n channels).  lda must be a
+ *               multiple of 8 and A 16-byte aligned.
+ *   T           tokens (>= 0; T = 0 leaves H = 0, or unchanged when accumulating)
+ *   n           channels (1 <= n); H is n x n
+ *   H           device fp32, n x n, leading dim ldh >= n.  On return H is the full
+ *               symmetric matrix (both triangles written).
+ *   accumulate  0: H = A^T A.  1: H += A^T A (H must hold a symmetric matrix).
+ * Products of bf16 values are exact in fp32; accumulation is fp32.
+ */
+kq_status kq_accumulate_hessian(const uint16_t* A_bf16, int64_t T, int64_t n, int64_t lda,
+                                float* H, int64_t ldh, int accumulate, void* stream);
+
+/*
+ * kq_sensitivity -- traces and the sensitivity s = tr(H_G) * tr(H_X).
+ *
+ * Follows: KronQ README, opening section ("inter-layer mixed precision ...
+ * guided by tr(H_G) tr(H_X) sensitivity"); KronQ arXiv abstract, point 2.
+ * Meant for the raw factors (before BiIP).
+ *
+ *   HX   device fp32, n_in x n_in (leading dim ldx); only the diagonal is read
+ *   HG   device fp32, n_out x n_out (leading dim ldg); only the diagonal is read
+ *   out3 host, 3 doubles: {tr H_X, tr H_G, tr H_G * tr H_X}; diagonals summed in fp64
+ * Synchronizes `stream` before returning.
+ */
+kq_status kq_sensitivity(const float* HX, int64_t n_in, int64_t ldx, const float* HG,
+                         int64_t n_out, int64_t ldg, double out3[3], void* stream);
+
+/*
+ * kq_biip_rotate -- bidirectional incoherence processing of one layer.
+ *
+ * Follows: KronQ README, opening section ("incoherence rotation + rescaling on
+ * both the input and output sides") and flags table (--incoh_kernel had,
+ * --alpha 0.25); KronQ arXiv abstract, point 1.
+ * With D_in = diag(d_in), D_out = diag(d_out) and P = blockdiag(Had_b) diag(S) / sqrt(b)
+ * (Sylvester Hadamard of order b in natural order, S the +-1 signs):
+ *   d_in[i]  = (H_X[i,i] / sum_r W[r,i]^2) ^ alpha      (1 if either is 0)
+ *   d_out[k] = (H_G[k,k] / sum_i W[k,i]^2) ^ alpha      (1 if either is 0)
+ *   W~   = P_out D_out W D_in P_in^T
+ *   H~_X = P_in D_in^-1 H_X D_in^-1 P_in^T
+ *   H~_G = P_out D_out^-1 H_G D_out^-1 P_out^T
+ * which leaves tr(H_G dW H_X dW^T) unchanged for dW mapped like W.
+ *
+ *   W_src, W_dst     device fp32, out x in, contiguous rows (ld = in); may alias
+ *   HX_src, HX_dst   device fp32, in x in symmetric, contiguous; may alias
+ *   HG_src, HG_dst   device fp32, out x out symmetric, contiguous; may alias.
+ *                    May both be NULL only in mode KQ_BIIP_IN_ONLY.
+ *   sign_in/out      device int8 +-1, lengths in / out (sign_out unused in IN_ONLY,
+ *                    sign_in unused in OUT_ONLY)
+ *   had_block_in/out Hadamard block per side: 0 = largest power of 2 dividing
+ *                    the size; else a power of 2 in [1, 16384] dividing it
+ *   alpha            rescale exponent (0.25 for weight-only KronQ)
+ *   mode             KQ_BIIP_*
+ *   d_in, d_out      device fp32 outputs, lengths in / out (1 where not rescaled)
+ * Sizes: 1 <= in, out; in and out must be multiples of 4.
+ */
+kq_status kq_biip_rotate(const float* W_src, float* W_dst, int64_t out, int64_t in,
+                         const float* HX_src, float* HX_dst, const float* HG_src, float* HG_dst,
+                         const int8_t* sign_in, const int8_t* sign_out, int64_t had_block_in,
+                         int64_t had_block_out, float alpha, int mode, float* d_in, float* d_out,
+                         void* stream);
+
+/*
+ * kq_quantize_layer_workspace -- device workspace bytes kq_quantize_layer needs.
+ *   with_loss: nonzero if the call will request losses.
+ */
+kq_status kq_quantize_layer_workspace(const kq_quant_params* p, int64_t out, int64_t in,
+                                      int with_loss, size_t* bytes);
+
+/*
+ * kq_quantize_layer -- damp, factor and GPTQ-quantize a processed layer to packed codes.
+ *
+ * Follows: KronQ README, opening section (weight-only W2-W4, GPTQ-based with
+ * the K-FAC objective tr(H_G dW H_X dW^T)) and flags table (GPTQ base
+ * quantizer, --w_asym, --w_groupsize).  Steps:
+ *   dead input channels (H~_X[i,i] == 0): diagonal set to 1, weight column zeroed;
+ *   lambda = damp * mean(diag H~_X);  H_d = H~_X + lambda I;
+ *   GPTQ column by column with U = chol_upper(H_d^-1): at each group's first
+ *   column the (row, group) grid is taken from the current weights
+ *   (xmin = min(0, min), xmax = max(0, max), s = (xmax - xmin) / (2^b - 1) or 1 if
+ *   equal, z = rint(-xmin / s)); code q = clamp(rint(w / s) + z, 0, 2^b - 1)
+ *   (round half to even); the rounding error is fed back into later columns.
+ * Implementation: reverse-order Cholesky H_d = R R^T (R upper, U = R^-1) and a
+ * left-looking blocked update; equal to the column recursion in exact arithmetic.
+ *
+ *   W_rot     device fp32, out x in (ld = in), the processed weights W~.  Clobbered:
+ *             on return holds dW = W~ - Qhat (dequantized error), dead columns 0.
+ *   HX_rot    device fp32, in x in symmetric (ld = in), H~_X; not modified
+ *   HG_rot    device fp32, out x out (ld = out), H~_G; used only for losses; may be NULL
+ *             (identity)
+ *   packed    device uint32, out x (in * bits / 32): row r's codes as one
+ *             little-endian bitstream, code i at bits [bits*i, bits*i + bits)
+ *   scales    device fp32, out x (in / group)
+ *   zeros     device uint8, out x (in / group)
+ *   codes_opt device uint8, out x in, or NULL
+ *   loss_opt  host double[2] or NULL: {tr(H~_G dW H~_X dW^T), the same with H_d}
+ *             (direct loss and GPTQ's predicted loss sum_j e_j^T H~_G e_j).
+ *             When non-NULL the call synchronizes `stream`.
+ *   ws        device workspace of ws_bytes >= kq_quantize_layer_workspace(...)
+ * Sizes: in % 32 == 0, in % group == 0, in % block == 0, 1 <= out.
+ * Synchronizes `stream` before returning (to report KQ_ENOTSPD).
+ */
+kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, const float* HX_rot,
+                            const float* HG_rot, int64_t out, int64_t in, uint32_t* packed,
+                            float* scales, uint8_t* zeros, uint8_t* codes_opt, double* loss_opt,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kq_allocate_bits -- per-sublayer bit widths from sensitivities (host only).
+ *
+ * Follows: KronQ README, opening section and flags table (inter-layer mixed
+ * precision, --inter_layer_mp); KronQ arXiv abstract, point 2.  The rule is
+ * not stated on the pages; this engine's rule: every sublayer starts at the
+ * smallest allowed width; while sum_l bits_l * numel_l stays within
+ * floor(sum_l numel_l * target_num / target_den), the sublayer with the
+ * largest gain_l = (sens_l * (4^-b_l - 4^-b_next)) / (numel_l * (b_next - b_l))
+ * moves to its next allowed width (ties: smallest index).  Deterministic.
+ *
+ *   sens      host, L fp64 sensitivities (>= 0)
+ *   numel     host, L int64 parameter counts (> 0)
+ *   allowed   host, n_allowed distinct widths in [1, 16] (any order)
+ *   target_num/target_den  average-bit budget as a fraction (> 0)
+ *   bits_out  host, L ints
+ */
+kq_status kq_allocate_bits(const double* sens, const int64_t* numel, int64_t L, const int* allowed,
+                           int n_allowed, int64_t target_num, int64_t target_den, int* bits_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KQ_H */

@@ -1,0 +1,66 @@
+// Error reporting, version and small utility kernels.
+#include "kq_internal.h"
+
+#include <string.h>
+
+namespace kq {
+
+static thread_local char g_last_error[512] = "";
+
+kq_status fail(kq_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+__global__ void fill_f32_kernel(float* __restrict__ p, int64_t n, float v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) p[i] = v;
+}
+
+__global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) p[i] = v;
+}
+
+kq_status fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return KQ_OK;
+  int64_t blocks = ceil_div(n, 256);
+  if (blocks > 8192) blocks = 8192;
+  fill_f32_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p, n, v);
+  KQ_LAUNCHED("fill_f32_kernel");
+  return KQ_OK;
+}
+
+kq_status fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
+  if (n <= 0) return KQ_OK;
+  int64_t blocks = ceil_div(n, 256);
+  if (blocks > 8192) blocks = 8192;
+  fill_u32_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p, n, v);
+  KQ_LAUNCHED("fill_u32_kernel");
+  return KQ_OK;
+}
+
+}  // namespace kq
+
+extern "C" int kq_version(void) { return 100; /* 0.1.0 */ }
+
+extern "C" const char* kq_last_error(void) { return kq::g_last_error; }

@@ -1,0 +1,36 @@
+"""Helpers for the GPU parity tests: moving seeded inputs to the device."""
+import sys
+
+import numpy as np
+import pytest
+
+
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    return torch
+
+
+def to_dev_bf16(bits: np.ndarray, lda: int | None = None):
+    """uint16 bf16 bit patterns [T x n] -> device bfloat16 tensor (optionally row-padded to lda)."""
+    torch = torch_cuda()
+    T, n = bits.shape
+    if lda is None or lda == n:
+        h = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+        return h.to("cuda").view(torch.bfloat16)
+    buf = np.zeros((T, lda), dtype=np.uint16)
+    buf[:, :n] = bits
+    h = torch.from_numpy(buf.view(np.int16)).to("cuda").view(torch.bfloat16)
+    return h[:, :n]
+
+
+def rel_fro(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def announce(msg: str) -> None:
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()

@@ -1,0 +1,100 @@
+"""Host-side checks of the C-ABI library: it loads, exports every declared
+symbol, rejects bad arguments before touching a GPU, and its host-only bit
+allocator matches the oracle bit for bit."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as o
+import post_quantization_syrk_amd as kq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "kq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kq_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_five_engine_calls():
+    syms = declared_symbols()
+    for name in ("kq_accumulate_hessian", "kq_biip_rotate", "kq_quantize_layer", "kq_sensitivity",
+                 "kq_allocate_bits"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kq.load_library()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert set(declared_symbols()) == set(kq.EXPORTED)
+    assert kq.version() >= 100
+
+
+def _raw():
+    return kq.load_library()
+
+
+def test_hessian_rejects_bad_arguments_on_host():
+    lib = _raw()
+    buf = ctypes.c_void_p(0x1000)
+    assert lib.kq_accumulate_hessian(buf, 16, 8, 8, None, 8, 0, None) == kq.KQ_EINVAL
+    assert lib.kq_accumulate_hessian(None, 16, 8, 8, buf, 8, 0, None) == kq.KQ_EINVAL
+    assert lib.kq_accumulate_hessian(buf, 16, 8, 7, buf, 8, 0, None) == kq.KQ_ESHAPE
+    assert lib.kq_accumulate_hessian(buf, 16, 8, 12, buf, 8, 0, None) == kq.KQ_ESHAPE
+    assert lib.kq_accumulate_hessian(buf, 16, 0, 8, buf, 8, 0, None) == kq.KQ_ESHAPE
+    assert lib.kq_accumulate_hessian(buf, 16, 8, 8, buf, 4, 0, None) == kq.KQ_ESHAPE
+    assert lib.kq_accumulate_hessian(buf, 16, 8, 8, buf, 8, 2, None) == kq.KQ_EINVAL
+    assert lib.kq_accumulate_hessian(ctypes.c_void_p(0x1002), 16, 8, 8, buf, 8, 0, None) == kq.KQ_EINVAL
+    assert b"lda" in lib.kq_last_error() or len(lib.kq_last_error()) > 0
+
+
+def test_sensitivity_rejects_bad_arguments_on_host():
+    lib = _raw()
+    buf = ctypes.c_void_p(0x1000)
+    out = (ctypes.c_double * 3)()
+    assert lib.kq_sensitivity(None, 4, 4, buf, 4, 4, ctypes.cast(out, ctypes.c_void_p), None) == kq.KQ_EINVAL
+    assert lib.kq_sensitivity(buf, 4, 4, buf, 4, 4, None, None) == kq.KQ_EINVAL
+    assert lib.kq_sensitivity(buf, 4, 3, buf, 4, 4, ctypes.cast(out, ctypes.c_void_p), None) == kq.KQ_ESHAPE
+
+
+def test_allocator_rejects_bad_arguments():
+    with pytest.raises(kq.KQError):
+        kq.kq_allocate_bits([1.0, -1.0], [10, 10])
+    with pytest.raises(kq.KQError):
+        kq.kq_allocate_bits([1.0, 2.0], [10, 0])
+    with pytest.raises(kq.KQError):
+        kq.kq_allocate_bits([1.0], [10], allowed=(2, 2))
+    with pytest.raises(kq.KQError):
+        kq.kq_allocate_bits([1.0], [10], target_num=0)
+    assert kq.kq_allocate_bits([], []) == []
+
+
+def test_allocator_worked_examples_match():
+    assert kq.kq_allocate_bits([64, 16, 4, 1], [1, 1, 1, 1]) == [4, 2, 2, 2]
+    assert kq.kq_allocate_bits([100, 10, 1, 0.1], [1, 1, 1, 1]) == [4, 2, 2, 2]
+    assert kq.kq_allocate_bits([1, 1, 1, 1], [1, 1, 1, 1]) == [3, 3, 2, 2]
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_allocator_bit_exact_against_oracle(seed):
+    rng = np.random.default_rng(100 + seed)
+    if seed % 3 == 0:
+        # decoder-stack shape: 32 layers x 7 sublayers of Llama-2-7B
+        numel = [4096 * 4096] * 4 + [11008 * 4096] * 3
+        numel = numel * 32
+    else:
+        numel = list(rng.integers(1, 50, size=int(rng.integers(1, 40))) * 128)
+    L = len(numel)
+    sens = np.exp(3.0 * rng.standard_normal(L)) * 1e12
+    if seed % 5 == 1:
+        sens[: L // 2] = sens[0]        # exact ties
+    allowed = (2, 3, 4) if seed % 4 else (2, 4, 8)
+    tn, td = ((5, 2), (3, 1), (11, 4), (2, 1))[seed % 4]
+    got = kq.kq_allocate_bits(sens, numel, allowed, tn, td)
+    want = o.allocate_bits(sens, numel, allowed, tn, td)
+    assert got == want
