@@ -137,8 +137,9 @@ kq_status kq_sensitivity(const float* HX, int64_t n_in, int64_t ldx, const float
  *                    May both be NULL only in mode KQ_BIIP_IN_ONLY.
  *   sign_in/out      device int8 +-1, lengths in / out (sign_out unused in IN_ONLY,
  *                    sign_in unused in OUT_ONLY)
- *   had_block_in/out Hadamard block per side: 0 = largest power of 2 dividing
- *                    the size; else a power of 2 in [1, 16384] dividing it
+ *   had_block_in/out Hadamard block per side: 0 = the largest power of 2 that
+ *                    divides the size, capped at 8192; else 1 (no transform on
+ *                    that side's rows) or a power of 2 in [4, 8192] dividing it
  *   alpha            rescale exponent (0.25 for weight-only KronQ)
  *   mode             KQ_BIIP_*
  *   d_in, d_out      device fp32 outputs, lengths in / out (1 where not rescaled)
@@ -170,11 +171,13 @@ kq_status kq_quantize_layer_workspace(const kq_quant_params* p, int64_t out, int
  *   (xmin = min(0, min), xmax = max(0, max), s = (xmax - xmin) / (2^b - 1) or 1 if
  *   equal, z = rint(-xmin / s)); code q = clamp(rint(w / s) + z, 0, 2^b - 1)
  *   (round half to even); the rounding error is fed back into later columns.
- * Implementation: reverse-order Cholesky H_d = R R^T (R upper, U = R^-1) and a
- * left-looking blocked update; equal to the column recursion in exact arithmetic.
+ * Implementation: reverse-order Cholesky H_d = R R^T (R upper), U = R^-1, and the
+ * column recursion run 128 (or 64) columns at a time with one matrix product per
+ * block for the feedback from earlier blocks.
  *
  *   W_rot     device fp32, out x in (ld = in), the processed weights W~.  Clobbered:
- *             on return holds dW = W~ - Qhat (dequantized error), dead columns 0.
+ *             on return column j holds GPTQ's error e_j = (w_j - qhat_j) / U_jj
+ *             (dead columns 0), so W~ - Qhat = E U.
  *   HX_rot    device fp32, in x in symmetric (ld = in), H~_X; not modified
  *   HG_rot    device fp32, out x out (ld = out), H~_G; used only for losses; may be NULL
  *             (identity)

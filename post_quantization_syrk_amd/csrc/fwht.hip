@@ -1,0 +1,433 @@
+// Bidirectional incoherence processing (BiIP): rescale + randomized Hadamard
+// rotation of W, H_X and H_G on the input and the output side.
+//
+// KronQ README, opening section: "incoherence rotation + rescaling on both the
+// input and output sides"; flags table: --incoh_kernel had, --alpha 0.25;
+// KronQ arXiv abstract, point 1: the input-side random rotation is extended
+// to the output dimension using the gradient covariance.
+//
+// With P = blockdiag(Had_b) diag(S) / sqrt(b) (Sylvester Hadamard, natural
+// order) and rescale vectors d_in, d_out:
+//   W~   = P_out D_out W D_in P_in^T
+//   H~_X = P_in D_in^-1 H_X D_in^-1 P_in^T,   H~_G = P_out D_out^-1 H_G D_out^-1 P_out^T
+// All diagonal factors (rescale, signs, 1/sqrt(b)) are folded into the loads
+// of one row pass; the transform along the strided (row) index is done by
+// tiled column passes.  Every pass reads and writes each element once.
+//
+// Row pass (wavefront-shuffle FWHT): a Hadamard block of b contiguous
+// elements is spread over b/EPT threads with EPT values each (16-byte
+// vectors).  Butterflies over the in-register index bits run in registers,
+// over the lane bits with cross-lane xor shuffles, and over the wave bits
+// (blocks longer than 64 * EPT) through LDS.
+// Column pass: a tile of R = 2^mb rows (stride 2^k0) x 64 columns; each
+// thread holds 4 columns x R/16 rows, butterflies the register bits, then
+// one LDS transpose brings the remaining row bits into registers.
+#include "kq_internal.h"
+
+#include <math.h>
+
+namespace kq {
+namespace {
+
+constexpr int NT = 256;
+
+// ---------------------------------------------------------------------------
+// norms and rescale vectors
+// ---------------------------------------------------------------------------
+// colsum[i] += sum over a stripe of rows of W[r][i]^2   (colsum pre-zeroed)
+__global__ __launch_bounds__(NT) void col_sumsq_kernel(const float* __restrict__ W, int64_t out,
+                                                       int64_t in, int rows_per_block,
+                                                       float* __restrict__ colsum) {
+  const int64_t c = ((int64_t)blockIdx.x * NT + threadIdx.x) * 4;
+  if (c >= in) return;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+  const int64_t r1 = min(out, r0 + rows_per_block);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t r = r0; r < r1; ++r) {
+    float4 v = *(const float4*)(W + r * in + c);
+    acc.x += v.x * v.x; acc.y += v.y * v.y; acc.z += v.z * v.z; acc.w += v.w * v.w;
+  }
+  atomicAdd(colsum + c + 0, acc.x);
+  atomicAdd(colsum + c + 1, acc.y);
+  atomicAdd(colsum + c + 2, acc.z);
+  atomicAdd(colsum + c + 3, acc.w);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// rowsum[r] = sum_i W[r][i]^2, one workgroup per row
+__global__ __launch_bounds__(NT) void row_sumsq_kernel(const float* __restrict__ W, int64_t in,
+                                                       float* __restrict__ rowsum) {
+  const float* row = W + (int64_t)blockIdx.x * in;
+  float acc = 0.f;
+  for (int64_t c = threadIdx.x * 4; c < in; c += NT * 4) {
+    float4 v = *(const float4*)(row + c);
+    acc += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  acc = wave_sum(acc);
+  __shared__ float part[NT / 64];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) rowsum[blockIdx.x] = part[0] + part[1] + part[2] + part[3];
+}
+
+// d[i] = (H[i,i] / norm[i])^alpha, 1 where either is not positive (in place over norm)
+__global__ void rescale_kernel(const float* __restrict__ H, int64_t n, float* __restrict__ d,
+                               float alpha) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const double h = (double)H[i * n + i];
+  const double c = (double)d[i];
+  d[i] = (h > 0.0 && c > 0.0) ? (float)pow(h / c, (double)alpha) : 1.0f;
+}
+
+// ---------------------------------------------------------------------------
+// row pass
+// ---------------------------------------------------------------------------
+struct Scale {
+  const float* d;       // rescale vector or NULL
+  const int8_t* sign;   // +-1 or NULL
+  int invert;           // use 1/d instead of d
+  float mul;            // constant factor (1/sqrt(b))
+};
+
+__device__ __forceinline__ float scale_at(const Scale& s, int64_t i) {
+  float v = s.mul;
+  if (s.d) v = s.invert ? v / s.d[i] : v * s.d[i];
+  if (s.sign) v = s.sign[i] < 0 ? -v : v;
+  return v;
+}
+
+template <int EPT>
+__global__ __launch_bounds__(NT) void row_fwht_kernel(const float* __restrict__ src,
+                                                      float* __restrict__ dst, int64_t rows,
+                                                      int64_t n, int b, Scale rs, Scale cs) {
+  extern __shared__ float sm[];
+  const int TPR = b / EPT;               // threads per Hadamard block (power of 2, <= 256)
+  const int BPW = NT / TPR;              // blocks per workgroup
+  const int tid = threadIdx.x;
+  const int lb = tid / TPR, tb = tid % TPR;
+  const int64_t blocks_per_row = n / b;
+  const int64_t g = (int64_t)blockIdx.x * BPW + lb;
+  const bool active = g < rows * blocks_per_row;
+  const int64_t r = active ? g / blocks_per_row : 0;
+  const int64_t c0 = active ? (g % blocks_per_row) * b : 0;
+
+  float v[EPT];
+  if (active) {
+    const float rsc = scale_at(rs, r);
+    const float* p = src + r * n + c0;
+#pragma unroll
+    for (int j = 0; j < EPT / 4; ++j) {
+      const int x = 4 * tb + 4 * TPR * j;
+      float4 q = *(const float4*)(p + x);
+      v[4 * j + 0] = q.x * rsc * scale_at(cs, c0 + x + 0);
+      v[4 * j + 1] = q.y * rsc * scale_at(cs, c0 + x + 1);
+      v[4 * j + 2] = q.z * rsc * scale_at(cs, c0 + x + 2);
+      v[4 * j + 3] = q.w * rsc * scale_at(cs, c0 + x + 3);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) v[e] = 0.f;
+  }
+  // register bits: e = 4j + q  <->  x = q + 4*tb + 4*TPR*j
+#pragma unroll
+  for (int m = 1; m < EPT; m <<= 1) {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      if (e & m) continue;
+      const float a = v[e], c = v[e | m];
+      v[e] = a + c;
+      v[e | m] = a - c;
+    }
+  }
+  // lane bits of tb (thread index inside the block, within one wave)
+  for (int k = 1; k < TPR && k < 64; k <<= 1) {
+    const bool hi = (tb & k) != 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const float p = __shfl_xor(v[e], k);
+      v[e] = hi ? p - v[e] : v[e] + p;
+    }
+  }
+  if (TPR <= 64) {
+    if (!active) return;
+    float* q = dst + r * n + c0;
+#pragma unroll
+    for (int j = 0; j < EPT / 4; ++j) {
+      const int x = 4 * tb + 4 * TPR * j;
+      *(float4*)(q + x) = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+    }
+    return;
+  }
+  // wave bits: butterflies in LDS over index bits of x at positions 8 .. log2(4*TPR)-1
+  float* blk = sm + lb * b;
+#pragma unroll
+  for (int j = 0; j < EPT / 4; ++j) {
+    const int x = 4 * tb + 4 * TPR * j;
+    *(float4*)(blk + x) = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+  }
+  for (int kb = 8; (1 << kb) < 4 * TPR; ++kb) {
+    __syncthreads();
+    // b/2 pairs per block = b/8 float4 pairs, spread over the TPR threads of the block
+    for (int p4 = tb; p4 < b / 8; p4 += TPR) {
+      const int pl = p4 * 4;  // pair index of the first of 4 consecutive pairs
+      const int lo = ((pl >> kb) << (kb + 1)) | (pl & ((1 << kb) - 1));
+      const int hi = lo | (1 << kb);
+      float4 a = *(float4*)(blk + lo), c = *(float4*)(blk + hi);
+      *(float4*)(blk + lo) = make_float4(a.x + c.x, a.y + c.y, a.z + c.z, a.w + c.w);
+      *(float4*)(blk + hi) = make_float4(a.x - c.x, a.y - c.y, a.z - c.z, a.w - c.w);
+    }
+  }
+  __syncthreads();
+  if (!active) return;
+  float* q = dst + r * n + c0;
+#pragma unroll
+  for (int j = 0; j < EPT / 4; ++j) {
+    const int x = 4 * tb + 4 * TPR * j;
+    *(float4*)(q + x) = *(const float4*)(blk + x);
+  }
+}
+
+// Pure scaling (no transform on this side): dst[r][c] = src[r][c] * rs(r) * cs(c)
+__global__ __launch_bounds__(NT) void scale_kernel(const float* __restrict__ src,
+                                                   float* __restrict__ dst, int64_t rows,
+                                                   int64_t n, Scale rs, Scale cs) {
+  const int64_t i4 = ((int64_t)blockIdx.x * NT + threadIdx.x) * 4;
+  if (i4 >= rows * n) return;
+  const int64_t r = i4 / n, c = i4 % n;
+  const float a = scale_at(rs, r);
+  float4 q = *(const float4*)(src + i4);
+  q.x *= a * scale_at(cs, c);
+  q.y *= a * scale_at(cs, c + 1);
+  q.z *= a * scale_at(cs, c + 2);
+  q.w *= a * scale_at(cs, c + 3);
+  *(float4*)(dst + i4) = q;
+}
+
+// ---------------------------------------------------------------------------
+// column pass: FWHT along the row index over bits [k0, k0 + MB)
+// ---------------------------------------------------------------------------
+constexpr int CW = 64;       // columns per tile
+constexpr int CLD = CW + 4;  // LDS row stride (floats)
+
+template <int MB>
+__global__ __launch_bounds__(NT) void col_fwht_kernel(float* __restrict__ M, int64_t rows,
+                                                      int64_t ncols, int k0) {
+  constexpr int R = 1 << MB;
+  constexpr int RA = R >= 16 ? R / 16 : 1;   // rows per thread in phase A (stride 16)
+  constexpr int GA = R >= 16 ? 16 : R;       // row groups in phase A
+  constexpr int RB = R >= 16 ? 16 : R;       // rows per thread in phase B (consecutive)
+  constexpr int GB = R >= 16 ? R / 16 : 1;   // row groups in phase B
+  __shared__ __attribute__((aligned(16))) float tile[R * CLD];
+
+  const int64_t beta = blockIdx.x;
+  const int64_t base = ((beta >> k0) << (k0 + MB)) | (beta & (((int64_t)1 << k0) - 1));
+  const int64_t c = (int64_t)blockIdx.y * CW + 4 * (threadIdx.x & 15);
+  const int cq = threadIdx.x & 15;
+  const int rg = threadIdx.x >> 4;
+  const bool cok = c < ncols;
+
+  // phase A: rows rg + 16*i (i = register index), butterflies over the i bits
+  if (rg < GA) {
+    float4 v[RA];
+#pragma unroll
+    for (int i = 0; i < RA; ++i) {
+      const int tr = rg + GA * i;
+      const int64_t gr = base + ((int64_t)tr << k0);
+      v[i] = cok ? *(const float4*)(M + gr * ncols + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int m = 1; m < RA; m <<= 1)
+#pragma unroll
+      for (int i = 0; i < RA; ++i) {
+        if (i & m) continue;
+        const float4 a = v[i], b = v[i | m];
+        v[i] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+        v[i | m] = make_float4(a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w);
+      }
+#pragma unroll
+    for (int i = 0; i < RA; ++i) *(float4*)(tile + (rg + GA * i) * CLD + 4 * cq) = v[i];
+  }
+  __syncthreads();
+  // phase B: rows RB*rg + i, butterflies over the low bits
+  if (rg < GB) {
+    float4 v[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) v[i] = *(const float4*)(tile + (RB * rg + i) * CLD + 4 * cq);
+#pragma unroll
+    for (int m = 1; m < RB; m <<= 1)
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        if (i & m) continue;
+        const float4 a = v[i], b = v[i | m];
+        v[i] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+        v[i | m] = make_float4(a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w);
+      }
+    if (cok) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const int64_t gr = base + ((int64_t)(RB * rg + i) << k0);
+        *(float4*)(M + gr * ncols + c) = v[i];
+      }
+    }
+  }
+}
+
+kq_status launch_col_pass(float* M, int64_t rows, int64_t ncols, int k0, int mb, hipStream_t s) {
+  dim3 grid((unsigned)(rows >> mb), (unsigned)ceil_div(ncols, CW));
+  switch (mb) {
+#define KQ_COL_CASE(X) \
+  case X: col_fwht_kernel<X><<<grid, dim3(NT), 0, s>>>(M, rows, ncols, k0); break;
+    KQ_COL_CASE(1) KQ_COL_CASE(2) KQ_COL_CASE(3) KQ_COL_CASE(4)
+    KQ_COL_CASE(5) KQ_COL_CASE(6) KQ_COL_CASE(7) KQ_COL_CASE(8)
+#undef KQ_COL_CASE
+    default: return fail(KQ_EINVAL, "column pass width %d", mb);
+  }
+  KQ_LAUNCHED("col_fwht_kernel");
+  return KQ_OK;
+}
+
+// FWHT of every column over blocks of b rows (b a power of 2): ceil(log2 b / 8) passes.
+kq_status column_transform(float* M, int64_t rows, int64_t ncols, int64_t b, hipStream_t s) {
+  int m = 0;
+  while (((int64_t)1 << m) < b) ++m;
+  if (m == 0) return KQ_OK;
+  const int passes = (m + 7) / 8;
+  int k0 = 0;
+  for (int p = 0; p < passes; ++p) {
+    const int mb = (m - k0) / (passes - p);
+    KQ_TRY(launch_col_pass(M, rows, ncols, k0, mb, s));
+    k0 += mb;
+  }
+  return KQ_OK;
+}
+
+// Row transform with fused scaling: every row of dst = FWHT_b(row of src * rs * cs).
+kq_status row_transform(const float* src, float* dst, int64_t rows, int64_t n, int64_t b,
+                        Scale rs, Scale cs, hipStream_t s) {
+  if (b <= 1) {
+    const int64_t tot4 = rows * n / 4;
+    scale_kernel<<<dim3((unsigned)ceil_div(tot4, NT)), dim3(NT), 0, s>>>(src, dst, rows, n, rs, cs);
+    KQ_LAUNCHED("scale_kernel");
+    return KQ_OK;
+  }
+  const int ept = b <= 1024 ? 4 : (int)(b / 256);
+  const int tpr = (int)(b / ept);
+  const int bpw = NT / tpr;
+  const int64_t nblocks = rows * (n / b);
+  const dim3 grid((unsigned)ceil_div(nblocks, bpw));
+  const size_t shm = tpr > 64 ? (size_t)bpw * b * sizeof(float) : 0;
+  switch (ept) {
+#define KQ_ROW_CASE(X)                                                                   \
+  case X:                                                                                \
+    row_fwht_kernel<X><<<grid, dim3(NT), shm, s>>>(src, dst, rows, n, (int)b, rs, cs); \
+    break;
+    KQ_ROW_CASE(4) KQ_ROW_CASE(8) KQ_ROW_CASE(16) KQ_ROW_CASE(32)
+#undef KQ_ROW_CASE
+    default: return fail(KQ_EINVAL, "row transform block %lld", (long long)b);
+  }
+  KQ_LAUNCHED("row_fwht_kernel");
+  return KQ_OK;
+}
+
+kq_status copy_if_needed(const float* src, float* dst, int64_t count, hipStream_t s) {
+  if (src == dst || count == 0) return KQ_OK;
+  KQ_HIP(hipMemcpyAsync(dst, src, count * sizeof(float), hipMemcpyDeviceToDevice, s));
+  return KQ_OK;
+}
+
+bool valid_block(int64_t n, int64_t b) {
+  if (b == 1) return true;
+  return b >= 4 && b <= 8192 && is_pow2(b) && n % b == 0;
+}
+
+}  // namespace
+}  // namespace kq
+
+extern "C" kq_status kq_biip_rotate(const float* W_src, float* W_dst, int64_t out, int64_t in,
+                                    const float* HX_src, float* HX_dst, const float* HG_src,
+                                    float* HG_dst, const int8_t* sign_in, const int8_t* sign_out,
+                                    int64_t had_block_in, int64_t had_block_out, float alpha,
+                                    int mode, float* d_in, float* d_out, void* stream) {
+  using namespace kq;
+  if (mode < KQ_BIIP_FULL || mode > KQ_BIIP_OUT_ONLY)
+    return fail(KQ_EINVAL, "kq_biip_rotate: bad mode %d", mode);
+  const bool do_in = mode != KQ_BIIP_OUT_ONLY;
+  const bool do_out = mode != KQ_BIIP_IN_ONLY;
+  const bool rescale = mode != KQ_BIIP_NO_RESCALE;
+  if (!W_src || !W_dst || !HX_src || !HX_dst || !d_in || !d_out)
+    return fail(KQ_EINVAL, "kq_biip_rotate: NULL argument");
+  if ((HG_src == nullptr) != (HG_dst == nullptr))
+    return fail(KQ_EINVAL, "kq_biip_rotate: HG_src and HG_dst must both be set or both NULL");
+  if (!HG_src && mode != KQ_BIIP_IN_ONLY)
+    return fail(KQ_EINVAL, "kq_biip_rotate: H_G is required unless mode is IN_ONLY");
+  if ((do_in && !sign_in) || (do_out && !sign_out))
+    return fail(KQ_EINVAL, "kq_biip_rotate: sign vector missing");
+  if (out < 1 || in < 1 || out % 4 || in % 4 || out > (1 << 30) || in > (1 << 30))
+    return fail(KQ_ESHAPE, "kq_biip_rotate: out and in must be positive multiples of 4");
+  if (!(alpha >= 0.f) || !isfinite(alpha)) return fail(KQ_EINVAL, "kq_biip_rotate: alpha");
+  int64_t bin = had_block_in == 0 ? (in & -in) : had_block_in;
+  int64_t bout = had_block_out == 0 ? (out & -out) : had_block_out;
+  if (had_block_in == 0) { while (bin > 8192) bin >>= 1; }
+  if (had_block_out == 0) { while (bout > 8192) bout >>= 1; }
+  if (do_in && !valid_block(in, bin))
+    return fail(KQ_ESHAPE, "kq_biip_rotate: input Hadamard block %lld does not tile in=%lld",
+                (long long)bin, (long long)in);
+  if (do_out && !valid_block(out, bout))
+    return fail(KQ_ESHAPE, "kq_biip_rotate: output Hadamard block %lld does not tile out=%lld",
+                (long long)bout, (long long)out);
+  hipStream_t s = as_stream(stream);
+
+  // 1. rescale vectors (norms of the original W, diagonals of the raw factors)
+  if (rescale && do_in) {
+    KQ_TRY(fill_f32(d_in, in, 0.f, s));
+    const int rpb = 64;
+    dim3 grid((unsigned)ceil_div(in / 4, NT), (unsigned)ceil_div(out, rpb));
+    col_sumsq_kernel<<<grid, dim3(NT), 0, s>>>(W_src, out, in, rpb, d_in);
+    KQ_LAUNCHED("col_sumsq_kernel");
+    rescale_kernel<<<dim3((unsigned)ceil_div(in, 256)), dim3(256), 0, s>>>(HX_src, in, d_in, alpha);
+    KQ_LAUNCHED("rescale_kernel");
+  } else {
+    KQ_TRY(fill_f32(d_in, in, 1.f, s));
+  }
+  if (rescale && do_out) {
+    row_sumsq_kernel<<<dim3((unsigned)out), dim3(NT), 0, s>>>(W_src, in, d_out);
+    KQ_LAUNCHED("row_sumsq_kernel");
+    rescale_kernel<<<dim3((unsigned)ceil_div(out, 256)), dim3(256), 0, s>>>(HG_src, out, d_out, alpha);
+    KQ_LAUNCHED("rescale_kernel");
+  } else {
+    KQ_TRY(fill_f32(d_out, out, 1.f, s));
+  }
+
+  const float isb_in = do_in ? (float)(1.0 / sqrt((double)bin)) : 1.f;
+  const float isb_out = do_out ? (float)(1.0 / sqrt((double)bout)) : 1.f;
+  // 2. W~ = P_out D_out W D_in P_in^T : fused scaling + row FWHT, then column FWHT
+  Scale w_rs{do_out ? d_out : nullptr, do_out ? sign_out : nullptr, 0, isb_out};
+  Scale w_cs{do_in ? d_in : nullptr, do_in ? sign_in : nullptr, 0, isb_in};
+  KQ_TRY(row_transform(W_src, W_dst, out, in, do_in ? bin : 1, w_rs, w_cs, s));
+  if (do_out) KQ_TRY(column_transform(W_dst, out, in, bout, s));
+  // 3. H~_X = P_in D_in^-1 H_X D_in^-1 P_in^T
+  if (do_in) {
+    Scale hs{d_in, sign_in, 1, isb_in};
+    KQ_TRY(row_transform(HX_src, HX_dst, in, in, bin, hs, hs, s));
+    KQ_TRY(column_transform(HX_dst, in, in, bin, s));
+  } else {
+    KQ_TRY(copy_if_needed(HX_src, HX_dst, in * in, s));
+  }
+  // 4. H~_G = P_out D_out^-1 H_G D_out^-1 P_out^T
+  if (HG_src) {
+    if (do_out) {
+      Scale hs{d_out, sign_out, 1, isb_out};
+      KQ_TRY(row_transform(HG_src, HG_dst, out, out, bout, hs, hs, s));
+      KQ_TRY(column_transform(HG_dst, out, out, bout, s));
+    } else {
+      KQ_TRY(copy_if_needed(HG_src, HG_dst, out * out, s));
+    }
+  }
+  return KQ_OK;
+}

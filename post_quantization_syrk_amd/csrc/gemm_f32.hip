@@ -1,0 +1,234 @@
+// fp32 matrix products on the matrix cores (v_mfma_f32_32x32x2_f32), used by
+// the quantizer: the blocked factorization's panel and trailing updates, the
+// left-looking GPTQ block update and the proxy-loss products.
+//
+// C[M x N] (+)= alpha * op(A) op(B), row-major.  128 x 128 tiles, 256 threads
+// (4 waves, each a 64 x 64 sub-tile = 2 x 2 MFMA blocks), 16-deep K stages
+// through LDS stored k-major so every MFMA operand read is 32 consecutive
+// floats.  Optional split-K with fp32 atomics, upper-triangle-only tile sets,
+// and a reduction epilogue sum(alpha * AB .* D) into an fp64 accumulator.
+#include "kq_internal.h"
+
+namespace kq {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int MT = 128, NTL = 128, BK = 16, THREADS = 256;
+constexpr int LDA_S = MT + 4, LDB_S = NTL + 4;
+
+struct Args {
+  int64_t M, N, K;
+  const float* A; int64_t lda; int transA;
+  const float* B; int64_t ldb; int transB;
+  float* C; int64_t ldc;
+  float alpha;
+  int accumulate, upper_only, a_upper, split_k;
+  int64_t k_per_split;
+  const float* D; int64_t ldd; double* red;
+};
+
+// Loads one BK-deep stage of op(A) (MT x BK) into registers: 2 float4 per thread.
+__device__ __forceinline__ void load_a(const Args& a, int64_t m0, int64_t k0, int64_t kend,
+                                       float4 (&r)[2]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!a.transA) {
+      // A row-major M x K: thread -> row (t/4 + 64u), k quad (t%4)
+      const int64_t row = m0 + (t >> 2) + 64 * u;
+      const int64_t k = k0 + 4 * (t & 3);
+      if (row < a.M && k < kend) v = *(const float4*)(a.A + row * a.lda + k);
+    } else {
+      // A stored K x M: thread -> k (t/32 + 8u), m quad (t%32)
+      const int64_t k = k0 + (t >> 5) + 8 * u;
+      const int64_t col = m0 + 4 * (t & 31);
+      if (k < kend && col < a.M) v = *(const float4*)(a.A + k * a.lda + col);
+    }
+    r[u] = v;
+  }
+}
+
+__device__ __forceinline__ void load_b(const Args& a, int64_t n0, int64_t k0, int64_t kend,
+                                       float4 (&r)[2]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!a.transB) {
+      // B row-major K x N: thread -> k (t/32 + 8u), n quad (t%32)
+      const int64_t k = k0 + (t >> 5) + 8 * u;
+      const int64_t col = n0 + 4 * (t & 31);
+      if (k < kend && col < a.N) v = *(const float4*)(a.B + k * a.ldb + col);
+    } else {
+      // B stored N x K: thread -> n row (t/4 + 64u), k quad (t%4)
+      const int64_t row = n0 + (t >> 2) + 64 * u;
+      const int64_t k = k0 + 4 * (t & 3);
+      if (row < a.N && k < kend) v = *(const float4*)(a.B + row * a.ldb + k);
+    }
+    r[u] = v;
+  }
+}
+
+// Stores a stage k-major: As[k][m], Bs[k][n]
+__device__ __forceinline__ void store_a(const Args& a, float* As, const float4 (&r)[2]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (!a.transA) {
+      const int m = (t >> 2) + 64 * u, k = 4 * (t & 3);
+      As[(k + 0) * LDA_S + m] = r[u].x;
+      As[(k + 1) * LDA_S + m] = r[u].y;
+      As[(k + 2) * LDA_S + m] = r[u].z;
+      As[(k + 3) * LDA_S + m] = r[u].w;
+    } else {
+      const int k = (t >> 5) + 8 * u, m = 4 * (t & 31);
+      *(float4*)(As + k * LDA_S + m) = r[u];
+    }
+  }
+}
+
+__device__ __forceinline__ void store_b(const Args& a, float* Bs, const float4 (&r)[2]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (!a.transB) {
+      const int k = (t >> 5) + 8 * u, n = 4 * (t & 31);
+      *(float4*)(Bs + k * LDB_S + n) = r[u];
+    } else {
+      const int n = (t >> 2) + 64 * u, k = 4 * (t & 3);
+      Bs[(k + 0) * LDB_S + n] = r[u].x;
+      Bs[(k + 1) * LDB_S + n] = r[u].y;
+      Bs[(k + 2) * LDB_S + n] = r[u].z;
+      Bs[(k + 3) * LDB_S + n] = r[u].w;
+    }
+  }
+}
+
+__global__ __launch_bounds__(THREADS) void gemm_f32_kernel(Args a) {
+  const int64_t tm = blockIdx.x, tn = blockIdx.y;
+  if (a.upper_only && tm > tn) return;
+  const int64_t m0 = tm * MT, n0 = tn * NTL;
+  int64_t kbeg = (int64_t)blockIdx.z * a.k_per_split;
+  const int64_t kend = min(a.K, kbeg + a.k_per_split);
+  // upper-triangular A: rows >= m0 are zero for k < m0
+  if (a.a_upper && kbeg < m0) kbeg = min(kend, (m0 / BK) * BK);
+  if (kbeg >= kend && a.split_k > 1) return;
+
+  __shared__ __attribute__((aligned(16))) float As[2][BK * LDA_S];
+  __shared__ __attribute__((aligned(16))) float Bs[2][BK * LDB_S];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int l32 = lane & 31, kh = lane >> 5;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  const int nst = (int)((kend - kbeg + BK - 1) / BK);
+  float4 ra[2], rb[2];
+  if (nst > 0) {
+    load_a(a, m0, kbeg, kend, ra);
+    load_b(a, n0, kbeg, kend, rb);
+    store_a(a, As[0], ra);
+    store_b(a, Bs[0], rb);
+  }
+  __syncthreads();
+  for (int s = 0; s < nst; ++s) {
+    const int buf = s & 1;
+    const bool more = s + 1 < nst;
+    if (more) {
+      load_a(a, m0, kbeg + (int64_t)(s + 1) * BK, kend, ra);
+      load_b(a, n0, kbeg + (int64_t)(s + 1) * BK, kend, rb);
+    }
+    const float* as = As[buf];
+    const float* bs = Bs[buf];
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 2) {
+      float av[2], bv[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) av[i] = as[(kk + kh) * LDA_S + wm + 32 * i + l32];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bv[j] = bs[(kk + kh) * LDB_S + wn + 32 * j + l32];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      store_a(a, As[buf ^ 1], ra);
+      store_b(a, Bs[buf ^ 1], rb);
+    }
+    __syncthreads();
+  }
+
+  const int rh = kh * 4;
+  if (a.red) {
+    double part = 0.0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t col = n0 + wn + 32 * j + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + rh + (r & 3);
+          if (row < a.M && col < a.N)
+            part += (double)(a.alpha * acc[i][j][r]) * (double)a.D[row * a.ldd + col];
+        }
+      }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
+    if (lane == 0) atomicAdd(a.red, part);
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = n0 + wn + 32 * j + l32;
+      if (col >= a.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + rh + (r & 3);
+        if (row >= a.M) continue;
+        float* c = a.C + row * a.ldc + col;
+        const float v = a.alpha * acc[i][j][r];
+        if (a.split_k > 1)
+          atomicAdd(c, v);
+        else
+          *c = a.accumulate ? *c + v : v;
+      }
+    }
+}
+
+}  // namespace
+
+kq_status gemm_f32(const GemmArgs& g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0) return KQ_OK;
+  if (g.split_k < 1 || (g.split_k > 1 && !g.accumulate && !g.red))
+    return fail(KQ_EINVAL, "gemm_f32: split_k > 1 needs accumulation");
+  Args a;
+  a.M = g.M; a.N = g.N; a.K = g.K;
+  a.A = g.A; a.lda = g.lda; a.transA = g.transA;
+  a.B = g.B; a.ldb = g.ldb; a.transB = g.transB;
+  a.C = g.C; a.ldc = g.ldc; a.alpha = g.alpha;
+  a.accumulate = g.accumulate; a.upper_only = g.upper_only; a.a_upper = g.a_upper;
+  a.split_k = g.split_k;
+  a.D = g.D; a.ldd = g.ldd; a.red = g.red;
+  a.k_per_split = ceil_div(ceil_div(g.K > 0 ? g.K : 1, g.split_k), BK) * BK;
+  const int splits = g.K > 0 ? (int)ceil_div(g.K, a.k_per_split) : 1;
+  // one split left: a plain read-add-write gives the same C += alpha AB
+  a.split_k = splits;
+  dim3 grid((unsigned)ceil_div(g.M, MT), (unsigned)ceil_div(g.N, NTL), (unsigned)splits);
+  gemm_f32_kernel<<<grid, dim3(THREADS), 0, s>>>(a);
+  KQ_LAUNCHED("gemm_f32_kernel");
+  return KQ_OK;
+}
+
+}  // namespace kq

@@ -1,0 +1,453 @@
+// GPTQ error-feedback quantization of a processed layer to packed codes.
+//
+// KronQ README, opening section: KronQ extends GPTQ/GPTAQ, quantizing weights
+// only (W2-W4) under the Kronecker objective tr(H_G dW H_X dW^T), with packed
+// int2/int4 storage; "Mapping paper results to flags": GPTQ is the base
+// quantizer, --w_asym / --w_groupsize set the grid.
+//
+// GPTQ's column recursion with U = chol_upper(H_d^-1):
+//   e_j = (w_j - qhat_j) / U_jj,   w_k -= e_j U_jk  (k > j)
+// where the (row, group) grid is taken from the current weights when a group's
+// first column is reached.  It is run blockwise, B columns at a time:
+//   Y = -E[:, <J] U[<J, J]              one fp32 MFMA product (split over K, atomics):
+//                                       the block's current weights are W0[:, J] + Y,
+//                                       exactly GPTQ's state when the block starts
+//   column kernel, column by column inside the block:
+//     (at group starts) min-max grid from the current weights of the group,
+//     q = clamp(rint(w/s) + z), e_j = (w_j - s (q - z)) / U_jj, w_k -= e_j U_jk (k in J)
+//   the codes are packed into the output words in the same kernel; e_j replaces W0_j.
+#include "kq_internal.h"
+
+#include <math.h>
+
+#include <utility>
+
+namespace kq {
+
+kq_status damp_and_factor(const float* HX, float* F, float* T, uint8_t* dead, double* lam,
+                          int* flag, int64_t n, float damp, hipStream_t s);
+
+namespace {
+
+constexpr int LPR = 16;             // lanes per matrix row in the column kernel
+constexpr int CTHREADS = 256;       // threads per workgroup in the column kernel
+constexpr int RPW = CTHREADS / LPR; // matrix rows per workgroup
+
+struct ColArgs {
+  float* W;            // out x in: W0 (unprocessed columns) / errors e (processed columns)
+  int64_t out, in;
+  float* Y;            // out x B corrections of the current block (-E U)
+  const float* U;      // in x in upper triangular, chol_upper(H_d^-1)
+  const uint8_t* dead; // in
+  int bits;
+  float maxq;
+  int64_t ngroups;     // in / group
+  float* scales;       // out x ngroups
+  uint8_t* zeros;      // out x ngroups
+  uint32_t* packed;    // out x (in * bits / 32)
+  uint8_t* codes;      // out x in or NULL
+};
+
+// Broadcast lane O of every 16-lane row to the whole row (DPP row_newbcast).
+template <int O>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + O, 0xF, 0xF, false));
+}
+
+// min / max over the 16 lanes of a row
+__device__ __forceinline__ float row_min(float v) {
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) v = fminf(v, __shfl_xor(v, m, LPR));
+  return v;
+}
+__device__ __forceinline__ float row_max(float v) {
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, LPR));
+  return v;
+}
+
+template <int CPL>
+struct RowState {
+  float w[CPL];    // current weights of this lane's columns
+  float el[CPL];   // errors e_j once quantized
+  float s, inv, z; // grid of the current group
+};
+
+struct StepCtx {
+  const float* Cb;  // LDS: B x B in-block U (zero on and below the diagonal)
+  const float* Ri;  // LDS: 1 / U_jj of the block's columns
+  uint8_t* Qrow;    // LDS: this row's B codes
+  int q;            // lane within the row
+  bool live;
+  int64_t r, j0;
+  const ColArgs* a;
+};
+
+// One column j of the block (all compile-time indices, so every array stays in registers).
+template <int B, int G, int J>
+__device__ __forceinline__ void gptq_step(RowState<B / LPR>& st, const StepCtx& cx) {
+  constexpr int CPL = B / LPR;
+  constexpr int O = J / CPL, E = J % CPL;
+  if constexpr (G > 0) {
+    if constexpr (J % G == 0) {
+      // group [J, J+G) lives on lanes [J/CPL, (J+G)/CPL); the range always includes 0
+      const bool in = cx.q >= J / CPL && cx.q < (J + G) / CPL;
+      float mn = 0.0f, mx = 0.0f;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        mn = fminf(mn, in ? st.w[e] : 0.0f);
+        mx = fmaxf(mx, in ? st.w[e] : 0.0f);
+      }
+      mn = row_min(mn);
+      mx = row_max(mx);
+      float s = (mx - mn) / cx.a->maxq;
+      if (mx == mn) s = 1.0f;
+      st.s = s;
+      st.inv = 1.0f / s;
+      st.z = rintf(-mn / s);
+      if (cx.live && cx.q == 0) {
+        const int64_t gi = cx.r * cx.a->ngroups + (cx.j0 + J) / G;
+        cx.a->scales[gi] = s;
+        cx.a->zeros[gi] = (uint8_t)st.z;
+      }
+    }
+  }
+  const float wj = row_bcast<O>(st.w[E]);
+  float qv = rintf(wj * st.inv) + st.z;
+  qv = fminf(fmaxf(qv, 0.0f), cx.a->maxq);
+  const float err = (wj - st.s * (qv - st.z)) * cx.Ri[J];
+  const float d = -err;
+  if (cx.q == O) {
+    st.el[E] = err;
+    cx.Qrow[J] = (uint8_t)qv;
+  }
+  const float* crow = cx.Cb + J * B + CPL * cx.q;
+#pragma unroll
+  for (int e = 0; e < CPL; e += 4) {
+    const float4 c = *(const float4*)(crow + e);
+    st.w[e] = fmaf(d, c.x, st.w[e]);
+    st.w[e + 1] = fmaf(d, c.y, st.w[e + 1]);
+    st.w[e + 2] = fmaf(d, c.z, st.w[e + 2]);
+    st.w[e + 3] = fmaf(d, c.w, st.w[e + 3]);
+  }
+}
+
+template <int B, int G, int... J>
+__device__ __forceinline__ void gptq_steps(RowState<B / LPR>& st, const StepCtx& cx,
+                                           std::integer_sequence<int, J...>) {
+  (gptq_step<B, G, J>(st, cx), ...);
+}
+
+// 16 lanes per matrix row, each holding B/16 consecutive columns of the block.
+// Per column: the current weight of column j is broadcast from the owning lane,
+// every lane rounds it (same result), and every lane applies the feedback to its
+// own columns (the LDS copy of U is zero on and below the diagonal, so no masks).
+template <int B, int G>
+__global__ __launch_bounds__(CTHREADS) void gptq_block_kernel(ColArgs a, int64_t j0) {
+  constexpr int CPL = B / LPR;
+  __shared__ __attribute__((aligned(16))) float Cb[B * B];
+  __shared__ float Ri[B];
+  __shared__ __attribute__((aligned(16))) uint8_t Qs[RPW * B];
+  const int t = threadIdx.x;
+  const int q = t % LPR, rl = t / LPR;
+  const int64_t r = (int64_t)blockIdx.x * RPW + rl;
+  const bool live = r < a.out;
+
+  for (int idx = t; idx < B * B / 4; idx += CTHREADS) {
+    const int i = idx / (B / 4), c = 4 * (idx % (B / 4));
+    float4 v = *(const float4*)(a.U + (j0 + i) * a.in + j0 + c);
+    if (i >= c && i < c + 4) {
+      const int k = i - c;
+      Ri[i] = 1.0f / (k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w);
+    }
+    v.x = c + 0 > i ? v.x : 0.0f;
+    v.y = c + 1 > i ? v.y : 0.0f;
+    v.z = c + 2 > i ? v.z : 0.0f;
+    v.w = c + 3 > i ? v.w : 0.0f;
+    *(float4*)(Cb + i * B + c) = v;
+  }
+
+  RowState<CPL> st;
+  const int64_t col = j0 + CPL * q;
+#pragma unroll
+  for (int e = 0; e < CPL; e += 4) {
+    float4 w0 = make_float4(0.f, 0.f, 0.f, 0.f), y = w0;
+    if (live) {
+      w0 = *(const float4*)(a.W + r * a.in + col + e);
+      y = *(const float4*)(a.Y + r * B + CPL * q + e);
+      *(float4*)(a.Y + r * B + CPL * q + e) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const uint8_t* dd = a.dead + col + e;
+    st.w[e] = (dd[0] ? 0.f : w0.x) + y.x;
+    st.w[e + 1] = (dd[1] ? 0.f : w0.y) + y.y;
+    st.w[e + 2] = (dd[2] ? 0.f : w0.z) + y.z;
+    st.w[e + 3] = (dd[3] ? 0.f : w0.w) + y.w;
+    st.el[e] = st.el[e + 1] = st.el[e + 2] = st.el[e + 3] = 0.f;
+  }
+  st.s = 1.0f; st.inv = 1.0f; st.z = 0.0f;
+  if constexpr (G == 0) {  // one group per row: grid taken from the original row beforehand
+    if (live) {
+      st.s = a.scales[r];
+      st.inv = 1.0f / st.s;
+      st.z = (float)a.zeros[r];
+    }
+  }
+  __syncthreads();
+
+  StepCtx cx{Cb, Ri, Qs + rl * B, q, live, r, j0, &a};
+  gptq_steps<B, G>(st, cx, std::make_integer_sequence<int, B>{});
+
+  if (live) {
+#pragma unroll
+    for (int e = 0; e < CPL; e += 4)
+      *(float4*)(a.W + r * a.in + col + e) = make_float4(st.el[e], st.el[e + 1], st.el[e + 2], st.el[e + 3]);
+  }
+  __syncthreads();
+  // pack this row's B codes: bits * B / 32 whole words starting at word j0 * bits / 32
+  if (live) {
+    const int words = a.bits * B / 32;
+    const int64_t wpr = a.in * a.bits / 32;
+    const uint8_t* qr = Qs + rl * B;
+    for (int wd = q; wd < words; wd += LPR) {
+      uint32_t acc = 0;
+      const int bit0 = 32 * wd;
+      for (int c = bit0 / a.bits; c < B && c * a.bits < bit0 + 32; ++c) {
+        const int off = c * a.bits - bit0;   // negative for a code straddling the word start
+        const uint32_t v = qr[c];
+        acc |= off >= 0 ? (v << off) : (v >> (-off));
+      }
+      a.packed[r * wpr + j0 * a.bits / 32 + wd] = acc;
+    }
+    if (a.codes) {
+#pragma unroll
+      for (int e = 0; e < CPL; e += 4)
+        *(uint32_t*)(a.codes + r * a.in + col + e) = *(const uint32_t*)(qr + CPL * q + e);
+    }
+  }
+}
+
+// One (row) group spanning the whole row: grid from the original row (dead columns zeroed).
+__global__ __launch_bounds__(256) void row_grid_kernel(const float* __restrict__ W, int64_t in,
+                                                       const uint8_t* __restrict__ dead, float maxq,
+                                                       float* __restrict__ scales,
+                                                       uint8_t* __restrict__ zeros) {
+  const int64_t r = blockIdx.x;
+  float mn = 0.f, mx = 0.f;
+  for (int64_t c = threadIdx.x; c < in; c += 256) {
+    const float v = dead[c] ? 0.f : W[r * in + c];
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+  }
+  __shared__ float smn[256], smx[256];
+  smn[threadIdx.x] = mn;
+  smx[threadIdx.x] = mx;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      smn[threadIdx.x] = fminf(smn[threadIdx.x], smn[threadIdx.x + w]);
+      smx[threadIdx.x] = fmaxf(smx[threadIdx.x], smx[threadIdx.x + w]);
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    float s = (smx[0] - smn[0]) / maxq;
+    if (smx[0] == smn[0]) s = 1.0f;
+    scales[r] = s;
+    zeros[r] = (uint8_t)rintf(-smn[0] / s);
+  }
+}
+
+// sum of a[i] * b[i] over n elements into *red (fp64)
+__global__ __launch_bounds__(256) void dot_kernel(const float* __restrict__ x,
+                                                  const float* __restrict__ y, int64_t n,
+                                                  double* __restrict__ red) {
+  double s = 0.0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    s += (double)x[i] * (double)y[i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if ((threadIdx.x & 63) == 0) atomicAdd(red, s);
+}
+
+using ColKernel = void (*)(ColArgs, int64_t);
+
+ColKernel pick_kernel(int B, int G) {
+  if (B == 64) {
+    switch (G) {
+      case 0: return gptq_block_kernel<64, 0>;
+      case 16: return gptq_block_kernel<64, 16>;
+      case 32: return gptq_block_kernel<64, 32>;
+      case 64: return gptq_block_kernel<64, 64>;
+    }
+  } else if (B == 128) {
+    switch (G) {
+      case 0: return gptq_block_kernel<128, 0>;
+      case 16: return gptq_block_kernel<128, 16>;
+      case 32: return gptq_block_kernel<128, 32>;
+      case 64: return gptq_block_kernel<128, 64>;
+      case 128: return gptq_block_kernel<128, 128>;
+    }
+  }
+  return nullptr;
+}
+
+struct Layout {
+  size_t f, t, y, dead, scal, flag, tmp, tmp2, total;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Layout layout(int64_t out, int64_t in, int B, bool with_loss) {
+  Layout L;
+  size_t o = 0;
+  L.f = o;    o = align256(o + (size_t)in * in * sizeof(float));
+  L.t = o;    o = align256(o + (size_t)in * 64 * sizeof(float));
+  L.y = o;    o = align256(o + (size_t)out * B * sizeof(float));
+  L.dead = o; o = align256(o + (size_t)in);
+  L.scal = o; o = align256(o + 8 * sizeof(double));
+  L.flag = o; o = align256(o + 4 * sizeof(int));
+  L.tmp = o;  if (with_loss) o = align256(o + (size_t)out * in * sizeof(float));
+  L.tmp2 = o; if (with_loss) o = align256(o + (size_t)out * in * sizeof(float));
+  L.total = o;
+  return L;
+}
+
+kq_status check_params(const kq_quant_params* p, int64_t out, int64_t in) {
+  if (!p) return fail(KQ_EINVAL, "kq_quantize_layer: params is NULL");
+  if (p->bits < 2 || p->bits > 4) return fail(KQ_EINVAL, "bits must be 2, 3 or 4 (got %d)", p->bits);
+  if (p->asym != 1) return fail(KQ_ENOTIMPL, "only the asymmetric grid (asym = 1) is implemented");
+  if (p->act_order != 0) return fail(KQ_ENOTIMPL, "act_order is not implemented");
+  if (!(p->damp >= 0.f) || !isfinite(p->damp)) return fail(KQ_EINVAL, "damp must be >= 0");
+  if (p->block != 64 && p->block != 128) return fail(KQ_EINVAL, "block must be 64 or 128");
+  if (out < 1 || in < 1 || in > (1 << 30) || out > (1 << 30))
+    return fail(KQ_ESHAPE, "bad layer shape");
+  if (in % 32 != 0) return fail(KQ_ESHAPE, "in must be a multiple of 32");
+  if (in % p->block != 0) return fail(KQ_ESHAPE, "in must be a multiple of block");
+  if (p->group <= 0 || in % p->group != 0)
+    return fail(KQ_ESHAPE, "group must be positive and divide in");
+  if (p->group != in && (p->group > p->block || p->block % p->group != 0 ||
+                         (p->group != 16 && p->group != 32 && p->group != 64 && p->group != 128)))
+    return fail(KQ_ESHAPE, "group must be in {16, 32, 64, 128} dividing block, or equal to in");
+  return KQ_OK;
+}
+
+}  // namespace
+}  // namespace kq
+
+extern "C" kq_status kq_quantize_layer_workspace(const kq_quant_params* p, int64_t out, int64_t in,
+                                                 int with_loss, size_t* bytes) {
+  using namespace kq;
+  if (!bytes) return fail(KQ_EINVAL, "kq_quantize_layer_workspace: bytes is NULL");
+  KQ_TRY(check_params(p, out, in));
+  *bytes = layout(out, in, p->block, with_loss != 0).total;
+  return KQ_OK;
+}
+
+extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, const float* HX_rot,
+                                       const float* HG_rot, int64_t out, int64_t in,
+                                       uint32_t* packed, float* scales, uint8_t* zeros,
+                                       uint8_t* codes_opt, double* loss_opt, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  using namespace kq;
+  KQ_TRY(check_params(p, out, in));
+  if (!W_rot || !HX_rot || !packed || !scales || !zeros)
+    return fail(KQ_EINVAL, "kq_quantize_layer: NULL argument");
+  const bool with_loss = loss_opt != nullptr;
+  const int B = p->block;
+  // a group spanning the whole row (group == in > block) takes its grid from the original row
+  const int G = p->group == in && p->group > B ? 0 : p->group;
+  const Layout L = layout(out, in, B, with_loss);
+  if (!ws || ws_bytes < L.total)
+    return fail(KQ_EWORKSPACE, "kq_quantize_layer: workspace of %zu bytes needed", L.total);
+  ColKernel kern = pick_kernel(B, G);
+  if (!kern) return fail(KQ_ESHAPE, "no column kernel for block %d group %d", B, G);
+  hipStream_t s = as_stream(stream);
+  char* base = (char*)ws;
+  float* F = (float*)(base + L.f);
+  float* T = (float*)(base + L.t);
+  float* Y = (float*)(base + L.y);
+  uint8_t* dead = (uint8_t*)(base + L.dead);
+  double* scal = (double*)(base + L.scal);
+  int* flag = (int*)(base + L.flag);
+
+  KQ_TRY(fill_u32((uint32_t*)scal, 16, 0u, s));
+  KQ_TRY(fill_u32((uint32_t*)flag, 4, 0u, s));
+  KQ_TRY(fill_f32(Y, out * B, 0.f, s));
+  KQ_TRY(damp_and_factor(HX_rot, F, T, dead, scal, flag, in, p->damp, s));
+
+  ColArgs a;
+  a.W = W_rot; a.out = out; a.in = in; a.Y = Y; a.U = F; a.dead = dead;
+  a.bits = p->bits; a.maxq = (float)((1 << p->bits) - 1);
+  a.ngroups = in / p->group; a.scales = scales; a.zeros = zeros;
+  a.packed = packed; a.codes = codes_opt;
+  if (G == 0) {
+    row_grid_kernel<<<dim3((unsigned)out), dim3(256), 0, s>>>(W_rot, in, dead, a.maxq, scales, zeros);
+    KQ_LAUNCHED("row_grid_kernel");
+  }
+  const int cus = device_cu_count();
+  const unsigned col_grid = (unsigned)ceil_div(out, RPW);
+  for (int64_t j0 = 0; j0 < in; j0 += B) {
+    if (j0 > 0) {
+      GemmArgs g{};
+      g.M = out; g.N = B; g.K = j0;
+      g.A = W_rot; g.lda = in; g.transA = false;
+      g.B = F + j0; g.ldb = in; g.transB = false;
+      g.C = Y; g.ldc = B; g.alpha = -1.0f; g.accumulate = true; g.upper_only = false;
+      const int64_t tiles = ceil_div(out, 128);
+      int64_t split = (2 * cus + tiles - 1) / tiles;
+      const int64_t max_split = ceil_div(j0, 256);
+      if (split > max_split) split = max_split;
+      if (split < 1) split = 1;
+      g.split_k = (int)split;
+      KQ_TRY(gemm_f32(g, s));
+    }
+    kern<<<dim3(col_grid), dim3(CTHREADS), 0, s>>>(a, j0);
+    KQ_LAUNCHED("gptq_block_kernel");
+  }
+
+  if (with_loss) {
+    float* dW = (float*)(base + L.tmp);
+    float* tmp = (float*)(base + L.tmp2);
+    // predicted loss  sum_j e_j^T H~_G e_j
+    if (HG_rot) {
+      GemmArgs r{};
+      r.M = out; r.N = out; r.K = in;
+      r.A = W_rot; r.lda = in; r.B = W_rot; r.ldb = in; r.transB = true;
+      r.alpha = 1.0f; r.split_k = 1; r.D = HG_rot; r.ldd = out; r.red = scal + 2;
+      KQ_TRY(gemm_f32(r, s));
+    } else {
+      dot_kernel<<<dim3(1024), dim3(256), 0, s>>>(W_rot, W_rot, out * in, scal + 2);
+      KQ_LAUNCHED("dot_kernel");
+    }
+    // dW = E U  (= W~ - Qhat), tmp = dW H~_X (undamped), direct loss sum (tmp dW^T) .* H~_G
+    GemmArgs g{};
+    g.M = out; g.N = in; g.K = in;
+    g.A = W_rot; g.lda = in; g.B = F; g.ldb = in; g.C = dW; g.ldc = in;
+    g.alpha = 1.0f; g.split_k = 1;
+    KQ_TRY(gemm_f32(g, s));
+    GemmArgs h = g;
+    h.A = dW; h.B = HX_rot; h.C = tmp;
+    KQ_TRY(gemm_f32(h, s));
+    if (HG_rot) {
+      GemmArgs r{};
+      r.M = out; r.N = out; r.K = in;
+      r.A = tmp; r.lda = in; r.B = dW; r.ldb = in; r.transB = true;
+      r.alpha = 1.0f; r.split_k = 1; r.D = HG_rot; r.ldd = out; r.red = scal + 1;
+      KQ_TRY(gemm_f32(r, s));
+    } else {
+      dot_kernel<<<dim3(1024), dim3(256), 0, s>>>(tmp, dW, out * in, scal + 1);
+      KQ_LAUNCHED("dot_kernel");
+    }
+  }
+  double host_scal[3] = {0, 0, 0};
+  int host_flag = 0;
+  KQ_HIP(hipMemcpyAsync(host_scal, scal, sizeof(host_scal), hipMemcpyDeviceToHost, s));
+  KQ_HIP(hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, s));
+  KQ_HIP(hipStreamSynchronize(s));
+  if (with_loss) {
+    loss_opt[0] = host_scal[1];
+    loss_opt[1] = host_scal[2];
+  }
+  if (host_flag) return fail(KQ_ENOTSPD, "kq_quantize_layer: damped H_X is not positive definite");
+  return KQ_OK;
+}

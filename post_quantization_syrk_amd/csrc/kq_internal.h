@@ -38,6 +38,7 @@ struct GemmArgs {
   float alpha;        // scale of the product
   bool accumulate;    // C += alpha*AB (else C = alpha*AB)
   bool upper_only;    // only tiles with row-tile <= col-tile
+  bool a_upper;       // op(A) is upper triangular (zeros below): skip K below the tile's rows
   int split_k;        // >= 1; > 1 requires accumulate (atomics)
   // reduce epilogue: instead of writing C, accumulate sum(alpha*AB .* D) into *red (fp64)
   const float* D; int64_t ldd; double* red;
