@@ -1,0 +1,251 @@
+"""Throughput of the KronQ per-layer quantization engine on one MI355X.
+
+One step = the whole per-layer path on one synthetic layer whose inputs are
+already resident in HBM: H_X = X^T X and H_G = G^T G (bf16 MFMA SYRK),
+sensitivity tr(H_G) tr(H_X), BiIP (rescale + randomized Hadamard on both
+sides), damping + reverse Cholesky + triangular inverse, blocked GPTQ to
+packed codes with scales and zero points.  The proxy loss is a verification
+output and is not part of the step.
+
+Default workload: Llama-2-7B-shaped q_proj, 4096 x 4096 weights (bf16 values,
+0.1 % outlier input channels x30), 131072 calibration tokens of X and G
+(bf16, log-normal channel scales sigma 1 / 1.5), W4 asymmetric min-max,
+group 128, block 128, 4096-point Hadamard on both sides.
+
+Prints one JSON line: quantized params/s, the dominant kernel's roofline
+(the SYRK, timed with HIP events on its stream) and the CPU oracle timed on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synthetic as syn  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {"c1": syn.C1, "c2": syn.C2, "c3": syn.C3, "c5": syn.C5}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="approximate CPU budget of the oracle sample")
+    return ap.parse_args()
+
+
+def syrk_flops(n: int, T: int) -> float:
+    """Algorithmic flops of one factor: n(n+1)/2 distinct entries x 2T."""
+    return float(n) * (n + 1) * T
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_src: str, launch_units: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "syrk_bf16_c2_hbm_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != source_hash(kernel_src):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(cfg, budget_s: float) -> dict:
+    """The fp64 CPU oracle, as it stands, on a bounded sample of the same workload.
+
+    Hessians on the first T_s tokens (cost linear in tokens: scaled by T / T_s),
+    BiIP and the damped factorization at full size, GPTQ on R_s rows (rows are
+    independent given U: scaled by out / R_s).  Reported, not a target.
+    """
+    import oracle as o
+
+    out_n, in_n, T = cfg.out, cfg.inp, cfg.tokens
+    scale = budget_s / 20.0
+    T_s = int(min(T, max(1024, 8192 * scale * (4096.0 / max(in_n, out_n)) ** 2)))
+    T_s -= T_s % 64
+    R_s = int(min(out_n, max(16, 256 * scale * 4096.0 / in_n)))
+    t = {}
+    t0 = time.perf_counter()
+    X = o.bf16_bits_to_f64(syn.stream(cfg, "x", tokens=T_s))
+    G = o.bf16_bits_to_f64(syn.stream(cfg, "g", tokens=T_s))
+    t["prep"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    HX = o.hessian_factor(X)
+    HG = o.hessian_factor(G)
+    t["hessians_sample"] = time.perf_counter() - t0
+    del X, G
+    t0 = time.perf_counter()
+    o.sensitivity(HX, HG)
+    Wt, HXt, HGt, _, _ = o.biip(syn.weights(cfg).astype(np.float64), HX, HG, syn.signs(cfg, "in"),
+                                syn.signs(cfg, "out"), cfg.alpha, o.BIIP_FULL, cfg.had_in, cfg.had_out)
+    t["sensitivity_biip"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    fac = o.damp_and_factor(HXt, cfg.damp)
+    t["factor"] = time.perf_counter() - t0
+    rows = np.random.default_rng(0).choice(out_n, R_s, replace=False)
+    t0 = time.perf_counter()
+    r = o.quantize_layer(Wt, HXt, None, cfg.bits, cfg.group, cfg.damp, rows=rows, factor=fac)
+    o.pack_codes(r["gptq"].codes, cfg.bits)
+    t["gptq_pack_sample"] = time.perf_counter() - t0
+    full = (t["hessians_sample"] * T / T_s + t["sensitivity_biip"] + t["factor"]
+            + t["gptq_pack_sample"] * out_n / R_s)
+    return {"value": round(out_n * in_n / full, 1), "unit": "params/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": (f"Hessians on {T_s} of {T} tokens (x{T / T_s:.1f}), BiIP and factorization at "
+                       f"full size, GPTQ+pack on {R_s} of {out_n} rows (x{out_n / R_s:.1f}); "
+                       f"extrapolated full-layer time {full:.1f} s"),
+            "measured_s": {k: round(v, 2) for k, v in t.items()}}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this engine runs on one GPU; --gpus {a.gpus} is not supported "
+              "(the multi-GPU sharding plan is described in the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import post_quantization_syrk_amd as kq
+
+    cfg = WORKLOADS[a.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kq.load_library()
+    stream = torch.cuda.current_stream()
+
+    # ---- inputs (untimed): seeded synthetic streams and weights, uploaded once ----
+    t0 = time.time()
+    bx = syn.stream(cfg, "x")
+    X = torch.from_numpy(bx.view(np.int16)).to(dev).view(torch.bfloat16)
+    del bx
+    bg = syn.stream(cfg, "g")
+    G = torch.from_numpy(bg.view(np.int16)).to(dev).view(torch.bfloat16)
+    del bg
+    W0 = torch.from_numpy(syn.weights(cfg)).to(dev)
+    s_in = torch.from_numpy(syn.signs(cfg, "in")).to(dev)
+    s_out = torch.from_numpy(syn.signs(cfg, "out")).to(dev)
+    gen_s = time.time() - t0
+
+    out_n, in_n, T = cfg.out, cfg.inp, cfg.tokens
+    HX = torch.empty((in_n, in_n), device=dev)
+    HG = torch.empty((out_n, out_n), device=dev)
+    Wt = torch.empty_like(W0)
+    d_in = torch.empty(in_n, device=dev)
+    d_out = torch.empty(out_n, device=dev)
+    p = kq.make_params(cfg.bits, cfg.group, cfg.block, cfg.damp)
+    ws = torch.empty(kq.kq_quantize_layer_workspace(p, out_n, in_n, False), dtype=torch.uint8, device=dev)
+    packed = torch.empty((out_n, in_n * cfg.bits // 32), dtype=torch.int32, device=dev)
+    scales = torch.empty((out_n, in_n // cfg.group), device=dev)
+    zeros = torch.empty((out_n, in_n // cfg.group), dtype=torch.uint8, device=dev)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    stage_names = ["syrk_x", "syrk_g", "sensitivity", "biip", "quantize"]
+
+    def step(record):
+        e = [ev() for _ in range(6)] if record else None
+        if record:
+            e[0].record(stream)
+        kq.kq_accumulate_hessian(X, HX, stream=stream)
+        if record:
+            e[1].record(stream)
+        kq.kq_accumulate_hessian(G, HG, stream=stream)
+        if record:
+            e[2].record(stream)
+        sens = kq.kq_sensitivity(HX, HG, stream=stream)
+        if record:
+            e[3].record(stream)
+        kq.kq_biip_rotate(W0, Wt, HX, HX, HG, HG, s_in, s_out, d_in, d_out, cfg.alpha,
+                          kq.KQ_BIIP_FULL, cfg.had_in, cfg.had_out, stream=stream)
+        if record:
+            e[4].record(stream)
+        kq.kq_quantize_layer(p, Wt, HX, HG, packed, scales, zeros, ws, stream=stream)
+        if record:
+            e[5].record(stream)
+        return e, sens
+
+    for _ in range(a.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    events = []
+    t_start = time.perf_counter()
+    for _ in range(a.steps):
+        e, _ = step(True)
+        events.append(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / a.steps
+    stage_ms = {nm: float(np.mean([es[i].elapsed_time(es[i + 1]) for es in events]))
+                for i, nm in enumerate(stage_names)}
+    params = out_n * in_n
+    value = params / (ms_per_step / 1e3)
+
+    # dominant kernel: the SYRK (one launch per factor); HIP events on its stream
+    syrk_launch_ms = float(np.mean([es[0].elapsed_time(es[1]) for es in events] +
+                                   [es[1].elapsed_time(es[2]) for es in events]))
+    flops_per_launch = 0.5 * (syrk_flops(in_n, T) + syrk_flops(out_n, T))
+    achieved = flops_per_launch / (syrk_launch_ms / 1e3) / 1e12
+    traffic = traffic_from_profile(os.path.join(ROOT, "post_quantization_syrk_amd", "csrc", "syrk.hip"),
+                                   flops_per_launch)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": "syrk_bf16_kernel",
+                "algorithmic_flops_per_launch": flops_per_launch}
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        del X, G
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline(cfg, a.cpu_seconds)
+
+    line = {
+        "metric": "quantized params/s per layer incl. Hessian build",
+        "value": round(value, 1), "unit": "params/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 products / f32 accumulate and quantizer",
+        "data": "synthetic (seeded log-normal-channel streams, Llama-shaped)",
+        "config": {"workload": cfg.name, "out": out_n, "in": in_n, "tokens": T, "bits": cfg.bits,
+                   "group": cfg.group, "block": cfg.block, "hadamard_in": cfg.had_in,
+                   "hadamard_out": cfg.had_out, "alpha": cfg.alpha, "damp": cfg.damp},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "input_generation_s": round(gen_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
