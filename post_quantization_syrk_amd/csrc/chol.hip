@@ -56,69 +56,58 @@ __global__ void add_diag_kernel(float* __restrict__ H, int64_t n, const double* 
   if (i < n) H[i * n + i] = (float)((double)H[i * n + i] + lam[0]);
 }
 
-// Factor the diagonal block at rows/cols [s0, s0 + nb) in place: A22 = R22 R22^T.
-__global__ __launch_bounds__(256) void diag_factor_kernel(float* __restrict__ H, int64_t n,
-                                                          int64_t s0, int nb,
-                                                          int* __restrict__ flag) {
-  __shared__ float A[NB * LD];
-  __shared__ int bad;
-  const int t = threadIdx.x;
-  if (t == 0) bad = 0;
-  for (int e = t; e < nb * nb; e += 256) {
-    const int i = e / nb, k = e % nb;
-    A[i * LD + k] = i <= k ? H[(s0 + i) * n + s0 + k] : 0.0f;
-  }
-  __syncthreads();
-  for (int j = nb - 1; j >= 0; --j) {
-    const float p = A[j * LD + j];
-    const float d = sqrtf(p);
-    if (t == 0 && !(p > 0.0f)) bad = 1;
-    if (t < j) A[t * LD + j] /= d;
-    __syncthreads();
-    if (t == 0) A[j * LD + j] = d;
-    // A[i][k] -= R[i][j] R[k][j] for i <= k < j
-    for (int e = t; e < j * j; e += 256) {
-      const int i = e / j, k = e % j;
-      if (i <= k) A[i * LD + k] -= A[i * LD + j] * A[k * LD + j];
-    }
-    __syncthreads();
-  }
-  for (int e = t; e < nb * nb; e += 256) {
-    const int i = e / nb, k = e % nb;
-    if (i <= k) H[(s0 + i) * n + s0 + k] = A[i * LD + k];
-  }
-  if (t == 0 && bad) atomicOr(flag, 1);
-}
-
-// Rows r < s0: solve x R22^T = h (h = H[r, s0:s0+nb]) and store x over h.
-__global__ __launch_bounds__(256) void panel_solve_kernel(float* __restrict__ H, int64_t n,
-                                                          int64_t s0) {
+// Diagonal block at rows/cols [s0, s0 + NB): factor A22 = R22 R22^T (R22 upper) and
+// store U22 = R22^-1 in its place (zeros below the diagonal).  One wave of 64 lanes,
+// so a barrier costs almost nothing:
+//   factor: lane i holds row i; column j of the elimination goes through LDS and is
+//           read back by every lane (broadcast), A[i][k] -= a_ij a_kj / p (i <= k < j);
+//   inverse: R is staged in LDS; lane c back-substitutes column c of U = R^-1,
+//           U[i][c] = -(sum_{k > i} R[i][k] U[k][c]) / R[i][i], U[c][c] = 1 / R[c][c].
+__global__ __launch_bounds__(NB) void diag_factor_inverse_kernel(float* __restrict__ H, int64_t n,
+                                                                 int64_t s0, int* __restrict__ flag) {
+  __shared__ float col[NB];
   __shared__ float R[NB * LD];
-  const int t = threadIdx.x;
-  for (int e = t; e < NB * NB; e += 256) {
-    const int i = e / NB, k = e % NB;
-    R[i * LD + k] = i <= k ? H[(s0 + i) * n + s0 + k] : 0.0f;
-  }
+  const int l = threadIdx.x;
+  // coalesced load of the block's upper triangle into LDS, then row l into registers
+  for (int i = 0; i < NB; ++i) R[i * LD + l] = l >= i ? H[(s0 + i) * n + s0 + l] : 0.0f;
   __syncthreads();
-  const int64_t r = (int64_t)blockIdx.x * 256 + t;
-  if (r >= s0) return;
-  float* row = H + r * n + s0;
-  float x[NB];
+  float a[NB];
 #pragma unroll
-  for (int k = 0; k < NB; k += 4) {
-    float4 v = *(const float4*)(row + k);
-    x[k] = v.x; x[k + 1] = v.y; x[k + 2] = v.z; x[k + 3] = v.w;
-  }
-  // h_j = sum_{k >= j} x_k R[j][k]  ->  x_j = (h_j - sum_{k > j} x_k R[j][k]) / R[j][j]
+  for (int k = 0; k < NB; ++k) a[k] = R[l * LD + k];
+  bool bad = false;
 #pragma unroll
   for (int j = NB - 1; j >= 0; --j) {
-    float acc = x[j];
+    col[l] = a[j];
+    __syncthreads();
+    const float p = col[j];
+    const float rs = rsqrtf(p);
+    const float f = a[j] * (1.0f / p);
 #pragma unroll
-    for (int k = j + 1; k < NB; ++k) acc -= x[k] * R[j * LD + k];
-    x[j] = acc / R[j * LD + j];
+    for (int k = 0; k < j; ++k) {
+      const float upd = fmaf(-f, col[k], a[k]);
+      a[k] = k >= l ? upd : a[k];
+    }
+    a[j] = l < j ? a[j] * rs : (l == j ? p * rs : a[j]);
+    bad |= (l == j) && !(p > 0.0f);
+    __syncthreads();
   }
 #pragma unroll
-  for (int k = 0; k < NB; k += 4) *(float4*)(row + k) = make_float4(x[k], x[k + 1], x[k + 2], x[k + 3]);
+  for (int k = 0; k < NB; ++k) R[l * LD + k] = a[k];
+  __syncthreads();
+  float x[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) x[i] = 0.0f;
+#pragma unroll
+  for (int i = NB - 1; i >= 0; --i) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = i + 1; k < NB; ++k) acc = fmaf(R[i * LD + k], x[k], acc);
+    const float rinv = 1.0f / R[i * LD + i];
+    x[i] = i == l ? rinv : (i < l ? -acc * rinv : 0.0f);
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) H[(s0 + i) * n + s0 + l] = x[i];
+  if (bad) atomicOr(flag, 1);
 }
 
 // Clears the strictly lower triangle (row k, columns j < k).
@@ -128,33 +117,11 @@ __global__ void zero_lower_kernel(float* __restrict__ H, int64_t n) {
   if (j < k) H[k * n + j] = 0.0f;
 }
 
-// In-place inverse of every 64 x 64 upper-triangular diagonal block (one block per
-// workgroup): column c of X = R^-1 by back substitution, X[c][c] = 1 / R[c][c],
-// X[i][c] = -(sum_{k=i+1..c} R[i][k] X[k][c]) / R[i][i] for i < c.
-__global__ __launch_bounds__(NB) void diag_inverse_kernel(float* __restrict__ H, int64_t n) {
-  __shared__ float R[NB * LD];
-  __shared__ float X[NB * LD];
-  const int64_t s0 = (int64_t)blockIdx.x * NB;
-  const int c = threadIdx.x;
-  for (int i = 0; i < NB; ++i) {
-    R[i * LD + c] = i <= c ? H[(s0 + i) * n + s0 + c] : 0.0f;
-    X[i * LD + c] = 0.0f;
-  }
-  __syncthreads();
-  X[c * LD + c] = 1.0f / R[c * LD + c];
-  for (int i = c - 1; i >= 0; --i) {
-    float acc = 0.0f;
-    for (int k = i + 1; k <= c; ++k) acc += R[i * LD + k] * X[k * LD + c];
-    X[i * LD + c] = -acc / R[i * LD + i];
-  }
-  for (int i = 0; i <= c; ++i) H[(s0 + i) * n + s0 + c] = X[i * LD + c];
-}
-
 }  // namespace
 
 // Copies HX into the workspace matrix F, damps it, factors it (H_d = R R^T) and
 // replaces R by U = R^-1 (upper triangle; the strictly lower triangle is zeroed).
-// T is scratch of n * NB floats.
+// T is scratch of n * n / 4 floats.
 kq_status damp_and_factor(const float* HX, float* F, float* T, uint8_t* dead, double* lam,
                           int* flag, int64_t n, float damp, hipStream_t s) {
   if (n % NB != 0) return fail(KQ_ESHAPE, "factorization needs n %% %d == 0", NB);
@@ -163,16 +130,21 @@ kq_status damp_and_factor(const float* HX, float* F, float* T, uint8_t* dead, do
   KQ_LAUNCHED("damp_stats_kernel");
   add_diag_kernel<<<dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s>>>(F, n, lam);
   KQ_LAUNCHED("add_diag_kernel");
+  // reverse Cholesky; diagonal blocks are left holding U_JJ = R_JJ^-1
   for (int64_t s0 = n - NB; s0 >= 0; s0 -= NB) {
-    diag_factor_kernel<<<1, 256, 0, s>>>(F, n, s0, NB, flag);
-    KQ_LAUNCHED("diag_factor_kernel");
+    diag_factor_inverse_kernel<<<1, NB, 0, s>>>(F, n, s0, flag);
+    KQ_LAUNCHED("diag_factor_inverse_kernel");
     if (s0 == 0) break;
-    panel_solve_kernel<<<dim3((unsigned)ceil_div(s0, 256)), dim3(256), 0, s>>>(F, n, s0);
-    KQ_LAUNCHED("panel_solve_kernel");
+    // R12 = A12 R22^-T = A12 U22^T  (in place; each row tile reads its 64 columns first)
+    GemmArgs p{};
+    p.M = s0; p.N = NB; p.K = NB;
+    p.A = F + s0; p.lda = n; p.B = F + s0 * n + s0; p.ldb = n; p.transB = true;
+    p.C = F + s0; p.ldc = n; p.alpha = 1.0f; p.split_k = 1;
+    KQ_TRY(gemm_f32(p, s));
+    // A11 -= R12 R12^T (upper tiles)
     GemmArgs g{};
     g.M = s0; g.N = s0; g.K = NB;
-    g.A = F + s0; g.lda = n; g.transA = false;
-    g.B = F + s0; g.ldb = n; g.transB = true;
+    g.A = F + s0; g.lda = n; g.B = F + s0; g.ldb = n; g.transB = true;
     g.C = F; g.ldc = n;
     g.alpha = -1.0f; g.accumulate = true; g.upper_only = true; g.split_k = 1;
     KQ_TRY(gemm_f32(g, s));
@@ -180,24 +152,52 @@ kq_status damp_and_factor(const float* HX, float* F, float* T, uint8_t* dead, do
   dim3 zgrid((unsigned)ceil_div(n, 256), (unsigned)n);
   zero_lower_kernel<<<zgrid, dim3(256), 0, s>>>(F, n);
   KQ_LAUNCHED("zero_lower_kernel");
-  // U = R^-1
-  diag_inverse_kernel<<<dim3((unsigned)(n / NB)), dim3(NB), 0, s>>>(F, n);
-  KQ_LAUNCHED("diag_inverse_kernel");
-  for (int64_t j0 = NB; j0 < n; j0 += NB) {
-    // T = U[<j0, <j0] R[<j0, J]   (U upper: row tile i only needs k >= its first row)
-    GemmArgs g{};
-    g.M = j0; g.N = NB; g.K = j0;
-    g.A = F; g.lda = n; g.B = F + j0; g.ldb = n;
-    g.C = T; g.ldc = NB; g.alpha = 1.0f; g.split_k = 1; g.a_upper = true;
-    KQ_TRY(gemm_f32(g, s));
-    // U[<j0, J] = -T U_JJ
-    GemmArgs h{};
-    h.M = j0; h.N = NB; h.K = NB;
-    h.A = T; h.lda = NB; h.B = F + j0 * n + j0; h.ldb = n;
-    h.C = F + j0; h.ldc = n; h.alpha = -1.0f; h.split_k = 1;
-    KQ_TRY(gemm_f32(h, s));
+  // U = R^-1 by recursive doubling over the diagonal blocks:
+  //   inv([[A, B], [0, D]]) = [[A^-1, -A^-1 B D^-1], [0, D^-1]]
+  // Neighbouring blocks are paired level by level; the pairs of one level with equal
+  // sizes form one batched product.
+  struct Blk { int64_t o, sz; };
+  int64_t nblk = n / NB;
+  Blk* blocks = new Blk[nblk];
+  Blk* next = new Blk[nblk];
+  for (int64_t b = 0; b < nblk; ++b) blocks[b] = Blk{b * NB, NB};
+  kq_status st = KQ_OK;
+  while (nblk > 1 && st == KQ_OK) {
+    int64_t nn = 0;
+    int64_t p = 0;
+    while (p + 1 < nblk && st == KQ_OK) {
+      // maximal run of consecutive pairs with the same sizes
+      const int64_t sa = blocks[p].sz, sd = blocks[p + 1].sz;
+      int64_t run = 1;
+      while (p + 2 * run + 1 < nblk && blocks[p + 2 * run].sz == sa && blocks[p + 2 * run + 1].sz == sd)
+        ++run;
+      const int64_t oa = blocks[p].o, od = blocks[p + 1].o;
+      const int64_t diag_stride = (sa + sd) * (n + 1);
+      GemmArgs t{};
+      t.M = sa; t.N = sd; t.K = sa;
+      t.A = F + oa * n + oa; t.lda = n; t.a_upper = true;
+      t.B = F + oa * n + od; t.ldb = n;
+      t.C = T; t.ldc = sd; t.alpha = 1.0f; t.split_k = 1;
+      t.batch = (int)run; t.strideA = diag_stride; t.strideB = diag_stride; t.strideC = sa * sd;
+      st = gemm_f32(t, s);
+      if (st != KQ_OK) break;
+      GemmArgs x{};
+      x.M = sa; x.N = sd; x.K = sd;
+      x.A = T; x.lda = sd;
+      x.B = F + od * n + od; x.ldb = n; x.b_upper = true;
+      x.C = F + oa * n + od; x.ldc = n; x.alpha = -1.0f; x.split_k = 1;
+      x.batch = (int)run; x.strideA = sa * sd; x.strideB = diag_stride; x.strideC = diag_stride;
+      st = gemm_f32(x, s);
+      for (int64_t r = 0; r < run; ++r) next[nn++] = Blk{blocks[p + 2 * r].o, sa + sd};
+      p += 2 * run;
+    }
+    if (p < nblk) next[nn++] = blocks[p];
+    Blk* tmp = blocks; blocks = next; next = tmp;
+    nblk = nn;
   }
-  return KQ_OK;
+  delete[] blocks;
+  delete[] next;
+  return st;
 }
 
 }  // namespace kq

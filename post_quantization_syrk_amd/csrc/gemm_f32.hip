@@ -23,8 +23,9 @@ struct Args {
   const float* B; int64_t ldb; int transB;
   float* C; int64_t ldc;
   float alpha;
-  int accumulate, upper_only, a_upper, split_k;
+  int accumulate, upper_only, a_upper, b_upper, split_k;
   int64_t k_per_split;
+  int64_t strideA, strideB, strideC;
   const float* D; int64_t ldd; double* red;
 };
 
@@ -110,10 +111,17 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(Args a) {
   const int64_t tm = blockIdx.x, tn = blockIdx.y;
   if (a.upper_only && tm > tn) return;
   const int64_t m0 = tm * MT, n0 = tn * NTL;
-  int64_t kbeg = (int64_t)blockIdx.z * a.k_per_split;
-  const int64_t kend = min(a.K, kbeg + a.k_per_split);
+  const int bz = blockIdx.z / a.split_k;           // batch index
+  const int sz = blockIdx.z % a.split_k;           // split index
+  a.A += bz * a.strideA;
+  a.B += bz * a.strideB;
+  a.C += bz * a.strideC;
+  int64_t kbeg = (int64_t)sz * a.k_per_split;
+  int64_t kend = min(a.K, kbeg + a.k_per_split);
   // upper-triangular A: rows >= m0 are zero for k < m0
   if (a.a_upper && kbeg < m0) kbeg = min(kend, (m0 / BK) * BK);
+  // upper-triangular B: columns < n0 + NTL are zero for k >= n0 + NTL
+  if (a.b_upper) kend = max(kbeg, min(kend, n0 + NTL));
   if (kbeg >= kend && a.split_k > 1) return;
 
   __shared__ __attribute__((aligned(16))) float As[2][BK * LDA_S];
@@ -219,13 +227,16 @@ kq_status gemm_f32(const GemmArgs& g, hipStream_t s) {
   a.B = g.B; a.ldb = g.ldb; a.transB = g.transB;
   a.C = g.C; a.ldc = g.ldc; a.alpha = g.alpha;
   a.accumulate = g.accumulate; a.upper_only = g.upper_only; a.a_upper = g.a_upper;
-  a.split_k = g.split_k;
+  a.b_upper = g.b_upper; a.split_k = g.split_k;
+  a.strideA = g.strideA; a.strideB = g.strideB; a.strideC = g.strideC;
+  const int batch = g.batch > 0 ? g.batch : 1;
+  if (batch > 1 && g.red) return fail(KQ_EINVAL, "gemm_f32: batched reduction not supported");
   a.D = g.D; a.ldd = g.ldd; a.red = g.red;
   a.k_per_split = ceil_div(ceil_div(g.K > 0 ? g.K : 1, g.split_k), BK) * BK;
   const int splits = g.K > 0 ? (int)ceil_div(g.K, a.k_per_split) : 1;
   // one split left: a plain read-add-write gives the same C += alpha AB
   a.split_k = splits;
-  dim3 grid((unsigned)ceil_div(g.M, MT), (unsigned)ceil_div(g.N, NTL), (unsigned)splits);
+  dim3 grid((unsigned)ceil_div(g.M, MT), (unsigned)ceil_div(g.N, NTL), (unsigned)(splits * batch));
   gemm_f32_kernel<<<grid, dim3(THREADS), 0, s>>>(a);
   KQ_LAUNCHED("gemm_f32_kernel");
   return KQ_OK;

@@ -301,7 +301,7 @@ Layout layout(int64_t out, int64_t in, int B, bool with_loss) {
   Layout L;
   size_t o = 0;
   L.f = o;    o = align256(o + (size_t)in * in * sizeof(float));
-  L.t = o;    o = align256(o + (size_t)in * 64 * sizeof(float));
+  L.t = o;    o = align256(o + ((size_t)in * in / 4 + (size_t)in * 64) * sizeof(float));
   L.y = o;    o = align256(o + (size_t)out * B * sizeof(float));
   L.dead = o; o = align256(o + (size_t)in);
   L.scal = o; o = align256(o + 8 * sizeof(double));

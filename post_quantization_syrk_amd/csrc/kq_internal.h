@@ -39,7 +39,10 @@ struct GemmArgs {
   bool accumulate;    // C += alpha*AB (else C = alpha*AB)
   bool upper_only;    // only tiles with row-tile <= col-tile
   bool a_upper;       // op(A) is upper triangular (zeros below): skip K below the tile's rows
+  bool b_upper;       // op(B) is upper triangular: skip K beyond the tile's columns
   int split_k;        // >= 1; > 1 requires accumulate (atomics)
+  int batch;          // >= 1 independent products, operands offset by the strides below
+  int64_t strideA, strideB, strideC;  // in elements
   // reduce epilogue: instead of writing C, accumulate sum(alpha*AB .* D) into *red (fp64)
   const float* D; int64_t ldd; double* red;
 };
