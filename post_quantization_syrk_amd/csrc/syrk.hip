@@ -6,23 +6,30 @@
 // E[x x^T] and E[g g^T]).  Both are the same operation on different streams.
 //
 // Kernel design (gfx950, CDNA4):
-//   * 256 x 256 output tiles over the lower block triangle, 512 threads
-//     (8 waves of 64); each wave owns a 128 x 64 sub-tile = 4 x 2 blocks of
-//     v_mfma_f32_32x32x16_bf16 (fp32 accumulators, bf16 products are exact).
+//   * 256 x 256 output tiles over the lower block triangle, 256 threads
+//     (4 waves of 64); each wave owns a 128 x 128 sub-tile = 4 x 4 blocks of
+//     v_mfma_f32_32x32x16_bf16 (fp32 accumulators, bf16 products are exact),
+//     which keeps LDS operand traffic at 8 KB per 16 MFMAs.
 //   * The token axis is the reduction axis and is the slow axis of the
-//     stream, so every 64-token stage is loaded as 8 tokens x 4 channels per
+//     stream, so every 64-token stage is loaded as 16 tokens x 4 channels per
 //     thread (coalesced 512-byte rows per wave), transposed in registers to
-//     channel-major order and stored to LDS with a padded stride, where each
-//     MFMA operand is one 16-byte read of 8 consecutive tokens.
+//     channel-major order and stored to LDS, where each MFMA operand is one
+//     16-byte read of 8 consecutive tokens.  A channel's 64 tokens fill one
+//     128-byte LDS row whose eight 16-byte chunks are permuted by
+//     chunk ^ ((c ^ (c >> 3)) & 7): both the transposed stores (lanes 4
+//     channels apart) and the operand reads (lanes 1 channel apart) then hit
+//     distinct banks.
 //   * Two LDS buffers: the next stage's global loads are in flight while the
 //     current stage runs on the matrix cores.
-//   * The token range is split S ways (S a multiple of 8).  Workgroups are
-//     numbered so that the split index equals blockIdx % 8 when S == 8:
-//     hardware dispatch places blockIdx round-robin on the 8 XCDs, so each
-//     XCD streams one token range and its L2 serves the row and column
-//     panels of all tiles it runs.  Tiles are visited in bands of 4 tile
-//     rows so consecutive tiles share panels.  Partial tiles are added to H
-//     with fp32 atomics (H is zeroed first unless accumulating).
+//   * The token range is split S ways (S a multiple of 8, about 2048
+//     workgroups in all).  Workgroups are numbered split-major: the ones
+//     dispatched together work on the same token range, so the streamed
+//     tokens are shared through the L2s and the last-level cache.  Tiles are
+//     visited in bands of 4 tile rows so neighbouring tiles share panels.
+//     Partial tiles are added to H with fp32 atomics (H is zeroed first
+//     unless accumulating).  Measured on the 4096-wide, 131072-token factor:
+//     8 waves per workgroup (2 per SIMD) beat 4 waves (1 per SIMD), and
+//     split-major beat tile-major order.
 //   * A final pass mirrors the lower triangle into the upper one.
 #include "kq_internal.h"
 
@@ -36,9 +43,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int TILE = 256;          // output tile edge (channels)
 constexpr int BK = 64;             // tokens per stage
-constexpr int LDK = BK + 8;        // LDS stride of one channel column (bf16 elements)
-constexpr int NTHR = 512;          // threads per workgroup
-constexpr int PANEL = TILE * LDK;  // bf16 elements of one panel in LDS
+constexpr int PANEL = TILE * BK;   // bf16 elements of one panel in LDS (no padding)
 constexpr int BAND = 4;            // tile rows per band in the visiting order
 
 struct SyrkArgs {
@@ -81,6 +86,11 @@ __device__ __forceinline__ void tile_of(int t, int nb, int& bi, int& bj) {
   }
 }
 
+// LDS offset (bf16 elements) of the 8-token chunk kc of channel c.
+__device__ __forceinline__ int lds_off(int c, int kc) {
+  return c * BK + ((kc ^ ((c ^ (c >> 3)) & 7)) << 3);
+}
+
 // 8 tokens x 4 channels of bf16 for one thread: r[i] holds token i, channels c..c+3.
 __device__ __forceinline__ void load_block(const uint16_t* __restrict__ A, int64_t lda, int64_t t,
                                            int64_t tend, int c, int n, bool full, uint2 (&r)[8]) {
@@ -109,8 +119,10 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ A, int64
   }
 }
 
-// Store the 8x4 block transposed: channel (cl + k) gets tokens tl .. tl+7 as one 16-byte word.
-__device__ __forceinline__ void store_block(uint16_t* __restrict__ panel, int cl, int tl,
+// Store the 8x4 block transposed: channel cl + k gets tokens 8*kc .. 8*kc+7 as one 16-byte
+// chunk.  Lanes of odd cl/4 write their channels in the order 1, 0, 3, 2, so the channels
+// written by one instruction alternate in parity across lanes (distinct banks).
+__device__ __forceinline__ void store_block(uint16_t* __restrict__ panel, int cl, int kc,
                                             const uint2 (&r)[8]) {
   uint4 v0, v1, v2, v3;
   // low / high halves of each 32-bit word are channels c and c+1 (x) or c+2 and c+3 (y)
@@ -130,18 +142,28 @@ __device__ __forceinline__ void store_block(uint16_t* __restrict__ panel, int cl
   v3.y = (r[2].y >> 16) | (r[3].y & 0xFFFF0000u);
   v3.z = (r[4].y >> 16) | (r[5].y & 0xFFFF0000u);
   v3.w = (r[6].y >> 16) | (r[7].y & 0xFFFF0000u);
-  *(uint4*)(panel + (cl + 0) * LDK + tl) = v0;
-  *(uint4*)(panel + (cl + 1) * LDK + tl) = v1;
-  *(uint4*)(panel + (cl + 2) * LDK + tl) = v2;
-  *(uint4*)(panel + (cl + 3) * LDK + tl) = v3;
+  const int o = (cl >> 2) & 1;
+  const uint4 w0 = o ? v1 : v0, w1 = o ? v0 : v1, w2 = o ? v3 : v2, w3 = o ? v2 : v3;
+  *(uint4*)(panel + lds_off(cl + (0 ^ o), kc)) = w0;
+  *(uint4*)(panel + lds_off(cl + (1 ^ o), kc)) = w1;
+  *(uint4*)(panel + lds_off(cl + (2 ^ o), kc)) = w2;
+  *(uint4*)(panel + lds_off(cl + (3 ^ o), kc)) = w3;
 }
 
-__global__ __launch_bounds__(NTHR) void syrk_bf16_kernel(SyrkArgs a) {
+// WAVES = 4: 128 x 128 per wave (1 wave per SIMD); WAVES = 8: 128 x 64 per wave (2 per SIMD).
+// SPLIT_MAJOR: consecutive workgroups share a token range (all tiles of one split run
+// together, so the concurrently streamed tokens stay in the last-level cache);
+// otherwise consecutive workgroups share a tile (split = blockIdx % S, one range per XCD).
+template <int WAVES, bool SPLIT_MAJOR>
+__global__ __launch_bounds__(WAVES * 64) void syrk_bf16_kernel(SyrkArgs a) {
+  constexpr int THREADS = WAVES * 64;
+  constexpr int TPT = 64 / (THREADS / 64);   // tokens per thread per stage (16 or 8)
+  constexpr int WN = WAVES == 4 ? 4 : 2;     // 32-wide column blocks per wave
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * PANEL];
 
   const int u = blockIdx.x;
-  const int split = u % a.splits;
-  const int tile = u / a.splits;
+  const int split = SPLIT_MAJOR ? u / a.ntiles : u % a.splits;
+  const int tile = SPLIT_MAJOR ? u % a.ntiles : u / a.splits;
   int bi, bj;
   tile_of(tile, a.nb, bi, bj);
   const bool diag = (bi == bj);
@@ -154,37 +176,50 @@ __global__ __launch_bounds__(NTHR) void syrk_bf16_kernel(SyrkArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  // loader mapping: tokens 8*tg .. 8*tg+7, channels 4*cg .. 4*cg+3 of the panel
-  const int tg = tid >> 6;       // 0..7
-  const int cg = tid & 63;       // 0..63
+  // loader mapping: TPT tokens (TPT/8 chunks) starting at TPT*tg, channels 4*cg .. 4*cg+3
+  const int tg = tid >> 6;
+  const int cg = tid & 63;
   const int ci = bi * TILE + 4 * cg;
   const int cj = bj * TILE + 4 * cg;
   const bool full_i = (bi + 1) * TILE <= a.n;
   const bool full_j = (bj + 1) * TILE <= a.n;
 
-  // compute mapping: wave tile rows [128*wr, +128) of panel i, cols [64*wc, +64) of panel j
-  const int wr = wave >> 2;
-  const int wc = wave & 3;
+  // compute mapping: wave tile rows [128*wr, +128) of panel i, cols [32*WN*wc, +32*WN) of panel j
+  const int wr = WAVES == 4 ? (wave >> 1) : (wave >> 2);
+  const int wc = WAVES == 4 ? (wave & 1) : (wave & 3);
   const int l32 = lane & 31;
-  const int khalf = (lane >> 5) * 8;
+  const int kh = lane >> 5;
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][WN];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int k = 0; k < 2; ++k) acc[m][k] = f32x16{};
+    for (int k = 0; k < WN; ++k) acc[m][k] = f32x16{};
 
-  uint2 ri[8], rj[8];
+  uint2 ri0[8], ri1[8], rj0[8], rj1[8];
 
-  // prologue: stage 0 into buffer 0
-  {
-    const int64_t t0 = tbeg + 8 * tg;
-    const bool tf = tbeg + BK <= tend;
-    load_block(a.A, a.lda, t0, tend, ci, a.n, tf && full_i, ri);
-    if (!diag) load_block(a.A, a.lda, t0, tend, cj, a.n, tf && full_j, rj);
-    store_block(lds, 4 * cg, 8 * tg, ri);
-    if (!diag) store_block(lds + PANEL, 4 * cg, 8 * tg, rj);
+#define KQ_SYRK_LOAD(T0)                                                                   \
+  {                                                                                        \
+    const bool tf = (T0) + BK <= tend;                                                     \
+    load_block(a.A, a.lda, (T0) + TPT * tg, tend, ci, a.n, tf && full_i, ri0);             \
+    if (TPT == 16) load_block(a.A, a.lda, (T0) + TPT * tg + 8, tend, ci, a.n, tf && full_i, ri1); \
+    if (!diag) {                                                                           \
+      load_block(a.A, a.lda, (T0) + TPT * tg, tend, cj, a.n, tf && full_j, rj0);           \
+      if (TPT == 16) load_block(a.A, a.lda, (T0) + TPT * tg + 8, tend, cj, a.n, tf && full_j, rj1); \
+    }                                                                                      \
   }
+#define KQ_SYRK_STORE(Q)                                                                   \
+  {                                                                                        \
+    store_block((Q), 4 * cg, (TPT / 8) * tg, ri0);                                         \
+    if (TPT == 16) store_block((Q), 4 * cg, 2 * tg + 1, ri1);                              \
+    if (!diag) {                                                                           \
+      store_block((Q) + PANEL, 4 * cg, (TPT / 8) * tg, rj0);                               \
+      if (TPT == 16) store_block((Q) + PANEL, 4 * cg, 2 * tg + 1, rj1);                    \
+    }                                                                                      \
+  }
+
+  KQ_SYRK_LOAD(tbeg)
+  KQ_SYRK_STORE(lds)
   __syncthreads();
 
   for (int s = 0; s < nstages; ++s) {
@@ -192,42 +227,36 @@ __global__ __launch_bounds__(NTHR) void syrk_bf16_kernel(SyrkArgs a) {
     const uint16_t* pi = lds + buf * 2 * PANEL;
     const uint16_t* pj = diag ? pi : pi + PANEL;
     const bool more = s + 1 < nstages;
-    if (more) {
-      const int64_t tn = tbeg + (int64_t)(s + 1) * BK;
-      const bool tf = tn + BK <= tend;
-      load_block(a.A, a.lda, tn + 8 * tg, tend, ci, a.n, tf && full_i, ri);
-      if (!diag) load_block(a.A, a.lda, tn + 8 * tg, tend, cj, a.n, tf && full_j, rj);
-    }
+    if (more) KQ_SYRK_LOAD(tbeg + (int64_t)(s + 1) * BK)
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 av[4], bv[2];
+      const int kc = 2 * ks + kh;
+      bf16x8 av[4], bv[WN];
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        av[m] = *(const bf16x8*)(pi + (128 * wr + 32 * m + l32) * LDK + 16 * ks + khalf);
+        av[m] = *(const bf16x8*)(pi + lds_off(128 * wr + 32 * m + l32, kc));
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
-        bv[k] = *(const bf16x8*)(pj + (64 * wc + 32 * k + l32) * LDK + 16 * ks + khalf);
+      for (int k = 0; k < WN; ++k)
+        bv[k] = *(const bf16x8*)(pj + lds_off(32 * WN * wc + 32 * k + l32, kc));
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int k = 0; k < 2; ++k)
+        for (int k = 0; k < WN; ++k)
           acc[m][k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[m], bv[k], acc[m][k], 0, 0, 0);
     }
-    if (more) {
-      uint16_t* qi = lds + (buf ^ 1) * 2 * PANEL;
-      store_block(qi, 4 * cg, 8 * tg, ri);
-      if (!diag) store_block(qi + PANEL, 4 * cg, 8 * tg, rj);
-    }
+    if (more) KQ_SYRK_STORE(lds + (buf ^ 1) * 2 * PANEL)
     __syncthreads();
   }
+#undef KQ_SYRK_LOAD
+#undef KQ_SYRK_STORE
 
   // epilogue: lane holds column l32 of each 32x32 block; rows 8*(r/4) + 4*(lane/32) + r%4
-  const int rh = (lane >> 5) * 4;
+  const int rh = kh * 4;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int gj = bj * TILE + 64 * wc + 32 * k + l32;
+    for (int k = 0; k < WN; ++k) {
+      const int gj = bj * TILE + 32 * WN * wc + 32 * k + l32;
       if (gj >= a.n) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -267,16 +296,26 @@ __global__ __launch_bounds__(256) void mirror_lower_to_upper(float* __restrict__
   }
 }
 
+// Kernel variant: bit 0 = 8 waves (else 4), bit 1 = split-major order.  KQ_SYRK_VARIANT
+// overrides the default (a tuning knob; every variant computes the same H).
+int syrk_variant() {
+  const char* env = getenv("KQ_SYRK_VARIANT");
+  if (env) {
+    const int v = atoi(env);
+    if (v >= 0 && v <= 3) return v;
+  }
+  return 3;
+}
+
 int choose_splits(int ntiles, int64_t T) {
   const char* env = getenv("KQ_SYRK_SPLITS");
   if (env) {
     int v = atoi(env);
     if (v >= 1) return v;
   }
-  const int cus = device_cu_count();
-  // at least two workgroups per CU overall, a multiple of 8 (one token range per XCD)
+  // at least ~2048 workgroups (8 per CU) for load balance, a multiple of 8, at least 8
   int s = 8;
-  while ((int64_t)ntiles * s < 2 * (int64_t)cus) s += 8;
+  while ((int64_t)ntiles * s < 2048 && s < 64) s += 8;
   // keep at least 8 stages per split
   int64_t max_s = T / (8 * BK);
   if (max_s < 1) max_s = 1;
@@ -320,7 +359,15 @@ extern "C" kq_status kq_accumulate_hessian(const uint16_t* A_bf16, int64_t T, in
     a.splits = (int)ceil_div(T, a.tok_split);
     const int64_t grid = (int64_t)a.ntiles * a.splits;
     if (grid > 0x7FFFFFFF) return fail(KQ_ESHAPE, "kq_accumulate_hessian: too many tiles");
-    syrk_bf16_kernel<<<dim3((unsigned)grid), dim3(NTHR), 0, s>>>(a);
+    const int variant = syrk_variant();
+    const bool split_major = (variant & 2) != 0;
+    if (variant & 1) {
+      if (split_major) syrk_bf16_kernel<8, true><<<dim3((unsigned)grid), dim3(512), 0, s>>>(a);
+      else syrk_bf16_kernel<8, false><<<dim3((unsigned)grid), dim3(512), 0, s>>>(a);
+    } else {
+      if (split_major) syrk_bf16_kernel<4, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
+      else syrk_bf16_kernel<4, false><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
+    }
     KQ_LAUNCHED("syrk_bf16_kernel");
   }
   const int m = (int)ceil_div(n, 64);
