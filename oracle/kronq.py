@@ -151,7 +151,8 @@ def rotate_cols(M: np.ndarray, signs: np.ndarray, block: int = 0) -> np.ndarray:
 # Bidirectional incoherence processing (BiIP)
 # ---------------------------------------------------------------------------
 def rescale_vectors(W: np.ndarray, HX: np.ndarray, HG: np.ndarray | None, alpha: float,
-                    mode: int = BIIP_FULL) -> tuple[np.ndarray, np.ndarray]:
+                    mode: int = BIIP_FULL, hg_diag: np.ndarray | None = None
+                    ) -> tuple[np.ndarray, np.ndarray]:
     """Diagonal rescale factors of BiIP, input side d_in and output side d_out.
 
     [KronQ-README] opening section: BiIP applies "rotation + rescaling on both
@@ -162,7 +163,8 @@ def rescale_vectors(W: np.ndarray, HX: np.ndarray, HG: np.ndarray | None, alpha:
     (alpha = 1/4 is the diagonal rescale that minimizes tr(D^-1 H D^-1) *
     ||W D||_F^2 on each side; a zero norm or diagonal gives d = 1).
     Parity unpinned for the rule itself: only the loss invariance and the
-    proxy-bound optimality constrain it.
+    proxy-bound optimality constrain it.  Only diag(H_G) enters d_out, so it can
+    be given directly as hg_diag (for output sizes whose full H_G is too large).
     """
     W = np.asarray(W, np.float64)
     out_n, in_n = W.shape
@@ -174,7 +176,7 @@ def rescale_vectors(W: np.ndarray, HX: np.ndarray, HG: np.ndarray | None, alpha:
         d_in[ok] = (h[ok] / c[ok]) ** alpha
     if mode in (BIIP_FULL, BIIP_OUT_ONLY):
         r = np.sum(W * W, axis=1)
-        h = np.diag(np.asarray(HG, np.float64))
+        h = np.asarray(hg_diag, np.float64) if hg_diag is not None else np.diag(np.asarray(HG, np.float64))
         ok = (r > 0) & (h > 0)
         d_out[ok] = (h[ok] / r[ok]) ** alpha
     return d_in, d_out
@@ -182,7 +184,7 @@ def rescale_vectors(W: np.ndarray, HX: np.ndarray, HG: np.ndarray | None, alpha:
 
 def biip(W: np.ndarray, HX: np.ndarray, HG: np.ndarray | None, sign_in: np.ndarray,
          sign_out: np.ndarray | None, alpha: float = 0.25, mode: int = BIIP_FULL,
-         had_in: int = 0, had_out: int = 0):
+         had_in: int = 0, had_out: int = 0, hg_diag: np.ndarray | None = None):
     """Bidirectional incoherence processing of one linear layer.
 
     [KronQ-abstract] point (1) and [KronQ-README] opening section: the
@@ -197,7 +199,8 @@ def biip(W: np.ndarray, HX: np.ndarray, HG: np.ndarray | None, sign_in: np.ndarr
     so tr(H_G dW H_X dW^T) is unchanged for any dW mapped like W.
     mode: FULL (both sides, rescale + rotate), NO_RESCALE (both sides, rotate
     only), IN_ONLY / OUT_ONLY (one side, rescale + rotate).
-    Returns (W~, H~_X, H~_G, d_in, d_out); H~_G is None when HG is None.
+    Returns (W~, H~_X, H~_G, d_in, d_out); H~_G is None when HG is None (then
+    hg_diag, if given, supplies diag(H_G) for the output rescale).
     """
     W = np.asarray(W, np.float64)
     HX = np.asarray(HX, np.float64)
@@ -205,7 +208,7 @@ def biip(W: np.ndarray, HX: np.ndarray, HG: np.ndarray | None, sign_in: np.ndarr
     if mode == BIIP_NO_RESCALE:
         d_in, d_out = np.ones(W.shape[1]), np.ones(W.shape[0])
     else:
-        d_in, d_out = rescale_vectors(W, HX, HG, alpha, mode)
+        d_in, d_out = rescale_vectors(W, HX, HG, alpha, mode, hg_diag)
     Wt = W * d_out[:, None] * d_in[None, :]
     HXt = HX / np.outer(d_in, d_in)
     HGt = None if HG is None else HG / np.outer(d_out, d_out)

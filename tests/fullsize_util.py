@@ -1,0 +1,107 @@
+"""Full-size parity helpers: run the engine exactly as the benchmark does, and
+compute the oracle's quantities at full size (chunked) or on samples."""
+import time
+
+import numpy as np
+
+import oracle as o
+import synthetic as syn
+from tests.gpu_util import announce, torch_cuda
+
+
+def oracle_hessian(bits: np.ndarray, chunk: int = 8192) -> np.ndarray:
+    """fp64 A^T A accumulated over token chunks (same sums as the oracle's hessian_factor)."""
+    n = bits.shape[1]
+    H = np.zeros((n, n))
+    for t in range(0, bits.shape[0], chunk):
+        H += o.hessian_factor(o.bf16_bits_to_f64(bits[t:t + chunk]))
+    return H
+
+
+def oracle_diag(bits: np.ndarray, chunk: int = 8192) -> np.ndarray:
+    """fp64 diagonal of A^T A (column sums of squares of the stream).
+
+    A bf16 value has 8 significant bits, so its square is exact in fp32; the
+    squares are summed in fp64, chunks in parallel threads."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    def part(t):
+        a = (bits[t:t + chunk].astype(np.uint32) << np.uint32(16)).view(np.float32)
+        return np.sum(a * a, axis=0, dtype=np.float64)
+
+    with ThreadPoolExecutor(16) as ex:
+        parts = list(ex.map(part, range(0, bits.shape[0], chunk)))
+    return np.sum(parts, axis=0)
+
+
+def run_engine(cfg, bx, bg, W, s_in, s_out, want_loss=True, keep_raw=True, hg_host=True,
+               hg_samples=None):
+    """kq_accumulate_hessian x2, kq_sensitivity, kq_biip_rotate, kq_quantize_layer, as bench.py."""
+    torch = torch_cuda()
+    import post_quantization_syrk_amd as kq
+    dev = "cuda"
+    t0 = time.time()
+    X = torch.from_numpy(bx.view(np.int16)).to(dev).view(torch.bfloat16)
+    HX = torch.empty((cfg.inp, cfg.inp), device=dev)
+    kq.kq_accumulate_hessian(X, HX)
+    del X
+    G = torch.from_numpy(bg.view(np.int16)).to(dev).view(torch.bfloat16)
+    HG = torch.empty((cfg.out, cfg.out), device=dev)
+    kq.kq_accumulate_hessian(G, HG)
+    del G
+    out = {"sens": kq.kq_sensitivity(HX, HG)}
+    if keep_raw:
+        out["HX"] = HX.cpu().numpy()
+        out["HG"] = HG.cpu().numpy() if hg_host else None
+    out["HG_diag"] = torch.diagonal(HG).cpu().numpy()
+    if hg_samples is not None:
+        ii, jj = (torch.from_numpy(np.asarray(v)).to(dev) for v in hg_samples)
+        out["HG_samples"] = HG[ii, jj].cpu().numpy()
+    Wd = torch.from_numpy(W).to(dev)
+    Wt = torch.empty_like(Wd)
+    di, do = torch.empty(cfg.inp, device=dev), torch.empty(cfg.out, device=dev)
+    kq.kq_biip_rotate(Wd, Wt, HX, HX, HG, HG, torch.from_numpy(s_in).to(dev),
+                      torch.from_numpy(s_out).to(dev), di, do, cfg.alpha, kq.KQ_BIIP_FULL,
+                      cfg.had_in, cfg.had_out)
+    out["Wt"] = Wt.cpu().numpy()
+    out["HXt"] = HX.cpu().numpy()
+    out["HGt_trace"] = float(torch.diagonal(HG).double().sum().item())
+    out["HGt"] = HG.cpu().numpy() if hg_host else None
+    out["d_in"], out["d_out"] = di.cpu().numpy(), do.cpu().numpy()
+    p = kq.make_params(cfg.bits, cfg.group, cfg.block, cfg.damp)
+    ws = torch.empty(kq.kq_quantize_layer_workspace(p, cfg.out, cfg.inp, want_loss), dtype=torch.uint8,
+                     device=dev)
+    packed = torch.zeros((cfg.out, cfg.inp * cfg.bits // 32), dtype=torch.int32, device=dev)
+    scales = torch.zeros((cfg.out, cfg.inp // cfg.group), device=dev)
+    zeros = torch.zeros((cfg.out, cfg.inp // cfg.group), dtype=torch.uint8, device=dev)
+    codes = torch.zeros((cfg.out, cfg.inp), dtype=torch.uint8, device=dev)
+    out["loss"] = kq.kq_quantize_layer(p, Wt, HX, HG, packed, scales, zeros, ws, codes=codes,
+                                       want_loss=want_loss)
+    torch.cuda.synchronize()
+    out.update(E=Wt.cpu().numpy(), packed=packed.cpu().numpy().view(np.uint32),
+               scales=scales.cpu().numpy(), zeros=zeros.cpu().numpy(),
+               codes=codes.cpu().numpy().astype(np.int64))
+    announce(f"{cfg.name}: engine done in {time.time() - t0:.1f} s")
+    return out
+
+
+def dequant(codes, scales, zeros, group):
+    s = np.repeat(scales.astype(np.float64), group, axis=1)
+    z = np.repeat(zeros.astype(np.float64), group, axis=1)
+    return s * (codes - z)
+
+
+def check_rows(g, Wt_ref, HXt_ref, cfg, rows, factor):
+    """Sampled-row GPTQ parity (replay rule) and packed/scale/zero/error checks."""
+    ref = o.quantize_layer(Wt_ref, HXt_ref, None, cfg.bits, cfg.group, cfg.damp,
+                           replay_codes=g["codes"][rows], rows=rows, factor=factor)
+    res = ref["gptq"]
+    assert res.hard_mismatches == 0, f"{res.hard_mismatches} hard mismatches, first {res.mismatch_positions[:5]}"
+    assert res.accepted_ties <= 0.001 * res.codes.size
+    assert np.array_equal(res.codes, g["codes"][rows])
+    assert np.max(np.abs(g["scales"][rows] - res.scales) / np.abs(res.scales)) <= 1e-5
+    assert np.array_equal(g["zeros"][rows].astype(np.int64), res.zeros.astype(np.int64))
+    assert np.array_equal(g["packed"][rows], o.pack_codes(g["codes"][rows], cfg.bits))
+    e = g["E"][rows].astype(np.float64)
+    assert np.linalg.norm(e - res.E) <= 1e-4 * np.linalg.norm(res.E)
+    return res

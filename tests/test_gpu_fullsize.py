@@ -1,0 +1,113 @@
+"""GPU parity at the workloads' full sizes, in the benchmark's launch configuration.
+
+For each layer workload the engine runs exactly as bench.py runs it (same entry
+points, same defaults).  The oracle computes at full size what fits (fp64
+factors chunked over tokens, rotations, the damped factor) and on samples what
+does not (GPTQ on a seeded row sample, rows being independent given U; sampled
+entries of the 28672-wide H_G).  Losses are checked for consistency with the
+engine's own codes and errors (direct loss of the dequantized codes against the
+oracle's processed factors; predicted loss sum_j e_j^T H~_G e_j).
+Tolerances as in the small-size tests: factors 1e-3 relative Frobenius (the
+fp32 accumulation gives ~1e-7), rotated quantities 1e-5, codes by the replay
+rule, losses 1e-3."""
+import time
+
+import numpy as np
+import pytest
+
+import oracle as o
+import synthetic as syn
+from tests.fullsize_util import check_rows, dequant, oracle_diag, oracle_hessian, run_engine
+from tests.gpu_util import announce, rel_fro, torch_cuda
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+N_ROWS = 48
+
+
+def _layer_inputs(cfg):
+    t0 = time.time()
+    bx, bg = syn.stream(cfg, "x"), syn.stream(cfg, "g")
+    W = syn.weights(cfg)
+    announce(f"{cfg.name}: inputs generated in {time.time() - t0:.1f} s")
+    return bx, bg, W, syn.signs(cfg, "in"), syn.signs(cfg, "out")
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_layer_full_pipeline(name):
+    """Llama-2-7B q_proj (W4) and down_proj (W2, 43 x 256 input Hadamard) at full size."""
+    torch_cuda()
+    cfg = {"c2": syn.C2, "c3": syn.C3}[name]
+    bx, bg, W, s_in, s_out = _layer_inputs(cfg)
+    g = run_engine(cfg, bx, bg, W, s_in, s_out, want_loss=True)
+    t0 = time.time()
+    HX = oracle_hessian(bx)
+    HG = oracle_hessian(bg)
+    del bx, bg
+    announce(f"{name}: oracle factors in {time.time() - t0:.1f} s")
+    ex, eg = rel_fro(g["HX"], HX), rel_fro(g["HG"], HG)
+    announce(f"{name}: H_X rel {ex:.2e}, H_G rel {eg:.2e}")
+    assert ex <= 1e-3 and eg <= 1e-3
+    assert np.array_equal(g["HX"], g["HX"].T)
+    tx, tg, sv = o.sensitivity(HX, HG)
+    assert g["sens"][2] == pytest.approx(sv, rel=1e-5)
+    Wt, HXt, HGt, d_in, d_out = o.biip(W.astype(np.float64), HX, HG, s_in, s_out, cfg.alpha,
+                                       o.BIIP_FULL, cfg.had_in, cfg.had_out)
+    assert rel_fro(g["d_in"], d_in) <= 1e-5 and rel_fro(g["d_out"], d_out) <= 1e-5
+    ew, ehx, ehg = rel_fro(g["Wt"], Wt), rel_fro(g["HXt"], HXt), rel_fro(g["HGt"], HGt)
+    announce(f"{name}: W~ rel {ew:.2e}, H~_X rel {ehx:.2e}, H~_G rel {ehg:.2e}")
+    assert ew <= 1e-5 and ehx <= 1e-5 and ehg <= 1e-5
+    t0 = time.time()
+    fac = o.damp_and_factor(HXt, cfg.damp)
+    rows = np.sort(np.random.default_rng(cfg.cfg_index).choice(cfg.out, N_ROWS, replace=False))
+    res = check_rows(g, Wt, HXt, cfg, rows, fac)
+    announce(f"{name}: {N_ROWS} sampled rows match ({res.accepted_ties} near-tie codes adopted) "
+             f"in {time.time() - t0:.1f} s")
+    # losses of the engine's own codes / errors against the oracle's processed factors
+    dW = Wt - dequant(g["codes"], g["scales"], g["zeros"], cfg.group)
+    L_direct = o.proxy_loss(dW, HXt, HGt)
+    L_pred = o.predicted_loss(g["E"], HGt)
+    assert g["loss"][0] == pytest.approx(L_direct, rel=1e-3)
+    assert g["loss"][1] == pytest.approx(L_pred, rel=1e-3)
+    # predicted (damped) loss exceeds the direct one by lam * tr(H_G dW dW^T) > 0
+    assert g["loss"][1] > g["loss"][0]
+
+
+def test_c5_llama3_70b_up_proj():
+    """28672 x 8192, 262144 tokens: 3.29 GB H_G built on one GPU, 7 x 4096 output Hadamard."""
+    torch = torch_cuda()
+    cfg = syn.C5
+    bx, bg, W, s_in, s_out = _layer_inputs(cfg)
+    rng = np.random.default_rng(55)
+    i = rng.integers(0, cfg.out, 32)
+    j = rng.integers(0, cfg.out, 32)
+    g = run_engine(cfg, bx, bg, W, s_in, s_out, want_loss=False, hg_host=False, hg_samples=(i, j))
+    t0 = time.time()
+    HX = oracle_hessian(bx)
+    hg_diag = oracle_diag(bg)
+    announce(f"c5: oracle H_X and diag(H_G) in {time.time() - t0:.1f} s")
+    assert rel_fro(g["HX"], HX) <= 1e-5
+    assert rel_fro(g["HG_diag"], hg_diag) <= 1e-5
+    # sampled entries of the 28672-wide H_G, one by one from the stream
+    del bx
+    Gi = o.bf16_bits_to_f64(bg[:, i])
+    Gj = o.bf16_bits_to_f64(bg[:, j])
+    ref = o.hessian_factor_entry(Gi, Gj)
+    scale = np.sqrt(hg_diag[i] * hg_diag[j])
+    assert np.max(np.abs(g["HG_samples"] - ref) / scale) <= 1e-5
+    del bg, Gi, Gj
+    tx = o.trace(HX)
+    assert g["sens"][0] == pytest.approx(tx, rel=1e-6)
+    assert g["sens"][1] == pytest.approx(float(np.sum(hg_diag)), rel=1e-6)
+    Wt, HXt, _, d_in, d_out = o.biip(W.astype(np.float64), HX, None, s_in, s_out, cfg.alpha,
+                                     o.BIIP_FULL, cfg.had_in, cfg.had_out, hg_diag=hg_diag)
+    assert rel_fro(g["d_in"], d_in) <= 1e-5 and rel_fro(g["d_out"], d_out) <= 1e-5
+    ew, ehx = rel_fro(g["Wt"], Wt), rel_fro(g["HXt"], HXt)
+    announce(f"c5: W~ rel {ew:.2e}, H~_X rel {ehx:.2e}")
+    assert ew <= 1e-5 and ehx <= 1e-5
+    # rotation keeps the trace: tr(H~_G) = sum_k H_G[k,k] / d_out[k]^2
+    assert g["HGt_trace"] == pytest.approx(float(np.sum(hg_diag / d_out ** 2)), rel=1e-5)
+    fac = o.damp_and_factor(HXt, cfg.damp)
+    rows = np.sort(np.random.default_rng(5).choice(cfg.out, N_ROWS, replace=False))
+    res = check_rows(g, Wt, HXt, cfg, rows, fac)
+    announce(f"c5: {N_ROWS} sampled rows match ({res.accepted_ties} near-tie codes adopted)")
