@@ -484,7 +484,8 @@ def unpack_codes(words: np.ndarray, bits: int, n: int) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Inter-layer bit allocation
 # ---------------------------------------------------------------------------
-def allocate_bits(sens, numel, allowed=(2, 3, 4), target_num: int = 5, target_den: int = 2):
+def allocate_bits(sens, numel, allowed=(2, 3, 4), target_num: int = 5, target_den: int = 2,
+                  report_margin: bool = False):
     """Per-sublayer bit widths from the tr(H_G) tr(H_X) sensitivities.
 
     [KronQ-README] opening section and flags table ("inter-layer mixed
@@ -496,6 +497,9 @@ def allocate_bits(sens, numel, allowed=(2, 3, 4), target_num: int = 5, target_de
     step the sublayer with the largest loss reduction per added bit-weight,
     gain_l = (s_l * (4^-b_l - 4^-b_next)) / n_l, ties to the smallest index.
     Integer budget; gains compared exactly in fp64 in that operation order.
+    With report_margin, also returns the smallest relative gap, over all steps,
+    between the chosen gain and the best gain it beat (how far the decisions
+    were from a tie).
     """
     sens = [float(s) for s in sens]
     numel = [int(n) for n in numel]
@@ -505,8 +509,10 @@ def allocate_bits(sens, numel, allowed=(2, 3, 4), target_num: int = 5, target_de
     total = sum(numel)
     budget = (total * target_num) // target_den
     used = allowed[0] * total
+    margin = math.inf
     while True:
         best, best_gain = -1, -1.0
+        gains = []
         for l in range(L):
             i = allowed.index(bits[l])
             if i + 1 >= len(allowed):
@@ -516,14 +522,18 @@ def allocate_bits(sens, numel, allowed=(2, 3, 4), target_num: int = 5, target_de
                 continue
             dq = 4.0 ** (-bits[l]) - 4.0 ** (-nb)
             gain = (sens[l] * dq) / float(numel[l] * (nb - bits[l]))
+            gains.append(gain)
             if gain > best_gain:
                 best, best_gain = l, gain
         if best < 0:
             break
+        if len(gains) > 1 and best_gain > 0:
+            runner = sorted(gains)[-2]
+            margin = min(margin, (best_gain - runner) / best_gain)
         i = allowed.index(bits[best])
         used += (allowed[i + 1] - bits[best]) * numel[best]
         bits[best] = allowed[i + 1]
-    return bits
+    return (bits, margin) if report_margin else bits
 
 
 # ---------------------------------------------------------------------------
