@@ -48,7 +48,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="approximate CPU budget of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 1 GiB fp32 tensor three times (scale for the HBM byte "
+                         "counters FETCH_SIZE / WRITE_SIZE) and exit")
     return ap.parse_args()
+
+
+def copy_calibration() -> None:
+    """A plain device copy of known size: 1 GiB read + 1 GiB written per dispatch."""
+    import torch
+    x = torch.ones(2 ** 28, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y = x.clone()
+    torch.cuda.synchronize()
+    del y
+    print(json.dumps({"copy_calibration_bytes_per_dispatch": 2 ** 30, "dispatches": 3}), flush=True)
 
 
 def syrk_flops(n: int, T: int) -> float:
@@ -64,7 +79,7 @@ def source_hash(path: str) -> str:
 def traffic_from_profile(kernel_src: str, launch_units: float):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", "syrk_bf16_c2_hbm_traffic.json")
+    p = os.path.join(ROOT, "profiles", "syrk_dma_kernel_c2_hbm_traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -136,6 +151,9 @@ def main():
         print(f"bench.py: this engine runs on one GPU; --gpus {a.gpus} is not supported "
               "(the multi-GPU sharding plan is described in the design notes)", file=sys.stderr)
         sys.exit(2)
+    if a.copy_calibration:
+        copy_calibration()
+        return
     import torch
     import post_quantization_syrk_amd as kq
 
@@ -220,7 +238,7 @@ def main():
                                    flops_per_launch)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": "syrk_bf16_kernel",
+                "traffic": traffic, "kernel": "syrk_dma_kernel",
                 "algorithmic_flops_per_launch": flops_per_launch}
 
     cpu = None

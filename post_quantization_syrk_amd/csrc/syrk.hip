@@ -5,32 +5,34 @@
 // output gradients (WaterKron and FlipFlop Hessian, Table 1, "Marginal":
 // E[x x^T] and E[g g^T]).  Both are the same operation on different streams.
 //
-// Kernel design (gfx950, CDNA4):
-//   * 256 x 256 output tiles over the lower block triangle, 256 threads
-//     (4 waves of 64); each wave owns a 128 x 128 sub-tile = 4 x 4 blocks of
-//     v_mfma_f32_32x32x16_bf16 (fp32 accumulators, bf16 products are exact),
-//     which keeps LDS operand traffic at 8 KB per 16 MFMAs.
-//   * The token axis is the reduction axis and is the slow axis of the
-//     stream, so every 64-token stage is loaded as 16 tokens x 4 channels per
-//     thread (coalesced 512-byte rows per wave), transposed in registers to
-//     channel-major order and stored to LDS, where each MFMA operand is one
-//     16-byte read of 8 consecutive tokens.  A channel's 64 tokens fill one
-//     128-byte LDS row whose eight 16-byte chunks are permuted by
-//     chunk ^ ((c ^ (c >> 3)) & 7): both the transposed stores (lanes 4
-//     channels apart) and the operand reads (lanes 1 channel apart) then hit
-//     distinct banks.
-//   * Two LDS buffers: the next stage's global loads are in flight while the
-//     current stage runs on the matrix cores.
-//   * The token range is split S ways (S a multiple of 8, about 2048
-//     workgroups in all).  Workgroups are numbered split-major: the ones
-//     dispatched together work on the same token range, so the streamed
-//     tokens are shared through the L2s and the last-level cache.  Tiles are
-//     visited in bands of 4 tile rows so neighbouring tiles share panels.
-//     Partial tiles are added to H with fp32 atomics (H is zeroed first
-//     unless accumulating).  Measured on the 4096-wide, 131072-token factor:
-//     8 waves per workgroup (2 per SIMD) beat 4 waves (1 per SIMD), and
-//     split-major beat tile-major order.
-//   * A final pass mirrors the lower triangle into the upper one.
+// Two kernels compute the same H; the direct-to-LDS one is the default.
+//
+// Direct-to-LDS kernel (syrk_dma_kernel):
+//   * 256 x 256 output tiles over the lower block triangle, 4 waves of 64; each wave owns a
+//     128 x 128 sub-tile = 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (fp32 accumulators in
+//     AGPRs; bf16 products are exact in fp32).
+//   * The stream is copied into LDS token-major, as it lies in memory, by the load unit
+//     itself (global_load_lds, 16 bytes per lane): no registers are spent on staging, and a
+//     ring of four 32-token stages (128 KB) keeps three stages of copies in flight.  The
+//     MFMA operands (8 consecutive tokens of one channel per lane) are read with the
+//     transposing LDS read ds_read_b64_tr_b16; a per-token-row XOR swizzle of the 16-byte
+//     chunks keeps those reads free of bank conflicts.
+//   * Each wave copies the same number of chunks in every stage (tokens outside the split
+//     read a 16-byte zero chunk), so the per-stage vmcnt waits are exact; one workgroup
+//     barrier per stage hands buffers over.  Operand reads, copies and MFMAs are interleaved
+//     explicitly, operands in the order the MFMAs consume them.
+//   * XCD-aware order: workgroup u runs on XCD u mod 8; each XCD walks a contiguous region
+//     of tiles split by split, so the tiles resident on one XCD share panels in its L2 and
+//     all XCDs stream the same token range at the same time (last-level cache reuse).  The
+//     token split count is the smallest that fills whole rounds of an XCD's CUs.
+//   * Partial tiles are added to H with fp32 atomics (H is zeroed first unless
+//     accumulating); a final pass mirrors the lower triangle into the upper one.
+//
+// Register-staged kernel (syrk_bf16_kernel, selected by KQ_SYRK_VARIANT=0..3): 64-token
+// stages loaded into registers as 8 tokens x 4 channels per thread, transposed in registers
+// and stored channel-major into two LDS buffers with an XOR-permuted chunk layout; 4 or 8
+// waves; split-major or tile-major order.  It also serves strides too large for the direct
+// kernel's 32-bit per-stage offsets.
 #include "kq_internal.h"
 
 #include <stdlib.h>
@@ -150,6 +152,7 @@ __device__ __forceinline__ void store_block(uint16_t* __restrict__ panel, int cl
   *(uint4*)(panel + lds_off(cl + (3 ^ o), kc)) = w3;
 }
 
+// Register-staged kernel.
 // WAVES = 4: 128 x 128 per wave (1 wave per SIMD); WAVES = 8: 128 x 64 per wave (2 per SIMD).
 // SPLIT_MAJOR: consecutive workgroups share a token range (all tiles of one split run
 // together, so the concurrently streamed tokens stay in the last-level cache);
@@ -267,6 +270,262 @@ __global__ __launch_bounds__(WAVES * 64) void syrk_bf16_kernel(SyrkArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Direct-to-LDS variant.  The stream is copied into LDS token-major, exactly as it lies in
+// memory, by the load unit itself (global_load_lds, 16 bytes per lane, 1 KB per wave
+// instruction): no registers are spent on staging and up to four 32-token stages are in
+// flight at once.  The MFMA operands, which need 8 consecutive tokens of one channel per lane,
+// are then read with the transposing LDS read ds_read_b64_tr_b16: within each 16-lane group,
+// lane 4e+q points at token e, channels 4q..4q+3, and lane i receives channel i, tokens 0..3.
+// A token row holds the tile's 256 channels as 32 chunks of 16 bytes; chunk k of token t is
+// stored in slot k ^ swz(t mod 4) with swz = {0, 10, 6, 12}, which puts the four token rows
+// read by each half-wave (and by each quarter-wave) on disjoint banks.
+// ---------------------------------------------------------------------------------------------
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+constexpr int DBK = 32;                  // tokens per stage
+constexpr int DPANEL = DBK * TILE;       // bf16 elements of one panel (16 KB)
+constexpr int DSTAGE = 2 * DPANEL;       // both panels of a stage (32 KB)
+constexpr int DWAVES = 4;
+constexpr int DMA_PER_PANEL = DPANEL * 2 / 1024 / DWAVES;   // 1 KB wave instructions per wave
+
+__device__ __forceinline__ int dswz(int e) { return (0xC6A0 >> (4 * e)) & 15; }
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int WAIT_LGKM0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+// Workgroup barrier for LDS hand-off; also a hard boundary for the instruction scheduler.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Sixteen zero bytes in device memory: the source of every copy lane whose token lies outside
+// the split, so that each wave issues the same number of copies in every stage and the
+// vmcnt-based waits stay exact.
+__device__ __attribute__((aligned(16))) uint32_t g_zero_chunk[4];
+
+// Copy tokens [t0, t0 + DBK) x channels [cbase, cbase + 256) of the stream into a panel.
+// Wave w fills 1 KB blocks DMA_PER_PANEL*w + r (two token rows each); lane l of a block
+// writes slot l & 31 of token row 2p + (l >> 5).  off[r] is the lane's element offset from
+// the stage's first token row (row * lda + channel; channels at or beyond n are read from
+// channel 0 of the same token, their products only reach entries of H outside the matrix).
+// dma_sources computes the lane's source addresses, dma_copy issues the copies.
+__device__ __forceinline__ void dma_sources(const uint16_t* __restrict__ base, int64_t t0,
+                                            int64_t tend, const uint32_t (&off)[DMA_PER_PANEL],
+                                            int wave, int lane,
+                                            const uint16_t* (&src)[DMA_PER_PANEL]) {
+  const uint16_t* zero = (const uint16_t*)g_zero_chunk;
+#pragma unroll
+  for (int r = 0; r < DMA_PER_PANEL; ++r) {
+    const int row = 2 * (DMA_PER_PANEL * wave + r) + (lane >> 5);
+    src[r] = t0 + row < tend ? base + off[r] : zero;
+  }
+}
+
+__device__ __forceinline__ void dma_copy(const uint16_t* const (&src)[DMA_PER_PANEL],
+                                         uint16_t* panel, int wave) {
+#pragma unroll
+  for (int r = 0; r < DMA_PER_PANEL; ++r)
+    __builtin_amdgcn_global_load_lds(
+        (const void*)src[r],
+        (__attribute__((address_space(3))) void*)(panel + (DMA_PER_PANEL * wave + r) * 512), 16,
+        0, 0);
+}
+
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) v4i16 lds_v4;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)p);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p + 4 * TILE));
+  const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+struct DmaArgs {
+  SyrkArgs s;
+  int per_xcd;   // tiles per XCD region
+  int xcds;
+};
+
+// DNST = stages in the LDS ring (4: 128 KB, 5: 160 KB); each buffer is its own LDS object so
+// that the compiler can tell the reads of one stage from the copies into another.
+template <int DNST>
+__global__ __launch_bounds__(DWAVES * 64) void syrk_dma_kernel(DmaArgs d) {
+  static_assert(DNST == 4 || DNST == 5, "ring of 4 or 5 stages");
+  const SyrkArgs& a = d.s;
+  __shared__ __attribute__((aligned(1024))) uint16_t b0[DSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t b1[DSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t b2[DSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t b3[DSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t b4[DNST == 5 ? DSTAGE : 8];
+
+  // workgroup u runs on XCD u mod xcds; each XCD walks its own contiguous region of tiles,
+  // split by split, so the tiles resident on one XCD share panels in its L2 and all XCDs
+  // stream the same token range at the same time
+  const int u = blockIdx.x;
+  const int xcd = u % d.xcds;
+  const int q = u / d.xcds;
+  const int split = q / d.per_xcd;
+  const int tile = xcd * d.per_xcd + q % d.per_xcd;
+  if (tile >= a.ntiles || split >= a.splits) return;
+  int bi, bj;
+  tile_of(tile, a.nb, bi, bj);
+  const int64_t tbeg = (int64_t)split * a.tok_split;
+  const int64_t tend = min(a.T, tbeg + a.tok_split);
+  if (tbeg >= tend) return;
+  const int nst_real = (int)((tend - tbeg + DBK - 1) / DBK);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int ci = bi * TILE, cj = bj * TILE;
+
+  // stage-invariant part of this lane's copy sources (see dma_panel)
+  uint32_t offi[DMA_PER_PANEL], offj[DMA_PER_PANEL];
+#pragma unroll
+  for (int r = 0; r < DMA_PER_PANEL; ++r) {
+    const int row = 2 * (DMA_PER_PANEL * wave + r) + (lane >> 5);
+    const int k8 = 8 * ((lane & 31) ^ dswz(row & 3));
+    offi[r] = (uint32_t)(row * a.lda) + (uint32_t)(ci + k8 < a.n ? ci + k8 : 0);
+    offj[r] = (uint32_t)(row * a.lda) + (uint32_t)(cj + k8 < a.n ? cj + k8 : 0);
+  }
+
+  // per-lane element offsets of the operand reads inside a panel (first token half, kk = 0)
+  const int e = (lane >> 2) & 3, qq = lane & 3, g = lane >> 4;
+  const int rowoff = (8 * (g >> 1) + e) * TILE + 4 * (qq & 1);
+  int offA[4], offB[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    offA[m] = rowoff + 8 * ((4 * m + 2 * (g & 1) + (qq >> 1)) ^ dswz(e)) + 128 * wr;
+    offB[m] = rowoff + 8 * ((4 * m + 2 * (g & 1) + (qq >> 1)) ^ dswz(e)) + 128 * wc;
+  }
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[m][k] = f32x16{};
+
+  // Stages at or beyond the split's end (the ring runs DNST stages ahead) copy zeros.
+  // Diagonal tiles copy their one panel twice, which keeps every tile on one code path.
+  const uint16_t* srci[DMA_PER_PANEL];
+  const uint16_t* srcj[DMA_PER_PANEL];
+  auto sources = [&](int s) {
+    const int64_t t0 = tbeg + (int64_t)s * DBK;
+    const uint16_t* base = a.A + min(t0, tend) * a.lda;
+    dma_sources(base, t0, tend, offi, wave, lane, srci);
+    dma_sources(base, t0, tend, offj, wave, lane, srcj);
+  };
+  auto issue = [&](uint16_t* buf) {
+    dma_copy(srci, buf, wave);
+    dma_copy(srcj, buf + DPANEL, wave);
+  };
+  // operands are read in the order the multiplies consume them: a0, b0..b3, a1..a3
+  auto read = [&](const uint16_t* buf, int kk, bf16x8 (&av)[4], bf16x8 (&bv)[4]) {
+    const uint16_t* pi = buf + kk * 16 * TILE;
+    const uint16_t* pj = buf + DPANEL + kk * 16 * TILE;
+    av[0] = tr_operand(pi + offA[0]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) bv[k] = tr_operand(pj + offB[k]);
+#pragma unroll
+    for (int m = 1; m < 4; ++m) av[m] = tr_operand(pi + offA[m]);
+  };
+  auto mma = [&](const bf16x8 (&av)[4], const bf16x8 (&bv)[4]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        acc[m][k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[m], bv[k], acc[m][k], 0, 0, 0);
+  };
+  // wait until this wave's copies of stage s+1 have landed: every stage issues the same number
+  // of copies and stages up to s + DNST - 1 have been issued
+  auto wait_next = [&]() { __builtin_amdgcn_s_waitcnt(wait_vm(2 * DMA_PER_PANEL * (DNST - 2))); };
+
+  // The stage count is rounded up to whole rounds of the ring; stages past the split's end
+  // are copied as zeros and add nothing.  Every stage of a round then uses a fixed buffer.
+  const int nst = ((nst_real + DNST - 1) / DNST) * DNST;
+  bf16x8 xa[4], xb[4], ya[4], yb[4];
+  sources(0); issue(b0);
+  sources(1); issue(b1);
+  sources(2); issue(b2);
+  sources(3); issue(b3);
+  if constexpr (DNST == 5) { sources(4); issue(b4); }
+  __builtin_amdgcn_s_waitcnt(wait_vm(2 * DMA_PER_PANEL * (DNST - 1)));
+  lds_barrier();
+  read(b0, 0, xa, xb);
+
+  // Stage s: operands of its first 16 tokens are already in registers (xa, xb).  Read the
+  // second 16 (ya, yb) early while multiplying the first, and prepare the copy sources of
+  // stage s + DNST; wait for this wave's copies of stage s+1 and for every wave's reads of
+  // stage s; refill stage s's buffer with stage s + DNST and read the first operands of
+  // stage s+1 while multiplying the second half of stage s.  (After the last stage the read
+  // of the next buffer is harmless and unused.)
+#define KQ_DMA_STEP(J, CUR, NXT)                                   \
+  {                                                                \
+    const int s = s0 + (J);                                        \
+    read(CUR, 1, ya, yb);                                          \
+    mma(xa, xb);                                                   \
+    sources(s + DNST);                                             \
+    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {             \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);           \
+    }                                                              \
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);             \
+    __builtin_amdgcn_sched_barrier(0);                             \
+    wait_next();                                                   \
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);                        \
+    lds_barrier();                                                 \
+    issue(CUR);                                                    \
+    read(NXT, 0, xa, xb);                                          \
+    mma(ya, yb);                                                   \
+    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {             \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);           \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);           \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);           \
+    }                                                              \
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);             \
+    __builtin_amdgcn_sched_barrier(0);                             \
+  }
+  for (int s0 = 0; s0 < nst; s0 += DNST) {
+    if constexpr (DNST == 4) {
+      KQ_DMA_STEP(0, b0, b1)
+      KQ_DMA_STEP(1, b1, b2)
+      KQ_DMA_STEP(2, b2, b3)
+      KQ_DMA_STEP(3, b3, b0)
+    } else {
+      KQ_DMA_STEP(0, b0, b1)
+      KQ_DMA_STEP(1, b1, b2)
+      KQ_DMA_STEP(2, b2, b3)
+      KQ_DMA_STEP(3, b3, b4)
+      KQ_DMA_STEP(4, b4, b0)
+    }
+  }
+#undef KQ_DMA_STEP
+  // the ring's trailing copies (zeros) must land before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+
+  // epilogue: lane holds column l32 of each 32x32 block; rows 8*(r/4) + 4*(lane/32) + r%4
+  const int l32 = lane & 31, rh = (lane >> 5) * 4;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int gj = cj + 128 * wc + 32 * k + l32;
+      if (gj >= a.n) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gi = ci + 128 * wr + 32 * m + 8 * (r >> 2) + rh + (r & 3);
+        if (gi < a.n) atomicAdd(a.H + (int64_t)gi * a.ldh + gj, acc[m][k][r]);
+      }
+    }
+  }
+}
+
 // Zero the lower block triangle of H (the region the tiles add into).
 __global__ void zero_lower_tiles(float* __restrict__ H, int64_t ldh, int n) {
   const int row = blockIdx.x;
@@ -296,15 +555,49 @@ __global__ __launch_bounds__(256) void mirror_lower_to_upper(float* __restrict__
   }
 }
 
-// Kernel variant: bit 0 = 8 waves (else 4), bit 1 = split-major order.  KQ_SYRK_VARIANT
-// overrides the default (a tuning knob; every variant computes the same H).
+// Kernel variant: 4 = direct-to-LDS kernel (default); 0..3 = register-staged kernel with
+// bit 0 = 8 waves (else 4), bit 1 = split-major order.  KQ_SYRK_VARIANT overrides the default
+// (a tuning knob; every variant computes the same H).
 int syrk_variant() {
   const char* env = getenv("KQ_SYRK_VARIANT");
   if (env) {
     const int v = atoi(env);
-    if (v >= 0 && v <= 3) return v;
+    if (v >= 0 && v <= 4) return v;
   }
-  return 3;
+  return 4;
+}
+
+// Stages in the direct-to-LDS kernel's ring (KQ_SYRK_RING = 4 or 5; a tuning knob).
+int syrk_ring() {
+  const char* env = getenv("KQ_SYRK_RING");
+  if (env && atoi(env) == 4) return 4;
+  if (env && atoi(env) == 5) return 5;
+  return 4;
+}
+
+// Token splits for the direct-to-LDS kernel: the smallest S (>= 2 stages of work per tile
+// each) whose per-XCD workgroup count fills whole rounds of the XCD's CUs to within 3 %, with
+// at least two workgroups per CU in all.
+int choose_splits_dma(int per_xcd, int cu_per_xcd, int xcds, int64_t T) {
+  const char* env = getenv("KQ_SYRK_SPLITS");
+  if (env) {
+    int v = atoi(env);
+    if (v >= 1) return v;
+  }
+  int64_t max_s = T / (8 * DBK);
+  if (max_s < 1) max_s = 1;
+  if (max_s > 64) max_s = 64;
+  int best = 1;
+  double best_eff = 0.0;
+  for (int s = 1; s <= max_s; ++s) {
+    const int64_t items = (int64_t)per_xcd * s;
+    const int64_t rounds = (items + cu_per_xcd - 1) / cu_per_xcd;
+    const double eff = (double)items / (double)(rounds * cu_per_xcd);
+    if (items * xcds < 2LL * cu_per_xcd * xcds) continue;
+    if (eff >= 0.97) return s;
+    if (eff > best_eff + 1e-9) { best_eff = eff; best = s; }
+  }
+  return best;
 }
 
 int choose_splits(int ntiles, int64_t T) {
@@ -357,9 +650,26 @@ extern "C" kq_status kq_accumulate_hessian(const uint16_t* A_bf16, int64_t T, in
     a.splits = choose_splits(a.ntiles, T);
     a.tok_split = ceil_div(ceil_div(T, a.splits), BK) * BK;
     a.splits = (int)ceil_div(T, a.tok_split);
+    int variant = syrk_variant();
+    // the direct-to-LDS kernel keeps 32-bit per-lane offsets within a 32-token stage
+    if (variant == 4 && (int64_t)DBK * lda + n >= ((int64_t)1 << 32)) variant = 3;
+    if (variant == 4) {
+      DmaArgs d;
+      d.xcds = device_cu_count() % 8 == 0 ? 8 : 1;
+      const int cu_per_xcd = device_cu_count() / d.xcds;
+      d.per_xcd = (int)ceil_div(a.ntiles, d.xcds);
+      a.splits = choose_splits_dma(d.per_xcd, cu_per_xcd, d.xcds, T);
+      a.tok_split = ceil_div(ceil_div(T, a.splits), DBK) * DBK;
+      a.splits = (int)ceil_div(T, a.tok_split);
+      d.s = a;
+      const int64_t g = (int64_t)d.xcds * d.per_xcd * a.splits;
+      if (g > 0x7FFFFFFF) return fail(KQ_ESHAPE, "kq_accumulate_hessian: too many tiles");
+      if (syrk_ring() == 5) syrk_dma_kernel<5><<<dim3((unsigned)g), dim3(DWAVES * 64), 0, s>>>(d);
+      else syrk_dma_kernel<4><<<dim3((unsigned)g), dim3(DWAVES * 64), 0, s>>>(d);
+      KQ_LAUNCHED("syrk_dma_kernel");
+    } else {
     const int64_t grid = (int64_t)a.ntiles * a.splits;
     if (grid > 0x7FFFFFFF) return fail(KQ_ESHAPE, "kq_accumulate_hessian: too many tiles");
-    const int variant = syrk_variant();
     const bool split_major = (variant & 2) != 0;
     if (variant & 1) {
       if (split_major) syrk_bf16_kernel<8, true><<<dim3((unsigned)grid), dim3(512), 0, s>>>(a);
@@ -369,6 +679,7 @@ extern "C" kq_status kq_accumulate_hessian(const uint16_t* A_bf16, int64_t T, in
       else syrk_bf16_kernel<4, false><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
     }
     KQ_LAUNCHED("syrk_bf16_kernel");
+    }
   }
   const int m = (int)ceil_div(n, 64);
   const int64_t mt = (int64_t)m * (m + 1) / 2;
