@@ -171,9 +171,10 @@ kq_status kq_quantize_layer_workspace(const kq_quant_params* p, int64_t out, int
  *   (xmin = min(0, min), xmax = max(0, max), s = (xmax - xmin) / (2^b - 1) or 1 if
  *   equal, z = rint(-xmin / s)); code q = clamp(rint(w / s) + z, 0, 2^b - 1)
  *   (round half to even); the rounding error is fed back into later columns.
- * Implementation: reverse-order Cholesky H_d = R R^T (R upper), U = R^-1, and the
- * column recursion run 128 (or 64) columns at a time with one matrix product per
- * block for the feedback from earlier blocks.
+ * Implementation: reverse-order Cholesky H_d = R R^T (R upper), U = R^-1 formed only
+ * in its diagonal blocks, and the column recursion run 128 (or 64) columns at a time
+ * with one matrix product per block for the feedback from earlier blocks
+ * ((W~ - Qhat)[:, <J] R[<J, J] U_JJ, which equals -E[:, <J] U[<J, J]).
  *
  *   W_rot     device fp32, out x in (ld = in), the processed weights W~.  Clobbered:
  *             on return column j holds GPTQ's error e_j = (w_j - qhat_j) / U_jj

@@ -3,7 +3,7 @@
 // left-looking GPTQ block update and the proxy-loss products.
 //
 // C[M x N] (+)= alpha * op(A) op(B), row-major.  128 x 128 tiles, 256 threads
-// (4 waves, each a 64 x 64 sub-tile = 2 x 2 MFMA blocks), 16-deep K stages
+// (4 waves, each a 64 x 64 sub-tile = 2 x 2 MFMA blocks), 32-deep K stages
 // through LDS stored k-major so every MFMA operand read is 32 consecutive
 // floats.  Optional split-K with fp32 atomics, upper-triangle-only tile sets,
 // and a reduction epilogue sum(alpha * AB .* D) into an fp64 accumulator.
@@ -14,7 +14,8 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int MT = 128, NTL = 128, BK = 16, THREADS = 256;
+constexpr int MT = 128, NTL = 128, BK = 32, THREADS = 256;
+constexpr int LD_UNITS = MT * BK / 4 / THREADS;   // float4 loads per thread per operand and stage
 constexpr int LDA_S = MT + 4, LDB_S = NTL + 4;
 
 struct Args {
@@ -29,17 +30,17 @@ struct Args {
   const float* D; int64_t ldd; double* red;
 };
 
-// Loads one BK-deep stage of op(A) (MT x BK) into registers: 2 float4 per thread.
+// Loads one BK-deep stage of op(A) (MT x BK) into registers: LD_UNITS float4 per thread.
 __device__ __forceinline__ void load_a(const Args& a, int64_t m0, int64_t k0, int64_t kend,
-                                       float4 (&r)[2]) {
+                                       float4 (&r)[LD_UNITS]) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < LD_UNITS; ++u) {
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (!a.transA) {
-      // A row-major M x K: thread -> row (t/4 + 64u), k quad (t%4)
-      const int64_t row = m0 + (t >> 2) + 64 * u;
-      const int64_t k = k0 + 4 * (t & 3);
+      // A row-major M x K: thread -> row (t/8 + 32u), k quad (t%8)
+      const int64_t row = m0 + (t >> 3) + 32 * u;
+      const int64_t k = k0 + 4 * (t & 7);
       if (row < a.M && k < kend) v = *(const float4*)(a.A + row * a.lda + k);
     } else {
       // A stored K x M: thread -> k (t/32 + 8u), m quad (t%32)
@@ -52,10 +53,10 @@ __device__ __forceinline__ void load_a(const Args& a, int64_t m0, int64_t k0, in
 }
 
 __device__ __forceinline__ void load_b(const Args& a, int64_t n0, int64_t k0, int64_t kend,
-                                       float4 (&r)[2]) {
+                                       float4 (&r)[LD_UNITS]) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < LD_UNITS; ++u) {
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (!a.transB) {
       // B row-major K x N: thread -> k (t/32 + 8u), n quad (t%32)
@@ -63,9 +64,9 @@ __device__ __forceinline__ void load_b(const Args& a, int64_t n0, int64_t k0, in
       const int64_t col = n0 + 4 * (t & 31);
       if (k < kend && col < a.N) v = *(const float4*)(a.B + k * a.ldb + col);
     } else {
-      // B stored N x K: thread -> n row (t/4 + 64u), k quad (t%4)
-      const int64_t row = n0 + (t >> 2) + 64 * u;
-      const int64_t k = k0 + 4 * (t & 3);
+      // B stored N x K: thread -> n row (t/8 + 32u), k quad (t%8)
+      const int64_t row = n0 + (t >> 3) + 32 * u;
+      const int64_t k = k0 + 4 * (t & 7);
       if (row < a.N && k < kend) v = *(const float4*)(a.B + row * a.ldb + k);
     }
     r[u] = v;
@@ -73,12 +74,12 @@ __device__ __forceinline__ void load_b(const Args& a, int64_t n0, int64_t k0, in
 }
 
 // Stores a stage k-major: As[k][m], Bs[k][n]
-__device__ __forceinline__ void store_a(const Args& a, float* As, const float4 (&r)[2]) {
+__device__ __forceinline__ void store_a(const Args& a, float* As, const float4 (&r)[LD_UNITS]) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < LD_UNITS; ++u) {
     if (!a.transA) {
-      const int m = (t >> 2) + 64 * u, k = 4 * (t & 3);
+      const int m = (t >> 3) + 32 * u, k = 4 * (t & 7);
       As[(k + 0) * LDA_S + m] = r[u].x;
       As[(k + 1) * LDA_S + m] = r[u].y;
       As[(k + 2) * LDA_S + m] = r[u].z;
@@ -90,15 +91,15 @@ __device__ __forceinline__ void store_a(const Args& a, float* As, const float4 (
   }
 }
 
-__device__ __forceinline__ void store_b(const Args& a, float* Bs, const float4 (&r)[2]) {
+__device__ __forceinline__ void store_b(const Args& a, float* Bs, const float4 (&r)[LD_UNITS]) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < LD_UNITS; ++u) {
     if (!a.transB) {
       const int k = (t >> 5) + 8 * u, n = 4 * (t & 31);
       *(float4*)(Bs + k * LDB_S + n) = r[u];
     } else {
-      const int n = (t >> 2) + 64 * u, k = 4 * (t & 3);
+      const int n = (t >> 3) + 32 * u, k = 4 * (t & 7);
       Bs[(k + 0) * LDB_S + n] = r[u].x;
       Bs[(k + 1) * LDB_S + n] = r[u].y;
       Bs[(k + 2) * LDB_S + n] = r[u].z;
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(Args a) {
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
   const int nst = (int)((kend - kbeg + BK - 1) / BK);
-  float4 ra[2], rb[2];
+  float4 ra[LD_UNITS], rb[LD_UNITS];
   if (nst > 0) {
     load_a(a, m0, kbeg, kend, ra);
     load_b(a, n0, kbeg, kend, rb);
@@ -155,19 +156,24 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(Args a) {
     }
     const float* as = As[buf];
     const float* bs = Bs[buf];
+    // all operands of the stage are read before the multiplies, so the LDS latency is paid
+    // once per stage instead of once per k step
+    float av[BK / 2][2], bv[BK / 2][2];
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 2) {
-      float av[2], bv[2];
+    for (int kk = 0; kk < BK / 2; ++kk) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) av[i] = as[(kk + kh) * LDA_S + wm + 32 * i + l32];
+      for (int i = 0; i < 2; ++i) av[kk][i] = as[(2 * kk + kh) * LDA_S + wm + 32 * i + l32];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bv[j] = bs[(kk + kh) * LDB_S + wn + 32 * j + l32];
+      for (int j = 0; j < 2; ++j) bv[kk][j] = bs[(2 * kk + kh) * LDB_S + wn + 32 * j + l32];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < BK / 2; ++kk)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], acc[i][j], 0, 0, 0);
-    }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[kk][i], bv[kk][j], acc[i][j], 0, 0, 0);
     if (more) {
       store_a(a, As[buf ^ 1], ra);
       store_b(a, Bs[buf ^ 1], rb);
@@ -195,6 +201,42 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(Args a) {
     if (lane == 0) atomicAdd(a.red, part);
     return;
   }
+  if (a.split_k > 1) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t col = n0 + wn + 32 * j + l32;
+        if (col >= a.N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + rh + (r & 3);
+          if (row < a.M) atomicAdd(a.C + row * a.ldc + col, a.alpha * acc[i][j][r]);
+        }
+      }
+    return;
+  }
+  // C += alpha AB: every C value of the thread is loaded before any is stored, so the
+  // loads are issued together instead of one round trip per element.
+  if (a.accumulate) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t col = n0 + wn + 32 * j + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + rh + (r & 3);
+          const float c = (row < a.M && col < a.N) ? a.C[row * a.ldc + col] : 0.0f;
+          acc[i][j][r] = fmaf(a.alpha, acc[i][j][r], c);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] *= a.alpha;
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -204,13 +246,7 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(Args a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + rh + (r & 3);
-        if (row >= a.M) continue;
-        float* c = a.C + row * a.ldc + col;
-        const float v = a.alpha * acc[i][j][r];
-        if (a.split_k > 1)
-          atomicAdd(c, v);
-        else
-          *c = a.accumulate ? *c + v : v;
+        if (row < a.M) a.C[row * a.ldc + col] = acc[i][j][r];
       }
     }
 }

@@ -9,13 +9,16 @@
 //   e_j = (w_j - qhat_j) / U_jj,   w_k -= e_j U_jk  (k > j)
 // where the (row, group) grid is taken from the current weights when a group's
 // first column is reached.  It is run blockwise, B columns at a time:
-//   Y = -E[:, <J] U[<J, J]              one fp32 MFMA product (split over K, atomics):
-//                                       the block's current weights are W0[:, J] + Y,
+//   Y = D[:, <J] P[<J, J]               one fp32 MFMA product (split over K, atomics):
+//                                       D = W0 - Qhat (the rounding error so far) and
+//                                       P = R[<J, J] U_JJ, so that Y = -E[:, <J] U[<J, J]
+//                                       and the block's current weights are W0[:, J] + Y,
 //                                       exactly GPTQ's state when the block starts
 //   column kernel, column by column inside the block:
 //     (at group starts) min-max grid from the current weights of the group,
 //     q = clamp(rint(w/s) + z), e_j = (w_j - s (q - z)) / U_jj, w_k -= e_j U_jk (k in J)
-//   the codes are packed into the output words in the same kernel; e_j replaces W0_j.
+//   the codes are packed into the output words in the same kernel; e_j replaces W0_j and
+//   W0_j - s (q - z) goes to D.
 #include "kq_internal.h"
 
 #include <math.h>
@@ -25,7 +28,7 @@
 namespace kq {
 
 kq_status damp_and_factor(const float* HX, float* F, float* T, uint8_t* dead, double* lam,
-                          int* flag, int64_t n, float damp, hipStream_t s);
+                          int* flag, int64_t n, float damp, int B, hipStream_t s);
 
 namespace {
 
@@ -36,8 +39,9 @@ constexpr int RPW = CTHREADS / LPR; // matrix rows per workgroup
 struct ColArgs {
   float* W;            // out x in: W0 (unprocessed columns) / errors e (processed columns)
   int64_t out, in;
-  float* Y;            // out x B corrections of the current block (-E U)
-  const float* U;      // in x in upper triangular, chol_upper(H_d^-1)
+  float* Y;            // out x B corrections of the current block (D P = -E U)
+  float* D;            // out x in: W0 - Qhat of the processed columns
+  const float* U;      // in x in: U_JJ in the diagonal B x B blocks
   const uint8_t* dead; // in
   int bits;
   float maxq;
@@ -69,7 +73,9 @@ __device__ __forceinline__ float row_max(float v) {
 template <int CPL>
 struct RowState {
   float w[CPL];    // current weights of this lane's columns
+  float w0[CPL];   // their starting weights (W0)
   float el[CPL];   // errors e_j once quantized
+  float dl[CPL];   // W0_j - qhat_j once quantized
   float s, inv, z; // grid of the current group
 };
 
@@ -119,6 +125,7 @@ __device__ __forceinline__ void gptq_step(RowState<B / LPR>& st, const StepCtx& 
   const float d = -err;
   if (cx.q == O) {
     st.el[E] = err;
+    st.dl[E] = st.w0[E] - st.s * (qv - st.z);
     cx.Qrow[J] = (uint8_t)qv;
   }
   const float* crow = cx.Cb + J * B + CPL * cx.q;
@@ -178,11 +185,16 @@ __global__ __launch_bounds__(CTHREADS) void gptq_block_kernel(ColArgs a, int64_t
       *(float4*)(a.Y + r * B + CPL * q + e) = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     const uint8_t* dd = a.dead + col + e;
-    st.w[e] = (dd[0] ? 0.f : w0.x) + y.x;
-    st.w[e + 1] = (dd[1] ? 0.f : w0.y) + y.y;
-    st.w[e + 2] = (dd[2] ? 0.f : w0.z) + y.z;
-    st.w[e + 3] = (dd[3] ? 0.f : w0.w) + y.w;
+    st.w0[e] = dd[0] ? 0.f : w0.x;
+    st.w0[e + 1] = dd[1] ? 0.f : w0.y;
+    st.w0[e + 2] = dd[2] ? 0.f : w0.z;
+    st.w0[e + 3] = dd[3] ? 0.f : w0.w;
+    st.w[e] = st.w0[e] + y.x;
+    st.w[e + 1] = st.w0[e + 1] + y.y;
+    st.w[e + 2] = st.w0[e + 2] + y.z;
+    st.w[e + 3] = st.w0[e + 3] + y.w;
     st.el[e] = st.el[e + 1] = st.el[e + 2] = st.el[e + 3] = 0.f;
+    st.dl[e] = st.dl[e + 1] = st.dl[e + 2] = st.dl[e + 3] = 0.f;
   }
   st.s = 1.0f; st.inv = 1.0f; st.z = 0.0f;
   if constexpr (G == 0) {  // one group per row: grid taken from the original row beforehand
@@ -199,8 +211,10 @@ __global__ __launch_bounds__(CTHREADS) void gptq_block_kernel(ColArgs a, int64_t
 
   if (live) {
 #pragma unroll
-    for (int e = 0; e < CPL; e += 4)
+    for (int e = 0; e < CPL; e += 4) {
       *(float4*)(a.W + r * a.in + col + e) = make_float4(st.el[e], st.el[e + 1], st.el[e + 2], st.el[e + 3]);
+      *(float4*)(a.D + r * a.in + col + e) = make_float4(st.dl[e], st.dl[e + 1], st.dl[e + 2], st.dl[e + 3]);
+    }
   }
   __syncthreads();
   // pack this row's B codes: bits * B / 32 whole words starting at word j0 * bits / 32
@@ -292,7 +306,7 @@ ColKernel pick_kernel(int B, int G) {
 }
 
 struct Layout {
-  size_t f, t, y, dead, scal, flag, tmp, tmp2, total;
+  size_t f, t, y, d, dead, scal, flag, tmp, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -301,13 +315,13 @@ Layout layout(int64_t out, int64_t in, int B, bool with_loss) {
   Layout L;
   size_t o = 0;
   L.f = o;    o = align256(o + (size_t)in * in * sizeof(float));
-  L.t = o;    o = align256(o + ((size_t)in * in / 4 + (size_t)in * 64) * sizeof(float));
+  L.t = o;    o = align256(o + (size_t)in * 64 * sizeof(float));
   L.y = o;    o = align256(o + (size_t)out * B * sizeof(float));
+  L.d = o;    o = align256(o + (size_t)out * in * sizeof(float));
   L.dead = o; o = align256(o + (size_t)in);
   L.scal = o; o = align256(o + 8 * sizeof(double));
   L.flag = o; o = align256(o + 4 * sizeof(int));
   L.tmp = o;  if (with_loss) o = align256(o + (size_t)out * in * sizeof(float));
-  L.tmp2 = o; if (with_loss) o = align256(o + (size_t)out * in * sizeof(float));
   L.total = o;
   return L;
 }
@@ -366,6 +380,7 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
   float* F = (float*)(base + L.f);
   float* T = (float*)(base + L.t);
   float* Y = (float*)(base + L.y);
+  float* Dm = (float*)(base + L.d);
   uint8_t* dead = (uint8_t*)(base + L.dead);
   double* scal = (double*)(base + L.scal);
   int* flag = (int*)(base + L.flag);
@@ -373,10 +388,10 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
   KQ_TRY(fill_u32((uint32_t*)scal, 16, 0u, s));
   KQ_TRY(fill_u32((uint32_t*)flag, 4, 0u, s));
   KQ_TRY(fill_f32(Y, out * B, 0.f, s));
-  KQ_TRY(damp_and_factor(HX_rot, F, T, dead, scal, flag, in, p->damp, s));
+  KQ_TRY(damp_and_factor(HX_rot, F, T, dead, scal, flag, in, p->damp, B, s));
 
   ColArgs a;
-  a.W = W_rot; a.out = out; a.in = in; a.Y = Y; a.U = F; a.dead = dead;
+  a.W = W_rot; a.out = out; a.in = in; a.Y = Y; a.D = Dm; a.U = F; a.dead = dead;
   a.bits = p->bits; a.maxq = (float)((1 << p->bits) - 1);
   a.ngroups = in / p->group; a.scales = scales; a.zeros = zeros;
   a.packed = packed; a.codes = codes_opt;
@@ -390,9 +405,9 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
     if (j0 > 0) {
       GemmArgs g{};
       g.M = out; g.N = B; g.K = j0;
-      g.A = W_rot; g.lda = in; g.transA = false;
+      g.A = Dm; g.lda = in; g.transA = false;
       g.B = F + j0; g.ldb = in; g.transB = false;
-      g.C = Y; g.ldc = B; g.alpha = -1.0f; g.accumulate = true; g.upper_only = false;
+      g.C = Y; g.ldc = B; g.alpha = 1.0f; g.accumulate = true; g.upper_only = false;
       const int64_t tiles = ceil_div(out, 128);
       int64_t split = (2 * cus + tiles - 1) / tiles;
       const int64_t max_split = ceil_div(j0, 256);
@@ -406,8 +421,8 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
   }
 
   if (with_loss) {
-    float* dW = (float*)(base + L.tmp);
-    float* tmp = (float*)(base + L.tmp2);
+    const float* dW = Dm;   // W~ - Qhat
+    float* tmp = (float*)(base + L.tmp);
     // predicted loss  sum_j e_j^T H~_G e_j
     if (HG_rot) {
       GemmArgs r{};
@@ -419,14 +434,11 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
       dot_kernel<<<dim3(1024), dim3(256), 0, s>>>(W_rot, W_rot, out * in, scal + 2);
       KQ_LAUNCHED("dot_kernel");
     }
-    // dW = E U  (= W~ - Qhat), tmp = dW H~_X (undamped), direct loss sum (tmp dW^T) .* H~_G
-    GemmArgs g{};
-    g.M = out; g.N = in; g.K = in;
-    g.A = W_rot; g.lda = in; g.B = F; g.ldb = in; g.C = dW; g.ldc = in;
-    g.alpha = 1.0f; g.split_k = 1;
-    KQ_TRY(gemm_f32(g, s));
-    GemmArgs h = g;
-    h.A = dW; h.B = HX_rot; h.C = tmp;
+    // tmp = dW H~_X (undamped), direct loss sum (tmp dW^T) .* H~_G
+    GemmArgs h{};
+    h.M = out; h.N = in; h.K = in;
+    h.A = dW; h.lda = in; h.B = HX_rot; h.ldb = in; h.C = tmp; h.ldc = in;
+    h.alpha = 1.0f; h.split_k = 1;
     KQ_TRY(gemm_f32(h, s));
     if (HG_rot) {
       GemmArgs r{};

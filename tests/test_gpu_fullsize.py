@@ -96,9 +96,11 @@ def test_c5_llama3_70b_up_proj():
     scale = np.sqrt(hg_diag[i] * hg_diag[j])
     assert np.max(np.abs(g["HG_samples"] - ref) / scale) <= 1e-5
     del bg, Gi, Gj
+    # traces to the same 1e-5 as the entries: every entry of the 28672-wide H_G sums all
+    # 262144 tokens in one fp32 accumulator (one token split fills the GPU at this width)
     tx = o.trace(HX)
-    assert g["sens"][0] == pytest.approx(tx, rel=1e-6)
-    assert g["sens"][1] == pytest.approx(float(np.sum(hg_diag)), rel=1e-6)
+    assert g["sens"][0] == pytest.approx(tx, rel=1e-5)
+    assert g["sens"][1] == pytest.approx(float(np.sum(hg_diag)), rel=1e-5)
     Wt, HXt, _, d_in, d_out = o.biip(W.astype(np.float64), HX, None, s_in, s_out, cfg.alpha,
                                      o.BIIP_FULL, cfg.had_in, cfg.had_out, hg_diag=hg_diag)
     assert rel_fro(g["d_in"], d_in) <= 1e-5 and rel_fro(g["d_out"], d_out) <= 1e-5
