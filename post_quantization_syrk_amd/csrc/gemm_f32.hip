@@ -9,6 +9,8 @@
 // and a reduction epilogue sum(alpha * AB .* D) into an fp64 accumulator.
 #include "kq_internal.h"
 
+#include <stdlib.h>
+
 namespace kq {
 namespace {
 
@@ -251,12 +253,266 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(Args a) {
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Direct-to-LDS kernel for C (+)= alpha A B with A row-major M x K and B row-major K x N (the
+// GPTQ feedback product).  Both tiles are copied into LDS as they lie in memory by the load
+// unit (global_load_lds, 16 bytes per lane) into a ring of four 32-deep K stages (128 KB).
+// The MFMA (v_mfma_f32_32x32x2f32) sums over its two k slots, so the lane half h of every
+// k step can take any true k as long as A and B agree: half h takes k = 16 h + s for the
+// 16 steps s of a stage.  A lane then needs 16 consecutive floats of one A row (four 16-byte
+// reads) and 16 rows of one B column.  A rows (32 floats) hold their 16-byte chunks at slot
+// chunk ^ ((row >> 1) & 7), B rows (128 floats) at chunk ^ (8 * ((k >> 4) & 1)), which
+// makes both reads conflict-free.  Chunks outside the matrix are read from a zero chunk, so
+// every wave issues the same number of copies per stage and the vmcnt waits are exact.
+// ---------------------------------------------------------------------------------------------
+constexpr int DBK = 32;               // k per stage
+constexpr int DSA = MT * DBK;         // floats of the A tile of a stage
+constexpr int DSB = DBK * NTL;        // floats of the B tile of a stage
+constexpr int DSTG = DSA + DSB;       // 32 KB per stage
+constexpr int DRING = 4;
+
+__device__ __attribute__((aligned(16))) float g_zero_chunk_f32[4];
+
+struct DArgs {
+  int64_t M, N, K;
+  const float* A; int64_t lda;
+  const float* B; int64_t ldb;
+  float* C; int64_t ldc;
+  float alpha;
+  int accumulate, split_k;
+  int64_t k_per_split;
+};
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+constexpr int gwait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int GWAIT_LGKM0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+__device__ __forceinline__ void gbarrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void gcopy(const float* src, float* dst) {
+  __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst,
+                                   16, 0, 0);
+}
+
+__global__ __launch_bounds__(THREADS) void gemm_nn_dma_kernel(DArgs a) {
+  __shared__ __attribute__((aligned(1024))) float r0[DSTG];
+  __shared__ __attribute__((aligned(1024))) float r1[DSTG];
+  __shared__ __attribute__((aligned(1024))) float r2[DSTG];
+  __shared__ __attribute__((aligned(1024))) float r3[DSTG];
+  const int64_t m0 = (int64_t)blockIdx.x * MT, n0 = (int64_t)blockIdx.y * NTL;
+  const int64_t kbeg = (int64_t)blockIdx.z * a.k_per_split;
+  const int64_t kend = min(a.K, kbeg + a.k_per_split);
+  if (kbeg >= kend) return;
+  const int nst = (int)(((kend - kbeg + DBK - 1) / DBK + DRING - 1) / DRING) * DRING;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+  const float* zero = g_zero_chunk_f32;
+
+  // copy sources (stage-invariant parts): A instruction r of wave w covers rows 8p..8p+7,
+  // p = 4w + r; B instruction r covers k rows 2p, 2p+1
+  uint32_t offA[4], offB[4];
+  int chA[4], krB[4];
+  bool okA[4], okB[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int p = 4 * wave + r;
+    const int m = 8 * p + (lane >> 3);
+    const int c = (lane & 7) ^ ((m >> 1) & 7);
+    chA[r] = c;
+    offA[r] = (uint32_t)(m * a.lda + 4 * c);
+    okA[r] = m0 + m < a.M;
+    const int kr = 2 * p + (lane >> 5);
+    const int cb = (lane & 31) ^ (((kr >> 4) & 1) << 3);
+    krB[r] = kr;
+    offB[r] = (uint32_t)(kr * a.ldb + 4 * cb);
+    okB[r] = n0 + 4 * cb < a.N;
+  }
+  const float* Abase = a.A + m0 * a.lda;
+  const float* Bbase = a.B + n0;
+  auto issue = [&](int st, float* buf) {
+    const int64_t k0 = kbeg + (int64_t)st * DBK;
+    const float* ab = Abase + min(k0, kend);
+    const float* bb = Bbase + min(k0, kend) * a.ldb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool v = okA[r] && k0 + 4 * chA[r] < kend;
+      gcopy(v ? ab + offA[r] : zero, buf + (4 * wave + r) * 256);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool v = okB[r] && k0 + krB[r] < kend;
+      gcopy(v ? bb + offB[r] : zero, buf + DSA + (4 * wave + r) * 256);
+    }
+  };
+
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  // operand read offsets (floats) inside a stage buffer
+  int oa[2][4], ob[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = wm + 32 * i + l32;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) oa[i][t] = m * DBK + 4 * ((4 * h + t) ^ ((m >> 1) & 7));
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = wn + 32 * j + l32;
+    ob[j] = DSA + 16 * h * NTL + 4 * ((n >> 2) ^ (h << 3)) + (n & 3);
+  }
+  float xa[2][16], xb[2][16], ya[2][16], yb[2][16];
+  auto read = [&](const float* buf, float (&av)[2][16], float (&bv)[2][16]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float4 v = *(const float4*)(buf + oa[i][t]);
+        av[i][4 * t] = v.x; av[i][4 * t + 1] = v.y; av[i][4 * t + 2] = v.z; av[i][4 * t + 3] = v.w;
+      }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) bv[j][s2] = buf[ob[j] + s2 * NTL];
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  auto mma = [&](const float (&av)[2][16], const float (&bv)[2][16]) {
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i][s2], bv[j][s2], acc[i][j], 0, 0, 0);
+  };
+
+  issue(0, r0);
+  issue(1, r1);
+  issue(2, r2);
+  issue(3, r3);
+  __builtin_amdgcn_s_waitcnt(gwait_vm(16));   // stages 0 and 1 of this wave
+  gbarrier();
+  read(r0, xa, xb);
+  __builtin_amdgcn_s_waitcnt(GWAIT_LGKM0);
+  gbarrier();
+
+  // Step s (operands of stage s in registers, stage s+1 visible): refill stage s's buffer
+  // with stage s + 4, multiply stage s while reading stage s+1, wait for this wave's copies of
+  // stage s+2 and every wave's reads of stage s+1.
+#define KQ_G_STEP(J, CUR, NXT, RA, RB, NA, NB)                     \
+  {                                                                \
+    issue(s0 + (J) + DRING, CUR);                                  \
+    read(NXT, NA, NB);                                             \
+    mma(RA, RB);                                                   \
+    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {             \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);           \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           \
+      __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);           \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           \
+    }                                                              \
+    __builtin_amdgcn_sched_barrier(0);                             \
+    __builtin_amdgcn_s_waitcnt(gwait_vm(16));                      \
+    __builtin_amdgcn_s_waitcnt(GWAIT_LGKM0);                       \
+    gbarrier();                                                    \
+  }
+  for (int s0 = 0; s0 < nst; s0 += DRING) {
+    KQ_G_STEP(0, r0, r1, xa, xb, ya, yb)
+    KQ_G_STEP(1, r1, r2, ya, yb, xa, xb)
+    KQ_G_STEP(2, r2, r3, xa, xb, ya, yb)
+    KQ_G_STEP(3, r3, r0, ya, yb, xa, xb)
+  }
+#undef KQ_G_STEP
+  __builtin_amdgcn_s_waitcnt(gwait_vm(0));
+
+  const int kh = h, rh = kh * 4;
+  if (a.split_k > 1) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t col = n0 + wn + 32 * j + l32;
+        if (col >= a.N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + rh + (r & 3);
+          if (row < a.M) atomicAdd(a.C + row * a.ldc + col, a.alpha * acc[i][j][r]);
+        }
+      }
+    return;
+  }
+  if (a.accumulate) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t col = n0 + wn + 32 * j + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + rh + (r & 3);
+          const float c = (row < a.M && col < a.N) ? a.C[row * a.ldc + col] : 0.0f;
+          acc[i][j][r] = fmaf(a.alpha, acc[i][j][r], c);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] *= a.alpha;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = n0 + wn + 32 * j + l32;
+      if (col >= a.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + rh + (r & 3);
+        if (row < a.M) a.C[row * a.ldc + col] = acc[i][j][r];
+      }
+    }
+}
+
+// 1 = direct-to-LDS kernel for plain row-major products (default), 0 = register-staged kernel
+// for every product (KQ_GEMM_VARIANT; a tuning knob, both compute the same C).
+int gemm_variant() {
+  const char* env = getenv("KQ_GEMM_VARIANT");
+  if (env && atoi(env) == 0) return 0;
+  return 1;
+}
+
 }  // namespace
 
 kq_status gemm_f32(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return KQ_OK;
   if (g.split_k < 1 || (g.split_k > 1 && !g.accumulate && !g.red))
     return fail(KQ_EINVAL, "gemm_f32: split_k > 1 needs accumulation");
+  // plain row-major products with 16-byte aligned rows take the direct-to-LDS kernel
+  const bool aligned = ((uintptr_t)g.A % 16 == 0) && ((uintptr_t)g.B % 16 == 0) &&
+                       g.lda % 4 == 0 && g.ldb % 4 == 0 && g.K % 4 == 0 && g.N % 4 == 0;
+  if (!g.transA && !g.transB && !g.a_upper && !g.b_upper && !g.upper_only && !g.red &&
+      (g.batch <= 1) && aligned && g.K > 0 && 128 * g.lda + (int64_t)DBK * g.ldb < ((int64_t)1 << 32) &&
+      gemm_variant() == 1) {
+    DArgs d;
+    d.M = g.M; d.N = g.N; d.K = g.K;
+    d.A = g.A; d.lda = g.lda; d.B = g.B; d.ldb = g.ldb; d.C = g.C; d.ldc = g.ldc;
+    d.alpha = g.alpha; d.accumulate = g.accumulate;
+    d.k_per_split = ceil_div(ceil_div(g.K, g.split_k), DBK) * DBK;
+    d.split_k = (int)ceil_div(g.K, d.k_per_split);
+    dim3 grid((unsigned)ceil_div(g.M, MT), (unsigned)ceil_div(g.N, NTL), (unsigned)d.split_k);
+    gemm_nn_dma_kernel<<<grid, dim3(THREADS), 0, s>>>(d);
+    KQ_LAUNCHED("gemm_nn_dma_kernel");
+    return KQ_OK;
+  }
   Args a;
   a.M = g.M; a.N = g.N; a.K = g.K;
   a.A = g.A; a.lda = g.lda; a.transA = g.transA;

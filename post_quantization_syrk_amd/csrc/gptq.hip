@@ -408,8 +408,10 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
       g.A = Dm; g.lda = in; g.transA = false;
       g.B = F + j0; g.ldb = in; g.transB = false;
       g.C = Y; g.ldc = B; g.alpha = 1.0f; g.accumulate = true; g.upper_only = false;
+      // one workgroup per CU (the product keeps a 128 KB LDS ring): split K so that one round
+      // of workgroups covers the GPU, with at least 256 of K per split
       const int64_t tiles = ceil_div(out, 128);
-      int64_t split = (2 * cus + tiles - 1) / tiles;
+      int64_t split = cus / tiles;
       const int64_t max_split = ceil_div(j0, 256);
       if (split > max_split) split = max_split;
       if (split < 1) split = 1;
