@@ -9,16 +9,19 @@
 // corner up; then U = R^-1, since U^T U = R^-T R^-1 = H_d^-1 and U is upper
 // with a positive diagonal.
 //
-// Reverse Cholesky, 64-column blocks from the last one up, two launches per block:
-//   panel:   R12 = A12 U22^T            (U22 = R22^-1 from the previous launch; fp32 MFMA)
-//   update:  A11 -= R12 R12^T           (fp32 MFMA, upper 128 x 128 tiles), while one extra
-//            workgroup updates the next diagonal block privately and factors it (one wave:
-//            R22 R22^T = A22; then U22 = R22^-1 by recursive doubling on all four waves),
-//            so the serial chain of small factorizations overlaps the bulk updates.
+// Reverse Cholesky, 64-column blocks from the last one up, one launch per block.  With A12
+// the current column block above the diagonal and M = A22^-1 = U22^T U22 (from the previous
+// block's leaf), each 128 x 128 tile forms Z = A12 M (= R12 U22) for its rows and subtracts
+// Z A12^T from A11 (fp32 MFMA, upper tiles); Z^T is kept in the free lower triangle.  One
+// extra workgroup of the same launch updates the next diagonal block privately and factors
+// it: one wave finds R22 R22^T = A22, all four then form U22 = R22^-1 by recursive doubling
+// and M = U22^T U22, so the serial chain of small factorizations overlaps the bulk updates.
 // Only the diagonal blocks of U are formed.  GPTQ's feedback into block J needs
 // U[<J, J] = -U[<J,<J] R[<J, J] U_JJ only through E[:, <J] U[<J, J], and
 // E[:, <J] U[<J,<J] = (W - Qhat)[:, <J] (the rounding error so far, in the layer's own
-// basis), so the factor kept for block J is P[<J, J] = R[<J, J] U_JJ.
+// basis), so the factor kept for block J is P[<J, J] = R[<J, J] U_JJ: for 64-column blocks
+// exactly Z; for 128-column blocks [Z_a, Z_b - Z_a Z_b[a rows]], the second half coupled
+// through U_ab = -U_a Z_b[a rows].
 #include "kq_internal.h"
 
 namespace kq {
@@ -75,34 +78,47 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // Leaf factorization, run by one wave: Ab (LDS, 64 x 64, row stride LB) holds the upper
 // triangle of a diagonal block A' (entries below the diagonal are ignored).  Factors
 // A' = R R^T from the last column up (R upper): lane l holds row l of A' (becoming row l of
-// R).  Step j: the lanes publish column j (col[]), p = A'_jj, R_jj = sqrt(p);
-// A'_lk -= A'_lj A'_kj / p for k < j (every lane updates its whole row; the lower part it
-// also touches is never read); R_lj = A'_lj / R_jj goes to Rl and 1 / R_jj to rsq.  Rl's
-// entries below the diagonal are left undefined.  Sets *flag on a non-positive pivot.
-__device__ __forceinline__ void leaf_factor(const float* Ab, float* Rl, float* col, float* rsq,
-                                            int* flag) {
+// R).  Step j: with column j of A' in registers (c[k] = A'_kj, from the other lanes),
+// p = A'_jj, R_jj = sqrt(p); A'_lk -= A'_lj A'_kj / p for k < j (every lane updates its whole
+// row; the lower part it also touches is never read); R_lj = A'_lj / R_jj goes to Rl and
+// 1 / R_jj to rsq.  Column j-1 is updated first and published through LDS (two buffers in
+// turn), and read back while the rest of the update runs.  Rl's entries below the diagonal
+// are left undefined.  Sets *flag on a non-positive pivot.
+__device__ __forceinline__ void leaf_factor(const float* Ab, float* Rl, float* col0, float* col1,
+                                            float* rsq, int* flag) {
   const int l = threadIdx.x & 63;
-  float a[64];
+  float a[64], c[64];
 #pragma unroll
   for (int k = 0; k < 64; k += 4) {
     const float4 v = *(const float4*)(Ab + l * LB + k);
     a[k] = v.x; a[k + 1] = v.y; a[k + 2] = v.z; a[k + 3] = v.w;
   }
+  col1[l] = a[63];
+  wave_sync();
+#pragma unroll
+  for (int k = 0; k < 64; ++k) c[k] = col1[k];
   bool bad = false;
 #pragma unroll
   for (int j = 63; j >= 0; --j) {
-    col[l] = a[j];
-    wave_sync();
-    const float p = col[j];
+    const float p = c[j];
     const float rs = rsqrtf(p);
     const float f = a[j] * (rs * rs);
+    if (j > 0) {
+      float* colx = ((j - 1) & 1) ? col1 : col0;
+      a[j - 1] = fmaf(-f, c[j - 1], a[j - 1]);
+      colx[l] = a[j - 1];
+      wave_sync();
 #pragma unroll
-    for (int k = 0; k < j; ++k) a[k] = fmaf(-f, col[k], a[k]);
+      for (int k = 0; k < j - 1; ++k) {
+        a[k] = fmaf(-f, c[k], a[k]);
+        c[k] = colx[k];
+      }
+      c[j - 1] = colx[j - 1];
+    }
     a[j] *= rs;
     Rl[l * LB + j] = a[j];
     rsq[j] = rs;
     bad |= (l == j) & !(p > 0.0f);
-    wave_sync();
   }
   if (bad) atomicOr(flag, 1);
 }
@@ -184,126 +200,115 @@ __device__ __forceinline__ void leaf_inverse(const float* Rl, const float* rsq, 
   __syncthreads();
 }
 
+// Swizzled slabs of 64 columns in LDS (no padding).  Element (r, k) of a slab read by the MFMA
+// with lanes along r (32 rows at one k; the other half wave at k + 1) sits at
+// r * 64 + (k ^ (2 r & 62)), which puts the 64 lanes on 64 distinct banks.
+__device__ __forceinline__ int sw(int r, int k) { return r * 64 + (k ^ ((2 * r) & 62)); }
+// A 64 x 64 matrix read with lanes along columns (B operand): odd rows shifted by 32 columns.
+__device__ __forceinline__ int swb(int k, int c) { return k * 64 + (c ^ ((k & 1) << 5)); }
+
 // LDS for a leaf: X (64 x LB: A', then U) and Y (64 x LB for R, 64 + 64 for the column and
 // 1 / R_jj, 32 x LB scratch).
 constexpr int LEAF_Y = 64 * LB + 128 + 32 * LB;
 
-// Factor + invert the diagonal block held in X; U goes to out (64 x 64 row-major).
-// Every thread of the 256-thread workgroup calls it.
-__device__ __forceinline__ void leaf(float* X, float* Y, float* __restrict__ out, int* flag) {
+// Factor + invert the diagonal block held in X.  Writes U = R^-1 to Uout and
+// M = U^T U = A'^-1 to Mout (64 x 64 row-major each).  Every thread of the 256-thread
+// workgroup calls it.
+__device__ __forceinline__ void leaf(float* X, float* Y, float* __restrict__ Uout,
+                                     float* __restrict__ Mout, int* flag) {
   float* Rl = Y;
   float* col = Y + 64 * LB;
   float* rsq = col + 64;
-  float* Ts = rsq + 64;
-  if (threadIdx.x < 64) leaf_factor(X, Rl, col, rsq, flag);
+  float* Ts = rsq + 64;   // also the factor's second column buffer (Ts is used afterwards)
+  if (threadIdx.x < 64) leaf_factor(X, Rl, col, Ts, rsq, flag);
   __syncthreads();
   leaf_inverse(Rl, rsq, X, Ts);
-  for (int q = threadIdx.x; q < 64 * 64; q += 256) out[q] = X[(q >> 6) * LB + (q & 63)];
+  // M = U^T U; wave (wi, wj) forms its 32 x 32 quadrant: A[i][k] = U[k][i], B[k][j] = U[k][j]
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63, l32 = lane & 31, kh = lane >> 5;
+  const int wi = w >> 1, wj = w & 1;
+  f32x16 acc = f32x16{};
+#pragma unroll 8
+  for (int k = 0; k < 64; k += 2)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(X[(k + kh) * LB + 32 * wi + l32],
+                                               X[(k + kh) * LB + 32 * wj + l32], acc, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    Mout[(32 * wi + 8 * (r >> 2) + 4 * kh + (r & 3)) * 64 + 32 * wj + l32] = acc[r];
+  for (int q = t; q < 64 * 64; q += 256) Uout[q] = X[(q >> 6) * LB + (q & 63)];
 }
 
 // The last diagonal block [s0, s0 + 64), factored on its own.
 __global__ __launch_bounds__(256) void leaf_kernel(const float* __restrict__ F, int64_t n,
                                                    int64_t s0, float* __restrict__ Uout,
+                                                   float* __restrict__ Mout,
                                                    int* __restrict__ flag) {
   __shared__ __attribute__((aligned(16))) float X[64 * LB];
   __shared__ __attribute__((aligned(16))) float Y[LEAF_Y];
   for (int q = threadIdx.x; q < 64 * 64; q += 256)
     X[(q >> 6) * LB + (q & 63)] = F[(s0 + (q >> 6)) * n + s0 + (q & 63)];
   __syncthreads();
-  leaf(X, Y, Uout, flag);
+  leaf(X, Y, Uout, Mout, flag);
 }
 
-// Panel R12 = A12 U22^T for rows [128 b, 128 b + 128) of [0, s0) and columns [s0, s0 + 64),
-// in place (each workgroup reads and writes its own rows).  U22 = R22^-1 comes from the
-// block buffer.  4 waves, each 32 rows x 64 columns of v_mfma_f32_32x32x2f32.
-__global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ F, int64_t n, int64_t s0,
-                                                    const float* __restrict__ U22) {
-  __shared__ float As[128 * LP];
-  __shared__ float Us[64 * LP];
-  const int t = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.x * 128;
-  for (int q = t; q < 128 * 16; q += 256) {
-    const int r = q >> 4, c4 = (q & 15) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (r0 + r < s0) v = *(const float4*)(F + (r0 + r) * n + s0 + c4);
-    float* d = As + r * LP + c4;
-    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-  }
-  for (int q = t; q < 64 * 16; q += 256) {
-    const int r = q >> 4, c4 = (q & 15) * 4;
-    const float4 v = *(const float4*)(U22 + r * 64 + c4);
-    float* d = Us + r * LP + c4;
-    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-  }
-  __syncthreads();
-  const int lane = t & 63, w = t >> 6, l32 = lane & 31, kh = lane >> 5;
-  f32x16 acc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    float av[16], bv[16][2];
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const int k = 32 * h + 2 * kk + kh;
-      av[kk] = As[(32 * w + l32) * LP + k];
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) bv[kk][jb] = Us[(32 * jb + l32) * LP + k];   // U22[c][k]
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk)
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-        acc[jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[kk], bv[kk][jb], acc[jb], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#pragma unroll
-  for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t row = r0 + 32 * w + 8 * (r >> 2) + 4 * kh + (r & 3);
-      if (row < s0) F[row * n + s0 + 32 * jb + l32] = acc[jb][r];
-    }
-}
-
-// Trailing update A11 -= R12 R12^T, R12 = F[0:s0, s0:s0+64], over the upper 128 x 128 tiles
-// of [0, s0)^2.  The next diagonal block D = [s0-64, s0)^2 is left alone by these tiles:
-// workgroup 0 instead forms D - R_D R_D^T (R_D = rows s0-64.. of R12) privately and factors
-// it (leaf), so the next block's factorization overlaps the bulk update.  Its U goes to Unext.
-// Tiles: 4 waves of 64 x 64 (2 x 2 v_mfma_f32_32x32x2f32 blocks), K = 64 in one LDS stage;
-// the tile's old values are loaded first so their latency overlaps the operand loads.
+// Step of the reverse factorization at block [s0, s0 + 64).  With A12 = F[0:s0, s0:s0+64]
+// (the current Schur complement's column block) and M = A22^-1 = U22^T U22 from the previous
+// step's leaf, the block's panel factor is Z = A12 M (= R12 U22 with R12 = A12 U22^T) and the
+// trailing update is A11 -= A12 M A12^T = Z A12^T.  Z is GPTQ's feedback factor P for this
+// 64-column block; it is stored transposed in the free lower triangle, F[s0 + c][r] = Z[r][c].
+// Tiles (upper 128 x 128 of [0, s0)^2): Z for the tile's rows (A12[I] M), then
+// C -= Z[I] A12[K]^T; the diagonal tiles also store Z^T.  The next diagonal block
+// D = [s0-64, s0)^2 is left alone by the tiles: workgroup 0 forms D - Z_D A12[D]^T privately
+// and factors it (leaf), so the next block's factorization overlaps the bulk update.
+// 4 waves of v_mfma_f32_32x32x2f32; K = 64 in one LDS stage; the tile's old values are loaded
+// first so their latency overlaps the operand loads.
 __global__ __launch_bounds__(256) void update_kernel(float* __restrict__ F, int64_t n, int64_t s0,
+                                                     const float* __restrict__ Mcur,
                                                      float* __restrict__ Unext,
+                                                     float* __restrict__ Mnext,
                                                      int* __restrict__ flag) {
-  __shared__ __attribute__((aligned(16))) float As[128 * LP];
-  __shared__ __attribute__((aligned(16))) float Bs[128 * LP];
+  __shared__ __attribute__((aligned(16))) float As[128 * 64];
+  __shared__ __attribute__((aligned(16))) float Bs[128 * 64];
+  __shared__ __attribute__((aligned(16))) float Ms[64 * 64];
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6, l32 = lane & 31, kh = lane >> 5;
   const int64_t d0 = s0 - 64;
+  for (int q = t; q < 64 * 16; q += 256) {
+    const int r = q >> 4, c4 = (q & 15) * 4;
+    const float4 v = *(const float4*)(Mcur + r * 64 + c4);
+    Ms[swb(r, c4)] = v.x; Ms[swb(r, c4 + 1)] = v.y; Ms[swb(r, c4 + 2)] = v.z; Ms[swb(r, c4 + 3)] = v.w;
+  }
   if (blockIdx.x == 0) {
-    // R_D (64 x 64) into As (stride LP); D into Bs (stride LB, the leaf's layout)
+    // A12[D] -> As rows 0..63, D -> Bs as the leaf's X (row stride LB)
     for (int q = t; q < 64 * 16; q += 256) {
       const int r = q >> 4, c4 = (q & 15) * 4;
       const float4 v = *(const float4*)(F + (d0 + r) * n + s0 + c4);
-      float* d = As + r * LP + c4;
-      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+      As[sw(r, c4)] = v.x; As[sw(r, c4 + 1)] = v.y; As[sw(r, c4 + 2)] = v.z; As[sw(r, c4 + 3)] = v.w;
       *(float4*)(Bs + r * LB + c4) = *(const float4*)(F + (d0 + r) * n + d0 + c4);
     }
     __syncthreads();
-    // wave (wi, wj) forms the 32 x 32 block (wi, wj) of D - R_D R_D^T
     const int wi = w >> 1, wj = w & 1;
+    // Z_D = A12[D] M into As rows 64..127
     f32x16 acc = f32x16{};
 #pragma unroll 8
     for (int k = 0; k < 64; k += 2)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[(32 * wi + l32) * LP + k + kh],
-                                                 As[(32 * wj + l32) * LP + k + kh], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[sw(32 * wi + l32, k + kh)],
+                                                 Ms[swb(k + kh, 32 * wj + l32)], acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) As[sw(64 + 32 * wi + 8 * (r >> 2) + 4 * kh + (r & 3), 32 * wj + l32)] = acc[r];
+    __syncthreads();
+    // D' = D - Z_D A12[D]^T
+    f32x16 acc2 = f32x16{};
+#pragma unroll 8
+    for (int k = 0; k < 64; k += 2)
+      acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(As[sw(64 + 32 * wi + l32, k + kh)],
+                                                  As[sw(32 * wj + l32, k + kh)], acc2, 0, 0, 0);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = 32 * wi + 8 * (r >> 2) + 4 * kh + (r & 3);
-      float* d = Bs + row * LB + 32 * wj + l32;
-      *d = *d - acc[r];
+      float* d = Bs + (32 * wi + 8 * (r >> 2) + 4 * kh + (r & 3)) * LB + 32 * wj + l32;
+      *d = *d - acc2[r];
     }
     __syncthreads();
-    leaf(Bs, As, Unext, flag);
+    leaf(Bs, As, Unext, Mnext, flag);
     return;
   }
   // upper tile (tm, tn), tm <= tn, enumerated row by row
@@ -327,38 +332,66 @@ __global__ __launch_bounds__(256) void update_kernel(float* __restrict__ F, int6
         const int ro = 32 * i + 8 * (r >> 2) + (r & 3);
         cv[i][j][r] = (ro < rlim && 32 * j < clim) ? cptr[(int64_t)ro * n + 32 * j] : 0.0f;
       }
-  const bool same = tm == tn;
   for (int q = t; q < 128 * 16; q += 256) {
     const int r = q >> 4, c4 = (q & 15) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f), u = v;
     if (i0 + r < s0) v = *(const float4*)(F + (i0 + r) * n + s0 + c4);
-    float* d = As + r * LP + c4;
-    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-    if (!same) {
-      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (j0 + r < s0) u = *(const float4*)(F + (j0 + r) * n + s0 + c4);
-      float* e = Bs + r * LP + c4;
-      e[0] = u.x; e[1] = u.y; e[2] = u.z; e[3] = u.w;
-    }
+    if (j0 + r < s0) u = *(const float4*)(F + (j0 + r) * n + s0 + c4);
+    As[sw(r, c4)] = v.x; As[sw(r, c4 + 1)] = v.y; As[sw(r, c4 + 2)] = v.z; As[sw(r, c4 + 3)] = v.w;
+    Bs[sw(r, c4)] = u.x; Bs[sw(r, c4 + 1)] = u.y; Bs[sw(r, c4 + 2)] = u.z; Bs[sw(r, c4 + 3)] = u.w;
   }
   __syncthreads();
-  const float* Bp = same ? As : Bs;
+  // Z[I] = A12[I] M: wave w forms rows 32 w .. 32 w + 31, all 64 columns
+  {
+    f32x16 az[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      float av[16], bv[16][2];
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        const int k = 32 * hh + 2 * kk + kh;
+        av[kk] = As[sw(32 * w + l32, k)];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bv[kk][j] = Ms[swb(k, 32 * j + l32)];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          az[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[kk], bv[kk][j], az[j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) As[sw(32 * w + 8 * (r >> 2) + 4 * kh + (r & 3), 32 * j + l32)] = az[j][r];
+    __syncthreads();
+  }
+  if (tm == tn) {
+    // Z^T of the tile's rows into the lower triangle: F[s0 + c][i0 + i] = Z[i][c]
+    for (int q = t; q < 128 * 64; q += 256) {
+      const int i = q & 127, c = q >> 7;
+      if (i0 + i < s0) F[(s0 + c) * n + i0 + i] = As[sw(i, c)];
+    }
+  }
+  // C -= Z[I] A12[K]^T in two halves of 32 k; each half's operands are read before its MFMAs
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-  // two halves of 32 k; each half's operands are read before its multiplies
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int hh = 0; hh < 2; ++hh) {
     float av[16][2], bv[16][2];
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
-      const int k = 32 * h + 2 * kk + kh;
+      const int k = 32 * hh + 2 * kk + kh;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) av[kk][i] = As[(wm + 32 * i + l32) * LP + k];
+      for (int i = 0; i < 2; ++i) av[kk][i] = As[sw(wm + 32 * i + l32, k)];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bv[kk][j] = Bp[(wn + 32 * j + l32) * LP + k];
+      for (int j = 0; j < 2; ++j) bv[kk][j] = Bs[sw(wn + 32 * j + l32, k)];
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -384,32 +417,25 @@ __global__ __launch_bounds__(256) void update_kernel(float* __restrict__ F, int6
       }
 }
 
-// Clears the strictly lower triangle and moves each diagonal block's U_JJ from the block
-// buffer into place.
+// Moves each diagonal block's U_JJ from the block buffer into place.
 __global__ void finalize_kernel(float* __restrict__ F, int64_t n, const float* __restrict__ Ubuf) {
-  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t k = blockIdx.y;
-  if (j >= n) return;
-  const int64_t bk = k >> 6, bj = j >> 6;
-  if (bj == bk) F[k * n + j] = Ubuf[bk * 4096 + (k & 63) * 64 + (j & 63)];
-  else if (j < k) F[k * n + j] = 0.0f;
+  const int64_t b = blockIdx.x;
+  for (int q = threadIdx.x; q < 64 * 64; q += 256)
+    F[(64 * b + (q >> 6)) * n + 64 * b + (q & 63)] = Ubuf[b * 4096 + q];
 }
 
 // For GPTQ blocks of 128 columns, the 128 x 128 diagonal block of U = R^-1 from its two
-// 64-blocks: U_ab = -U_a R_ab U_b (written over R_ab).  One workgroup per 128-block; each wave
-// forms a 32 x 32 quadrant of each product (v_mfma_f32_32x32x2f32).
+// 64-blocks a, b: U_ab = -U_a R_ab U_b = -U_a Z_b[a rows] (Z_b^T lies in the lower triangle).
+// One workgroup per 128-block; each wave forms a 32 x 32 quadrant (v_mfma_f32_32x32x2f32).
 __global__ __launch_bounds__(256) void ujj128_kernel(float* __restrict__ F, int64_t n) {
   __shared__ float Ua[64 * LP];
-  __shared__ float Rab[64 * LP];
-  __shared__ float Ub[64 * LP];
-  __shared__ float Ts[64 * LP];
+  __shared__ float Zs[64 * LP];
   const int t = threadIdx.x, w = t >> 6, lane = t & 63, l32 = lane & 31, kh = lane >> 5;
   const int64_t a0 = (int64_t)blockIdx.x * 128, b0 = a0 + 64;
   for (int q = t; q < 64 * 64; q += 256) {
     const int r = q >> 6, c = q & 63;
     Ua[r * LP + c] = F[(a0 + r) * n + a0 + c];
-    Rab[r * LP + c] = F[(a0 + r) * n + b0 + c];
-    Ub[r * LP + c] = F[(b0 + r) * n + b0 + c];
+    Zs[c * LP + r] = F[(b0 + r) * n + a0 + c];   // Z_b[a0 + c][r] stored at F[b0 + r][a0 + c]
   }
   __syncthreads();
   const int wi = w >> 1, wj = w & 1;
@@ -417,83 +443,66 @@ __global__ __launch_bounds__(256) void ujj128_kernel(float* __restrict__ F, int6
 #pragma unroll 8
   for (int k = 0; k < 64; k += 2)
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Ua[(32 * wi + l32) * LP + k + kh],
-                                               Rab[(k + kh) * LP + 32 * wj + l32], acc, 0, 0, 0);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) Ts[(32 * wi + 8 * (r >> 2) + 4 * kh + (r & 3)) * LP + 32 * wj + l32] = acc[r];
-  __syncthreads();
-  f32x16 acc2 = f32x16{};
-#pragma unroll 8
-  for (int k = 0; k < 64; k += 2)
-    acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(Ts[(32 * wi + l32) * LP + k + kh],
-                                                Ub[(k + kh) * LP + 32 * wj + l32], acc2, 0, 0, 0);
+                                               Zs[(k + kh) * LP + 32 * wj + l32], acc, 0, 0, 0);
 #pragma unroll
   for (int r = 0; r < 16; ++r)
-    F[(a0 + 32 * wi + 8 * (r >> 2) + 4 * kh + (r & 3)) * n + b0 + 32 * wj + l32] = -acc2[r];
+    F[(a0 + 32 * wi + 8 * (r >> 2) + 4 * kh + (r & 3)) * n + b0 + 32 * wj + l32] = -acc[r];
 }
 
-// GPTQ feedback factors P[<J, J] = R[<J, J] U_JJ for every column block J of width B, in place
-// over R (one workgroup per (row tile i, block J) with i < J; tiles of B x B, K = B).
-// Waves: B = 128, 64 x 64 each (2 x 2 MFMA blocks); B = 64, 32 x 32 each.
+// GPTQ feedback factors P[<J, J] above each B x B diagonal block, from the Z^T of the
+// factorization (lower triangle).  B = 64: P = Z.  B = 128 (blocks a, b):
+// P = [Z_a, Z_b - Z_a Z_b[a rows]].  One workgroup per (128-row tile, block J) with the tile
+// above the block; 4 waves of v_mfma_f32_32x32x2f32 for the B = 128 correction.
 template <int B>
 __global__ __launch_bounds__(256) void pmat_kernel(float* __restrict__ F, int64_t n) {
-  constexpr int LDQ = B + 1;
-  constexpr int WT = B / 2;           // wave tile edge
-  constexpr int NBK = WT / 32;        // 32 x 32 blocks per wave edge
-  __shared__ float Rs[B * LDQ];
-  __shared__ float Us[B * LDQ];
+  __shared__ float Za[128 * LP];
+  __shared__ float Zb[B == 128 ? 128 * LP : 4];
+  __shared__ float Zba[B == 128 ? 64 * LP : 4];
   int idx = blockIdx.x, J = 1;
-  while (idx >= J) { idx -= J; ++J; }
-  const int64_t r0 = (int64_t)idx * B, c0 = (int64_t)J * B;
-  const int t = threadIdx.x, w = t >> 6, lane = t & 63, l32 = lane & 31, kh = lane >> 5;
-  for (int q = t; q < B * B / 4; q += 256) {
-    const int r = q / (B / 4), c4 = 4 * (q % (B / 4));
-    const float4 v = *(const float4*)(F + (r0 + r) * n + c0 + c4);
-    const float4 u = *(const float4*)(F + (c0 + r) * n + c0 + c4);
-    float* d = Rs + r * LDQ + c4;
-    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-    float* e = Us + r * LDQ + c4;
-    // U_JJ is upper triangular; entries below its diagonal are not U's
-    e[0] = c4 + 0 >= r ? u.x : 0.0f;
-    e[1] = c4 + 1 >= r ? u.y : 0.0f;
-    e[2] = c4 + 2 >= r ? u.z : 0.0f;
-    e[3] = c4 + 3 >= r ? u.w : 0.0f;
+  // tiles of 128 rows above block J: ceil(J * B / 128)
+  for (;;) {
+    const int nt = (J * B + 127) / 128;
+    if (idx < nt) break;
+    idx -= nt;
+    ++J;
+  }
+  const int64_t r0 = (int64_t)idx * 128, a0 = (int64_t)J * B, rows = min((int64_t)128, a0 - r0);
+  const int t = threadIdx.x;
+  for (int q = t; q < 64 * 128; q += 256) {
+    const int c = q >> 7, r = q & 127;   // lanes along r: coalesced reads of Z^T rows
+    Za[r * LP + c] = r < rows ? F[(a0 + c) * n + r0 + r] : 0.0f;
+    if constexpr (B == 128) Zb[r * LP + c] = r < rows ? F[(a0 + 64 + c) * n + r0 + r] : 0.0f;
+  }
+  if constexpr (B == 128) {
+    for (int q = t; q < 64 * 64; q += 256) {
+      const int c = q >> 6, r = q & 63;
+      Zba[r * LP + c] = F[(a0 + 64 + c) * n + a0 + r];
+    }
   }
   __syncthreads();
-  const int wm = (w >> 1) * WT, wn = (w & 1) * WT;
-  f32x16 acc[NBK][NBK];
-#pragma unroll
-  for (int i = 0; i < NBK; ++i)
-#pragma unroll
-    for (int j = 0; j < NBK; ++j) acc[i][j] = f32x16{};
-#pragma unroll
-  for (int h = 0; h < B / 32; ++h) {
-    float av[16][NBK], bv[16][NBK];
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const int k = 32 * h + 2 * kk + kh;
-#pragma unroll
-      for (int i = 0; i < NBK; ++i) av[kk][i] = Rs[(wm + 32 * i + l32) * LDQ + k];
-#pragma unroll
-      for (int j = 0; j < NBK; ++j) bv[kk][j] = Us[k * LDQ + wn + 32 * j + l32];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk)
-#pragma unroll
-      for (int i = 0; i < NBK; ++i)
-#pragma unroll
-        for (int j = 0; j < NBK; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[kk][i], bv[kk][j], acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int q = t; q < 128 * 64; q += 256) {
+    const int r = q >> 6, c = q & 63;
+    if (r < rows) F[(r0 + r) * n + a0 + c] = Za[r * LP + c];
   }
+  if constexpr (B == 128) {
+    const int w = t >> 6, lane = t & 63, l32 = lane & 31, kh = lane >> 5;
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll 4
+    for (int k = 0; k < 64; k += 2) {
+      const float av = Za[(32 * w + l32) * LP + k + kh];
 #pragma unroll
-  for (int i = 0; i < NBK; ++i)
+      for (int j = 0; j < 2; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, Zba[(k + kh) * LP + 32 * j + l32], acc[j],
+                                                      0, 0, 0);
+    }
 #pragma unroll
-    for (int j = 0; j < NBK; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        F[(r0 + wm + 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3)) * n + c0 + wn + 32 * j + l32] =
-            acc[i][j][r];
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * w + 8 * (r >> 2) + 4 * kh + (r & 3), c = 32 * j + l32;
+        if (row < rows) F[(r0 + row) * n + a0 + 64 + c] = Zb[row * LP + c] - acc[j][r];
+      }
+  }
 }
 
 }  // namespace
@@ -501,7 +510,7 @@ __global__ __launch_bounds__(256) void pmat_kernel(float* __restrict__ F, int64_
 // Copies HX into the workspace matrix F, damps it and factors it (H_d = R R^T).  On return F
 // holds, above its B x B diagonal blocks, GPTQ's feedback factors P = R[<J, J] U_JJ, and in
 // those blocks U_JJ (U = R^-1 = chol_upper(H_d^-1)); the strictly lower triangle is zero.
-// T is scratch of 64 n floats.
+// T is scratch of 128 n floats.
 kq_status damp_and_factor(const float* HX, float* F, float* T, uint8_t* dead, double* lam,
                           int* flag, int64_t n, float damp, int B, hipStream_t s) {
   if (n % NB != 0) return fail(KQ_ESHAPE, "factorization needs n %% %d == 0", NB);
@@ -511,35 +520,34 @@ kq_status damp_and_factor(const float* HX, float* F, float* T, uint8_t* dead, do
   KQ_LAUNCHED("damp_stats_kernel");
   add_diag_kernel<<<dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s>>>(F, n, lam);
   KQ_LAUNCHED("add_diag_kernel");
-  // reverse Cholesky.  The diagonal blocks' U_JJ = R_JJ^-1 are kept in the block buffer T
-  // (64 n floats); F holds A, then R above the diagonal blocks.
+  // reverse Cholesky.  The diagonal blocks' U_JJ = R_JJ^-1 and M_JJ = U_JJ^T U_JJ are kept
+  // in the block buffers T (64 n floats each); F holds A above the diagonal blocks and the
+  // panel factors Z^T below them.
   float* Ubuf = T;
+  float* Mbuf = T + 64 * n;
   const int64_t nb = n / NB;
-  leaf_kernel<<<1, 256, 0, s>>>(F, n, n - NB, Ubuf + (nb - 1) * 4096, flag);
+  leaf_kernel<<<1, 256, 0, s>>>(F, n, n - NB, Ubuf + (nb - 1) * 4096, Mbuf + (nb - 1) * 4096, flag);
   KQ_LAUNCHED("leaf_kernel");
   for (int64_t s0 = n - NB; s0 >= NB; s0 -= NB) {
-    panel_kernel<<<dim3((unsigned)ceil_div(s0, 128)), dim3(256), 0, s>>>(F, n, s0,
-                                                                        Ubuf + (s0 / NB) * 4096);
-    KQ_LAUNCHED("panel_kernel");
     const int64_t m = ceil_div(s0, 128);
-    const int64_t tiles = s0 > NB ? m * (m + 1) / 2 : 0;
+    const int64_t tiles = m * (m + 1) / 2;
+    const int64_t jb = s0 / NB;
     update_kernel<<<dim3((unsigned)(1 + tiles)), dim3(256), 0, s>>>(
-        F, n, s0, Ubuf + (s0 / NB - 1) * 4096, flag);
+        F, n, s0, Mbuf + jb * 4096, Ubuf + (jb - 1) * 4096, Mbuf + (jb - 1) * 4096, flag);
     KQ_LAUNCHED("update_kernel");
   }
-  dim3 zgrid((unsigned)ceil_div(n, 256), (unsigned)n);
-  finalize_kernel<<<zgrid, dim3(256), 0, s>>>(F, n, Ubuf);
+  finalize_kernel<<<dim3((unsigned)nb), dim3(256), 0, s>>>(F, n, Ubuf);
   KQ_LAUNCHED("finalize_kernel");
   // GPTQ's feedback factors: the B x B diagonal blocks of U and P[<J, J] = R[<J, J] U_JJ
   if (B == 128) {
     ujj128_kernel<<<dim3((unsigned)(n / 128)), dim3(256), 0, s>>>(F, n);
     KQ_LAUNCHED("ujj128_kernel");
   }
-  const int64_t nbl = n / B;
-  const int64_t pairs = nbl * (nbl - 1) / 2;
-  if (pairs > 0) {
-    if (B == 128) pmat_kernel<128><<<dim3((unsigned)pairs), dim3(256), 0, s>>>(F, n);
-    else pmat_kernel<64><<<dim3((unsigned)pairs), dim3(256), 0, s>>>(F, n);
+  int64_t ptiles = 0;
+  for (int64_t J = 1; J < n / B; ++J) ptiles += ceil_div(J * B, 128);
+  if (ptiles > 0) {
+    if (B == 128) pmat_kernel<128><<<dim3((unsigned)ptiles), dim3(256), 0, s>>>(F, n);
+    else pmat_kernel<64><<<dim3((unsigned)ptiles), dim3(256), 0, s>>>(F, n);
     KQ_LAUNCHED("pmat_kernel");
   }
   return KQ_OK;

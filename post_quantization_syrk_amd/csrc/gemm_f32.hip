@@ -1,6 +1,5 @@
 // fp32 matrix products on the matrix cores (v_mfma_f32_32x32x2_f32), used by
-// the quantizer: the blocked factorization's panel and trailing updates, the
-// left-looking GPTQ block update and the proxy-loss products.
+// the quantizer: GPTQ's blocked error feedback and the proxy-loss products.
 //
 // C[M x N] (+)= alpha * op(A) op(B), row-major.  128 x 128 tiles, 256 threads
 // (4 waves, each a 64 x 64 sub-tile = 2 x 2 MFMA blocks), 32-deep K stages

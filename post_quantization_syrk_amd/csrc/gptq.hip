@@ -81,7 +81,6 @@ struct RowState {
 
 struct StepCtx {
   const float* Cb;  // LDS: B x B in-block U (zero on and below the diagonal)
-  const float* Ri;  // LDS: 1 / U_jj of the block's columns
   uint8_t* Qrow;    // LDS: this row's B codes
   int q;            // lane within the row
   bool live;
@@ -89,11 +88,28 @@ struct StepCtx {
   const ColArgs* a;
 };
 
+// Operands a column step reads ahead of time: this lane's slice of U row J and, on lane
+// J % 16 of every row, 1 / U_jj for columns J = lane + 16 i (broadcast with DPP).
+template <int CPL>
+struct Ahead {
+  float4 u[3][CPL / 4];   // U rows J, J+1, J+2 (ring indexed by J % 3)
+  float ri[CPL];          // ri[i] = 1 / U_jj of column 16 i + lane
+};
+
 // One column j of the block (all compile-time indices, so every array stays in registers).
 template <int B, int G, int J>
-__device__ __forceinline__ void gptq_step(RowState<B / LPR>& st, const StepCtx& cx) {
+__device__ __forceinline__ void gptq_step(RowState<B / LPR>& st, Ahead<B / LPR>& ah,
+                                          const StepCtx& cx) {
   constexpr int CPL = B / LPR;
   constexpr int O = J / CPL, E = J % CPL;
+  // read U row J + 2 now; it is used two columns later
+  if constexpr (J + 2 < B) {
+    const float* crow = cx.Cb + (J + 2) * B + 4 * cx.q;
+#pragma unroll
+    for (int e = 0; e < CPL; e += 4) ah.u[(J + 2) % 3][e / 4] = *(const float4*)(crow + LPR * e);
+  }
+  // keep those reads here (ALU work and LDS writes may still move across)
+  __builtin_amdgcn_sched_barrier(0x607);
   if constexpr (G > 0) {
     if constexpr (J % G == 0) {
       // group [J, J+G) lives on lanes [J/CPL, (J+G)/CPL); the range always includes 0
@@ -119,19 +135,19 @@ __device__ __forceinline__ void gptq_step(RowState<B / LPR>& st, const StepCtx& 
     }
   }
   const float wj = row_bcast<O>(st.w[E]);
+  const float rij = row_bcast<J % LPR>(ah.ri[J / LPR]);
   float qv = rintf(wj * st.inv) + st.z;
   qv = fminf(fmaxf(qv, 0.0f), cx.a->maxq);
-  const float err = (wj - st.s * (qv - st.z)) * cx.Ri[J];
+  const float qh = st.s * (qv - st.z);
+  const float err = (wj - qh) * rij;
   const float d = -err;
-  if (cx.q == O) {
-    st.el[E] = err;
-    st.dl[E] = st.w0[E] - st.s * (qv - st.z);
-    cx.Qrow[J] = (uint8_t)qv;
-  }
-  const float* crow = cx.Cb + J * B + CPL * cx.q;
+  // every lane of the row holds the same qv and err; the owning lane keeps them
+  st.el[E] = cx.q == O ? err : st.el[E];
+  st.dl[E] = cx.q == O ? st.w0[E] - qh : st.dl[E];
+  cx.Qrow[J] = (uint8_t)qv;
 #pragma unroll
   for (int e = 0; e < CPL; e += 4) {
-    const float4 c = *(const float4*)(crow + e);
+    const float4 c = ah.u[J % 3][e / 4];
     st.w[e] = fmaf(d, c.x, st.w[e]);
     st.w[e + 1] = fmaf(d, c.y, st.w[e + 1]);
     st.w[e + 2] = fmaf(d, c.z, st.w[e + 2]);
@@ -140,9 +156,9 @@ __device__ __forceinline__ void gptq_step(RowState<B / LPR>& st, const StepCtx& 
 }
 
 template <int B, int G, int... J>
-__device__ __forceinline__ void gptq_steps(RowState<B / LPR>& st, const StepCtx& cx,
-                                           std::integer_sequence<int, J...>) {
-  (gptq_step<B, G, J>(st, cx), ...);
+__device__ __forceinline__ void gptq_steps(RowState<B / LPR>& st, Ahead<B / LPR>& ah,
+                                           const StepCtx& cx, std::integer_sequence<int, J...>) {
+  (gptq_step<B, G, J>(st, ah, cx), ...);
 }
 
 // 16 lanes per matrix row, each holding B/16 consecutive columns of the block.
@@ -160,6 +176,8 @@ __global__ __launch_bounds__(CTHREADS) void gptq_block_kernel(ColArgs a, int64_t
   const int64_t r = (int64_t)blockIdx.x * RPW + rl;
   const bool live = r < a.out;
 
+  // LDS copy of U_JJ, chunk-interleaved: columns [CPL q + 4 h, +4) of row i sit at
+  // i * B + 4 (LPR h + q), so the 16 lanes of a row read 256 contiguous bytes per chunk
   for (int idx = t; idx < B * B / 4; idx += CTHREADS) {
     const int i = idx / (B / 4), c = 4 * (idx % (B / 4));
     float4 v = *(const float4*)(a.U + (j0 + i) * a.in + j0 + c);
@@ -171,7 +189,8 @@ __global__ __launch_bounds__(CTHREADS) void gptq_block_kernel(ColArgs a, int64_t
     v.y = c + 1 > i ? v.y : 0.0f;
     v.z = c + 2 > i ? v.z : 0.0f;
     v.w = c + 3 > i ? v.w : 0.0f;
-    *(float4*)(Cb + i * B + c) = v;
+    const int qq = c / CPL, hh = (c % CPL) / 4;
+    *(float4*)(Cb + i * B + 4 * (LPR * hh + qq)) = v;
   }
 
   RowState<CPL> st;
@@ -206,8 +225,15 @@ __global__ __launch_bounds__(CTHREADS) void gptq_block_kernel(ColArgs a, int64_t
   }
   __syncthreads();
 
-  StepCtx cx{Cb, Ri, Qs + rl * B, q, live, r, j0, &a};
-  gptq_steps<B, G>(st, cx, std::make_integer_sequence<int, B>{});
+  StepCtx cx{Cb, Qs + rl * B, q, live, r, j0, &a};
+  Ahead<CPL> ah;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) ah.ri[i] = Ri[LPR * i + q];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int e = 0; e < CPL; e += 4) ah.u[jj][e / 4] = *(const float4*)(Cb + jj * B + 4 * q + LPR * e);
+  gptq_steps<B, G>(st, ah, cx, std::make_integer_sequence<int, B>{});
 
   if (live) {
 #pragma unroll
@@ -315,7 +341,7 @@ Layout layout(int64_t out, int64_t in, int B, bool with_loss) {
   Layout L;
   size_t o = 0;
   L.f = o;    o = align256(o + (size_t)in * in * sizeof(float));
-  L.t = o;    o = align256(o + (size_t)in * 64 * sizeof(float));
+  L.t = o;    o = align256(o + (size_t)in * 128 * sizeof(float));
   L.y = o;    o = align256(o + (size_t)out * B * sizeof(float));
   L.d = o;    o = align256(o + (size_t)out * in * sizeof(float));
   L.dead = o; o = align256(o + (size_t)in);
