@@ -83,7 +83,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // row; the lower part it also touches is never read); R_lj = A'_lj / R_jj goes to Rl and
 // 1 / R_jj to rsq.  Column j-1 is updated first and published through LDS (two buffers in
 // turn), and read back while the rest of the update runs.  Rl's entries below the diagonal
-// are left undefined.  Sets *flag on a non-positive pivot.
+// are left undefined.  Sets *flag on a non-positive pivot (the damped blocks' pivots are far
+// from the denormal range, so the hardware reciprocal square root is used as it is).
 __device__ __forceinline__ void leaf_factor(const float* Ab, float* Rl, float* col0, float* col1,
                                             float* rsq, int* flag) {
   const int l = threadIdx.x & 63;
@@ -101,19 +102,20 @@ __device__ __forceinline__ void leaf_factor(const float* Ab, float* Rl, float* c
 #pragma unroll
   for (int j = 63; j >= 0; --j) {
     const float p = c[j];
-    const float rs = rsqrtf(p);
+    const float rs = __builtin_amdgcn_rsqf(p);
     const float f = a[j] * (rs * rs);
     if (j > 0) {
       float* colx = ((j - 1) & 1) ? col1 : col0;
       a[j - 1] = fmaf(-f, c[j - 1], a[j - 1]);
       colx[l] = a[j - 1];
       wave_sync();
+      // the next pivot first, then the column from the end the next step starts at
+      c[j - 1] = colx[j - 1];
 #pragma unroll
-      for (int k = 0; k < j - 1; ++k) {
+      for (int k = j - 2; k >= 0; --k) {
         a[k] = fmaf(-f, c[k], a[k]);
         c[k] = colx[k];
       }
-      c[j - 1] = colx[j - 1];
     }
     a[j] *= rs;
     Rl[l * LB + j] = a[j];
@@ -133,26 +135,38 @@ __device__ __forceinline__ void leaf_inverse(const float* Rl, const float* rsq, 
                                              float* Ts) {
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
   const int r16 = lane & 15, k4 = lane >> 4;
-  for (int q = t; q < 64 * LB; q += 256) Ul[q] = 0.0f;
-  __syncthreads();
   {
-    // diagonal block w: x = column c of its inverse
+    // diagonal block w: lane group 0 forms column c of its inverse (U_ic = (delta_ic -
+    // sum_{k > i} R_ik U_kc) / R_ii, from the bottom up); groups 1..3 clear the blocks below
     const int b = 16 * w, c = r16;
-    float x[16];
+    float rr[16][16], rq[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = 0.0f;
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int k = 0; k < 16; k += 4) {
+        const float4 v = *(const float4*)(Rl + (b + i) * LB + b + k);
+        rr[i][k] = v.x; rr[i][k + 1] = v.y; rr[i][k + 2] = v.z; rr[i][k + 3] = v.w;
+      }
+#pragma unroll
+    for (int k = 0; k < 16; k += 4) {
+      const float4 v = *(const float4*)(rsq + b + k);
+      rq[k] = v.x; rq[k + 1] = v.y; rq[k + 2] = v.z; rq[k + 3] = v.w;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float x[16];
 #pragma unroll
     for (int i = 15; i >= 0; --i) {
       float sum = 0.0f;
 #pragma unroll
-      for (int k = i + 1; k < 16; ++k) sum = fmaf(Rl[(b + i) * LB + b + k], x[k], sum);
-      const float r = rsq[b + i];
-      const float v = -r * sum;
-      x[i] = i == c ? r : (i < c ? v : 0.0f);
+      for (int k = i + 1; k < 16; ++k) sum = fmaf(rr[i][k], x[k], sum);
+      x[i] = i == c ? rq[i] : (i < c ? -rq[i] * sum : 0.0f);
     }
-    if (lane < 16) {
+    if (k4 == 0) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) Ul[(b + i) * LB + b + c] = x[i];
+    } else if (w + k4 <= 3) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Ul[(b + 16 * k4 + i) * LB + b + c] = 0.0f;
     }
   }
   __syncthreads();
@@ -207,6 +221,27 @@ __device__ __forceinline__ int sw(int r, int k) { return r * 64 + (k ^ ((2 * r) 
 // A 64 x 64 matrix read with lanes along columns (B operand): odd rows shifted by 32 columns.
 __device__ __forceinline__ int swb(int k, int c) { return k * 64 + (c ^ ((k & 1) << 5)); }
 
+// Raw buffer access with per-lane masking: a lane whose byte offset is OOB (at or past the
+// descriptor's record count) reads 0 and its store is dropped, so the masked loads and stores
+// of a tile's edge need no branches (a branch per access would make each one wait for every
+// earlier memory operation).  0x00020000 is the descriptor's data-format word on gfx9.
+constexpr int OOB = 0x7ffffff0;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const float* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, OOB, 0x00020000);
+}
+__device__ __forceinline__ float4 bload4(__amdgpu_buffer_rsrc_t r, int off) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                     __uint_as_float(v.w));
+}
+__device__ __forceinline__ float bload(__amdgpu_buffer_rsrc_t r, int off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void bstore(float v, __amdgpu_buffer_rsrc_t r, int off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+
 // LDS for a leaf: X (64 x LB: A', then U) and Y (64 x LB for R, 64 + 64 for the column and
 // 1 / R_jj, 32 x LB scratch).
 constexpr int LEAF_Y = 64 * LB + 128 + 32 * LB;
@@ -223,18 +258,39 @@ __device__ __forceinline__ void leaf(float* X, float* Y, float* __restrict__ Uou
   if (threadIdx.x < 64) leaf_factor(X, Rl, col, Ts, rsq, flag);
   __syncthreads();
   leaf_inverse(Rl, rsq, X, Ts);
-  // M = U^T U; wave (wi, wj) forms its 32 x 32 quadrant: A[i][k] = U[k][i], B[k][j] = U[k][j]
+  // M = U^T U.  U is upper, so quadrant (I, J) of 32 x 32 sums only k < 32 max(I, J) + 32:
+  // wave 0 forms M00 and wave 1 M01 (= M10^T) over k < 32; waves 2 and 3 form the k < 32
+  // and k >= 32 parts of M11.  M goes to LDS over R (no longer needed), then out with U.
   const int t = threadIdx.x, w = t >> 6, lane = t & 63, l32 = lane & 31, kh = lane >> 5;
-  const int wi = w >> 1, wj = w & 1;
+  const int ci = w >= 2 ? 32 : 0, cj = w == 0 ? 0 : 32, kb = w == 3 ? 32 : 0;
   f32x16 acc = f32x16{};
-#pragma unroll 8
-  for (int k = 0; k < 64; k += 2)
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(X[(k + kh) * LB + 32 * wi + l32],
-                                               X[(k + kh) * LB + 32 * wj + l32], acc, 0, 0, 0);
 #pragma unroll
-  for (int r = 0; r < 16; ++r)
-    Mout[(32 * wi + 8 * (r >> 2) + 4 * kh + (r & 3)) * 64 + 32 * wj + l32] = acc[r];
-  for (int q = t; q < 64 * 64; q += 256) Uout[q] = X[(q >> 6) * LB + (q & 63)];
+  for (int k = 0; k < 32; k += 2)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(X[(kb + k + kh) * LB + ci + l32],
+                                               X[(kb + k + kh) * LB + cj + l32], acc, 0, 0, 0);
+  float* Ml = Rl;
+  if (w != 2) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
+      Ml[(ci + row) * LB + cj + l32] = acc[r];
+      if (w == 1) Ml[(cj + l32) * LB + ci + row] = acc[r];
+    }
+  }
+  __syncthreads();
+  if (w == 2) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float* m = Ml + (32 + 8 * (r >> 2) + 4 * kh + (r & 3)) * LB + 32 + l32;
+      *m = *m + acc[r];
+    }
+  }
+  __syncthreads();
+  for (int q = t; q < 64 * 16; q += 256) {
+    const int r = q >> 4, c4 = (q & 15) * 4;
+    *(float4*)(Uout + r * 64 + c4) = *(const float4*)(X + r * LB + c4);
+    *(float4*)(Mout + r * 64 + c4) = *(const float4*)(Ml + r * LB + c4);
+  }
 }
 
 // The last diagonal block [s0, s0 + 64), factored on its own.
@@ -244,8 +300,11 @@ __global__ __launch_bounds__(256) void leaf_kernel(const float* __restrict__ F, 
                                                    int* __restrict__ flag) {
   __shared__ __attribute__((aligned(16))) float X[64 * LB];
   __shared__ __attribute__((aligned(16))) float Y[LEAF_Y];
-  for (int q = threadIdx.x; q < 64 * 64; q += 256)
-    X[(q >> 6) * LB + (q & 63)] = F[(s0 + (q >> 6)) * n + s0 + (q & 63)];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int r = (threadIdx.x >> 4) + 16 * it, c4 = (threadIdx.x & 15) * 4;
+    *(float4*)(X + r * LB + c4) = *(const float4*)(F + (s0 + r) * n + s0 + c4);
+  }
   __syncthreads();
   leaf(X, Y, Uout, Mout, flag);
 }
@@ -259,9 +318,10 @@ __global__ __launch_bounds__(256) void leaf_kernel(const float* __restrict__ F, 
 // C -= Z[I] A12[K]^T; the diagonal tiles also store Z^T.  The next diagonal block
 // D = [s0-64, s0)^2 is left alone by the tiles: workgroup 0 forms D - Z_D A12[D]^T privately
 // and factors it (leaf), so the next block's factorization overlaps the bulk update.
-// 4 waves of v_mfma_f32_32x32x2f32; K = 64 in one LDS stage; the tile's old values are loaded
-// first so their latency overlaps the operand loads.
-__global__ __launch_bounds__(256) void update_kernel(float* __restrict__ F, int64_t n, int64_t s0,
+// 4 waves of v_mfma_f32_32x32x2f32; K = 64 in one LDS stage.  80 KB of LDS and at most 256
+// registers per lane let two workgroups share a CU, so one tile's loads overlap another's
+// products.
+__global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ F, int64_t n, int64_t s0,
                                                      const float* __restrict__ Mcur,
                                                      float* __restrict__ Unext,
                                                      float* __restrict__ Mnext,
@@ -272,15 +332,17 @@ __global__ __launch_bounds__(256) void update_kernel(float* __restrict__ F, int6
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6, l32 = lane & 31, kh = lane >> 5;
   const int64_t d0 = s0 - 64;
-  for (int q = t; q < 64 * 16; q += 256) {
-    const int r = q >> 4, c4 = (q & 15) * 4;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int q = t + 256 * it, r = q >> 4, c4 = (q & 15) * 4;
     const float4 v = *(const float4*)(Mcur + r * 64 + c4);
     Ms[swb(r, c4)] = v.x; Ms[swb(r, c4 + 1)] = v.y; Ms[swb(r, c4 + 2)] = v.z; Ms[swb(r, c4 + 3)] = v.w;
   }
   if (blockIdx.x == 0) {
     // A12[D] -> As rows 0..63, D -> Bs as the leaf's X (row stride LB)
-    for (int q = t; q < 64 * 16; q += 256) {
-      const int r = q >> 4, c4 = (q & 15) * 4;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int q = t + 256 * it, r = q >> 4, c4 = (q & 15) * 4;
       const float4 v = *(const float4*)(F + (d0 + r) * n + s0 + c4);
       As[sw(r, c4)] = v.x; As[sw(r, c4 + 1)] = v.y; As[sw(r, c4 + 2)] = v.z; As[sw(r, c4 + 3)] = v.w;
       *(float4*)(Bs + r * LB + c4) = *(const float4*)(F + (d0 + r) * n + d0 + c4);
@@ -320,25 +382,22 @@ __global__ __launch_bounds__(256) void update_kernel(float* __restrict__ F, int6
   const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
   // this lane's tile entries: rows rbase + 32 i + 8 (r / 4) + r % 4, columns cbase + 32 j
   const int64_t rbase = i0 + wm + 4 * kh, cbase = j0 + wn + l32;
-  const float* cptr = F + rbase * n + cbase;
   const int rlim = (int)min((int64_t)128, s0 - rbase), clim = (int)min((int64_t)128, s0 - cbase);
-  float cv[2][2][16];
+  // A12[I] and A12[K] (rows past s0 read as 0): all loads first
+  const __amdgpu_buffer_rsrc_t ra = rsrc(F + i0 * n + s0), rb = rsrc(F + j0 * n + s0);
+  float4 va[8], vb[8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int it = 0; it < 8; ++it) {
+    const int r = (t >> 4) + 16 * it, off = (r * (int)n + (t & 15) * 4) * 4;
+    va[it] = bload4(ra, i0 + r < s0 ? off : OOB);
+    vb[it] = bload4(rb, j0 + r < s0 ? off : OOB);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ro = 32 * i + 8 * (r >> 2) + (r & 3);
-        cv[i][j][r] = (ro < rlim && 32 * j < clim) ? cptr[(int64_t)ro * n + 32 * j] : 0.0f;
-      }
-  for (int q = t; q < 128 * 16; q += 256) {
-    const int r = q >> 4, c4 = (q & 15) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f), u = v;
-    if (i0 + r < s0) v = *(const float4*)(F + (i0 + r) * n + s0 + c4);
-    if (j0 + r < s0) u = *(const float4*)(F + (j0 + r) * n + s0 + c4);
-    As[sw(r, c4)] = v.x; As[sw(r, c4 + 1)] = v.y; As[sw(r, c4 + 2)] = v.z; As[sw(r, c4 + 3)] = v.w;
-    Bs[sw(r, c4)] = u.x; Bs[sw(r, c4 + 1)] = u.y; Bs[sw(r, c4 + 2)] = u.z; Bs[sw(r, c4 + 3)] = u.w;
+  for (int it = 0; it < 8; ++it) {
+    const int r = (t >> 4) + 16 * it, c4 = (t & 15) * 4;
+    As[sw(r, c4)] = va[it].x; As[sw(r, c4 + 1)] = va[it].y; As[sw(r, c4 + 2)] = va[it].z; As[sw(r, c4 + 3)] = va[it].w;
+    Bs[sw(r, c4)] = vb[it].x; Bs[sw(r, c4 + 1)] = vb[it].y; Bs[sw(r, c4 + 2)] = vb[it].z; Bs[sw(r, c4 + 3)] = vb[it].w;
   }
   __syncthreads();
   // Z[I] = A12[I] M: wave w forms rows 32 w .. 32 w + 31, all 64 columns
@@ -371,9 +430,12 @@ __global__ __launch_bounds__(256) void update_kernel(float* __restrict__ F, int6
   }
   if (tm == tn) {
     // Z^T of the tile's rows into the lower triangle: F[s0 + c][i0 + i] = Z[i][c]
-    for (int q = t; q < 128 * 64; q += 256) {
-      const int i = q & 127, c = q >> 7;
-      if (i0 + i < s0) F[(s0 + c) * n + i0 + i] = As[sw(i, c)];
+    const __amdgpu_buffer_rsrc_t rz = rsrc(F + s0 * n + i0);
+    const int i = t & 127;
+#pragma unroll
+    for (int it = 0; it < 32; ++it) {
+      const int c = 2 * it + (t >> 7);
+      bstore(As[sw(i, c)], rz, i0 + i < s0 ? (c * (int)n + i) * 4 : OOB);
     }
   }
   // C -= Z[I] A12[K]^T in two halves of 32 k; each half's operands are read before its MFMAs
@@ -403,7 +465,11 @@ __global__ __launch_bounds__(256) void update_kernel(float* __restrict__ F, int6
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[kk][i], bv[kk][j], acc[i][j], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
-  float* optr = F + rbase * n + cbase;
+  // the tile's old values: all loads first, then all stores.  This lane's entries sit at tile
+  // rows wm + 4 kh + 32 i + 8 (r / 4) + r % 4 and columns wn + l32 + 32 j; entries past s0 or
+  // inside the next diagonal block D (which workgroup 0 owns) are masked.
+  const __amdgpu_buffer_rsrc_t rc = rsrc(F + i0 * n + j0);
+  int off[2][2][16];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -412,9 +478,23 @@ __global__ __launch_bounds__(256) void update_kernel(float* __restrict__ F, int6
       for (int r = 0; r < 16; ++r) {
         const int ro = 32 * i + 8 * (r >> 2) + (r & 3);
         const bool in_d = rbase + ro >= d0 && cbase + 32 * j >= d0;
-        if (ro < rlim && 32 * j < clim && !in_d)
-          optr[(int64_t)ro * n + 32 * j] = cv[i][j][r] - acc[i][j][r];
+        off[i][j][r] = (ro < rlim && 32 * j < clim && !in_d)
+                           ? ((wm + 4 * kh + ro) * (int)n + wn + l32 + 32 * j) * 4
+                           : OOB;
       }
+  float cv[2][2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cv[i][j][r] = bload(rc, off[i][j][r]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) bstore(cv[i][j][r] - acc[i][j][r], rc, off[i][j][r]);
 }
 
 // Moves each diagonal block's U_JJ from the block buffer into place.
