@@ -4,8 +4,9 @@
 // C[M x N] (+)= alpha * op(A) op(B), row-major.  128 x 128 tiles, 256 threads
 // (4 waves, each a 64 x 64 sub-tile = 2 x 2 MFMA blocks), 32-deep K stages
 // through LDS stored k-major so every MFMA operand read is 32 consecutive
-// floats.  Optional split-K with fp32 atomics, upper-triangle-only tile sets,
-// and a reduction epilogue sum(alpha * AB .* D) into an fp64 accumulator.
+// floats.  Optional split-K (fp32 atomics into C, or one partial product per split
+// stored to its own slice), upper-triangle-only tile sets, and a reduction epilogue
+// sum(alpha * AB .* D) into an fp64 accumulator.
 #include "kq_internal.h"
 
 #include <stdlib.h>
@@ -26,6 +27,7 @@ struct Args {
   float* C; int64_t ldc;
   float alpha;
   int accumulate, upper_only, a_upper, b_upper, split_k;
+  int64_t partial_stride;
   int64_t k_per_split;
   int64_t strideA, strideB, strideC;
   const float* D; int64_t ldd; double* red;
@@ -202,6 +204,22 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(Args a) {
     if (lane == 0) atomicAdd(a.red, part);
     return;
   }
+  if (a.partial_stride > 0) {
+    float* Cp = a.C + (int64_t)sz * a.partial_stride;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t col = n0 + wn + 32 * j + l32;
+        if (col >= a.N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + rh + (r & 3);
+          if (row < a.M) Cp[row * a.ldc + col] = a.alpha * acc[i][j][r];
+        }
+      }
+    return;
+  }
   if (a.split_k > 1) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -280,6 +298,7 @@ struct DArgs {
   float alpha;
   int accumulate, split_k;
   int64_t k_per_split;
+  int64_t partial_stride;
 };
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
@@ -308,7 +327,8 @@ __global__ __launch_bounds__(THREADS) void gemm_nn_dma_kernel(DArgs a) {
   const int64_t kbeg = (int64_t)blockIdx.z * a.k_per_split;
   const int64_t kend = min(a.K, kbeg + a.k_per_split);
   if (kbeg >= kend) return;
-  const int nst = (int)(((kend - kbeg + DBK - 1) / DBK + DRING - 1) / DRING) * DRING;
+  const int nst = (int)((kend - kbeg + DBK - 1) / DBK);   // stages of this split
+  const int nfull = nst / DRING * DRING;                   // in whole turns of the ring
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, h = lane >> 5;
@@ -423,16 +443,39 @@ __global__ __launch_bounds__(THREADS) void gemm_nn_dma_kernel(DArgs a) {
     __builtin_amdgcn_s_waitcnt(GWAIT_LGKM0);                       \
     gbarrier();                                                    \
   }
-  for (int s0 = 0; s0 < nst; s0 += DRING) {
+  for (int s0 = 0; s0 < nfull; s0 += DRING) {
     KQ_G_STEP(0, r0, r1, xa, xb, ya, yb)
     KQ_G_STEP(1, r1, r2, ya, yb, xa, xb)
     KQ_G_STEP(2, r2, r3, xa, xb, ya, yb)
     KQ_G_STEP(3, r3, r0, ya, yb, xa, xb)
   }
+  {
+    // the last nst % DRING stages (uniform branches; copies past kend read the zero chunk)
+    const int s0 = nfull;
+    if (nst > s0) KQ_G_STEP(0, r0, r1, xa, xb, ya, yb)
+    if (nst > s0 + 1) KQ_G_STEP(1, r1, r2, ya, yb, xa, xb)
+    if (nst > s0 + 2) KQ_G_STEP(2, r2, r3, xa, xb, ya, yb)
+  }
 #undef KQ_G_STEP
   __builtin_amdgcn_s_waitcnt(gwait_vm(0));
 
   const int kh = h, rh = kh * 4;
+  if (a.partial_stride > 0) {
+    float* Cp = a.C + (int64_t)blockIdx.z * a.partial_stride;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t col = n0 + wn + 32 * j + l32;
+        if (col >= a.N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + rh + (r & 3);
+          if (row < a.M) Cp[row * a.ldc + col] = a.alpha * acc[i][j][r];
+        }
+      }
+    return;
+  }
   if (a.split_k > 1) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -493,8 +536,12 @@ int gemm_variant() {
 
 kq_status gemm_f32(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return KQ_OK;
-  if (g.split_k < 1 || (g.split_k > 1 && !g.accumulate && !g.red))
-    return fail(KQ_EINVAL, "gemm_f32: split_k > 1 needs accumulation");
+  const bool partial = g.partial_stride > 0;
+  if (g.split_k < 1 || (g.split_k > 1 && !g.accumulate && !g.red && !partial))
+    return fail(KQ_EINVAL, "gemm_f32: split_k > 1 needs accumulation or partial slices");
+  if (partial && (g.accumulate || g.red || g.batch > 1 || g.upper_only || g.a_upper || g.b_upper ||
+                  g.K <= 0 || g.partial_stride < g.M * g.ldc))
+    return fail(KQ_EINVAL, "gemm_f32: partial slices need a plain product with K > 0");
   // plain row-major products with 16-byte aligned rows take the direct-to-LDS kernel
   const bool aligned = ((uintptr_t)g.A % 16 == 0) && ((uintptr_t)g.B % 16 == 0) &&
                        g.lda % 4 == 0 && g.ldb % 4 == 0 && g.K % 4 == 0 && g.N % 4 == 0;
@@ -507,6 +554,8 @@ kq_status gemm_f32(const GemmArgs& g, hipStream_t s) {
     d.alpha = g.alpha; d.accumulate = g.accumulate;
     d.k_per_split = ceil_div(ceil_div(g.K, g.split_k), DBK) * DBK;
     d.split_k = (int)ceil_div(g.K, d.k_per_split);
+    d.partial_stride = g.partial_stride;
+    if (g.splits_used) *g.splits_used = d.split_k;
     dim3 grid((unsigned)ceil_div(g.M, MT), (unsigned)ceil_div(g.N, NTL), (unsigned)d.split_k);
     gemm_nn_dma_kernel<<<grid, dim3(THREADS), 0, s>>>(d);
     KQ_LAUNCHED("gemm_nn_dma_kernel");
@@ -527,6 +576,8 @@ kq_status gemm_f32(const GemmArgs& g, hipStream_t s) {
   const int splits = g.K > 0 ? (int)ceil_div(g.K, a.k_per_split) : 1;
   // one split left: a plain read-add-write gives the same C += alpha AB
   a.split_k = splits;
+  a.partial_stride = g.partial_stride;
+  if (g.splits_used) *g.splits_used = splits;
   dim3 grid((unsigned)ceil_div(g.M, MT), (unsigned)ceil_div(g.N, NTL), (unsigned)(splits * batch));
   gemm_f32_kernel<<<grid, dim3(THREADS), 0, s>>>(a);
   KQ_LAUNCHED("gemm_f32_kernel");

@@ -9,7 +9,8 @@
 //   e_j = (w_j - qhat_j) / U_jj,   w_k -= e_j U_jk  (k > j)
 // where the (row, group) grid is taken from the current weights when a group's
 // first column is reached.  It is run blockwise, B columns at a time:
-//   Y = D[:, <J] P[<J, J]               one fp32 MFMA product (split over K, atomics):
+//   Y = D[:, <J] P[<J, J]               one fp32 MFMA product, split over K into up to 8
+//                                       partial slices that the column kernel sums:
 //                                       D = W0 - Qhat (the rounding error so far) and
 //                                       P = R[<J, J] U_JJ, so that Y = -E[:, <J] U[<J, J]
 //                                       and the block's current weights are W0[:, J] + Y,
@@ -35,11 +36,36 @@ namespace {
 constexpr int LPR = 16;             // lanes per matrix row in the column kernel
 constexpr int CTHREADS = 256;       // threads per workgroup in the column kernel
 constexpr int RPW = CTHREADS / LPR; // matrix rows per workgroup
+constexpr int YSLOTS = 8;           // most K splits of the feedback product
+
+// Raw buffer loads with per-lane masking: a byte offset at or past OOB reads 0 (no branch).
+// 0x00020000 is the descriptor's data-format word on gfx9.
+constexpr int OOB = 0x7ffffff0;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const float* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, OOB, 0x00020000);
+}
+__device__ __forceinline__ float4 bload4(__amdgpu_buffer_rsrc_t r, int off) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                     __uint_as_float(v.w));
+}
+
+// Slices of the feedback product's workspace: enough K splits to give every CU of a 256-CU
+// device one 128-row tile, at most YSLOTS.
+inline int64_t y_slots(int64_t out) {
+  const int64_t tiles = (out + 127) / 128;
+  const int64_t s = 256 / tiles;
+  return s < 1 ? 1 : (s > YSLOTS ? YSLOTS : s);
+}
 
 struct ColArgs {
   float* W;            // out x in: W0 (unprocessed columns) / errors e (processed columns)
   int64_t out, in;
-  float* Y;            // out x B corrections of the current block (D P = -E U)
+  float* Y;            // nsplit slices of out x B: partial corrections of the current block,
+                       // summed in slice order (D P = -E U)
+  int nsplit;          // slices written for this block (0: no correction)
+  int64_t ystride;     // floats between slices
   float* D;            // out x in: W0 - Qhat of the processed columns
   const float* U;      // in x in: U_JJ in the diagonal B x B blocks
   const uint8_t* dead; // in
@@ -198,10 +224,12 @@ __global__ __launch_bounds__(CTHREADS) void gptq_block_kernel(ColArgs a, int64_t
 #pragma unroll
   for (int e = 0; e < CPL; e += 4) {
     float4 w0 = make_float4(0.f, 0.f, 0.f, 0.f), y = w0;
-    if (live) {
-      w0 = *(const float4*)(a.W + r * a.in + col + e);
-      y = *(const float4*)(a.Y + r * B + CPL * q + e);
-      *(float4*)(a.Y + r * B + CPL * q + e) = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (live) w0 = *(const float4*)(a.W + r * a.in + col + e);
+    const int yoff = live ? (int)((r * B + CPL * q + e) * 4) : OOB;
+#pragma unroll
+    for (int sp = 0; sp < YSLOTS; ++sp) {
+      const float4 v = bload4(rsrc(a.Y + sp * a.ystride), sp < a.nsplit ? yoff : OOB);
+      y.x += v.x; y.y += v.y; y.z += v.z; y.w += v.w;
     }
     const uint8_t* dd = a.dead + col + e;
     st.w0[e] = dd[0] ? 0.f : w0.x;
@@ -342,7 +370,7 @@ Layout layout(int64_t out, int64_t in, int B, bool with_loss) {
   size_t o = 0;
   L.f = o;    o = align256(o + (size_t)in * in * sizeof(float));
   L.t = o;    o = align256(o + (size_t)in * 128 * sizeof(float));
-  L.y = o;    o = align256(o + (size_t)out * B * sizeof(float));
+  L.y = o;    o = align256(o + (size_t)y_slots(out) * out * B * sizeof(float));
   L.d = o;    o = align256(o + (size_t)out * in * sizeof(float));
   L.dead = o; o = align256(o + (size_t)in);
   L.scal = o; o = align256(o + 8 * sizeof(double));
@@ -359,7 +387,7 @@ kq_status check_params(const kq_quant_params* p, int64_t out, int64_t in) {
   if (p->act_order != 0) return fail(KQ_ENOTIMPL, "act_order is not implemented");
   if (!(p->damp >= 0.f) || !isfinite(p->damp)) return fail(KQ_EINVAL, "damp must be >= 0");
   if (p->block != 64 && p->block != 128) return fail(KQ_EINVAL, "block must be 64 or 128");
-  if (out < 1 || in < 1 || in > (1 << 30) || out > (1 << 30))
+  if (out < 1 || in < 1 || in > (1 << 30) || out > (1 << 22))
     return fail(KQ_ESHAPE, "bad layer shape");
   if (in % 32 != 0) return fail(KQ_ESHAPE, "in must be a multiple of 32");
   if (in % p->block != 0) return fail(KQ_ESHAPE, "in must be a multiple of block");
@@ -413,11 +441,11 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
 
   KQ_TRY(fill_u32((uint32_t*)scal, 16, 0u, s));
   KQ_TRY(fill_u32((uint32_t*)flag, 4, 0u, s));
-  KQ_TRY(fill_f32(Y, out * B, 0.f, s));
   KQ_TRY(damp_and_factor(HX_rot, F, T, dead, scal, flag, in, p->damp, B, s));
 
   ColArgs a;
   a.W = W_rot; a.out = out; a.in = in; a.Y = Y; a.D = Dm; a.U = F; a.dead = dead;
+  a.nsplit = 0; a.ystride = out * B;
   a.bits = p->bits; a.maxq = (float)((1 << p->bits) - 1);
   a.ngroups = in / p->group; a.scales = scales; a.zeros = zeros;
   a.packed = packed; a.codes = codes_opt;
@@ -433,15 +461,19 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
       g.M = out; g.N = B; g.K = j0;
       g.A = Dm; g.lda = in; g.transA = false;
       g.B = F + j0; g.ldb = in; g.transB = false;
-      g.C = Y; g.ldc = B; g.alpha = 1.0f; g.accumulate = true; g.upper_only = false;
+      g.C = Y; g.ldc = B; g.alpha = 1.0f; g.accumulate = false; g.upper_only = false;
       // one workgroup per CU (the product keeps a 128 KB LDS ring): split K so that one round
-      // of workgroups covers the GPU, with at least 256 of K per split
+      // of workgroups covers the GPU, with at least 256 of K per split; each split stores its
+      // own slice, which the column kernel sums
       const int64_t tiles = ceil_div(out, 128);
       int64_t split = cus / tiles;
       const int64_t max_split = ceil_div(j0, 256);
       if (split > max_split) split = max_split;
+      if (split > y_slots(out)) split = y_slots(out);
       if (split < 1) split = 1;
       g.split_k = (int)split;
+      g.partial_stride = out * B;
+      g.splits_used = &a.nsplit;
       KQ_TRY(gemm_f32(g, s));
     }
     kern<<<dim3(col_grid), dim3(CTHREADS), 0, s>>>(a, j0);

@@ -40,11 +40,16 @@ struct GemmArgs {
   bool upper_only;    // only tiles with row-tile <= col-tile
   bool a_upper;       // op(A) is upper triangular (zeros below): skip K below the tile's rows
   bool b_upper;       // op(B) is upper triangular: skip K beyond the tile's columns
-  int split_k;        // >= 1; > 1 requires accumulate (atomics)
+  int split_k;        // >= 1; > 1 requires accumulate (atomics) or partial_stride
   int batch;          // >= 1 independent products, operands offset by the strides below
   int64_t strideA, strideB, strideC;  // in elements
   // reduce epilogue: instead of writing C, accumulate sum(alpha*AB .* D) into *red (fp64)
   const float* D; int64_t ldd; double* red;
+  // split partials: with partial_stride > 0, split z of the K range stores alpha times its
+  // partial product to C + z * partial_stride (plain stores; C is not read).  The number of
+  // splits launched (none of them empty) goes to *splits_used when that is not NULL.
+  int64_t partial_stride;
+  int* splits_used;
 };
 kq_status gemm_f32(const GemmArgs& g, hipStream_t s);
 
