@@ -102,12 +102,12 @@ struct RowState {
   float w0[CPL];   // their starting weights (W0)
   float el[CPL];   // errors e_j once quantized
   float dl[CPL];   // W0_j - qhat_j once quantized
+  float ql[CPL];   // codes once quantized
   float s, inv, z; // grid of the current group
 };
 
 struct StepCtx {
   const float* Cb;  // LDS: B x B in-block U (zero on and below the diagonal)
-  uint8_t* Qrow;    // LDS: this row's B codes
   int q;            // lane within the row
   bool live;
   int64_t r, j0;
@@ -170,7 +170,7 @@ __device__ __forceinline__ void gptq_step(RowState<B / LPR>& st, Ahead<B / LPR>&
   // every lane of the row holds the same qv and err; the owning lane keeps them
   st.el[E] = cx.q == O ? err : st.el[E];
   st.dl[E] = cx.q == O ? st.w0[E] - qh : st.dl[E];
-  cx.Qrow[J] = (uint8_t)qv;
+  st.ql[E] = cx.q == O ? qv : st.ql[E];
 #pragma unroll
   for (int e = 0; e < CPL; e += 4) {
     const float4 c = ah.u[J % 3][e / 4];
@@ -196,21 +196,47 @@ __global__ __launch_bounds__(CTHREADS) void gptq_block_kernel(ColArgs a, int64_t
   constexpr int CPL = B / LPR;
   __shared__ __attribute__((aligned(16))) float Cb[B * B];
   __shared__ float Ri[B];
-  __shared__ __attribute__((aligned(16))) uint8_t Qs[RPW * B];
   const int t = threadIdx.x;
   const int q = t % LPR, rl = t / LPR;
   const int64_t r = (int64_t)blockIdx.x * RPW + rl;
   const bool live = r < a.out;
 
+  // All global loads first: U_JJ, its diagonal, this row's starting weights, feedback slices
+  // and dead flags.
+  constexpr int NIT = B * B / 4 / CTHREADS;
+  float4 uv[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int idx = t + CTHREADS * it, i = idx / (B / 4), c = 4 * (idx % (B / 4));
+    uv[it] = *(const float4*)(a.U + (j0 + i) * a.in + j0 + c);
+  }
+  const int td = t < B ? t : B - 1;
+  const float udiag = a.U[(j0 + td) * a.in + j0 + td];
+  RowState<CPL> st;
+  const int64_t col = j0 + CPL * q;
+  float4 w0v[CPL / 4], yv[CPL / 4][YSLOTS];
+  uint32_t dv[CPL / 4];
+  const int woff = live ? (int)((CPL * q) * 4) : OOB;
+  const __amdgpu_buffer_rsrc_t rw = rsrc(a.W + (live ? r : 0) * a.in + j0);
+#pragma unroll
+  for (int e = 0; e < CPL; e += 4) {
+    w0v[e / 4] = bload4(rw, woff == OOB ? OOB : woff + 4 * e);
+    dv[e / 4] = *(const uint32_t*)(a.dead + col + e);
+    const int yoff = live ? (int)((r * B + CPL * q + e) * 4) : OOB;
+#pragma unroll
+    for (int sp = 0; sp < YSLOTS; ++sp)
+      yv[e / 4][sp] = bload4(rsrc(a.Y + sp * a.ystride), sp < a.nsplit ? yoff : OOB);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
   // LDS copy of U_JJ, chunk-interleaved: columns [CPL q + 4 h, +4) of row i sit at
-  // i * B + 4 (LPR h + q), so the 16 lanes of a row read 256 contiguous bytes per chunk
-  for (int idx = t; idx < B * B / 4; idx += CTHREADS) {
-    const int i = idx / (B / 4), c = 4 * (idx % (B / 4));
-    float4 v = *(const float4*)(a.U + (j0 + i) * a.in + j0 + c);
-    if (i >= c && i < c + 4) {
-      const int k = i - c;
-      Ri[i] = 1.0f / (k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w);
-    }
+  // i * B + 4 (LPR h + q), so the 16 lanes of a row read 256 contiguous bytes per chunk;
+  // entries on and below the diagonal are zeroed.  Ri = 1 / diag(U_JJ).
+  if (t < B) Ri[t] = 1.0f / udiag;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int idx = t + CTHREADS * it, i = idx / (B / 4), c = 4 * (idx % (B / 4));
+    float4 v = uv[it];
     v.x = c + 0 > i ? v.x : 0.0f;
     v.y = c + 1 > i ? v.y : 0.0f;
     v.z = c + 2 > i ? v.z : 0.0f;
@@ -219,29 +245,26 @@ __global__ __launch_bounds__(CTHREADS) void gptq_block_kernel(ColArgs a, int64_t
     *(float4*)(Cb + i * B + 4 * (LPR * hh + qq)) = v;
   }
 
-  RowState<CPL> st;
-  const int64_t col = j0 + CPL * q;
 #pragma unroll
   for (int e = 0; e < CPL; e += 4) {
-    float4 w0 = make_float4(0.f, 0.f, 0.f, 0.f), y = w0;
-    if (live) w0 = *(const float4*)(a.W + r * a.in + col + e);
-    const int yoff = live ? (int)((r * B + CPL * q + e) * 4) : OOB;
+    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int sp = 0; sp < YSLOTS; ++sp) {
-      const float4 v = bload4(rsrc(a.Y + sp * a.ystride), sp < a.nsplit ? yoff : OOB);
-      y.x += v.x; y.y += v.y; y.z += v.z; y.w += v.w;
+      y.x += yv[e / 4][sp].x; y.y += yv[e / 4][sp].y; y.z += yv[e / 4][sp].z; y.w += yv[e / 4][sp].w;
     }
-    const uint8_t* dd = a.dead + col + e;
-    st.w0[e] = dd[0] ? 0.f : w0.x;
-    st.w0[e + 1] = dd[1] ? 0.f : w0.y;
-    st.w0[e + 2] = dd[2] ? 0.f : w0.z;
-    st.w0[e + 3] = dd[3] ? 0.f : w0.w;
+    const float4 w0 = w0v[e / 4];
+    const uint32_t dd = dv[e / 4];
+    st.w0[e] = (dd & 0xffu) ? 0.f : w0.x;
+    st.w0[e + 1] = (dd & 0xff00u) ? 0.f : w0.y;
+    st.w0[e + 2] = (dd & 0xff0000u) ? 0.f : w0.z;
+    st.w0[e + 3] = (dd & 0xff000000u) ? 0.f : w0.w;
     st.w[e] = st.w0[e] + y.x;
     st.w[e + 1] = st.w0[e + 1] + y.y;
     st.w[e + 2] = st.w0[e + 2] + y.z;
     st.w[e + 3] = st.w0[e + 3] + y.w;
     st.el[e] = st.el[e + 1] = st.el[e + 2] = st.el[e + 3] = 0.f;
     st.dl[e] = st.dl[e + 1] = st.dl[e + 2] = st.dl[e + 3] = 0.f;
+    st.ql[e] = st.ql[e + 1] = st.ql[e + 2] = st.ql[e + 3] = 0.f;
   }
   st.s = 1.0f; st.inv = 1.0f; st.z = 0.0f;
   if constexpr (G == 0) {  // one group per row: grid taken from the original row beforehand
@@ -253,7 +276,7 @@ __global__ __launch_bounds__(CTHREADS) void gptq_block_kernel(ColArgs a, int64_t
   }
   __syncthreads();
 
-  StepCtx cx{Cb, Qs + rl * B, q, live, r, j0, &a};
+  StepCtx cx{Cb, q, live, r, j0, &a};
   Ahead<CPL> ah;
 #pragma unroll
   for (int i = 0; i < CPL; ++i) ah.ri[i] = Ri[LPR * i + q];
@@ -263,33 +286,41 @@ __global__ __launch_bounds__(CTHREADS) void gptq_block_kernel(ColArgs a, int64_t
     for (int e = 0; e < CPL; e += 4) ah.u[jj][e / 4] = *(const float4*)(Cb + jj * B + 4 * q + LPR * e);
   gptq_steps<B, G>(st, ah, cx, std::make_integer_sequence<int, B>{});
 
+  // Pack the row's B codes into bits * B / 32 whole words starting at word j0 * bits / 32.
+  // Lane q's CPL codes form one field of CPL * bits <= 32 bits at bit CPL * bits * q of the
+  // row's code stream; word w (bits [32 w, 32 w + 32)) is gathered from the fields of the at
+  // most five lanes that reach into it, placed in a 64-bit window 32 bits up so that every
+  // shift is non-negative.
+  uint32_t f = 0;
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) f |= (uint32_t)st.ql[e] << (e * a.bits);
+  const int fbits = CPL * a.bits;
+  const int qa = (32 * q) / fbits;
+  uint32_t fk[5];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) fk[k] = __shfl(f, qa + k < LPR ? qa + k : LPR - 1, LPR);
+  uint64_t word = 0;
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const int off = (qa + k) * fbits - 32 * q;
+    const bool use = qa + k < LPR && off < 32;
+    word |= (uint64_t)(use ? fk[k] : 0u) << (use ? off + 32 : 0);
+  }
   if (live) {
+    const int64_t wpr = a.in * a.bits / 32;
+    if (q < a.bits * B / 32) a.packed[r * wpr + j0 * a.bits / 32 + q] = (uint32_t)(word >> 32);
+    if (a.codes) {
+#pragma unroll
+      for (int e = 0; e < CPL; e += 4)
+        *(uint32_t*)(a.codes + r * a.in + col + e) =
+            (uint32_t)st.ql[e] | ((uint32_t)st.ql[e + 1] << 8) | ((uint32_t)st.ql[e + 2] << 16) |
+            ((uint32_t)st.ql[e + 3] << 24);
+    }
+    // errors replace the processed weights; W0 - qhat goes to D
 #pragma unroll
     for (int e = 0; e < CPL; e += 4) {
       *(float4*)(a.W + r * a.in + col + e) = make_float4(st.el[e], st.el[e + 1], st.el[e + 2], st.el[e + 3]);
       *(float4*)(a.D + r * a.in + col + e) = make_float4(st.dl[e], st.dl[e + 1], st.dl[e + 2], st.dl[e + 3]);
-    }
-  }
-  __syncthreads();
-  // pack this row's B codes: bits * B / 32 whole words starting at word j0 * bits / 32
-  if (live) {
-    const int words = a.bits * B / 32;
-    const int64_t wpr = a.in * a.bits / 32;
-    const uint8_t* qr = Qs + rl * B;
-    for (int wd = q; wd < words; wd += LPR) {
-      uint32_t acc = 0;
-      const int bit0 = 32 * wd;
-      for (int c = bit0 / a.bits; c < B && c * a.bits < bit0 + 32; ++c) {
-        const int off = c * a.bits - bit0;   // negative for a code straddling the word start
-        const uint32_t v = qr[c];
-        acc |= off >= 0 ? (v << off) : (v >> (-off));
-      }
-      a.packed[r * wpr + j0 * a.bits / 32 + wd] = acc;
-    }
-    if (a.codes) {
-#pragma unroll
-      for (int e = 0; e < CPL; e += 4)
-        *(uint32_t*)(a.codes + r * a.in + col + e) = *(const uint32_t*)(qr + CPL * q + e);
     }
   }
 }

@@ -75,7 +75,7 @@ def check_against_oracle(g, Wt, HXt, HGt, bits, group, damp=0.01, rows=None):
 
 
 @pytest.mark.parametrize("bits,group,block", [(2, 64, 64), (2, 128, 128), (3, 32, 128), (4, 128, 128),
-                                              (4, 16, 64), (3, 64, 128), (2, 256, 64)])
+                                              (4, 16, 64), (3, 64, 128), (2, 256, 64), (3, 32, 64)])
 def test_quantize_synthetic_layers(bits, group, block):
     announce(f"gptq synthetic bits={bits} group={group} block={block}")
     rng = np.random.default_rng(bits * 100 + group + block)
