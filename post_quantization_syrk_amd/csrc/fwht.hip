@@ -14,7 +14,9 @@
 // of one row pass; the transform along the strided (row) index is done by
 // tiled column passes.  Every pass reads and writes each element once.
 //
-// Row pass (wavefront-shuffle FWHT): a Hadamard block of b contiguous
+// Row pass, 4096-element blocks: three rounds of 4 index bits in registers with two LDS
+// regroupings (row_fwht4096_kernel).
+// Row pass, other blocks (wavefront-shuffle FWHT): a Hadamard block of b contiguous
 // elements is spread over b/EPT threads with EPT values each (16-byte
 // vectors).  Butterflies over the in-register index bits run in registers,
 // over the lane bits with cross-lane xor shuffles, and over the wave bits
@@ -94,6 +96,42 @@ struct Scale {
   int invert;           // use 1/d instead of d
   float mul;            // constant factor (1/sqrt(b))
 };
+
+constexpr int OOB = 0x7ffffff0;   // buffer offsets at or past this read 0 / drop the store
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
+  // 0x00020000: the descriptor's data-format word on gfx9
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, OOB, 0x00020000);
+}
+
+// out[k] = scale_at(s, i0 + o[k]) for K indices, with every load issued before any is used
+// (a missing vector is read at an out-of-range offset, which returns 0).  The descriptor
+// base i0 must be the same for the whole wave; o[k] is the lane's offset (< 2^29).
+template <int K>
+__device__ __forceinline__ void scales_nb(const Scale& s, int64_t i0, const int (&o)[K],
+                                          float (&out)[K]) {
+  const bool hd = s.d != nullptr, hs = s.sign != nullptr;
+  const __amdgpu_buffer_rsrc_t rd = rsrc(hd ? s.d + i0 : s.d), rg = rsrc(hs ? s.sign + i0 : s.sign);
+  float d[K];
+  int g[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    d[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, hd ? 4 * o[k] : OOB, 0, 0));
+    g[k] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(rg, hs ? o[k] : OOB, 0, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) out[k] = s.mul;
+  if (hd) {
+    if (s.invert) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) out[k] = out[k] / d[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < K; ++k) out[k] = out[k] * d[k];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) out[k] = hs && g[k] < 0 ? -out[k] : out[k];
+}
 
 __device__ __forceinline__ float scale_at(const Scale& s, int64_t i) {
   float v = s.mul;
@@ -190,6 +228,100 @@ __global__ __launch_bounds__(NT) void row_fwht_kernel(const float* __restrict__ 
   for (int j = 0; j < EPT / 4; ++j) {
     const int x = 4 * tb + 4 * TPR * j;
     *(float4*)(q + x) = *(const float4*)(blk + x);
+  }
+}
+
+// Row pass for 4096-element blocks: one workgroup per (column block, R rows), 16 values per
+// thread.  The 12 butterfly stages commute, so they run as three rounds of 4 index bits in
+// registers, with the values regrouped through LDS between rounds:
+//   round A: x = 16 t + i     (bits 0-3 in registers; contiguous 64-byte loads)
+//   round B: x = (t & 15) + 16 i + 256 (t >> 4)
+//   round C: x = t + 256 i    (bits 8-11; a wave stores 64 consecutive values per i)
+// LDS index x + (x >> 4) keeps the round A writes and round B accesses free of bank conflicts.
+// The thread's 16 column scales are formed once and reused for the workgroup's R rows.
+constexpr int RB = 4096;
+template <int R>
+__global__ __launch_bounds__(NT) void row_fwht4096_kernel(const float* __restrict__ src,
+                                                          float* __restrict__ dst, int64_t rows,
+                                                          int64_t n, Scale rs, Scale cs) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  __shared__ float sm[RB + RB / 16];
+  const int t = threadIdx.x;
+  const int64_t nb = n / RB;
+  const int64_t cb = blockIdx.x % nb, r0 = (int64_t)(blockIdx.x / nb) * R;
+  const int64_t c0 = cb * RB;
+  float csc[16], rsv[R];
+  int oc[16], orow[R];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) oc[i] = 16 * t + i;
+#pragma unroll
+  for (int k = 0; k < R; ++k) orow[k] = r0 + k < rows ? k : 0;
+  scales_nb<16>(cs, c0, oc, csc);
+  scales_nb<R>(rs, r0, orow, rsv);
+  // row k's loads are issued while row k - 1 is transformed (rows past the end read 0)
+  u32x4 nxt[4];
+  auto load = [&](int64_t r) {
+    const __amdgpu_buffer_rsrc_t rr = rsrc(src + (r < rows ? r : 0) * n + c0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      nxt[j] = __builtin_amdgcn_raw_buffer_load_b128(rr, r < rows ? (16 * t + 4 * j) * 4 : OOB, 0, 0);
+  };
+  load(r0);
+#pragma unroll 1
+  for (int k = 0; k < R; ++k) {
+    const int64_t r = r0 + k;
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[4 * j] = __uint_as_float(nxt[j].x); v[4 * j + 1] = __uint_as_float(nxt[j].y);
+      v[4 * j + 2] = __uint_as_float(nxt[j].z); v[4 * j + 3] = __uint_as_float(nxt[j].w);
+    }
+    if (k + 1 < R) load(r + 1);
+    float rsc = rsv[0];
+#pragma unroll
+    for (int kk = 1; kk < R; ++kk) rsc = kk == k ? rsv[kk] : rsc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] *= rsc * csc[i];
+    auto bfly = [&]() {
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if (e & m) continue;
+          const float a = v[e], c = v[e | m];
+          v[e] = a + c;
+          v[e | m] = a - c;
+        }
+    };
+    bfly();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sm[17 * t + i] = v[i];   // x = 16 t + i
+    __syncthreads();
+    const int xb = (t & 15) + 256 * (t >> 4);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int x = xb + 16 * i;
+      v[i] = sm[x + (x >> 4)];
+    }
+    bfly();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int x = xb + 16 * i;
+      sm[x + (x >> 4)] = v[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int x = t + 256 * i;
+      v[i] = sm[x + (x >> 4)];
+    }
+    bfly();
+    const __amdgpu_buffer_rsrc_t rd = rsrc(dst + (r < rows ? r : 0) * n + c0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[i]), rd,
+                                            r < rows ? (t + 256 * i) * 4 : OOB, 0, 0);
+    __syncthreads();   // the next row reuses sm
   }
 }
 
@@ -314,6 +446,22 @@ kq_status row_transform(const float* src, float* dst, int64_t rows, int64_t n, i
     const int64_t tot4 = rows * n / 4;
     scale_kernel<<<dim3((unsigned)ceil_div(tot4, NT)), dim3(NT), 0, s>>>(src, dst, rows, n, rs, cs);
     KQ_LAUNCHED("scale_kernel");
+    return KQ_OK;
+  }
+  if (b == RB) {
+    // about four workgroups per CU on a 256-CU device, at most 16 rows each
+    const int64_t nb = n / RB;
+    int64_t rpw = (rows * nb) / 1024;
+    rpw = rpw < 1 ? 1 : (rpw > 16 ? 16 : rpw);
+    const int R = rpw >= 16 ? 16 : rpw >= 8 ? 8 : rpw >= 4 ? 4 : rpw >= 2 ? 2 : 1;
+    const dim3 grid((unsigned)(nb * ceil_div(rows, R)));
+    switch (R) {
+#define KQ_R4096(X) \
+  case X: row_fwht4096_kernel<X><<<grid, dim3(NT), 0, s>>>(src, dst, rows, n, rs, cs); break;
+      KQ_R4096(1) KQ_R4096(2) KQ_R4096(4) KQ_R4096(8) KQ_R4096(16)
+#undef KQ_R4096
+    }
+    KQ_LAUNCHED("row_fwht4096_kernel");
     return KQ_OK;
   }
   const int ept = b <= 1024 ? 4 : (int)(b / 256);

@@ -216,11 +216,12 @@ __global__ __launch_bounds__(CTHREADS) void gptq_block_kernel(ColArgs a, int64_t
   const int64_t col = j0 + CPL * q;
   float4 w0v[CPL / 4], yv[CPL / 4][YSLOTS];
   uint32_t dv[CPL / 4];
-  const int woff = live ? (int)((CPL * q) * 4) : OOB;
-  const __amdgpu_buffer_rsrc_t rw = rsrc(a.W + (live ? r : 0) * a.in + j0);
+  // descriptor bases are per workgroup; the row goes into the lane's offset (r0 = first row)
+  const int64_t r0 = (int64_t)blockIdx.x * RPW;
+  const __amdgpu_buffer_rsrc_t rw = rsrc(a.W + r0 * a.in + j0);
 #pragma unroll
   for (int e = 0; e < CPL; e += 4) {
-    w0v[e / 4] = bload4(rw, woff == OOB ? OOB : woff + 4 * e);
+    w0v[e / 4] = bload4(rw, live ? (int)(((r - r0) * a.in + CPL * q + e) * 4) : OOB);
     dv[e / 4] = *(const uint32_t*)(a.dead + col + e);
     const int yoff = live ? (int)((r * B + CPL * q + e) * 4) : OOB;
 #pragma unroll
