@@ -348,8 +348,9 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* p) {
 
 struct DmaArgs {
   SyrkArgs s;
-  int per_xcd;   // tiles per XCD region
+  int per_xcd;      // tiles per XCD region (region order) / (split, tile) items per XCD
   int xcds;
+  int token_major;  // 1: each XCD walks a contiguous range of (split, tile) items
 };
 
 // DNST = stages in the LDS ring (4: 128 KB, 5: 160 KB); each buffer is its own LDS object so
@@ -367,11 +368,20 @@ __global__ __launch_bounds__(DWAVES * 64) void syrk_dma_kernel(DmaArgs d) {
   // workgroup u runs on XCD u mod xcds; each XCD walks its own contiguous region of tiles,
   // split by split, so the tiles resident on one XCD share panels in its L2 and all XCDs
   // stream the same token range at the same time
+  // (token-major order: each XCD walks its own range of (split, tile) items in split-major
+  // order, so its resident workgroups share one token range and a compact set of tiles)
   const int u = blockIdx.x;
   const int xcd = u % d.xcds;
   const int q = u / d.xcds;
-  const int split = q / d.per_xcd;
-  const int tile = xcd * d.per_xcd + q % d.per_xcd;
+  int split, tile;
+  if (d.token_major) {
+    const int item = xcd * d.per_xcd + q;
+    split = item / a.ntiles;
+    tile = item % a.ntiles;
+  } else {
+    split = q / d.per_xcd;
+    tile = xcd * d.per_xcd + q % d.per_xcd;
+  }
   if (tile >= a.ntiles || split >= a.splits) return;
   int bi, bj;
   tile_of(tile, a.nb, bi, bj);
@@ -568,6 +578,36 @@ int syrk_variant() {
 }
 
 // Stages in the direct-to-LDS kernel's ring (KQ_SYRK_RING = 4 or 5; a tuning knob).
+int syrk_order() {
+  const char* env = getenv("KQ_SYRK_ORDER");
+  return env && atoi(env) == 1 ? 1 : 0;
+}
+
+// Token splits for the token-major order: the smallest S whose items per XCD
+// (ceil(ntiles S / xcds)) fill whole rounds of the XCD's CUs to within 3 %, at least two
+// workgroups per CU.
+int choose_splits_tm(int ntiles, int cu_per_xcd, int xcds, int64_t T) {
+  const char* env = getenv("KQ_SYRK_SPLITS");
+  if (env) {
+    int v = atoi(env);
+    if (v >= 1) return v;
+  }
+  int64_t max_s = T / (8 * DBK);
+  if (max_s < 1) max_s = 1;
+  if (max_s > 64) max_s = 64;
+  int best = 1;
+  double best_eff = 0.0;
+  for (int s = 1; s <= max_s; ++s) {
+    const int64_t items = ((int64_t)ntiles * s + xcds - 1) / xcds;
+    const int64_t rounds = (items + cu_per_xcd - 1) / cu_per_xcd;
+    const double eff = (double)ntiles * s / (double)(rounds * cu_per_xcd * xcds);
+    if (items < 2LL * cu_per_xcd) continue;
+    if (eff >= 0.97) return s;
+    if (eff > best_eff + 1e-9) { best_eff = eff; best = s; }
+  }
+  return best;
+}
+
 int syrk_ring() {
   const char* env = getenv("KQ_SYRK_RING");
   if (env && atoi(env) == 4) return 4;
@@ -657,12 +697,15 @@ extern "C" kq_status kq_accumulate_hessian(const uint16_t* A_bf16, int64_t T, in
       DmaArgs d;
       d.xcds = device_cu_count() % 8 == 0 ? 8 : 1;
       const int cu_per_xcd = device_cu_count() / d.xcds;
+      d.token_major = syrk_order();
       d.per_xcd = (int)ceil_div(a.ntiles, d.xcds);
-      a.splits = choose_splits_dma(d.per_xcd, cu_per_xcd, d.xcds, T);
+      a.splits = d.token_major ? choose_splits_tm(a.ntiles, cu_per_xcd, d.xcds, T)
+                               : choose_splits_dma(d.per_xcd, cu_per_xcd, d.xcds, T);
       a.tok_split = ceil_div(ceil_div(T, a.splits), DBK) * DBK;
       a.splits = (int)ceil_div(T, a.tok_split);
+      if (d.token_major) d.per_xcd = (int)ceil_div((int64_t)a.ntiles * a.splits, d.xcds);
       d.s = a;
-      const int64_t g = (int64_t)d.xcds * d.per_xcd * a.splits;
+      const int64_t g = (int64_t)d.xcds * d.per_xcd * (d.token_major ? 1 : a.splits);
       if (g > 0x7FFFFFFF) return fail(KQ_ESHAPE, "kq_accumulate_hessian: too many tiles");
       if (syrk_ring() == 5) syrk_dma_kernel<5><<<dim3((unsigned)g), dim3(DWAVES * 64), 0, s>>>(d);
       else syrk_dma_kernel<4><<<dim3((unsigned)g), dim3(DWAVES * 64), 0, s>>>(d);

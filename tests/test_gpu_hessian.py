@@ -50,16 +50,18 @@ def test_ragged_shapes(T, n, lda):
     assert np.array_equal(H, H.T)
 
 
-@pytest.mark.parametrize("variant", ["0", "1", "2", "3", "4", "4/5"])
+@pytest.mark.parametrize("variant", ["0", "1", "2", "3", "4", "4/5", "4/tm"])
 @pytest.mark.parametrize("T,n,lda", [(20000, 600, 608), (31, 256, 256), (1000, 300, 304)])
 def test_kernel_variants_agree(variant, T, n, lda, monkeypatch):
     """Every SYRK kernel variant (register-staged 4/8 waves, tile/split-major; direct-to-LDS
-    with a 4- or 5-stage ring) against the oracle, on shapes with many token splits, a ragged
-    last stage and a ragged last tile."""
-    v, _, ring = variant.partition("/")
+    with a 4- or 5-stage ring, region or token-major workgroup order) against the oracle, on
+    shapes with many token splits, a ragged last stage and a ragged last tile."""
+    v, _, opt = variant.partition("/")
     monkeypatch.setenv("KQ_SYRK_VARIANT", v)
-    if ring:
-        monkeypatch.setenv("KQ_SYRK_RING", ring)
+    if opt == "tm":
+        monkeypatch.setenv("KQ_SYRK_ORDER", "1")
+    elif opt:
+        monkeypatch.setenv("KQ_SYRK_RING", opt)
     announce(f"hessian variant {variant} T={T} n={n} lda={lda}")
     rng = np.random.default_rng(T + n)
     x = (rng.standard_normal((T, n)) * np.exp(rng.standard_normal(n))).astype(np.float32)
