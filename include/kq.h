@@ -191,7 +191,7 @@ kq_status kq_quantize_layer_workspace(const kq_quant_params* p, int64_t out, int
  *             (direct loss and GPTQ's predicted loss sum_j e_j^T H~_G e_j).
  *             When non-NULL the call synchronizes `stream`.
  *   ws        device workspace of ws_bytes >= kq_quantize_layer_workspace(...)
- * Sizes: in % 32 == 0, in % group == 0, in % block == 0, 1 <= out.
+ * Sizes: in % 32 == 0, in % group == 0, in % block == 0, 1 <= out <= 2^22.
  * Synchronizes `stream` before returning (to report KQ_ENOTSPD).
  */
 kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, const float* HX_rot,
