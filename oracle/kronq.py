@@ -24,7 +24,8 @@ __all__ = [
     "rotation_matrix", "rescale_vectors", "biip", "BIIP_FULL", "BIIP_NO_RESCALE", "BIIP_IN_ONLY",
     "BIIP_OUT_ONLY", "damp_and_factor", "AsymMinMaxGrid", "FixedUniformGrid", "gptq",
     "GptqResult", "quantize_layer", "pack_codes", "unpack_codes", "proxy_loss", "predicted_loss",
-    "allocate_bits", "brute_force_min_loss", "NotSPDError",
+    "allocate_bits", "brute_force_min_loss", "NotSPDError", "ClippedMinMaxGrid",
+    "act_order_perm", "CLIP_NORM", "CLIP_GRID", "CLIP_MAXSHRINK",
 ]
 
 BIIP_FULL, BIIP_NO_RESCALE, BIIP_IN_ONLY, BIIP_OUT_ONLY = 0, 1, 2, 3
@@ -292,6 +293,92 @@ class AsymMinMaxGrid:
         return self.scale * (q - self.zero)
 
 
+# The base recipe's `--w_clip` (KronQ README, "Reproduce from scratch"), which
+# the pages name but do not define: READING, the shrink search of the GPTQ line
+# of work, with these constants.
+CLIP_NORM, CLIP_GRID, CLIP_MAXSHRINK = 2.4, 100, 0.8
+
+
+class ClippedMinMaxGrid(AsymMinMaxGrid):
+    """Min-max grid with a clip-ratio search (`--w_clip`).
+
+    [KronQ-README] "Reproduce from scratch": the base recipe quantizes with
+    `--w_clip --w_asym --w_groupsize -1`; the pages do not define the search.
+    READING: for p = 1 - i / grid, i = 0 .. maxshrink * grid - 1, take the
+    min-max grid (as AsymMinMaxGrid) of the shrunk range [p xmin, p xmax],
+    quantize the group with it, and keep, per row, the p whose error
+    sum |qhat - w|^norm is smallest (the first such p on equal errors).
+
+    replay_scales (parity protocol, optional): another implementation's scale
+    per row for the next group.  Where it picks a different candidate, its
+    choice is adopted when that candidate's error here is within `tol`
+    (relative) of the smallest (accepted_ties); otherwise this grid keeps its
+    own choice (hard_mismatches).
+    """
+
+    def __init__(self, bits: int, group: int, norm: float = CLIP_NORM, grid: int = CLIP_GRID,
+                 maxshrink: float = CLIP_MAXSHRINK, replay_scales=None, tol: float = 1e-5):
+        super().__init__(bits, group)
+        self.norm, self.grid, self.maxshrink = norm, grid, maxshrink
+        self.replay_scales = replay_scales
+        self.tol = tol
+        self.accepted_ties = self.hard_mismatches = 0
+        self.choice = None
+        self.errors = None
+
+    def candidates(self, block: np.ndarray):
+        """Scales, zeros and errors of every candidate p, each [K x rows]."""
+        block = np.asarray(block, np.float64)
+        xmin0 = np.minimum(block.min(axis=1), 0.0)
+        xmax0 = np.maximum(block.max(axis=1), 0.0)
+        S, Z, E = [], [], []
+        for i in range(int(self.maxshrink * self.grid)):
+            p = 1.0 - i / self.grid
+            xmin, xmax = p * xmin0, p * xmax0
+            s = (xmax - xmin) / self.maxq
+            s[xmax == xmin] = 1.0
+            z = np.rint(-xmin / s)
+            q = np.clip(np.rint(block / s[:, None]) + z[:, None], 0, self.maxq)
+            err = np.sum(np.abs(s[:, None] * (q - z[:, None]) - block) ** self.norm, axis=1)
+            S.append(s)
+            Z.append(z)
+            E.append(err)
+        return np.array(S), np.array(Z), np.array(E)
+
+    def set_params(self, block: np.ndarray) -> None:
+        S, Z, E = self.candidates(block)
+        rows = np.arange(S.shape[1])
+        k = np.argmin(E, axis=0)   # first minimum
+        if self.replay_scales is not None:
+            other = np.asarray(self.replay_scales, np.float64)
+            match = np.argmin(np.abs(S - other[None, :]), axis=0)
+            found = np.abs(S[match, rows] - other) <= 1e-5 * np.abs(other)
+            diff = match != k
+            near = E[match, rows] <= E[k, rows] * (1.0 + self.tol)
+            ok = diff & found & near
+            k = np.where(ok, match, k)
+            self.accepted_ties += int(ok.sum())
+            self.hard_mismatches += int((diff & ~(found & near)).sum())
+        self.choice = k
+        self.errors = E
+        self.scale = S[k, rows]
+        self.zero = Z[k, rows]
+
+
+def act_order_perm(HX: np.ndarray) -> np.ndarray:
+    """Column order of `--act_order`: descending diag(H~_X).
+
+    [KronQ-README] "Reproduce from scratch": the base recipe runs GPTQ with
+    `--act_order`; the pages do not define it.  READING (GPTQ convention): a
+    dead channel's zero diagonal counts as 1, as in damp_and_factor, and equal
+    diagonals keep their index order (stable sort).  perm[p] is the original
+    column quantized at position p.
+    """
+    d = np.array(np.diag(HX), dtype=np.float64, copy=True)
+    d[d == 0] = 1.0
+    return np.argsort(-d, kind="stable")
+
+
 class FixedUniformGrid:
     """Unbounded uniform grid with one fixed step per column (no clamping).
 
@@ -419,7 +506,8 @@ def predicted_loss(E: np.ndarray, HG: np.ndarray | None = None) -> float:
 
 def quantize_layer(Wt: np.ndarray, HXt: np.ndarray, HGt: np.ndarray | None, bits: int,
                    group: int, damp: float = 0.01, replay_codes: np.ndarray | None = None,
-                   rows: np.ndarray | None = None, factor=None):
+                   rows: np.ndarray | None = None, factor=None, act_order: bool = False,
+                   w_clip: bool = False, replay_scales: np.ndarray | None = None):
     """Damp, factor and GPTQ-quantize a processed layer; also the two losses.
 
     [KronQ-README] opening section: KronQ extends GPTQ with H_G under the
@@ -428,16 +516,48 @@ def quantize_layer(Wt: np.ndarray, HXt: np.ndarray, HGt: np.ndarray | None, bits
     H~_X, dW~ = W~ - Qhat) and the predicted loss sum_j e_j^T H~_G e_j (which
     equals the direct loss taken with the damped H~_X).  With `rows`, only
     those rows are quantized (losses are then not computed).
+
+    act_order / w_clip: the base recipe's `--act_order` and `--w_clip`
+    ([KronQ-README] "Reproduce from scratch", with `--w_groupsize -1`), both
+    for one grid per row (group = in).  With act_order, GPTQ runs on the
+    columns in act_order_perm order (W~ and H~_X permuted, U refactored) and
+    every per-column result is returned in the original order.  `factor`,
+    when given, is that of the (permuted) H~_X; replay_codes are in the
+    original order; replay_scales (w_clip) are per row.
     """
-    if factor is None:
-        U, lam, dead, Hd = damp_and_factor(HXt, damp)
-    else:
-        U, lam, dead, Hd = factor
     W = np.asarray(Wt, np.float64)
+    n = W.shape[1]
+    if (act_order or w_clip) and group != n:
+        raise ValueError("act_order and w_clip take one grid per row (group = in)")
+    perm = act_order_perm(HXt) if act_order else np.arange(n)
+    HXp = np.asarray(HXt, np.float64)[np.ix_(perm, perm)] if act_order else HXt
+    if factor is None:
+        U, lam, dead_p, Hd = damp_and_factor(HXp, damp)
+    else:
+        U, lam, dead_p, Hd = factor
     if rows is not None:
         W = W[rows]
-    res = gptq(W, U, AsymMinMaxGrid(bits, group), dead, replay_codes)
-    out = {"gptq": res, "U": U, "lam": lam, "dead": dead}
+    grid = (ClippedMinMaxGrid(bits, group, replay_scales=replay_scales) if w_clip
+            else AsymMinMaxGrid(bits, group))
+    rp = None if replay_codes is None else np.asarray(replay_codes)[:, perm]
+    res = gptq(W[:, perm], U, grid, dead_p, rp)
+    if act_order:
+        for name in ("codes", "qhat", "E", "unrounded"):
+            x = getattr(res, name)
+            y = np.empty_like(x)
+            y[:, perm] = x
+            setattr(res, name, y)
+        res.mismatch_positions = [(r, int(perm[j])) for r, j in res.mismatch_positions]
+    dead = np.empty_like(dead_p)
+    dead[perm] = dead_p
+    out = {"gptq": res, "U": U, "lam": lam, "dead": dead, "perm": perm}
+    if w_clip:
+        out["clip_accepted_ties"] = grid.accepted_ties
+        out["clip_hard_mismatches"] = grid.hard_mismatches
+        out["clip_choice"] = grid.choice
+        E = np.sort(grid.errors, axis=0)
+        # smallest relative gap between the best and the runner-up candidate, over rows
+        out["clip_margin"] = float(np.min((E[1] - E[0]) / np.maximum(E[0], 1e-300)))
     if rows is None:
         W0 = np.array(W, copy=True)
         W0[:, dead] = 0.0

@@ -379,6 +379,147 @@ def test_replay_accepts_only_near_ties():
 
 
 # ---------------------------------------------------------------------------
+# act_order and w_clip (the base recipe's flags; readings, see the oracle)
+# ---------------------------------------------------------------------------
+def test_act_order_perm_hand_example():
+    # diagonal (2, 5, 0, 5, 3): the dead entry counts as 1; descending, equal values by index
+    H = np.diag([2.0, 5.0, 0.0, 5.0, 3.0])
+    np.testing.assert_array_equal(o.act_order_perm(H), [1, 3, 4, 0, 2])
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_act_order_with_diagonal_hessian_is_rtn(bits):
+    # no off-diagonal coupling: GPTQ is RTN in any column order, so the codes must land back
+    # in their own columns after the permutation (a wrong inverse permutation scrambles them)
+    rng = np.random.default_rng(31)
+    W = rng.standard_normal((12, 40)) * 0.05
+    HX = np.diag(np.exp(2.0 * rng.standard_normal(40)))
+    r = o.quantize_layer(W, HX, None, bits, 40, 0.01, act_order=True)
+    assert not np.array_equal(r["perm"], np.arange(40))
+    codes, Q = _textbook_rtn(W, bits, 40)
+    np.testing.assert_array_equal(r["gptq"].codes, codes)
+    np.testing.assert_allclose(r["gptq"].qhat, Q, atol=1e-15)
+
+
+def test_act_order_result_is_independent_of_input_column_order():
+    # act_order processes columns in a canonical order (descending diagonal), so quantizing a
+    # column-permuted layer gives the same codes, moved with the columns
+    rng = np.random.default_rng(32)
+    n = 24
+    W = rng.standard_normal((10, n)) * 0.05
+    HX = spd(rng, n)
+    pi = rng.permutation(n)
+    a = o.quantize_layer(W, HX, None, 3, n, 0.01, act_order=True)
+    b = o.quantize_layer(W[:, pi], HX[np.ix_(pi, pi)], None, 3, n, 0.01, act_order=True)
+    np.testing.assert_array_equal(b["gptq"].codes, a["gptq"].codes[:, pi])
+    np.testing.assert_allclose(b["gptq"].E, a["gptq"].E[:, pi], rtol=0, atol=0)
+    # and the order matters without act_order (the check above is not vacuous)
+    c = o.quantize_layer(W[:, pi], HX[np.ix_(pi, pi)], None, 3, n, 0.01)
+    d = o.quantize_layer(W, HX, None, 3, n, 0.01)
+    assert not np.array_equal(c["gptq"].codes, d["gptq"].codes[:, pi])
+
+
+def test_act_order_equal_diagonal_is_natural_order():
+    rng = np.random.default_rng(33)
+    n = 16
+    A = spd(rng, n)
+    dA = np.sqrt(np.diag(A))
+    HX = A / np.outer(dA, dA)   # correlation matrix
+    HX[np.arange(n), np.arange(n)] = 1.0   # exactly unit diagonal
+    W = rng.standard_normal((6, n)) * 0.05
+    a = o.quantize_layer(W, HX, None, 2, n, 0.01, act_order=True)
+    b = o.quantize_layer(W, HX, None, 2, n, 0.01)
+    np.testing.assert_array_equal(a["perm"], np.arange(n))
+    np.testing.assert_array_equal(a["gptq"].codes, b["gptq"].codes)
+
+
+def test_act_order_keeps_the_gptq_identity():
+    # W0 - Qhat = E U in the permuted order, so sum_j |e_j|^2 = tr(dW H_d dW^T) in any order
+    rng = np.random.default_rng(34)
+    n = 32
+    W = rng.standard_normal((8, n)) * 0.05
+    HX = spd(rng, n)
+    r = o.quantize_layer(W, HX, None, 3, n, 0.01, act_order=True)
+    Hd = HX + r["lam"] * np.eye(n)
+    dW = W - r["gptq"].qhat
+    assert r["loss_pred"] == pytest.approx(o.proxy_loss(dW, Hd), rel=1e-10)
+
+
+def test_clip_hand_example():
+    # row (3, 3, 3, 3, 10) at 2 bits (maxq 3); xmin = 0, so z = 0 and s = 10 p / 3.  By hand,
+    # sum |qhat - w|^2.4 for p = 1: 4 (1/3)^2.4 = 0.2864; 0.99: 4 (0.3)^2.4 + 0.1^2.4 = 0.2265;
+    # 0.98: 4 (0.2667)^2.4 + 0.2^2.4 = 0.1886; 0.97: 4 (0.2333)^2.4 + 0.3^2.4 = 0.1773;
+    # 0.96: 4 (0.2)^2.4 + 0.4^2.4 = 0.1949; 0.95: 0.243; below 0.95 the 10 loses at least 0.5 and
+    # below 2/3 the 3s round to 2 s.  So p = 0.97 (candidate 3).
+    g = o.ClippedMinMaxGrid(2, 5)
+    g.set_params(np.array([[3.0, 3.0, 3.0, 3.0, 10.0]]))
+    assert g.choice[0] == 3
+    assert g.scale[0] == pytest.approx(0.97 * 10 / 3, rel=1e-15) and g.zero[0] == 0
+    assert g.errors[3, 0] == pytest.approx(0.1773, abs=2e-4)
+    assert g.errors[0, 0] == pytest.approx(0.2864, abs=2e-4)
+
+
+def test_clip_with_one_candidate_is_the_minmax_grid():
+    rng = np.random.default_rng(35)
+    blk = rng.standard_normal((9, 50))
+    a = o.ClippedMinMaxGrid(3, 50, maxshrink=0.01)   # only p = 1
+    b = o.AsymMinMaxGrid(3, 50)
+    a.set_params(blk)
+    b.set_params(blk)
+    np.testing.assert_array_equal(a.scale, b.scale)
+    np.testing.assert_array_equal(a.zero, b.zero)
+
+
+def test_clip_keeps_exactly_representable_rows_and_never_loses():
+    rng = np.random.default_rng(36)
+    # values on the p = 1 grid of their own range: error 0 at p = 1, which is then kept
+    q = rng.integers(0, 4, size=(5, 30)).astype(float)
+    q[:, 0], q[:, 1] = 0, 3
+    exact = (q - 1.0) * 0.25
+    g = o.ClippedMinMaxGrid(2, 30)
+    g.set_params(exact)
+    np.testing.assert_array_equal(g.choice, 0)
+    # random rows: the chosen error never exceeds the plain grid's (p = 1 is a candidate),
+    # and on Gaussian rows at 2 bits some clipping wins
+    blk = rng.standard_normal((20, 256))
+    g.set_params(blk)
+    best = g.errors[g.choice, np.arange(20)]
+    assert np.all(best <= g.errors[0])
+    assert np.all(g.choice > 0)
+
+
+def test_clip_is_scale_equivariant():
+    # a power-of-two rescale is exact: same candidate, scale times 4, same zero and codes
+    rng = np.random.default_rng(37)
+    W = rng.standard_normal((7, 64)) * 0.05
+    HX = spd(rng, 64)
+    a = o.quantize_layer(W, HX, None, 3, 64, 0.01, act_order=True, w_clip=True)
+    b = o.quantize_layer(4.0 * W, HX, None, 3, 64, 0.01, act_order=True, w_clip=True)
+    np.testing.assert_array_equal(a["clip_choice"], b["clip_choice"])
+    np.testing.assert_array_equal(b["gptq"].scales, 4.0 * a["gptq"].scales)
+    np.testing.assert_array_equal(b["gptq"].zeros, a["gptq"].zeros)
+    np.testing.assert_array_equal(b["gptq"].codes, a["gptq"].codes)
+
+
+def test_clip_replay_accepts_only_near_ties():
+    # another implementation's scale is adopted only when its candidate's error is within
+    # the tolerance of the best one
+    blk = np.array([[3.0, 3.0, 3.0, 3.0, 10.0]])
+    g = o.ClippedMinMaxGrid(2, 5)
+    g.set_params(blk)
+    s3, s2 = g.scale[0], 0.98 * 10 / 3
+    far = o.ClippedMinMaxGrid(2, 5, replay_scales=np.array([s2]))
+    far.set_params(blk)      # candidate 2 is 6 % worse: kept own choice
+    assert far.choice[0] == 3 and far.hard_mismatches == 1 and far.accepted_ties == 0
+    near = o.ClippedMinMaxGrid(2, 5, replay_scales=np.array([s2]), tol=0.07)
+    near.set_params(blk)     # within a 7 % tolerance: adopted
+    assert near.choice[0] == 2 and near.accepted_ties == 1 and near.scale[0] == pytest.approx(s2)
+    same = o.ClippedMinMaxGrid(2, 5, replay_scales=np.array([s3]))
+    same.set_params(blk)
+    assert same.choice[0] == 3 and same.hard_mismatches == 0 and same.accepted_ties == 0
+
+
+# ---------------------------------------------------------------------------
 # Packing
 # ---------------------------------------------------------------------------
 def test_pack_hand_examples():
