@@ -72,7 +72,8 @@ typedef struct kq_quant_params {
   int block;      /* GPTQ block width: 64 or 128; block % group == 0 or group % block == 0 */
   float damp;     /* lambda = damp * mean(diag H_X), damp >= 0 */
   int asym;       /* must be 1 (asymmetric min-max grid) */
-  int act_order;  /* must be 0 (natural column order) */
+  int act_order;  /* 0: natural column order; 1: descending diag(H~_X) (needs group == in) */
+  int w_clip;     /* 0: min-max grid; 1: clip-ratio search per row (needs group == in) */
 } kq_quant_params;
 
 /* Library version: major * 10000 + minor * 100 + patch. */
@@ -171,6 +172,15 @@ kq_status kq_quantize_layer_workspace(const kq_quant_params* p, int64_t out, int
  *   (xmin = min(0, min), xmax = max(0, max), s = (xmax - xmin) / (2^b - 1) or 1 if
  *   equal, z = rint(-xmin / s)); code q = clamp(rint(w / s) + z, 0, 2^b - 1)
  *   (round half to even); the rounding error is fed back into later columns.
+ * Base-recipe options (KronQ README, "Reproduce from scratch": --act_order and --w_clip
+ * with --w_groupsize -1; the pages name them without defining them), both for one grid
+ * per row (group == in):
+ *   act_order = 1: GPTQ visits the columns in descending order of diag(H~_X) (a dead
+ *     channel's zero counts as 1; equal values keep index order).  Every output (codes,
+ *     packed words, errors in W_rot, losses) is still in the original column order.
+ *   w_clip = 1: the row's grid is the min-max grid of the shrunk range [p xmin, p xmax]
+ *     for the p in {1 - i/100 : i = 0..79} with the smallest sum |qhat - w|^2.4 over the
+ *     row (the first such p on equal sums; errors in fp32, summed in fp64).
  * Implementation: reverse-order Cholesky H_d = R R^T (R upper), U = R^-1 formed only
  * in its diagonal blocks, and the column recursion run 128 (or 64) columns at a time
  * with one matrix product per block for the feedback from earlier blocks

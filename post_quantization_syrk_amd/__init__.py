@@ -39,7 +39,8 @@ class NotSPDError(KQError):
 
 class QuantParams(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int), ("group", ctypes.c_int), ("block", ctypes.c_int),
-                ("damp", ctypes.c_float), ("asym", ctypes.c_int), ("act_order", ctypes.c_int)]
+                ("damp", ctypes.c_float), ("asym", ctypes.c_int), ("act_order", ctypes.c_int),
+                ("w_clip", ctypes.c_int)]
 
 
 _vp, _i64, _int, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -166,8 +167,8 @@ def kq_biip_rotate(W_src, W_dst, HX_src, HX_dst, HG_src, HG_dst, sign_in, sign_o
 
 
 def make_params(bits: int = 2, group: int = 128, block: int = 128, damp: float = 0.01,
-                asym: int = 1, act_order: int = 0) -> QuantParams:
-    return QuantParams(bits, group, block, damp, asym, act_order)
+                asym: int = 1, act_order: int = 0, w_clip: int = 0) -> QuantParams:
+    return QuantParams(bits, group, block, damp, asym, act_order, w_clip)
 
 
 def kq_quantize_layer_workspace(p: QuantParams, out_n: int, in_n: int, with_loss: bool) -> int:

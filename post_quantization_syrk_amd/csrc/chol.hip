@@ -595,7 +595,8 @@ kq_status damp_and_factor(const float* HX, float* F, float* T, uint8_t* dead, do
                           int* flag, int64_t n, float damp, int B, hipStream_t s) {
   if (n % NB != 0) return fail(KQ_ESHAPE, "factorization needs n %% %d == 0", NB);
   if ((B != 64 && B != 128) || n % B != 0) return fail(KQ_ESHAPE, "bad GPTQ block %d", B);
-  KQ_HIP(hipMemcpyAsync(F, HX, n * n * sizeof(float), hipMemcpyDeviceToDevice, s));
+  // HX == NULL: F already holds the matrix
+  if (HX) KQ_HIP(hipMemcpyAsync(F, HX, n * n * sizeof(float), hipMemcpyDeviceToDevice, s));
   damp_stats_kernel<<<1, 1024, 0, s>>>(F, n, dead, damp, lam);
   KQ_LAUNCHED("damp_stats_kernel");
   add_diag_kernel<<<dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s>>>(F, n, lam);

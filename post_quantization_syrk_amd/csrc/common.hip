@@ -61,6 +61,6 @@ kq_status fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
 
 }  // namespace kq
 
-extern "C" int kq_version(void) { return 100; /* 0.1.0 */ }
+extern "C" int kq_version(void) { return 200; /* 0.2.0: act_order, w_clip */ }
 
 extern "C" const char* kq_last_error(void) { return kq::g_last_error; }

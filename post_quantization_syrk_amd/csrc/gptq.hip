@@ -23,6 +23,7 @@
 #include "kq_internal.h"
 
 #include <math.h>
+#include <stdlib.h>
 
 #include <utility>
 
@@ -74,7 +75,7 @@ struct ColArgs {
   int64_t ngroups;     // in / group
   float* scales;       // out x ngroups
   uint8_t* zeros;      // out x ngroups
-  uint32_t* packed;    // out x (in * bits / 32)
+  uint32_t* packed;    // out x (in * bits / 32), or NULL (codes packed afterwards)
   uint8_t* codes;      // out x in or NULL
 };
 
@@ -309,7 +310,8 @@ __global__ __launch_bounds__(CTHREADS) void gptq_block_kernel(ColArgs a, int64_t
   }
   if (live) {
     const int64_t wpr = a.in * a.bits / 32;
-    if (q < a.bits * B / 32) a.packed[r * wpr + j0 * a.bits / 32 + q] = (uint32_t)(word >> 32);
+    if (a.packed && q < a.bits * B / 32)
+      a.packed[r * wpr + j0 * a.bits / 32 + q] = (uint32_t)(word >> 32);
     if (a.codes) {
 #pragma unroll
       for (int e = 0; e < CPL; e += 4)
@@ -326,35 +328,166 @@ __global__ __launch_bounds__(CTHREADS) void gptq_block_kernel(ColArgs a, int64_t
   }
 }
 
-// One (row) group spanning the whole row: grid from the original row (dead columns zeroed).
+// |d|^2.4 in fp32 from the hardware base-2 log and exponential (0 for d = 0)
+__device__ __forceinline__ float pow24(float d) {
+  return __builtin_amdgcn_exp2f(2.4f * __builtin_amdgcn_logf(d));
+}
+
+// One (row) group spanning the whole row: grid from the original row (dead columns zeroed),
+// one workgroup per row.  With clip, the grid of the shrunk range [p xmin, p xmax] for
+// p = 1 - i/100, i < 80, with the smallest sum |s (q - z) - w|^2.4 over the row (the first
+// such p on equal sums; per-element terms in fp32, summed in fp64).  The row is staged in
+// LDS when it fits (rows_in_lds).
+constexpr int CLIP_CANDIDATES = 80;
 __global__ __launch_bounds__(256) void row_grid_kernel(const float* __restrict__ W, int64_t in,
                                                        const uint8_t* __restrict__ dead, float maxq,
                                                        float* __restrict__ scales,
-                                                       uint8_t* __restrict__ zeros) {
+                                                       uint8_t* __restrict__ zeros, int clip,
+                                                       int rows_in_lds) {
+  extern __shared__ float rowbuf[];
   const int64_t r = blockIdx.x;
+  const int t = threadIdx.x;
+  const float* row = W + r * in;
   float mn = 0.f, mx = 0.f;
-  for (int64_t c = threadIdx.x; c < in; c += 256) {
-    const float v = dead[c] ? 0.f : W[r * in + c];
+#pragma unroll 4
+  for (int64_t c = t; c < in; c += 256) {
+    const float v = dead[c] ? 0.f : row[c];
+    if (rows_in_lds) rowbuf[c] = v;
     mn = fminf(mn, v);
     mx = fmaxf(mx, v);
   }
   __shared__ float smn[256], smx[256];
-  smn[threadIdx.x] = mn;
-  smx[threadIdx.x] = mx;
+  __shared__ double sred[4];
+  smn[t] = mn;
+  smx[t] = mx;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) {
-      smn[threadIdx.x] = fminf(smn[threadIdx.x], smn[threadIdx.x + w]);
-      smx[threadIdx.x] = fmaxf(smx[threadIdx.x], smx[threadIdx.x + w]);
+    if (t < w) {
+      smn[t] = fminf(smn[t], smn[t + w]);
+      smx[t] = fmaxf(smx[t], smx[t + w]);
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    float s = (smx[0] - smn[0]) / maxq;
-    if (smx[0] == smn[0]) s = 1.0f;
-    scales[r] = s;
-    zeros[r] = (uint8_t)rintf(-smn[0] / s);
+  const float xmin0 = smn[0], xmax0 = smx[0];
+  if (!clip) {
+    if (t == 0) {
+      float s = (xmax0 - xmin0) / maxq;
+      if (xmax0 == xmin0) s = 1.0f;
+      scales[r] = s;
+      zeros[r] = (uint8_t)rintf(-xmin0 / s);
+    }
+    return;
   }
+  double best = INFINITY;
+  float best_s = 1.0f, best_z = 0.0f;
+  for (int i = 0; i < CLIP_CANDIDATES; ++i) {
+    const double p = 1.0 - i / 100.0;
+    const float xmin = (float)(p * xmin0), xmax = (float)(p * xmax0);
+    float s = (xmax - xmin) / maxq;
+    if (xmax == xmin) s = 1.0f;
+    const float z = rintf(-xmin / s), inv = 1.0f / s;
+    double e = 0.0;
+#pragma unroll 4
+    for (int64_t c = t; c < in; c += 256) {
+      const float w = rows_in_lds ? rowbuf[c] : (dead[c] ? 0.f : row[c]);
+      const float q = fminf(fmaxf(rintf(w * inv) + z, 0.0f), maxq);
+      e += (double)pow24(fabsf(s * (q - z) - w));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) e += __shfl_xor(e, o);
+    if ((t & 63) == 0) sred[t >> 6] = e;
+    __syncthreads();
+    if (t == 0) {
+      const double tot = (sred[0] + sred[1]) + (sred[2] + sred[3]);
+      if (tot < best) {
+        best = tot;
+        best_s = s;
+        best_z = z;
+      }
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    scales[r] = best_s;
+    zeros[r] = (uint8_t)best_z;
+  }
+}
+
+// act_order: rank of column i by descending diag(H) (a zero diagonal counts as 1, equal values
+// by index); perm[rank] = i, invperm[i] = rank.  The diagonal is staged through LDS in chunks.
+// A NaN diagonal counts as -inf, so the order stays total and the ranks a permutation.
+__device__ __forceinline__ float act_key(float v) {
+  return v == 0.f ? 1.f : (v != v ? -INFINITY : v);
+}
+__global__ __launch_bounds__(256) void act_order_perm_kernel(const float* __restrict__ H, int64_t n,
+                                                             int32_t* __restrict__ perm,
+                                                             int32_t* __restrict__ invperm) {
+  __shared__ float dch[1024];
+  const int t = threadIdx.x;
+  const int64_t i = (int64_t)blockIdx.x * 256 + t;
+  const float di = i < n ? act_key(H[i * n + i]) : 0.f;
+  int64_t rank = 0;
+  for (int64_t j0 = 0; j0 < n; j0 += 1024) {
+    __syncthreads();
+    for (int k = t; k < 1024; k += 256) {
+      const int64_t j = j0 + k;
+      dch[k] = j < n ? act_key(H[j * n + j]) : 0.f;
+    }
+    __syncthreads();
+    const int64_t m = min((int64_t)1024, n - j0);
+    for (int64_t k = 0; k < m; ++k) {
+      const float dj = dch[k];
+      rank += (dj > di) | ((dj == di) & (j0 + k < i));
+    }
+  }
+  if (i < n) {
+    perm[rank] = (int32_t)i;
+    invperm[i] = (int32_t)rank;
+  }
+}
+
+// dst[r][c] = src[rows ? rows[r] : r][idx[c]], c < n: one workgroup per row, the source row
+// staged in LDS (n * sizeof(T) bytes of dynamic LDS).  src and dst must not overlap.
+template <typename T>
+__global__ __launch_bounds__(256) void gather_cols_kernel(const T* __restrict__ src,
+                                                          T* __restrict__ dst, int64_t n,
+                                                          const int32_t* __restrict__ idx,
+                                                          const int32_t* __restrict__ rows) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char gbuf[];
+  T* row = (T*)gbuf;
+  const int64_t r = blockIdx.x;
+  const int64_t sr = rows ? rows[r] : r;
+  const int t = threadIdx.x;
+#pragma unroll 4
+  for (int64_t c = t; c < n; c += 256) row[c] = src[sr * n + c];
+  __syncthreads();
+#pragma unroll 4
+  for (int64_t c = t; c < n; c += 256) dst[r * n + c] = row[idx[c]];
+}
+
+// Packs rows of codes (column order) into bits * in / 32 words per row: word w holds bits
+// [32 w, 32 w + 32) of the row's stream, i.e. codes c0 .. c0 + 16 at most, gathered in a
+// 64-bit window 8 bits up so that every shift is non-negative.
+__global__ __launch_bounds__(256) void pack_rows_kernel(const uint8_t* __restrict__ codes,
+                                                        int64_t out, int64_t in, int bits,
+                                                        uint32_t* __restrict__ packed) {
+  const int64_t words = in * bits / 32;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= out * words) return;
+  const int64_t r = idx / words, w = idx % words;
+  const int64_t bit0 = 32 * w, c0 = bit0 / bits;
+  const uint8_t* cr = codes + r * in;
+  uint32_t v[17];
+#pragma unroll
+  for (int k = 0; k < 17; ++k) v[k] = cr[c0 + k < in ? c0 + k : in - 1];
+  uint64_t acc = 0;
+#pragma unroll
+  for (int k = 0; k < 17; ++k) {
+    const int64_t c = c0 + k, off = c * bits - bit0;
+    const bool use = c < in && off < 32;
+    acc |= (uint64_t)(use ? v[k] : 0u) << (use ? off + 8 : 0);
+  }
+  packed[r * words + w] = (uint32_t)(acc >> 8);
 }
 
 // sum of a[i] * b[i] over n elements into *red (fp64)
@@ -391,13 +524,52 @@ ColKernel pick_kernel(int B, int G) {
   return nullptr;
 }
 
+// dst[r][c] = src[rows ? rows[r] : r][idx[c]] without LDS staging (rows longer than 64 KB)
+template <typename T>
+__global__ __launch_bounds__(256) void gather_cols_direct_kernel(const T* __restrict__ src,
+                                                                 T* __restrict__ dst, int64_t n,
+                                                                 const int32_t* __restrict__ idx,
+                                                                 const int32_t* __restrict__ rows) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r = blockIdx.y;
+  if (c >= n) return;
+  const int64_t sr = rows ? rows[r] : r;
+  dst[r * n + c] = src[sr * n + idx[c]];
+}
+
+// Largest row staged in LDS by the row kernels (KQ_ROW_LDS_MAX bytes; 0 forces the direct
+// paths, which otherwise serve rows longer than 16384 floats).
+size_t row_lds_max() {
+  const char* env = getenv("KQ_ROW_LDS_MAX");
+  if (env) {
+    const long v = atol(env);
+    if (v >= 0 && v <= 65536) return (size_t)v;
+  }
+  return 65536;
+}
+
+template <typename T>
+kq_status gather_cols(const T* src, T* dst, int64_t nrows, int64_t n, const int32_t* idx,
+                      const int32_t* rows, hipStream_t s) {
+  const size_t bytes = (size_t)n * sizeof(T);
+  if (bytes <= row_lds_max()) {
+    gather_cols_kernel<T><<<dim3((unsigned)nrows), dim3(256), bytes, s>>>(src, dst, n, idx, rows);
+    KQ_LAUNCHED("gather_cols_kernel");
+  } else {
+    gather_cols_direct_kernel<T><<<dim3((unsigned)ceil_div(n, 256), (unsigned)nrows), dim3(256), 0,
+                                   s>>>(src, dst, n, idx, rows);
+    KQ_LAUNCHED("gather_cols_direct_kernel");
+  }
+  return KQ_OK;
+}
+
 struct Layout {
-  size_t f, t, y, d, dead, scal, flag, tmp, total;
+  size_t f, t, y, d, dead, scal, flag, tmp, perm, invperm, ptmp, ctmp, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-Layout layout(int64_t out, int64_t in, int B, bool with_loss) {
+Layout layout(int64_t out, int64_t in, int B, bool with_loss, bool act_order) {
   Layout L;
   size_t o = 0;
   L.f = o;    o = align256(o + (size_t)in * in * sizeof(float));
@@ -408,6 +580,14 @@ Layout layout(int64_t out, int64_t in, int B, bool with_loss) {
   L.scal = o; o = align256(o + 8 * sizeof(double));
   L.flag = o; o = align256(o + 4 * sizeof(int));
   L.tmp = o;  if (with_loss) o = align256(o + (size_t)out * in * sizeof(float));
+  // act_order: the permutation and its inverse, a staging matrix and the permuted codes
+  L.perm = L.invperm = L.ptmp = L.ctmp = o;
+  if (act_order) {
+    L.perm = o;    o = align256(o + (size_t)in * sizeof(int32_t));
+    L.invperm = o; o = align256(o + (size_t)in * sizeof(int32_t));
+    L.ptmp = o;    o = align256(o + (size_t)out * in * sizeof(float));
+    L.ctmp = o;    o = align256(o + (size_t)out * in);
+  }
   L.total = o;
   return L;
 }
@@ -416,7 +596,8 @@ kq_status check_params(const kq_quant_params* p, int64_t out, int64_t in) {
   if (!p) return fail(KQ_EINVAL, "kq_quantize_layer: params is NULL");
   if (p->bits < 2 || p->bits > 4) return fail(KQ_EINVAL, "bits must be 2, 3 or 4 (got %d)", p->bits);
   if (p->asym != 1) return fail(KQ_ENOTIMPL, "only the asymmetric grid (asym = 1) is implemented");
-  if (p->act_order != 0) return fail(KQ_ENOTIMPL, "act_order is not implemented");
+  if (p->act_order != 0 && p->act_order != 1) return fail(KQ_EINVAL, "act_order must be 0 or 1");
+  if (p->w_clip != 0 && p->w_clip != 1) return fail(KQ_EINVAL, "w_clip must be 0 or 1");
   if (!(p->damp >= 0.f) || !isfinite(p->damp)) return fail(KQ_EINVAL, "damp must be >= 0");
   if (p->block != 64 && p->block != 128) return fail(KQ_EINVAL, "block must be 64 or 128");
   if (out < 1 || in < 1 || in > (1 << 30) || out > (1 << 22))
@@ -428,6 +609,8 @@ kq_status check_params(const kq_quant_params* p, int64_t out, int64_t in) {
   if (p->group != in && (p->group > p->block || p->block % p->group != 0 ||
                          (p->group != 16 && p->group != 32 && p->group != 64 && p->group != 128)))
     return fail(KQ_ESHAPE, "group must be in {16, 32, 64, 128} dividing block, or equal to in");
+  if ((p->act_order || p->w_clip) && p->group != in)
+    return fail(KQ_ENOTIMPL, "act_order and w_clip take one grid per row (group == in)");
   return KQ_OK;
 }
 
@@ -439,7 +622,7 @@ extern "C" kq_status kq_quantize_layer_workspace(const kq_quant_params* p, int64
   using namespace kq;
   if (!bytes) return fail(KQ_EINVAL, "kq_quantize_layer_workspace: bytes is NULL");
   KQ_TRY(check_params(p, out, in));
-  *bytes = layout(out, in, p->block, with_loss != 0).total;
+  *bytes = layout(out, in, p->block, with_loss != 0, p->act_order != 0).total;
   return KQ_OK;
 }
 
@@ -454,9 +637,11 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
     return fail(KQ_EINVAL, "kq_quantize_layer: NULL argument");
   const bool with_loss = loss_opt != nullptr;
   const int B = p->block;
-  // a group spanning the whole row (group == in > block) takes its grid from the original row
-  const int G = p->group == in && p->group > B ? 0 : p->group;
-  const Layout L = layout(out, in, B, with_loss);
+  const bool ao = p->act_order != 0, clip = p->w_clip != 0;
+  // a group spanning the whole row (group == in > block, or any row grid with act_order or
+  // w_clip) takes its grid from the original row
+  const int G = p->group == in && (p->group > B || ao || clip) ? 0 : p->group;
+  const Layout L = layout(out, in, B, with_loss, ao);
   if (!ws || ws_bytes < L.total)
     return fail(KQ_EWORKSPACE, "kq_quantize_layer: workspace of %zu bytes needed", L.total);
   ColKernel kern = pick_kernel(B, G);
@@ -471,18 +656,34 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
   double* scal = (double*)(base + L.scal);
   int* flag = (int*)(base + L.flag);
 
+  int32_t* perm = (int32_t*)(base + L.perm);
+  int32_t* invperm = (int32_t*)(base + L.invperm);
+  float* Ptmp = (float*)(base + L.ptmp);
+  uint8_t* ctmp = (uint8_t*)(base + L.ctmp);
+
   KQ_TRY(fill_u32((uint32_t*)scal, 16, 0u, s));
   KQ_TRY(fill_u32((uint32_t*)flag, 4, 0u, s));
-  KQ_TRY(damp_and_factor(HX_rot, F, T, dead, scal, flag, in, p->damp, B, s));
+  if (ao) {
+    // act_order: F = H~_X[perm][perm] and W~ <- W~[:, perm]; GPTQ then runs in that order
+    act_order_perm_kernel<<<dim3((unsigned)ceil_div(in, 256)), dim3(256), 0, s>>>(HX_rot, in, perm,
+                                                                                  invperm);
+    KQ_LAUNCHED("act_order_perm_kernel");
+    KQ_TRY(gather_cols<float>(HX_rot, F, in, in, perm, perm, s));
+    KQ_TRY(gather_cols<float>(W_rot, Ptmp, out, in, perm, nullptr, s));
+    KQ_HIP(hipMemcpyAsync(W_rot, Ptmp, (size_t)out * in * sizeof(float), hipMemcpyDeviceToDevice, s));
+  }
+  KQ_TRY(damp_and_factor(ao ? nullptr : HX_rot, F, T, dead, scal, flag, in, p->damp, B, s));
 
   ColArgs a;
   a.W = W_rot; a.out = out; a.in = in; a.Y = Y; a.D = Dm; a.U = F; a.dead = dead;
   a.nsplit = 0; a.ystride = out * B;
   a.bits = p->bits; a.maxq = (float)((1 << p->bits) - 1);
   a.ngroups = in / p->group; a.scales = scales; a.zeros = zeros;
-  a.packed = packed; a.codes = codes_opt;
+  a.packed = ao ? nullptr : packed; a.codes = ao ? ctmp : codes_opt;
   if (G == 0) {
-    row_grid_kernel<<<dim3((unsigned)out), dim3(256), 0, s>>>(W_rot, in, dead, a.maxq, scales, zeros);
+    const int lds_row = clip && in * sizeof(float) <= row_lds_max();
+    row_grid_kernel<<<dim3((unsigned)out), dim3(256), lds_row ? in * sizeof(float) : 0, s>>>(
+        W_rot, in, dead, a.maxq, scales, zeros, clip ? 1 : 0, lds_row);
     KQ_LAUNCHED("row_grid_kernel");
   }
   const int cus = device_cu_count();
@@ -495,11 +696,11 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
       g.B = F + j0; g.ldb = in; g.transB = false;
       g.C = Y; g.ldc = B; g.alpha = 1.0f; g.accumulate = false; g.upper_only = false;
       // one workgroup per CU (the product keeps a 128 KB LDS ring): split K so that one round
-      // of workgroups covers the GPU, with at least 256 of K per split; each split stores its
-      // own slice, which the column kernel sums
+      // of workgroups covers the GPU, down to one 32-deep stage per split; each split stores
+      // its own slice, which the column kernel sums
       const int64_t tiles = ceil_div(out, 128);
       int64_t split = cus / tiles;
-      const int64_t max_split = ceil_div(j0, 256);
+      const int64_t max_split = ceil_div(j0, 32);
       if (split > max_split) split = max_split;
       if (split > y_slots(out)) split = y_slots(out);
       if (split < 1) split = 1;
@@ -510,6 +711,21 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
     }
     kern<<<dim3(col_grid), dim3(CTHREADS), 0, s>>>(a, j0);
     KQ_LAUNCHED("gptq_block_kernel");
+  }
+  if (ao) {
+    // back to the original column order: errors, W~ - Qhat (for the losses), codes, packing
+    KQ_TRY(gather_cols<float>(W_rot, Ptmp, out, in, invperm, nullptr, s));
+    KQ_HIP(hipMemcpyAsync(W_rot, Ptmp, (size_t)out * in * sizeof(float), hipMemcpyDeviceToDevice, s));
+    if (with_loss) {
+      KQ_TRY(gather_cols<float>(Dm, Ptmp, out, in, invperm, nullptr, s));
+      KQ_HIP(hipMemcpyAsync(Dm, Ptmp, (size_t)out * in * sizeof(float), hipMemcpyDeviceToDevice, s));
+    }
+    uint8_t* cout = codes_opt ? codes_opt : (uint8_t*)Ptmp;
+    KQ_TRY(gather_cols<uint8_t>(ctmp, cout, out, in, invperm, nullptr, s));
+    const int64_t nw = out * (in * p->bits / 32);
+    pack_rows_kernel<<<dim3((unsigned)ceil_div(nw, 256)), dim3(256), 0, s>>>(cout, out, in, p->bits,
+                                                                            packed);
+    KQ_LAUNCHED("pack_rows_kernel");
   }
 
   if (with_loss) {

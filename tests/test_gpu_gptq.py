@@ -26,11 +26,12 @@ def spd(rng, n, T=None, outliers=0):
     return A.T @ A
 
 
-def gpu_quantize(Wt, HXt, HGt, bits, group, block, damp=0.01, want_loss=True):
+def gpu_quantize(Wt, HXt, HGt, bits, group, block, damp=0.01, want_loss=True, act_order=0,
+                 w_clip=0):
     torch = torch_cuda()
     import post_quantization_syrk_amd as kq
     out_n, in_n = Wt.shape
-    p = kq.make_params(bits, group, block, damp)
+    p = kq.make_params(bits, group, block, damp, act_order=act_order, w_clip=w_clip)
     ws = torch.empty(kq.kq_quantize_layer_workspace(p, out_n, in_n, want_loss), dtype=torch.uint8,
                      device="cuda")
     W = torch.from_numpy(np.ascontiguousarray(Wt, dtype=np.float32)).cuda()
@@ -48,9 +49,15 @@ def gpu_quantize(Wt, HXt, HGt, bits, group, block, damp=0.01, want_loss=True):
                 codes=codes.cpu().numpy().astype(np.int64), loss=loss)
 
 
-def check_against_oracle(g, Wt, HXt, HGt, bits, group, damp=0.01, rows=None):
-    ref = o.quantize_layer(Wt, HXt, HGt, bits, group, damp, replay_codes=g["codes"] if rows is None
-                           else g["codes"][rows], rows=rows)
+def check_against_oracle(g, Wt, HXt, HGt, bits, group, damp=0.01, rows=None, act_order=False,
+                         w_clip=False):
+    sel = slice(None) if rows is None else rows
+    ref = o.quantize_layer(Wt, HXt, HGt, bits, group, damp, replay_codes=g["codes"][sel],
+                           rows=rows, act_order=act_order, w_clip=w_clip,
+                           replay_scales=g["scales"][sel][:, 0] if w_clip else None)
+    if w_clip:
+        # the clip search: same candidate as the oracle, or one within 1e-5 of its best error
+        assert ref["clip_hard_mismatches"] == 0
     res = ref["gptq"]
     n_codes = res.codes.size
     assert res.hard_mismatches == 0, f"{res.hard_mismatches} hard mismatches at {res.mismatch_positions[:5]}"
@@ -86,6 +93,55 @@ def test_quantize_synthetic_layers(bits, group, block):
     Wt = Wt.astype(np.float32).astype(np.float64)
     g = gpu_quantize(Wt, HXt, HGt, bits, group, block)
     check_against_oracle(g, Wt, HXt, HGt, bits, group)
+
+
+@pytest.mark.parametrize("bits,block,act_order,w_clip,with_hg", [
+    (2, 128, 1, 0, True), (3, 64, 1, 0, False), (4, 128, 0, 1, True), (2, 64, 0, 1, False),
+    (2, 128, 1, 1, True), (3, 128, 1, 1, False), (4, 64, 1, 1, True)])
+def test_quantize_act_order_and_clip(bits, block, act_order, w_clip, with_hg):
+    """The base recipe's options: one grid per row (group = in), act_order and/or w_clip."""
+    announce(f"gptq act_order={act_order} w_clip={w_clip} bits={bits} block={block}")
+    rng = np.random.default_rng(bits * 10 + block + 3 * act_order + 5 * w_clip)
+    out_n, in_n = 72, 256
+    Wt = rng.standard_normal((out_n, in_n)) * 0.05
+    Wt[:, rng.choice(in_n, 3, replace=False)] *= 8
+    HXt = spd(rng, in_n, outliers=3).astype(np.float32).astype(np.float64)
+    HGt = spd(rng, out_n).astype(np.float32).astype(np.float64) if with_hg else None
+    Wt = Wt.astype(np.float32).astype(np.float64)
+    g = gpu_quantize(Wt, HXt, HGt, bits, in_n, block, act_order=act_order, w_clip=w_clip)
+    ref = check_against_oracle(g, Wt, HXt, HGt, bits, in_n, act_order=bool(act_order),
+                               w_clip=bool(w_clip))
+    if act_order:
+        assert not np.array_equal(ref["perm"], np.arange(in_n))
+    if w_clip:
+        assert np.any(ref["clip_choice"] > 0)
+
+
+def test_quantize_act_order_dead_channel_and_direct_paths(monkeypatch):
+    """act_order with a dead channel (its zero diagonal ranks as 1), and the row kernels'
+    direct (no LDS staging) paths that rows longer than 16384 floats take."""
+    monkeypatch.setenv("KQ_ROW_LDS_MAX", "0")
+    announce("gptq act_order + w_clip, dead channel, direct row paths")
+    rng = np.random.default_rng(41)
+    HXt = spd(rng, 192, outliers=2)
+    HXt[7, :] = 0
+    HXt[:, 7] = 0
+    HXt = HXt.astype(np.float32).astype(np.float64)
+    Wt = (rng.standard_normal((40, 192)) * 0.05).astype(np.float32).astype(np.float64)
+    g = gpu_quantize(Wt, HXt, None, 3, 192, 64, act_order=1, w_clip=1)
+    ref = check_against_oracle(g, Wt, HXt, None, 3, 192, act_order=True, w_clip=True)
+    assert ref["dead"][7]
+    assert np.all(g["codes"][:, 7] == g["zeros"][:, 0])   # a zeroed column codes as the zero point
+
+
+def test_act_order_needs_one_grid_per_row():
+    torch = torch_cuda()
+    import post_quantization_syrk_amd as kq
+    for kw in ({"act_order": 1}, {"w_clip": 1}):
+        p = kq.make_params(2, 64, 64, **kw)
+        with pytest.raises(kq.KQError) as e:
+            kq.kq_quantize_layer_workspace(p, 16, 128, False)
+        assert e.value.status == kq.KQ_ENOTIMPL
 
 
 def test_quantize_without_hg_and_ragged_rows():
