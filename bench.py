@@ -36,7 +36,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 
-WORKLOADS = {"c1": syn.C1, "c2": syn.C2, "c3": syn.C3, "c5": syn.C5}
+WORKLOADS = {"c1": syn.C1, "c2": syn.C2, "c2r": syn.C2R, "c3": syn.C3, "c5": syn.C5}
 
 
 def parse():
@@ -128,11 +128,13 @@ def cpu_baseline(cfg, budget_s: float) -> dict:
                                 syn.signs(cfg, "out"), cfg.alpha, o.BIIP_FULL, cfg.had_in, cfg.had_out)
     t["sensitivity_biip"] = time.perf_counter() - t0
     t0 = time.perf_counter()
-    fac = o.damp_and_factor(HXt, cfg.damp)
+    perm = o.act_order_perm(HXt) if cfg.act_order else np.arange(in_n)
+    fac = o.damp_and_factor(HXt[np.ix_(perm, perm)] if cfg.act_order else HXt, cfg.damp)
     t["factor"] = time.perf_counter() - t0
     rows = np.random.default_rng(0).choice(out_n, R_s, replace=False)
     t0 = time.perf_counter()
-    r = o.quantize_layer(Wt, HXt, None, cfg.bits, cfg.group, cfg.damp, rows=rows, factor=fac)
+    r = o.quantize_layer(Wt, HXt, None, cfg.bits, cfg.group, cfg.damp, rows=rows, factor=fac,
+                         act_order=bool(cfg.act_order), w_clip=bool(cfg.w_clip))
     o.pack_codes(r["gptq"].codes, cfg.bits)
     t["gptq_pack_sample"] = time.perf_counter() - t0
     full = (t["hessians_sample"] * T / T_s + t["sensitivity_biip"] + t["factor"]
@@ -182,7 +184,8 @@ def main():
     Wt = torch.empty_like(W0)
     d_in = torch.empty(in_n, device=dev)
     d_out = torch.empty(out_n, device=dev)
-    p = kq.make_params(cfg.bits, cfg.group, cfg.block, cfg.damp)
+    p = kq.make_params(cfg.bits, cfg.group, cfg.block, cfg.damp, act_order=cfg.act_order,
+                       w_clip=cfg.w_clip)
     ws = torch.empty(kq.kq_quantize_layer_workspace(p, out_n, in_n, False), dtype=torch.uint8, device=dev)
     packed = torch.empty((out_n, in_n * cfg.bits // 32), dtype=torch.int32, device=dev)
     scales = torch.empty((out_n, in_n // cfg.group), device=dev)
@@ -256,7 +259,8 @@ def main():
         "data": "synthetic (seeded log-normal-channel streams, Llama-shaped)",
         "config": {"workload": cfg.name, "out": out_n, "in": in_n, "tokens": T, "bits": cfg.bits,
                    "group": cfg.group, "block": cfg.block, "hadamard_in": cfg.had_in,
-                   "hadamard_out": cfg.had_out, "alpha": cfg.alpha, "damp": cfg.damp},
+                   "hadamard_out": cfg.had_out, "alpha": cfg.alpha, "damp": cfg.damp,
+                   "act_order": cfg.act_order, "w_clip": cfg.w_clip},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},

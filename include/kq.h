@@ -180,7 +180,7 @@ kq_status kq_quantize_layer_workspace(const kq_quant_params* p, int64_t out, int
  *     packed words, errors in W_rot, losses) is still in the original column order.
  *   w_clip = 1: the row's grid is the min-max grid of the shrunk range [p xmin, p xmax]
  *     for the p in {1 - i/100 : i = 0..79} with the smallest sum |qhat - w|^2.4 over the
- *     row (the first such p on equal sums; errors in fp32, summed in fp64).
+ *     row (the first such p on equal sums; fp32 terms and per-thread sums, added in fp64).
  * Implementation: reverse-order Cholesky H_d = R R^T (R upper), U = R^-1 formed only
  * in its diagonal blocks, and the column recursion run 128 (or 64) columns at a time
  * with one matrix product per block for the feedback from earlier blocks

@@ -336,8 +336,8 @@ __device__ __forceinline__ float pow24(float d) {
 // One (row) group spanning the whole row: grid from the original row (dead columns zeroed),
 // one workgroup per row.  With clip, the grid of the shrunk range [p xmin, p xmax] for
 // p = 1 - i/100, i < 80, with the smallest sum |s (q - z) - w|^2.4 over the row (the first
-// such p on equal sums; per-element terms in fp32, summed in fp64).  The row is staged in
-// LDS when it fits (rows_in_lds).
+// such p on equal sums; each thread sums its terms in fp32, the threads' sums are added in
+// fp64).  The row is staged in LDS when it fits (rows_in_lds).
 constexpr int CLIP_CANDIDATES = 80;
 __global__ __launch_bounds__(256) void row_grid_kernel(const float* __restrict__ W, int64_t in,
                                                        const uint8_t* __restrict__ dead, float maxq,
@@ -386,13 +386,14 @@ __global__ __launch_bounds__(256) void row_grid_kernel(const float* __restrict__
     float s = (xmax - xmin) / maxq;
     if (xmax == xmin) s = 1.0f;
     const float z = rintf(-xmin / s), inv = 1.0f / s;
-    double e = 0.0;
+    float ef = 0.0f;
 #pragma unroll 4
     for (int64_t c = t; c < in; c += 256) {
       const float w = rows_in_lds ? rowbuf[c] : (dead[c] ? 0.f : row[c]);
-      const float q = fminf(fmaxf(rintf(w * inv) + z, 0.0f), maxq);
-      e += (double)pow24(fabsf(s * (q - z) - w));
+      const float q = __builtin_amdgcn_fmed3f(rintf(w * inv) + z, 0.0f, maxq);
+      ef += pow24(fabsf(s * (q - z) - w));
     }
+    double e = (double)ef;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) e += __shfl_xor(e, o);
     if ((t & 63) == 0) sred[t >> 6] = e;
@@ -413,36 +414,73 @@ __global__ __launch_bounds__(256) void row_grid_kernel(const float* __restrict__
   }
 }
 
-// act_order: rank of column i by descending diag(H) (a zero diagonal counts as 1, equal values
-// by index); perm[rank] = i, invperm[i] = rank.  The diagonal is staged through LDS in chunks.
-// A NaN diagonal counts as -inf, so the order stays total and the ranks a permutation.
+// act_order: column i's rank by descending diag(H) (a zero diagonal counts as 1, equal values
+// by index), perm[rank] = i, invperm[i] = rank.  A NaN diagonal counts as -inf, so the order
+// stays total and the ranks a permutation.  Three steps: the keys; partial ranks of 256
+// columns against a 1024-key chunk per workgroup (atomically added); perm from the ranks.
 __device__ __forceinline__ float act_key(float v) {
   return v == 0.f ? 1.f : (v != v ? -INFINITY : v);
 }
-__global__ __launch_bounds__(256) void act_order_perm_kernel(const float* __restrict__ H, int64_t n,
-                                                             int32_t* __restrict__ perm,
-                                                             int32_t* __restrict__ invperm) {
-  __shared__ float dch[1024];
+
+__global__ __launch_bounds__(256) void act_keys_kernel(const float* __restrict__ H, int64_t n,
+                                                       float* __restrict__ key,
+                                                       int32_t* __restrict__ rank) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) {
+    key[i] = act_key(H[i * n + i]);
+    rank[i] = 0;
+  }
+}
+
+constexpr int RCHUNK = 1024;
+__global__ __launch_bounds__(256) void act_rank_kernel(const float* __restrict__ key, int64_t n,
+                                                       int32_t* __restrict__ rank) {
+  __shared__ __attribute__((aligned(16))) float kc[RCHUNK];
   const int t = threadIdx.x;
   const int64_t i = (int64_t)blockIdx.x * 256 + t;
-  const float di = i < n ? act_key(H[i * n + i]) : 0.f;
-  int64_t rank = 0;
-  for (int64_t j0 = 0; j0 < n; j0 += 1024) {
-    __syncthreads();
-    for (int k = t; k < 1024; k += 256) {
-      const int64_t j = j0 + k;
-      dch[k] = j < n ? act_key(H[j * n + j]) : 0.f;
+  const int64_t j0 = (int64_t)blockIdx.y * RCHUNK;
+#pragma unroll
+  for (int k = t; k < RCHUNK; k += 256) {
+    const int64_t j = j0 + k;
+    // past the end: -inf with an index above every i, so it never outranks anything
+    kc[k] = j < n ? key[j] : -INFINITY;
+  }
+  __syncthreads();
+  if (i >= n) return;
+  const float di = key[i];
+  int cnt = 0;
+  const int64_t m = min((int64_t)RCHUNK, n - j0);
+  if (j0 + m <= i) {
+    // every key of the chunk has a smaller index, so ties count (the chunk is full here:
+    // only the last chunk is short, and it ends at n > i)
+#pragma unroll 8
+    for (int k = 0; k < RCHUNK; k += 4) {
+      const float4 v = *(const float4*)(kc + k);
+      cnt += (v.x >= di) + (v.y >= di) + (v.z >= di) + (v.w >= di);
     }
-    __syncthreads();
-    const int64_t m = min((int64_t)1024, n - j0);
-    for (int64_t k = 0; k < m; ++k) {
-      const float dj = dch[k];
-      rank += (dj > di) | ((dj == di) & (j0 + k < i));
+  } else if (j0 > i) {
+    // every key has a larger index, so ties do not count (padding keys are -inf: never greater)
+#pragma unroll 8
+    for (int k = 0; k < RCHUNK; k += 4) {
+      const float4 v = *(const float4*)(kc + k);
+      cnt += (v.x > di) + (v.y > di) + (v.z > di) + (v.w > di);
+    }
+  } else {
+    for (int k = 0; k < m; ++k) {
+      const float dj = kc[k];
+      cnt += (dj > di) | ((dj == di) & (j0 + k < i));
     }
   }
+  atomicAdd(rank + i, cnt);
+}
+
+__global__ __launch_bounds__(256) void act_perm_kernel(const int32_t* __restrict__ rank, int64_t n,
+                                                       int32_t* __restrict__ perm,
+                                                       int32_t* __restrict__ invperm) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) {
-    perm[rank] = (int32_t)i;
-    invperm[i] = (int32_t)rank;
+    perm[rank[i]] = (int32_t)i;
+    invperm[i] = rank[i];
   }
 }
 
@@ -665,17 +703,24 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
   KQ_TRY(fill_u32((uint32_t*)flag, 4, 0u, s));
   if (ao) {
     // act_order: F = H~_X[perm][perm] and W~ <- W~[:, perm]; GPTQ then runs in that order
-    act_order_perm_kernel<<<dim3((unsigned)ceil_div(in, 256)), dim3(256), 0, s>>>(HX_rot, in, perm,
-                                                                                  invperm);
-    KQ_LAUNCHED("act_order_perm_kernel");
+    float* keys = Ptmp;   // free until W~ is gathered
+    int32_t* rank = invperm;
+    const unsigned cb = (unsigned)ceil_div(in, 256);
+    act_keys_kernel<<<dim3(cb), dim3(256), 0, s>>>(HX_rot, in, keys, rank);
+    KQ_LAUNCHED("act_keys_kernel");
+    act_rank_kernel<<<dim3(cb, (unsigned)ceil_div(in, RCHUNK)), dim3(256), 0, s>>>(keys, in, rank);
+    KQ_LAUNCHED("act_rank_kernel");
+    act_perm_kernel<<<dim3(cb), dim3(256), 0, s>>>(rank, in, perm, invperm);
+    KQ_LAUNCHED("act_perm_kernel");
     KQ_TRY(gather_cols<float>(HX_rot, F, in, in, perm, perm, s));
     KQ_TRY(gather_cols<float>(W_rot, Ptmp, out, in, perm, nullptr, s));
-    KQ_HIP(hipMemcpyAsync(W_rot, Ptmp, (size_t)out * in * sizeof(float), hipMemcpyDeviceToDevice, s));
   }
+  // the weights GPTQ works on (and leaves its errors in): W~, or its permuted copy
+  float* Wq = ao ? Ptmp : W_rot;
   KQ_TRY(damp_and_factor(ao ? nullptr : HX_rot, F, T, dead, scal, flag, in, p->damp, B, s));
 
   ColArgs a;
-  a.W = W_rot; a.out = out; a.in = in; a.Y = Y; a.D = Dm; a.U = F; a.dead = dead;
+  a.W = Wq; a.out = out; a.in = in; a.Y = Y; a.D = Dm; a.U = F; a.dead = dead;
   a.nsplit = 0; a.ystride = out * B;
   a.bits = p->bits; a.maxq = (float)((1 << p->bits) - 1);
   a.ngroups = in / p->group; a.scales = scales; a.zeros = zeros;
@@ -683,7 +728,7 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
   if (G == 0) {
     const int lds_row = clip && in * sizeof(float) <= row_lds_max();
     row_grid_kernel<<<dim3((unsigned)out), dim3(256), lds_row ? in * sizeof(float) : 0, s>>>(
-        W_rot, in, dead, a.maxq, scales, zeros, clip ? 1 : 0, lds_row);
+        Wq, in, dead, a.maxq, scales, zeros, clip ? 1 : 0, lds_row);
     KQ_LAUNCHED("row_grid_kernel");
   }
   const int cus = device_cu_count();
@@ -712,15 +757,17 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
     kern<<<dim3(col_grid), dim3(CTHREADS), 0, s>>>(a, j0);
     KQ_LAUNCHED("gptq_block_kernel");
   }
+  // W~ - Qhat in the original column order, for the losses
+  const float* dW = Dm;
   if (ao) {
-    // back to the original column order: errors, W~ - Qhat (for the losses), codes, packing
-    KQ_TRY(gather_cols<float>(W_rot, Ptmp, out, in, invperm, nullptr, s));
-    KQ_HIP(hipMemcpyAsync(W_rot, Ptmp, (size_t)out * in * sizeof(float), hipMemcpyDeviceToDevice, s));
+    // back to the original column order: errors into W_rot, W~ - Qhat (for the losses) into
+    // the staging buffer, codes (into D's memory when the caller keeps none), packing
+    KQ_TRY(gather_cols<float>(Ptmp, W_rot, out, in, invperm, nullptr, s));
     if (with_loss) {
       KQ_TRY(gather_cols<float>(Dm, Ptmp, out, in, invperm, nullptr, s));
-      KQ_HIP(hipMemcpyAsync(Dm, Ptmp, (size_t)out * in * sizeof(float), hipMemcpyDeviceToDevice, s));
+      dW = Ptmp;
     }
-    uint8_t* cout = codes_opt ? codes_opt : (uint8_t*)Ptmp;
+    uint8_t* cout = codes_opt ? codes_opt : (uint8_t*)Dm;
     KQ_TRY(gather_cols<uint8_t>(ctmp, cout, out, in, invperm, nullptr, s));
     const int64_t nw = out * (in * p->bits / 32);
     pack_rows_kernel<<<dim3((unsigned)ceil_div(nw, 256)), dim3(256), 0, s>>>(cout, out, in, p->bits,
@@ -729,7 +776,7 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
   }
 
   if (with_loss) {
-    const float* dW = Dm;   // W~ - Qhat
+    // dW = W~ - Qhat
     float* tmp = (float*)(base + L.tmp);
     // predicted loss  sum_j e_j^T H~_G e_j
     if (HG_rot) {

@@ -59,6 +59,8 @@ class LayerConfig:
     had_out: int = 0
     damp: float = 0.01
     alpha: float = 0.25
+    act_order: int = 0             # quantizer options (group must then equal inp)
+    w_clip: int = 0
     seed: int = 0
     layer: int = 0
     # streams shared between sublayers (c4): ids of the X and G streams
@@ -96,7 +98,11 @@ C5 = LayerConfig(name="llama3-70b-up_proj-28672x8192-T262144-W2", cfg_index=5, o
                  sigma_x=1.0, sigma_g=1.5, bits=2, group=128, block=128,
                  had_in=8192, had_out=4096)
 
-CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c5": C5}
+# c2 with the base recipe's quantizer options (--w_groupsize -1 --w_clip --act_order)
+C2R = C2.scaled(name="llama2-7b-q_proj-4096x4096-T131072-W4-rowgrid-clip-actorder", group=4096,
+                act_order=1, w_clip=1)
+
+CONFIGS = {"c1": C1, "c2": C2, "c2r": C2R, "c3": C3, "c5": C5}
 
 # Decoder-stack workload (32 Llama-2-7B layers, 7 linears each, 32768 tokens).
 LLAMA2_7B_SUBLAYERS = (

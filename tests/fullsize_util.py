@@ -68,7 +68,8 @@ def run_engine(cfg, bx, bg, W, s_in, s_out, want_loss=True, keep_raw=True, hg_ho
     out["HGt_trace"] = float(torch.diagonal(HG).double().sum().item())
     out["HGt"] = HG.cpu().numpy() if hg_host else None
     out["d_in"], out["d_out"] = di.cpu().numpy(), do.cpu().numpy()
-    p = kq.make_params(cfg.bits, cfg.group, cfg.block, cfg.damp)
+    p = kq.make_params(cfg.bits, cfg.group, cfg.block, cfg.damp, act_order=cfg.act_order,
+                       w_clip=cfg.w_clip)
     ws = torch.empty(kq.kq_quantize_layer_workspace(p, cfg.out, cfg.inp, want_loss), dtype=torch.uint8,
                      device=dev)
     packed = torch.zeros((cfg.out, cfg.inp * cfg.bits // 32), dtype=torch.int32, device=dev)
@@ -91,10 +92,22 @@ def dequant(codes, scales, zeros, group):
     return s * (codes - z)
 
 
+def oracle_factor(HXt, cfg):
+    """The oracle's damped factor of H~_X, in the column order GPTQ visits (act_order)."""
+    if cfg.act_order:
+        perm = o.act_order_perm(HXt)
+        return o.damp_and_factor(HXt[np.ix_(perm, perm)], cfg.damp)
+    return o.damp_and_factor(HXt, cfg.damp)
+
+
 def check_rows(g, Wt_ref, HXt_ref, cfg, rows, factor):
     """Sampled-row GPTQ parity (replay rule) and packed/scale/zero/error checks."""
     ref = o.quantize_layer(Wt_ref, HXt_ref, None, cfg.bits, cfg.group, cfg.damp,
-                           replay_codes=g["codes"][rows], rows=rows, factor=factor)
+                           replay_codes=g["codes"][rows], rows=rows, factor=factor,
+                           act_order=bool(cfg.act_order), w_clip=bool(cfg.w_clip),
+                           replay_scales=g["scales"][rows][:, 0] if cfg.w_clip else None)
+    if cfg.w_clip:
+        assert ref["clip_hard_mismatches"] == 0
     res = ref["gptq"]
     assert res.hard_mismatches == 0, f"{res.hard_mismatches} hard mismatches, first {res.mismatch_positions[:5]}"
     assert res.accepted_ties <= 0.001 * res.codes.size

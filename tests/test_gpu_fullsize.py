@@ -17,7 +17,8 @@ import pytest
 
 import oracle as o
 import synthetic as syn
-from tests.fullsize_util import check_rows, dequant, oracle_diag, oracle_hessian, run_engine
+from tests.fullsize_util import (check_rows, dequant, oracle_diag, oracle_factor, oracle_hessian,
+                                 run_engine)
 from tests.gpu_util import announce, rel_fro, torch_cuda
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -33,11 +34,12 @@ def _layer_inputs(cfg):
     return bx, bg, W, syn.signs(cfg, "in"), syn.signs(cfg, "out")
 
 
-@pytest.mark.parametrize("name", ["c2", "c3"])
+@pytest.mark.parametrize("name", ["c2", "c3", "c2r"])
 def test_layer_full_pipeline(name):
-    """Llama-2-7B q_proj (W4) and down_proj (W2, 43 x 256 input Hadamard) at full size."""
+    """Llama-2-7B q_proj (W4) and down_proj (W2, 43 x 256 input Hadamard) at full size; q_proj
+    again with the base recipe's quantizer options (one grid per row, w_clip, act_order)."""
     torch_cuda()
-    cfg = {"c2": syn.C2, "c3": syn.C3}[name]
+    cfg = {"c2": syn.C2, "c3": syn.C3, "c2r": syn.C2R}[name]
     bx, bg, W, s_in, s_out = _layer_inputs(cfg)
     g = run_engine(cfg, bx, bg, W, s_in, s_out, want_loss=True)
     t0 = time.time()
@@ -58,11 +60,21 @@ def test_layer_full_pipeline(name):
     announce(f"{name}: W~ rel {ew:.2e}, H~_X rel {ehx:.2e}, H~_G rel {ehg:.2e}")
     assert ew <= 1e-5 and ehx <= 1e-5 and ehg <= 1e-5
     t0 = time.time()
-    fac = o.damp_and_factor(HXt, cfg.damp)
+    # GPTQ stage.  act_order ranks a nearly flat rotated diagonal, so its order follows the
+    # 1e-7 differences between the engine's fp32 H~_X and the oracle's fp64 one: with act_order
+    # the stage takes the engine's upstream output (H~_X, W~ upcast), as the stage-wise protocol
+    # does for every stage; without it the oracle's own processed factors serve.
+    Wq, Hq = (g["Wt"].astype(np.float64), g["HXt"].astype(np.float64)) if cfg.act_order else (Wt, HXt)
+    fac = oracle_factor(Hq, cfg)
     rows = np.sort(np.random.default_rng(cfg.cfg_index).choice(cfg.out, N_ROWS, replace=False))
-    res = check_rows(g, Wt, HXt, cfg, rows, fac)
+    res = check_rows(g, Wq, Hq, cfg, rows, fac)
     announce(f"{name}: {N_ROWS} sampled rows match ({res.accepted_ties} near-tie codes adopted) "
              f"in {time.time() - t0:.1f} s")
+    if cfg.act_order:
+        # how far the two diagonals' orders differ (reported, not gated)
+        pg, po = o.act_order_perm(Hq), o.act_order_perm(HXt)
+        announce(f"{name}: act_order positions differing between engine and oracle H~_X: "
+                 f"{int(np.sum(pg != po))} of {cfg.inp}")
     # losses of the engine's own codes / errors against the oracle's processed factors
     dW = Wt - dequant(g["codes"], g["scales"], g["zeros"], cfg.group)
     L_direct = o.proxy_loss(dW, HXt, HGt)
