@@ -25,7 +25,7 @@ __all__ = [
     "BIIP_OUT_ONLY", "damp_and_factor", "AsymMinMaxGrid", "FixedUniformGrid", "gptq",
     "GptqResult", "quantize_layer", "pack_codes", "unpack_codes", "proxy_loss", "predicted_loss",
     "allocate_bits", "brute_force_min_loss", "NotSPDError", "ClippedMinMaxGrid",
-    "act_order_perm", "CLIP_NORM", "CLIP_GRID", "CLIP_MAXSHRINK",
+    "act_order_perm", "CLIP_NORM", "CLIP_GRID", "CLIP_MAXSHRINK", "dequant", "deploy_linear",
 ]
 
 BIIP_FULL, BIIP_NO_RESCALE, BIIP_IN_ONLY, BIIP_OUT_ONLY = 0, 1, 2, 3
@@ -565,6 +565,36 @@ def quantize_layer(Wt: np.ndarray, HXt: np.ndarray, HGt: np.ndarray | None, bits
         out["loss_direct"] = proxy_loss(dW, HXt, HGt)
         out["loss_pred"] = predicted_loss(res.E, HGt)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Deploy side: the quantized layer's forward
+# ---------------------------------------------------------------------------
+def dequant(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray, group: int) -> np.ndarray:
+    """Qhat[r, c] = s[r, g] (q[r, c] - z[r, g]), g = c // group (the asymmetric grid's values)."""
+    g = np.arange(codes.shape[1]) // group
+    return np.asarray(scales, np.float64)[:, g] * (np.asarray(codes, np.float64)
+                                                   - np.asarray(zeros, np.float64)[:, g])
+
+
+def deploy_linear(Qhat: np.ndarray, d_in: np.ndarray, d_out: np.ndarray, sign_in: np.ndarray,
+                  sign_out: np.ndarray, had_in: int, had_out: int, x: np.ndarray) -> np.ndarray:
+    """y = D_out^-1 P_out^T Qhat P_in D_in^-1 x: a BiIP-quantized layer applied to x.
+
+    [KronQ-README] opening section: the packed weights are dequantized on the
+    fly in a fused dequant + BiIP matvec (the online BiIP forward of the
+    deploy path).  Since W~ = P_out D_out W D_in P_in^T with P orthogonal and
+    Qhat approximates W~, the layer is W ~ D_out^-1 P_out^T Qhat P_in D_in^-1:
+    rescale and rotate the activation, multiply by Qhat, rotate back and
+    rescale.  x may be one vector or a [batch x in] matrix (rows).
+    """
+    P_in = rotation_matrix(sign_in, had_in)
+    P_out = rotation_matrix(sign_out, had_out)
+    X = np.atleast_2d(np.asarray(x, np.float64))
+    Xt = (X / np.asarray(d_in, np.float64)[None, :]) @ P_in.T
+    Yt = Xt @ np.asarray(Qhat, np.float64).T
+    Y = (Yt @ P_out) / np.asarray(d_out, np.float64)[None, :]
+    return Y[0] if np.ndim(x) == 1 else Y
 
 
 # ---------------------------------------------------------------------------

@@ -520,6 +520,40 @@ def test_clip_replay_accepts_only_near_ties():
 
 
 # ---------------------------------------------------------------------------
+# Deploy side
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("out_n,in_n,bo,bi", [(32, 96, 32, 32), (48, 64, 16, 64), (8, 256, 8, 0)])
+def test_deploy_undoes_biip(out_n, in_n, bo, bi):
+    # an unquantized W~ = BiIP(W) in the deploy forward must give back W x: the activation's
+    # rescale and rotation and the output's inverse rotation and rescale exactly undo BiIP
+    rng = np.random.default_rng(out_n + in_n)
+    W = rng.standard_normal((out_n, in_n))
+    HX, HG = spd(rng, in_n), spd(rng, out_n)
+    s_in, s_out = rng.choice([-1, 1], in_n), rng.choice([-1, 1], out_n)
+    Wt, _, _, d_in, d_out = o.biip(W, HX, HG, s_in, s_out, 0.25, o.BIIP_FULL, bi, bo)
+    assert np.max(np.abs(d_in - 1)) > 0.1 and np.max(np.abs(d_out - 1)) > 0.1
+    x = rng.standard_normal(in_n)
+    y = o.deploy_linear(Wt, d_in, d_out, s_in, s_out, bi, bo, x)
+    np.testing.assert_allclose(y, W @ x, rtol=1e-10, atol=1e-10 * np.linalg.norm(W @ x))
+    X = rng.standard_normal((3, in_n))
+    np.testing.assert_allclose(o.deploy_linear(Wt, d_in, d_out, s_in, s_out, bi, bo, X), X @ W.T,
+                               rtol=1e-10, atol=1e-9)
+
+
+def test_deploy_without_processing_is_the_plain_product():
+    # no rescale (d = 1), plus signs, 1-blocks (no Hadamard): y = Qhat x; and the dequantized
+    # values are s (q - z) per (row, group)
+    codes = np.array([[0, 1, 2, 3], [3, 2, 1, 0]])
+    scales = np.array([[0.5, 2.0], [1.0, 0.25]])
+    zeros = np.array([[1, 0], [2, 3]])
+    Q = o.dequant(codes, scales, zeros, 2)
+    np.testing.assert_array_equal(Q, [[-0.5, 0.0, 4.0, 6.0], [1.0, 0.0, -0.5, -0.75]])
+    x = np.array([1.0, -2.0, 0.5, 4.0])
+    y = o.deploy_linear(Q, np.ones(4), np.ones(2), np.ones(4), np.ones(2), 1, 1, x)
+    np.testing.assert_array_equal(y, Q @ x)
+
+
+# ---------------------------------------------------------------------------
 # Packing
 # ---------------------------------------------------------------------------
 def test_pack_hand_examples():
