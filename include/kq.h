@@ -229,6 +229,42 @@ kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, const float*
 kq_status kq_allocate_bits(const double* sens, const int64_t* numel, int64_t L, const int* allowed,
                            int n_allowed, int64_t target_num, int64_t target_den, int* bits_out);
 
+/*
+ * kq_deploy_linear_workspace -- device workspace bytes of kq_deploy_linear for a layer with
+ * `out` rows and output Hadamard block had_out (as for kq_deploy_linear).
+ */
+kq_status kq_deploy_linear_workspace(int64_t out, int64_t had_out, size_t* bytes);
+
+/*
+ * kq_deploy_linear -- one quantized layer applied to an activation vector (batch 1):
+ *   y = D_out^-1 P_out^T Qhat P_in D_in^-1 x,   Qhat[r, c] = s[r, g] (q[r, c] - z[r, g]),
+ * P = blockdiag(Had_b) diag(S) / sqrt(b) on each side, D = diag(d).
+ *
+ * Follows: KronQ README, opening section (packed int4/int2 weights dequantized on the fly
+ * by a fused dequant + BiIP matvec for single-token decode).  Since kq_biip_rotate gives
+ * W~ = P_out D_out W D_in P_in^T and Qhat quantizes W~, y approximates W x.
+ *
+ *   packed, scales, zeros  device, as written by kq_quantize_layer (natural column order):
+ *             uint32 out x (in * bits / 32), fp32 and uint8 out x (in / group)
+ *   bits      2 or 4;  group divides in and is a multiple of 128 / bits (or equals in)
+ *   d_in, d_out      device fp32 rescale vectors (in, out), or NULL for 1
+ *   sign_in, sign_out device int8 +-1 (in, out), or NULL for +1
+ *   had_in, had_out  Hadamard blocks: powers of 2 (<= 8192) dividing in / out; 1: none;
+ *             0: the largest power of 2 dividing the size (at most 8192), as kq_biip_rotate
+ *   x         device fp32 [in];  y  device fp32 [out] (not aliasing x)
+ *   ws        device workspace of kq_deploy_linear_workspace(out, had_out) bytes, needed
+ *             when had_out > 16.  It holds per-block counters that must be zero before the
+ *             first call (allocate it zeroed); every call leaves them zero.  Calls that share
+ *             a workspace must not run concurrently.
+ * Sizes: in % 32 == 0, in <= 2^20, the LDS row max(in, had_out) * 4 bytes <= 160 KB.
+ * Asynchronous on `stream`.
+ */
+kq_status kq_deploy_linear(const uint32_t* packed, const float* scales, const uint8_t* zeros,
+                           int bits, int group, int64_t out, int64_t in, const float* d_in,
+                           const float* d_out, const int8_t* sign_in, const int8_t* sign_out,
+                           int64_t had_in, int64_t had_out, const float* x, float* y, void* ws,
+                           size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
