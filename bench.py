@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="approximate CPU budget of the oracle sample")
+    ap.add_argument("--deploy-bits", type=int, choices=(2, 4), default=None,
+                    help="time the deploy side instead: one decode token (batch 1) through the "
+                         "224 packed linears of Llama-2-7B at this width")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB fp32 tensor three times (scale for the HBM byte "
                          "counters FETCH_SIZE / WRITE_SIZE) and exit")
@@ -146,6 +149,167 @@ def cpu_baseline(cfg, budget_s: float) -> dict:
                        f"extrapolated full-layer time {full:.1f} s"),
             "measured_s": {k: round(v, 2) for k, v in t.items()}}
 
+# The seven linears of one Llama-2-7B decoder block (out, in) and the block count: the
+# model the pages time decoding on.  32 x 7 = 224 packed layers per token.
+LLAMA2_7B_LINEARS = (("q_proj", 4096, 4096), ("k_proj", 4096, 4096), ("v_proj", 4096, 4096),
+                     ("o_proj", 4096, 4096), ("gate_proj", 11008, 4096), ("up_proj", 11008, 4096),
+                     ("down_proj", 4096, 11008))
+LLAMA2_7B_BLOCKS = 32
+DEPLOY_GROUP = 128
+
+
+def deploy_bytes(out_n: int, in_n: int, bits: int, group: int) -> int:
+    """Algorithmic HBM bytes of one batch-1 deploy launch: packed codes, fp32 scales, u8 zero
+    points, the fp32 rescale vectors and int8 signs of both sides, x read and y written."""
+    ng = in_n // group
+    return (out_n * in_n * bits // 8 + out_n * ng * 5 + (in_n + out_n) * (4 + 1)
+            + in_n * 4 + out_n * 4)
+
+
+def deploy_cpu_baseline(bits: int, budget_s: float) -> dict:
+    """The oracle's deploy forward (dequantize from codes, rotate, multiply, rotate back) on
+    the seven linears of one block; the token time is that x 32."""
+    import oracle as o
+    rng = np.random.default_rng(2024)
+    t_total, done = 0.0, []
+    for name, out_n, in_n in LLAMA2_7B_LINEARS:
+        codes = rng.integers(0, 2 ** bits, size=(out_n, in_n))
+        ng = in_n // DEPLOY_GROUP
+        sc = rng.random((out_n, ng)) * 0.01 + 1e-3
+        zr = rng.integers(0, 2 ** bits, size=(out_n, ng))
+        d_in, d_out = np.exp(0.5 * rng.standard_normal(in_n)), np.exp(0.5 * rng.standard_normal(out_n))
+        s_in, s_out = rng.choice([-1.0, 1.0], in_n), rng.choice([-1.0, 1.0], out_n)
+        x = rng.standard_normal(in_n)
+        t0 = time.perf_counter()
+        Q = o.dequant(codes, sc, zr, DEPLOY_GROUP)
+        o.deploy_linear(Q, d_in, d_out, s_in, s_out, o.hadamard_block_size(in_n, 0),
+                        o.hadamard_block_size(out_n, 0), x)
+        t_total += time.perf_counter() - t0
+        done.append(name)
+        if t_total > budget_s:
+            break
+    per_block = t_total * len(LLAMA2_7B_LINEARS) / len(done)
+    token_s = per_block * LLAMA2_7B_BLOCKS
+    return {"value": round(1.0 / token_s, 4), "unit": "tokens/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": (f"{', '.join(done)} of one block (dequantize from codes + rotated fp64 "
+                       f"matvec), x{LLAMA2_7B_BLOCKS * len(LLAMA2_7B_LINEARS) / len(done):.0f} "
+                       f"to a token; {token_s:.1f} s per token"),
+            "measured_s": round(t_total, 2)}
+
+
+def deploy_main(a) -> None:
+    """One decode token at batch 1 through all 224 quantized linears of Llama-2-7B: each layer
+    its own packed codes, scales, zero points, rescale vectors and signs (nothing stays in
+    cache from one layer to the next), the Hadamard blocks BiIP picks by default (4096 on
+    the 4096 sides, 256 on the 11008 sides).  The 224 launches are captured in one HIP graph
+    and replayed; the roofline is the HBM bound of the kernel class with the most time."""
+    import torch
+    import post_quantization_syrk_amd as kq
+    bits, group = a.deploy_bits, DEPLOY_GROUP
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kq.load_library()
+    g = torch.Generator(device=dev)
+    g.manual_seed(20240 + bits)
+    t0 = time.time()
+    layers = []
+    for blk in range(LLAMA2_7B_BLOCKS):
+        for name, out_n, in_n in LLAMA2_7B_LINEARS:
+            ng = in_n // group
+            packed = torch.randint(0, 256, (out_n, in_n * bits // 8), dtype=torch.uint8, device=dev,
+                                   generator=g).view(torch.int32)
+            scales = torch.rand((out_n, ng), device=dev, generator=g) * 0.01 + 1e-3
+            zeros = torch.randint(0, 2 ** bits, (out_n, ng), dtype=torch.uint8, device=dev, generator=g)
+            d_in = torch.exp(0.5 * torch.randn(in_n, device=dev, generator=g))
+            d_out = torch.exp(0.5 * torch.randn(out_n, device=dev, generator=g))
+            s_in = (torch.randint(0, 2, (in_n,), dtype=torch.int8, device=dev, generator=g) * 2 - 1)
+            s_out = (torch.randint(0, 2, (out_n,), dtype=torch.int8, device=dev, generator=g) * 2 - 1)
+            layers.append((name, out_n, in_n, packed, scales, zeros, d_in, d_out, s_in, s_out,
+                           torch.empty(out_n, device=dev)))
+    xs = {n: torch.randn(n, device=dev, generator=g) for n in (4096, 11008)}
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+
+    def token(stream, events=None):
+        for i, (_, out_n, in_n, packed, sc, zr, di, do, si, so, y) in enumerate(layers):
+            if events is not None:
+                events[i][0].record(stream)
+            kq.kq_deploy_linear(packed, sc, zr, bits, group, di, do, si, so, 0, 0, xs[in_n], y,
+                                stream=stream)
+            if events is not None:
+                events[i][1].record(stream)
+
+    # eager token with an event pair around every launch: per-launch kernel durations
+    stream = torch.cuda.current_stream()
+    token(stream)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in layers]
+    token(stream, events)
+    torch.cuda.synchronize()
+    eager_y = [l[-1].clone() for l in layers]
+    per = {}
+    for (name, out_n, in_n, *_), (e0, e1) in zip(layers, events):
+        per.setdefault((out_n, in_n), []).append(e0.elapsed_time(e1))
+
+    # the token as one HIP graph; replays must give the eager outputs bit for bit
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        token(side)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        token(side)
+    for _ in range(a.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(a.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_token = wall * 1e3 / a.steps
+    for l, ye in zip(layers, eager_y):
+        if not torch.equal(l[-1], ye):
+            raise RuntimeError(f"graph replay of {l[0]} differs from the eager launch")
+
+    tot_bytes = sum(deploy_bytes(o_, i_, bits, group) for _, o_, i_ in LLAMA2_7B_LINEARS) * LLAMA2_7B_BLOCKS
+    classes = {}
+    for (out_n, in_n), ts in per.items():
+        avg = float(np.mean(ts))
+        b = deploy_bytes(out_n, in_n, bits, group)
+        classes[f"{out_n}x{in_n}"] = {"launches": len(ts), "avg_us": round(avg * 1e3, 2),
+                                      "GB/s": round(b / (avg / 1e3) / 1e9, 1), "bytes": b}
+    dom = max(classes.items(), key=lambda kv: kv[1]["launches"] * kv[1]["avg_us"])
+    kernel_sum_ms = sum(c["launches"] * c["avg_us"] for c in classes.values()) / 1e3
+    roofline = {"bound": "hbm", "achieved": dom[1]["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(dom[1]["GB/s"] / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": f"deploy_matvec_kernel<{bits}> + deploy_outrot_kernel, {dom[0]} (one call)",
+                "algorithmic_bytes_per_launch": dom[1]["bytes"]}
+    cpu = None if a.no_cpu_baseline else deploy_cpu_baseline(bits, a.cpu_seconds)
+    line = {
+        "metric": "decode tokens/s through the quantized linears (batch 1)",
+        "value": round(1e3 / ms_per_token, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_token, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"u{bits} codes / f32 activations and accumulate",
+        "data": "synthetic (seeded random codes, scales, zero points, rescale vectors, signs)",
+        "config": {"workload": f"llama2-7b-decode-linears-W{bits}-g{group}", "layers": len(layers),
+                   "bits": bits, "group": group, "hadamard": "4096 / 256 (default blocks)",
+                   "graph": True},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "hbm_bytes_per_token": tot_bytes,
+        "token_GB/s": round(tot_bytes / (ms_per_token / 1e3) / 1e9, 1),
+        "kernel_sum_ms_eager": round(kernel_sum_ms, 4),
+        "classes": classes,
+        "input_generation_s": round(gen_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
 
 def main():
     a = parse()
@@ -155,6 +319,9 @@ def main():
         sys.exit(2)
     if a.copy_calibration:
         copy_calibration()
+        return
+    if a.deploy_bits is not None:
+        deploy_main(a)
         return
     import torch
     import post_quantization_syrk_amd as kq

@@ -230,12 +230,6 @@ kq_status kq_allocate_bits(const double* sens, const int64_t* numel, int64_t L, 
                            int n_allowed, int64_t target_num, int64_t target_den, int* bits_out);
 
 /*
- * kq_deploy_linear_workspace -- device workspace bytes of kq_deploy_linear for a layer with
- * `out` rows and output Hadamard block had_out (as for kq_deploy_linear).
- */
-kq_status kq_deploy_linear_workspace(int64_t out, int64_t had_out, size_t* bytes);
-
-/*
  * kq_deploy_linear -- one quantized layer applied to an activation vector (batch 1):
  *   y = D_out^-1 P_out^T Qhat P_in D_in^-1 x,   Qhat[r, c] = s[r, g] (q[r, c] - z[r, g]),
  * P = blockdiag(Had_b) diag(S) / sqrt(b) on each side, D = diag(d).
@@ -252,18 +246,16 @@ kq_status kq_deploy_linear_workspace(int64_t out, int64_t had_out, size_t* bytes
  *   had_in, had_out  Hadamard blocks: powers of 2 (<= 8192) dividing in / out; 1: none;
  *             0: the largest power of 2 dividing the size (at most 8192), as kq_biip_rotate
  *   x         device fp32 [in];  y  device fp32 [out] (not aliasing x)
- *   ws        device workspace of kq_deploy_linear_workspace(out, had_out) bytes, needed
- *             when had_out > 16.  It holds per-block counters that must be zero before the
- *             first call (allocate it zeroed); every call leaves them zero.  Calls that share
- *             a workspace must not run concurrently.
- * Sizes: in % 32 == 0, in <= 2^20, the LDS row max(in, had_out) * 4 bytes <= 160 KB.
- * Asynchronous on `stream`.
+ * Sizes: in % 32 == 0; the LDS copy of x~ (in rounded up to 64 * 128 / bits entries, plus
+ * 1/16 padding) must fit in 160 KB, i.e. in <= 36864.  No workspace: with had_out > 16 a
+ * second kernel on the same stream rotates y in place.  Asynchronous on `stream`;
+ * KQ_ESHAPE / KQ_ENOTIMPL / KQ_EINVAL for unsupported arguments, before any launch.
  */
 kq_status kq_deploy_linear(const uint32_t* packed, const float* scales, const uint8_t* zeros,
                            int bits, int group, int64_t out, int64_t in, const float* d_in,
                            const float* d_out, const int8_t* sign_in, const int8_t* sign_out,
-                           int64_t had_in, int64_t had_out, const float* x, float* y, void* ws,
-                           size_t ws_bytes, void* stream);
+                           int64_t had_in, int64_t had_out, const float* x, float* y,
+                           void* stream);
 
 #ifdef __cplusplus
 }

@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "KQ_OK", 1: "KQ_EINVAL", 2: "KQ_ESHAPE", 3: "KQ_ENOTSPD", 4: 
 
 EXPORTED = ("kq_version", "kq_last_error", "kq_accumulate_hessian", "kq_sensitivity",
             "kq_biip_rotate", "kq_quantize_layer_workspace", "kq_quantize_layer",
-            "kq_allocate_bits", "kq_deploy_linear_workspace", "kq_deploy_linear")
+            "kq_allocate_bits", "kq_deploy_linear")
 
 
 class KQError(RuntimeError):
@@ -56,9 +56,8 @@ _SIGS = {
     "kq_quantize_layer": ([ctypes.POINTER(QuantParams), _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp,
                            _vp, _vp, _sz, _vp], _int),
     "kq_allocate_bits": ([_vp, _vp, _i64, _vp, _int, _i64, _i64, _vp], _int),
-    "kq_deploy_linear_workspace": ([_i64, _i64, _vp], _int),
     "kq_deploy_linear": ([_vp, _vp, _vp, _int, _int, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _i64,
-                          _vp, _vp, _vp, _sz, _vp], _int),
+                          _vp, _vp, _vp], _int),
 }
 
 _lib = None
@@ -219,19 +218,9 @@ def kq_allocate_bits(sens, numel, allowed=(2, 3, 4), target_num: int = 5, target
     return out.tolist()
 
 
-def kq_deploy_linear_workspace(out_n: int, had_out: int) -> int:
-    lib = load_library()
-    b = ctypes.c_size_t(0)
-    _check(lib.kq_deploy_linear_workspace(out_n, had_out, ctypes.byref(b)), "kq_deploy_linear_workspace")
-    return b.value
-
-
 def kq_deploy_linear(packed, scales, zeros, bits: int, group: int, d_in, d_out, sign_in, sign_out,
-                     had_in: int, had_out: int, x, y, ws=None, stream=None) -> None:
-    """y = D_out^-1 P_out^T Qhat P_in D_in^-1 x for one quantized layer (batch 1).
-
-    ws: a zero-initialized uint8 device tensor of kq_deploy_linear_workspace() bytes (needed
-    when had_out > 16; every call leaves it zeroed)."""
+                     had_in: int, had_out: int, x, y, stream=None) -> None:
+    """y = D_out^-1 P_out^T Qhat P_in D_in^-1 x for one quantized layer (batch 1)."""
     torch = _torch()
     lib = load_library()
     out_n = packed.shape[0]
@@ -243,6 +232,5 @@ def kq_deploy_linear(packed, scales, zeros, bits: int, group: int, d_in, d_out, 
         _dev_ptr(d_in, "d_in", (torch.float32,), True), _dev_ptr(d_out, "d_out", (torch.float32,), True),
         _dev_ptr(sign_in, "sign_in", (torch.int8,), True),
         _dev_ptr(sign_out, "sign_out", (torch.int8,), True), had_in, had_out,
-        _dev_ptr(x, "x", (torch.float32,)), _dev_ptr(y, "y", (torch.float32,)),
-        _dev_ptr(ws, "ws", (torch.uint8,), True), 0 if ws is None else ws.numel(), _stream(stream))
+        _dev_ptr(x, "x", (torch.float32,)), _dev_ptr(y, "y", (torch.float32,)), _stream(stream))
     _check(st, "kq_deploy_linear")

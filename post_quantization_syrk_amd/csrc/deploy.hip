@@ -2,27 +2,34 @@
 //   y = D_out^-1 P_out^T Qhat P_in D_in^-1 x,   Qhat[r, c] = s[r, g] (q[r, c] - z[r, g]).
 //
 // KronQ README, opening section: the packed int4/int2 weights are dequantized on the fly by a
-// fused dequant + BiIP matvec for single-token decode.  Here, one kernel per layer:
-//   * each workgroup owns 16 rows (4 per wave) and first issues the loads of its rows' packed
-//     words (16 bytes per lane, a row's words contiguous across the wave's lanes);
-//   * while they are in flight it forms x~ = Had_b(S_in . x / d_in) / sqrt(b) in LDS
-//     (every workgroup for itself: a few microseconds of ALU work hidden by the loads);
+// fused dequant + BiIP matvec for single-token decode.  Here:
+//   * matvec kernel: each workgroup owns 16 rows (4 per wave) and first issues the loads of
+//     its rows' packed words (16 bytes per lane, a row's words contiguous across the wave's
+//     lanes), scales and zero points;
+//   * while they are in flight it forms x~ = Had_b(S_in . x / d_in) / sqrt(b) in LDS (every
+//     workgroup for itself): each thread loads 16 contiguous entries and takes the first four
+//     butterfly stages in registers, the remaining stages go in radix-16 rounds through LDS;
 //   * a lane's codes are unpacked byte-wise (v_cvt_f32_ubyte) and a row's dot product is taken
 //     as s (sum q x~ - z sum x~) per chunk, the x~ values read once for the wave's 4 rows;
-//   * the output rotation needs every row of an output Hadamard block: blocks of at most 16
-//     rows are finished by the workgroup that owns them; larger ones by the workgroup whose
-//     rows complete the block (a per-block row counter, reset by that workgroup).
-// The layer is HBM-bound: out * in * bits / 8 bytes of packed words per call.
+//   * output blocks of at most 16 rows are rotated by the workgroup that owns them; larger
+//     ones need rows of many workgroups, so the matvec kernel writes y~ = Qhat x~ to y and a
+//     second kernel rotates and rescales y in place (one workgroup per 4096 entries or per
+//     block).  The kernel boundary orders the two: no device-wide fence inside a kernel, which
+//     on this chip writes back and invalidates the whole L2 of the workgroup's XCD.
+// At full rate the layer is HBM-bound: out * in * bits / 8 bytes of packed words per call.
 #include "kq_internal.h"
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace kq {
 namespace {
 
-constexpr int DT = 256;   // threads per workgroup
-constexpr int DR = 16;    // rows per workgroup (4 per wave)
-constexpr int MAXC = 8;   // 16-byte chunks per lane and row kept in flight
+constexpr int DT = 256;     // threads per workgroup
+constexpr int DR = 16;      // rows per workgroup of the matvec kernel (4 per wave)
+constexpr int MAXC = 8;     // 16-byte chunks per lane and row kept in flight
+constexpr int SEG = 4096;   // entries per workgroup of the output rotation (or one block)
 
 struct DeployArgs {
   const uint32_t* packed;  // out x wpr words
@@ -38,10 +45,11 @@ struct DeployArgs {
   float isb_in, isb_out;   // 1 / sqrt(block)
   const float* x;
   float* y;
-  float* yt;               // out floats: the rotated output before the output rotation
-  int* cnt;                // per output block: rows finished
-  int64_t xlen;            // LDS length of x~ (in rounded up to whole chunks)
+  int xlen;                // entries of x~ in LDS (in rounded up to whole chunks)
+  int seg;                 // entries per workgroup of the output rotation
 };
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int OOB = 0x7ffffff0;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
@@ -49,71 +57,129 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, OOB, 0x00020000);
 }
 
-// In-place Walsh-Hadamard transform (Sylvester order, unnormalized) of every b-block of
-// v[0..n) in LDS, all threads; n a multiple of b, b a power of 2.
-__device__ __forceinline__ void lds_fwht(float* v, int64_t n, int b) {
-  const int t = threadIdx.x;
-  for (int h = 1; h < b; h <<= 1) {
-    const int lh = __builtin_ctz(h);
-    for (int64_t p = t; p < n / 2; p += DT) {
-      const int64_t i = ((p >> lh) << (lh + 1)) | (p & (h - 1));
-      const float a = v[i], c = v[i + h];
-      v[i] = a + c;
-      v[i + h] = a - c;
+// LDS index of entry i: 16 floats of padding after every 256 entries, so that the strided
+// accesses of the radix-16 rounds spread over the banks; runs of 16 stay contiguous and
+// 16-byte aligned.
+__device__ __forceinline__ int pad(int i) { return i + ((i >> 8) << 4); }
+__host__ __device__ constexpr int padded_len(int n) { return n + (((n + 255) >> 8) << 4); }
+
+// Butterfly stages of strides 1, 2, .., R/2 on r[0..N) (unnormalized, Sylvester order):
+// the R-point transform of every R-run of r[0..N).
+template <int R, int N = R>
+__device__ __forceinline__ void bfly(float (&r)[16]) {
+#pragma unroll
+  for (int s = 1; s < R; s <<= 1)
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+      if ((j & s) == 0) {
+        const float a = r[j], c = r[j | s];
+        r[j] = a + c;
+        r[j | s] = a - c;
+      }
+}
+
+// The R-point transforms (R = 1, 2, 4, 8 or 16) of the 16 / R runs of r.
+__device__ __forceinline__ void bfly_runs16(float (&r)[16], int R) {
+  switch (R) {
+    case 16: bfly<16, 16>(r); break;
+    case 8: bfly<8, 16>(r); break;
+    case 4: bfly<4, 16>(r); break;
+    case 2: bfly<2, 16>(r); break;
+    default: break;
+  }
+}
+
+// One radix-R round over v (LDS, padded) of n entries: the stages of strides h .. h R / 2.
+template <int R>
+__device__ __forceinline__ void lds_round(float* v, int n, int h, int lh) {
+  for (int p = threadIdx.x; p < n / R; p += DT) {
+    const int base = (((p >> lh) * R) << lh) | (p & (h - 1));
+    float r[16];
+#pragma unroll
+    for (int j = 0; j < R; ++j) r[j] = v[pad(base + j * h)];
+    bfly<R>(r);
+#pragma unroll
+    for (int j = 0; j < R; ++j) v[pad(base + j * h)] = r[j];
+  }
+}
+
+// Stages of strides 16 .. b/2 of the b-block Walsh-Hadamard transform of v[0..n) in LDS,
+// after the thread-local stages of strides 1 .. 8 (all threads; a barrier after each round).
+__device__ __forceinline__ void lds_fwht_rest(float* v, int n, int b) {
+  for (int h = 16; h < b; h <<= 4) {
+    const int R = b / h >= 16 ? 16 : b / h, lh = __builtin_ctz(h);
+    switch (R) {
+      case 16: lds_round<16>(v, n, h, lh); break;
+      case 8: lds_round<8>(v, n, h, lh); break;
+      case 4: lds_round<4>(v, n, h, lh); break;
+      default: lds_round<2>(v, n, h, lh); break;
     }
     __syncthreads();
   }
 }
 
-// o[k] = v[c0 + c] for c = threadIdx.x + DT k, k < NF (0 at or past n): global memory only,
-// loads without branches (masked through out-of-range offsets).
-template <int NF>
-__device__ __forceinline__ void masked_loads(const float* v, int64_t n, int64_t c0, float (&o)[NF]) {
-  const __amdgpu_buffer_rsrc_t rv = rsrc(v + c0);
+// f[j] = mul * sign[c + j] / d[c + j] for j < 16 (an absent vector counts as 1); loads only
+// when `ok`.  d and sg are uniform across the workgroup.
+__device__ __forceinline__ void factors16(const float* d, const int8_t* sg, float mul, int c,
+                                          bool ok, float (&f)[16]) {
+  const bool hd = d != nullptr, hs = sg != nullptr;
+  const __amdgpu_buffer_rsrc_t rd = rsrc(d), rg = rsrc(sg);
+  u32x4 dv[4];
 #pragma unroll
-  for (int k = 0; k < NF; ++k) {
-    const int c = threadIdx.x + DT * k;
-    o[k] = __uint_as_float(
-        __builtin_amdgcn_raw_buffer_load_b32(rv, c0 + c < n ? 4 * c : OOB, 0, 0));
+  for (int q = 0; q < 4; ++q)
+    dv[q] = __builtin_amdgcn_raw_buffer_load_b128(rd, ok && hd ? 4 * (c + 4 * q) : OOB, 0, 0);
+  const u32x4 sv = __builtin_amdgcn_raw_buffer_load_b128(rg, ok && hs ? c : OOB, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float v = mul;
+    if (hd) v = v / __uint_as_float(dv[j >> 2][j & 3]);
+    const int sgn = (int)(int8_t)((sv[j >> 2] >> (8 * (j & 3))) & 0xffu);
+    if (hs && sgn < 0) v = -v;
+    f[j] = v;
   }
 }
 
-// f[k] = mul * sign[c0 + c] / d[c0 + c] for c = threadIdx.x + DT k (an absent vector counts as
-// 1; 0 at or past n, where the unmasked division would give inf): global memory, loads
-// without branches.
-template <int NF>
-__device__ __forceinline__ void scale_factors(const float* d, const int8_t* sg, float mul,
-                                              int64_t n, int64_t c0, float (&f)[NF]) {
-  const bool hd = d != nullptr, hs = sg != nullptr;
-  const __amdgpu_buffer_rsrc_t rd = rsrc(hd ? d + c0 : d), rg = rsrc(hs ? sg + c0 : sg);
-  float dv[NF];
-  int gv[NF];
-  bool ok[NF];
+// v (LDS, padded) <- the b-block transform of src[0..n) (times the input factors when `pre`),
+// entries n .. len zero.  n and len are multiples of 16; src is uniform across the workgroup.
+__device__ __forceinline__ void stage_rotated(float* v, const float* src, const float* d,
+                                              const int8_t* sg, float mul, bool pre, int n,
+                                              int len, int b) {
+  const __amdgpu_buffer_rsrc_t rs = rsrc(src);
+  const int R = b >= 16 ? 16 : b;
+  for (int g = threadIdx.x; g < len / 16; g += DT) {
+    const int c = 16 * g;
+    const bool ok = c < n;
+    u32x4 xv[4];
 #pragma unroll
-  for (int k = 0; k < NF; ++k) {
-    const int c = threadIdx.x + DT * k;
-    ok[k] = c0 + c < n;
-    dv[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, ok[k] && hd ? 4 * c : OOB, 0, 0));
-    gv[k] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(rg, ok[k] && hs ? c : OOB, 0, 0);
-  }
+    for (int q = 0; q < 4; ++q)
+      xv[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? 4 * (c + 4 * q) : OOB, 0, 0);
+    float r[16];
+    if (pre) {
+      float f[16];
+      factors16(d, sg, mul, c, ok, f);
 #pragma unroll
-  for (int k = 0; k < NF; ++k) {
-    float x = mul;
-    if (hd) x = x / (ok[k] ? dv[k] : 1.0f);
-    x = gv[k] < 0 ? -x : x;
-    f[k] = ok[k] ? x : 0.0f;
+      for (int j = 0; j < 16; ++j) r[j] = ok ? __uint_as_float(xv[j >> 2][j & 3]) * f[j] : 0.f;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) r[j] = __uint_as_float(xv[j >> 2][j & 3]);
+    }
+    bfly_runs16(r, R);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *(float4*)(v + pad(c + 4 * q)) = make_float4(r[4 * q], r[4 * q + 1], r[4 * q + 2], r[4 * q + 3]);
   }
+  __syncthreads();
+  lds_fwht_rest(v, n, b);
 }
 
 template <int BITS, int MC>
-__global__ __launch_bounds__(DT) void deploy_kernel(DeployArgs a) {
+__global__ __launch_bounds__(DT) void deploy_matvec_kernel(DeployArgs a) {
   constexpr int CPW = 32 / BITS;        // codes per word
   constexpr int CPC = 4 * CPW;          // codes per 16-byte chunk
   constexpr int BPC = 8 / BITS;         // codes per byte
   constexpr unsigned MASK = BITS == 4 ? 0x0F0F0F0Fu : 0x03030303u;
   extern __shared__ __attribute__((aligned(16))) float xs[];
   __shared__ float yloc[DR];
-  __shared__ int s_last;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int64_t rw0 = (int64_t)blockIdx.x * DR;          // the workgroup's first row
   const int64_t r0 = rw0 + 4 * wv;                        // this wave's first row
@@ -122,7 +188,6 @@ __global__ __launch_bounds__(DT) void deploy_kernel(DeployArgs a) {
   // 1. packed words, scales and zeros of the wave's 4 rows, MC chunks at a time (rows past
   //    `out` and words past the row read 0 through out-of-range offsets)
   const __amdgpu_buffer_rsrc_t rp = rsrc(a.packed + rw0 * a.wpr);
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   u32x4 wq[4][MC];
   float sc[4][MC], zc[4][MC];
   auto load_chunks = [&](int64_t c0) {
@@ -143,20 +208,9 @@ __global__ __launch_bounds__(DT) void deploy_kernel(DeployArgs a) {
   };
   load_chunks(0);
 
-  // 2. x~ = S_in . x / d_in / sqrt(b) into LDS (zero past `in`), then the block Hadamard,
-  //    while the weight loads are in flight
-  for (int64_t c0 = 0; c0 < a.xlen; c0 += 8 * DT) {
-    float v[8], f[8];
-    masked_loads<8>(a.x, a.in, c0, v);
-    scale_factors<8>(a.d_in, a.s_in, a.isb_in, a.in, c0, f);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int64_t c = c0 + t + DT * k;
-      if (c < a.xlen) xs[c] = v[k] * f[k];
-    }
-  }
-  __syncthreads();
-  if (a.bin > 1) lds_fwht(xs, a.in, a.bin);
+  // 2. x~ = Had_b(S_in . x / d_in) / sqrt(b) into LDS (zero past `in`) while the weight loads
+  //    are in flight
+  stage_rotated(xs, a.x, a.d_in, a.s_in, a.isb_in, true, (int)a.in, a.xlen, a.bin);
 
   // 3. dot products: row r's chunk contributes s (sum q x~ - z sum x~)
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -165,11 +219,11 @@ __global__ __launch_bounds__(DT) void deploy_kernel(DeployArgs a) {
 #pragma unroll
     for (int c = 0; c < MC; ++c) {
       if (c0 + c >= nck) break;   // uniform; only in the last batch
-      const int64_t pos = ((c0 + c) * 64 + lane) * CPC;   // first code of the chunk (< xlen)
+      const int pos = (int)(((c0 + c) * 64 + lane) * CPC);   // first code of the chunk (< xlen)
       float xv[CPC];
 #pragma unroll
       for (int k = 0; k < CPC; k += 4) {
-        const float4 v = *(const float4*)(xs + pos + k);
+        const float4 v = *(const float4*)(xs + pad(pos + k));
         xv[k] = v.x; xv[k + 1] = v.y; xv[k + 2] = v.z; xv[k + 3] = v.w;
       }
       float sx = 0.f;
@@ -199,74 +253,64 @@ __global__ __launch_bounds__(DT) void deploy_kernel(DeployArgs a) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) acc[i] += __shfl_xor(acc[i], o);
 
-  // 4. output rotation and rescale: y = S_out . Had_b(y~) / sqrt(b) / d_out
-  const int64_t nrows = min((int64_t)DR, a.out - rw0);
-  if (a.bout <= DR) {
-    // this workgroup holds whole output blocks: Had_b[j][k] = (-1)^popcount(j & k)
+  if (a.bout > DR) {
+    // y~ for the output-rotation kernel
     if (lane == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) yloc[4 * wv + i] = acc[i];
-    }
-    __syncthreads();
-    float f[1];
-    scale_factors<1>(a.d_out, a.s_out, a.isb_out, a.out, rw0, f);
-    if (t < nrows) {
-      const int b = a.bout, j = t % b, blk0 = t - j;
-      float v = 0.f;
-      for (int k = 0; k < b; ++k) {
-        const float yk = yloc[blk0 + k];
-        v += (__builtin_popcount(j & k) & 1) ? -yk : yk;
-      }
-      a.y[rw0 + t] = v * f[0];
+      for (int i = 0; i < 4; ++i)
+        if (r0 + i < a.out) a.y[r0 + i] = acc[i];
     }
     return;
   }
+  // 4. this workgroup holds whole output blocks: y = S_out . Had_b(y~) / sqrt(b) / d_out,
+  //    Had_b[j][k] = (-1)^popcount(j & k)
+  const int64_t nrows = min((int64_t)DR, a.out - rw0);
   if (lane == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (r0 + i < a.out) a.yt[r0 + i] = acc[i];
-  }
-  __threadfence();
-  __syncthreads();
-  const int64_t blk = rw0 / a.bout;
-  if (t == 0) {
-    const int old = atomicAdd(a.cnt + blk, (int)nrows);
-    s_last = old + (int)nrows == a.bout ? 1 : 0;
+    for (int i = 0; i < 4; ++i) yloc[4 * wv + i] = acc[i];
   }
   __syncthreads();
-  if (!s_last) return;
-  // the last workgroup of the block: every row's y~ is visible after this fence
-  __threadfence();
-  const int64_t base = blk * a.bout;
-  for (int64_t c0 = 0; c0 < a.bout; c0 += 8 * DT) {
-    float v[8];
-    masked_loads<8>(a.yt + base, a.bout, c0, v);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int64_t c = c0 + t + DT * k;
-      if (c < a.bout) xs[c] = v[k];
+  if (t < nrows) {
+    float v = a.isb_out;
+    if (a.d_out) v = v / a.d_out[rw0 + t];
+    if (a.s_out && a.s_out[rw0 + t] < 0) v = -v;
+    const int b = a.bout, j = t % b, blk0 = t - j;
+    float s = 0.f;
+    for (int k = 0; k < b; ++k) {
+      const float yk = yloc[blk0 + k];
+      s += (__builtin_popcount(j & k) & 1) ? -yk : yk;
     }
+    a.y[rw0 + t] = s * v;
   }
-  __syncthreads();
-  lds_fwht(xs, a.bout, a.bout);
-  for (int64_t c0 = 0; c0 < a.bout; c0 += 8 * DT) {
-    float f[8];
-    scale_factors<8>(a.d_out ? a.d_out + base : nullptr, a.s_out ? a.s_out + base : nullptr,
-                     a.isb_out, a.bout, c0, f);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int64_t c = c0 + t + DT * k;
-      if (c < a.bout) a.y[base + c] = xs[c] * f[k];
-    }
-  }
-  if (t == 0) atomicExch(a.cnt + blk, 0);
 }
 
-}  // namespace
-}  // namespace kq
+// y[s0 .. s0 + n) <- S_out . Had_b(y~) / sqrt(b) / d_out over the workgroup's segment (whole
+// blocks), in place.
+__global__ __launch_bounds__(DT) void deploy_outrot_kernel(DeployArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float ys[];
+  const int64_t s0 = (int64_t)blockIdx.x * a.seg;
+  const int n = (int)min((int64_t)a.seg, a.out - s0);
+  stage_rotated(ys, a.y + s0, nullptr, nullptr, 1.f, false, n, n, a.bout);
+  for (int g = threadIdx.x; g < n / 16; g += DT) {
+    const int c = 16 * g;
+    float f[16];
+    factors16(a.d_out ? a.d_out + s0 : nullptr, a.s_out ? a.s_out + s0 : nullptr, a.isb_out, c,
+              true, f);
+    float r[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = *(const float4*)(ys + pad(c + 4 * q));
+      r[4 * q] = v.x * f[4 * q];
+      r[4 * q + 1] = v.y * f[4 * q + 1];
+      r[4 * q + 2] = v.z * f[4 * q + 2];
+      r[4 * q + 3] = v.w * f[4 * q + 3];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *(float4*)(a.y + s0 + c + 4 * q) = make_float4(r[4 * q], r[4 * q + 1], r[4 * q + 2], r[4 * q + 3]);
+  }
+}
 
-namespace kq {
-namespace {
 // Hadamard block of a side: 0 = the largest power of 2 dividing n (at most 8192), as in
 // kq_biip_rotate; 1 = none
 int64_t deploy_block(int64_t n, int64_t had) {
@@ -275,25 +319,29 @@ int64_t deploy_block(int64_t n, int64_t had) {
   while (b > 8192) b >>= 1;
   return b;
 }
-}  // namespace
-}  // namespace kq
 
-extern "C" kq_status kq_deploy_linear_workspace(int64_t out, int64_t had_out, size_t* bytes) {
-  using namespace kq;
-  if (!bytes) return fail(KQ_EINVAL, "kq_deploy_linear_workspace: bytes is NULL");
-  if (out < 1 || had_out < 0) return fail(KQ_ESHAPE, "kq_deploy_linear_workspace: bad sizes");
-  const int64_t b = deploy_block(out, had_out);
-  const int64_t nblk = (out + b - 1) / b;
-  *bytes = ((size_t)nblk * sizeof(int) + 255) / 256 * 256 + (size_t)out * sizeof(float);
+constexpr size_t LDS_MAX = 160 * 1024;
+
+template <typename K>
+kq_status launch_with_lds(K kernel, dim3 grid, size_t lds, hipStream_t s, const DeployArgs& a,
+                          const char* name) {
+  if (lds > 64 * 1024)
+    KQ_HIP(hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds));
+  kernel<<<grid, dim3(DT), lds, s>>>(a);
+  KQ_LAUNCHED(name);
   return KQ_OK;
 }
+
+}  // namespace
+}  // namespace kq
 
 extern "C" kq_status kq_deploy_linear(const uint32_t* packed, const float* scales,
                                       const uint8_t* zeros, int bits, int group, int64_t out,
                                       int64_t in, const float* d_in, const float* d_out,
                                       const int8_t* sign_in, const int8_t* sign_out,
                                       int64_t had_in, int64_t had_out, const float* x, float* y,
-                                      void* ws, size_t ws_bytes, void* stream) {
+                                      void* stream) {
   using namespace kq;
   if (!packed || !scales || !zeros || !x || !y) return fail(KQ_EINVAL, "kq_deploy_linear: NULL argument");
   if (bits != 2 && bits != 4) return fail(KQ_ENOTIMPL, "kq_deploy_linear: bits must be 2 or 4");
@@ -306,10 +354,11 @@ extern "C" kq_status kq_deploy_linear(const uint32_t* packed, const float* scale
   const int64_t bin = deploy_block(in, had_in), bout = deploy_block(out, had_out);
   if (!is_pow2(bin) || in % bin != 0 || bin > 8192 || !is_pow2(bout) || out % bout != 0 || bout > 8192)
     return fail(KQ_ESHAPE, "kq_deploy_linear: Hadamard blocks must be powers of 2 dividing the sizes");
-  size_t need = 0;
-  KQ_TRY(kq_deploy_linear_workspace(out, bout, &need));
-  if (bout > DR && (!ws || ws_bytes < need))
-    return fail(KQ_EWORKSPACE, "kq_deploy_linear: workspace of %zu bytes needed", need);
+  const int64_t chunk = 64 * cpc;   // codes per chunk column of a wave
+  const int64_t xlen = (in + chunk - 1) / chunk * chunk;
+  const size_t lds = (size_t)padded_len((int)xlen) * sizeof(float);
+  if (lds > LDS_MAX)
+    return fail(KQ_ESHAPE, "kq_deploy_linear: in = %lld too large for the LDS copy of x", (long long)in);
   DeployArgs a;
   a.packed = packed; a.scales = scales; a.zeros = zeros;
   a.out = out; a.in = in; a.wpr = in * bits / 32; a.ngroups = in / group; a.group = group;
@@ -318,25 +367,25 @@ extern "C" kq_status kq_deploy_linear(const uint32_t* packed, const float* scale
   a.isb_in = (float)(1.0 / sqrt((double)bin));
   a.isb_out = (float)(1.0 / sqrt((double)bout));
   a.x = x; a.y = y;
-  const int64_t nblk = (out + bout - 1) / bout;
-  a.cnt = (int*)ws;
-  a.yt = ws ? (float*)((char*)ws + (nblk * sizeof(int) + 255) / 256 * 256) : nullptr;
-  const int64_t chunk = 64 * cpc;   // codes per chunk column of a wave
-  a.xlen = (in + chunk - 1) / chunk * chunk;
-  const size_t lds = (size_t)(a.xlen > bout ? a.xlen : bout) * sizeof(float);
-  if (lds > 160 * 1024) return fail(KQ_ESHAPE, "kq_deploy_linear: in too large for LDS");
+  a.xlen = (int)xlen;
+  a.seg = (int)std::max<int64_t>(bout, SEG);
   hipStream_t s = as_stream(stream);
   const dim3 grid((unsigned)ceil_div(out, DR));
   // 16-byte chunks per lane and row: all of them in flight when they fit in MAXC
   const int64_t nck = (a.wpr + 255) / 256;
   const int mc = nck <= 2 ? 2 : nck <= 4 ? 4 : MAXC;
-#define KQ_DEPLOY(B, M) deploy_kernel<B, M><<<grid, dim3(DT), lds, s>>>(a)
-  if (bits == 4) {
-    if (mc == 2) KQ_DEPLOY(4, 2); else if (mc == 4) KQ_DEPLOY(4, 4); else KQ_DEPLOY(4, MAXC);
-  } else {
-    if (mc == 2) KQ_DEPLOY(2, 2); else if (mc == 4) KQ_DEPLOY(2, 4); else KQ_DEPLOY(2, MAXC);
-  }
-#undef KQ_DEPLOY
-  KQ_LAUNCHED("deploy_kernel");
-  return KQ_OK;
+  const char* nm = "deploy_matvec_kernel";
+  kq_status st;
+  if (bits == 4)
+    st = mc == 2 ? launch_with_lds(deploy_matvec_kernel<4, 2>, grid, lds, s, a, nm)
+       : mc == 4 ? launch_with_lds(deploy_matvec_kernel<4, 4>, grid, lds, s, a, nm)
+                 : launch_with_lds(deploy_matvec_kernel<4, MAXC>, grid, lds, s, a, nm);
+  else
+    st = mc == 2 ? launch_with_lds(deploy_matvec_kernel<2, 2>, grid, lds, s, a, nm)
+       : mc == 4 ? launch_with_lds(deploy_matvec_kernel<2, 4>, grid, lds, s, a, nm)
+                 : launch_with_lds(deploy_matvec_kernel<2, MAXC>, grid, lds, s, a, nm);
+  if (st != KQ_OK || bout <= DR) return st;
+  const size_t lds2 = (size_t)padded_len(a.seg) * sizeof(float);
+  return launch_with_lds(deploy_outrot_kernel, dim3((unsigned)ceil_div(out, a.seg)), lds2, s, a,
+                         "deploy_outrot_kernel");
 }

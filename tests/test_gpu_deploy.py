@@ -25,22 +25,19 @@ def _layer(rng, out_n, in_n, bits, group, rescale=True, signs=True):
 
 
 def _gpu(torch, codes, scales, zeros, bits, group, d_in, d_out, s_in, s_out, bin_, bout, x,
-         ws=None, repeat=1):
+         repeat=1):
     import post_quantization_syrk_amd as kq
     dev = "cuda"
     t = lambda a, dt=None: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
     packed = t(o.pack_codes(codes, bits).view(np.int32))
-    if ws is None:
-        ws = torch.zeros(kq.kq_deploy_linear_workspace(codes.shape[0], bout), dtype=torch.uint8,
-                         device=dev)
     y = torch.empty(codes.shape[0], device=dev)
     ys = []
     for _ in range(repeat):
         kq.kq_deploy_linear(packed, t(scales), t(zeros), bits, group, t(d_in), t(d_out), t(s_in),
-                            t(s_out), bin_, bout, t(x), y, ws)
+                            t(s_out), bin_, bout, t(x), y)
         torch.cuda.synchronize()
         ys.append(y.cpu().numpy().copy())
-    return ys, ws
+    return ys
 
 
 def _ref(codes, scales, zeros, group, d_in, d_out, s_in, s_out, bin_, bout, x):
@@ -52,39 +49,43 @@ def _ref(codes, scales, zeros, group, d_in, d_out, s_in, s_out, bin_, bout, x):
 
 
 @pytest.mark.parametrize("out_n,in_n,bits,group,bin_,bout", [
-    (64, 256, 4, 128, 256, 64),        # output blocks finished through the row counters
+    (64, 256, 4, 128, 256, 64),        # output blocks rotated by the second kernel
+    (96, 256, 2, 128, 2, 32),          # radix-2 input stages; a 32-row output block
     (48, 512, 2, 512, 128, 16),        # blocks within one workgroup; per-channel grid
     (40, 96, 4, 96, 32, 8),            # ragged last workgroup
     (4096, 4096, 4, 128, 4096, 4096),  # Llama-2-7B q/k/v/o
     (11008, 4096, 2, 128, 4096, 256),  # gate/up: 43 output blocks of 256
     (4096, 11008, 4, 128, 256, 4096),  # down: 43 input blocks of 256, several chunk batches
     (4096, 11008, 2, 11008, 256, 4096),
+    (256, 8192, 4, 128, 8192, 256),    # 8192-entry input blocks (a last radix-2 round)
+    (8192, 256, 2, 128, 256, 8192),    # 8192-entry output blocks: one workgroup per block
+    (6144, 1024, 2, 128, 1024, 1),     # no output rotation; 384 workgroups
 ])
 def test_deploy_matches_oracle(out_n, in_n, bits, group, bin_, bout):
     torch = torch_cuda()
     announce(f"deploy out={out_n} in={in_n} W{bits} g{group} b=({bin_},{bout})")
     rng = np.random.default_rng(out_n + 3 * in_n + bits)
     codes, scales, zeros, d_in, d_out, s_in, s_out, x = _layer(rng, out_n, in_n, bits, group)
-    ys, _ = _gpu(torch, codes, scales, zeros, bits, group, d_in, d_out, s_in, s_out, bin_, bout, x)
+    ys = _gpu(torch, codes, scales, zeros, bits, group, d_in, d_out, s_in, s_out, bin_, bout, x)
     ref = _ref(codes, scales, zeros, group, d_in, d_out, s_in, s_out, bin_, bout, x)
     assert rel_fro(ys[0], ref) <= 1e-5
 
 
 def test_deploy_without_processing_and_repeated_calls():
-    """No rescale, no signs, no Hadamard: the plain dequantized product; and the row counters
-    are left zero, so a second call on the same workspace gives the same result."""
+    """No rescale, no signs, no Hadamard: the plain dequantized product; and repeated calls
+    (the output rotated in place by the second kernel) give the same result."""
     torch = torch_cuda()
     announce("deploy plain product / repeated calls")
     rng = np.random.default_rng(7)
     codes, scales, zeros, _, _, _, _, x = _layer(rng, 96, 256, 4, 128, rescale=False, signs=False)
-    ys, _ = _gpu(torch, codes, scales, zeros, 4, 128, None, None, None, None, 1, 1, x)
+    ys = _gpu(torch, codes, scales, zeros, 4, 128, None, None, None, None, 1, 1, x)
     Q = o.dequant(codes, scales, zeros, 128)
     assert rel_fro(ys[0], Q @ x.astype(np.float64)) <= 1e-5
     codes, scales, zeros, d_in, d_out, s_in, s_out, x = _layer(rng, 512, 1024, 2, 128)
-    ys, ws = _gpu(torch, codes, scales, zeros, 2, 128, d_in, d_out, s_in, s_out, 1024, 512, x,
-                  repeat=3)
+    ys = _gpu(torch, codes, scales, zeros, 2, 128, d_in, d_out, s_in, s_out, 1024, 512, x, repeat=3)
     assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[1], ys[2])
-    assert int(ws.sum().item()) == int(ws[256:].sum().item())   # counters (first 256 bytes) zero
+    ref = _ref(codes, scales, zeros, 128, d_in, d_out, s_in, s_out, 1024, 512, x)
+    assert rel_fro(ys[0], ref) <= 1e-5
 
 
 def test_deploy_rejects_unsupported():
@@ -98,12 +99,13 @@ def test_deploy_rejects_unsupported():
         kq.kq_deploy_linear(packed, sc, zr, 3, 128, None, None, None, None, 1, 1, x, y)
     with pytest.raises(kq.KQError):   # an output block of 64 does not divide 16 rows
         kq.kq_deploy_linear(packed, sc, zr, 4, 128, None, None, None, None, 1, 64, x, y)
-    p32 = torch.zeros((32, 16), dtype=torch.int32, device="cuda")
-    s32, z32 = torch.ones((32, 1), device="cuda"), torch.zeros((32, 1), dtype=torch.uint8, device="cuda")
-    with pytest.raises(kq.KQError) as e:   # an output block over 16 rows needs the workspace
-        kq.kq_deploy_linear(p32, s32, z32, 4, 128, None, None, None, None, 1, 0, x,
-                            torch.zeros(32, device="cuda"))
-    assert e.value.status == kq.KQ_EWORKSPACE
+    big = 36864 + 2048   # the LDS copy of x~ would exceed 160 KB
+    pb = torch.zeros((16, big * 4 // 32), dtype=torch.int32, device="cuda")
+    sb, zb = torch.ones((16, big // 128), device="cuda"), torch.zeros((16, big // 128), dtype=torch.uint8, device="cuda")
+    with pytest.raises(kq.KQError) as e:
+        kq.kq_deploy_linear(pb, sb, zb, 4, 128, None, None, None, None, 1, 1,
+                            torch.zeros(big, device="cuda"), torch.zeros(16, device="cuda"))
+    assert e.value.status == kq.KQ_ESHAPE
 
 
 def test_deploy_after_engine_quantization():
@@ -136,8 +138,7 @@ def test_deploy_after_engine_quantization():
     kq.kq_quantize_layer(p, Wt, HX, HG, packed, scales, zeros, ws, codes=codes)
     x = torch.from_numpy(rng.standard_normal(in_n).astype(np.float32)).to(dev)
     y = torch.empty(out_n, device=dev)
-    dws = torch.zeros(kq.kq_deploy_linear_workspace(out_n, 0), dtype=torch.uint8, device=dev)
-    kq.kq_deploy_linear(packed, scales, zeros, bits, group, di, do, s_in, s_out, 0, 0, x, y, dws)
+    kq.kq_deploy_linear(packed, scales, zeros, bits, group, di, do, s_in, s_out, 0, 0, x, y)
     torch.cuda.synchronize()
     Q = o.dequant(codes.cpu().numpy().astype(np.int64), scales.cpu().numpy(), zeros.cpu().numpy(), group)
     ref = o.deploy_linear(Q, di.cpu().numpy(), do.cpu().numpy(), s_in.cpu().numpy(),
@@ -146,3 +147,60 @@ def test_deploy_after_engine_quantization():
     assert rel_fro(yv, ref) <= 1e-5
     exact = W.astype(np.float64) @ x.cpu().numpy()
     assert rel_fro(yv, exact) < 0.2   # W4 quantization error of a random layer
+
+
+def test_deploy_in_a_captured_graph():
+    """Three layers (two of them with the second, output-rotation kernel) captured in one HIP
+    graph: every replay, with eager launches and synchronizations between the replays, gives
+    the eager outputs bit for bit."""
+    torch = torch_cuda()
+    import post_quantization_syrk_amd as kq
+    announce("deploy in a captured graph")
+    rng = np.random.default_rng(21)
+    shapes = [(512, 1024, 4, 128), (1024, 512, 2, 128), (384, 256, 4, 256)]
+    dev = "cuda"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    calls = []
+    for out_n, in_n, bits, group in shapes:
+        codes, scales, zeros, d_in, d_out, s_in, s_out, x = _layer(rng, out_n, in_n, bits, group)
+        calls.append((t(o.pack_codes(codes, bits).view(np.int32)), t(scales), t(zeros), bits, group,
+                      t(d_in), t(d_out), t(s_in), t(s_out), t(x), torch.empty(out_n, device=dev)))
+
+    def run(stream=None):
+        for p, sc, zr, bits, group, di, do, si, so, x, y in calls:
+            kq.kq_deploy_linear(p, sc, zr, bits, group, di, do, si, so, 0, 0, x, y, stream=stream)
+
+    run()
+    torch.cuda.synchronize()
+    eager = [c[-1].clone() for c in calls]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        run(side)
+    for rep in range(4):
+        for c in calls:
+            c[-1].fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for c, ye in zip(calls, eager):
+            assert torch.equal(c[-1], ye), f"replay {rep}"
+        run()                      # eager work between the replays
+        torch.cuda.synchronize()
+
+
+def test_deploy_long_rows():
+    """in = 28672 (Llama-2-70B down_proj): the LDS copy of x~ is over 64 KB.  Reference from
+    the oracle's block rotations (the dense P_in would not fit in memory)."""
+    torch = torch_cuda()
+    announce("deploy long rows 128 x 28672")
+    rng = np.random.default_rng(28672)
+    out_n, in_n, bits, group, bin_, bout = 128, 28672, 4, 128, 4096, 128
+    codes, scales, zeros, d_in, d_out, s_in, s_out, x = _layer(rng, out_n, in_n, bits, group)
+    ys = _gpu(torch, codes, scales, zeros, bits, group, d_in, d_out, s_in, s_out, bin_, bout, x)
+    Q = o.dequant(codes, scales, zeros, group)
+    xt = o.rotate_cols((x.astype(np.float64) / d_in)[:, None], s_in.astype(np.float64), bin_)[:, 0]
+    yt = Q @ xt
+    # P_out^T yt = S_out Had(yt) / sqrt(b): the block transform of yt with unit signs, then S
+    ref = o.rotate_cols(yt[:, None], np.ones(out_n), bout)[:, 0] * s_out / d_out
+    assert rel_fro(ys[0], ref) <= 1e-5
