@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--deploy-bits", type=int, choices=(2, 4), default=None,
                     help="time the deploy side instead: one decode token (batch 1) through the "
                          "224 packed linears of Llama-2-7B at this width")
+    ap.add_argument("--deploy-single", action="store_true",
+                    help="with --deploy-bits: one call per layer instead of grouped calls")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB fp32 tensor three times (scale for the HBM byte "
                          "counters FETCH_SIZE / WRITE_SIZE) and exit")
@@ -90,6 +92,20 @@ def traffic_from_profile(kernel_src: str, launch_units: float):
     if d.get("kernel_source_sha256_16") != source_hash(kernel_src):
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def deploy_traffic_from_profile(bits: int, call: str):
+    """HBM bytes of one deploy call of the given class (matvec + output rotation kernels), from
+    the committed rocprofv3 counter summary if it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"deploy_w{bits}_hbm_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    src = os.path.join(ROOT, "post_quantization_syrk_amd", "csrc", "deploy.hip")
+    if d.get("kernel_source_sha256_16") != source_hash(src):
+        return None
+    return d.get("classes", {}).get(call, {}).get("hbm_bytes_per_call")
 
 
 def blas_threads() -> int:
@@ -202,8 +218,11 @@ def deploy_main(a) -> None:
     """One decode token at batch 1 through all 224 quantized linears of Llama-2-7B: each layer
     its own packed codes, scales, zero points, rescale vectors and signs (nothing stays in
     cache from one layer to the next), the Hadamard blocks BiIP picks by default (4096 on
-    the 4096 sides, 256 on the 11008 sides).  The 224 launches are captured in one HIP graph
-    and replayed; the roofline is the HBM bound of the kernel class with the most time."""
+    the 4096 sides, 256 on the 11008 sides).  Calls follow a decoder's dependencies: the
+    layers that read the same activation go in one grouped call (q/k/v, then o, then
+    gate/up, then down: 128 calls), or one call per layer with --deploy-single.  The token is
+    captured in one HIP graph and replayed; the roofline is the HBM bound of the call class
+    with the most time."""
     import torch
     import post_quantization_syrk_amd as kq
     bits, group = a.deploy_bits, DEPLOY_GROUP
@@ -213,45 +232,59 @@ def deploy_main(a) -> None:
     g = torch.Generator(device=dev)
     g.manual_seed(20240 + bits)
     t0 = time.time()
-    layers = []
+    blocks = []
     for blk in range(LLAMA2_7B_BLOCKS):
+        lay = {}
         for name, out_n, in_n in LLAMA2_7B_LINEARS:
             ng = in_n // group
-            packed = torch.randint(0, 256, (out_n, in_n * bits // 8), dtype=torch.uint8, device=dev,
-                                   generator=g).view(torch.int32)
-            scales = torch.rand((out_n, ng), device=dev, generator=g) * 0.01 + 1e-3
-            zeros = torch.randint(0, 2 ** bits, (out_n, ng), dtype=torch.uint8, device=dev, generator=g)
-            d_in = torch.exp(0.5 * torch.randn(in_n, device=dev, generator=g))
-            d_out = torch.exp(0.5 * torch.randn(out_n, device=dev, generator=g))
-            s_in = (torch.randint(0, 2, (in_n,), dtype=torch.int8, device=dev, generator=g) * 2 - 1)
-            s_out = (torch.randint(0, 2, (out_n,), dtype=torch.int8, device=dev, generator=g) * 2 - 1)
-            layers.append((name, out_n, in_n, packed, scales, zeros, d_in, d_out, s_in, s_out,
-                           torch.empty(out_n, device=dev)))
+            lay[name] = dict(
+                packed=torch.randint(0, 256, (out_n, in_n * bits // 8), dtype=torch.uint8, device=dev,
+                                     generator=g).view(torch.int32),
+                scales=torch.rand((out_n, ng), device=dev, generator=g) * 0.01 + 1e-3,
+                zeros=torch.randint(0, 2 ** bits, (out_n, ng), dtype=torch.uint8, device=dev, generator=g),
+                bits=bits, group=group,
+                d_in=torch.exp(0.5 * torch.randn(in_n, device=dev, generator=g)),
+                d_out=torch.exp(0.5 * torch.randn(out_n, device=dev, generator=g)),
+                sign_in=torch.randint(0, 2, (in_n,), dtype=torch.int8, device=dev, generator=g) * 2 - 1,
+                sign_out=torch.randint(0, 2, (out_n,), dtype=torch.int8, device=dev, generator=g) * 2 - 1,
+                had_in=0, had_out=0, y=torch.empty(out_n, device=dev))
+        blocks.append(lay)
     xs = {n: torch.randn(n, device=dev, generator=g) for n in (4096, 11008)}
+    shape = {name: (o_, i_) for name, o_, i_ in LLAMA2_7B_LINEARS}
+    groups = ([["q_proj"], ["k_proj"], ["v_proj"], ["o_proj"], ["gate_proj"], ["up_proj"], ["down_proj"]]
+              if a.deploy_single else
+              [["q_proj", "k_proj", "v_proj"], ["o_proj"], ["gate_proj", "up_proj"], ["down_proj"]])
+    calls = [("+".join(gr), [blk[nm] for nm in gr], shape[gr[0]][1]) for blk in blocks for gr in groups]
     torch.cuda.synchronize()
     gen_s = time.time() - t0
 
     def token(stream, events=None):
-        for i, (_, out_n, in_n, packed, sc, zr, di, do, si, so, y) in enumerate(layers):
+        for i, (_, lays, in_n) in enumerate(calls):
             if events is not None:
                 events[i][0].record(stream)
-            kq.kq_deploy_linear(packed, sc, zr, bits, group, di, do, si, so, 0, 0, xs[in_n], y,
-                                stream=stream)
+            if len(lays) == 1:
+                L = lays[0]
+                kq.kq_deploy_linear(L["packed"], L["scales"], L["zeros"], bits, group, L["d_in"],
+                                    L["d_out"], L["sign_in"], L["sign_out"], 0, 0, xs[in_n], L["y"],
+                                    stream=stream)
+            else:
+                kq.kq_deploy_linear_group(lays, xs[in_n], stream=stream)
             if events is not None:
                 events[i][1].record(stream)
 
-    # eager token with an event pair around every launch: per-launch kernel durations
+    # eager token with an event pair around every call: per-call kernel durations
     stream = torch.cuda.current_stream()
     token(stream)
     torch.cuda.synchronize()
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in layers]
+              for _ in calls]
     token(stream, events)
     torch.cuda.synchronize()
-    eager_y = [l[-1].clone() for l in layers]
+    outs = [L["y"] for _, lays, _ in calls for L in lays]
+    eager_y = [y.clone() for y in outs]
     per = {}
-    for (name, out_n, in_n, *_), (e0, e1) in zip(layers, events):
-        per.setdefault((out_n, in_n), []).append(e0.elapsed_time(e1))
+    for (name, lays, in_n), (e0, e1) in zip(calls, events):
+        per.setdefault(name, []).append(e0.elapsed_time(e1))
 
     # the token as one HIP graph; replays must give the eager outputs bit for bit
     graph = torch.cuda.CUDAGraph()
@@ -272,22 +305,23 @@ def deploy_main(a) -> None:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_token = wall * 1e3 / a.steps
-    for l, ye in zip(layers, eager_y):
-        if not torch.equal(l[-1], ye):
-            raise RuntimeError(f"graph replay of {l[0]} differs from the eager launch")
+    for y, ye in zip(outs, eager_y):
+        if not torch.equal(y, ye):
+            raise RuntimeError("graph replay differs from the eager calls")
 
     tot_bytes = sum(deploy_bytes(o_, i_, bits, group) for _, o_, i_ in LLAMA2_7B_LINEARS) * LLAMA2_7B_BLOCKS
     classes = {}
-    for (out_n, in_n), ts in per.items():
+    for name, ts in per.items():
         avg = float(np.mean(ts))
-        b = deploy_bytes(out_n, in_n, bits, group)
-        classes[f"{out_n}x{in_n}"] = {"launches": len(ts), "avg_us": round(avg * 1e3, 2),
-                                      "GB/s": round(b / (avg / 1e3) / 1e9, 1), "bytes": b}
-    dom = max(classes.items(), key=lambda kv: kv[1]["launches"] * kv[1]["avg_us"])
-    kernel_sum_ms = sum(c["launches"] * c["avg_us"] for c in classes.values()) / 1e3
+        b = sum(deploy_bytes(*shape[nm], bits, group) for nm in name.split("+"))
+        classes[name] = {"calls": len(ts), "avg_us": round(avg * 1e3, 2),
+                         "GB/s": round(b / (avg / 1e3) / 1e9, 1), "bytes": b}
+    dom = max(classes.items(), key=lambda kv: kv[1]["calls"] * kv[1]["avg_us"])
+    kernel_sum_ms = sum(c["calls"] * c["avg_us"] for c in classes.values()) / 1e3
     roofline = {"bound": "hbm", "achieved": dom[1]["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(dom[1]["GB/s"] / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": f"deploy_matvec_kernel<{bits}> + deploy_outrot_kernel, {dom[0]} (one call)",
+                "frac": round(dom[1]["GB/s"] / PEAK_HBM_GBS, 4),
+                "traffic": deploy_traffic_from_profile(bits, dom[0]),
+                "kernel": f"deploy_matvec_kernel + deploy_outrot_kernel: one {dom[0]} call",
                 "algorithmic_bytes_per_launch": dom[1]["bytes"]}
     cpu = None if a.no_cpu_baseline else deploy_cpu_baseline(bits, a.cpu_seconds)
     line = {
@@ -297,9 +331,10 @@ def deploy_main(a) -> None:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": f"u{bits} codes / f32 activations and accumulate",
         "data": "synthetic (seeded random codes, scales, zero points, rescale vectors, signs)",
-        "config": {"workload": f"llama2-7b-decode-linears-W{bits}-g{group}", "layers": len(layers),
-                   "bits": bits, "group": group, "hadamard": "4096 / 256 (default blocks)",
-                   "graph": True},
+        "config": {"workload": f"llama2-7b-decode-linears-W{bits}-g{group}",
+                   "layers": len(LLAMA2_7B_LINEARS) * LLAMA2_7B_BLOCKS, "calls": len(calls),
+                   "grouped": not a.deploy_single, "bits": bits, "group": group,
+                   "hadamard": "4096 / 256 (default blocks)", "graph": True},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "hbm_bytes_per_token": tot_bytes,

@@ -257,6 +257,39 @@ kq_status kq_deploy_linear(const uint32_t* packed, const float* scales, const ui
                            int64_t had_in, int64_t had_out, const float* x, float* y,
                            void* stream);
 
+/*
+ * One layer of kq_deploy_linear_group: the arguments of kq_deploy_linear other than in and x
+ * (same meaning, layout and limits).
+ */
+typedef struct kq_deploy_layer {
+  const uint32_t* packed;
+  const float* scales;
+  const uint8_t* zeros;
+  int bits;
+  int group;
+  int64_t out;
+  const float* d_in;
+  const float* d_out;
+  const int8_t* sign_in;
+  const int8_t* sign_out;
+  int64_t had_in;
+  int64_t had_out;
+  float* y;
+} kq_deploy_layer;
+
+/*
+ * kq_deploy_linear_group -- kq_deploy_linear for n_layers (1 .. 8) layers that read the same
+ * activation x [in] (a decoder's q/k/v projections, or its gate/up pair), in one launch of
+ * the matvec kernel (and at most one of the output rotation).  Each layer has its own codes,
+ * width (2 or 4 bits), group, rescale vectors, signs, Hadamard blocks and output y; the
+ * outputs must not overlap each other or x.  `layers` is a host array, read during the call.
+ * Follows: KronQ README, opening section (the fused dequant + BiIP matvec of the packed
+ * deploy path), applied to each layer as kq_deploy_linear.  Errors as kq_deploy_linear,
+ * naming the layer; KQ_ESHAPE for n_layers outside 1 .. 8.
+ */
+kq_status kq_deploy_linear_group(const kq_deploy_layer* layers, int n_layers, int64_t in,
+                                 const float* x, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

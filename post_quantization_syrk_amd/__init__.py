@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "KQ_OK", 1: "KQ_EINVAL", 2: "KQ_ESHAPE", 3: "KQ_ENOTSPD", 4: 
 
 EXPORTED = ("kq_version", "kq_last_error", "kq_accumulate_hessian", "kq_sensitivity",
             "kq_biip_rotate", "kq_quantize_layer_workspace", "kq_quantize_layer",
-            "kq_allocate_bits", "kq_deploy_linear")
+            "kq_allocate_bits", "kq_deploy_linear", "kq_deploy_linear_group")
 
 
 class KQError(RuntimeError):
@@ -35,6 +35,15 @@ class KQError(RuntimeError):
 
 class NotSPDError(KQError):
     pass
+
+
+class DeployLayer(ctypes.Structure):
+    """kq_deploy_layer (include/kq.h)."""
+    _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p),
+                ("bits", ctypes.c_int), ("group", ctypes.c_int), ("out", ctypes.c_int64),
+                ("d_in", ctypes.c_void_p), ("d_out", ctypes.c_void_p), ("sign_in", ctypes.c_void_p),
+                ("sign_out", ctypes.c_void_p), ("had_in", ctypes.c_int64), ("had_out", ctypes.c_int64),
+                ("y", ctypes.c_void_p)]
 
 
 class QuantParams(ctypes.Structure):
@@ -58,6 +67,7 @@ _SIGS = {
     "kq_allocate_bits": ([_vp, _vp, _i64, _vp, _int, _i64, _i64, _vp], _int),
     "kq_deploy_linear": ([_vp, _vp, _vp, _int, _int, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _i64,
                           _vp, _vp, _vp], _int),
+    "kq_deploy_linear_group": ([ctypes.POINTER(DeployLayer), _int, _i64, _vp, _vp], _int),
 }
 
 _lib = None
@@ -234,3 +244,26 @@ def kq_deploy_linear(packed, scales, zeros, bits: int, group: int, d_in, d_out, 
         _dev_ptr(sign_out, "sign_out", (torch.int8,), True), had_in, had_out,
         _dev_ptr(x, "x", (torch.float32,)), _dev_ptr(y, "y", (torch.float32,)), _stream(stream))
     _check(st, "kq_deploy_linear")
+
+
+def kq_deploy_linear_group(layers, x, stream=None) -> None:
+    """kq_deploy_linear for several layers reading the same x, in one launch.
+
+    layers: sequence of dicts with the keyword arguments of kq_deploy_linear other than x
+    (packed, scales, zeros, bits, group, d_in, d_out, sign_in, sign_out, had_in, had_out, y)."""
+    torch = _torch()
+    lib = load_library()
+    arr = (DeployLayer * max(1, len(layers)))()
+    for i, L in enumerate(layers):
+        arr[i] = DeployLayer(
+            _dev_ptr(L["packed"], "packed", (torch.int32, torch.uint32)),
+            _dev_ptr(L["scales"], "scales", (torch.float32,)),
+            _dev_ptr(L["zeros"], "zeros", (torch.uint8,)), L["bits"], L["group"], L["packed"].shape[0],
+            _dev_ptr(L.get("d_in"), "d_in", (torch.float32,), True),
+            _dev_ptr(L.get("d_out"), "d_out", (torch.float32,), True),
+            _dev_ptr(L.get("sign_in"), "sign_in", (torch.int8,), True),
+            _dev_ptr(L.get("sign_out"), "sign_out", (torch.int8,), True),
+            L.get("had_in", 0), L.get("had_out", 0), _dev_ptr(L["y"], "y", (torch.float32,)))
+    st = lib.kq_deploy_linear_group(arr, len(layers), x.shape[-1], _dev_ptr(x, "x", (torch.float32,)),
+                                    _stream(stream))
+    _check(st, "kq_deploy_linear_group")

@@ -21,6 +21,8 @@
 
 #include <math.h>
 
+#include <string.h>
+
 #include <algorithm>
 
 namespace kq {
@@ -31,30 +33,48 @@ constexpr int DR = 16;      // rows per workgroup of the matvec kernel (4 per wa
 constexpr int MAXC = 8;     // 16-byte chunks per lane and row kept in flight
 constexpr int SEG = 4096;   // entries per workgroup of the output rotation (or one block)
 
-struct DeployArgs {
+constexpr int MAXL = 8;     // layers per grouped call
+
+// One layer of a call (all layers of a call read the same x).
+struct LayerArgs {
   const uint32_t* packed;  // out x wpr words
   const float* scales;     // out x ngroups
   const uint8_t* zeros;    // out x ngroups
-  int64_t out, in, wpr, ngroups;
-  int group;
   const float* d_in;
   const float* d_out;
   const int8_t* s_in;
   const int8_t* s_out;
+  float* y;
+  int out, wpr, ngroups, bits;
   int bin, bout;
   float isb_in, isb_out;   // 1 / sqrt(block)
-  const float* x;
-  float* y;
-  int xlen;                // entries of x~ in LDS (in rounded up to whole chunks)
-  int seg;                 // entries per workgroup of the output rotation
+  unsigned gmagic;         // ceil(2^32 / group): c / group = umulhi(c, gmagic) for c < 2^16
+  int wg0;                 // first matvec workgroup of the layer
+  int seg, sg0;            // output rotation: entries per workgroup, first workgroup
 };
+
+struct GroupArgs {
+  LayerArgs L[MAXL];
+  const float* x;
+  int nl, in, xlen;        // layers; x entries; LDS length of x~ (whole chunks)
+};
+
+// The layer of workgroup `wg` given ascending first workgroups (empty ranges allowed).
+__device__ __forceinline__ int layer_of(const GroupArgs& a, int wg, bool outrot) {
+  int l = 0;
+  for (int k = 1; k < a.nl; ++k)
+    if (wg >= (outrot ? a.L[k].sg0 : a.L[k].wg0)) l = k;
+  return l;
+}
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int OOB = 0x7ffffff0;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
+// Buffer descriptor over `bytes` bytes at base: loads at or past the end read 0, so that
+// masked lanes need no branch (a branch around a load makes the compiler wait for every
+// load in flight where the paths join).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
   // 0x00020000: the descriptor's data-format word on gfx9
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, OOB, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
 // LDS index of entry i: 16 floats of padding after every 256 entries, so that the strided
@@ -118,108 +138,164 @@ __device__ __forceinline__ void lds_fwht_rest(float* v, int n, int b) {
   }
 }
 
-// f[j] = mul * sign[c + j] / d[c + j] for j < 16 (an absent vector counts as 1); loads only
-// when `ok`.  d and sg are uniform across the workgroup.
+// mul * sign / d from a loaded d word and the word holding the sign byte (an absent d reads
+// 0 and counts as 1; an absent sign reads 0, i.e. +1).  v_rcp_f32: 1 ulp.
+__device__ __forceinline__ float factor(unsigned dw, unsigned sw, int byte, bool hd, float mul) {
+  const float d = hd ? __uint_as_float(dw) : 1.f;
+  const float f = mul * __builtin_amdgcn_rcpf(d);
+  return ((sw >> (8 * byte + 7)) & 1u) ? -f : f;
+}
+
+// f[j] = mul * sign[c + j] / d[c + j] for j < 16 (an absent vector counts as 1); d and sg
+// hold n entries and are uniform across the workgroup.
 __device__ __forceinline__ void factors16(const float* d, const int8_t* sg, float mul, int c,
-                                          bool ok, float (&f)[16]) {
+                                          int n, float (&f)[16]) {
   const bool hd = d != nullptr, hs = sg != nullptr;
-  const __amdgpu_buffer_rsrc_t rd = rsrc(d), rg = rsrc(sg);
+  const __amdgpu_buffer_rsrc_t rd = rsrc(d, hd ? 4 * n : 0), rg = rsrc(sg, hs ? n : 0);
   u32x4 dv[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    dv[q] = __builtin_amdgcn_raw_buffer_load_b128(rd, ok && hd ? 4 * (c + 4 * q) : OOB, 0, 0);
-  const u32x4 sv = __builtin_amdgcn_raw_buffer_load_b128(rg, ok && hs ? c : OOB, 0, 0);
+  for (int q = 0; q < 4; ++q) dv[q] = __builtin_amdgcn_raw_buffer_load_b128(rd, 4 * (c + 4 * q), 0, 0);
+  const u32x4 sv = __builtin_amdgcn_raw_buffer_load_b128(rg, c, 0, 0);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    float v = mul;
-    if (hd) v = v / __uint_as_float(dv[j >> 2][j & 3]);
-    const int sgn = (int)(int8_t)((sv[j >> 2] >> (8 * (j & 3))) & 0xffu);
-    if (hs && sgn < 0) v = -v;
-    f[j] = v;
+  for (int j = 0; j < 16; ++j) f[j] = factor(dv[j >> 2][j & 3], sv[j >> 2], j & 3, hd, mul);
+}
+
+// Loads of B groups of 16 entries per thread (groups g0 + DT k): src entries and, when the
+// input factors are applied, d and the signs; groups at or past n read zero.
+template <int B>
+struct StageRegs {
+  u32x4 xv[B][4];
+  u32x4 dv[B][4];
+  u32x4 sv[B];
+};
+
+template <int B>
+__device__ __forceinline__ void stage_load(StageRegs<B>& S, const __amdgpu_buffer_rsrc_t rs,
+                                           const __amdgpu_buffer_rsrc_t rd,
+                                           const __amdgpu_buffer_rsrc_t rg, bool pre, int g0) {
+#pragma unroll
+  for (int k = 0; k < B; ++k) {
+    const int c = 16 * (g0 + DT * k);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      S.xv[k][q] = __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * (c + 4 * q), 0, 0);
+      if (pre) S.dv[k][q] = __builtin_amdgcn_raw_buffer_load_b128(rd, 4 * (c + 4 * q), 0, 0);
+    }
+    if (pre) S.sv[k] = __builtin_amdgcn_raw_buffer_load_b128(rg, c, 0, 0);
   }
 }
 
-// v (LDS, padded) <- the b-block transform of src[0..n) (times the input factors when `pre`),
-// entries n .. len zero.  n and len are multiples of 16; src is uniform across the workgroup.
-__device__ __forceinline__ void stage_rotated(float* v, const float* src, const float* d,
-                                              const int8_t* sg, float mul, bool pre, int n,
-                                              int len, int b) {
-  const __amdgpu_buffer_rsrc_t rs = rsrc(src);
-  const int R = b >= 16 ? 16 : b;
-  for (int g = threadIdx.x; g < len / 16; g += DT) {
-    const int c = 16 * g;
+// v (LDS, padded) <- the loaded groups below len, times mul * sign / d when `pre` (zero at or
+// past n), with their thread-local butterfly stages (R-point runs).
+template <int B, bool GUARD>
+__device__ __forceinline__ void stage_finish(float* v, const StageRegs<B>& S, bool hd, bool pre,
+                                             float mul, int n, int len, int R, int g0) {
+#pragma unroll
+  for (int k = 0; k < B; ++k) {
+    const int c = 16 * (g0 + DT * k);
+    if (GUARD && c >= len) break;
     const bool ok = c < n;
-    u32x4 xv[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      xv[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? 4 * (c + 4 * q) : OOB, 0, 0);
     float r[16];
-    if (pre) {
-      float f[16];
-      factors16(d, sg, mul, c, ok, f);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) r[j] = ok ? __uint_as_float(xv[j >> 2][j & 3]) * f[j] : 0.f;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) r[j] = __uint_as_float(xv[j >> 2][j & 3]);
+    for (int j = 0; j < 16; ++j) {
+      const float xj = __uint_as_float(S.xv[k][j >> 2][j & 3]);
+      if (pre) {
+        const float f = factor(S.dv[k][j >> 2][j & 3], S.sv[k][j >> 2], j & 3, hd, mul);
+        r[j] = ok ? xj * f : 0.f;
+      } else {
+        r[j] = xj;
+      }
     }
     bfly_runs16(r, R);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       *(float4*)(v + pad(c + 4 * q)) = make_float4(r[4 * q], r[4 * q + 1], r[4 * q + 2], r[4 * q + 3]);
   }
+}
+
+// v (LDS, padded) <- the b-block transform of src[0..n) (times mul * sign / d when `pre`),
+// entries n .. len zero.  n and len are multiples of 16; src, d, sg uniform across the
+// workgroup.  `between` runs after the first batch of loads is issued and before any of
+// them is used (it issues other loads that then overlap the transform).  The first batch is
+// written whole, so v holds at least 16 * DT * B entries (beyond len: zeros); an unguarded
+// first batch keeps its loads ahead of `between` (a guard would let the compiler sink them
+// into the guarded block, after the other loads).
+template <int B, typename F>
+__device__ __forceinline__ void stage_rotated(float* v, const float* src, const float* d,
+                                              const int8_t* sg, float mul, bool pre, int n,
+                                              int len, int b, F between) {
+  const bool hd = d != nullptr, hs = sg != nullptr;
+  const __amdgpu_buffer_rsrc_t rs = rsrc(src, 4 * n), rd = rsrc(d, pre && hd ? 4 * n : 0),
+                               rg = rsrc(sg, pre && hs ? n : 0);
+  const int R = b >= 16 ? 16 : b, ng = len / 16, t = threadIdx.x;
+  {
+    StageRegs<B> S;
+    stage_load<B>(S, rs, rd, rg, pre, t);
+    __builtin_amdgcn_sched_barrier(0);
+    between();
+    __builtin_amdgcn_sched_barrier(0);
+    stage_finish<B, false>(v, S, hd, pre, mul, n, len, R, t);
+  }
+  for (int g0 = t + B * DT; g0 < ng; g0 += B * DT) {
+    StageRegs<B> S;
+    stage_load<B>(S, rs, rd, rg, pre, g0);
+    stage_finish<B, true>(v, S, hd, pre, mul, n, len, R, g0);
+  }
   __syncthreads();
   lds_fwht_rest(v, n, b);
 }
 
-template <int BITS, int MC>
-__global__ __launch_bounds__(DT) void deploy_matvec_kernel(DeployArgs a) {
+// Rows [rw0, rw0 + 16) of layer L: y~ (or y, when its output blocks fit in 16 rows).
+template <int BITS, int MC, int B>
+__device__ __forceinline__ void matvec_rows(const GroupArgs& a, const LayerArgs& L, int rw0,
+                                            float* xs) {
   constexpr int CPW = 32 / BITS;        // codes per word
   constexpr int CPC = 4 * CPW;          // codes per 16-byte chunk
   constexpr int BPC = 8 / BITS;         // codes per byte
   constexpr unsigned MASK = BITS == 4 ? 0x0F0F0F0Fu : 0x03030303u;
-  extern __shared__ __attribute__((aligned(16))) float xs[];
   __shared__ float yloc[DR];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int64_t rw0 = (int64_t)blockIdx.x * DR;          // the workgroup's first row
-  const int64_t r0 = rw0 + 4 * wv;                        // this wave's first row
-  const int64_t nck = (a.wpr + 4 * 64 - 1) / (4 * 64);    // 16-byte chunks per lane and row
+  const int wpr = L.wpr, ngr = L.ngroups, in = a.in;
+  const int nck = (wpr + 4 * 64 - 1) / (4 * 64);      // 16-byte chunks per lane and row
+  const int rows = min(DR, L.out - rw0), wr0 = 4 * wv;   // rows of the workgroup; the wave's
 
-  // 1. packed words, scales and zeros of the wave's 4 rows, MC chunks at a time (rows past
-  //    `out` and words past the row read 0 through out-of-range offsets)
-  const __amdgpu_buffer_rsrc_t rp = rsrc(a.packed + rw0 * a.wpr);
+  // 1. loads of the packed words, scales and zeros of the wave's 4 rows, MC chunks at a time.
+  //    Descriptors over the workgroup's rows only: rows past `out` read 0.  Words past a
+  //    row's end read the next row (or 0); they meet x~ entries past `in`, which are 0.
+  const __amdgpu_buffer_rsrc_t rp = rsrc(L.packed + (int64_t)rw0 * wpr, rows * wpr * 4);
+  const __amdgpu_buffer_rsrc_t rsc = rsrc(L.scales + (int64_t)rw0 * ngr, rows * ngr * 4);
+  const __amdgpu_buffer_rsrc_t rzp = rsrc(L.zeros + (int64_t)rw0 * ngr, rows * ngr);
   u32x4 wq[4][MC];
   float sc[4][MC], zc[4][MC];
-  auto load_chunks = [&](int64_t c0) {
+  auto load_chunks = [&](int c0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int c = 0; c < MC; ++c) {
+      const int word = ((c0 + c) * 64 + lane) * 4;
+      const int pos = word * CPW;
+      const int g = (int)__umulhi((unsigned)(pos < in ? pos : in - 1), L.gmagic);
 #pragma unroll
-      for (int c = 0; c < MC; ++c) {
-        const int64_t word = ((c0 + c) * 64 + lane) * 4;
-        const bool ok = r0 + i < a.out && word < a.wpr;
-        wq[i][c] = __builtin_amdgcn_raw_buffer_load_b128(
-            rp, ok ? (int)(((r0 + i - rw0) * a.wpr + word) * 4) : OOB, 0, 0);
-        const int64_t r = r0 + i < a.out ? r0 + i : a.out - 1;
-        const int64_t pos = word * CPW;
-        const int64_t g = (pos < a.in ? pos : a.in - 1) / a.group;
-        sc[i][c] = a.scales[r * a.ngroups + g];
-        zc[i][c] = (float)a.zeros[r * a.ngroups + g];
+      for (int i = 0; i < 4; ++i) {
+        wq[i][c] = __builtin_amdgcn_raw_buffer_load_b128(rp, ((wr0 + i) * wpr + word) * 4, 0, 0);
+        const int go = (wr0 + i) * ngr + g;
+        sc[i][c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsc, 4 * go, 0, 0));
+        zc[i][c] = (float)__builtin_amdgcn_raw_buffer_load_b8(rzp, go, 0, 0);
       }
+    }
   };
-  load_chunks(0);
 
-  // 2. x~ = Had_b(S_in . x / d_in) / sqrt(b) into LDS (zero past `in`) while the weight loads
-  //    are in flight
-  stage_rotated(xs, a.x, a.d_in, a.s_in, a.isb_in, true, (int)a.in, a.xlen, a.bin);
+  // 2. x~ = Had_b(S_in . x / d_in) / sqrt(b) into LDS (zero past `in`): its loads first, then
+  //    the weight loads, whose latency the transform then overlaps
+  stage_rotated<B>(xs, a.x, L.d_in, L.s_in, L.isb_in, true, in, a.xlen, L.bin,
+                   [&] { load_chunks(0); });
 
   // 3. dot products: row r's chunk contributes s (sum q x~ - z sum x~)
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t c0 = 0; c0 < nck; c0 += MC) {
+  for (int c0 = 0; c0 < nck; c0 += MC) {
     if (c0 > 0) load_chunks(c0);
 #pragma unroll
     for (int c = 0; c < MC; ++c) {
       if (c0 + c >= nck) break;   // uniform; only in the last batch
-      const int pos = (int)(((c0 + c) * 64 + lane) * CPC);   // first code of the chunk (< xlen)
+      const int pos = ((c0 + c) * 64 + lane) * CPC;   // first code of the chunk (< xlen)
       float xv[CPC];
 #pragma unroll
       for (int k = 0; k < CPC; k += 4) {
@@ -253,61 +329,80 @@ __global__ __launch_bounds__(DT) void deploy_matvec_kernel(DeployArgs a) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) acc[i] += __shfl_xor(acc[i], o);
 
-  if (a.bout > DR) {
+  if (L.bout > DR) {
     // y~ for the output-rotation kernel
     if (lane == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (r0 + i < a.out) a.y[r0 + i] = acc[i];
+        if (wr0 + i < rows) L.y[rw0 + wr0 + i] = acc[i];
     }
     return;
   }
   // 4. this workgroup holds whole output blocks: y = S_out . Had_b(y~) / sqrt(b) / d_out,
   //    Had_b[j][k] = (-1)^popcount(j & k)
-  const int64_t nrows = min((int64_t)DR, a.out - rw0);
   if (lane == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) yloc[4 * wv + i] = acc[i];
+    for (int i = 0; i < 4; ++i) yloc[wr0 + i] = acc[i];
   }
   __syncthreads();
-  if (t < nrows) {
-    float v = a.isb_out;
-    if (a.d_out) v = v / a.d_out[rw0 + t];
-    if (a.s_out && a.s_out[rw0 + t] < 0) v = -v;
-    const int b = a.bout, j = t % b, blk0 = t - j;
+  if (t < rows) {
+    float v = L.isb_out;
+    if (L.d_out) v = v / L.d_out[rw0 + t];
+    if (L.s_out && L.s_out[rw0 + t] < 0) v = -v;
+    const int b = L.bout, j = t % b, blk0 = t - j;
     float s = 0.f;
     for (int k = 0; k < b; ++k) {
       const float yk = yloc[blk0 + k];
       s += (__builtin_popcount(j & k) & 1) ? -yk : yk;
     }
-    a.y[rw0 + t] = s * v;
+    L.y[rw0 + t] = s * v;
   }
 }
 
-// y[s0 .. s0 + n) <- S_out . Had_b(y~) / sqrt(b) / d_out over the workgroup's segment (whole
-// blocks), in place.
-__global__ __launch_bounds__(DT) void deploy_outrot_kernel(DeployArgs a) {
+// One workgroup per 16 rows of every layer of the call.  W: 4 or 2 when every layer of the
+// call has codes of that width, 0 for a mix (both bodies compiled in, more registers).
+template <int W, int MC, int B>
+__global__ __launch_bounds__(DT) void deploy_matvec_kernel(GroupArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float xs[];
+  const int l = layer_of(a, blockIdx.x, false);
+  const LayerArgs& L = a.L[l];
+  const int rw0 = ((int)blockIdx.x - L.wg0) * DR;
+  if (W == 4 || (W == 0 && L.bits == 4))
+    matvec_rows<4, MC, B>(a, L, rw0, xs);
+  else
+    matvec_rows<2, MC, B>(a, L, rw0, xs);
+}
+
+// y[s0 .. s0 + n) <- S_out . Had_b(y~) / sqrt(b) / d_out over a segment (whole blocks,
+// n <= 2 * 16 * DT) of a layer whose output blocks exceed 16 rows, in place.  The output
+// factors are loaded before the transform.
+__global__ __launch_bounds__(DT) void deploy_outrot_kernel(GroupArgs a) {
   extern __shared__ __attribute__((aligned(16))) float ys[];
-  const int64_t s0 = (int64_t)blockIdx.x * a.seg;
-  const int n = (int)min((int64_t)a.seg, a.out - s0);
-  stage_rotated(ys, a.y + s0, nullptr, nullptr, 1.f, false, n, n, a.bout);
-  for (int g = threadIdx.x; g < n / 16; g += DT) {
-    const int c = 16 * g;
-    float f[16];
-    factors16(a.d_out ? a.d_out + s0 : nullptr, a.s_out ? a.s_out + s0 : nullptr, a.isb_out, c,
-              true, f);
+  const LayerArgs& L = a.L[layer_of(a, blockIdx.x, true)];
+  const int s0 = ((int)blockIdx.x - L.sg0) * L.seg;
+  const int n = min(L.seg, L.out - s0), t = threadIdx.x;
+  const float* d = L.d_out ? L.d_out + s0 : nullptr;
+  const int8_t* sg = L.s_out ? L.s_out + s0 : nullptr;
+  float f[2][16];
+  factors16(d, sg, L.isb_out, 16 * t, n, f[0]);
+  factors16(d, sg, L.isb_out, 16 * (t + DT), n, f[1]);
+  stage_rotated<2>(ys, L.y + s0, nullptr, nullptr, 1.f, false, n, n, L.bout, [] {});
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = 16 * (t + DT * k);
+    if (c >= n) break;
     float r[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 v = *(const float4*)(ys + pad(c + 4 * q));
-      r[4 * q] = v.x * f[4 * q];
-      r[4 * q + 1] = v.y * f[4 * q + 1];
-      r[4 * q + 2] = v.z * f[4 * q + 2];
-      r[4 * q + 3] = v.w * f[4 * q + 3];
+      r[4 * q] = v.x * f[k][4 * q];
+      r[4 * q + 1] = v.y * f[k][4 * q + 1];
+      r[4 * q + 2] = v.z * f[k][4 * q + 2];
+      r[4 * q + 3] = v.w * f[k][4 * q + 3];
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      *(float4*)(a.y + s0 + c + 4 * q) = make_float4(r[4 * q], r[4 * q + 1], r[4 * q + 2], r[4 * q + 3]);
+      *(float4*)(L.y + s0 + c + 4 * q) = make_float4(r[4 * q], r[4 * q + 1], r[4 * q + 2], r[4 * q + 3]);
   }
 }
 
@@ -323,18 +418,92 @@ int64_t deploy_block(int64_t n, int64_t had) {
 constexpr size_t LDS_MAX = 160 * 1024;
 
 template <typename K>
-kq_status launch_with_lds(K kernel, dim3 grid, size_t lds, hipStream_t s, const DeployArgs& a,
+kq_status launch_with_lds(K kernel, unsigned grid, size_t lds, hipStream_t s, const GroupArgs& a,
                           const char* name) {
   if (lds > 64 * 1024)
     KQ_HIP(hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)lds));
-  kernel<<<grid, dim3(DT), lds, s>>>(a);
+  kernel<<<dim3(grid), dim3(DT), lds, s>>>(a);
   KQ_LAUNCHED(name);
   return KQ_OK;
 }
 
+kq_status deploy_group(const kq_deploy_layer* layers, int nl, int64_t in, const float* x,
+                       void* stream, const char* fn) {
+  if (!layers || !x) return fail(KQ_EINVAL, "%s: NULL argument", fn);
+  if (nl < 1 || nl > MAXL) return fail(KQ_ESHAPE, "%s: %d layers (1 .. %d per call)", fn, nl, MAXL);
+  if (in < 32 || in % 32 != 0 || in > (1 << 20))
+    return fail(KQ_ESHAPE, "%s: in = %lld (a multiple of 32)", fn, (long long)in);
+  GroupArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.nl = nl;
+  a.in = (int)in;
+  int64_t chunk = 0, wg = 0, sg = 0, nck = 0;
+  int wmask = 0;   // 1: some layer has 4-bit codes; 2: some layer has 2-bit codes
+  for (int l = 0; l < nl; ++l) {
+    const kq_deploy_layer& q = layers[l];
+    LayerArgs& L = a.L[l];
+    if (!q.packed || !q.scales || !q.zeros || !q.y) return fail(KQ_EINVAL, "%s: layer %d: NULL argument", fn, l);
+    if (q.bits != 2 && q.bits != 4) return fail(KQ_ENOTIMPL, "%s: layer %d: bits must be 2 or 4", fn, l);
+    if (q.out < 1 || q.out > (1 << 24)) return fail(KQ_ESHAPE, "%s: layer %d: out = %lld", fn, l, (long long)q.out);
+    const int cpc = 4 * 32 / q.bits;
+    if (q.group < 1 || in % q.group != 0 || (q.group != in && q.group % cpc != 0))
+      return fail(KQ_ESHAPE, "%s: layer %d: group must divide in and be a multiple of %d (or in)", fn, l, cpc);
+    if (q.had_in < 0 || q.had_out < 0) return fail(KQ_ESHAPE, "%s: layer %d: negative block", fn, l);
+    const int64_t bin = deploy_block(in, q.had_in), bout = deploy_block(q.out, q.had_out);
+    if (!is_pow2(bin) || in % bin != 0 || bin > 8192 || !is_pow2(bout) || q.out % bout != 0 || bout > 8192)
+      return fail(KQ_ESHAPE, "%s: layer %d: Hadamard blocks must be powers of 2 (<= 8192) dividing the sizes", fn, l);
+    L.packed = q.packed; L.scales = q.scales; L.zeros = q.zeros;
+    L.d_in = q.d_in; L.d_out = q.d_out; L.s_in = q.sign_in; L.s_out = q.sign_out; L.y = q.y;
+    L.out = (int)q.out; L.wpr = (int)(in * q.bits / 32); L.ngroups = (int)(in / q.group); L.bits = q.bits;
+    L.bin = (int)bin; L.bout = (int)bout;
+    L.isb_in = (float)(1.0 / sqrt((double)bin));
+    L.isb_out = (float)(1.0 / sqrt((double)bout));
+    // exact for every code position below 2^16 (the LDS limit keeps in below that)
+    L.gmagic = (unsigned)(((1ull << 32) + (unsigned)q.group - 1) / (unsigned)q.group);
+    L.wg0 = (int)wg;
+    wg += ceil_div(q.out, DR);
+    L.seg = (int)std::max<int64_t>(bout, SEG);
+    L.sg0 = (int)sg;
+    if (bout > DR) sg += ceil_div(q.out, L.seg);
+    chunk = std::max<int64_t>(chunk, 64 * cpc);   // codes per chunk column of a wave
+    wmask |= q.bits == 4 ? 1 : 2;
+    nck = std::max<int64_t>(nck, (L.wpr + 255) / 256);
+  }
+  const int64_t xlen = (in + chunk - 1) / chunk * chunk;
+  const bool b1 = xlen / 16 <= DT;   // one staging group per thread
+  const size_t lds = (size_t)padded_len((int)std::max<int64_t>(xlen, 16 * DT * (b1 ? 1 : 2))) * sizeof(float);
+  if (lds > LDS_MAX)
+    return fail(KQ_ESHAPE, "%s: in = %lld too large for the LDS copy of x", fn, (long long)in);
+  a.xlen = (int)xlen;
+  hipStream_t s = as_stream(stream);
+  // 16-byte chunks per lane and row: all of them in flight when they fit in MAXC
+  const int mc = nck <= 2 ? 2 : nck <= 4 ? 4 : MAXC;
+  const char* nm = "deploy_matvec_kernel";
+  const unsigned grid = (unsigned)wg;
+  kq_status st;
+#define KQ_MV(W)                                                                             \
+  (b1 ? (mc == 2 ? launch_with_lds(deploy_matvec_kernel<W, 2, 1>, grid, lds, s, a, nm)        \
+         : mc == 4 ? launch_with_lds(deploy_matvec_kernel<W, 4, 1>, grid, lds, s, a, nm)      \
+                   : launch_with_lds(deploy_matvec_kernel<W, MAXC, 1>, grid, lds, s, a, nm))  \
+      : (mc == 2 ? launch_with_lds(deploy_matvec_kernel<W, 2, 2>, grid, lds, s, a, nm)        \
+         : mc == 4 ? launch_with_lds(deploy_matvec_kernel<W, 4, 2>, grid, lds, s, a, nm)      \
+                   : launch_with_lds(deploy_matvec_kernel<W, MAXC, 2>, grid, lds, s, a, nm)))
+  st = wmask == 1 ? KQ_MV(4) : wmask == 2 ? KQ_MV(2) : KQ_MV(0);
+#undef KQ_MV
+  if (st != KQ_OK || sg == 0) return st;
+  const size_t lds2 = (size_t)padded_len(2 * 16 * DT) * sizeof(float);   // seg <= 8192
+  return launch_with_lds(deploy_outrot_kernel, (unsigned)sg, lds2, s, a, "deploy_outrot_kernel");
+}
+
 }  // namespace
 }  // namespace kq
+
+extern "C" kq_status kq_deploy_linear_group(const kq_deploy_layer* layers, int n_layers,
+                                            int64_t in, const float* x, void* stream) {
+  return kq::deploy_group(layers, n_layers, in, x, stream, "kq_deploy_linear_group");
+}
 
 extern "C" kq_status kq_deploy_linear(const uint32_t* packed, const float* scales,
                                       const uint8_t* zeros, int bits, int group, int64_t out,
@@ -342,50 +511,9 @@ extern "C" kq_status kq_deploy_linear(const uint32_t* packed, const float* scale
                                       const int8_t* sign_in, const int8_t* sign_out,
                                       int64_t had_in, int64_t had_out, const float* x, float* y,
                                       void* stream) {
-  using namespace kq;
-  if (!packed || !scales || !zeros || !x || !y) return fail(KQ_EINVAL, "kq_deploy_linear: NULL argument");
-  if (bits != 2 && bits != 4) return fail(KQ_ENOTIMPL, "kq_deploy_linear: bits must be 2 or 4");
-  if (out < 1 || in < 1 || in % 32 != 0 || out > (1 << 24) || in > (1 << 20))
-    return fail(KQ_ESHAPE, "kq_deploy_linear: bad shape %lld x %lld", (long long)out, (long long)in);
-  const int cpc = 4 * 32 / bits;
-  if (group < 1 || in % group != 0 || (group != in && group % cpc != 0))
-    return fail(KQ_ESHAPE, "kq_deploy_linear: group must divide in and be a multiple of %d (or in)", cpc);
-  if (had_in < 0 || had_out < 0) return fail(KQ_ESHAPE, "kq_deploy_linear: negative block");
-  const int64_t bin = deploy_block(in, had_in), bout = deploy_block(out, had_out);
-  if (!is_pow2(bin) || in % bin != 0 || bin > 8192 || !is_pow2(bout) || out % bout != 0 || bout > 8192)
-    return fail(KQ_ESHAPE, "kq_deploy_linear: Hadamard blocks must be powers of 2 dividing the sizes");
-  const int64_t chunk = 64 * cpc;   // codes per chunk column of a wave
-  const int64_t xlen = (in + chunk - 1) / chunk * chunk;
-  const size_t lds = (size_t)padded_len((int)xlen) * sizeof(float);
-  if (lds > LDS_MAX)
-    return fail(KQ_ESHAPE, "kq_deploy_linear: in = %lld too large for the LDS copy of x", (long long)in);
-  DeployArgs a;
-  a.packed = packed; a.scales = scales; a.zeros = zeros;
-  a.out = out; a.in = in; a.wpr = in * bits / 32; a.ngroups = in / group; a.group = group;
-  a.d_in = d_in; a.d_out = d_out; a.s_in = sign_in; a.s_out = sign_out;
-  a.bin = (int)bin; a.bout = (int)bout;
-  a.isb_in = (float)(1.0 / sqrt((double)bin));
-  a.isb_out = (float)(1.0 / sqrt((double)bout));
-  a.x = x; a.y = y;
-  a.xlen = (int)xlen;
-  a.seg = (int)std::max<int64_t>(bout, SEG);
-  hipStream_t s = as_stream(stream);
-  const dim3 grid((unsigned)ceil_div(out, DR));
-  // 16-byte chunks per lane and row: all of them in flight when they fit in MAXC
-  const int64_t nck = (a.wpr + 255) / 256;
-  const int mc = nck <= 2 ? 2 : nck <= 4 ? 4 : MAXC;
-  const char* nm = "deploy_matvec_kernel";
-  kq_status st;
-  if (bits == 4)
-    st = mc == 2 ? launch_with_lds(deploy_matvec_kernel<4, 2>, grid, lds, s, a, nm)
-       : mc == 4 ? launch_with_lds(deploy_matvec_kernel<4, 4>, grid, lds, s, a, nm)
-                 : launch_with_lds(deploy_matvec_kernel<4, MAXC>, grid, lds, s, a, nm);
-  else
-    st = mc == 2 ? launch_with_lds(deploy_matvec_kernel<2, 2>, grid, lds, s, a, nm)
-       : mc == 4 ? launch_with_lds(deploy_matvec_kernel<2, 4>, grid, lds, s, a, nm)
-                 : launch_with_lds(deploy_matvec_kernel<2, MAXC>, grid, lds, s, a, nm);
-  if (st != KQ_OK || bout <= DR) return st;
-  const size_t lds2 = (size_t)padded_len(a.seg) * sizeof(float);
-  return launch_with_lds(deploy_outrot_kernel, dim3((unsigned)ceil_div(out, a.seg)), lds2, s, a,
-                         "deploy_outrot_kernel");
+  kq_deploy_layer l;
+  l.packed = packed; l.scales = scales; l.zeros = zeros; l.bits = bits; l.group = group;
+  l.out = out; l.d_in = d_in; l.d_out = d_out; l.sign_in = sign_in; l.sign_out = sign_out;
+  l.had_in = had_in; l.had_out = had_out; l.y = y;
+  return kq::deploy_group(&l, 1, in, x, stream, "kq_deploy_linear");
 }

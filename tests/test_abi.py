@@ -98,3 +98,41 @@ def test_allocator_bit_exact_against_oracle(seed):
     got = kq.kq_allocate_bits(sens, numel, allowed, tn, td)
     want = o.allocate_bits(sens, numel, allowed, tn, td)
     assert got == want
+
+
+def test_deploy_layer_struct_matches_the_header(tmp_path):
+    """The binding's kq_deploy_layer has the size and field offsets the C compiler gives the
+    header's struct."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [f[0] for f in kq.DeployLayer._fields_]
+    prog = tmp_path / "layout.c"
+    prog.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "kq.h"\nint main(void) {\n'
+                    '  printf("%zu", sizeof(kq_deploy_layer));\n'
+                    + "".join(f'  printf(" %zu", offsetof(kq_deploy_layer, {f}));\n' for f in fields)
+                    + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(prog), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [ctypes.sizeof(kq.DeployLayer)] + [getattr(kq.DeployLayer, f).offset for f in fields]
+    assert got == want
+
+
+def test_deploy_rejects_bad_arguments_on_host():
+    lib = _raw()
+    buf = ctypes.c_void_p(0x1000)
+    L = kq.DeployLayer(buf, buf, buf, 4, 128, 64, None, None, None, None, 0, 0, buf)
+    arr = (kq.DeployLayer * 9)(*([L] * 9))
+    assert lib.kq_deploy_linear_group(arr, 0, 256, buf, None) == kq.KQ_ESHAPE
+    assert lib.kq_deploy_linear_group(arr, 9, 256, buf, None) == kq.KQ_ESHAPE
+    assert lib.kq_deploy_linear_group(arr, 1, 100, buf, None) == kq.KQ_ESHAPE
+    assert lib.kq_deploy_linear_group(arr, 1, 256, None, None) == kq.KQ_EINVAL
+    bad = (kq.DeployLayer * 2)(L, kq.DeployLayer(buf, buf, buf, 3, 128, 64, None, None, None, None,
+                                                  0, 0, buf))
+    assert lib.kq_deploy_linear_group(bad, 2, 256, buf, None) == kq.KQ_ENOTIMPL
+    assert b"layer 1" in lib.kq_last_error()
+    assert lib.kq_deploy_linear(buf, buf, buf, 4, 100, 64, 256, None, None, None, None, 0, 0, buf,
+                                buf, None) == kq.KQ_ESHAPE

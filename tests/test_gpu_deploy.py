@@ -204,3 +204,48 @@ def test_deploy_long_rows():
     # P_out^T yt = S_out Had(yt) / sqrt(b): the block transform of yt with unit signs, then S
     ref = o.rotate_cols(yt[:, None], np.ones(out_n), bout)[:, 0] * s_out / d_out
     assert rel_fro(ys[0], ref) <= 1e-5
+
+
+def _group_case(torch, rng, in_n, specs):
+    """specs: (out, bits, group, had_in, had_out) per layer; returns the binding's layer dicts,
+    the oracle's outputs and x."""
+    dev = "cuda"
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    x = rng.standard_normal(in_n).astype(np.float32)
+    layers, refs = [], []
+    for out_n, bits, group, bin_, bout in specs:
+        codes, scales, zeros, d_in, d_out, s_in, s_out, _ = _layer(rng, out_n, in_n, bits, group)
+        layers.append(dict(packed=t(o.pack_codes(codes, bits).view(np.int32)), scales=t(scales),
+                           zeros=t(zeros), bits=bits, group=group, d_in=t(d_in), d_out=t(d_out),
+                           sign_in=t(s_in), sign_out=t(s_out), had_in=bin_, had_out=bout,
+                           y=torch.full((out_n,), float("nan"), device=dev)))
+        refs.append(_ref(codes, scales, zeros, group, d_in, d_out, s_in, s_out, bin_, bout, x))
+    return layers, refs, t(x)
+
+
+@pytest.mark.parametrize("in_n,specs", [
+    # mixed widths, groups, blocks: an output rotation kernel for two layers, a local one
+    (1024, [(256, 4, 128, 1024, 256), (96, 2, 1024, 256, 16), (512, 2, 128, 0, 512)]),
+    # Llama-2-7B q/k/v with mixed widths (inter-layer mixed precision)
+    (4096, [(4096, 4, 128, 0, 0), (4096, 2, 128, 0, 0), (4096, 4, 128, 0, 0)]),
+    # gate/up
+    (4096, [(11008, 4, 128, 0, 0), (11008, 4, 128, 0, 0)]),
+    # eight layers of different heights
+    (512, [(16 * (k + 1), 4 if k % 2 else 2, 128, 0, 0) for k in range(8)]),
+])
+def test_deploy_group_matches_oracle_and_single_calls(in_n, specs):
+    torch = torch_cuda()
+    import post_quantization_syrk_amd as kq
+    announce(f"deploy group in={in_n} layers={len(specs)}")
+    rng = np.random.default_rng(in_n + len(specs))
+    layers, refs, x = _group_case(torch, rng, in_n, specs)
+    kq.kq_deploy_linear_group(layers, x)
+    torch.cuda.synchronize()
+    for k, (L, ref) in enumerate(zip(layers, refs)):
+        yg = L["y"].cpu().numpy()
+        assert rel_fro(yg, ref) <= 1e-5, k
+        ys = torch.empty_like(L["y"])
+        kq.kq_deploy_linear(L["packed"], L["scales"], L["zeros"], L["bits"], L["group"], L["d_in"],
+                            L["d_out"], L["sign_in"], L["sign_out"], L["had_in"], L["had_out"], x, ys)
+        torch.cuda.synchronize()
+        assert np.allclose(yg, ys.cpu().numpy(), rtol=1e-6, atol=1e-7), k
