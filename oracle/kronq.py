@@ -26,6 +26,8 @@ __all__ = [
     "GptqResult", "quantize_layer", "pack_codes", "unpack_codes", "proxy_loss", "predicted_loss",
     "allocate_bits", "brute_force_min_loss", "NotSPDError", "ClippedMinMaxGrid",
     "act_order_perm", "CLIP_NORM", "CLIP_GRID", "CLIP_MAXSHRINK", "dequant", "deploy_linear",
+    "quadratic_forms", "flipflop_input_factor", "flipflop_output_factor", "flipflop",
+    "flipflop_objective",
 ]
 
 BIIP_FULL, BIIP_NO_RESCALE, BIIP_IN_ONLY, BIIP_OUT_ONLY = 0, 1, 2, 3
@@ -597,6 +599,85 @@ def deploy_linear(Qhat: np.ndarray, d_in: np.ndarray, d_out: np.ndarray, sign_in
     Yt = Xt @ np.asarray(Qhat, np.float64).T
     Y = (Yt @ P_out) / np.asarray(d_out, np.float64)[None, :]
     return Y[0] if np.ndim(x) == 1 else Y
+
+
+# ---------------------------------------------------------------------------
+# FlipFlop Hessian factors
+# ---------------------------------------------------------------------------
+def _dead_to_unit(M: np.ndarray) -> np.ndarray:
+    """Copy of M whose zero diagonal entries are 1.
+
+    READING: a channel whose calibration data are all zero has a zero row and
+    column in its factor; it counts as 1 on the diagonal, which leaves every
+    quadratic form of the data unchanged (its entries are zero)."""
+    M = np.array(M, dtype=np.float64, copy=True)
+    d = np.diag(M).copy()
+    z = d == 0.0
+    M[np.flatnonzero(z), np.flatnonzero(z)] = 1.0
+    return M
+
+
+def quadratic_forms(S: np.ndarray, M: np.ndarray) -> np.ndarray:
+    """q_t = s_t^T M^-1 s_t for every row s_t of S (zero-diagonal channels as in
+    _dead_to_unit).  Written out: the explicit inverse, then a row-wise dot."""
+    S = np.asarray(S, dtype=np.float64)
+    Minv = np.linalg.inv(_dead_to_unit(M))
+    return np.einsum("ti,ij,tj->t", S, Minv, S)
+
+
+def flipflop_input_factor(X: np.ndarray, G: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """A = E_t[(g_t^T B^-1 g_t) x_t x_t^T] / m.
+
+    [WaterKron] Table 1, row "FlipFlop", input factor; E is the mean over the T
+    calibration tokens (x_t, g_t are one token's activation and output
+    gradient).  READING: the table gives the factors without constants; the
+    1/m here (1/n for the output factor) is the classical flip-flop's, the
+    maximum-likelihood fit of a Kronecker covariance to the samples
+    vec(x_t g_t^T), and gives the iteration a fixed point when m != n.  A (x) B
+    itself does not depend on it."""
+    X = np.asarray(X, dtype=np.float64)
+    G = np.asarray(G, dtype=np.float64)
+    T, m = G.shape
+    w = quadratic_forms(G, B)
+    return (X.T * w) @ X / (T * m)
+
+
+def flipflop_output_factor(X: np.ndarray, G: np.ndarray, A: np.ndarray) -> np.ndarray:
+    """B = E_t[(x_t^T A^-1 x_t) g_t g_t^T] / n ([WaterKron] Table 1, "FlipFlop",
+    output factor; constants as in flipflop_input_factor)."""
+    X = np.asarray(X, dtype=np.float64)
+    G = np.asarray(G, dtype=np.float64)
+    T, n = X.shape
+    v = quadratic_forms(X, A)
+    return (G.T * v) @ G / (T * n)
+
+
+def flipflop(X: np.ndarray, G: np.ndarray, iters: int, B0: np.ndarray | None = None):
+    """The alternating fixed-point iteration of [WaterKron] Table 1 ("Frobenius
+    and FlipFlop approximations are computed using the alternating fixed-point
+    iteration, starting from the identity matrix").  READING: it starts from
+    B = I and each iteration updates A from the current B, then B from the new
+    A.  Returns [(A_1, B_1), ..., (A_iters, B_iters)]."""
+    m = np.asarray(G).shape[1]
+    B = np.eye(m) if B0 is None else np.asarray(B0, dtype=np.float64)
+    out = []
+    for _ in range(iters):
+        A = flipflop_input_factor(X, G, B)
+        B = flipflop_output_factor(X, G, A)
+        out.append((A, B))
+    return out
+
+
+def flipflop_objective(X: np.ndarray, G: np.ndarray, A: np.ndarray, B: np.ndarray) -> float:
+    """E_t[(x_t^T A^-1 x_t)(g_t^T B^-1 g_t)] + m log det A + n log det B: the Gaussian
+    covariance fit of A (x) B to H = E[x x^T (x) g g^T], i.e. tr((A (x) B)^-1 H) +
+    log det(A (x) B) ([WaterKron] abstract: minimizing the mismatch factor is a
+    Gaussian covariance-fitting problem).  Each half step of flipflop minimizes
+    it over one factor."""
+    n, m = np.asarray(A).shape[0], np.asarray(B).shape[0]
+    v = quadratic_forms(X, A)
+    w = quadratic_forms(G, B)
+    return float(np.mean(v * w) + m * np.linalg.slogdet(A)[1] + n * np.linalg.slogdet(B)[1])
 
 
 # ---------------------------------------------------------------------------

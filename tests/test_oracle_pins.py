@@ -628,3 +628,113 @@ def test_allocator_budget_and_monotonicity():
             for b in range(4):
                 if s[a] > s[b]:
                     assert bits[a] >= bits[b]
+
+
+# ---------------------------------------------------------------------------
+# FlipFlop Hessian factors ([WaterKron] Table 1)
+# ---------------------------------------------------------------------------
+def _factorial_tokens(rng, nx, n, ng, m):
+    """Every pair (x_i, g_j) of two small sets: then E[x x^T (x) g g^T] = Abar (x) Gbar."""
+    xs = rng.standard_normal((nx, n)) * np.exp(rng.standard_normal(n))
+    gs = rng.standard_normal((ng, m)) * np.exp(rng.standard_normal(m))
+    X = np.repeat(xs, ng, axis=0)
+    G = np.tile(gs, (nx, 1))
+    return X, G, xs.T @ xs / nx, gs.T @ gs / ng
+
+
+def test_flipflop_full_factorial_closed_form():
+    """Full-factorial tokens: the iteration from B = I reaches its fixed point in one step,
+    A = Abar tr(Gbar) / m and B = m Gbar / tr(Gbar) (derived by hand from the two updates)."""
+    rng = np.random.default_rng(31)
+    n, m = 4, 3
+    X, G, Abar, Gbar = _factorial_tokens(rng, 9, n, 7, m)
+    for A, B in o.flipflop(X, G, 4):
+        assert np.allclose(A, Abar * np.trace(Gbar) / m, rtol=1e-12, atol=0)
+        assert np.allclose(B, m * Gbar / np.trace(Gbar), rtol=1e-12, atol=0)
+
+
+def test_flipflop_single_output_channel():
+    """m = 1: B stays 1 and A = E[g^2 x x^T] at every iteration."""
+    rng = np.random.default_rng(32)
+    X = rng.standard_normal((50, 5))
+    G = rng.standard_normal((50, 1)) * 3.0
+    want = sum(G[t, 0] ** 2 * np.outer(X[t], X[t]) for t in range(50)) / 50
+    for A, B in o.flipflop(X, G, 3):
+        assert np.allclose(B, [[1.0]], rtol=1e-12)
+        assert np.allclose(A, want, rtol=1e-12)
+
+
+def test_flipflop_first_step_by_loops():
+    """From B = I: A_1 = (1/(T m)) sum_t |g_t|^2 x_t x_t^T and B_1 from A_1, by explicit loops."""
+    rng = np.random.default_rng(33)
+    T, n, m = 30, 3, 4
+    X, G = rng.standard_normal((T, n)), rng.standard_normal((T, m))
+    A1 = np.zeros((n, n))
+    for t in range(T):
+        A1 += sum(G[t, j] ** 2 for j in range(m)) * np.outer(X[t], X[t])
+    A1 /= T * m
+    Ai = np.linalg.inv(A1)
+    B1 = np.zeros((m, m))
+    for t in range(T):
+        B1 += sum(X[t, i] * Ai[i, k] * X[t, k] for i in range(n) for k in range(n)) * np.outer(G[t], G[t])
+    B1 /= T * n
+    (A, B), = o.flipflop(X, G, 1)
+    assert np.allclose(A, A1, rtol=1e-12) and np.allclose(B, B1, rtol=1e-12)
+
+
+def test_flipflop_objective_is_the_kronecker_fit_and_decreases():
+    """The objective equals tr((A (x) B)^-1 H) + log det(A (x) B) with H = E[x x^T (x) g g^T]
+    built densely; it never increases over half steps; the converged pair satisfies both
+    updates and beats the marginal factors and random perturbations of itself."""
+    rng = np.random.default_rng(34)
+    T, n, m = 60, 3, 2
+    scale_x = np.exp(rng.standard_normal(n))
+    X = rng.standard_normal((T, n)) * scale_x
+    G = rng.standard_normal((T, m)) * (1.0 + np.abs(X[:, :1]))   # g depends on x: H is not Kronecker
+    H = sum(np.kron(np.outer(X[t], X[t]), np.outer(G[t], G[t])) for t in range(T)) / T
+
+    def dense(A, B):
+        K = np.kron(A, B)
+        return float(np.trace(np.linalg.solve(K, H)) + np.linalg.slogdet(K)[1])
+
+    A0 = np.eye(n)
+    B = np.eye(m)
+    prev = dense(A0, B)
+    for _ in range(60):
+        A = o.flipflop_input_factor(X, G, B)
+        cur = dense(A, B)
+        assert cur <= prev + 1e-12
+        assert abs(o.flipflop_objective(X, G, A, B) - cur) < 1e-10 * max(1.0, abs(cur))
+        prev = cur
+        B = o.flipflop_output_factor(X, G, A)
+        cur = dense(A, B)
+        assert cur <= prev + 1e-12
+        prev = cur
+    assert np.allclose(o.flipflop_input_factor(X, G, B), A, rtol=1e-9)
+    assert np.allclose(o.flipflop_output_factor(X, G, A), B, rtol=1e-9)
+    Am, Bm = X.T @ X / T, G.T @ G / T
+    best_marginal = min(dense(Am * c, Bm) for c in np.geomspace(1e-3, 1e3, 61))
+    assert prev < best_marginal
+    for _ in range(20):
+        Pa = rng.standard_normal((n, n)) * 1e-3
+        Pb = rng.standard_normal((m, m)) * 1e-3
+        assert dense(A + Pa @ Pa.T + 1e-4 * np.eye(n), B) >= prev - 1e-12
+        assert dense(A, B + Pb @ Pb.T + 1e-4 * np.eye(m)) >= prev - 1e-12
+
+
+def test_flipflop_dead_channel_counts_as_one():
+    """A channel whose activations are all zero: its row and column of A are zero and its
+    diagonal counts as 1 in the inverse, so the other channels see the same weights as if it
+    were absent."""
+    rng = np.random.default_rng(35)
+    T, n, m = 40, 4, 3
+    X = rng.standard_normal((T, n))
+    X[:, 2] = 0.0
+    G = rng.standard_normal((T, m))
+    (A, B), = o.flipflop(X, G, 1)
+    (A3, B3), = o.flipflop(np.delete(X, 2, axis=1), G, 1)
+    assert np.all(A[2] == 0) and np.all(A[:, 2] == 0)
+    keep = [0, 1, 3]
+    assert np.allclose(A[np.ix_(keep, keep)], A3, rtol=1e-12)
+    # B is divided by n: the dead channel still counts in the dimension
+    assert np.allclose(B * n, B3 * (n - 1), rtol=1e-12)
