@@ -290,6 +290,40 @@ typedef struct kq_deploy_layer {
 kq_status kq_deploy_linear_group(const kq_deploy_layer* layers, int n_layers, int64_t in,
                                  const float* x, void* stream);
 
+/*
+ * kq_flipflop_workspace -- device workspace bytes of kq_flipflop for T tokens, n input and m
+ * output channels.
+ */
+kq_status kq_flipflop_workspace(int64_t T, int64_t n, int64_t m, size_t* bytes);
+
+/*
+ * kq_flipflop -- the FlipFlop Hessian factors by the alternating fixed-point iteration:
+ *   B_0 = I;  for k = 1 .. iters:
+ *     A_k = E_t[(g_t^T B_{k-1}^-1 g_t) x_t x_t^T] / m,
+ *     B_k = E_t[(x_t^T A_k^-1 x_t) g_t g_t^T] / n,
+ * E_t the mean over the T tokens (x_t, g_t: token t's activation and output gradient).
+ *
+ * Follows: WaterKron and FlipFlop Hessian, Table 1 (row "FlipFlop": input factor
+ * E[(g^T B^-1 g) x x^T], output factor E[(x^T A^-1 x) g g^T]) and its caption (alternating
+ * fixed-point iteration from the identity).  The 1/m and 1/n are the classical flip-flop's
+ * normalization; A (x) B does not depend on it.  Inverses: the reverse Cholesky factor of
+ * the current factor without damping (a zero diagonal entry counts as 1); the inverse
+ * factor enters the per-token quadratic forms rounded to bf16, as the streams are, with
+ * fp32 accumulation, and the scaled streams are rounded to bf16 for the SYRK.
+ *
+ *   X, G     device bf16 bit patterns, T x n and T x m, token-major, leading dims ldx, ldg
+ *            (multiples of 8, >= the widths), 16-byte aligned
+ *   T        tokens (>= 1);  n, m  channels, multiples of 128 (<= 65536)
+ *   iters    1 .. 1000
+ *   A, B     device fp32, n x n and m x m, contiguous: A_iters and B_iters (full symmetric)
+ *   ws       device workspace of kq_flipflop_workspace(T, n, m) bytes
+ * Synchronizes `stream` before returning; KQ_ENOTSPD when a factor has a non-positive
+ * pivot (results undefined).  KQ_ESHAPE / KQ_EINVAL / KQ_EWORKSPACE before any launch.
+ */
+kq_status kq_flipflop(const uint16_t* X, int64_t ldx, const uint16_t* G, int64_t ldg, int64_t T,
+                      int64_t n, int64_t m, int iters, float* A, float* B, void* ws,
+                      size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "KQ_OK", 1: "KQ_EINVAL", 2: "KQ_ESHAPE", 3: "KQ_ENOTSPD", 4: 
 
 EXPORTED = ("kq_version", "kq_last_error", "kq_accumulate_hessian", "kq_sensitivity",
             "kq_biip_rotate", "kq_quantize_layer_workspace", "kq_quantize_layer",
-            "kq_allocate_bits", "kq_deploy_linear", "kq_deploy_linear_group")
+            "kq_allocate_bits", "kq_deploy_linear", "kq_deploy_linear_group",
+            "kq_flipflop_workspace", "kq_flipflop")
 
 
 class KQError(RuntimeError):
@@ -68,6 +69,8 @@ _SIGS = {
     "kq_deploy_linear": ([_vp, _vp, _vp, _int, _int, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _i64,
                           _vp, _vp, _vp], _int),
     "kq_deploy_linear_group": ([ctypes.POINTER(DeployLayer), _int, _i64, _vp, _vp], _int),
+    "kq_flipflop_workspace": ([_i64, _i64, _i64, ctypes.POINTER(_sz)], _int),
+    "kq_flipflop": ([_vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _sz, _vp], _int),
 }
 
 _lib = None
@@ -267,3 +270,28 @@ def kq_deploy_linear_group(layers, x, stream=None) -> None:
     st = lib.kq_deploy_linear_group(arr, len(layers), x.shape[-1], _dev_ptr(x, "x", (torch.float32,)),
                                     _stream(stream))
     _check(st, "kq_deploy_linear_group")
+
+
+def kq_flipflop_workspace(T: int, n: int, m: int) -> int:
+    lib = load_library()
+    b = ctypes.c_size_t(0)
+    _check(lib.kq_flipflop_workspace(T, n, m, ctypes.byref(b)), "kq_flipflop_workspace")
+    return b.value
+
+
+def kq_flipflop(X, G, iters: int, A, B, ws=None, stream=None) -> None:
+    """FlipFlop factors A (n x n) and B (m x m) from bf16 streams X (T x n) and G (T x m),
+    given as int16/uint16/bfloat16 tensors of bit patterns, after `iters` iterations."""
+    torch = _torch()
+    lib = load_library()
+    T, n = X.shape
+    m = G.shape[1]
+    if G.shape[0] != T:
+        raise ValueError("X and G need the same token count")
+    if ws is None:
+        ws = torch.empty(kq_flipflop_workspace(T, n, m), dtype=torch.uint8, device=X.device)
+    bf = (torch.int16, torch.uint16, torch.bfloat16)
+    st = lib.kq_flipflop(_dev_ptr(X, "X", bf), _ld(X, "X"), _dev_ptr(G, "G", bf), _ld(G, "G"), T, n, m,
+                         iters, _dev_ptr(A, "A", (torch.float32,)), _dev_ptr(B, "B", (torch.float32,)),
+                         _dev_ptr(ws, "ws", (torch.uint8,)), ws.numel(), _stream(stream))
+    _check(st, "kq_flipflop")

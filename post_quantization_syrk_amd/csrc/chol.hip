@@ -589,7 +589,8 @@ __global__ __launch_bounds__(256) void pmat_kernel(float* __restrict__ F, int64_
 
 // Copies HX into the workspace matrix F, damps it and factors it (H_d = R R^T).  On return F
 // holds, above its B x B diagonal blocks, GPTQ's feedback factors P = R[<J, J] U_JJ, and in
-// those blocks U_JJ (U = R^-1 = chol_upper(H_d^-1)); the strictly lower triangle is zero.
+// the upper triangles of those blocks U_JJ (U = R^-1 = chol_upper(H_d^-1)); the strictly
+// lower triangle keeps the factorization's panels Z^T (not part of U or P).
 // T is scratch of 128 n floats.
 kq_status damp_and_factor(const float* HX, float* F, float* T, uint8_t* dead, double* lam,
                           int* flag, int64_t n, float damp, int B, hipStream_t s) {

@@ -1,0 +1,405 @@
+// FlipFlop Hessian factors: A = E[(g^T B^-1 g) x x^T] / m and B = E[(x^T A^-1 x) g g^T] / n,
+// by the alternating fixed-point iteration from B = I.
+//
+// WaterKron and FlipFlop Hessian, Table 1 (row "FlipFlop") and its caption (the alternating
+// fixed-point iteration from the identity); the 1/m and 1/n are the classical flip-flop's
+// (the maximum-likelihood fit of a Kronecker covariance to the samples vec(x g^T)), which
+// A (x) B does not depend on.  E is the mean over the T calibration tokens.
+//
+// One half step, A from B (the other half swaps the streams):
+//   1. B = R R^T (the engine's reverse Cholesky, no damping; a zero diagonal counts as 1),
+//      then the explicit U = R^-1 (upper): its diagonal blocks and the panels P = R U_JJ
+//      come from the factorization, the blocks above from U[<J, J] = -U[<J,<J] P[<J, J],
+//      one fp32 MFMA product per block column.  g^T B^-1 g = |U g|^2.
+//   2. w_t = |U g_t|^2 for every token: a bf16 MFMA product of the stream with U (rounded
+//      to bf16, as the streams are), fp32 accumulation, the squares summed per token in the
+//      epilogue; tiles left of the diagonal of U are skipped.
+//   3. The scaled stream sqrt(w_t / (T m)) x_t, rounded to bf16, goes through the SYRK:
+//      A = sum_t (w_t / (T m)) x_t x_t^T.
+//
+// qform_kernel: 256-token x 256-output tiles, 4 waves of 128 x 128 (4 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16); stages of 32 contraction indices: both panels (256 rows x 64
+// bytes each) copied into LDS by the load unit (global_load_lds, 16 bytes per lane) in a
+// ring of four stages, operands read with ds_read_b128 (8 consecutive contraction indices of
+// one row per lane, as the MFMA takes them); the 16-byte chunks of row r sit in slot
+// c ^ ((r >> 2) & 3), which spreads the rows read together over the banks.
+#include "kq_internal.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+namespace kq {
+
+kq_status damp_and_factor(const float* HX, float* F, float* T, uint8_t* dead, double* lam,
+                          int* flag, int64_t n, float damp, int B, hipStream_t s);
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int QT = 256;                 // tile edge (tokens, outputs)
+constexpr int QK = 32;                  // contraction indices per stage
+constexpr int QPANEL = QT * QK;         // bf16 elements of one panel (16 KB)
+constexpr int QSTAGE = 2 * QPANEL;      // both panels of a stage (32 KB)
+constexpr int QNST = 4;                 // stages in the ring (128 KB)
+constexpr int QCOPIES = QPANEL * 2 / 1024 / 4;   // 1 KB wave copies per panel and wave (4)
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Sixteen zero bytes: the source of every copy lane whose row lies outside the matrix, so that
+// each wave issues the same number of copies per stage and the vmcnt waits stay exact.
+__device__ __attribute__((aligned(16))) uint32_t q_zero_chunk[4];
+
+__device__ __forceinline__ int qswz(int r) { return (r >> 2) & 3; }
+
+struct QArgs {
+  const uint16_t* S;   // stream, T x k bf16, leading dim lds (elements)
+  int64_t lds;
+  const uint16_t* U;   // k x k bf16, upper triangular (row j: U[j, j..k)), leading dim k
+  int64_t T;
+  int k;
+  float* part;         // T x np partial sums of squares (np = 2 * ceil(k / 256))
+  int np;
+  int ntt, njt;        // token tiles, output tiles
+  int per_xcd;         // tiles per XCD
+};
+
+// part[t, 2 jt + wc] = sum over the 128 outputs j of wave column wc of tile jt of
+// (sum_i U[j, i] S[t, i])^2.
+__global__ __launch_bounds__(256) void qform_kernel(QArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[QNST][QSTAGE];
+  // workgroup u runs on XCD u mod 8; each XCD takes a contiguous range of tiles in
+  // token-major order, so the 256 x k panel of one token tile stays in that XCD's L2 while
+  // its output tiles pass
+  const int u = blockIdx.x;
+  const int q = (u & 7) * a.per_xcd + (u >> 3);
+  if (q >= a.ntt * a.njt) return;
+  const int tt = q / a.njt, jt = q % a.njt;
+  const int64_t t0 = (int64_t)tt * QT;
+  const int j0 = jt * QT;
+  const int i_begin = j0;                       // U[j, i] = 0 for i < j
+  const int nst = (a.k - i_begin) / QK;         // k % 128 == 0
+  const int nst_round = (nst + QNST - 1) / QNST * QNST;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+
+  // copy sources: wave w fills 1 KB blocks 4w + c of each panel (16 rows of 64 bytes); lane l
+  // writes slot l & 3 of row 16 (4w + c) + (l >> 2), which holds chunk (l & 3) ^ qswz(row)
+  const uint16_t* zero = (const uint16_t*)q_zero_chunk;
+  const uint16_t* srcS[QCOPIES];
+  const uint16_t* srcU[QCOPIES];
+#pragma unroll
+  for (int c = 0; c < QCOPIES; ++c) {
+    const int row = 16 * (4 * wave + c) + (lane >> 2);
+    const int chunk = (lane & 3) ^ qswz(row);
+    srcS[c] = t0 + row < a.T ? a.S + (t0 + row) * a.lds + i_begin + 8 * chunk : zero;
+    srcU[c] = j0 + row < a.k ? a.U + (int64_t)(j0 + row) * a.k + i_begin + 8 * chunk : zero;
+  }
+  auto issue = [&](int s, uint16_t* buf) {
+    const bool live = s < nst;
+#pragma unroll
+    for (int c = 0; c < QCOPIES; ++c) {
+      const uint16_t* ps = live && srcS[c] != zero ? srcS[c] + s * QK : zero;
+      const uint16_t* pu = live && srcU[c] != zero ? srcU[c] + s * QK : zero;
+      __builtin_amdgcn_global_load_lds((const void*)ps,
+                                       (__attribute__((address_space(3))) void*)(buf + (4 * wave + c) * 512),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)pu,
+                                       (__attribute__((address_space(3))) void*)(buf + QPANEL + (4 * wave + c) * 512),
+                                       16, 0, 0);
+    }
+  };
+
+  // operand read offsets (elements) inside a panel: row 32 b + (l & 31) of the wave's half,
+  // chunk 2 h + (l >> 5)
+  int offS[2][4], offU[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int rs = 128 * wr + 32 * b + (lane & 31), ru = 128 * wc + 32 * b + (lane & 31);
+      const int c = 2 * h + (lane >> 5);
+      offS[h][b] = rs * QK + 8 * (c ^ qswz(rs));
+      offU[h][b] = QPANEL + ru * QK + 8 * (c ^ qswz(ru));
+    }
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[m][n] = f32x16{};
+
+#pragma unroll
+  for (int s = 0; s < QNST; ++s) issue(s, ring[s]);
+
+  for (int s0 = 0; s0 < nst_round; s0 += QNST) {
+#pragma unroll
+    for (int r = 0; r < QNST; ++r) {
+      const int s = s0 + r;
+      uint16_t* buf = ring[r];
+      // this wave's copies of stage s have landed once at most the later stages' remain
+      __builtin_amdgcn_s_waitcnt(wait_vm(2 * QCOPIES * (QNST - 1)));
+      lds_barrier();
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 av[4], bv[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          av[b] = *(const bf16x8*)(buf + offS[h][b]);
+          bv[b] = *(const bf16x8*)(buf + offU[h][b]);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[m], bv[n], acc[m][n], 0, 0, 0);
+      }
+      lds_barrier();
+      issue(s + QNST, buf);
+    }
+  }
+  // the ring's trailing copies (zeros) must land before the LDS is reused
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  lds_barrier();
+
+  // epilogue: lane holds output column l & 31 of each 32 x 32 block, rows
+  // 8 (r / 4) + 4 (l / 32) + r % 4.  Sum the squares over the wave's 128 columns: over the
+  // four column blocks in registers, then over the 32 lanes of a half-wave through LDS.
+  float* red = (float*)ring[wave];   // 128 x 33 floats
+  const int l32 = lane & 31, rh = (lane >> 5) * 4;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = 0.f;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) v = fmaf(acc[m][n][r], acc[m][n][r], v);
+      const int row = 32 * m + 8 * (r >> 2) + rh + (r & 3);
+      red[row * 33 + l32] = v;
+    }
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = lane + 64 * h;
+    float v = 0.f;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) v += red[row * 33 + c];
+    const int64_t t = t0 + 128 * wr + row;
+    if (t < a.T) a.part[t * a.np + 2 * jt + wc] = v;
+  }
+}
+
+// out[t, :] = bf16(sqrt(c * sum_p part[t, p]) * S[t, :]) (round to nearest even); one
+// workgroup per token, 8 channels per thread and step.
+__global__ __launch_bounds__(256) void ff_scale_kernel(const uint16_t* __restrict__ S, int64_t lds,
+                                                       int k, const float* __restrict__ part,
+                                                       int np, float c, uint16_t* __restrict__ out,
+                                                       int64_t ldo) {
+  const int64_t t = blockIdx.x;
+  __shared__ float sf;
+  if (threadIdx.x < 64) {
+    float w = 0.f;
+    for (int p = threadIdx.x; p < np; p += 64) w += part[t * np + p];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) w += __shfl_xor(w, o);
+    if (threadIdx.x == 0) sf = sqrtf(c * w);
+  }
+  __syncthreads();
+  const float f = sf;
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  for (int i = 8 * threadIdx.x; i < k; i += 8 * 256) {
+    const u32x4 v = *(const u32x4*)(S + t * lds + i);
+    u32x4 o;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      unsigned r = 0;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float x = __uint_as_float(((v[h] >> (16 * e)) & 0xffffu) << 16) * f;
+        unsigned u = __float_as_uint(x);
+        u += 0x7fffu + ((u >> 16) & 1u);
+        r |= (u >> 16) << (16 * e);
+      }
+      o[h] = r;
+    }
+    *(u32x4*)(out + t * ldo + i) = o;
+  }
+}
+
+// The diagonal 128-blocks of U: the upper triangles of F's diagonal blocks (U_JJ); below
+// the diagonal F holds the factorization's panels, which are not part of U.
+__global__ __launch_bounds__(256) void copy_diag_blocks(const float* __restrict__ F,
+                                                        float* __restrict__ U, int64_t k) {
+  const int64_t J = blockIdx.x;
+  for (int e = threadIdx.x; e < 128 * 128; e += 256) {
+    const int r = e >> 7, c = e & 127;
+    U[(J * 128 + r) * k + J * 128 + c] = c >= r ? F[(J * 128 + r) * k + J * 128 + c] : 0.0f;
+  }
+}
+
+// bf16 copy of an fp32 matrix (round to nearest even), 4 entries per thread.
+__global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ src,
+                                                      uint16_t* __restrict__ dst, int64_t count) {
+  const int64_t i = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+  if (i >= count) return;
+  const float4 v = *(const float4*)(src + i);
+  const float e[4] = {v.x, v.y, v.z, v.w};
+  unsigned short o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    unsigned u = __float_as_uint(e[j]);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    o[j] = (unsigned short)(u >> 16);
+  }
+  *(ushort4*)(dst + i) = make_ushort4(o[0], o[1], o[2], o[3]);
+}
+
+__global__ void identity_kernel(float* __restrict__ M, int64_t k) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < k * k) M[i] = (i / k == i % k) ? 1.f : 0.f;
+}
+
+struct Workspace {
+  uint16_t* Ss;    // scaled stream, T x ldS bf16
+  int64_t ldS;
+  float* part;     // T x npmax
+  float* F;        // factorization, kmax^2
+  float* Tsc;      // factorization scratch, 128 kmax
+  float* Uf;       // explicit inverse factor, kmax^2
+  uint16_t* Ub;    // its bf16 copy, kmax^2
+  uint8_t* dead;   // kmax
+  double* lam;
+  int* flag;
+};
+
+inline int64_t al256(int64_t b) { return (b + 255) / 256 * 256; }
+
+int64_t layout(int64_t T, int64_t n, int64_t m, char* base, Workspace* w) {
+  const int64_t k = std::max(n, m);
+  const int64_t np = 2 * ((k + 255) / 256);
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) { const int64_t o = off; off += al256(bytes); return base ? base + o : nullptr; };
+  Workspace x;
+  x.ldS = (k + 7) / 8 * 8;
+  x.Ss = (uint16_t*)take(T * x.ldS * 2);
+  x.part = (float*)take(T * np * 4);
+  x.F = (float*)take(k * k * 4);
+  x.Tsc = (float*)take(128 * k * 4);
+  x.Uf = (float*)take(k * k * 4);
+  x.Ub = (uint16_t*)take(k * k * 2);
+  x.dead = (uint8_t*)take(k);
+  x.lam = (double*)take(8);
+  x.flag = (int*)take(4);
+  if (w) *w = x;
+  return off;
+}
+
+// Ub = bf16(U), U = R^-1 for M = R R^T (no damping; zero diagonals count as 1).
+kq_status inverse_factor(const float* M, int64_t k, const Workspace& w, hipStream_t s) {
+  KQ_TRY(damp_and_factor(M, w.F, w.Tsc, w.dead, w.lam, w.flag, k, 0.0f, 128, s));
+  KQ_TRY(fill_f32(w.Uf, k * k, 0.0f, s));
+  copy_diag_blocks<<<dim3((unsigned)(k / 128)), dim3(256), 0, s>>>(w.F, w.Uf, k);
+  KQ_LAUNCHED("copy_diag_blocks");
+  for (int64_t J = 1; J < k / 128; ++J) {
+    const int64_t c0 = 128 * J;
+    GemmArgs g = {};
+    g.M = c0; g.N = 128; g.K = c0;
+    g.A = w.Uf; g.lda = k; g.transA = false;
+    g.B = w.F + c0; g.ldb = k; g.transB = false;
+    g.C = w.Uf + c0; g.ldc = k;
+    // Ufull is zero there: accumulate, with the contraction split over enough workgroups
+    g.alpha = -1.0f; g.accumulate = true; g.upper_only = false;
+    g.a_upper = true; g.b_upper = false;
+    g.split_k = (int)std::max<int64_t>(1, std::min<int64_t>(16, 256 / J)); g.batch = 1;
+    KQ_TRY(gemm_f32(g, s));
+  }
+  const int64_t cnt = k * k;
+  to_bf16_kernel<<<dim3((unsigned)ceil_div(cnt / 4, 256)), dim3(256), 0, s>>>(w.Uf, w.Ub, cnt);
+  KQ_LAUNCHED("to_bf16_kernel");
+  return KQ_OK;
+}
+
+// part <- per-token partial sums of |U s_t|^2 (U = w.Ub, k x k)
+kq_status quadratic_forms(const uint16_t* S, int64_t lds, int64_t T, int64_t k, const Workspace& w,
+                          hipStream_t s) {
+  QArgs a;
+  a.S = S; a.lds = lds; a.U = w.Ub; a.T = T; a.k = (int)k; a.part = w.part;
+  a.njt = (int)((k + QT - 1) / QT);
+  a.np = 2 * a.njt;
+  a.ntt = (int)((T + QT - 1) / QT);
+  const int64_t tiles = (int64_t)a.ntt * a.njt;
+  a.per_xcd = (int)ceil_div(tiles, 8);
+  const int64_t grid = 8 * (int64_t)a.per_xcd;
+  if (grid > 0x7fffffff) return fail(KQ_ESHAPE, "kq_flipflop: too many tiles");
+  qform_kernel<<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
+  KQ_LAUNCHED("qform_kernel");
+  return KQ_OK;
+}
+
+// One half step: F_out = sum_t (|U s2_t|^2 / (T k2)) s1_t s1_t^T, U from M (k2 x k2).
+kq_status half_step(const float* M, const uint16_t* S2, int64_t ld2, int64_t k2, const uint16_t* S1,
+                    int64_t ld1, int64_t k1, int64_t T, float* out, const Workspace& w,
+                    hipStream_t s) {
+  KQ_TRY(inverse_factor(M, k2, w, s));
+  KQ_TRY(quadratic_forms(S2, ld2, T, k2, w, s));
+  const int np = 2 * (int)((k2 + QT - 1) / QT);
+  const float c = (float)(1.0 / ((double)T * (double)k2));
+  ff_scale_kernel<<<dim3((unsigned)T), dim3(256), 0, s>>>(S1, ld1, (int)k1, w.part, np, c, w.Ss, w.ldS);
+  KQ_LAUNCHED("ff_scale_kernel");
+  return kq_accumulate_hessian(w.Ss, T, k1, w.ldS, out, k1, 0, s);
+}
+
+}  // namespace
+}  // namespace kq
+
+extern "C" kq_status kq_flipflop_workspace(int64_t T, int64_t n, int64_t m, size_t* bytes) {
+  using namespace kq;
+  if (!bytes) return fail(KQ_EINVAL, "kq_flipflop_workspace: bytes is NULL");
+  if (T < 1 || n < 128 || m < 128 || n % 128 != 0 || m % 128 != 0 || T > (1ll << 31) ||
+      n > (1 << 16) || m > (1 << 16))
+    return fail(KQ_ESHAPE, "kq_flipflop_workspace: T >= 1, n and m multiples of 128");
+  *bytes = (size_t)layout(T, n, m, nullptr, nullptr);
+  return KQ_OK;
+}
+
+extern "C" kq_status kq_flipflop(const uint16_t* X, int64_t ldx, const uint16_t* G, int64_t ldg,
+                                 int64_t T, int64_t n, int64_t m, int iters, float* A, float* B,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  using namespace kq;
+  if (!X || !G || !A || !B || !ws) return fail(KQ_EINVAL, "kq_flipflop: NULL argument");
+  size_t need = 0;
+  KQ_TRY(kq_flipflop_workspace(T, n, m, &need));
+  if (ws_bytes < need) return fail(KQ_EWORKSPACE, "kq_flipflop: workspace of %zu bytes needed", need);
+  if (iters < 1 || iters > 1000) return fail(KQ_ESHAPE, "kq_flipflop: iters must be 1 .. 1000");
+  if (ldx < n || ldg < m || ldx % 8 != 0 || ldg % 8 != 0 || ((uintptr_t)X & 15) || ((uintptr_t)G & 15))
+    return fail(KQ_ESHAPE, "kq_flipflop: leading dims >= the widths, multiples of 8; 16-byte aligned streams");
+  Workspace w;
+  layout(T, n, m, (char*)ws, &w);
+  hipStream_t s = as_stream(stream);
+  KQ_HIP(hipMemsetAsync(w.flag, 0, sizeof(int), s));
+  identity_kernel<<<dim3((unsigned)ceil_div(m * m, 256)), dim3(256), 0, s>>>(B, m);
+  KQ_LAUNCHED("identity_kernel");
+  for (int it = 0; it < iters; ++it) {
+    KQ_TRY(half_step(B, G, ldg, m, X, ldx, n, T, A, w, s));
+    KQ_TRY(half_step(A, X, ldx, n, G, ldg, m, T, B, w, s));
+  }
+  int flag = 0;
+  KQ_HIP(hipMemcpyAsync(&flag, w.flag, sizeof(int), hipMemcpyDeviceToHost, s));
+  KQ_HIP(hipStreamSynchronize(s));
+  if (flag) return fail(KQ_ENOTSPD, "kq_flipflop: a factor has no Cholesky factor");
+  return KQ_OK;
+}

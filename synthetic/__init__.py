@@ -21,6 +21,10 @@ parallel and reproducibly):
                    columns multiplied by a constant, rounded to bf16 unless
                    the config keeps fp32 weights
   signs            int8 +-1, uniform
+  token magnitudes (streams for the FlipFlop factors) a_t = exp(0.5 z_t) on X's
+                   rows and b_t = exp(0.5 (0.8 z_t + 0.6 u_t)) on G's rows, z, u
+                   N(0,1): correlated per-token sizes, so E[(g^T B^-1 g) x x^T]
+                   differs from the marginal factor
 """
 from __future__ import annotations
 
@@ -33,6 +37,7 @@ import numpy as np
 # tensor ids inside the seed sequence
 _TID_W, _TID_X, _TID_G, _TID_SIN, _TID_SOUT, _TID_SCALE_X, _TID_SCALE_G, _TID_OUTL = range(8)
 _TID_LAYER_SIGMA = 8
+_TID_TOKMAG = 9
 
 CHUNK_TOKENS = 8192
 
@@ -201,6 +206,27 @@ def stream(cfg: LayerConfig, which: str, tokens: int | None = None, threads: int
         with ThreadPoolExecutor(nthr) as ex:
             list(ex.map(lambda j: _stream_chunk(cfg, which, scales, j[0], j[1], j[2], out), jobs))
     return out
+
+
+def token_magnitudes(cfg: LayerConfig, tokens: int) -> tuple[np.ndarray, np.ndarray]:
+    """Per-token row factors (a, b) of the X and G streams for the FlipFlop workload."""
+    rng = _rng(cfg, _TID_TOKMAG, cfg.x_stream, 0)
+    z = rng.standard_normal(tokens)
+    u = rng.standard_normal(tokens)
+    return np.exp(0.5 * z).astype(np.float32), np.exp(0.5 * (0.8 * z + 0.6 * u)).astype(np.float32)
+
+
+def flipflop_streams(cfg: LayerConfig, tokens: int | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """The X and G streams with their rows scaled by token_magnitudes, re-rounded to bf16."""
+    T = cfg.tokens if tokens is None else tokens
+    X = stream(cfg, "x", T)
+    G = stream(cfg, "g", T)
+    a, b = token_magnitudes(cfg, T)
+    for t0 in range(0, T, CHUNK_TOKENS):
+        t1 = min(T, t0 + CHUNK_TOKENS)
+        X[t0:t1] = f32_to_bf16_bits(bf16_bits_to_f32(X[t0:t1]) * a[t0:t1, None])
+        G[t0:t1] = f32_to_bf16_bits(bf16_bits_to_f32(G[t0:t1]) * b[t0:t1, None])
+    return X, G
 
 
 def weights(cfg: LayerConfig) -> np.ndarray:

@@ -136,3 +136,18 @@ def test_deploy_rejects_bad_arguments_on_host():
     assert b"layer 1" in lib.kq_last_error()
     assert lib.kq_deploy_linear(buf, buf, buf, 4, 100, 64, 256, None, None, None, None, 0, 0, buf,
                                 buf, None) == kq.KQ_ESHAPE
+
+
+def test_flipflop_rejects_bad_arguments_on_host():
+    lib = _raw()
+    buf = ctypes.c_void_p(0x1000)
+    b = ctypes.c_size_t(0)
+    assert lib.kq_flipflop_workspace(1000, 256, 384, ctypes.byref(b)) == kq.KQ_OK and b.value > 0
+    assert lib.kq_flipflop_workspace(1000, 200, 384, ctypes.byref(b)) == kq.KQ_ESHAPE
+    assert lib.kq_flipflop_workspace(0, 256, 384, ctypes.byref(b)) == kq.KQ_ESHAPE
+    need = kq.kq_flipflop_workspace(1000, 256, 384)
+    args = (buf, 256, buf, 384, 1000, 256, 384)
+    assert lib.kq_flipflop(*args, 0, buf, buf, buf, need, None) == kq.KQ_ESHAPE
+    assert lib.kq_flipflop(*args, 1, buf, buf, buf, need - 1, None) == kq.KQ_EWORKSPACE
+    assert lib.kq_flipflop(buf, 256, buf, 384, 1000, 256, 384, 1, None, buf, buf, need, None) == kq.KQ_EINVAL
+    assert lib.kq_flipflop(buf, 260, buf, 384, 1000, 256, 384, 1, buf, buf, buf, need, None) == kq.KQ_ESHAPE
