@@ -619,10 +619,11 @@ def _dead_to_unit(M: np.ndarray) -> np.ndarray:
 
 def quadratic_forms(S: np.ndarray, M: np.ndarray) -> np.ndarray:
     """q_t = s_t^T M^-1 s_t for every row s_t of S (zero-diagonal channels as in
-    _dead_to_unit).  Written out: the explicit inverse, then a row-wise dot."""
+    _dead_to_unit).  Written out: the explicit inverse, the product S M^-1, then a
+    row-wise dot with S."""
     S = np.asarray(S, dtype=np.float64)
     Minv = np.linalg.inv(_dead_to_unit(M))
-    return np.einsum("ti,ij,tj->t", S, Minv, S)
+    return np.einsum("ti,ti->t", S @ Minv, S)
 
 
 def flipflop_input_factor(X: np.ndarray, G: np.ndarray, B: np.ndarray) -> np.ndarray:
