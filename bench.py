@@ -53,6 +53,9 @@ def parse():
                          "224 packed linears of Llama-2-7B at this width")
     ap.add_argument("--deploy-single", action="store_true",
                     help="with --deploy-bits: one call per layer instead of grouped calls")
+    ap.add_argument("--flipflop", type=int, default=None, metavar="ITERS",
+                    help="time the FlipFlop Hessian factors instead: ITERS alternating "
+                         "iterations from the identity on the workload's streams")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB fp32 tensor three times (scale for the HBM byte "
                          "counters FETCH_SIZE / WRITE_SIZE) and exit")
@@ -346,6 +349,88 @@ def deploy_main(a) -> None:
     print(json.dumps(line), flush=True)
 
 
+def flipflop_cpu_baseline(cfg, iters: int, budget_s: float) -> dict:
+    """The oracle's FlipFlop iteration on token samples of the same streams; its cost is
+    a + b T (inverses, then products linear in the tokens), fitted on two samples and
+    evaluated at the workload's T."""
+    import oracle as o
+    Xb, Gb = syn.flipflop_streams(cfg, tokens=4096)
+    times = []
+    for Ts in (2048, 4096):
+        X = syn.bf16_bits_to_f32(Xb[:Ts]).astype(np.float64)
+        G = syn.bf16_bits_to_f32(Gb[:Ts]).astype(np.float64)
+        t0 = time.perf_counter()
+        o.flipflop(X, G, 1)
+        times.append(time.perf_counter() - t0)
+    b = (times[1] - times[0]) / 2048.0
+    a0 = max(times[0] - b * 2048, 0.0)
+    per_iter = a0 + b * cfg.tokens
+    return {"value": round(1.0 / per_iter, 5), "unit": "iterations/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": (f"one iteration on 2048 and 4096 tokens ({times[0]:.1f} s, {times[1]:.1f} s), "
+                       f"fitted a + b T and evaluated at T = {cfg.tokens}: {per_iter:.0f} s per iteration")}
+
+
+def flipflop_main(a) -> None:
+    """FlipFlop Hessian factors (kq_flipflop) on the workload's streams with correlated
+    per-token magnitudes: one step = a.flipflop iterations from the identity.  The
+    roofline is the per-token quadratic-form kernel (bf16 MFMA), its HIP-event time per
+    launch from the call's phase timer."""
+    import torch
+    import post_quantization_syrk_amd as kq
+    cfg = WORKLOADS[a.workload]
+    iters = a.flipflop
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kq.load_library()
+    t0 = time.time()
+    Xb, Gb = syn.flipflop_streams(cfg)
+    X = torch.from_numpy(Xb.view(np.int16)).to(dev)
+    G = torch.from_numpy(Gb.view(np.int16)).to(dev)
+    del Xb, Gb
+    gen_s = time.time() - t0
+    T, n, m = cfg.tokens, cfg.inp, cfg.out
+    A = torch.empty((n, n), device=dev)
+    B = torch.empty((m, m), device=dev)
+    ws = torch.empty(kq.kq_flipflop_workspace(T, n, m), dtype=torch.uint8, device=dev)
+    for _ in range(a.warmup):
+        kq.kq_flipflop(X, G, iters, A, B, ws)
+    torch.cuda.synchronize()
+    phases = {"factor": 0.0, "quadratic_forms": 0.0, "scale": 0.0, "syrk": 0.0}
+    t_start = time.perf_counter()
+    for _ in range(a.steps):
+        ph = kq.kq_flipflop(X, G, iters, A, B, ws, phases=True)
+        for k_, v in ph.items():
+            phases[k_] += v
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / a.steps
+    launches = 2 * iters * a.steps           # quadratic-form launches (one per half step)
+    qf_ms = phases["quadratic_forms"] / launches
+    # algorithmic flops of one launch: T k (k + 1) (only U's upper triangle), averaged over
+    # the two half steps (k = m, then n)
+    flops = 0.5 * (T * m * (m + 1) + T * n * (n + 1))
+    achieved = flops / (qf_ms / 1e3) / 1e12
+    cpu = None if a.no_cpu_baseline else flipflop_cpu_baseline(cfg, iters, a.cpu_seconds)
+    line = {
+        "metric": "FlipFlop Hessian iterations per second (both factors, from the identity)",
+        "value": round(iters / (ms_per_step / 1e3), 3), "unit": "iterations/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 products / f32 accumulate",
+        "data": "synthetic (seeded log-normal-channel streams with correlated per-token magnitudes)",
+        "config": {"workload": cfg.name + "-flipflop", "in": n, "out": m, "tokens": T,
+                   "iterations_per_step": iters},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "qform_kernel", "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": cpu,
+        "phases_ms_per_iteration": {k_: round(v / (iters * a.steps), 3) for k_, v in phases.items()},
+        "input_generation_s": round(gen_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -357,6 +442,9 @@ def main():
         return
     if a.deploy_bits is not None:
         deploy_main(a)
+        return
+    if a.flipflop is not None:
+        flipflop_main(a)
         return
     import torch
     import post_quantization_syrk_amd as kq

@@ -317,12 +317,15 @@ kq_status kq_flipflop_workspace(int64_t T, int64_t n, int64_t m, size_t* bytes);
  *   iters    1 .. 1000
  *   A, B     device fp32, n x n and m x m, contiguous: A_iters and B_iters (full symmetric)
  *   ws       device workspace of kq_flipflop_workspace(T, n, m) bytes
+ *   phase_ms host, 4 doubles, or NULL: HIP-event durations on `stream`, summed over all
+ *            half steps, of {factor and inverse factor, per-token quadratic forms,
+ *            stream scaling, SYRK}
  * Synchronizes `stream` before returning; KQ_ENOTSPD when a factor has a non-positive
  * pivot (results undefined).  KQ_ESHAPE / KQ_EINVAL / KQ_EWORKSPACE before any launch.
  */
 kq_status kq_flipflop(const uint16_t* X, int64_t ldx, const uint16_t* G, int64_t ldg, int64_t T,
                       int64_t n, int64_t m, int iters, float* A, float* B, void* ws,
-                      size_t ws_bytes, void* stream);
+                      size_t ws_bytes, double* phase_ms, void* stream);
 
 #ifdef __cplusplus
 }

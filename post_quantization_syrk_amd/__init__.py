@@ -70,7 +70,8 @@ _SIGS = {
                           _vp, _vp, _vp], _int),
     "kq_deploy_linear_group": ([ctypes.POINTER(DeployLayer), _int, _i64, _vp, _vp], _int),
     "kq_flipflop_workspace": ([_i64, _i64, _i64, ctypes.POINTER(_sz)], _int),
-    "kq_flipflop": ([_vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _sz, _vp], _int),
+    "kq_flipflop": ([_vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _sz,
+                     ctypes.POINTER(ctypes.c_double), _vp], _int),
 }
 
 _lib = None
@@ -279,9 +280,11 @@ def kq_flipflop_workspace(T: int, n: int, m: int) -> int:
     return b.value
 
 
-def kq_flipflop(X, G, iters: int, A, B, ws=None, stream=None) -> None:
+def kq_flipflop(X, G, iters: int, A, B, ws=None, stream=None, phases: bool = False):
     """FlipFlop factors A (n x n) and B (m x m) from bf16 streams X (T x n) and G (T x m),
-    given as int16/uint16/bfloat16 tensors of bit patterns, after `iters` iterations."""
+    given as int16/uint16/bfloat16 tensors of bit patterns, after `iters` iterations.
+    With phases=True, returns the summed HIP-event milliseconds of {factor, quadratic
+    forms, scaling, syrk}."""
     torch = _torch()
     lib = load_library()
     T, n = X.shape
@@ -291,7 +294,11 @@ def kq_flipflop(X, G, iters: int, A, B, ws=None, stream=None) -> None:
     if ws is None:
         ws = torch.empty(kq_flipflop_workspace(T, n, m), dtype=torch.uint8, device=X.device)
     bf = (torch.int16, torch.uint16, torch.bfloat16)
+    ph = (ctypes.c_double * 4)() if phases else None
     st = lib.kq_flipflop(_dev_ptr(X, "X", bf), _ld(X, "X"), _dev_ptr(G, "G", bf), _ld(G, "G"), T, n, m,
                          iters, _dev_ptr(A, "A", (torch.float32,)), _dev_ptr(B, "B", (torch.float32,)),
-                         _dev_ptr(ws, "ws", (torch.uint8,)), ws.numel(), _stream(stream))
+                         _dev_ptr(ws, "ws", (torch.uint8,)), ws.numel(), ph, _stream(stream))
     _check(st, "kq_flipflop")
+    if phases:
+        return dict(zip(("factor", "quadratic_forms", "scale", "syrk"), list(ph)))
+    return None

@@ -28,6 +28,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <vector>
 
 namespace kq {
 
@@ -350,17 +351,50 @@ kq_status quadratic_forms(const uint16_t* S, int64_t lds, int64_t T, int64_t k, 
   return KQ_OK;
 }
 
+// HIP events around the phases of every half step (factor + inverse factor, quadratic
+// forms, scaling, SYRK), on the call's stream; read once the stream has drained.
+struct PhaseTimer {
+  bool on = false;
+  std::vector<hipEvent_t> ev;   // 5 per half step
+  kq_status mark(hipStream_t s) {
+    if (!on) return KQ_OK;
+    hipEvent_t e;
+    KQ_HIP(hipEventCreate(&e));
+    ev.push_back(e);
+    KQ_HIP(hipEventRecord(e, s));
+    return KQ_OK;
+  }
+  kq_status read(double* ms) {
+    for (int p = 0; p < 4; ++p) ms[p] = 0.0;
+    for (size_t h = 0; h + 4 < ev.size(); h += 5)
+      for (int p = 0; p < 4; ++p) {
+        float t = 0.f;
+        KQ_HIP(hipEventElapsedTime(&t, ev[h + p], ev[h + p + 1]));
+        ms[p] += t;
+      }
+    return KQ_OK;
+  }
+  ~PhaseTimer() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  }
+};
+
 // One half step: F_out = sum_t (|U s2_t|^2 / (T k2)) s1_t s1_t^T, U from M (k2 x k2).
 kq_status half_step(const float* M, const uint16_t* S2, int64_t ld2, int64_t k2, const uint16_t* S1,
                     int64_t ld1, int64_t k1, int64_t T, float* out, const Workspace& w,
-                    hipStream_t s) {
+                    PhaseTimer& pt, hipStream_t s) {
+  KQ_TRY(pt.mark(s));
   KQ_TRY(inverse_factor(M, k2, w, s));
+  KQ_TRY(pt.mark(s));
   KQ_TRY(quadratic_forms(S2, ld2, T, k2, w, s));
+  KQ_TRY(pt.mark(s));
   const int np = 2 * (int)((k2 + QT - 1) / QT);
   const float c = (float)(1.0 / ((double)T * (double)k2));
   ff_scale_kernel<<<dim3((unsigned)T), dim3(256), 0, s>>>(S1, ld1, (int)k1, w.part, np, c, w.Ss, w.ldS);
   KQ_LAUNCHED("ff_scale_kernel");
-  return kq_accumulate_hessian(w.Ss, T, k1, w.ldS, out, k1, 0, s);
+  KQ_TRY(pt.mark(s));
+  KQ_TRY(kq_accumulate_hessian(w.Ss, T, k1, w.ldS, out, k1, 0, s));
+  return pt.mark(s);
 }
 
 }  // namespace
@@ -378,7 +412,7 @@ extern "C" kq_status kq_flipflop_workspace(int64_t T, int64_t n, int64_t m, size
 
 extern "C" kq_status kq_flipflop(const uint16_t* X, int64_t ldx, const uint16_t* G, int64_t ldg,
                                  int64_t T, int64_t n, int64_t m, int iters, float* A, float* B,
-                                 void* ws, size_t ws_bytes, void* stream) {
+                                 void* ws, size_t ws_bytes, double* phase_ms, void* stream) {
   using namespace kq;
   if (!X || !G || !A || !B || !ws) return fail(KQ_EINVAL, "kq_flipflop: NULL argument");
   size_t need = 0;
@@ -393,13 +427,16 @@ extern "C" kq_status kq_flipflop(const uint16_t* X, int64_t ldx, const uint16_t*
   KQ_HIP(hipMemsetAsync(w.flag, 0, sizeof(int), s));
   identity_kernel<<<dim3((unsigned)ceil_div(m * m, 256)), dim3(256), 0, s>>>(B, m);
   KQ_LAUNCHED("identity_kernel");
+  PhaseTimer pt;
+  pt.on = phase_ms != nullptr;
   for (int it = 0; it < iters; ++it) {
-    KQ_TRY(half_step(B, G, ldg, m, X, ldx, n, T, A, w, s));
-    KQ_TRY(half_step(A, X, ldx, n, G, ldg, m, T, B, w, s));
+    KQ_TRY(half_step(B, G, ldg, m, X, ldx, n, T, A, w, pt, s));
+    KQ_TRY(half_step(A, X, ldx, n, G, ldg, m, T, B, w, pt, s));
   }
   int flag = 0;
   KQ_HIP(hipMemcpyAsync(&flag, w.flag, sizeof(int), hipMemcpyDeviceToHost, s));
   KQ_HIP(hipStreamSynchronize(s));
+  if (pt.on) KQ_TRY(pt.read(phase_ms));
   if (flag) return fail(KQ_ENOTSPD, "kq_flipflop: a factor has no Cholesky factor");
   return KQ_OK;
 }

@@ -147,7 +147,7 @@ def test_flipflop_rejects_bad_arguments_on_host():
     assert lib.kq_flipflop_workspace(0, 256, 384, ctypes.byref(b)) == kq.KQ_ESHAPE
     need = kq.kq_flipflop_workspace(1000, 256, 384)
     args = (buf, 256, buf, 384, 1000, 256, 384)
-    assert lib.kq_flipflop(*args, 0, buf, buf, buf, need, None) == kq.KQ_ESHAPE
-    assert lib.kq_flipflop(*args, 1, buf, buf, buf, need - 1, None) == kq.KQ_EWORKSPACE
-    assert lib.kq_flipflop(buf, 256, buf, 384, 1000, 256, 384, 1, None, buf, buf, need, None) == kq.KQ_EINVAL
-    assert lib.kq_flipflop(buf, 260, buf, 384, 1000, 256, 384, 1, buf, buf, buf, need, None) == kq.KQ_ESHAPE
+    assert lib.kq_flipflop(*args, 0, buf, buf, buf, need, None, None) == kq.KQ_ESHAPE
+    assert lib.kq_flipflop(*args, 1, buf, buf, buf, need - 1, None, None) == kq.KQ_EWORKSPACE
+    assert lib.kq_flipflop(buf, 256, buf, 384, 1000, 256, 384, 1, None, buf, buf, need, None, None) == kq.KQ_EINVAL
+    assert lib.kq_flipflop(buf, 260, buf, 384, 1000, 256, 384, 1, buf, buf, buf, need, None, None) == kq.KQ_ESHAPE
