@@ -27,7 +27,7 @@ __all__ = [
     "allocate_bits", "brute_force_min_loss", "NotSPDError", "ClippedMinMaxGrid",
     "act_order_perm", "CLIP_NORM", "CLIP_GRID", "CLIP_MAXSHRINK", "dequant", "deploy_linear",
     "quadratic_forms", "flipflop_input_factor", "flipflop_output_factor", "flipflop",
-    "flipflop_objective",
+    "flipflop_objective", "static_grid", "TwoSidedResult", "two_sided_gptq",
 ]
 
 BIIP_FULL, BIIP_NO_RESCALE, BIIP_IN_ONLY, BIIP_OUT_ONLY = 0, 1, 2, 3
@@ -679,6 +679,91 @@ def flipflop_objective(X: np.ndarray, G: np.ndarray, A: np.ndarray, B: np.ndarra
     v = quadratic_forms(X, A)
     w = quadratic_forms(G, B)
     return float(np.mean(v * w) + m * np.linalg.slogdet(A)[1] + n * np.linalg.slogdet(B)[1])
+
+
+# ---------------------------------------------------------------------------
+# Two-sided rounding (GPTQ in the vectorized weight domain)
+# ---------------------------------------------------------------------------
+def static_grid(W: np.ndarray, bits: int, group: int) -> tuple[np.ndarray, np.ndarray]:
+    """Per-(row, group) asymmetric min-max grid taken once from W (the rules of
+    AsymMinMaxGrid: range forced to include 0, s = (xmax - xmin) / (2^b - 1) or 1,
+    z = rint(-xmin / s)).  READING for two-sided rounding: the grid does not follow
+    the error-updated weights, so that every order of the rounding that respects
+    the feedback's dependencies gives the same result."""
+    W = np.asarray(W, dtype=np.float64)
+    m, n = W.shape
+    g = AsymMinMaxGrid(bits, group)
+    ng = (n + group - 1) // group
+    scales, zeros = np.zeros((m, ng)), np.zeros((m, ng))
+    for k in range(ng):
+        g.set_params(W[:, k * group:(k + 1) * group])
+        scales[:, k], zeros[:, k] = g.scale, g.zero
+    return scales, zeros
+
+
+@dataclass
+class TwoSidedResult:
+    codes: np.ndarray
+    scales: np.ndarray
+    zeros: np.ndarray
+    qhat: np.ndarray
+    accepted_ties: int = 0
+    hard_mismatches: int = 0
+
+
+def two_sided_gptq(W: np.ndarray, HX: np.ndarray, HG: np.ndarray, bits: int, group: int,
+                   damp: float = 0.01, replay_codes: np.ndarray | None = None,
+                   tie_window: float = 1e-4) -> TwoSidedResult:
+    """GPTQ on vec(W) under the Kronecker Hessian H = H_X (x) H_G.
+
+    [BaKron] abstract: GPTQ-style rounding applied directly in the vectorized
+    weight domain with a two-sided Kronecker-factored Hessian (the formulation
+    of BoA and YAQA), which BaKron then computes in O(m+n) sequential steps.
+    Written out: with c = i m + r the position of W[r, i] in vec(W) (columns
+    stacked), H_d = (H_X + lam_X I) (x) (H_G + lam_G I) and
+    U = chol_upper(H_d^-1) = U_X (x) U_G, the coordinates are rounded in the
+    order c = 0, 1, ...: q = code(w_c), e = (w_c - qhat_c) / U[c, c],
+    w_c' -= e U[c, c'] for c' > c.  Since U[(i, r), (i', r')] = U_X[i, i']
+    U_G[r, r'] vanishes unless i' >= i and r' >= r, each rounding feeds only the
+    quadrant below and to the right of its coordinate; the update is written as
+    that quadrant's outer product.  READINGS: damping and dead channels as in
+    damp_and_factor on each factor (a dead output channel's row is zeroed like a
+    dead input channel's column); grids from static_grid.  replay_codes: the
+    tie protocol of gptq (another implementation's code is adopted at a value
+    within tie_window of a rounding midpoint).
+    """
+    W = np.array(W, dtype=np.float64, copy=True)
+    m, n = W.shape
+    UX, _, deadX, _ = damp_and_factor(HX, damp)
+    UG, _, deadG, _ = damp_and_factor(HG, damp)
+    W[:, deadX] = 0.0
+    W[deadG, :] = 0.0
+    scales, zeros = static_grid(W, bits, group)
+    maxq = (1 << bits) - 1
+    codes = np.zeros((m, n), dtype=np.int64)
+    qhat = np.zeros((m, n))
+    acc = hard = 0
+    for i in range(n):
+        g = i // group
+        for r in range(m):
+            s, z = scales[r, g], zeros[r, g]
+            u = W[r, i] / s
+            q = int(np.clip(np.rint(u) + z, 0, maxq))
+            if replay_codes is not None and int(replay_codes[r, i]) != q:
+                other = int(replay_codes[r, i])
+                lo = np.clip(np.floor(u) + z, 0, maxq)
+                hi = np.clip(np.floor(u) + 1 + z, 0, maxq)
+                if abs(u - np.floor(u) - 0.5) < tie_window and other in (lo, hi):
+                    q = other
+                    acc += 1
+                else:
+                    hard += 1
+            qh = s * (q - z)
+            e = (W[r, i] - qh) / (UX[i, i] * UG[r, r])
+            W[r + 1:, i] -= e * UG[r, r + 1:] * UX[i, i]
+            W[r:, i + 1:] -= e * np.outer(UG[r, r:], UX[i, i + 1:])
+            codes[r, i], qhat[r, i] = q, qh
+    return TwoSidedResult(codes, scales, zeros, qhat, acc, hard)
 
 
 # ---------------------------------------------------------------------------

@@ -738,3 +738,105 @@ def test_flipflop_dead_channel_counts_as_one():
     assert np.allclose(A[np.ix_(keep, keep)], A3, rtol=1e-12)
     # B is divided by n: the dead channel still counts in the dimension
     assert np.allclose(B * n, B3 * (n - 1), rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Two-sided rounding ([BaKron] abstract: GPTQ in the vectorized weight domain)
+# ---------------------------------------------------------------------------
+class _StaticGrid:
+    """A grid for o.gptq whose parameters are fixed per (row of its input, column)."""
+
+    def __init__(self, scale_of_col, zero_of_col, bits):
+        self.S, self.Z, self.maxq, self.group = scale_of_col, zero_of_col, (1 << bits) - 1, 1
+
+    def starts_group(self, j):
+        self.j = j
+        return True
+
+    def set_params(self, block):
+        self.scale, self.zero = self.S[:, self.j], self.Z[:, self.j]
+
+    def unrounded(self, w):
+        return w / self.scale
+
+    def code(self, u):
+        return np.clip(np.rint(u) + self.zero, 0, self.maxq)
+
+    def dequant(self, q):
+        return self.scale * (q - self.zero)
+
+
+def _two_sided_case(seed, m=12, n=20, corr=True):
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((m, n)) * 0.1
+    A = rng.standard_normal((60, n)) * np.exp(0.5 * rng.standard_normal(n))
+    B = rng.standard_normal((50, m)) * np.exp(0.5 * rng.standard_normal(m))
+    if corr:
+        A[:, 1] += A[:, 0]
+        B[:, 2] -= 0.8 * B[:, 1]
+    return W, A.T @ A, B.T @ B
+
+
+def _per_element(scales, zeros, group, n):
+    g = np.arange(n) // group
+    return scales[:, g], zeros[:, g]
+
+
+def test_two_sided_with_identity_output_factor_is_row_gptq():
+    """H_G = I: no feedback across rows, so every row is one-sided GPTQ with U_X (static grid)."""
+    W, HX, _ = _two_sided_case(51)
+    m, n = W.shape
+    res = o.two_sided_gptq(W, HX, np.eye(m), 3, 4, damp=0.01)
+    UX = o.damp_and_factor(HX, 0.01)[0]
+    S, Z = _per_element(res.scales, res.zeros, 4, n)
+    for r in range(m):
+        g = o.gptq(W[r:r + 1], UX, _StaticGrid(S[r:r + 1], Z[r:r + 1], 3))
+        assert np.array_equal(g.codes[0], res.codes[r])
+        assert np.allclose(g.qhat[0], res.qhat[r], rtol=0, atol=1e-12)
+
+
+def test_two_sided_with_identity_input_factor_is_column_gptq():
+    """H_X = I: every column is GPTQ over the output channels with U_G."""
+    W, _, HG = _two_sided_case(52)
+    m, n = W.shape
+    res = o.two_sided_gptq(W, np.eye(n), HG, 4, 5, damp=0.02)
+    UG = o.damp_and_factor(HG, 0.02)[0]
+    S, Z = _per_element(res.scales, res.zeros, 5, n)
+    for i in range(n):
+        g = o.gptq(W[:, i:i + 1].T, UG, _StaticGrid(S[:, i:i + 1].T, Z[:, i:i + 1].T, 4))
+        assert np.array_equal(g.codes[0], res.codes[:, i])
+
+
+def test_two_sided_with_identity_factors_is_rtn():
+    W, _, _ = _two_sided_case(53)
+    m, n = W.shape
+    res = o.two_sided_gptq(W, np.eye(n), np.eye(m), 2, n)
+    S, Z = _per_element(res.scales, res.zeros, n, n)
+    assert np.array_equal(res.codes, np.clip(np.rint(W / S) + Z, 0, 3))
+
+
+@pytest.mark.parametrize("order", ["antidiagonal", "rows"])
+def test_two_sided_is_gptq_on_vec_w_in_any_dependency_order(order):
+    """Rounding vec(W) through the explicit U = kron(U_X, U_G) in another order that respects
+    the dependencies (anti-diagonals r + i, or row-major) gives the same codes: the feedback
+    of (r, i) reaches exactly the coordinates (r' >= r, i' >= i)."""
+    W, HX, HG = _two_sided_case(54, m=6, n=9)
+    m, n = W.shape
+    res = o.two_sided_gptq(W, HX, HG, 3, 3, damp=0.01)
+    UX = o.damp_and_factor(HX, 0.01)[0]
+    UG = o.damp_and_factor(HG, 0.01)[0]
+    U = np.kron(UX, UG)                      # index c = i m + r
+    w = W.T.reshape(-1).copy()
+    S, Z = _per_element(res.scales, res.zeros, 3, n)
+    coords = [(r, i) for i in range(n) for r in range(m)]
+    key = (lambda c: (c[0] + c[1], c[0])) if order == "antidiagonal" else (lambda c: (c[0], c[1]))
+    done = np.zeros(m * n, dtype=bool)
+    codes = np.zeros((m, n), dtype=np.int64)
+    for r, i in sorted(coords, key=key):
+        c = i * m + r
+        q = np.clip(np.rint(w[c] / S[r, i]) + Z[r, i], 0, 7)
+        e = (w[c] - S[r, i] * (q - Z[r, i])) / U[c, c]
+        done[c] = True
+        w[~done] -= e * U[c, ~done]
+        codes[r, i] = q
+    assert np.array_equal(codes, res.codes)
