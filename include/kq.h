@@ -291,6 +291,40 @@ kq_status kq_deploy_linear_group(const kq_deploy_layer* layers, int n_layers, in
                                  const float* x, void* stream);
 
 /*
+ * kq_quantize_two_sided_workspace -- device workspace bytes of kq_quantize_two_sided.
+ */
+kq_status kq_quantize_two_sided_workspace(const kq_quant_params* p, int64_t out, int64_t in,
+                                          size_t* bytes);
+
+/*
+ * kq_quantize_two_sided -- two-sided rounding: GPTQ on vec(W) under the Kronecker Hessian
+ * H_d = (H_X + lam_X I) (x) (H_G + lam_G I), lam = damp * mean(diag) per factor.
+ *
+ * Follows: BaKron abstract (two-sided adaptive rounding with a Kronecker-factored Hessian,
+ * O(m + n) sequential steps, O(mn(m + n)) work).  With U = U_X (x) U_G (U_* the upper
+ * Cholesky factors of the damped inverses) each coordinate W[r, i] is rounded to its grid,
+ * e = (w - qhat) / (U_X[i,i] U_G[r,r]), and every W[r', i'] with r' >= r, i' >= i receives
+ * -e U_G[r, r'] U_X[i, i'] (the order within that dependency does not change the result).
+ * Grids: per (row, group) asymmetric min-max taken from W before rounding (static).  Dead
+ * channels (zero diagonal) of either factor zero their column / row of W.
+ *
+ *   p        bits 2..4, asym 1, act_order 0, w_clip 0, group a multiple of 32 dividing in
+ *   W        device fp32, out x in (W~, processed as for kq_quantize_layer), contiguous
+ *   HX, HG   device fp32, in x in and out x out symmetric (H~_X, H~_G), contiguous
+ *   out, in  multiples of 128 (<= 32768)
+ *   packed   device uint32, out x (in * bits / 32): the codes as one bitstream per row
+ *   scales   device fp32, out x (in / group);  zeros  device uint8, out x (in / group)
+ *   ws       device workspace of kq_quantize_two_sided_workspace bytes
+ *   codes_opt device uint8 out x in (the codes unpacked), or NULL
+ * Synchronizes `stream` before returning; KQ_ENOTSPD when a damped factor is not positive
+ * definite.  KQ_EINVAL / KQ_ESHAPE / KQ_ENOTIMPL / KQ_EWORKSPACE before any launch.
+ */
+kq_status kq_quantize_two_sided(const kq_quant_params* p, const float* W, const float* HX,
+                                const float* HG, int64_t out, int64_t in, uint32_t* packed,
+                                float* scales, uint8_t* zeros, void* ws, size_t ws_bytes,
+                                uint8_t* codes_opt, void* stream);
+
+/*
  * kq_flipflop_workspace -- device workspace bytes of kq_flipflop for T tokens, n input and m
  * output channels.
  */

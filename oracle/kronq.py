@@ -27,7 +27,7 @@ __all__ = [
     "allocate_bits", "brute_force_min_loss", "NotSPDError", "ClippedMinMaxGrid",
     "act_order_perm", "CLIP_NORM", "CLIP_GRID", "CLIP_MAXSHRINK", "dequant", "deploy_linear",
     "quadratic_forms", "flipflop_input_factor", "flipflop_output_factor", "flipflop",
-    "flipflop_objective", "static_grid", "TwoSidedResult", "two_sided_gptq",
+    "flipflop_objective", "static_grid", "TwoSidedResult", "two_sided_gptq", "two_sided_rounding",
 ]
 
 BIIP_FULL, BIIP_NO_RESCALE, BIIP_IN_ONLY, BIIP_OUT_ONLY = 0, 1, 2, 3
@@ -733,12 +733,23 @@ def two_sided_gptq(W: np.ndarray, HX: np.ndarray, HG: np.ndarray, bits: int, gro
     within tie_window of a rounding midpoint).
     """
     W = np.array(W, dtype=np.float64, copy=True)
-    m, n = W.shape
     UX, _, deadX, _ = damp_and_factor(HX, damp)
     UG, _, deadG, _ = damp_and_factor(HG, damp)
     W[:, deadX] = 0.0
     W[deadG, :] = 0.0
     scales, zeros = static_grid(W, bits, group)
+    return two_sided_rounding(W, UX, UG, scales, zeros, bits, group, replay_codes, tie_window)
+
+
+def two_sided_rounding(W: np.ndarray, UX: np.ndarray, UG: np.ndarray, scales: np.ndarray,
+                       zeros: np.ndarray, bits: int, group: int,
+                       replay_codes: np.ndarray | None = None,
+                       tie_window: float = 1e-4) -> TwoSidedResult:
+    """The rounding loop of two_sided_gptq for given factors and grids.  Any leading block
+    W[:a, :b] with the leading blocks of U_X and U_G is a problem of its own: its
+    coordinates depend on none outside it."""
+    W = np.array(W, dtype=np.float64, copy=True)
+    m, n = W.shape
     maxq = (1 << bits) - 1
     codes = np.zeros((m, n), dtype=np.int64)
     qhat = np.zeros((m, n))

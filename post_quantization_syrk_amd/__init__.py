@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "KQ_OK", 1: "KQ_EINVAL", 2: "KQ_ESHAPE", 3: "KQ_ENOTSPD", 4: 
 EXPORTED = ("kq_version", "kq_last_error", "kq_accumulate_hessian", "kq_sensitivity",
             "kq_biip_rotate", "kq_quantize_layer_workspace", "kq_quantize_layer",
             "kq_allocate_bits", "kq_deploy_linear", "kq_deploy_linear_group",
-            "kq_flipflop_workspace", "kq_flipflop")
+            "kq_flipflop_workspace", "kq_flipflop", "kq_quantize_two_sided_workspace",
+            "kq_quantize_two_sided")
 
 
 class KQError(RuntimeError):
@@ -70,6 +71,9 @@ _SIGS = {
                           _vp, _vp, _vp], _int),
     "kq_deploy_linear_group": ([ctypes.POINTER(DeployLayer), _int, _i64, _vp, _vp], _int),
     "kq_flipflop_workspace": ([_i64, _i64, _i64, ctypes.POINTER(_sz)], _int),
+    "kq_quantize_two_sided_workspace": ([ctypes.POINTER(QuantParams), _i64, _i64, ctypes.POINTER(_sz)], _int),
+    "kq_quantize_two_sided": ([ctypes.POINTER(QuantParams), _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp,
+                               _sz, _vp, _vp], _int),
     "kq_flipflop": ([_vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _sz,
                      ctypes.POINTER(ctypes.c_double), _vp], _int),
 }
@@ -302,3 +306,31 @@ def kq_flipflop(X, G, iters: int, A, B, ws=None, stream=None, phases: bool = Fal
     if phases:
         return dict(zip(("factor", "quadratic_forms", "scale", "syrk"), list(ph)))
     return None
+
+
+def kq_quantize_two_sided_workspace(p: QuantParams, out_n: int, in_n: int) -> int:
+    lib = load_library()
+    b = ctypes.c_size_t(0)
+    _check(lib.kq_quantize_two_sided_workspace(ctypes.byref(p), out_n, in_n, ctypes.byref(b)),
+           "kq_quantize_two_sided_workspace")
+    return b.value
+
+
+def kq_quantize_two_sided(p: QuantParams, W, HX, HG, packed, scales, zeros, ws=None, codes=None,
+                          stream=None) -> None:
+    """Two-sided rounding of W (out x in) under H_X (x) H_G into packed codes, scales and
+    zero points (the layout of kq_quantize_layer)."""
+    torch = _torch()
+    lib = load_library()
+    out_n, in_n = W.shape
+    if ws is None:
+        ws = torch.empty(kq_quantize_two_sided_workspace(p, out_n, in_n), dtype=torch.uint8,
+                         device=W.device)
+    f32 = (torch.float32,)
+    st = lib.kq_quantize_two_sided(
+        ctypes.byref(p), _dev_ptr(W, "W", f32), _dev_ptr(HX, "HX", f32), _dev_ptr(HG, "HG", f32),
+        out_n, in_n, _dev_ptr(packed, "packed", (torch.int32, torch.uint32)),
+        _dev_ptr(scales, "scales", f32), _dev_ptr(zeros, "zeros", (torch.uint8,)),
+        _dev_ptr(ws, "ws", (torch.uint8,)), ws.numel(), _dev_ptr(codes, "codes", (torch.uint8,), True),
+        _stream(stream))
+    _check(st, "kq_quantize_two_sided")

@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkq.so")
 
 SOURCES = ["common.hip", "syrk.hip", "reduce.hip", "alloc.hip", "fwht.hip", "gemm_f32.hip", "chol.hip",
-           "gptq.hip", "deploy.hip", "flipflop.hip"]
+           "gptq.hip", "deploy.hip", "flipflop.hip", "twosided.hip"]
 # host-only arithmetic that must match IEEE operation by operation
 NO_CONTRACT = {"alloc.hip"}
 

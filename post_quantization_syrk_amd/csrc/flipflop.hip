@@ -311,23 +311,7 @@ int64_t layout(int64_t T, int64_t n, int64_t m, char* base, Workspace* w) {
 
 // Ub = bf16(U), U = R^-1 for M = R R^T (no damping; zero diagonals count as 1).
 kq_status inverse_factor(const float* M, int64_t k, const Workspace& w, hipStream_t s) {
-  KQ_TRY(damp_and_factor(M, w.F, w.Tsc, w.dead, w.lam, w.flag, k, 0.0f, 128, s));
-  KQ_TRY(fill_f32(w.Uf, k * k, 0.0f, s));
-  copy_diag_blocks<<<dim3((unsigned)(k / 128)), dim3(256), 0, s>>>(w.F, w.Uf, k);
-  KQ_LAUNCHED("copy_diag_blocks");
-  for (int64_t J = 1; J < k / 128; ++J) {
-    const int64_t c0 = 128 * J;
-    GemmArgs g = {};
-    g.M = c0; g.N = 128; g.K = c0;
-    g.A = w.Uf; g.lda = k; g.transA = false;
-    g.B = w.F + c0; g.ldb = k; g.transB = false;
-    g.C = w.Uf + c0; g.ldc = k;
-    // Ufull is zero there: accumulate, with the contraction split over enough workgroups
-    g.alpha = -1.0f; g.accumulate = true; g.upper_only = false;
-    g.a_upper = true; g.b_upper = false;
-    g.split_k = (int)std::max<int64_t>(1, std::min<int64_t>(16, 256 / J)); g.batch = 1;
-    KQ_TRY(gemm_f32(g, s));
-  }
+  KQ_TRY(explicit_inverse_factor(M, k, 0.0f, w.F, w.Tsc, w.dead, w.lam, w.flag, w.Uf, s));
   const int64_t cnt = k * k;
   to_bf16_kernel<<<dim3((unsigned)ceil_div(cnt / 4, 256)), dim3(256), 0, s>>>(w.Uf, w.Ub, cnt);
   KQ_LAUNCHED("to_bf16_kernel");
@@ -398,6 +382,34 @@ kq_status half_step(const float* M, const uint16_t* S2, int64_t ld2, int64_t k2,
 }
 
 }  // namespace
+
+// U = R^-1 (explicit, upper triangular, k x k, ld k) for M + lambda I = R R^T with
+// lambda = damp * mean(diag M) (a zero diagonal counts as 1; its channel is flagged in
+// dead): the factorization leaves the diagonal blocks U_JJ and the panels
+// P[<J, J] = R[<J, J] U_JJ, and U[<J, J] = -U[<J, <J] P[<J, J] column block by column
+// block (fp32 MFMA products, the contraction split over enough workgroups).
+kq_status explicit_inverse_factor(const float* M, int64_t k, float damp, float* F, float* Tsc,
+                                  uint8_t* dead, double* lam, int* flag, float* U, hipStream_t s) {
+  KQ_TRY(damp_and_factor(M, F, Tsc, dead, lam, flag, k, damp, 128, s));
+  KQ_TRY(fill_f32(U, k * k, 0.0f, s));
+  copy_diag_blocks<<<dim3((unsigned)(k / 128)), dim3(256), 0, s>>>(F, U, k);
+  KQ_LAUNCHED("copy_diag_blocks");
+  for (int64_t J = 1; J < k / 128; ++J) {
+    const int64_t c0 = 128 * J;
+    GemmArgs g = {};
+    g.M = c0; g.N = 128; g.K = c0;
+    g.A = U; g.lda = k; g.transA = false;
+    g.B = F + c0; g.ldb = k; g.transB = false;
+    g.C = U + c0; g.ldc = k;
+    // U is zero there: accumulate, with the contraction split over enough workgroups
+    g.alpha = -1.0f; g.accumulate = true; g.upper_only = false;
+    g.a_upper = true; g.b_upper = false;
+    g.split_k = (int)std::max<int64_t>(1, std::min<int64_t>(16, 256 / J)); g.batch = 1;
+    KQ_TRY(gemm_f32(g, s));
+  }
+  return KQ_OK;
+}
+
 }  // namespace kq
 
 extern "C" kq_status kq_flipflop_workspace(int64_t T, int64_t n, int64_t m, size_t* bytes) {

@@ -53,6 +53,13 @@ struct GemmArgs {
 };
 kq_status gemm_f32(const GemmArgs& g, hipStream_t s);
 
+// U = R^-1 (explicit upper triangular, k x k, ld k; k % 128 == 0) for M + lambda I = R R^T,
+// lambda = damp * mean(diag M); zero diagonals count as 1 and are flagged in dead (k bytes).
+// F: k * k and Tsc: 128 * k floats of scratch; lam: 1 double; flag: set on a non-positive
+// pivot (flipflop.hip).
+kq_status explicit_inverse_factor(const float* M, int64_t k, float damp, float* F, float* Tsc,
+                                  uint8_t* dead, double* lam, int* flag, float* U, hipStream_t s);
+
 }  // namespace kq
 
 #define KQ_HIP(expr)                                                                  \

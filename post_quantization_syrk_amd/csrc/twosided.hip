@@ -1,0 +1,316 @@
+// Two-sided rounding: GPTQ on vec(W) under the Kronecker Hessian
+//   H_d = (H_X + lam_X I) (x) (H_G + lam_G I),  U = chol_upper(H_d^-1) = U_X (x) U_G.
+//
+// BaKron abstract (the two-sided adaptive-rounding formulation of BoA and YAQA, computed
+// in O(m + n) sequential steps with O(mn(m + n)) work).  With c = i m + r the position of
+// W[r, i] in vec(W), coordinate c is rounded with q = code(w_c), e = (w_c - qhat_c) / U[c, c]
+// and feeds w_c' -= e U[c, c'].  U[(i, r), (i', r')] = U_X[i, i'] U_G[r, r'] vanishes unless
+// i' >= i and r' >= r, so a coordinate depends only on those above and to its left, and all
+// coordinates of one anti-diagonal r + i can be rounded together.
+//
+// Schedule: 32 x 32 tiles, one launch per anti-diagonal of tiles, one workgroup per tile.
+// F = E U_X (E the scaled errors, zero until a tile has run) collects each finished tile's
+// errors pushed to the right; a tile (R, I) then
+//   1. pulls its pending feedback  W~[R, I] - sum_{R'' <= R} U_G[R'', R]^T F[R'', I]
+//      (every tile above or to the left is done; fp32 MFMA, the contraction split over the
+//      four waves),
+//   2. rounds its own 63 anti-diagonals: the diagonal's errors e_k (one per row) feed the
+//      whole tile through U_G[k, r'] U_X[d - k, i'], a 32 x 32 x 32 product per step split
+//      over the waves and added into the LDS tile with LDS atomics,
+//   3. pushes its errors:  F[R, I..] += E_tile U_X[I, I..]  (fp32 MFMA).
+// Pulls cost O(m^2 n) and pushes O(m n^2) in all, as in the BaKron bound.
+//
+// Grids: per (row, group) asymmetric min-max from W~ before rounding (a static grid; every
+// dependency-respecting order then gives the same codes), groups of whole tiles.  Scales in
+// fp32 from an fp64 division, zero points in fp64 as the oracle takes them.
+#include "kq_internal.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+namespace kq {
+namespace {
+
+constexpr int TS = 32;   // tile edge
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct TSArgs {
+  const float* W;        // m x n, ld n (W~)
+  const float* UX;       // n x n, ld n, explicit upper inverse factor
+  const float* UG;       // m x m, ld m
+  const float* scale;    // m x ng
+  const uint8_t* zero;   // m x ng
+  const uint8_t* deadX;  // n: zero column of W
+  const uint8_t* deadG;  // m: zero row of W
+  float* F;              // m x n, E U_X of the finished tiles
+  uint8_t* codes;        // m x n
+  int m, n, ng, group, maxq;
+  int d;                 // tile anti-diagonal
+  int r_lo;              // its first tile row
+};
+
+__global__ __launch_bounds__(256) void ts_tile_kernel(TSArgs a) {
+  __shared__ float wt[TS][TS + 1];    // the tile's weights, updated
+  __shared__ float ugd[TS][TS + 1];   // U_G diagonal block [k][r']
+  __shared__ float uxd[TS][TS + 1];   // U_X diagonal block [i][i']
+  __shared__ float et[TS][TS + 1];    // scaled errors
+  __shared__ float ed[TS];            // errors of the current in-tile anti-diagonal, by row
+  __shared__ float srow[TS], zrow[TS];
+  __shared__ float red[4][TS * TS];   // per-wave partial sums of the pulled feedback
+
+  const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, kh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int R = a.r_lo + blockIdx.x, I = a.d - R;
+  const int r0 = TS * R, c0 = TS * I;
+  const int64_t n = a.n, m = a.m;
+
+  // 1. pull: acc[r'][i'] = sum_{k < r0 + 32} U_G[k][r0 + r'] F[k][c0 + i']
+  {
+    f32x16 acc = f32x16{};
+    const int K = r0 + TS;
+    for (int k0 = 2 * wave; k0 < K; k0 += 8) {
+      const int k = k0 + kh;
+      const float av = a.UG[(int64_t)k * m + r0 + l32];
+      const float bv = a.F[(int64_t)k * n + c0 + l32];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[wave][(8 * (r >> 2) + 4 * kh + (r & 3)) * TS + l32] = acc[r];
+  }
+  // diagonal blocks and the tile's grid (groups hold whole tiles)
+  const int g = c0 / a.group;
+  for (int e = t; e < TS * TS; e += 256) {
+    const int r = e >> 5, c = e & 31;
+    ugd[r][c] = a.UG[(int64_t)(r0 + r) * m + r0 + c];
+    uxd[r][c] = a.UX[(int64_t)(c0 + r) * n + c0 + c];
+  }
+  if (t < TS) {
+    srow[t] = a.scale[(int64_t)(r0 + t) * a.ng + g];
+    zrow[t] = (float)a.zero[(int64_t)(r0 + t) * a.ng + g];
+  }
+  __syncthreads();
+  for (int e = t; e < TS * TS; e += 256) {
+    const int r = e >> 5, c = e & 31;
+    const bool dead = a.deadG[r0 + r] || a.deadX[c0 + c];
+    const float w = dead ? 0.f : a.W[(int64_t)(r0 + r) * n + c0 + c];
+    wt[r][c] = w - (red[0][e] + red[1][e] + red[2][e] + red[3][e]);
+  }
+  __syncthreads();
+
+  // 2. the tile's anti-diagonals.  Wave w owns rows k = 8w .. 8w + 7 of the feedback product:
+  //    A[r'][kk] = U_G[k][r'] (fixed), B[kk][i'] = e_k U_X[dd - k][i'].
+  float aop[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) aop[j] = ugd[8 * wave + 2 * j + kh][l32];
+  for (int dd = 0; dd < 2 * TS - 1; ++dd) {
+    if (t < TS) {
+      const int i = dd - t;
+      float e = 0.f;
+      if (i >= 0 && i < TS) {
+        const float w = wt[t][i], s = srow[t], z = zrow[t];
+        const float q = fminf(fmaxf(rintf(w / s) + z, 0.f), (float)a.maxq);
+        const float qh = s * (q - z);
+        e = (w - qh) / (ugd[t][t] * uxd[i][i]);
+        et[t][i] = e;
+        a.codes[(int64_t)(r0 + t) * n + c0 + i] = (uint8_t)q;
+      }
+      ed[t] = e;
+    }
+    __syncthreads();
+    // rows of this wave that lie on the diagonal: k in [8w, 8w + 8) with 0 <= dd - k < 32
+    const int klo = 8 * wave, khi = klo + 7;
+    if (khi >= dd - (TS - 1) && klo <= dd) {
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = klo + 2 * j + kh, ii = dd - k;
+        const float bv = (ii >= 0 && ii < TS) ? ed[k] * uxd[ii < 0 ? 0 : (ii >= TS ? TS - 1 : ii)][l32] : 0.f;
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(aop[j], bv, acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) atomicAdd(&wt[8 * (r >> 2) + 4 * kh + (r & 3)][l32], -acc[r]);
+    }
+    __syncthreads();
+  }
+
+  // 3. push: F[r0 + r][c] += sum_k E[r][k] U_X[c0 + k][c] for c >= c0, 32 columns per block,
+  //    blocks spread over the waves
+  float eop[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) eop[j] = et[l32][2 * j + kh];
+  const int nblk = (a.n - c0) / TS;
+  for (int b = wave; b < nblk; b += 4) {
+    const int cb = c0 + TS * b;
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float bv = a.UX[(int64_t)(c0 + 2 * j + kh) * n + cb + l32];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(eop[j], bv, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float* p = a.F + (int64_t)(r0 + 8 * (r >> 2) + 4 * kh + (r & 3)) * n + cb + l32;
+      *p += acc[r];
+    }
+  }
+}
+
+// Static grid per (row, group) from W~ with dead rows and columns zeroed: one wave each.
+// xmin = min(0, min), xmax = max(0, max), s = (xmax - xmin) / maxq (1 when equal),
+// z = rint(-xmin / s); s and z in fp64, s stored as fp32.
+__global__ __launch_bounds__(256) void ts_grid_kernel(const float* __restrict__ W, int64_t m, int64_t n,
+                                                      int group, int maxq, const uint8_t* __restrict__ deadX,
+                                                      const uint8_t* __restrict__ deadG,
+                                                      float* __restrict__ scale, uint8_t* __restrict__ zero) {
+  const int64_t ng = n / group;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= m * ng) return;
+  const int64_t r = item / ng, g = item % ng;
+  const int lane = threadIdx.x & 63;
+  float lo = 0.f, hi = 0.f;
+  if (!deadG[r]) {
+    for (int64_t c = g * group + lane; c < (g + 1) * group; c += 64) {
+      const float w = deadX[c] ? 0.f : W[r * n + c];
+      lo = fminf(lo, w);
+      hi = fmaxf(hi, w);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = fminf(lo, __shfl_xor(lo, o));
+    hi = fmaxf(hi, __shfl_xor(hi, o));
+  }
+  if (lane == 0) {
+    double s = ((double)hi - (double)lo) / (double)maxq;
+    if (hi == lo) s = 1.0;
+    const double z = rint(-(double)lo / s);
+    scale[item] = (float)s;
+    zero[item] = (uint8_t)z;
+  }
+}
+
+// Packed words: bit k of row r's stream is bit (k mod bits) of code floor(k / bits).
+__global__ __launch_bounds__(256) void ts_pack_kernel(const uint8_t* __restrict__ codes, int64_t m,
+                                                      int64_t n, int bits, uint32_t* __restrict__ packed) {
+  const int64_t wpr = n * bits / 32;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= m * wpr) return;
+  const int64_t r = idx / wpr, wd = idx % wpr;
+  uint32_t v = 0;
+  for (int b = 0; b < 32; ++b) {
+    const int64_t k = 32 * wd + b;
+    v |= (uint32_t)((codes[r * n + k / bits] >> (k % bits)) & 1u) << b;
+  }
+  packed[idx] = v;
+}
+
+struct TSWorkspace {
+  float* UX;
+  float* UG;
+  float* Ffac;   // factorization scratch: kmax^2
+  float* Tsc;    // 128 kmax
+  float* F;      // m x n
+  uint8_t* codes;
+  uint8_t* deadX;
+  uint8_t* deadG;
+  double* lam;
+  int* flag;
+};
+
+int64_t ts_layout(int64_t m, int64_t n, char* base, TSWorkspace* w) {
+  const int64_t k = std::max(m, n);
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return base ? base + o : nullptr;
+  };
+  TSWorkspace x;
+  x.UX = (float*)take(n * n * 4);
+  x.UG = (float*)take(m * m * 4);
+  x.Ffac = (float*)take(k * k * 4);
+  x.Tsc = (float*)take(128 * k * 4);
+  x.F = (float*)take(m * n * 4);
+  x.codes = (uint8_t*)take(m * n);
+  x.deadX = (uint8_t*)take(n);
+  x.deadG = (uint8_t*)take(m);
+  x.lam = (double*)take(8);
+  x.flag = (int*)take(4);
+  if (w) *w = x;
+  return off;
+}
+
+kq_status ts_check(const kq_quant_params* p, int64_t out, int64_t in) {
+  if (!p) return fail(KQ_EINVAL, "kq_quantize_two_sided: params is NULL");
+  if (p->bits < 2 || p->bits > 4) return fail(KQ_EINVAL, "kq_quantize_two_sided: bits must be 2, 3 or 4");
+  if (p->asym != 1) return fail(KQ_ENOTIMPL, "kq_quantize_two_sided: only the asymmetric grid (asym = 1)");
+  if (p->act_order != 0 || p->w_clip != 0)
+    return fail(KQ_ENOTIMPL, "kq_quantize_two_sided: act_order and w_clip are not implemented");
+  if (!(p->damp >= 0.0f)) return fail(KQ_EINVAL, "kq_quantize_two_sided: damp must be >= 0");
+  if (out < 128 || in < 128 || out % 128 != 0 || in % 128 != 0 || out > 32768 || in > 32768)
+    return fail(KQ_ESHAPE, "kq_quantize_two_sided: out and in must be multiples of 128 (<= 32768)");
+  if (p->group < TS || p->group % TS != 0 || in % p->group != 0)
+    return fail(KQ_ESHAPE, "kq_quantize_two_sided: group must be a multiple of 32 dividing in");
+  if ((in * p->bits) % 32 != 0) return fail(KQ_ESHAPE, "kq_quantize_two_sided: in * bits %% 32 != 0");
+  return KQ_OK;
+}
+
+}  // namespace
+}  // namespace kq
+
+extern "C" kq_status kq_quantize_two_sided_workspace(const kq_quant_params* p, int64_t out,
+                                                     int64_t in, size_t* bytes) {
+  using namespace kq;
+  if (!bytes) return fail(KQ_EINVAL, "kq_quantize_two_sided_workspace: bytes is NULL");
+  KQ_TRY(ts_check(p, out, in));
+  *bytes = (size_t)ts_layout(out, in, nullptr, nullptr);
+  return KQ_OK;
+}
+
+extern "C" kq_status kq_quantize_two_sided(const kq_quant_params* p, const float* W, const float* HX,
+                                           const float* HG, int64_t out, int64_t in, uint32_t* packed,
+                                           float* scales, uint8_t* zeros, void* ws, size_t ws_bytes,
+                                           uint8_t* codes_opt, void* stream) {
+  using namespace kq;
+  KQ_TRY(ts_check(p, out, in));
+  if (!W || !HX || !HG || !packed || !scales || !zeros || !ws)
+    return fail(KQ_EINVAL, "kq_quantize_two_sided: NULL argument");
+  const size_t need = (size_t)ts_layout(out, in, nullptr, nullptr);
+  if (ws_bytes < need) return fail(KQ_EWORKSPACE, "kq_quantize_two_sided: workspace of %zu bytes needed", need);
+  TSWorkspace w;
+  ts_layout(out, in, (char*)ws, &w);
+  hipStream_t s = as_stream(stream);
+  const int64_t m = out, n = in;
+  KQ_HIP(hipMemsetAsync(w.flag, 0, sizeof(int), s));
+  KQ_TRY(explicit_inverse_factor(HX, n, p->damp, w.Ffac, w.Tsc, w.deadX, w.lam, w.flag, w.UX, s));
+  KQ_TRY(explicit_inverse_factor(HG, m, p->damp, w.Ffac, w.Tsc, w.deadG, w.lam, w.flag, w.UG, s));
+  const int maxq = (1 << p->bits) - 1;
+  const int64_t items = m * (n / p->group);
+  ts_grid_kernel<<<dim3((unsigned)ceil_div(items, 4)), dim3(256), 0, s>>>(W, m, n, p->group, maxq, w.deadX,
+                                                                         w.deadG, scales, zeros);
+  KQ_LAUNCHED("ts_grid_kernel");
+  KQ_TRY(fill_f32(w.F, m * n, 0.0f, s));
+  uint8_t* codes = codes_opt ? codes_opt : w.codes;
+  TSArgs a;
+  a.W = W; a.UX = w.UX; a.UG = w.UG; a.scale = scales; a.zero = zeros;
+  a.deadX = w.deadX; a.deadG = w.deadG; a.F = w.F; a.codes = codes;
+  a.m = (int)m; a.n = (int)n; a.ng = (int)(n / p->group); a.group = p->group; a.maxq = maxq;
+  const int NR = (int)(m / TS), NI = (int)(n / TS);
+  for (int d = 0; d < NR + NI - 1; ++d) {
+    a.d = d;
+    a.r_lo = std::max(0, d - (NI - 1));
+    const int r_hi = std::min(d, NR - 1);
+    ts_tile_kernel<<<dim3((unsigned)(r_hi - a.r_lo + 1)), dim3(256), 0, s>>>(a);
+    KQ_LAUNCHED("ts_tile_kernel");
+  }
+  const int64_t words = m * (n * p->bits / 32);
+  ts_pack_kernel<<<dim3((unsigned)ceil_div(words, 256)), dim3(256), 0, s>>>(codes, m, n, p->bits, packed);
+  KQ_LAUNCHED("ts_pack_kernel");
+  int flag = 0;
+  KQ_HIP(hipMemcpyAsync(&flag, w.flag, sizeof(int), hipMemcpyDeviceToHost, s));
+  KQ_HIP(hipStreamSynchronize(s));
+  if (flag) return fail(KQ_ENOTSPD, "kq_quantize_two_sided: a damped factor has no Cholesky factor");
+  return KQ_OK;
+}
