@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--flipflop", type=int, default=None, metavar="ITERS",
                     help="time the FlipFlop Hessian factors instead: ITERS alternating "
                          "iterations from the identity on the workload's streams")
+    ap.add_argument("--two-sided", action="store_true",
+                    help="round with two-sided GPTQ under H_X (x) H_G instead of GPTQ")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB fp32 tensor three times (scale for the HBM byte "
                          "counters FETCH_SIZE / WRITE_SIZE) and exit")
@@ -431,6 +433,27 @@ def flipflop_main(a) -> None:
     print(json.dumps(line), flush=True)
 
 
+def two_sided_cpu_baseline(cfg) -> dict:
+    """The oracle's two-sided rounding on the layer's leading 128 x 128 block (a problem of
+    its own), scaled by the work count sum_{r, i} (m - r)(n - i) of the full layer; the
+    Hessian and BiIP legs of the step are not added (they are the GPTQ baseline's)."""
+    import oracle as o
+    b = 128
+    rng = np.random.default_rng(0)
+    W = rng.standard_normal((b, b)) * 0.02
+    A = rng.standard_normal((3 * b, b))
+    B = rng.standard_normal((3 * b, b))
+    t0 = time.perf_counter()
+    o.two_sided_gptq(W, A.T @ A, B.T @ B, cfg.bits, min(cfg.group, b))
+    t = time.perf_counter() - t0
+    work = lambda m, n: (m * (m + 1) / 2) * (n * (n + 1) / 2)  # noqa: E731
+    full = t * work(cfg.out, cfg.inp) / work(b, b)
+    return {"value": round(cfg.out * cfg.inp / full, 3), "unit": "params/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": (f"two-sided rounding of a {b} x {b} block in {t:.1f} s, scaled by the "
+                       f"O(m^2 n^2) work count to {cfg.out} x {cfg.inp}: {full:.3g} s")}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -476,7 +499,10 @@ def main():
     d_out = torch.empty(out_n, device=dev)
     p = kq.make_params(cfg.bits, cfg.group, cfg.block, cfg.damp, act_order=cfg.act_order,
                        w_clip=cfg.w_clip)
-    ws = torch.empty(kq.kq_quantize_layer_workspace(p, out_n, in_n, False), dtype=torch.uint8, device=dev)
+    if a.two_sided:
+        ws = torch.empty(kq.kq_quantize_two_sided_workspace(p, out_n, in_n), dtype=torch.uint8, device=dev)
+    else:
+        ws = torch.empty(kq.kq_quantize_layer_workspace(p, out_n, in_n, False), dtype=torch.uint8, device=dev)
     packed = torch.empty((out_n, in_n * cfg.bits // 32), dtype=torch.int32, device=dev)
     scales = torch.empty((out_n, in_n // cfg.group), device=dev)
     zeros = torch.empty((out_n, in_n // cfg.group), dtype=torch.uint8, device=dev)
@@ -501,7 +527,10 @@ def main():
                           kq.KQ_BIIP_FULL, cfg.had_in, cfg.had_out, stream=stream)
         if record:
             e[4].record(stream)
-        kq.kq_quantize_layer(p, Wt, HX, HG, packed, scales, zeros, ws, stream=stream)
+        if a.two_sided:
+            kq.kq_quantize_two_sided(p, Wt, HX, HG, packed, scales, zeros, ws, stream=stream)
+        else:
+            kq.kq_quantize_layer(p, Wt, HX, HG, packed, scales, zeros, ws, stream=stream)
         if record:
             e[5].record(stream)
         return e, sens
@@ -533,12 +562,21 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel": "syrk_dma_kernel",
                 "algorithmic_flops_per_launch": flops_per_launch}
+    if a.two_sided:
+        # the rounding wavefront dominates: its pulls and pushes are m n (m + n) / 2 fp32 MACs
+        ts_ms = stage_ms["quantize"]
+        ts_flops = float(out_n) * in_n * (out_n + in_n)
+        ts_ach = ts_flops / (ts_ms / 1e3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(ts_ach, 2), "peak": PEAK_FP32_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ts_ach / PEAK_FP32_TFLOPS, 4), "traffic": None,
+                    "kernel": "two-sided rounding (pull / round / push wavefront, with its factors)",
+                    "algorithmic_flops_per_launch": ts_flops}
 
     cpu = None
     if not a.no_cpu_baseline:
         del X, G
         torch.cuda.empty_cache()
-        cpu = cpu_baseline(cfg, a.cpu_seconds)
+        cpu = two_sided_cpu_baseline(cfg) if a.two_sided else cpu_baseline(cfg, a.cpu_seconds)
 
     line = {
         "metric": "quantized params/s per layer incl. Hessian build",
@@ -550,7 +588,8 @@ def main():
         "config": {"workload": cfg.name, "out": out_n, "in": in_n, "tokens": T, "bits": cfg.bits,
                    "group": cfg.group, "block": cfg.block, "hadamard_in": cfg.had_in,
                    "hadamard_out": cfg.had_out, "alpha": cfg.alpha, "damp": cfg.damp,
-                   "act_order": cfg.act_order, "w_clip": cfg.w_clip},
+                   "act_order": cfg.act_order, "w_clip": cfg.w_clip,
+                   "rounding": "two-sided" if a.two_sided else "gptq"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},

@@ -8,16 +8,16 @@
 // i' >= i and r' >= r, so a coordinate depends only on those above and to its left, and all
 // coordinates of one anti-diagonal r + i can be rounded together.
 //
-// Schedule: 32 x 32 tiles, one launch per anti-diagonal of tiles, one workgroup per tile.
-// F = E U_X (E the scaled errors, zero until a tile has run) collects each finished tile's
-// errors pushed to the right; a tile (R, I) then
-//   1. pulls its pending feedback  W~[R, I] - sum_{R'' <= R} U_G[R'', R]^T F[R'', I]
-//      (every tile above or to the left is done; fp32 MFMA, the contraction split over the
-//      four waves),
-//   2. rounds its own 63 anti-diagonals: the diagonal's errors e_k (one per row) feed the
-//      whole tile through U_G[k, r'] U_X[d - k, i'], a 32 x 32 x 32 product per step split
-//      over the waves and added into the LDS tile with LDS atomics,
-//   3. pushes its errors:  F[R, I..] += E_tile U_X[I, I..]  (fp32 MFMA).
+// Schedule: 32 x 32 tiles and, per anti-diagonal of tiles, three launches.  F = E U_X (E
+// the scaled errors, zero until a tile has run) collects each finished tile's errors
+// pushed to the right.  For every tile (R, I) of the diagonal:
+//   1. pull: the pending feedback sum_{R'' <= R} U_G[R'', R]^T F[R'', I] (every tile above
+//      or to the left is done), split over slices of 256 contraction indices, one workgroup
+//      each (fp32 MFMA), partial sums kept per slice and added in a fixed order;
+//   2. round: one workgroup per tile rounds its 63 anti-diagonals; each step's errors e_k
+//      (one per row) feed the whole tile through U_G[k, r'] U_X[d - k, i'], a 32 x 32 x 32
+//      product split over the waves and added into the LDS tile with LDS atomics;
+//   3. push: F[R, I..] += E_tile U_X[I, I..], split over chunks of 256 columns (fp32 MFMA).
 // Pulls cost O(m^2 n) and pushes O(m n^2) in all, as in the BaKron bound.
 //
 // Grids: per (row, group) asymmetric min-max from W~ before rounding (a static grid; every
@@ -36,6 +36,9 @@ constexpr int TS = 32;   // tile edge
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+constexpr int KS = 256;  // contraction indices per pull slice
+constexpr int PS = 256;  // columns per push chunk
+
 struct TSArgs {
   const float* W;        // m x n, ld n (W~)
   const float* UX;       // n x n, ld n, explicit upper inverse factor
@@ -45,62 +48,88 @@ struct TSArgs {
   const uint8_t* deadX;  // n: zero column of W
   const uint8_t* deadG;  // m: zero row of W
   float* F;              // m x n, E U_X of the finished tiles
+  float* E;              // m x n, scaled errors
+  float* part;           // pull partial sums: [tile of the diagonal][slice][32 x 32]
   uint8_t* codes;        // m x n
   int m, n, ng, group, maxq;
   int d;                 // tile anti-diagonal
   int r_lo;              // its first tile row
+  int nslice;            // slices per tile in part (the most any tile of a diagonal needs)
 };
 
-__global__ __launch_bounds__(256) void ts_tile_kernel(TSArgs a) {
+__device__ __forceinline__ int acc_row(int r, int kh) { return 8 * (r >> 2) + 4 * kh + (r & 3); }
+
+// 1. pull, slice s of tile (R, I): sum over k in [s KS, min(32 (R + 1), (s + 1) KS)) of
+//    U_G[k][r0 + r'] F[k][c0 + i'].  The four waves take interleaved k pairs, 16 pairs' loads
+//    in flight before their products.
+__global__ __launch_bounds__(256) void ts_pull_kernel(TSArgs a) {
+  __shared__ float red[4][TS * TS];
+  const int tix = blockIdx.x / a.nslice, sl = blockIdx.x % a.nslice;
+  const int R = a.r_lo + tix, I = a.d - R;
+  const int r0 = TS * R, c0 = TS * I;
+  const int K = r0 + TS, kb = sl * KS, ke = min(K, kb + KS);
+  if (kb >= ke) return;
+  const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, kh = lane >> 5;
+  const int wave = t >> 6;
+  const int64_t n = a.n, m = a.m;
+  f32x16 acc = f32x16{};
+  // pairs k0 = kb + 2 (wave + 4 j), j = 0 .. (ke - kb) / 8 - 1 (ke - kb is a multiple of 32)
+  const int npairs = (ke - kb) / 8;
+  for (int j0 = 0; j0 < npairs; j0 += 16) {
+    float av[16], bv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int k = kb + 2 * (wave + 4 * min(j0 + j, npairs - 1)) + kh;
+      av[j] = a.UG[(int64_t)k * m + r0 + l32];
+      bv[j] = a.F[(int64_t)k * n + c0 + l32];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j0 + j < npairs) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[j], bv[j], acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) red[wave][acc_row(r, kh) * TS + l32] = acc[r];
+  __syncthreads();
+  float* out = a.part + ((int64_t)tix * a.nslice + sl) * (TS * TS);
+  for (int e = t; e < TS * TS; e += 256) out[e] = red[0][e] + red[1][e] + red[2][e] + red[3][e];
+}
+
+// 2. round tile (R, I): W~ (dead rows / columns zero) minus the pulled feedback, then the
+//    tile's own anti-diagonals.
+__global__ __launch_bounds__(256) void ts_round_kernel(TSArgs a) {
   __shared__ float wt[TS][TS + 1];    // the tile's weights, updated
   __shared__ float ugd[TS][TS + 1];   // U_G diagonal block [k][r']
   __shared__ float uxd[TS][TS + 1];   // U_X diagonal block [i][i']
   __shared__ float et[TS][TS + 1];    // scaled errors
+  __shared__ uint8_t ct[TS][TS];      // codes
   __shared__ float ed[TS];            // errors of the current in-tile anti-diagonal, by row
   __shared__ float srow[TS], zrow[TS];
-  __shared__ float red[4][TS * TS];   // per-wave partial sums of the pulled feedback
-
   const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, kh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int R = a.r_lo + blockIdx.x, I = a.d - R;
+  const int tix = blockIdx.x;
+  const int R = a.r_lo + tix, I = a.d - R;
   const int r0 = TS * R, c0 = TS * I;
   const int64_t n = a.n, m = a.m;
-
-  // 1. pull: acc[r'][i'] = sum_{k < r0 + 32} U_G[k][r0 + r'] F[k][c0 + i']
-  {
-    f32x16 acc = f32x16{};
-    const int K = r0 + TS;
-    for (int k0 = 2 * wave; k0 < K; k0 += 8) {
-      const int k = k0 + kh;
-      const float av = a.UG[(int64_t)k * m + r0 + l32];
-      const float bv = a.F[(int64_t)k * n + c0 + l32];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) red[wave][(8 * (r >> 2) + 4 * kh + (r & 3)) * TS + l32] = acc[r];
-  }
-  // diagonal blocks and the tile's grid (groups hold whole tiles)
-  const int g = c0 / a.group;
+  const int nsl = (r0 + TS + KS - 1) / KS;   // slices this tile's pull used
+  const int g = c0 / a.group;                // groups hold whole tiles
   for (int e = t; e < TS * TS; e += 256) {
     const int r = e >> 5, c = e & 31;
     ugd[r][c] = a.UG[(int64_t)(r0 + r) * m + r0 + c];
     uxd[r][c] = a.UX[(int64_t)(c0 + r) * n + c0 + c];
+    const bool dead = a.deadG[r0 + r] || a.deadX[c0 + c];
+    float w = dead ? 0.f : a.W[(int64_t)(r0 + r) * n + c0 + c];
+    const float* p = a.part + (int64_t)tix * a.nslice * (TS * TS) + e;
+    for (int sl = 0; sl < nsl; ++sl) w -= p[(int64_t)sl * (TS * TS)];
+    wt[r][c] = w;
   }
   if (t < TS) {
     srow[t] = a.scale[(int64_t)(r0 + t) * a.ng + g];
     zrow[t] = (float)a.zero[(int64_t)(r0 + t) * a.ng + g];
   }
   __syncthreads();
-  for (int e = t; e < TS * TS; e += 256) {
-    const int r = e >> 5, c = e & 31;
-    const bool dead = a.deadG[r0 + r] || a.deadX[c0 + c];
-    const float w = dead ? 0.f : a.W[(int64_t)(r0 + r) * n + c0 + c];
-    wt[r][c] = w - (red[0][e] + red[1][e] + red[2][e] + red[3][e]);
-  }
-  __syncthreads();
 
-  // 2. the tile's anti-diagonals.  Wave w owns rows k = 8w .. 8w + 7 of the feedback product:
-  //    A[r'][kk] = U_G[k][r'] (fixed), B[kk][i'] = e_k U_X[dd - k][i'].
+  // Wave w owns rows k = 8w .. 8w + 7 of each step's feedback product:
+  // A[r'][kk] = U_G[k][r'] (fixed), B[kk][i'] = e_k U_X[dd - k][i'].
   float aop[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) aop[j] = ugd[8 * wave + 2 * j + kh][l32];
@@ -114,7 +143,7 @@ __global__ __launch_bounds__(256) void ts_tile_kernel(TSArgs a) {
         const float qh = s * (q - z);
         e = (w - qh) / (ugd[t][t] * uxd[i][i]);
         et[t][i] = e;
-        a.codes[(int64_t)(r0 + t) * n + c0 + i] = (uint8_t)q;
+        ct[t][i] = (uint8_t)q;
       }
       ed[t] = e;
     }
@@ -130,30 +159,47 @@ __global__ __launch_bounds__(256) void ts_tile_kernel(TSArgs a) {
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(aop[j], bv, acc, 0, 0, 0);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) atomicAdd(&wt[8 * (r >> 2) + 4 * kh + (r & 3)][l32], -acc[r]);
+      for (int r = 0; r < 16; ++r) atomicAdd(&wt[acc_row(r, kh)][l32], -acc[r]);
     }
     __syncthreads();
   }
+  // errors and codes out once the tile is done (a global store inside the loop would make
+  // every barrier wait for it)
+  for (int e = t; e < TS * TS; e += 256) {
+    const int r = e >> 5, c = e & 31;
+    a.E[(int64_t)(r0 + r) * n + c0 + c] = et[r][c];
+    a.codes[(int64_t)(r0 + r) * n + c0 + c] = ct[r][c];
+  }
+}
 
-  // 3. push: F[r0 + r][c] += sum_k E[r][k] U_X[c0 + k][c] for c >= c0, 32 columns per block,
-  //    blocks spread over the waves
+// 3. push, chunk c of tile (R, I): F[r0 + r][col] += sum_k E[r0 + r][c0 + k] U_X[c0 + k][col]
+//    for the chunk's columns (at or right of c0), 32 per wave block.
+__global__ __launch_bounds__(256) void ts_push_kernel(TSArgs a, int nchunk) {
+  const int tix = blockIdx.x / nchunk, ch = blockIdx.x % nchunk;
+  const int R = a.r_lo + tix, I = a.d - R;
+  const int r0 = TS * R, c0 = TS * I;
+  const int cb0 = c0 + ch * PS;
+  if (cb0 >= a.n) return;
+  const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, kh = lane >> 5;
+  const int wave = t >> 6;
+  const int64_t n = a.n;
   float eop[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) eop[j] = et[l32][2 * j + kh];
-  const int nblk = (a.n - c0) / TS;
+  for (int j = 0; j < 16; ++j) eop[j] = a.E[(int64_t)(r0 + l32) * n + c0 + 2 * j + kh];
+  const int nblk = min(PS, a.n - cb0) / TS;
   for (int b = wave; b < nblk; b += 4) {
-    const int cb = c0 + TS * b;
+    const int cb = cb0 + TS * b;
+    float bv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) bv[j] = a.UX[(int64_t)(c0 + 2 * j + kh) * n + cb + l32];
+    float fo[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) fo[r] = a.F[(int64_t)(r0 + acc_row(r, kh)) * n + cb + l32];
     f32x16 acc = f32x16{};
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float bv = a.UX[(int64_t)(c0 + 2 * j + kh) * n + cb + l32];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(eop[j], bv, acc, 0, 0, 0);
-    }
+    for (int j = 0; j < 16; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(eop[j], bv[j], acc, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float* p = a.F + (int64_t)(r0 + 8 * (r >> 2) + 4 * kh + (r & 3)) * n + cb + l32;
-      *p += acc[r];
-    }
+    for (int r = 0; r < 16; ++r) a.F[(int64_t)(r0 + acc_row(r, kh)) * n + cb + l32] = fo[r] + acc[r];
   }
 }
 
@@ -212,6 +258,8 @@ struct TSWorkspace {
   float* Ffac;   // factorization scratch: kmax^2
   float* Tsc;    // 128 kmax
   float* F;      // m x n
+  float* E;      // m x n
+  float* part;   // pull partial sums
   uint8_t* codes;
   uint8_t* deadX;
   uint8_t* deadG;
@@ -233,6 +281,8 @@ int64_t ts_layout(int64_t m, int64_t n, char* base, TSWorkspace* w) {
   x.Ffac = (float*)take(k * k * 4);
   x.Tsc = (float*)take(128 * k * 4);
   x.F = (float*)take(m * n * 4);
+  x.E = (float*)take(m * n * 4);
+  x.part = (float*)take(std::min(m, n) / TS * (m / KS + 1) * TS * TS * 4);
   x.codes = (uint8_t*)take(m * n);
   x.deadX = (uint8_t*)take(n);
   x.deadG = (uint8_t*)take(m);
@@ -295,15 +345,23 @@ extern "C" kq_status kq_quantize_two_sided(const kq_quant_params* p, const float
   uint8_t* codes = codes_opt ? codes_opt : w.codes;
   TSArgs a;
   a.W = W; a.UX = w.UX; a.UG = w.UG; a.scale = scales; a.zero = zeros;
-  a.deadX = w.deadX; a.deadG = w.deadG; a.F = w.F; a.codes = codes;
+  a.deadX = w.deadX; a.deadG = w.deadG; a.F = w.F; a.E = w.E; a.part = w.part; a.codes = codes;
   a.m = (int)m; a.n = (int)n; a.ng = (int)(n / p->group); a.group = p->group; a.maxq = maxq;
   const int NR = (int)(m / TS), NI = (int)(n / TS);
   for (int d = 0; d < NR + NI - 1; ++d) {
     a.d = d;
     a.r_lo = std::max(0, d - (NI - 1));
     const int r_hi = std::min(d, NR - 1);
-    ts_tile_kernel<<<dim3((unsigned)(r_hi - a.r_lo + 1)), dim3(256), 0, s>>>(a);
-    KQ_LAUNCHED("ts_tile_kernel");
+    const int tiles = r_hi - a.r_lo + 1;
+    a.nslice = (TS * (r_hi + 1) + KS - 1) / KS;           // the lowest tile pulls the most
+    ts_pull_kernel<<<dim3((unsigned)(tiles * a.nslice)), dim3(256), 0, s>>>(a);
+    KQ_LAUNCHED("ts_pull_kernel");
+    ts_round_kernel<<<dim3((unsigned)tiles), dim3(256), 0, s>>>(a);
+    KQ_LAUNCHED("ts_round_kernel");
+    const int I_lo = d - r_hi;                              // the leftmost tile pushes the most
+    const int nchunk = (int)ceil_div(n - (int64_t)TS * I_lo, PS);
+    ts_push_kernel<<<dim3((unsigned)(tiles * nchunk)), dim3(256), 0, s>>>(a, nchunk);
+    KQ_LAUNCHED("ts_push_kernel");
   }
   const int64_t words = m * (n * p->bits / 32);
   ts_pack_kernel<<<dim3((unsigned)ceil_div(words, 256)), dim3(256), 0, s>>>(codes, m, n, p->bits, packed);
