@@ -1,5 +1,7 @@
 """Helpers for the GPU parity tests: moving seeded inputs to the device."""
+import os
 import sys
+import time
 
 import numpy as np
 import pytest
@@ -31,6 +33,18 @@ def rel_fro(a, b) -> float:
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
+_PROGRESS = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out",
+                         "test_progress.log")
+
+
 def announce(msg: str) -> None:
+    """Name the case on stdout (shown with -s) and append it to gpurun_out/test_progress.log,
+    which a captured run still writes as it goes."""
     print(f"[gpu-case] {msg}", flush=True)
     sys.stdout.flush()
+    try:
+        os.makedirs(os.path.dirname(_PROGRESS), exist_ok=True)
+        with open(_PROGRESS, "a") as f:
+            f.write(f"{time.strftime('%H:%M:%S')} {msg}\n")
+    except OSError:
+        pass
