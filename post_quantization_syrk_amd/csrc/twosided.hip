@@ -16,7 +16,8 @@
 //      each (fp32 MFMA), partial sums kept per slice and added in a fixed order;
 //   2. round: one workgroup per tile rounds its 63 anti-diagonals; each step's errors e_k
 //      (one per row) feed the whole tile through U_G[k, r'] U_X[d - k, i'], a 32 x 32 x 32
-//      product split over the waves and added into the LDS tile with LDS atomics;
+//      product of which each wave forms and applies one 16 x 16 quadrant (LDS float atomics,
+//      or partials summed across waves, cost several times the whole loop here);
 //   3. push: F[R, I..] += E_tile U_X[I, I..], split over chunks of 256 columns (fp32 MFMA).
 // Pulls cost O(m^2 n) and pushes O(m n^2) in all, as in the BaKron bound.
 //
@@ -38,6 +39,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int KS = 256;  // contraction indices per pull slice
 constexpr int PS = 256;  // columns per push chunk
+constexpr int MAXSL = 16;  // pull slices summed per batch of loads in the round kernel
 
 struct TSArgs {
   const float* W;        // m x n, ld n (W~)
@@ -112,15 +114,36 @@ __global__ __launch_bounds__(256) void ts_round_kernel(TSArgs a) {
   const int64_t n = a.n, m = a.m;
   const int nsl = (r0 + TS + KS - 1) / KS;   // slices this tile's pull used
   const int g = c0 / a.group;                // groups hold whole tiles
-  for (int e = t; e < TS * TS; e += 256) {
-    const int r = e >> 5, c = e & 31;
-    ugd[r][c] = a.UG[(int64_t)(r0 + r) * m + r0 + c];
-    uxd[r][c] = a.UX[(int64_t)(c0 + r) * n + c0 + c];
-    const bool dead = a.deadG[r0 + r] || a.deadX[c0 + c];
-    float w = dead ? 0.f : a.W[(int64_t)(r0 + r) * n + c0 + c];
-    const float* p = a.part + (int64_t)tix * a.nslice * (TS * TS) + e;
-    for (int sl = 0; sl < nsl; ++sl) w -= p[(int64_t)sl * (TS * TS)];
-    wt[r][c] = w;
+  {
+    // the slices' partial sums through a descriptor bounded to them: every load issued at
+    // once, the ones past the last slice read 0
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        a.part + (int64_t)tix * a.nslice * (TS * TS), 0, nsl * TS * TS * 4, 0x00020000);
+    float ps[4][MAXSL];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int sl = 0; sl < MAXSL; ++sl)
+        ps[q][sl] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rp, 4 * (sl * TS * TS + t + 256 * q), 0, 0));
+    for (int sl0 = MAXSL; sl0 < nsl; sl0 += MAXSL)   // tiles below row 2^12 / 32: more slices
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int sl = 0; sl < MAXSL; ++sl)
+          ps[q][sl] += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rp, 4 * ((sl0 + sl) * TS * TS + t + 256 * q), 0, 0));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = t + 256 * q, r = e >> 5, c = e & 31;
+      ugd[r][c] = a.UG[(int64_t)(r0 + r) * m + r0 + c];
+      uxd[r][c] = a.UX[(int64_t)(c0 + r) * n + c0 + c];
+      const bool dead = a.deadG[r0 + r] || a.deadX[c0 + c];
+      float w = dead ? 0.f : a.W[(int64_t)(r0 + r) * n + c0 + c];
+#pragma unroll
+      for (int sl = 0; sl < MAXSL; ++sl) w -= ps[q][sl];
+      wt[r][c] = w;
+    }
   }
   if (t < TS) {
     srow[t] = a.scale[(int64_t)(r0 + t) * a.ng + g];
@@ -128,11 +151,13 @@ __global__ __launch_bounds__(256) void ts_round_kernel(TSArgs a) {
   }
   __syncthreads();
 
-  // Wave w owns rows k = 8w .. 8w + 7 of each step's feedback product:
-  // A[r'][kk] = U_G[k][r'] (fixed), B[kk][i'] = e_k U_X[dd - k][i'].
-  float aop[4];
+  // Wave w owns the 16 x 16 quadrant (rows 16 (w >> 1), columns 16 (w & 1)) of each step's
+  // feedback Delta[r'][i'] = sum_k U_G[k][r'] e_k U_X[dd - k][i'] (v_mfma_f32_16x16x4f32, k in
+  // fours): A[r'][kk] = U_G[k][r'] is fixed, B[kk][i'] = e_k U_X[dd - k][i'].
+  const int q0 = 16 * (wave >> 1), q1 = 16 * (wave & 1), l16 = lane & 15, kq = lane >> 4;
+  float aop[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) aop[j] = ugd[8 * wave + 2 * j + kh][l32];
+  for (int j = 0; j < 8; ++j) aop[j] = ugd[4 * j + kq][q0 + l16];
   for (int dd = 0; dd < 2 * TS - 1; ++dd) {
     if (t < TS) {
       const int i = dd - t;
@@ -148,18 +173,21 @@ __global__ __launch_bounds__(256) void ts_round_kernel(TSArgs a) {
       ed[t] = e;
     }
     __syncthreads();
-    // rows of this wave that lie on the diagonal: k in [8w, 8w + 8) with 0 <= dd - k < 32
-    const int klo = 8 * wave, khi = klo + 7;
-    if (khi >= dd - (TS - 1) && klo <= dd) {
-      f32x16 acc = f32x16{};
+    // k-blocks with a coordinate on the diagonal: 4 j + 3 >= dd - 31 and 4 j <= dd; only rows
+    // k <= r' reach the quadrant (U_G upper), so blocks past its last row add nothing
+    const int jlo = max(0, (dd - (TS - 1)) >> 2), jhi = min(min(7, dd >> 2), (q0 + 15) >> 2);
+    if (jlo <= jhi) {
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int k = klo + 2 * j + kh, ii = dd - k;
-        const float bv = (ii >= 0 && ii < TS) ? ed[k] * uxd[ii < 0 ? 0 : (ii >= TS ? TS - 1 : ii)][l32] : 0.f;
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(aop[j], bv, acc, 0, 0, 0);
+      for (int j = 0; j < 8; ++j) {
+        if (j < jlo || j > jhi) continue;   // uniform
+        const int k = 4 * j + kq, ii = dd - k;
+        const float bv = (ii >= 0 && ii < TS) ? ed[k] * uxd[ii < 0 ? 0 : (ii >= TS ? TS - 1 : ii)][q1 + l16] : 0.f;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[j], bv, acc, 0, 0, 0);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) atomicAdd(&wt[acc_row(r, kh)][l32], -acc[r]);
+      for (int j = 0; j < 4; ++j) wt[q0 + 4 * kq + j][q1 + l16] -= acc[j];
     }
     __syncthreads();
   }
