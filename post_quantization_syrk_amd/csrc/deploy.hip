@@ -29,7 +29,7 @@ namespace kq {
 namespace {
 
 constexpr int DT = 256;     // threads per workgroup
-constexpr int DR = 16;      // rows per workgroup of the matvec kernel (4 per wave)
+constexpr int DR = 16;      // output blocks up to this many rows are rotated in the matvec kernel
 constexpr int MAXC = 8;     // 16-byte chunks per lane and row kept in flight
 constexpr int SEG = 4096;   // entries per workgroup of the output rotation (or one block)
 
@@ -245,28 +245,29 @@ __device__ __forceinline__ void stage_rotated(float* v, const float* src, const 
   lds_fwht_rest(v, n, b);
 }
 
-// Rows [rw0, rw0 + 16) of layer L: y~ (or y, when its output blocks fit in 16 rows).
-template <int BITS, int MC, int B>
+// Rows [rw0, rw0 + 4 RPW) of layer L (RPW rows per wave): y~ (or y, when its output blocks
+// fit in 16 rows).
+template <int BITS, int MC, int B, int RPW>
 __device__ __forceinline__ void matvec_rows(const GroupArgs& a, const LayerArgs& L, int rw0,
                                             float* xs) {
   constexpr int CPW = 32 / BITS;        // codes per word
   constexpr int CPC = 4 * CPW;          // codes per 16-byte chunk
   constexpr int BPC = 8 / BITS;         // codes per byte
   constexpr unsigned MASK = BITS == 4 ? 0x0F0F0F0Fu : 0x03030303u;
-  __shared__ float yloc[DR];
+  __shared__ float yloc[4 * RPW];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int wpr = L.wpr, ngr = L.ngroups, in = a.in;
   const int nck = (wpr + 4 * 64 - 1) / (4 * 64);      // 16-byte chunks per lane and row
-  const int rows = min(DR, L.out - rw0), wr0 = 4 * wv;   // rows of the workgroup; the wave's
+  const int rows = min(4 * RPW, L.out - rw0), wr0 = RPW * wv;   // the workgroup's rows; the wave's
 
-  // 1. loads of the packed words, scales and zeros of the wave's 4 rows, MC chunks at a time.
+  // 1. loads of the packed words, scales and zeros of the wave's rows, MC chunks at a time.
   //    Descriptors over the workgroup's rows only: rows past `out` read 0.  Words past a
   //    row's end read the next row (or 0); they meet x~ entries past `in`, which are 0.
   const __amdgpu_buffer_rsrc_t rp = rsrc(L.packed + (int64_t)rw0 * wpr, rows * wpr * 4);
   const __amdgpu_buffer_rsrc_t rsc = rsrc(L.scales + (int64_t)rw0 * ngr, rows * ngr * 4);
   const __amdgpu_buffer_rsrc_t rzp = rsrc(L.zeros + (int64_t)rw0 * ngr, rows * ngr);
-  u32x4 wq[4][MC];
-  float sc[4][MC], zc[4][MC];
+  u32x4 wq[RPW][MC];
+  float sc[RPW][MC], zc[RPW][MC];
   auto load_chunks = [&](int c0) {
 #pragma unroll
     for (int c = 0; c < MC; ++c) {
@@ -274,7 +275,7 @@ __device__ __forceinline__ void matvec_rows(const GroupArgs& a, const LayerArgs&
       const int pos = word * CPW;
       const int g = (int)__umulhi((unsigned)(pos < in ? pos : in - 1), L.gmagic);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < RPW; ++i) {
         wq[i][c] = __builtin_amdgcn_raw_buffer_load_b128(rp, ((wr0 + i) * wpr + word) * 4, 0, 0);
         const int go = (wr0 + i) * ngr + g;
         sc[i][c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsc, 4 * go, 0, 0));
@@ -289,7 +290,9 @@ __device__ __forceinline__ void matvec_rows(const GroupArgs& a, const LayerArgs&
                    [&] { load_chunks(0); });
 
   // 3. dot products: row r's chunk contributes s (sum q x~ - z sum x~)
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float acc[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) acc[i] = 0.f;
   for (int c0 = 0; c0 < nck; c0 += MC) {
     if (c0 > 0) load_chunks(c0);
 #pragma unroll
@@ -306,7 +309,7 @@ __device__ __forceinline__ void matvec_rows(const GroupArgs& a, const LayerArgs&
 #pragma unroll
       for (int k = 0; k < CPC; ++k) sx += xv[k];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < RPW; ++i) {
         float qx = 0.f;
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd) {
@@ -325,7 +328,7 @@ __device__ __forceinline__ void matvec_rows(const GroupArgs& a, const LayerArgs&
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RPW; ++i)
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) acc[i] += __shfl_xor(acc[i], o);
 
@@ -333,7 +336,7 @@ __device__ __forceinline__ void matvec_rows(const GroupArgs& a, const LayerArgs&
     // y~ for the output-rotation kernel
     if (lane == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < RPW; ++i)
         if (wr0 + i < rows) L.y[rw0 + wr0 + i] = acc[i];
     }
     return;
@@ -342,7 +345,7 @@ __device__ __forceinline__ void matvec_rows(const GroupArgs& a, const LayerArgs&
   //    Had_b[j][k] = (-1)^popcount(j & k)
   if (lane == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) yloc[wr0 + i] = acc[i];
+    for (int i = 0; i < RPW; ++i) yloc[wr0 + i] = acc[i];
   }
   __syncthreads();
   if (t < rows) {
@@ -359,18 +362,20 @@ __device__ __forceinline__ void matvec_rows(const GroupArgs& a, const LayerArgs&
   }
 }
 
-// One workgroup per 16 rows of every layer of the call.  W: 4 or 2 when every layer of the
+// One workgroup per 4 RPW rows of every layer of the call.  W: 4 or 2 when every layer of the
 // call has codes of that width, 0 for a mix (both bodies compiled in, more registers).
-template <int W, int MC, int B>
+// RPW = 8 halves the workgroups (and the input transforms) of calls with more row tiles
+// than the device holds at once, so they run in one round.
+template <int W, int MC, int B, int RPW>
 __global__ __launch_bounds__(DT) void deploy_matvec_kernel(GroupArgs a) {
   extern __shared__ __attribute__((aligned(16))) float xs[];
   const int l = layer_of(a, blockIdx.x, false);
   const LayerArgs& L = a.L[l];
-  const int rw0 = ((int)blockIdx.x - L.wg0) * DR;
+  const int rw0 = ((int)blockIdx.x - L.wg0) * 4 * RPW;
   if (W == 4 || (W == 0 && L.bits == 4))
-    matvec_rows<4, MC, B>(a, L, rw0, xs);
+    matvec_rows<4, MC, B, RPW>(a, L, rw0, xs);
   else
-    matvec_rows<2, MC, B>(a, L, rw0, xs);
+    matvec_rows<2, MC, B, RPW>(a, L, rw0, xs);
 }
 
 // y[s0 .. s0 + n) <- S_out . Had_b(y~) / sqrt(b) / d_out over a segment (whole blocks,
@@ -439,7 +444,7 @@ kq_status deploy_group(const kq_deploy_layer* layers, int nl, int64_t in, const 
   a.x = x;
   a.nl = nl;
   a.in = (int)in;
-  int64_t chunk = 0, wg = 0, sg = 0, nck = 0;
+  int64_t chunk = 0, wg = 0, sg = 0, nck = 0, tiles16 = 0;
   int wmask = 0;   // 1: some layer has 4-bit codes; 2: some layer has 2-bit codes
   for (int l = 0; l < nl; ++l) {
     const kq_deploy_layer& q = layers[l];
@@ -462,8 +467,7 @@ kq_status deploy_group(const kq_deploy_layer* layers, int nl, int64_t in, const 
     L.isb_out = (float)(1.0 / sqrt((double)bout));
     // exact for every code position below 2^16 (the LDS limit keeps in below that)
     L.gmagic = (unsigned)(((1ull << 32) + (unsigned)q.group - 1) / (unsigned)q.group);
-    L.wg0 = (int)wg;
-    wg += ceil_div(q.out, DR);
+    tiles16 += ceil_div(q.out, 16);
     L.seg = (int)std::max<int64_t>(bout, SEG);
     L.sg0 = (int)sg;
     if (bout > DR) sg += ceil_div(q.out, L.seg);
@@ -480,18 +484,29 @@ kq_status deploy_group(const kq_deploy_layer* layers, int nl, int64_t in, const 
   hipStream_t s = as_stream(stream);
   // 16-byte chunks per lane and row: all of them in flight when they fit in MAXC
   const int mc = nck <= 2 ? 2 : nck <= 4 ? 4 : MAXC;
+  // 8 rows per wave when the 16-row tiles outnumber what the device holds at once (about
+  // four workgroups per CU) and the weights of 8 rows fit in registers
+  const int rpw = (tiles16 > 4 * (int64_t)device_cu_count() && mc <= 4) ? 8 : 4;
+  for (int l = 0; l < nl; ++l) {
+    a.L[l].wg0 = (int)wg;
+    wg += ceil_div(a.L[l].out, 4 * rpw);
+  }
   const char* nm = "deploy_matvec_kernel";
   const unsigned grid = (unsigned)wg;
   kq_status st;
+#define KQ_MV4(W, M)                                                                         \
+  (b1 ? launch_with_lds(deploy_matvec_kernel<W, M, 1, 4>, grid, lds, s, a, nm)               \
+      : launch_with_lds(deploy_matvec_kernel<W, M, 2, 4>, grid, lds, s, a, nm))
+#define KQ_MV8(W, M)                                                                         \
+  (b1 ? launch_with_lds(deploy_matvec_kernel<W, M, 1, 8>, grid, lds, s, a, nm)               \
+      : launch_with_lds(deploy_matvec_kernel<W, M, 2, 8>, grid, lds, s, a, nm))
 #define KQ_MV(W)                                                                             \
-  (b1 ? (mc == 2 ? launch_with_lds(deploy_matvec_kernel<W, 2, 1>, grid, lds, s, a, nm)        \
-         : mc == 4 ? launch_with_lds(deploy_matvec_kernel<W, 4, 1>, grid, lds, s, a, nm)      \
-                   : launch_with_lds(deploy_matvec_kernel<W, MAXC, 1>, grid, lds, s, a, nm))  \
-      : (mc == 2 ? launch_with_lds(deploy_matvec_kernel<W, 2, 2>, grid, lds, s, a, nm)        \
-         : mc == 4 ? launch_with_lds(deploy_matvec_kernel<W, 4, 2>, grid, lds, s, a, nm)      \
-                   : launch_with_lds(deploy_matvec_kernel<W, MAXC, 2>, grid, lds, s, a, nm)))
+  (rpw == 8 ? (mc == 2 ? KQ_MV8(W, 2) : KQ_MV8(W, 4))                                        \
+            : (mc == 2 ? KQ_MV4(W, 2) : mc == 4 ? KQ_MV4(W, 4) : KQ_MV4(W, MAXC)))
   st = wmask == 1 ? KQ_MV(4) : wmask == 2 ? KQ_MV(2) : KQ_MV(0);
 #undef KQ_MV
+#undef KQ_MV8
+#undef KQ_MV4
   if (st != KQ_OK || sg == 0) return st;
   const size_t lds2 = (size_t)padded_len(2 * 16 * DT) * sizeof(float);   // seg <= 8192
   return launch_with_lds(deploy_outrot_kernel, (unsigned)sg, lds2, s, a, "deploy_outrot_kernel");

@@ -232,6 +232,9 @@ def _group_case(torch, rng, in_n, specs):
     (4096, [(11008, 4, 128, 0, 0), (11008, 4, 128, 0, 0)]),
     # eight layers of different heights
     (512, [(16 * (k + 1), 4 if k % 2 else 2, 128, 0, 0) for k in range(8)]),
+    # more 16-row tiles than the device holds at once: 32 rows per workgroup, a ragged last
+    # workgroup of 8 rows, output blocks of 8 rotated in the matvec kernel
+    (512, [(8200, 4, 128, 0, 0), (8200, 2, 128, 0, 0)]),
 ])
 def test_deploy_group_matches_oracle_and_single_calls(in_n, specs):
     torch = torch_cuda()
