@@ -36,18 +36,24 @@ constexpr int NT = 256;
 // ---------------------------------------------------------------------------
 // norms and rescale vectors
 // ---------------------------------------------------------------------------
-// colsum[i] += sum over a stripe of rows of W[r][i]^2   (colsum pre-zeroed)
+// colsum[i] += sum over a stripe of CS_ROWS rows of W[r][i]^2   (colsum pre-zeroed).  Every
+// row's load is issued before any is used (rows past the end are read at the last row and
+// count as zero, a select rather than a branch around the load).
+constexpr int CS_ROWS = 32;
 __global__ __launch_bounds__(NT) void col_sumsq_kernel(const float* __restrict__ W, int64_t out,
-                                                       int64_t in, int rows_per_block,
-                                                       float* __restrict__ colsum) {
+                                                       int64_t in, float* __restrict__ colsum) {
   const int64_t c = ((int64_t)blockIdx.x * NT + threadIdx.x) * 4;
   if (c >= in) return;
-  const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
-  const int64_t r1 = min(out, r0 + rows_per_block);
+  const int64_t r0 = (int64_t)blockIdx.y * CS_ROWS;
+  float4 v[CS_ROWS];
+#pragma unroll
+  for (int k = 0; k < CS_ROWS; ++k) v[k] = *(const float4*)(W + min(r0 + k, out - 1) * in + c);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int64_t r = r0; r < r1; ++r) {
-    float4 v = *(const float4*)(W + r * in + c);
-    acc.x += v.x * v.x; acc.y += v.y * v.y; acc.z += v.z * v.z; acc.w += v.w * v.w;
+#pragma unroll
+  for (int k = 0; k < CS_ROWS; ++k) {
+    const float m = r0 + k < out ? 1.f : 0.f;
+    acc.x += m * v[k].x * v[k].x; acc.y += m * v[k].y * v[k].y;
+    acc.z += m * v[k].z * v[k].z; acc.w += m * v[k].w * v[k].w;
   }
   atomicAdd(colsum + c + 0, acc.x);
   atomicAdd(colsum + c + 1, acc.y);
@@ -103,34 +109,75 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, OOB, 0x00020000);
 }
 
-// out[k] = scale_at(s, i0 + o[k]) for K indices, with every load issued before any is used
-// (a missing vector is read at an out-of-range offset, which returns 0).  The descriptor
-// base i0 must be the same for the whole wave; o[k] is the lane's offset (< 2^29).
-template <int K>
-__device__ __forceinline__ void scales_nb(const Scale& s, int64_t i0, const int (&o)[K],
-                                          float (&out)[K]) {
+// Branch-free (a branch here would let the compiler sink loads issued before it past it):
+// mul * d, mul / d or mul from the raw d word, negated when the sign bit is set.
+__device__ __forceinline__ float factor_of(const Scale& s, unsigned dword, bool neg) {
+  const bool hd = s.d != nullptr, hs = s.sign != nullptr;
+  const bool mul_d = hd && !s.invert, div_d = hd && s.invert;
+  const float d = __uint_as_float(dword);
+  const float v = (s.mul * (mul_d ? d : 1.f)) / (div_d ? d : 1.f);
+  return hs && neg ? -v : v;
+}
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// The factors of the 16 consecutive entries i0 + c .. i0 + c + 15 (c a multiple of 16): four
+// 16-byte loads of d and one of the signs (a missing vector is read out of range, as 0).
+struct ScaleLoads16 {
+  u32x4 d[4];
+  u32x4 g;
+};
+
+__device__ __forceinline__ void scales16_issue(const Scale& s, int64_t i0, int c,
+                                               ScaleLoads16& L) {
   const bool hd = s.d != nullptr, hs = s.sign != nullptr;
   const __amdgpu_buffer_rsrc_t rd = rsrc(hd ? s.d + i0 : s.d), rg = rsrc(hs ? s.sign + i0 : s.sign);
-  float d[K];
-  int g[K];
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    d[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, hd ? 4 * o[k] : OOB, 0, 0));
-    g[k] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(rg, hs ? o[k] : OOB, 0, 0);
+  for (int q = 0; q < 4; ++q)
+    L.d[q] = __builtin_amdgcn_raw_buffer_load_b128(rd, hd ? 4 * (c + 4 * q) : OOB, 0, 0);
+  L.g = __builtin_amdgcn_raw_buffer_load_b128(rg, hs ? c : OOB, 0, 0);
+}
+
+__device__ __forceinline__ void scales16_form(const Scale& s, const ScaleLoads16& L,
+                                              float (&out)[16]) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    out[k] = factor_of(s, L.d[k >> 2][k & 3], ((L.g[k >> 2] >> (8 * (k & 3) + 7)) & 1u) != 0);
+}
+
+// The factors of R consecutive rows r0 .. r0 + R - 1 (rows at or past `rows` get any value):
+// one word of d and the word holding the sign byte per row.  The sign words are read at
+// 4-byte-aligned offsets within the vector, whose length is a multiple of 4, so no read
+// passes its end.  Raw words: their use comes after the other loads have been issued.
+template <int R>
+struct RowLoads {
+  unsigned d[R];
+  unsigned g[R];
+};
+
+template <int R>
+__device__ __forceinline__ void rows_issue(const Scale& s, int64_t r0, int64_t rows,
+                                          RowLoads<R>& L) {
+  const bool hd = s.d != nullptr, hs = s.sign != nullptr;
+  const __amdgpu_buffer_rsrc_t rd = rsrc(hd ? s.d + r0 : s.d);
+  const __amdgpu_buffer_rsrc_t rg = rsrc(hs ? s.sign + (r0 & ~(int64_t)3) : s.sign);
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const bool ok = r0 + k < rows;
+    const int rel = (int)(r0 & 3) + k;
+    L.d[k] = __builtin_amdgcn_raw_buffer_load_b32(rd, hd && ok ? 4 * k : OOB, 0, 0);
+    L.g[k] = __builtin_amdgcn_raw_buffer_load_b32(rg, hs && ok ? (rel & ~3) : OOB, 0, 0);
   }
+}
+
+template <int R>
+__device__ __forceinline__ void rows_form(const Scale& s, int64_t r0, const RowLoads<R>& L,
+                                          float (&out)[R]) {
 #pragma unroll
-  for (int k = 0; k < K; ++k) out[k] = s.mul;
-  if (hd) {
-    if (s.invert) {
-#pragma unroll
-      for (int k = 0; k < K; ++k) out[k] = out[k] / d[k];
-    } else {
-#pragma unroll
-      for (int k = 0; k < K; ++k) out[k] = out[k] * d[k];
-    }
+  for (int k = 0; k < R; ++k) {
+    const int rel = (int)(r0 & 3) + k;
+    out[k] = factor_of(s, L.d[k], ((L.g[k] >> (8 * (rel & 3) + 7)) & 1u) != 0);
   }
-#pragma unroll
-  for (int k = 0; k < K; ++k) out[k] = hs && g[k] < 0 ? -out[k] : out[k];
 }
 
 __device__ __forceinline__ float scale_at(const Scale& s, int64_t i) {
@@ -238,62 +285,62 @@ __global__ __launch_bounds__(NT) void row_fwht_kernel(const float* __restrict__ 
 //   round B: x = (t & 15) + 16 i + 256 (t >> 4)
 //   round C: x = t + 256 i    (bits 8-11; a wave stores 64 consecutive values per i)
 // LDS index x + (x >> 4) keeps the round A writes and round B accesses free of bank conflicts.
+// The loads of all R rows are issued at the start (after the scale loads, which are shared
+// by every workgroup and come from the cache): a row's transform is short next to the memory
+// latency under full load, so a workgroup that fetched one row ahead would wait on every row.
 // The thread's 16 column scales are formed once and reused for the workgroup's R rows.
 constexpr int RB = 4096;
 template <int R>
 __global__ __launch_bounds__(NT) void row_fwht4096_kernel(const float* __restrict__ src,
                                                           float* __restrict__ dst, int64_t rows,
                                                           int64_t n, Scale rs, Scale cs) {
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   __shared__ float sm[RB + RB / 16];
   const int t = threadIdx.x;
   const int64_t nb = n / RB;
   const int64_t cb = blockIdx.x % nb, r0 = (int64_t)(blockIdx.x / nb) * R;
   const int64_t c0 = cb * RB;
   float csc[16], rsv[R];
-  int oc[16], orow[R];
+  ScaleLoads16 lc;
+  RowLoads<R> lr;
+  scales16_issue(cs, c0, 16 * t, lc);
+  rows_issue<R>(rs, r0, rows, lr);
+  // every row's loads (rows past the end read 0), then the factors
+  u32x4 in[R][4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) oc[i] = 16 * t + i;
-#pragma unroll
-  for (int k = 0; k < R; ++k) orow[k] = r0 + k < rows ? k : 0;
-  scales_nb<16>(cs, c0, oc, csc);
-  scales_nb<R>(rs, r0, orow, rsv);
-  // row k's loads are issued while row k - 1 is transformed (rows past the end read 0)
-  u32x4 nxt[4];
-  auto load = [&](int64_t r) {
+  for (int k = 0; k < R; ++k) {
+    const int64_t r = r0 + k;
     const __amdgpu_buffer_rsrc_t rr = rsrc(src + (r < rows ? r : 0) * n + c0);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      nxt[j] = __builtin_amdgcn_raw_buffer_load_b128(rr, r < rows ? (16 * t + 4 * j) * 4 : OOB, 0, 0);
+      in[k][j] = __builtin_amdgcn_raw_buffer_load_b128(rr, r < rows ? (16 * t + 4 * j) * 4 : OOB, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  scales16_form(cs, lc, csc);
+  rows_form<R>(rs, r0, lr, rsv);
+  float v[16];
+  auto bfly = [&]() {
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if (e & m) continue;
+        const float a = v[e], c = v[e | m];
+        v[e] = a + c;
+        v[e | m] = a - c;
+      }
   };
-  load(r0);
-#pragma unroll 1
+#pragma unroll
   for (int k = 0; k < R; ++k) {
     const int64_t r = r0 + k;
-    float v[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[4 * j] = __uint_as_float(nxt[j].x); v[4 * j + 1] = __uint_as_float(nxt[j].y);
-      v[4 * j + 2] = __uint_as_float(nxt[j].z); v[4 * j + 3] = __uint_as_float(nxt[j].w);
+      v[4 * j] = __uint_as_float(in[k][j].x); v[4 * j + 1] = __uint_as_float(in[k][j].y);
+      v[4 * j + 2] = __uint_as_float(in[k][j].z); v[4 * j + 3] = __uint_as_float(in[k][j].w);
     }
-    if (k + 1 < R) load(r + 1);
-    float rsc = rsv[0];
 #pragma unroll
-    for (int kk = 1; kk < R; ++kk) rsc = kk == k ? rsv[kk] : rsc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] *= rsc * csc[i];
-    auto bfly = [&]() {
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          if (e & m) continue;
-          const float a = v[e], c = v[e | m];
-          v[e] = a + c;
-          v[e | m] = a - c;
-        }
-    };
+    for (int i = 0; i < 16; ++i) v[i] *= rsv[k] * csc[i];
     bfly();
+    if (k > 0) __syncthreads();   // the previous row's round C reads of sm are done
 #pragma unroll
     for (int i = 0; i < 16; ++i) sm[17 * t + i] = v[i];   // x = 16 t + i
     __syncthreads();
@@ -321,7 +368,6 @@ __global__ __launch_bounds__(NT) void row_fwht4096_kernel(const float* __restric
     for (int i = 0; i < 16; ++i)
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[i]), rd,
                                             r < rows ? (t + 256 * i) * 4 : OOB, 0, 0);
-    __syncthreads();   // the next row reuses sm
   }
 }
 
@@ -449,16 +495,16 @@ kq_status row_transform(const float* src, float* dst, int64_t rows, int64_t n, i
     return KQ_OK;
   }
   if (b == RB) {
-    // about four workgroups per CU on a 256-CU device, at most 16 rows each
+    // rows per workgroup: all of a workgroup's loads are in flight at once, four rows (64 KB)
+    // at most; about four workgroups per CU on a 256-CU device
     const int64_t nb = n / RB;
-    int64_t rpw = (rows * nb) / 1024;
-    rpw = rpw < 1 ? 1 : (rpw > 16 ? 16 : rpw);
-    const int R = rpw >= 16 ? 16 : rpw >= 8 ? 8 : rpw >= 4 ? 4 : rpw >= 2 ? 2 : 1;
+    const int64_t rpw = (rows * nb) / 1024;
+    const int R = rpw >= 4 ? 4 : rpw >= 2 ? 2 : 1;
     const dim3 grid((unsigned)(nb * ceil_div(rows, R)));
     switch (R) {
 #define KQ_R4096(X) \
   case X: row_fwht4096_kernel<X><<<grid, dim3(NT), 0, s>>>(src, dst, rows, n, rs, cs); break;
-      KQ_R4096(1) KQ_R4096(2) KQ_R4096(4) KQ_R4096(8) KQ_R4096(16)
+      KQ_R4096(1) KQ_R4096(2) KQ_R4096(4)
 #undef KQ_R4096
     }
     KQ_LAUNCHED("row_fwht4096_kernel");
@@ -534,9 +580,8 @@ extern "C" kq_status kq_biip_rotate(const float* W_src, float* W_dst, int64_t ou
   // 1. rescale vectors (norms of the original W, diagonals of the raw factors)
   if (rescale && do_in) {
     KQ_TRY(fill_f32(d_in, in, 0.f, s));
-    const int rpb = 64;
-    dim3 grid((unsigned)ceil_div(in / 4, NT), (unsigned)ceil_div(out, rpb));
-    col_sumsq_kernel<<<grid, dim3(NT), 0, s>>>(W_src, out, in, rpb, d_in);
+    dim3 grid((unsigned)ceil_div(in / 4, NT), (unsigned)ceil_div(out, CS_ROWS));
+    col_sumsq_kernel<<<grid, dim3(NT), 0, s>>>(W_src, out, in, d_in);
     KQ_LAUNCHED("col_sumsq_kernel");
     rescale_kernel<<<dim3((unsigned)ceil_div(in, 256)), dim3(256), 0, s>>>(HX_src, in, d_in, alpha);
     KQ_LAUNCHED("rescale_kernel");

@@ -544,7 +544,9 @@ __global__ void zero_lower_tiles(float* __restrict__ H, int64_t ldh, int n) {
   for (int c = threadIdx.x; c < cend; c += blockDim.x) p[c] = 0.0f;
 }
 
-// H[i][j] = H[j][i] for i < j, in 64 x 64 tiles through LDS.
+// H[i][j] = H[j][i] for i < j, in 64 x 64 tiles through LDS.  A thread's 16 loads are issued
+// before any is used: indices are clamped into the matrix (a branch around a load would make
+// the compiler wait for it), and only entries inside the matrix are stored.
 __global__ __launch_bounds__(256) void mirror_lower_to_upper(float* __restrict__ H, int64_t ldh,
                                                              int n, int m) {
   __shared__ float t[64][65];
@@ -553,13 +555,20 @@ __global__ __launch_bounds__(256) void mirror_lower_to_upper(float* __restrict__
   while (idx >= m - ti) { idx -= m - ti; ++ti; }
   const int tj = ti + idx;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  // read source tile (tj, ti) of the lower part: rows tj*64.., cols ti*64..
-  for (int r = ty; r < 64; r += 4) {
-    const int gi = tj * 64 + r, gj = ti * 64 + tx;
-    if (gi < n && gj < n) t[r][tx] = H[(int64_t)gi * ldh + gj];
+  // source tile (tj, ti) of the lower part: rows tj*64.., cols ti*64..
+  float v[16];
+  const int sj = min(ti * 64 + tx, n - 1);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int si = min(tj * 64 + ty + 4 * k, n - 1);
+    v[k] = H[(int64_t)si * ldh + sj];
   }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) t[ty + 4 * k][tx] = v[k];
   __syncthreads();
-  for (int r = ty; r < 64; r += 4) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = ty + 4 * k;
     const int gi = ti * 64 + r, gj = tj * 64 + tx;  // destination (upper)
     if (gi < n && gj < n && gi < gj) H[(int64_t)gi * ldh + gj] = t[tx][r];
   }

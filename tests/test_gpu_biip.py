@@ -47,7 +47,8 @@ def run_gpu_biip(W, HX, HG, s_in, s_out, alpha, mode, bin_, bout, inplace=False)
 @pytest.mark.parametrize("out_n,in_n,bin_,bout", [(256, 256, 256, 256), (96, 768, 256, 32),
                                                   (512, 1024, 1024, 512), (64, 2048, 2048, 16),
                                                   (40, 4096, 0, 8), (24, 8192, 8192, 4),
-                                                  (48, 1536, 0, 0), (16, 8192, 4096, 16)])
+                                                  (48, 1536, 0, 0), (16, 8192, 4096, 16),
+                                                  (2048, 4096, 0, 16)])
 def test_biip_matches_oracle(mode, out_n, in_n, bin_, bout):
     announce(f"biip {mode} out={out_n} in={in_n} b=({bin_},{bout})")
     rng = np.random.default_rng(out_n * 7 + in_n)
