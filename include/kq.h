@@ -118,6 +118,22 @@ kq_status kq_sensitivity(const float* HX, int64_t n_in, int64_t ldx, const float
                          int64_t n_out, int64_t ldg, double out3[3], void* stream);
 
 /*
+ * kq_sensitivity_async -- kq_sensitivity with its result left in device memory.
+ *
+ * Follows: the same passages as kq_sensitivity, and computes the same three values (the same
+ * reduction order, so bit-identical results).  Enqueues one kernel on `stream` and returns
+ * without synchronizing, so a caller that quantizes many layers in a row keeps the GPU busy
+ * and reads all sensitivities after its own synchronization.
+ *
+ *   HX, HG    as for kq_sensitivity
+ *   out3_dev  device, 3 doubles owned by the caller: {tr H_X, tr H_G, tr H_G * tr H_X},
+ *             written when the kernel runs
+ * Errors (NULL argument, bad sizes) are reported before anything is enqueued.
+ */
+kq_status kq_sensitivity_async(const float* HX, int64_t n_in, int64_t ldx, const float* HG,
+                               int64_t n_out, int64_t ldg, double* out3_dev, void* stream);
+
+/*
  * kq_biip_rotate -- bidirectional incoherence processing of one layer.
  *
  * Follows: KronQ README, opening section ("incoherence rotation + rescaling on

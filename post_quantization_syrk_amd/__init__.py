@@ -23,6 +23,7 @@ STATUS_NAMES = {0: "KQ_OK", 1: "KQ_EINVAL", 2: "KQ_ESHAPE", 3: "KQ_ENOTSPD", 4: 
                 5: "KQ_ENOTIMPL", 6: "KQ_EHIP"}
 
 EXPORTED = ("kq_version", "kq_last_error", "kq_accumulate_hessian", "kq_sensitivity",
+            "kq_sensitivity_async",
             "kq_biip_rotate", "kq_quantize_layer_workspace", "kq_quantize_layer",
             "kq_allocate_bits", "kq_deploy_linear", "kq_deploy_linear_group",
             "kq_flipflop_workspace", "kq_flipflop", "kq_quantize_two_sided_workspace",
@@ -60,6 +61,7 @@ _SIGS = {
     "kq_last_error": ([], ctypes.c_char_p),
     "kq_accumulate_hessian": ([_vp, _i64, _i64, _i64, _vp, _i64, _int, _vp], _int),
     "kq_sensitivity": ([_vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp], _int),
+    "kq_sensitivity_async": ([_vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp], _int),
     "kq_biip_rotate": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int,
                         _vp, _vp, _vp], _int),
     "kq_quantize_layer_workspace": ([ctypes.POINTER(QuantParams), _i64, _i64, _int,
@@ -165,6 +167,18 @@ def kq_sensitivity(HX, HG, stream=None) -> tuple[float, float, float]:
                             ctypes.cast(out, ctypes.c_void_p), _stream(stream))
     _check(st, "kq_sensitivity")
     return out[0], out[1], out[2]
+
+
+def kq_sensitivity_async(HX, HG, out, stream=None) -> None:
+    """Traces and sensitivity into `out` (device float64, 3 entries); does not synchronize."""
+    torch = _torch()
+    lib = load_library()
+    if out.numel() < 3:
+        raise ValueError("kq_sensitivity_async: out needs 3 entries")
+    st = lib.kq_sensitivity_async(_dev_ptr(HX, "HX", (torch.float32,)), HX.shape[0], _ld(HX, "HX"),
+                                  _dev_ptr(HG, "HG", (torch.float32,)), HG.shape[0], _ld(HG, "HG"),
+                                  _dev_ptr(out, "out", (torch.float64,)), _stream(stream))
+    _check(st, "kq_sensitivity_async")
 
 
 def kq_biip_rotate(W_src, W_dst, HX_src, HX_dst, HG_src, HG_dst, sign_in, sign_out, d_in, d_out,

@@ -60,6 +60,10 @@ def test_sensitivity_rejects_bad_arguments_on_host():
     assert lib.kq_sensitivity(None, 4, 4, buf, 4, 4, ctypes.cast(out, ctypes.c_void_p), None) == kq.KQ_EINVAL
     assert lib.kq_sensitivity(buf, 4, 4, buf, 4, 4, None, None) == kq.KQ_EINVAL
     assert lib.kq_sensitivity(buf, 4, 3, buf, 4, 4, ctypes.cast(out, ctypes.c_void_p), None) == kq.KQ_ESHAPE
+    assert lib.kq_sensitivity_async(None, 4, 4, buf, 4, 4, buf, None) == kq.KQ_EINVAL
+    assert lib.kq_sensitivity_async(buf, 4, 4, buf, 4, 4, None, None) == kq.KQ_EINVAL
+    assert lib.kq_sensitivity_async(buf, 4, 4, buf, 0, 4, buf, None) == kq.KQ_ESHAPE
+    assert lib.kq_sensitivity_async(buf, 4, 4, buf, 4, 3, buf, None) == kq.KQ_ESHAPE
 
 
 def test_allocator_rejects_bad_arguments():

@@ -112,6 +112,11 @@ def test_c1_sensitivity_matches_oracle():
     assert s == pytest.approx(os_, rel=1e-5)
     # independent route: stream norms
     assert s == pytest.approx(o.stream_sq_norm(X) * o.stream_sq_norm(G), rel=1e-5)
+    # the device-memory variant: the same three values, bit for bit
+    dev = torch.full((3,), float("nan"), dtype=torch.float64, device="cuda")
+    kq.kq_sensitivity_async(HX, HG, dev)
+    torch.cuda.synchronize()
+    assert dev.cpu().tolist() == [tx, tg, s]
 
 
 @pytest.mark.slow
