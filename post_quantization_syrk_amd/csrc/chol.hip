@@ -548,15 +548,38 @@ __global__ __launch_bounds__(256) void pmat_kernel(float* __restrict__ F, int64_
   }
   const int64_t r0 = (int64_t)idx * 128, a0 = (int64_t)J * B, rows = min((int64_t)128, a0 - r0);
   const int t = threadIdx.x;
-  for (int q = t; q < 64 * 128; q += 256) {
-    const int c = q >> 7, r = q & 127;   // lanes along r: coalesced reads of Z^T rows
-    Za[r * LP + c] = r < rows ? F[(a0 + c) * n + r0 + r] : 0.0f;
-    if constexpr (B == 128) Zb[r * LP + c] = r < rows ? F[(a0 + 64 + c) * n + r0 + r] : 0.0f;
+  // lanes along r: coalesced reads of Z^T rows.  Batches of loads are issued before any is
+  // used: rows past `rows` are read at the last row and stored as zero (a select, not a
+  // branch around the load, which would make every load wait for the ones before it).
+  constexpr int NQ = 64 * 128 / 256;
+#pragma unroll
+  for (int q0 = 0; q0 < NQ; q0 += 8) {
+    float va[8], vb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = t + 256 * (q0 + i), c = q >> 7, r = q & 127;
+      const int64_t rr = r0 + min(r, (int)rows - 1);
+      va[i] = F[(a0 + c) * n + rr];
+      if constexpr (B == 128) vb[i] = F[(a0 + 64 + c) * n + rr];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = t + 256 * (q0 + i), c = q >> 7, r = q & 127;
+      Za[r * LP + c] = r < rows ? va[i] : 0.0f;
+      if constexpr (B == 128) Zb[r * LP + c] = r < rows ? vb[i] : 0.0f;
+    }
   }
   if constexpr (B == 128) {
-    for (int q = t; q < 64 * 64; q += 256) {
-      const int c = q >> 6, r = q & 63;
-      Zba[r * LP + c] = F[(a0 + 64 + c) * n + a0 + r];
+    float vz[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int q = t + 256 * i, c = q >> 6, r = q & 63;
+      vz[i] = F[(a0 + 64 + c) * n + a0 + r];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int q = t + 256 * i, c = q >> 6, r = q & 63;
+      Zba[r * LP + c] = vz[i];
     }
   }
   __syncthreads();
