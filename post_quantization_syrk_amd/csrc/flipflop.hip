@@ -78,8 +78,17 @@ struct QArgs {
 
 // part[t, 2 jt + wc] = sum over the 128 outputs j of wave column wc of tile jt of
 // (sum_i U[j, i] S[t, i])^2.
+// Stage s of the ring: the operands of its first 16 contraction indices are in registers
+// (xa, xb); the second 16 (ya, yb) are read while the first are multiplied; then, once this
+// wave's copies of stage s+1 have landed and every wave's reads of stage s are done (one
+// barrier), stage s's buffer is refilled with stage s + QNST and the first operands of stage
+// s+1 are read while the second half of stage s is multiplied.  Each buffer is its own LDS
+// object, so the compiler can tell the reads of one stage from the copies into another.
 __global__ __launch_bounds__(256) void qform_kernel(QArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[QNST][QSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t b0[QSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t b1[QSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t b2[QSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t b3[QSTAGE];
   // workgroup u runs on XCD u mod 8; each XCD takes a contiguous range of tiles in
   // token-major order, so the 256 x k panel of one token tile stays in that XCD's L2 while
   // its output tiles pass
@@ -136,50 +145,77 @@ __global__ __launch_bounds__(256) void qform_kernel(QArgs a) {
       offS[h][b] = rs * QK + 8 * (c ^ qswz(rs));
       offU[h][b] = QPANEL + ru * QK + 8 * (c ^ qswz(ru));
     }
+  auto read = [&](const uint16_t* buf, int h, bf16x8 (&av)[4], bf16x8 (&bv)[4]) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      av[b] = *(const bf16x8*)(buf + offS[h][b]);
+      bv[b] = *(const bf16x8*)(buf + offU[h][b]);
+    }
+  };
 
   f32x16 acc[4][4];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int n = 0; n < 4; ++n) acc[m][n] = f32x16{};
+  auto mma = [&](const bf16x8 (&av)[4], const bf16x8 (&bv)[4]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[m], bv[n], acc[m][n], 0, 0, 0);
+  };
 
-#pragma unroll
-  for (int s = 0; s < QNST; ++s) issue(s, ring[s]);
-
-  for (int s0 = 0; s0 < nst_round; s0 += QNST) {
-#pragma unroll
-    for (int r = 0; r < QNST; ++r) {
-      const int s = s0 + r;
-      uint16_t* buf = ring[r];
-      // this wave's copies of stage s have landed once at most the later stages' remain
-      __builtin_amdgcn_s_waitcnt(wait_vm(2 * QCOPIES * (QNST - 1)));
-      lds_barrier();
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        bf16x8 av[4], bv[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          av[b] = *(const bf16x8*)(buf + offS[h][b]);
-          bv[b] = *(const bf16x8*)(buf + offU[h][b]);
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int n = 0; n < 4; ++n)
-            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[m], bv[n], acc[m][n], 0, 0, 0);
-      }
-      lds_barrier();
-      issue(s + QNST, buf);
-    }
+  bf16x8 xa[4], xb[4], ya[4], yb[4];
+  issue(0, b0);
+  issue(1, b1);
+  issue(2, b2);
+  issue(3, b3);
+  // this wave's copies of stage 0 have landed once at most those of stages 1..3 remain
+  __builtin_amdgcn_s_waitcnt(wait_vm(2 * QCOPIES * (QNST - 1)));
+  lds_barrier();
+  read(b0, 0, xa, xb);
+#define KQ_QF_STEP(J, CUR, NXT)                                    \
+  {                                                                \
+    read(CUR, 1, ya, yb);                                          \
+    mma(xa, xb);                                                   \
+    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {             \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);           \
+    }                                                              \
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);             \
+    __builtin_amdgcn_sched_barrier(0);                             \
+    __builtin_amdgcn_s_waitcnt(wait_vm(2 * QCOPIES * (QNST - 2))); \
+    __builtin_amdgcn_s_waitcnt(0xc07f);                            \
+    lds_barrier();                                                 \
+    issue(s0 + (J) + QNST, CUR);                                   \
+    read(NXT, 0, xa, xb);                                          \
+    mma(ya, yb);                                                   \
+    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {             \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);           \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);           \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);           \
+    }                                                              \
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);             \
+    __builtin_amdgcn_sched_barrier(0);                             \
   }
-  // the ring's trailing copies (zeros) must land before the LDS is reused
+  for (int s0 = 0; s0 < nst_round; s0 += QNST) {
+    KQ_QF_STEP(0, b0, b1)
+    KQ_QF_STEP(1, b1, b2)
+    KQ_QF_STEP(2, b2, b3)
+    KQ_QF_STEP(3, b3, b0)
+  }
+#undef KQ_QF_STEP
+  // the ring's trailing copies (zeros) must land, and every wave's last reads be done, before
+  // the LDS is reused
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  __builtin_amdgcn_s_waitcnt(0xc07f);
   lds_barrier();
 
   // epilogue: lane holds output column l & 31 of each 32 x 32 block, rows
   // 8 (r / 4) + 4 (l / 32) + r % 4.  Sum the squares over the wave's 128 columns: over the
   // four column blocks in registers, then over the 32 lanes of a half-wave through LDS.
-  float* red = (float*)ring[wave];   // 128 x 33 floats
+  float* red = (float*)(wave == 0 ? b0 : wave == 1 ? b1 : wave == 2 ? b2 : b3);   // 128 x 33 floats
   const int l32 = lane & 31, rh = (lane >> 5) * 4;
 #pragma unroll
   for (int m = 0; m < 4; ++m)
