@@ -63,10 +63,11 @@ inline int64_t y_slots(int64_t out) {
 struct ColArgs {
   float* W;            // out x in: W0 (unprocessed columns) / errors e (processed columns)
   int64_t out, in;
-  float* Y;            // nsplit slices of out x B: partial corrections of the current block,
-                       // summed in slice order (D P = -E U)
-  int nsplit;          // slices written for this block (0: no correction)
+  float* Y;            // nsplit slices of out x (nblk B): partial corrections of the launch's
+                       // blocks from the columns before them, summed in slice order (D P = -E U)
+  int nsplit;          // slices written for this launch (0: no correction)
   int64_t ystride;     // floats between slices
+  int nblk;            // blocks of B columns per launch (1 or 2); row pitch of Y is nblk B
   float* D;            // out x in: W0 - Qhat of the processed columns
   const float* U;      // in x in: U_JJ in the diagonal B x B blocks
   const uint8_t* dead; // in
@@ -104,11 +105,13 @@ struct RowState {
   float el[CPL];   // errors e_j once quantized
   float dl[CPL];   // W0_j - qhat_j once quantized
   float ql[CPL];   // codes once quantized
+  float corr[CPL]; // next block's feedback from this block's W0 - qhat, as it forms
   float s, inv, z; // grid of the current group
 };
 
 struct StepCtx {
   const float* Cb;  // LDS: B x B in-block U (zero on and below the diagonal)
+  const float* Pb;  // LDS: B x B feedback factor into the next block (CORR steps only)
   int q;            // lane within the row
   bool live;
   int64_t r, j0;
@@ -124,7 +127,8 @@ struct Ahead {
 };
 
 // One column j of the block (all compile-time indices, so every array stays in registers).
-template <int B, int G, int J>
+// CORR: also accumulate the next block's feedback, corr += (W0_j - qhat_j) P[j, next block].
+template <int B, int G, bool CORR, int J>
 __device__ __forceinline__ void gptq_step(RowState<B / LPR>& st, Ahead<B / LPR>& ah,
                                           const StepCtx& cx) {
   constexpr int CPL = B / LPR;
@@ -134,6 +138,12 @@ __device__ __forceinline__ void gptq_step(RowState<B / LPR>& st, Ahead<B / LPR>&
     const float* crow = cx.Cb + (J + 2) * B + 4 * cx.q;
 #pragma unroll
     for (int e = 0; e < CPL; e += 4) ah.u[(J + 2) % 3][e / 4] = *(const float4*)(crow + LPR * e);
+  }
+  float4 pj[CORR ? CPL / 4 : 1];
+  if constexpr (CORR) {
+    const float* prow = cx.Pb + J * B + 4 * cx.q;
+#pragma unroll
+    for (int e = 0; e < CPL; e += 4) pj[e / 4] = *(const float4*)(prow + LPR * e);
   }
   // keep those reads here (ALU work and LDS writes may still move across)
   __builtin_amdgcn_sched_barrier(0x607);
@@ -180,151 +190,202 @@ __device__ __forceinline__ void gptq_step(RowState<B / LPR>& st, Ahead<B / LPR>&
     st.w[e + 2] = fmaf(d, c.z, st.w[e + 2]);
     st.w[e + 3] = fmaf(d, c.w, st.w[e + 3]);
   }
+  if constexpr (CORR) {
+    // W0_j - qhat_j, the same on every lane of the row
+    const float dk = row_bcast<O>(st.w0[E]) - qh;
+#pragma unroll
+    for (int e = 0; e < CPL; e += 4) {
+      st.corr[e] = fmaf(dk, pj[e / 4].x, st.corr[e]);
+      st.corr[e + 1] = fmaf(dk, pj[e / 4].y, st.corr[e + 1]);
+      st.corr[e + 2] = fmaf(dk, pj[e / 4].z, st.corr[e + 2]);
+      st.corr[e + 3] = fmaf(dk, pj[e / 4].w, st.corr[e + 3]);
+    }
+  }
 }
 
-template <int B, int G, int... J>
+template <int B, int G, bool CORR, int... J>
 __device__ __forceinline__ void gptq_steps(RowState<B / LPR>& st, Ahead<B / LPR>& ah,
                                            const StepCtx& cx, std::integer_sequence<int, J...>) {
-  (gptq_step<B, G, J>(st, ah, cx), ...);
+  (gptq_step<B, G, CORR, J>(st, ah, cx), ...);
 }
 
 // 16 lanes per matrix row, each holding B/16 consecutive columns of the block.
 // Per column: the current weight of column j is broadcast from the owning lane,
 // every lane rounds it (same result), and every lane applies the feedback to its
 // own columns (the LDS copy of U is zero on and below the diagonal, so no masks).
-template <int B, int G>
+// A launch takes nblk (1 or 2) consecutive blocks.  The feedback product covers the
+// columns before the launch; the second block's feedback from the first, D_1 P[1, 2]
+// (D_1 = W0 - Qhat of the first block's columns), is accumulated column by column while
+// the first block is quantized (P[1, 2] in LDS next to U_11).
+// NBLK: the most blocks a launch takes (2 where the second block's state fits the registers
+// next to the first's, else 1).
+template <int B, int G, int NBLK>
 __global__ __launch_bounds__(CTHREADS) void gptq_block_kernel(ColArgs a, int64_t j0) {
   constexpr int CPL = B / LPR;
   __shared__ __attribute__((aligned(16))) float Cb[B * B];
   __shared__ float Ri[B];
+  __shared__ __attribute__((aligned(16))) float Pb[NBLK > 1 ? B * B : 4];
   const int t = threadIdx.x;
   const int q = t % LPR, rl = t / LPR;
   const int64_t r = (int64_t)blockIdx.x * RPW + rl;
   const bool live = r < a.out;
+  const int64_t ypitch = (int64_t)a.nblk * B;
+  // feedback into the current block from the launch's earlier block (zero for the first)
+  float corr[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) corr[e] = 0.f;
 
-  // All global loads first: U_JJ, its diagonal, this row's starting weights, feedback slices
-  // and dead flags.
-  constexpr int NIT = B * B / 4 / CTHREADS;
-  float4 uv[NIT];
+  const int nblk = NBLK > 1 ? a.nblk : 1;
+#pragma unroll 1
+  for (int b = 0; b < nblk; ++b) {
+    const int64_t jb = j0 + (int64_t)b * B;
+    // the first of two blocks also forms the second's feedback from its own columns
+    const bool corr_blk = NBLK > 1 && b + 1 < nblk;
+    // All global loads first: U_JJ (and P[1, 2]), its diagonal, this row's starting weights,
+    // feedback slices and dead flags.
+    constexpr int NIT = B * B / 4 / CTHREADS;
+    float4 uv[NIT], pv[NBLK > 1 ? NIT : 1];
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int idx = t + CTHREADS * it, i = idx / (B / 4), c = 4 * (idx % (B / 4));
-    uv[it] = *(const float4*)(a.U + (j0 + i) * a.in + j0 + c);
-  }
-  const int td = t < B ? t : B - 1;
-  const float udiag = a.U[(j0 + td) * a.in + j0 + td];
-  RowState<CPL> st;
-  const int64_t col = j0 + CPL * q;
-  float4 w0v[CPL / 4], yv[CPL / 4][YSLOTS];
-  uint32_t dv[CPL / 4];
-  // descriptor bases are per workgroup; the row goes into the lane's offset (r0 = first row)
-  const int64_t r0 = (int64_t)blockIdx.x * RPW;
-  const __amdgpu_buffer_rsrc_t rw = rsrc(a.W + r0 * a.in + j0);
-#pragma unroll
-  for (int e = 0; e < CPL; e += 4) {
-    w0v[e / 4] = bload4(rw, live ? (int)(((r - r0) * a.in + CPL * q + e) * 4) : OOB);
-    dv[e / 4] = *(const uint32_t*)(a.dead + col + e);
-    const int yoff = live ? (int)((r * B + CPL * q + e) * 4) : OOB;
-#pragma unroll
-    for (int sp = 0; sp < YSLOTS; ++sp)
-      yv[e / 4][sp] = bload4(rsrc(a.Y + sp * a.ystride), sp < a.nsplit ? yoff : OOB);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // LDS copy of U_JJ, chunk-interleaved: columns [CPL q + 4 h, +4) of row i sit at
-  // i * B + 4 (LPR h + q), so the 16 lanes of a row read 256 contiguous bytes per chunk;
-  // entries on and below the diagonal are zeroed.  Ri = 1 / diag(U_JJ).
-  if (t < B) Ri[t] = 1.0f / udiag;
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int idx = t + CTHREADS * it, i = idx / (B / 4), c = 4 * (idx % (B / 4));
-    float4 v = uv[it];
-    v.x = c + 0 > i ? v.x : 0.0f;
-    v.y = c + 1 > i ? v.y : 0.0f;
-    v.z = c + 2 > i ? v.z : 0.0f;
-    v.w = c + 3 > i ? v.w : 0.0f;
-    const int qq = c / CPL, hh = (c % CPL) / 4;
-    *(float4*)(Cb + i * B + 4 * (LPR * hh + qq)) = v;
-  }
-
-#pragma unroll
-  for (int e = 0; e < CPL; e += 4) {
-    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int sp = 0; sp < YSLOTS; ++sp) {
-      y.x += yv[e / 4][sp].x; y.y += yv[e / 4][sp].y; y.z += yv[e / 4][sp].z; y.w += yv[e / 4][sp].w;
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = t + CTHREADS * it, i = idx / (B / 4), c = 4 * (idx % (B / 4));
+      uv[it] = *(const float4*)(a.U + (jb + i) * a.in + jb + c);
     }
-    const float4 w0 = w0v[e / 4];
-    const uint32_t dd = dv[e / 4];
-    st.w0[e] = (dd & 0xffu) ? 0.f : w0.x;
-    st.w0[e + 1] = (dd & 0xff00u) ? 0.f : w0.y;
-    st.w0[e + 2] = (dd & 0xff0000u) ? 0.f : w0.z;
-    st.w0[e + 3] = (dd & 0xff000000u) ? 0.f : w0.w;
-    st.w[e] = st.w0[e] + y.x;
-    st.w[e + 1] = st.w0[e + 1] + y.y;
-    st.w[e + 2] = st.w0[e + 2] + y.z;
-    st.w[e + 3] = st.w0[e + 3] + y.w;
-    st.el[e] = st.el[e + 1] = st.el[e + 2] = st.el[e + 3] = 0.f;
-    st.dl[e] = st.dl[e + 1] = st.dl[e + 2] = st.dl[e + 3] = 0.f;
-    st.ql[e] = st.ql[e + 1] = st.ql[e + 2] = st.ql[e + 3] = 0.f;
-  }
-  st.s = 1.0f; st.inv = 1.0f; st.z = 0.0f;
-  if constexpr (G == 0) {  // one group per row: grid taken from the original row beforehand
-    if (live) {
-      st.s = a.scales[r];
-      st.inv = 1.0f / st.s;
-      st.z = (float)a.zeros[r];
+    if constexpr (NBLK > 1) {
+      // P rows jb .. jb + B, columns jb + B .. jb + 2B (F above the next diagonal block);
+      // read out of range (as 0, no branch around the loads) when there is no next block
+      const __amdgpu_buffer_rsrc_t rp = rsrc(a.U + jb * a.in + jb + B);
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int idx = t + CTHREADS * it, i = idx / (B / 4), c = 4 * (idx % (B / 4));
+        pv[it] = bload4(rp, corr_blk ? (int)((i * a.in + c) * 4) : OOB);
+      }
     }
-  }
-  __syncthreads();
-
-  StepCtx cx{Cb, q, live, r, j0, &a};
-  Ahead<CPL> ah;
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) ah.ri[i] = Ri[LPR * i + q];
-#pragma unroll
-  for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-    for (int e = 0; e < CPL; e += 4) ah.u[jj][e / 4] = *(const float4*)(Cb + jj * B + 4 * q + LPR * e);
-  gptq_steps<B, G>(st, ah, cx, std::make_integer_sequence<int, B>{});
-
-  // Pack the row's B codes into bits * B / 32 whole words starting at word j0 * bits / 32.
-  // Lane q's CPL codes form one field of CPL * bits <= 32 bits at bit CPL * bits * q of the
-  // row's code stream; word w (bits [32 w, 32 w + 32)) is gathered from the fields of the at
-  // most five lanes that reach into it, placed in a 64-bit window 32 bits up so that every
-  // shift is non-negative.
-  uint32_t f = 0;
-#pragma unroll
-  for (int e = 0; e < CPL; ++e) f |= (uint32_t)st.ql[e] << (e * a.bits);
-  const int fbits = CPL * a.bits;
-  const int qa = (32 * q) / fbits;
-  uint32_t fk[5];
-#pragma unroll
-  for (int k = 0; k < 5; ++k) fk[k] = __shfl(f, qa + k < LPR ? qa + k : LPR - 1, LPR);
-  uint64_t word = 0;
-#pragma unroll
-  for (int k = 0; k < 5; ++k) {
-    const int off = (qa + k) * fbits - 32 * q;
-    const bool use = qa + k < LPR && off < 32;
-    word |= (uint64_t)(use ? fk[k] : 0u) << (use ? off + 32 : 0);
-  }
-  if (live) {
-    const int64_t wpr = a.in * a.bits / 32;
-    if (a.packed && q < a.bits * B / 32)
-      a.packed[r * wpr + j0 * a.bits / 32 + q] = (uint32_t)(word >> 32);
-    if (a.codes) {
-#pragma unroll
-      for (int e = 0; e < CPL; e += 4)
-        *(uint32_t*)(a.codes + r * a.in + col + e) =
-            (uint32_t)st.ql[e] | ((uint32_t)st.ql[e + 1] << 8) | ((uint32_t)st.ql[e + 2] << 16) |
-            ((uint32_t)st.ql[e + 3] << 24);
-    }
-    // errors replace the processed weights; W0 - qhat goes to D
+    const int td = t < B ? t : B - 1;
+    const float udiag = a.U[(jb + td) * a.in + jb + td];
+    RowState<CPL> st;
+    const int64_t col = jb + CPL * q;
+    float4 w0v[CPL / 4], yv[CPL / 4][YSLOTS];
+    uint32_t dv[CPL / 4];
+    // descriptor bases are per workgroup; the row goes into the lane's offset (r0 = first row)
+    const int64_t r0 = (int64_t)blockIdx.x * RPW;
+    const __amdgpu_buffer_rsrc_t rw = rsrc(a.W + r0 * a.in + jb);
 #pragma unroll
     for (int e = 0; e < CPL; e += 4) {
-      *(float4*)(a.W + r * a.in + col + e) = make_float4(st.el[e], st.el[e + 1], st.el[e + 2], st.el[e + 3]);
-      *(float4*)(a.D + r * a.in + col + e) = make_float4(st.dl[e], st.dl[e + 1], st.dl[e + 2], st.dl[e + 3]);
+      w0v[e / 4] = bload4(rw, live ? (int)(((r - r0) * a.in + CPL * q + e) * 4) : OOB);
+      dv[e / 4] = *(const uint32_t*)(a.dead + col + e);
+      const int yoff = live ? (int)((r * ypitch + b * B + CPL * q + e) * 4) : OOB;
+#pragma unroll
+      for (int sp = 0; sp < YSLOTS; ++sp)
+        yv[e / 4][sp] = bload4(rsrc(a.Y + sp * a.ystride), sp < a.nsplit ? yoff : OOB);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // the previous block's readers of Cb and Ri are done
+    if (b > 0) __syncthreads();
+
+    // LDS copy of U_JJ, chunk-interleaved: columns [CPL q + 4 h, +4) of row i sit at
+    // i * B + 4 (LPR h + q), so the 16 lanes of a row read 256 contiguous bytes per chunk;
+    // entries on and below the diagonal are zeroed.  Ri = 1 / diag(U_JJ).
+    if (t < B) Ri[t] = 1.0f / udiag;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = t + CTHREADS * it, i = idx / (B / 4), c = 4 * (idx % (B / 4));
+      float4 v = uv[it];
+      v.x = c + 0 > i ? v.x : 0.0f;
+      v.y = c + 1 > i ? v.y : 0.0f;
+      v.z = c + 2 > i ? v.z : 0.0f;
+      v.w = c + 3 > i ? v.w : 0.0f;
+      const int qq = c / CPL, hh = (c % CPL) / 4;
+      *(float4*)(Cb + i * B + 4 * (LPR * hh + qq)) = v;
+      if constexpr (NBLK > 1) *(float4*)(Pb + i * B + 4 * (LPR * hh + qq)) = pv[it];
+    }
+
+#pragma unroll
+    for (int e = 0; e < CPL; e += 4) {
+      float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int sp = 0; sp < YSLOTS; ++sp) {
+        y.x += yv[e / 4][sp].x; y.y += yv[e / 4][sp].y; y.z += yv[e / 4][sp].z; y.w += yv[e / 4][sp].w;
+      }
+      const float4 w0 = w0v[e / 4];
+      const uint32_t dd = dv[e / 4];
+      st.w0[e] = (dd & 0xffu) ? 0.f : w0.x;
+      st.w0[e + 1] = (dd & 0xff00u) ? 0.f : w0.y;
+      st.w0[e + 2] = (dd & 0xff0000u) ? 0.f : w0.z;
+      st.w0[e + 3] = (dd & 0xff000000u) ? 0.f : w0.w;
+      st.w[e] = st.w0[e] + y.x + corr[e];
+      st.w[e + 1] = st.w0[e + 1] + y.y + corr[e + 1];
+      st.w[e + 2] = st.w0[e + 2] + y.z + corr[e + 2];
+      st.w[e + 3] = st.w0[e + 3] + y.w + corr[e + 3];
+      st.el[e] = st.el[e + 1] = st.el[e + 2] = st.el[e + 3] = 0.f;
+      st.corr[e] = st.corr[e + 1] = st.corr[e + 2] = st.corr[e + 3] = 0.f;
+      st.dl[e] = st.dl[e + 1] = st.dl[e + 2] = st.dl[e + 3] = 0.f;
+      st.ql[e] = st.ql[e + 1] = st.ql[e + 2] = st.ql[e + 3] = 0.f;
+    }
+    st.s = 1.0f; st.inv = 1.0f; st.z = 0.0f;
+    if constexpr (G == 0) {  // one group per row: grid taken from the original row beforehand
+      if (live) {
+        st.s = a.scales[r];
+        st.inv = 1.0f / st.s;
+        st.z = (float)a.zeros[r];
+      }
+    }
+    __syncthreads();
+
+    StepCtx cx{Cb, Pb, q, live, r, jb, &a};
+    Ahead<CPL> ah;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) ah.ri[i] = Ri[LPR * i + q];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int e = 0; e < CPL; e += 4) ah.u[jj][e / 4] = *(const float4*)(Cb + jj * B + 4 * q + LPR * e);
+    if (NBLK > 1 && corr_blk) {
+      gptq_steps<B, G, true>(st, ah, cx, std::make_integer_sequence<int, B>{});
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) corr[e] = st.corr[e];
+    } else {
+      gptq_steps<B, G, false>(st, ah, cx, std::make_integer_sequence<int, B>{});
+    }
+
+    // Pack the row's B codes into bits * B / 32 whole words starting at word jb * bits / 32.
+    // Lane q's CPL codes form one field of CPL * bits <= 32 bits at bit CPL * bits * q of the
+    // row's code stream; word w (bits [32 w, 32 w + 32)) is gathered from the fields of the at
+    // most five lanes that reach into it, placed in a 64-bit window 32 bits up so that every
+    // shift is non-negative.
+    uint32_t f = 0;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) f |= (uint32_t)st.ql[e] << (e * a.bits);
+    const int fbits = CPL * a.bits;
+    const int qa = (32 * q) / fbits;
+    uint32_t fk[5];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) fk[k] = __shfl(f, qa + k < LPR ? qa + k : LPR - 1, LPR);
+    uint64_t word = 0;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      const int off = (qa + k) * fbits - 32 * q;
+      const bool use = qa + k < LPR && off < 32;
+      word |= (uint64_t)(use ? fk[k] : 0u) << (use ? off + 32 : 0);
+    }
+    if (live) {
+      const int64_t wpr = a.in * a.bits / 32;
+      if (a.packed && q < a.bits * B / 32)
+        a.packed[r * wpr + jb * a.bits / 32 + q] = (uint32_t)(word >> 32);
+      if (a.codes) {
+#pragma unroll
+        for (int e = 0; e < CPL; e += 4)
+          *(uint32_t*)(a.codes + r * a.in + col + e) =
+              (uint32_t)st.ql[e] | ((uint32_t)st.ql[e + 1] << 8) | ((uint32_t)st.ql[e + 2] << 16) |
+              ((uint32_t)st.ql[e + 3] << 24);
+      }
+      // errors replace the processed weights; W0 - qhat goes to D
+#pragma unroll
+      for (int e = 0; e < CPL; e += 4) {
+        *(float4*)(a.W + r * a.in + col + e) = make_float4(st.el[e], st.el[e + 1], st.el[e + 2], st.el[e + 3]);
+        *(float4*)(a.D + r * a.in + col + e) = make_float4(st.dl[e], st.dl[e + 1], st.dl[e + 2], st.dl[e + 3]);
+      }
+    }
+
   }
 }
 
@@ -542,21 +603,24 @@ __global__ __launch_bounds__(256) void dot_kernel(const float* __restrict__ x,
 
 using ColKernel = void (*)(ColArgs, int64_t);
 
-ColKernel pick_kernel(int B, int G) {
+// The column kernel for block B and group G, and the most blocks it takes per launch.
+ColKernel pick_kernel(int B, int G, int* nblk) {
+  *nblk = 1;
   if (B == 64) {
+    *nblk = 2;
     switch (G) {
-      case 0: return gptq_block_kernel<64, 0>;
-      case 16: return gptq_block_kernel<64, 16>;
-      case 32: return gptq_block_kernel<64, 32>;
-      case 64: return gptq_block_kernel<64, 64>;
+      case 0: return gptq_block_kernel<64, 0, 2>;
+      case 16: return gptq_block_kernel<64, 16, 2>;
+      case 32: return gptq_block_kernel<64, 32, 2>;
+      case 64: return gptq_block_kernel<64, 64, 2>;
     }
   } else if (B == 128) {
     switch (G) {
-      case 0: return gptq_block_kernel<128, 0>;
-      case 16: return gptq_block_kernel<128, 16>;
-      case 32: return gptq_block_kernel<128, 32>;
-      case 64: return gptq_block_kernel<128, 64>;
-      case 128: return gptq_block_kernel<128, 128>;
+      case 0: *nblk = 2; return gptq_block_kernel<128, 0, 2>;
+      case 16: return gptq_block_kernel<128, 16, 1>;
+      case 32: return gptq_block_kernel<128, 32, 1>;
+      case 64: return gptq_block_kernel<128, 64, 1>;
+      case 128: *nblk = 2; return gptq_block_kernel<128, 128, 2>;
     }
   }
   return nullptr;
@@ -612,7 +676,7 @@ Layout layout(int64_t out, int64_t in, int B, bool with_loss, bool act_order) {
   size_t o = 0;
   L.f = o;    o = align256(o + (size_t)in * in * sizeof(float));
   L.t = o;    o = align256(o + (size_t)in * 128 * sizeof(float));
-  L.y = o;    o = align256(o + (size_t)y_slots(out) * out * B * sizeof(float));
+  L.y = o;    o = align256(o + (size_t)y_slots(out) * out * 2 * B * sizeof(float));
   L.d = o;    o = align256(o + (size_t)out * in * sizeof(float));
   L.dead = o; o = align256(o + (size_t)in);
   L.scal = o; o = align256(o + 8 * sizeof(double));
@@ -682,7 +746,8 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
   const Layout L = layout(out, in, B, with_loss, ao);
   if (!ws || ws_bytes < L.total)
     return fail(KQ_EWORKSPACE, "kq_quantize_layer: workspace of %zu bytes needed", L.total);
-  ColKernel kern = pick_kernel(B, G);
+  int max_blk = 1;
+  ColKernel kern = pick_kernel(B, G, &max_blk);
   if (!kern) return fail(KQ_ESHAPE, "no column kernel for block %d group %d", B, G);
   hipStream_t s = as_stream(stream);
   char* base = (char*)ws;
@@ -721,7 +786,7 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
 
   ColArgs a;
   a.W = Wq; a.out = out; a.in = in; a.Y = Y; a.D = Dm; a.U = F; a.dead = dead;
-  a.nsplit = 0; a.ystride = out * B;
+  a.nsplit = 0; a.ystride = out * B; a.nblk = 1;
   a.bits = p->bits; a.maxq = (float)((1 << p->bits) - 1);
   a.ngroups = in / p->group; a.scales = scales; a.zeros = zeros;
   a.packed = ao ? nullptr : packed; a.codes = ao ? ctmp : codes_opt;
@@ -733,24 +798,31 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
   }
   const int cus = device_cu_count();
   const unsigned col_grid = (unsigned)ceil_div(out, RPW);
-  for (int64_t j0 = 0; j0 < in; j0 += B) {
+  // two blocks per launch where the kernel takes them (it forms the second block's feedback
+  // from the first); a last odd block alone
+  for (int64_t j0 = 0; j0 < in; j0 += (int64_t)a.nblk * B) {
+    a.nblk = max_blk > 1 && j0 + 2 * B <= in ? 2 : 1;
+    const int64_t N = (int64_t)a.nblk * B;
+    a.ystride = out * N;
+    a.nsplit = 0;
     if (j0 > 0) {
       GemmArgs g{};
-      g.M = out; g.N = B; g.K = j0;
+      g.M = out; g.N = N; g.K = j0;
       g.A = Dm; g.lda = in; g.transA = false;
       g.B = F + j0; g.ldb = in; g.transB = false;
-      g.C = Y; g.ldc = B; g.alpha = 1.0f; g.accumulate = false; g.upper_only = false;
+      g.C = Y; g.ldc = N; g.alpha = 1.0f; g.accumulate = false; g.upper_only = false;
       // one workgroup per CU (the product keeps a 128 KB LDS ring): split K so that one round
       // of workgroups covers the GPU, down to one 32-deep stage per split; each split stores
-      // its own slice, which the column kernel sums
-      const int64_t tiles = ceil_div(out, 128);
+      // its own slice (out x N, as many as the workspace holds), which the column kernel sums
+      const int64_t tiles = ceil_div(out, 128) * ceil_div(N, 128);
       int64_t split = cus / tiles;
       const int64_t max_split = ceil_div(j0, 32);
       if (split > max_split) split = max_split;
-      if (split > y_slots(out)) split = y_slots(out);
+      const int64_t cap = std::min<int64_t>(YSLOTS, 2 * y_slots(out) / a.nblk);
+      if (split > cap) split = cap;
       if (split < 1) split = 1;
       g.split_k = (int)split;
-      g.partial_stride = out * B;
+      g.partial_stride = out * N;
       g.splits_used = &a.nsplit;
       KQ_TRY(gemm_f32(g, s));
     }
