@@ -78,50 +78,78 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // Leaf factorization, run by one wave: Ab (LDS, 64 x 64, row stride LB) holds the upper
 // triangle of a diagonal block A' (entries below the diagonal are ignored).  Factors
 // A' = R R^T from the last column up (R upper): lane l holds row l of A' (becoming row l of
-// R).  Step j: with column j of A' in registers (c[k] = A'_kj, from the other lanes),
-// p = A'_jj, R_jj = sqrt(p); A'_lk -= A'_lj A'_kj / p for k < j (every lane updates its whole
-// row; the lower part it also touches is never read); R_lj = A'_lj / R_jj goes to Rl and
-// 1 / R_jj to rsq.  Column j-1 is updated first and published through LDS (two buffers in
-// turn), and read back while the rest of the update runs.  Rl's entries below the diagonal
-// are left undefined.  Sets *flag on a non-positive pivot (the damped blocks' pivots are far
-// from the denormal range, so the hardware reciprocal square root is used as it is).
-__device__ __forceinline__ void leaf_factor(const float* Ab, float* Rl, float* col0, float* col1,
-                                            float* rsq, int* flag) {
+// R).  Column j: p = A'_jj, R_jj = sqrt(p), R_lj = A'_lj / R_jj, and A'_lk -= R_lj R_kj for
+// k < j.  The columns go in panels of 16 from the end: inside a panel the rank-1 updates
+// touch only the panel's columns (A'_kj from lane k with v_readlane, so no LDS round trip per
+// column), and after the panel the columns left of it take the panel's rank-16 update at once,
+// A'[<16p, <16p] -= R[<16p, P] R[<16p, P]^T, as v_mfma_f32_16x16x4f32 products through LDS
+// (Ab, read into registers first, is the scratch).  The same updates as column by column,
+// in another order.  Rl's entries below the diagonal are left undefined.  Sets *flag on a
+// non-positive pivot (the damped blocks' pivots are far from the denormal range, so the
+// hardware reciprocal square root is used as it is).
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ __forceinline__ void leaf_factor(float* Ab, float* Rl, float* rsq, int* flag) {
   const int l = threadIdx.x & 63;
-  float a[64], c[64];
+  const int r16 = l & 15, k4 = l >> 4;
+  float a[64];
 #pragma unroll
   for (int k = 0; k < 64; k += 4) {
     const float4 v = *(const float4*)(Ab + l * LB + k);
     a[k] = v.x; a[k + 1] = v.y; a[k + 2] = v.z; a[k + 3] = v.w;
   }
-  col1[l] = a[63];
   wave_sync();
-#pragma unroll
-  for (int k = 0; k < 64; ++k) c[k] = col1[k];
   bool bad = false;
+  float rs_own = 1.0f;   // 1 / R_ll, stored by lane l at the end
 #pragma unroll
-  for (int j = 63; j >= 0; --j) {
-    const float p = c[j];
-    const float rs = __builtin_amdgcn_rsqf(p);
-    const float f = a[j] * (rs * rs);
-    if (j > 0) {
-      float* colx = ((j - 1) & 1) ? col1 : col0;
-      a[j - 1] = fmaf(-f, c[j - 1], a[j - 1]);
-      colx[l] = a[j - 1];
-      wave_sync();
-      // the next pivot first, then the column from the end the next step starts at
-      c[j - 1] = colx[j - 1];
+  for (int p = 3; p >= 0; --p) {
+    const int lo = 16 * p;
 #pragma unroll
-      for (int k = j - 2; k >= 0; --k) {
-        a[k] = fmaf(-f, c[k], a[k]);
-        c[k] = colx[k];
-      }
+    for (int j = lo + 15; j >= lo; --j) {
+      // column j's entries in the panel's rows (uniform values), all read before they are
+      // used so that the reads go back to back into distinct scalar registers
+      float ck[16];
+#pragma unroll
+      for (int k = lo; k <= j; ++k) ck[k - lo] = lane_value(a[j], k);
+      const float pj = ck[j - lo];
+      const float rs = __builtin_amdgcn_rsqf(pj);
+      const float f = a[j] * (rs * rs);
+#pragma unroll
+      for (int k = j - 1; k >= lo; --k) a[k] = fmaf(-f, ck[k - lo], a[k]);
+      a[j] *= rs;
+      Rl[l * LB + j] = a[j];
+      rs_own = l == j ? rs : rs_own;
+      bad |= (l == j) & !(pj > 0.0f);
     }
-    a[j] *= rs;
-    Rl[l * LB + j] = a[j];
-    rsq[j] = rs;
-    bad |= (l == j) & !(p > 0.0f);
+    if (p > 0) {
+      wave_sync();
+      // delta = R[<lo, P] R[<lo, P]^T, 16 x 16 tiles (lt, kt) on and above the diagonal
+#pragma unroll
+      for (int lt = 0; lt < p; ++lt)
+#pragma unroll
+        for (int kt = lt; kt < p; ++kt) {
+          f32x4 acc = f32x4{};
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Rl[(16 * lt + r16) * LB + lo + 4 * s + k4],
+                                                       Rl[(16 * kt + r16) * LB + lo + 4 * s + k4],
+                                                       acc, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Ab[(16 * lt + 4 * k4 + i) * LB + 16 * kt + r16] = acc[i];
+        }
+      wave_sync();
+      // row l, columns k < lo (those below the diagonal, never computed, are never read)
+#pragma unroll
+      for (int k = 0; k < lo; k += 4) {
+        const float4 d = *(const float4*)(Ab + l * LB + k);
+        a[k] -= d.x; a[k + 1] -= d.y; a[k + 2] -= d.z; a[k + 3] -= d.w;
+      }
+      wave_sync();
+    }
   }
+  rsq[l] = rs_own;
   if (bad) atomicOr(flag, 1);
 }
 
@@ -242,9 +270,9 @@ __device__ __forceinline__ void bstore(float v, __amdgpu_buffer_rsrc_t r, int of
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
 
-// LDS for a leaf: X (64 x LB: A', then U) and Y (64 x LB for R, 64 + 64 for the column and
+// LDS for a leaf: X (64 x LB: A', the factor's scratch, then U) and Y (64 x LB for R, 64 for
 // 1 / R_jj, 32 x LB scratch).
-constexpr int LEAF_Y = 64 * LB + 128 + 32 * LB;
+constexpr int LEAF_Y = 64 * LB + 64 + 32 * LB;
 
 // Factor + invert the diagonal block held in X.  Writes U = R^-1 to Uout and
 // M = U^T U = A'^-1 to Mout (64 x 64 row-major each).  Every thread of the 256-thread
@@ -252,10 +280,9 @@ constexpr int LEAF_Y = 64 * LB + 128 + 32 * LB;
 __device__ __forceinline__ void leaf(float* X, float* Y, float* __restrict__ Uout,
                                      float* __restrict__ Mout, int* flag) {
   float* Rl = Y;
-  float* col = Y + 64 * LB;
-  float* rsq = col + 64;
-  float* Ts = rsq + 64;   // also the factor's second column buffer (Ts is used afterwards)
-  if (threadIdx.x < 64) leaf_factor(X, Rl, col, Ts, rsq, flag);
+  float* rsq = Y + 64 * LB;
+  float* Ts = rsq + 64;
+  if (threadIdx.x < 64) leaf_factor(X, Rl, rsq, flag);
   __syncthreads();
   leaf_inverse(Rl, rsq, X, Ts);
   // M = U^T U.  U is upper, so quadrant (I, J) of 32 x 32 sums only k < 32 max(I, J) + 32:
