@@ -105,7 +105,8 @@ __global__ __launch_bounds__(256) void ts_round_kernel(TSArgs a) {
   __shared__ float et[TS][TS + 1];    // scaled errors
   __shared__ uint8_t ct[TS][TS];      // codes
   __shared__ float ed[TS];            // errors of the current in-tile anti-diagonal, by row
-  __shared__ float srow[TS], zrow[TS];
+  __shared__ float srow[TS], zrow[TS], sinv[TS];
+  __shared__ float rug[TS], rux[TS];  // 1 / U_G[r][r], 1 / U_X[i][i] of the tile's rows, columns
   const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, kh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int tix = blockIdx.x;
@@ -146,8 +147,15 @@ __global__ __launch_bounds__(256) void ts_round_kernel(TSArgs a) {
     }
   }
   if (t < TS) {
-    srow[t] = a.scale[(int64_t)(r0 + t) * a.ng + g];
+    const float sc = a.scale[(int64_t)(r0 + t) * a.ng + g];
+    srow[t] = sc;
+    sinv[t] = 1.0f / sc;
     zrow[t] = (float)a.zero[(int64_t)(r0 + t) * a.ng + g];
+  }
+  __syncthreads();
+  if (t < TS) {
+    rug[t] = 1.0f / ugd[t][t];
+    rux[t] = 1.0f / uxd[t][t];
   }
   __syncthreads();
 
@@ -164,9 +172,9 @@ __global__ __launch_bounds__(256) void ts_round_kernel(TSArgs a) {
       float e = 0.f;
       if (i >= 0 && i < TS) {
         const float w = wt[t][i], s = srow[t], z = zrow[t];
-        const float q = fminf(fmaxf(rintf(w / s) + z, 0.f), (float)a.maxq);
+        const float q = fminf(fmaxf(rintf(w * sinv[t]) + z, 0.f), (float)a.maxq);
         const float qh = s * (q - z);
-        e = (w - qh) / (ugd[t][t] * uxd[i][i]);
+        e = (w - qh) * (rug[t] * rux[i]);
         et[t][i] = e;
         ct[t][i] = (uint8_t)q;
       }
