@@ -19,8 +19,20 @@ std::mutex g_trace_mutex;
 // then a fixed tree), out = {tr H_X, tr H_G, tr H_G * tr H_X}.
 __device__ __forceinline__ double diag_sum(const float* __restrict__ H, int64_t n, int64_t ld,
                                            double* red) {
+  // the same order as one entry at a time; eight loads in flight per thread (indices past n
+  // read the last entry and count as zero, a select rather than a branch around the load)
   double s = 0.0;
-  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) s += (double)H[i * ld + i];
+  for (int64_t i0 = threadIdx.x; i0 < n; i0 += 8 * (int64_t)blockDim.x) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t i = min(i0 + (int64_t)k * blockDim.x, n - 1);
+      v[k] = H[i * ld + i];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (i0 + (int64_t)k * blockDim.x < n) s += (double)v[k];
+  }
   red[threadIdx.x] = s;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
