@@ -144,6 +144,21 @@ def test_act_order_needs_one_grid_per_row():
         assert e.value.status == kq.KQ_ENOTIMPL
 
 
+@pytest.mark.parametrize("bits,group,block", [(4, 128, 128), (2, 64, 64), (3, 640, 128)])
+def test_quantize_block_pairs(bits, group, block):
+    """640 columns: two-block launches whose feedback product has columns before them, and a
+    last odd block alone (block 128); group 640 takes the one-grid-per-row kernel."""
+    announce(f"gptq block pairs bits={bits} group={group} block={block}")
+    rng = np.random.default_rng(bits * 1000 + group + block)
+    out_n, in_n = 72, 640
+    Wt = rng.standard_normal((out_n, in_n)) * 0.05
+    HXt = spd(rng, in_n, outliers=2).astype(np.float32).astype(np.float64)
+    HGt = spd(rng, out_n).astype(np.float32).astype(np.float64)
+    Wt = Wt.astype(np.float32).astype(np.float64)
+    g = gpu_quantize(Wt, HXt, HGt, bits, group, block)
+    check_against_oracle(g, Wt, HXt, HGt, bits, group)
+
+
 def test_quantize_without_hg_and_ragged_rows():
     announce("gptq no H_G, out=50")
     rng = np.random.default_rng(11)
