@@ -24,6 +24,8 @@
 // through U_ab = -U_a Z_b[a rows].
 #include "kq_internal.h"
 
+#include <stdlib.h>
+
 namespace kq {
 namespace {
 
@@ -336,6 +338,88 @@ __global__ __launch_bounds__(256) void leaf_kernel(const float* __restrict__ F, 
   leaf(X, Y, Uout, Mout, flag);
 }
 
+// Z = A12[I] M for one 128-row block: As (LDS, 128 x 64, sw layout) holds A12[I] on entry and
+// Z on return; wave w forms rows 32 w .. 32 w + 31, all 64 columns.  Every thread calls it.
+__device__ __forceinline__ void panel_z(float* As, const float* Ms) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, l32 = lane & 31, kh = lane >> 5;
+  f32x16 az[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    float av[16], bv[16][2];
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const int k = 32 * hh + 2 * kk + kh;
+      av[kk] = As[sw(32 * w + l32, k)];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bv[kk][j] = Ms[swb(k, 32 * j + l32)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        az[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[kk], bv[kk][j], az[j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) As[sw(32 * w + 8 * (r >> 2) + 4 * kh + (r & 3), 32 * j + l32)] = az[j][r];
+  __syncthreads();
+}
+
+// Z^T of rows i0 .. i0 + 128 (those below s0) into the free lower triangle:
+// F[s0 + c][i0 + i] = Z[i][c], Z in As.
+__device__ __forceinline__ void store_zt(float* __restrict__ F, int64_t n, int64_t s0, int64_t i0,
+                                         const float* As) {
+  const int t = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rz = rsrc(F + s0 * n + i0);
+  const int i = t & 127;
+#pragma unroll
+  for (int it = 0; it < 32; ++it) {
+    const int c = 2 * it + (t >> 7);
+    bstore(As[sw(i, c)], rz, i0 + i < s0 ? (c * (int)n + i) * 4 : OOB);
+  }
+}
+
+// The panel factor of a whole step at once, for steps whose update has many tiles: one
+// workgroup per 128-row block forms Z = A12 M and stores Z^T in the lower triangle, where the
+// update's tiles (and its leaf workgroup) then read it instead of each forming it again.
+// The same products in the same order as the tiles', so the factorization does not change.
+__global__ __launch_bounds__(256) void z_kernel(float* __restrict__ F, int64_t n, int64_t s0,
+                                                const float* __restrict__ Mcur) {
+  __shared__ __attribute__((aligned(16))) float As[128 * 64];
+  __shared__ __attribute__((aligned(16))) float Ms[64 * 64];
+  const int t = threadIdx.x;
+  const int64_t i0 = (int64_t)blockIdx.x * 128;
+  const __amdgpu_buffer_rsrc_t ra = rsrc(F + i0 * n + s0);
+  float4 va[8], mv[4];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int r = (t >> 4) + 16 * it, off = (r * (int)n + (t & 15) * 4) * 4;
+    va[it] = bload4(ra, i0 + r < s0 ? off : OOB);
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int q = t + 256 * it, r = q >> 4, c4 = (q & 15) * 4;
+    mv[it] = *(const float4*)(Mcur + r * 64 + c4);
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int q = t + 256 * it, r = q >> 4, c4 = (q & 15) * 4;
+    Ms[swb(r, c4)] = mv[it].x; Ms[swb(r, c4 + 1)] = mv[it].y; Ms[swb(r, c4 + 2)] = mv[it].z; Ms[swb(r, c4 + 3)] = mv[it].w;
+  }
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int r = (t >> 4) + 16 * it, c4 = (t & 15) * 4;
+    As[sw(r, c4)] = va[it].x; As[sw(r, c4 + 1)] = va[it].y; As[sw(r, c4 + 2)] = va[it].z; As[sw(r, c4 + 3)] = va[it].w;
+  }
+  __syncthreads();
+  panel_z(As, Ms);
+  store_zt(F, n, s0, i0, As);
+}
+
 // Step of the reverse factorization at block [s0, s0 + 64).  With A12 = F[0:s0, s0:s0+64]
 // (the current Schur complement's column block) and M = A22^-1 = U22^T U22 from the previous
 // step's leaf, the block's panel factor is Z = A12 M (= R12 U22 with R12 = A12 U22^T) and the
@@ -352,7 +436,7 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ F, i
                                                      const float* __restrict__ Mcur,
                                                      float* __restrict__ Unext,
                                                      float* __restrict__ Mnext,
-                                                     int* __restrict__ flag) {
+                                                     int* __restrict__ flag, int zpre) {
   __shared__ __attribute__((aligned(16))) float As[128 * 64];
   __shared__ __attribute__((aligned(16))) float Bs[128 * 64];
   __shared__ __attribute__((aligned(16))) float Ms[64 * 64];
@@ -374,17 +458,26 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ F, i
       As[sw(r, c4)] = v.x; As[sw(r, c4 + 1)] = v.y; As[sw(r, c4 + 2)] = v.z; As[sw(r, c4 + 3)] = v.w;
       *(float4*)(Bs + r * LB + c4) = *(const float4*)(F + (d0 + r) * n + d0 + c4);
     }
-    __syncthreads();
     const int wi = w >> 1, wj = w & 1;
-    // Z_D = A12[D] M into As rows 64..127
-    f32x16 acc = f32x16{};
+    if (zpre) {
+      // Z_D from the lower triangle, where this step's z_kernel left Z^T
+      for (int q = t; q < 64 * 64; q += 256) {
+        const int c = q >> 6, r = q & 63;
+        As[sw(64 + r, c)] = F[(s0 + c) * n + d0 + r];
+      }
+      __syncthreads();
+    } else {
+      __syncthreads();
+      // Z_D = A12[D] M into As rows 64..127
+      f32x16 acc = f32x16{};
 #pragma unroll 8
-    for (int k = 0; k < 64; k += 2)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[sw(32 * wi + l32, k + kh)],
-                                                 Ms[swb(k + kh, 32 * wj + l32)], acc, 0, 0, 0);
+      for (int k = 0; k < 64; k += 2)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[sw(32 * wi + l32, k + kh)],
+                                                   Ms[swb(k + kh, 32 * wj + l32)], acc, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) As[sw(64 + 32 * wi + 8 * (r >> 2) + 4 * kh + (r & 3), 32 * wj + l32)] = acc[r];
-    __syncthreads();
+      for (int r = 0; r < 16; ++r) As[sw(64 + 32 * wi + 8 * (r >> 2) + 4 * kh + (r & 3), 32 * wj + l32)] = acc[r];
+      __syncthreads();
+    }
     // D' = D - Z_D A12[D]^T
     f32x16 acc2 = f32x16{};
 #pragma unroll 8
@@ -410,60 +503,53 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ F, i
   // this lane's tile entries: rows rbase + 32 i + 8 (r / 4) + r % 4, columns cbase + 32 j
   const int64_t rbase = i0 + wm + 4 * kh, cbase = j0 + wn + l32;
   const int rlim = (int)min((int64_t)128, s0 - rbase), clim = (int)min((int64_t)128, s0 - cbase);
-  // A12[I] and A12[K] (rows past s0 read as 0): all loads first
-  const __amdgpu_buffer_rsrc_t ra = rsrc(F + i0 * n + s0), rb = rsrc(F + j0 * n + s0);
+  // A12[I] (or, with zpre, Z[I] from the lower triangle) and A12[K] (rows past s0 read as 0):
+  // all loads first
+  const __amdgpu_buffer_rsrc_t ra = zpre ? rsrc(F + s0 * n + i0) : rsrc(F + i0 * n + s0);
+  const __amdgpu_buffer_rsrc_t rb = rsrc(F + j0 * n + s0);
   float4 va[8], vb[8];
+  float vz[32];
+  if (zpre) {
+    // Z[I][r][c] = F[s0 + c][i0 + r]: lanes along r
+#pragma unroll
+    for (int it = 0; it < 32; ++it) {
+      const int c = 2 * it + (t >> 7), r = t & 127;
+      vz[it] = bload(ra, i0 + r < s0 ? (c * (int)n + r) * 4 : OOB);
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = (t >> 4) + 16 * it, off = (r * (int)n + (t & 15) * 4) * 4;
+      va[it] = bload4(ra, i0 + r < s0 ? off : OOB);
+    }
+  }
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int r = (t >> 4) + 16 * it, off = (r * (int)n + (t & 15) * 4) * 4;
-    va[it] = bload4(ra, i0 + r < s0 ? off : OOB);
     vb[it] = bload4(rb, j0 + r < s0 ? off : OOB);
   }
   __builtin_amdgcn_sched_barrier(0);
+  if (zpre) {
+#pragma unroll
+    for (int it = 0; it < 32; ++it) As[sw(t & 127, 2 * it + (t >> 7))] = vz[it];
+  } else {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = (t >> 4) + 16 * it, c4 = (t & 15) * 4;
+      As[sw(r, c4)] = va[it].x; As[sw(r, c4 + 1)] = va[it].y; As[sw(r, c4 + 2)] = va[it].z; As[sw(r, c4 + 3)] = va[it].w;
+    }
+  }
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int r = (t >> 4) + 16 * it, c4 = (t & 15) * 4;
-    As[sw(r, c4)] = va[it].x; As[sw(r, c4 + 1)] = va[it].y; As[sw(r, c4 + 2)] = va[it].z; As[sw(r, c4 + 3)] = va[it].w;
     Bs[sw(r, c4)] = vb[it].x; Bs[sw(r, c4 + 1)] = vb[it].y; Bs[sw(r, c4 + 2)] = vb[it].z; Bs[sw(r, c4 + 3)] = vb[it].w;
   }
   __syncthreads();
-  // Z[I] = A12[I] M: wave w forms rows 32 w .. 32 w + 31, all 64 columns
-  {
-    f32x16 az[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      float av[16], bv[16][2];
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk) {
-        const int k = 32 * hh + 2 * kk + kh;
-        av[kk] = As[sw(32 * w + l32, k)];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) bv[kk][j] = Ms[swb(k, 32 * j + l32)];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          az[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[kk], bv[kk][j], az[j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) As[sw(32 * w + 8 * (r >> 2) + 4 * kh + (r & 3), 32 * j + l32)] = az[j][r];
-    __syncthreads();
-  }
-  if (tm == tn) {
-    // Z^T of the tile's rows into the lower triangle: F[s0 + c][i0 + i] = Z[i][c]
-    const __amdgpu_buffer_rsrc_t rz = rsrc(F + s0 * n + i0);
-    const int i = t & 127;
-#pragma unroll
-    for (int it = 0; it < 32; ++it) {
-      const int c = 2 * it + (t >> 7);
-      bstore(As[sw(i, c)], rz, i0 + i < s0 ? (c * (int)n + i) * 4 : OOB);
-    }
+  if (!zpre) {
+    // Z[I] = A12[I] M
+    panel_z(As, Ms);
+    // the diagonal tiles also store Z^T
+    if (tm == tn) store_zt(F, n, s0, i0, As);
   }
   // C -= Z[I] A12[K]^T in two halves of 32 k; each half's operands are read before its MFMAs
   f32x16 acc[2][2];
@@ -660,12 +746,24 @@ kq_status damp_and_factor(const float* HX, float* F, float* T, uint8_t* dead, do
   const int64_t nb = n / NB;
   leaf_kernel<<<1, 256, 0, s>>>(F, n, n - NB, Ubuf + (nb - 1) * 4096, Mbuf + (nb - 1) * 4096, flag);
   KQ_LAUNCHED("leaf_kernel");
+  // steps whose update takes more than one round of workgroups (two per CU) form their panel
+  // factor once, ahead of the update, instead of in every tile (a third of a tile's products);
+  // on the shorter steps the extra launch would cost more than it saves (c3, 11008 wide:
+  // quantize 17.5 -> 16.1 ms; c2 is unchanged)
+  // (KQ_ZPRE_TILES overrides the threshold; a tuning knob, both paths give the same factor)
+  int64_t zpre_tiles = 2 * (int64_t)device_cu_count();
+  if (const char* env = getenv("KQ_ZPRE_TILES")) zpre_tiles = atoll(env);
   for (int64_t s0 = n - NB; s0 >= NB; s0 -= NB) {
     const int64_t m = ceil_div(s0, 128);
     const int64_t tiles = m * (m + 1) / 2;
     const int64_t jb = s0 / NB;
+    const int zpre = tiles > zpre_tiles ? 1 : 0;
+    if (zpre) {
+      z_kernel<<<dim3((unsigned)m), dim3(256), 0, s>>>(F, n, s0, Mbuf + jb * 4096);
+      KQ_LAUNCHED("z_kernel");
+    }
     update_kernel<<<dim3((unsigned)(1 + tiles)), dim3(256), 0, s>>>(
-        F, n, s0, Mbuf + jb * 4096, Ubuf + (jb - 1) * 4096, Mbuf + (jb - 1) * 4096, flag);
+        F, n, s0, Mbuf + jb * 4096, Ubuf + (jb - 1) * 4096, Mbuf + (jb - 1) * 4096, flag, zpre);
     KQ_LAUNCHED("update_kernel");
   }
   finalize_kernel<<<dim3((unsigned)nb), dim3(256), 0, s>>>(F, n, Ubuf);

@@ -159,6 +159,24 @@ def test_quantize_block_pairs(bits, group, block):
     check_against_oracle(g, Wt, HXt, HGt, bits, group)
 
 
+def test_factor_panel_formed_once_matches_per_tile(monkeypatch):
+    """The factorization forms each step's panel factor Z once, ahead of the update, on steps
+    with many tiles; forcing that path on every step gives the same bits as forming Z in each
+    tile (the same products in the same order)."""
+    announce("gptq factorization with the panel factor formed once")
+    rng = np.random.default_rng(21)
+    out_n, in_n = 72, 1024
+    Wt = (rng.standard_normal((out_n, in_n)) * 0.05).astype(np.float32).astype(np.float64)
+    HXt = spd(rng, in_n, outliers=2).astype(np.float32).astype(np.float64)
+    HGt = spd(rng, out_n).astype(np.float32).astype(np.float64)
+    ref = gpu_quantize(Wt, HXt, HGt, 3, 128, 128)
+    monkeypatch.setenv("KQ_ZPRE_TILES", "0")
+    g = gpu_quantize(Wt, HXt, HGt, 3, 128, 128)
+    for key in ("E", "packed", "scales", "zeros", "codes"):
+        assert np.array_equal(g[key], ref[key]), key
+    check_against_oracle(g, Wt, HXt, HGt, 3, 128)
+
+
 def test_quantize_without_hg_and_ragged_rows():
     announce("gptq no H_G, out=50")
     rng = np.random.default_rng(11)
