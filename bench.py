@@ -86,10 +86,11 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_src: str, launch_units: float):
+def traffic_from_profile(kernel_src: str, launch_units: float,
+                         profile: str = "syrk_dma_kernel_c2_hbm_traffic.json"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", "syrk_dma_kernel_c2_hbm_traffic.json")
+    p = os.path.join(ROOT, "profiles", profile)
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -424,7 +425,10 @@ def flipflop_main(a) -> None:
         "config": {"workload": cfg.name + "-flipflop", "in": n, "out": m, "tokens": T,
                    "iterations_per_step": iters},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_profile(
+                         os.path.join(ROOT, "post_quantization_syrk_amd", "csrc", "flipflop.hip"), 1,
+                         "qform_kernel_c2_hbm_traffic.json"),
                      "kernel": "qform_kernel", "algorithmic_flops_per_launch": flops},
         "cpu_baseline": cpu,
         "phases_ms_per_iteration": {k_: round(v / (iters * a.steps), 3) for k_, v in phases.items()},
