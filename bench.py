@@ -576,6 +576,20 @@ def main():
                     "kernel": "two-sided rounding (pull / round / push wavefront, with its factors)",
                     "algorithmic_flops_per_launch": ts_flops}
 
+    # whole-path lower bound at the datasheet peaks: both SYRKs on bf16 MFMA, the feedback
+    # products out in (in - B) and the factorization 2 in^3 / 3 on fp32 MFMA, one read and one
+    # write of W, H_X and H_G in fp32 for the rotation plus the codes' packing through HBM
+    pipeline = None
+    if not a.two_sided:
+        lb = {"syrk": (syrk_flops(in_n, T) + syrk_flops(out_n, T)) / (PEAK_BF16_TFLOPS * 1e12),
+              "factor_and_feedback": (float(out_n) * in_n * (in_n - cfg.block) + 2.0 * in_n ** 3 / 3)
+              / (PEAK_FP32_TFLOPS * 1e12),
+              "hbm": (8.0 * (out_n * in_n + in_n * in_n + out_n * out_n)
+                      + out_n * in_n * (1 + cfg.bits / 8)) / (PEAK_HBM_GBS * 1e9)}
+        lb_ms = sum(lb.values()) * 1e3
+        pipeline = {"lower_bound_ms": round(lb_ms, 4), "frac": round(lb_ms / ms_per_step, 4),
+                    "terms_ms": {k: round(v * 1e3, 4) for k, v in lb.items()}}
+
     cpu = None
     if not a.no_cpu_baseline:
         del X, G
@@ -596,6 +610,7 @@ def main():
                    "rounding": "two-sided" if a.two_sided else "gptq"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "pipeline_roofline": pipeline,
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "input_generation_s": round(gen_s, 2),
     }
