@@ -33,17 +33,18 @@ def rel_fro(a, b) -> float:
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
-_PROGRESS = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out",
-                         "test_progress.log")
+_PROGRESS = os.environ.get("KQ_TEST_PROGRESS", "")
 
 
 def announce(msg: str) -> None:
-    """Name the case on stdout (shown with -s) and append it to gpurun_out/test_progress.log,
-    which a captured run still writes as it goes."""
+    """Name the case on stdout (shown with -s) and, when KQ_TEST_PROGRESS names a file, append
+    it there too: a captured run still writes that file as it goes."""
     print(f"[gpu-case] {msg}", flush=True)
     sys.stdout.flush()
+    if not _PROGRESS:
+        return
     try:
-        os.makedirs(os.path.dirname(_PROGRESS), exist_ok=True)
+        os.makedirs(os.path.dirname(os.path.abspath(_PROGRESS)), exist_ok=True)
         with open(_PROGRESS, "a") as f:
             f.write(f"{time.strftime('%H:%M:%S')} {msg}\n")
     except OSError:
