@@ -112,7 +112,9 @@ kq_status kq_accumulate_hessian(const uint16_t* A_bf16, int64_t T, int64_t n, in
  *   HX   device fp32, n_in x n_in (leading dim ldx); only the diagonal is read
  *   HG   device fp32, n_out x n_out (leading dim ldg); only the diagonal is read
  *   out3 host, 3 doubles: {tr H_X, tr H_G, tr H_G * tr H_X}; diagonals summed in fp64
- * Synchronizes `stream` before returning.
+ * Synchronizes `stream` before returning.  The result passes through a 24-byte buffer in
+ * the library's device memory, one per GPU, so calls from several host threads take turns
+ * (a process-wide lock); kq_sensitivity_async, with memory of the caller's, runs unserialized.
  */
 kq_status kq_sensitivity(const float* HX, int64_t n_in, int64_t ldx, const float* HG,
                          int64_t n_out, int64_t ldg, double out3[3], void* stream);
