@@ -81,6 +81,19 @@ def syrk_flops(n: int, T: int) -> float:
     return float(n) * (n + 1) * T
 
 
+def pipeline_lower_bound_ms(out_n: int, in_n: int, T: int, block: int, bits: int) -> dict:
+    """Whole-path time at the datasheet peaks, by term (ms): both SYRKs on bf16 MFMA; the
+    feedback products out in (in - B) and the factorization 2 in^3 / 3 on fp32 MFMA; one read
+    and one write of W, H_X and H_G in fp32 for the rotation, plus the codes (one byte each)
+    read and packed at `bits` bits, through HBM."""
+    syrk = syrk_flops(in_n, T) + syrk_flops(out_n, T)
+    fp32 = float(out_n) * in_n * (in_n - block) + 2.0 * float(in_n) ** 3 / 3
+    hbm = 8.0 * (out_n * in_n + in_n * in_n + out_n * out_n) + out_n * in_n * (1 + bits / 8)
+    return {"syrk": syrk / (PEAK_BF16_TFLOPS * 1e9),
+            "factor_and_feedback": fp32 / (PEAK_FP32_TFLOPS * 1e9),
+            "hbm": hbm / (PEAK_HBM_GBS * 1e6)}
+
+
 def source_hash(path: str) -> str:
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -576,19 +589,12 @@ def main():
                     "kernel": "two-sided rounding (pull / round / push wavefront, with its factors)",
                     "algorithmic_flops_per_launch": ts_flops}
 
-    # whole-path lower bound at the datasheet peaks: both SYRKs on bf16 MFMA, the feedback
-    # products out in (in - B) and the factorization 2 in^3 / 3 on fp32 MFMA, one read and one
-    # write of W, H_X and H_G in fp32 for the rotation plus the codes' packing through HBM
     pipeline = None
     if not a.two_sided:
-        lb = {"syrk": (syrk_flops(in_n, T) + syrk_flops(out_n, T)) / (PEAK_BF16_TFLOPS * 1e12),
-              "factor_and_feedback": (float(out_n) * in_n * (in_n - cfg.block) + 2.0 * in_n ** 3 / 3)
-              / (PEAK_FP32_TFLOPS * 1e12),
-              "hbm": (8.0 * (out_n * in_n + in_n * in_n + out_n * out_n)
-                      + out_n * in_n * (1 + cfg.bits / 8)) / (PEAK_HBM_GBS * 1e9)}
-        lb_ms = sum(lb.values()) * 1e3
+        lb = pipeline_lower_bound_ms(out_n, in_n, T, cfg.block, cfg.bits)
+        lb_ms = sum(lb.values())
         pipeline = {"lower_bound_ms": round(lb_ms, 4), "frac": round(lb_ms / ms_per_step, 4),
-                    "terms_ms": {k: round(v * 1e3, 4) for k, v in lb.items()}}
+                    "terms_ms": {k: round(v, 4) for k, v in lb.items()}}
 
     cpu = None
     if not a.no_cpu_baseline:
