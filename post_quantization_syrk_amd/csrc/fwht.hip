@@ -202,22 +202,37 @@ __global__ __launch_bounds__(NT) void row_fwht_kernel(const float* __restrict__ 
   const int64_t r = active ? g / blocks_per_row : 0;
   const int64_t c0 = active ? (g % blocks_per_row) * b : 0;
 
+  // Every load is issued before any value is used, with no branch around them (a branch
+  // would make each wait for the ones before it): a thread of an inactive block reads block 0
+  // of row 0 and stores nothing; a missing scale vector reads as 0 through an out-of-range
+  // offset, which factor_of ignores.
   float v[EPT];
-  if (active) {
-    const float rsc = scale_at(rs, r);
+  {
+    const bool rhd = rs.d != nullptr, rhs = rs.sign != nullptr;
+    const bool chd = cs.d != nullptr, chs = cs.sign != nullptr;
+    const __amdgpu_buffer_rsrc_t rrd = rsrc(rs.d), rrg = rsrc(rs.sign);
+    const __amdgpu_buffer_rsrc_t rcd = rsrc(cs.d), rcg = rsrc(cs.sign);
+    const unsigned rdw = __builtin_amdgcn_raw_buffer_load_b32(rrd, rhd ? (int)(4 * r) : OOB, 0, 0);
+    const unsigned rgb = __builtin_amdgcn_raw_buffer_load_b8(rrg, rhs ? (int)r : OOB, 0, 0);
     const float* p = src + r * n + c0;
+    float4 qv[EPT / 4];
+    u32x4 cd[EPT / 4];
+    unsigned cg[EPT / 4];
 #pragma unroll
     for (int j = 0; j < EPT / 4; ++j) {
       const int x = 4 * tb + 4 * TPR * j;
-      float4 q = *(const float4*)(p + x);
-      v[4 * j + 0] = q.x * rsc * scale_at(cs, c0 + x + 0);
-      v[4 * j + 1] = q.y * rsc * scale_at(cs, c0 + x + 1);
-      v[4 * j + 2] = q.z * rsc * scale_at(cs, c0 + x + 2);
-      v[4 * j + 3] = q.w * rsc * scale_at(cs, c0 + x + 3);
+      qv[j] = *(const float4*)(p + x);
+      cd[j] = __builtin_amdgcn_raw_buffer_load_b128(rcd, chd ? (int)(4 * (c0 + x)) : OOB, 0, 0);
+      cg[j] = __builtin_amdgcn_raw_buffer_load_b32(rcg, chs ? (int)(c0 + x) : OOB, 0, 0);
     }
-  } else {
+    const float rsc = factor_of(rs, rdw, (rgb & 0x80u) != 0);
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) v[e] = 0.f;
+    for (int j = 0; j < EPT / 4; ++j) {
+      v[4 * j + 0] = qv[j].x * rsc * factor_of(cs, cd[j][0], ((cg[j] >> 7) & 1u) != 0);
+      v[4 * j + 1] = qv[j].y * rsc * factor_of(cs, cd[j][1], ((cg[j] >> 15) & 1u) != 0);
+      v[4 * j + 2] = qv[j].z * rsc * factor_of(cs, cd[j][2], ((cg[j] >> 23) & 1u) != 0);
+      v[4 * j + 3] = qv[j].w * rsc * factor_of(cs, cd[j][3], ((cg[j] >> 31) & 1u) != 0);
+    }
   }
   // register bits: e = 4j + q  <->  x = q + 4*tb + 4*TPR*j
 #pragma unroll
@@ -510,7 +525,8 @@ kq_status row_transform(const float* src, float* dst, int64_t rows, int64_t n, i
     KQ_LAUNCHED("row_fwht4096_kernel");
     return KQ_OK;
   }
-  const int ept = b <= 1024 ? 4 : (int)(b / 256);
+  // 16 values per thread up to 1024-point blocks (at most 64 threads, one wave, per block)
+  const int ept = b <= 16 ? (int)b : b <= 1024 ? 16 : (int)(b / 256);
   const int tpr = (int)(b / ept);
   const int bpw = NT / tpr;
   const int64_t nblocks = rows * (n / b);
