@@ -157,8 +157,9 @@ kq_status kq_sensitivity_async(const float* HX, int64_t n_in, int64_t ldx, const
  *   sign_in/out      device int8 +-1, lengths in / out (sign_out unused in IN_ONLY,
  *                    sign_in unused in OUT_ONLY)
  *   had_block_in/out Hadamard block per side: 0 = the largest power of 2 that
- *                    divides the size, capped at 8192; else 1 (no transform on
- *                    that side's rows) or a power of 2 in [4, 8192] dividing it
+ *                    divides the size (KQ_ENOTIMPL when that exceeds 8192, the
+ *                    largest block implemented); else 1 (no transform on that
+ *                    side's rows) or a power of 2 in [4, 8192] dividing it
  *   alpha            rescale exponent (0.25 for weight-only KronQ)
  *   mode             KQ_BIIP_*
  *   d_in, d_out      device fp32 outputs, lengths in / out (1 where not rescaled)
@@ -262,7 +263,8 @@ kq_status kq_allocate_bits(const double* sens, const int64_t* numel, int64_t L, 
  *   d_in, d_out      device fp32 rescale vectors (in, out), or NULL for 1
  *   sign_in, sign_out device int8 +-1 (in, out), or NULL for +1
  *   had_in, had_out  Hadamard blocks: powers of 2 (<= 8192) dividing in / out; 1: none;
- *             0: the largest power of 2 dividing the size (at most 8192), as kq_biip_rotate
+ *             0: the largest power of 2 dividing the size, as kq_biip_rotate (KQ_ENOTIMPL
+ *             when that exceeds 8192)
  *   x         device fp32 [in];  y  device fp32 [out] (not aliasing x)
  * Sizes: in % 32 == 0; the LDS copy of x~ (in rounded up to 64 * 128 / bits entries, plus
  * 1/16 padding) must fit in 160 KB, i.e. in <= 36864.  No workspace: with had_out > 16 a

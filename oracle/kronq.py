@@ -112,11 +112,10 @@ def sylvester_hadamard(b: int) -> np.ndarray:
 
 def hadamard_block_size(n: int, block: int = 0) -> int:
     """Block of the block-diagonal Hadamard.  READING: 0 selects the largest
-    power of two that divides n, at most 8192 (11008 = 43 x 256, 28672 = 7 x 4096)."""
+    power of two that divides n (11008 = 43 x 256, 28672 = 7 x 4096, 4096 and
+    8192 whole)."""
     if block == 0:
         block = n & (-n)
-        while block > 8192:
-            block >>= 1
     if block <= 0 or block & (block - 1) or n % block:
         raise ValueError(f"Hadamard block {block} does not tile n={n}")
     return block

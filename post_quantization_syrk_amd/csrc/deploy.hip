@@ -411,14 +411,9 @@ __global__ __launch_bounds__(DT) void deploy_outrot_kernel(GroupArgs a) {
   }
 }
 
-// Hadamard block of a side: 0 = the largest power of 2 dividing n (at most 8192), as in
-// kq_biip_rotate; 1 = none
-int64_t deploy_block(int64_t n, int64_t had) {
-  if (had != 0) return had;
-  int64_t b = n & -n;
-  while (b > 8192) b >>= 1;
-  return b;
-}
+// Hadamard block of a side: 0 = the largest power of 2 dividing n, as in kq_biip_rotate;
+// 1 = none
+int64_t deploy_block(int64_t n, int64_t had) { return had != 0 ? had : (n & -n); }
 
 constexpr size_t LDS_MAX = 160 * 1024;
 
@@ -457,6 +452,9 @@ kq_status deploy_group(const kq_deploy_layer* layers, int nl, int64_t in, const 
       return fail(KQ_ESHAPE, "%s: layer %d: group must divide in and be a multiple of %d (or in)", fn, l, cpc);
     if (q.had_in < 0 || q.had_out < 0) return fail(KQ_ESHAPE, "%s: layer %d: negative block", fn, l);
     const int64_t bin = deploy_block(in, q.had_in), bout = deploy_block(q.out, q.had_out);
+    if ((q.had_in == 0 && bin > 8192) || (q.had_out == 0 && bout > 8192))
+      return fail(KQ_ENOTIMPL, "%s: layer %d: the automatic Hadamard block (the largest power of 2 "
+                  "dividing the size) exceeds 8192; pass a block of at most 8192", fn, l);
     if (!is_pow2(bin) || in % bin != 0 || bin > 8192 || !is_pow2(bout) || q.out % bout != 0 || bout > 8192)
       return fail(KQ_ESHAPE, "%s: layer %d: Hadamard blocks must be powers of 2 (<= 8192) dividing the sizes", fn, l);
     L.packed = q.packed; L.scales = q.scales; L.zeros = q.zeros;

@@ -581,10 +581,12 @@ extern "C" kq_status kq_biip_rotate(const float* W_src, float* W_dst, int64_t ou
   if (out < 1 || in < 1 || out % 4 || in % 4 || out > (1 << 30) || in > (1 << 30))
     return fail(KQ_ESHAPE, "kq_biip_rotate: out and in must be positive multiples of 4");
   if (!(alpha >= 0.f) || !isfinite(alpha)) return fail(KQ_EINVAL, "kq_biip_rotate: alpha");
-  int64_t bin = had_block_in == 0 ? (in & -in) : had_block_in;
-  int64_t bout = had_block_out == 0 ? (out & -out) : had_block_out;
-  if (had_block_in == 0) { while (bin > 8192) bin >>= 1; }
-  if (had_block_out == 0) { while (bout > 8192) bout >>= 1; }
+  const int64_t bin = had_block_in == 0 ? (in & -in) : had_block_in;
+  const int64_t bout = had_block_out == 0 ? (out & -out) : had_block_out;
+  if ((do_in && had_block_in == 0 && bin > 8192) || (do_out && had_block_out == 0 && bout > 8192))
+    return fail(KQ_ENOTIMPL,
+                "kq_biip_rotate: the automatic Hadamard block (the largest power of 2 dividing the "
+                "size) exceeds 8192, the largest block implemented; pass a block of at most 8192");
   if (do_in && !valid_block(in, bin))
     return fail(KQ_ESHAPE, "kq_biip_rotate: input Hadamard block %lld does not tile in=%lld",
                 (long long)bin, (long long)in);

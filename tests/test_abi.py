@@ -155,3 +155,25 @@ def test_flipflop_rejects_bad_arguments_on_host():
     assert lib.kq_flipflop(*args, 1, buf, buf, buf, need - 1, None, None) == kq.KQ_EWORKSPACE
     assert lib.kq_flipflop(buf, 256, buf, 384, 1000, 256, 384, 1, None, buf, buf, need, None, None) == kq.KQ_EINVAL
     assert lib.kq_flipflop(buf, 260, buf, 384, 1000, 256, 384, 1, buf, buf, buf, need, None, None) == kq.KQ_ESHAPE
+
+
+def test_automatic_hadamard_block_beyond_8192_is_refused_on_host():
+    """Block 0 means the largest power of 2 dividing the size.  For 16384 that is 16384, which
+    no kernel here runs: the library says so instead of rotating with a smaller block, and an
+    explicit block of 8192 is accepted by the host checks."""
+    lib = _raw()
+    buf = ctypes.c_void_p(0x1000)
+    f = ctypes.c_float(0.25)
+    # in = 16384, automatic input block
+    assert lib.kq_biip_rotate(buf, buf, 64, 16384, buf, buf, buf, buf, buf, buf, 0, 0, f,
+                              kq.KQ_BIIP_FULL, buf, buf, None) == kq.KQ_ENOTIMPL
+    assert b"8192" in lib.kq_last_error()
+    # out = 16384 on the output side only
+    assert lib.kq_biip_rotate(buf, buf, 16384, 64, buf, buf, buf, buf, buf, buf, 0, 0, f,
+                              kq.KQ_BIIP_OUT_ONLY, buf, buf, None) == kq.KQ_ENOTIMPL
+    L = kq.DeployLayer(buf, buf, buf, 4, 128, 64, None, None, None, None, 0, 0, buf)
+    arr = (kq.DeployLayer * 1)(L)
+    assert lib.kq_deploy_linear_group(arr, 1, 16384, buf, None) == kq.KQ_ENOTIMPL
+    L2 = kq.DeployLayer(buf, buf, buf, 4, 128, 16384, None, None, None, None, 0, 0, buf)
+    arr2 = (kq.DeployLayer * 1)(L2)
+    assert lib.kq_deploy_linear_group(arr2, 1, 256, buf, None) == kq.KQ_ENOTIMPL

@@ -101,6 +101,9 @@ def test_hadamard_block_rule():
     assert o.hadamard_block_size(11008) == 256
     assert o.hadamard_block_size(28672) == 4096
     assert o.hadamard_block_size(4096) == 4096
+    assert o.hadamard_block_size(8192) == 8192
+    assert o.hadamard_block_size(16384) == 16384     # no cap: the whole power of 2
+    assert o.hadamard_block_size(3 * 16384) == 16384
     assert o.hadamard_block_size(8192, 4096) == 4096
     with pytest.raises(ValueError):
         o.hadamard_block_size(96, 64)
@@ -359,6 +362,63 @@ def test_dead_channel_rule():
     r = o.quantize_layer(W, HX, None, 2, 8, 0.01)
     assert r["dead"][3] and r["dead"].sum() == 1
     assert np.all(r["gptq"].qhat[:, 3] == 0)
+
+
+# ---------------------------------------------------------------------------
+# Damping: lambda = damp * mean(diag H~_X) on the processed factor, after a dead channel's
+# diagonal is set to 1 (the single-layer workload's "damping 1% of mean diag(H_X)", read as
+# GPTQ's relative damping of the factor it factors)
+# ---------------------------------------------------------------------------
+def test_damping_hand_example_with_dead_channel():
+    """H = diag(4, 0, 8, 12), damp 0.01.  The dead channel counts as 1, so the mean diagonal
+    is (4 + 1 + 8 + 12) / 4 = 6.25 and lambda = 0.0625: not 0.06 (mean taken before the dead
+    diagonal is set), not 0.25 (1 % of the trace).  For a diagonal H the factor of
+    (H + lambda I)^-1 is diag(1 / sqrt(h_i + lambda)) by hand."""
+    H = np.diag([4.0, 0.0, 8.0, 12.0])
+    U, lam, dead, Hd = o.damp_and_factor(H, 0.01)
+    assert lam == pytest.approx(0.0625, rel=1e-15)
+    assert list(dead) == [False, True, False, False]
+    hd = [4.0625, 1.0625, 8.0625, 12.0625]
+    np.testing.assert_allclose(np.diag(Hd), hd, rtol=1e-15)
+    np.testing.assert_allclose(U, np.diag([1.0 / math.sqrt(v) for v in hd]), rtol=1e-14, atol=1e-300)
+
+
+def test_damping_hand_example_2x2():
+    """H = [[2, 1], [1, 2]], damp 0.5: lambda = 0.5 * 2 = 1, H_d = [[3, 1], [1, 3]],
+    H_d^-1 = [[3, -1], [-1, 3]] / 8, whose upper Cholesky factor is, by hand,
+    U = [[sqrt(3/8), -1 / (8 sqrt(3/8))], [0, 1 / sqrt(3)]]."""
+    U, lam, _, Hd = o.damp_and_factor(np.array([[2.0, 1.0], [1.0, 2.0]]), 0.5)
+    assert lam == 1.0
+    np.testing.assert_array_equal(Hd, [[3.0, 1.0], [1.0, 3.0]])
+    a = math.sqrt(3.0 / 8.0)
+    np.testing.assert_allclose(U, [[a, -1.0 / (8.0 * a)], [0.0, 1.0 / math.sqrt(3.0)]], rtol=1e-14)
+
+
+def test_damping_is_taken_on_the_processed_factor():
+    """After BiIP the mean diagonal of H~_X is sum_i H_ii / d_i^2 / n: the rotation keeps the
+    trace, the rescale divides entry (i, i) by d_i^2, with d_i = (H_ii / c_i)^(1/4) and c_i the
+    squared norm of W's column i.  Here that mean is far from the raw one, so lambda taken
+    from the raw H_X (or with damp times the trace) fails; the factor GPTQ then uses must
+    whiten H~_X + lambda I."""
+    rng = np.random.default_rng(77)
+    n, out = 16, 8
+    A = rng.standard_normal((64, n)) * np.exp(1.5 * rng.standard_normal(n))[None, :]
+    HX = A.T @ A
+    B = rng.standard_normal((64, out))
+    HG = B.T @ B
+    W = rng.standard_normal((out, n)) * 0.02 * np.exp(rng.standard_normal(n))[None, :]
+    c = [sum(W[r, i] ** 2 for r in range(out)) for i in range(n)]
+    d = [math.sqrt(math.sqrt(HX[i, i] / c[i])) for i in range(n)]
+    mean_t = sum(HX[i, i] / d[i] ** 2 for i in range(n)) / n
+    mean_raw = sum(HX[i, i] for i in range(n)) / n
+    assert abs(mean_t - mean_raw) > 0.5 * mean_raw      # the case tells the two apart
+    s_in = rng.choice([-1, 1], n).astype(np.int8)
+    s_out = rng.choice([-1, 1], out).astype(np.int8)
+    Wt, HXt, HGt, _, _ = o.biip(W, HX, HG, s_in, s_out, 0.25, o.BIIP_FULL, 0, 0)
+    r = o.quantize_layer(Wt, HXt, HGt, 2, n, 0.01)
+    assert r["lam"] == pytest.approx(0.01 * mean_t, rel=1e-12)
+    U = r["U"]
+    np.testing.assert_allclose(U @ (HXt + 0.01 * mean_t * np.eye(n)) @ U.T, np.eye(n), atol=1e-9)
 
 
 def test_replay_accepts_only_near_ties():
