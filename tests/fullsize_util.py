@@ -35,7 +35,7 @@ def oracle_diag(bits: np.ndarray, chunk: int = 8192) -> np.ndarray:
 
 
 def run_engine(cfg, bx, bg, W, s_in, s_out, want_loss=True, keep_raw=True, hg_host=True,
-               hg_samples=None):
+               hg_samples=None, keep_raw_hg=None):
     """kq_accumulate_hessian x2, kq_sensitivity, kq_biip_rotate, kq_quantize_layer, as bench.py."""
     torch = torch_cuda()
     import post_quantization_syrk_amd as kq
@@ -52,7 +52,7 @@ def run_engine(cfg, bx, bg, W, s_in, s_out, want_loss=True, keep_raw=True, hg_ho
     out = {"sens": kq.kq_sensitivity(HX, HG)}
     if keep_raw:
         out["HX"] = HX.cpu().numpy()
-        out["HG"] = HG.cpu().numpy() if hg_host else None
+        out["HG"] = HG.cpu().numpy() if (hg_host if keep_raw_hg is None else keep_raw_hg) else None
     out["HG_diag"] = torch.diagonal(HG).cpu().numpy()
     if hg_samples is not None:
         ii, jj = (torch.from_numpy(np.asarray(v)).to(dev) for v in hg_samples)

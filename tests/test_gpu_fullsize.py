@@ -93,7 +93,7 @@ def test_c5_llama3_70b_up_proj():
     rng = np.random.default_rng(55)
     i = rng.integers(0, cfg.out, 32)
     j = rng.integers(0, cfg.out, 32)
-    g = run_engine(cfg, bx, bg, W, s_in, s_out, want_loss=False, hg_host=False, hg_samples=(i, j))
+    g = run_engine(cfg, bx, bg, W, s_in, s_out, want_loss=True, hg_host=True, hg_samples=(i, j))
     t0 = time.time()
     HX = oracle_hessian(bx)
     hg_diag = oracle_diag(bg)
@@ -121,7 +121,32 @@ def test_c5_llama3_70b_up_proj():
     assert ew <= 1e-5 and ehx <= 1e-5
     # rotation keeps the trace: tr(H~_G) = sum_k H_G[k,k] / d_out[k]^2
     assert g["HGt_trace"] == pytest.approx(float(np.sum(hg_diag / d_out ** 2)), rel=1e-5)
+    # the output-side rotation at full width, on the first 4096-row Hadamard block of H~_G:
+    # the oracle's rescale and rotation applied to the engine's raw H_G rows (stage-wise)
+    b0 = cfg.had_out
+    stripe = g.pop("HG")[:b0].astype(np.float64) / np.outer(d_out[:b0], d_out)
+    ref_t = o.rotate_cols(o.rotate_rows(stripe, s_out, cfg.had_out), s_out[:b0], cfg.had_out)
+    ehg = rel_fro(g["HGt"][:b0], ref_t)
+    announce(f"c5: H~_G rows 0..{b0 - 1} rel {ehg:.2e}")
+    assert ehg <= 1e-5
+    del stripe, ref_t
     fac = o.damp_and_factor(HXt, cfg.damp)
     rows = np.sort(np.random.default_rng(5).choice(cfg.out, N_ROWS, replace=False))
     res = check_rows(g, Wt, HXt, cfg, rows, fac)
     announce(f"c5: {N_ROWS} sampled rows match ({res.accepted_ties} near-tie codes adopted)")
+    # Losses.  The oracle's fp64 H_G would need the whole 262144 x 28672 stream in a SYRK of
+    # its own, so this stage takes the engine's H~_G, upcast (the stage-wise protocol; H~_G's
+    # raw factor is pinned above by sampled entries, its diagonal and its trace), with the
+    # oracle's own W~ and H~_X and the engine's codes: the direct loss
+    # tr(H~_G dW~ H~_X dW~^T) and the predicted loss sum_j e_j^T H~_G e_j.
+    t0 = time.time()
+    HGt = g.pop("HGt").astype(np.float64)
+    assert float(np.trace(HGt)) == pytest.approx(float(np.sum(hg_diag / d_out ** 2)), rel=1e-5)
+    dW = Wt - dequant(g["codes"], g["scales"], g["zeros"], cfg.group)
+    L_direct = o.proxy_loss(dW, HXt, HGt)
+    L_pred = o.predicted_loss(g["E"], HGt)
+    announce(f"c5: losses engine {g['loss'][0]:.6e} / {g['loss'][1]:.6e}, oracle {L_direct:.6e} / "
+             f"{L_pred:.6e} ({time.time() - t0:.0f} s)")
+    assert g["loss"][0] == pytest.approx(L_direct, rel=1e-3)
+    assert g["loss"][1] == pytest.approx(L_pred, rel=1e-3)
+    assert g["loss"][1] > g["loss"][0]

@@ -263,3 +263,35 @@ def test_c1_end_to_end():
     # the raw-domain loss equals the rotated-domain loss (BiIP invariance)
     print(f"c1: loss_direct {loss[0]:.6e} (oracle {ref['loss_direct']:.6e}), "
           f"accepted ties {ref['gptq'].accepted_ties}")
+
+
+@pytest.mark.parametrize("dead_ch", [None, 7])
+def test_engine_damping_read_from_its_losses(dead_ch):
+    """The engine's lambda, pinned without the oracle: with H_G = I the predicted loss exceeds
+    the direct one by exactly lambda ||W~ - Qhat||_F^2 (W~ - Qhat = E U and U H_d U^T = I).
+    lambda must be 1 % of the mean diagonal of the H~_X it is given, a dead channel (zero
+    diagonal) counting as 1.  The diagonal is scaled to a mean of 1e-3, so a mean taken before
+    the dead channel is set (or a trace, or another damp) misses by far more than the
+    tolerance."""
+    torch_cuda()
+    rng = np.random.default_rng(41)
+    out_n, n = 64, 256
+    H = spd(rng, n, outliers=6)
+    H *= 1e-3 / np.mean(np.diag(H))       # diagonal ~1e-3: a dead channel's 1 moves the mean 4x
+    if dead_ch is not None:
+        H[dead_ch, :] = 0.0
+        H[:, dead_ch] = 0.0
+    H = H.astype(np.float32).astype(np.float64)
+    diag = [1.0 if H[i, i] == 0.0 else float(H[i, i]) for i in range(n)]
+    lam_hand = 0.01 * sum(diag) / n
+    W = (rng.standard_normal((out_n, n)) * 0.02).astype(np.float32)
+    g = gpu_quantize(W, H, None, 2, 64, 64, damp=0.01, want_loss=True)
+    W0 = W.astype(np.float64)
+    if dead_ch is not None:
+        W0[:, dead_ch] = 0.0
+    s = np.repeat(g["scales"].astype(np.float64), 64, axis=1)
+    z = np.repeat(g["zeros"].astype(np.float64), 64, axis=1)
+    dW = W0 - s * (g["codes"] - z)
+    lam_engine = (g["loss"][1] - g["loss"][0]) / float(np.sum(dW * dW))
+    announce(f"damping: engine lambda {lam_engine:.6e}, by hand {lam_hand:.6e}")
+    assert lam_engine == pytest.approx(lam_hand, rel=1e-3)
