@@ -36,24 +36,108 @@ constexpr int NT = 256;
 // ---------------------------------------------------------------------------
 // norms and rescale vectors
 // ---------------------------------------------------------------------------
-// colsum[i] += sum over a stripe of CS_ROWS rows of W[r][i]^2   (colsum pre-zeroed).  Every
-// row's load is issued before any is used (rows past the end are read at the last row and
-// count as zero, a select rather than a branch around the load).
-constexpr int CS_ROWS = 32;
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int OOB = 0x7ffffff0;   // buffer offsets at or past this read 0 / drop the store
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
+  // 0x00020000: the descriptor's data-format word on gfx9
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, OOB, 0x00020000);
+}
+
+// Both squared-norm vectors of W from one read of it.  A workgroup takes NR_ROWS whole rows;
+// thread t reads the 16-byte column chunks 4t + 1024 j of each row.
+//   rowsum[r] = sum_i W[r][i]^2: per-thread partial sums, then a fixed reduction order
+//               (wave shuffles, then the four waves' values), stored directly (deterministic);
+//   colsum[i] += sum over the workgroup's rows of W[r][i]^2 (atomics; colsum pre-zeroed).
+// Either output may be NULL.  Rows past `out` and chunks past `in` read 0 (buffer offsets out
+// of range), so no load sits behind a branch.
+constexpr int NR_ROWS = 32;
+template <int J>
+__global__ __launch_bounds__(NT) void norms_kernel(const float* __restrict__ W, int64_t out,
+                                                   int64_t in, float* __restrict__ colsum,
+                                                   float* __restrict__ rowsum) {
+  // rows in flight per unrolled step: about 16 chunk loads per thread
+  constexpr int UR = J <= 2 ? 8 : J <= 4 ? 4 : J <= 8 ? 2 : 1;
+  __shared__ float part[NT / 64][NR_ROWS];
+  const int t = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * NR_ROWS;
+  const __amdgpu_buffer_rsrc_t rr = rsrc(W + r0 * in);
+  float4 cacc[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) cacc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll UR
+  for (int k = 0; k < NR_ROWS; ++k) {
+    u32x4 q[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int64_t c = 4 * t + 1024 * j;
+      const bool ok = r0 + k < out && c < in;
+      q[j] = __builtin_amdgcn_raw_buffer_load_b128(rr, ok ? (int)(((int64_t)k * in + c) * 4) : OOB, 0, 0);
+    }
+    float rs = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const float a = __uint_as_float(q[j].x), b = __uint_as_float(q[j].y);
+      const float c = __uint_as_float(q[j].z), d = __uint_as_float(q[j].w);
+      cacc[j].x += a * a; cacc[j].y += b * b; cacc[j].z += c * c; cacc[j].w += d * d;
+      rs += a * a + b * b + c * c + d * d;
+    }
+    rs = wave_sum(rs);
+    if ((t & 63) == 0) part[t >> 6][k] = rs;
+  }
+  if (colsum) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int64_t c = 4 * t + 1024 * j;
+      if (c < in) {
+        atomicAdd(colsum + c + 0, cacc[j].x);
+        atomicAdd(colsum + c + 1, cacc[j].y);
+        atomicAdd(colsum + c + 2, cacc[j].z);
+        atomicAdd(colsum + c + 3, cacc[j].w);
+      }
+    }
+  }
+  if (rowsum) {
+    __syncthreads();
+    if (t < NR_ROWS && r0 + t < out)
+      rowsum[r0 + t] = (part[0][t] + part[1][t]) + (part[2][t] + part[3][t]);
+  }
+}
+
+kq_status launch_norms(const float* W, int64_t out, int64_t in, float* colsum, float* rowsum,
+                       hipStream_t s) {
+  const dim3 grid((unsigned)ceil_div(out, NR_ROWS));
+  switch (ceil_div(in, 1024)) {
+#define KQ_NORMS_CASE(X) \
+  case X: norms_kernel<X><<<grid, dim3(NT), 0, s>>>(W, out, in, colsum, rowsum); break;
+    KQ_NORMS_CASE(1) KQ_NORMS_CASE(2) KQ_NORMS_CASE(3) KQ_NORMS_CASE(4) KQ_NORMS_CASE(5)
+    KQ_NORMS_CASE(6) KQ_NORMS_CASE(7) KQ_NORMS_CASE(8) KQ_NORMS_CASE(9) KQ_NORMS_CASE(10)
+    KQ_NORMS_CASE(11) KQ_NORMS_CASE(12) KQ_NORMS_CASE(13) KQ_NORMS_CASE(14) KQ_NORMS_CASE(15)
+    KQ_NORMS_CASE(16)
+#undef KQ_NORMS_CASE
+    default: return KQ_ENOTIMPL;
+  }
+  KQ_LAUNCHED("norms_kernel");
+  return KQ_OK;
+}
+
+// Two-pass fallback for rows longer than 16384: colsum over stripes of 32 rows (atomics),
+// rowsum one workgroup per row.
 __global__ __launch_bounds__(NT) void col_sumsq_kernel(const float* __restrict__ W, int64_t out,
                                                        int64_t in, float* __restrict__ colsum) {
   const int64_t c = ((int64_t)blockIdx.x * NT + threadIdx.x) * 4;
   if (c >= in) return;
-  const int64_t r0 = (int64_t)blockIdx.y * CS_ROWS;
-  float4 v[CS_ROWS];
-#pragma unroll
-  for (int k = 0; k < CS_ROWS; ++k) v[k] = *(const float4*)(W + min(r0 + k, out - 1) * in + c);
+  const int64_t r0 = (int64_t)blockIdx.y * NR_ROWS;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int k = 0; k < CS_ROWS; ++k) {
-    const float m = r0 + k < out ? 1.f : 0.f;
-    acc.x += m * v[k].x * v[k].x; acc.y += m * v[k].y * v[k].y;
-    acc.z += m * v[k].z * v[k].z; acc.w += m * v[k].w * v[k].w;
+  for (int k = 0; k < NR_ROWS && r0 + k < out; ++k) {
+    const float4 v = *(const float4*)(W + (r0 + k) * in + c);
+    acc.x += v.x * v.x; acc.y += v.y * v.y; acc.z += v.z * v.z; acc.w += v.w * v.w;
   }
   atomicAdd(colsum + c + 0, acc.x);
   atomicAdd(colsum + c + 1, acc.y);
@@ -61,13 +145,6 @@ __global__ __launch_bounds__(NT) void col_sumsq_kernel(const float* __restrict__
   atomicAdd(colsum + c + 3, acc.w);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-// rowsum[r] = sum_i W[r][i]^2, one workgroup per row
 __global__ __launch_bounds__(NT) void row_sumsq_kernel(const float* __restrict__ W, int64_t in,
                                                        float* __restrict__ rowsum) {
   const float* row = W + (int64_t)blockIdx.x * in;
@@ -81,6 +158,24 @@ __global__ __launch_bounds__(NT) void row_sumsq_kernel(const float* __restrict__
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
   __syncthreads();
   if (threadIdx.x == 0) rowsum[blockIdx.x] = part[0] + part[1] + part[2] + part[3];
+}
+
+// colsum (pre-zeroed) and / or rowsum of W, from one read of W where the row fits the fused
+// kernel.
+kq_status squared_norms(const float* W, int64_t out, int64_t in, float* colsum, float* rowsum,
+                        hipStream_t s) {
+  if (in <= 16 * 1024 && (int64_t)NR_ROWS * in * 4 < ((int64_t)1 << 31))
+    return launch_norms(W, out, in, colsum, rowsum, s);
+  if (colsum) {
+    dim3 grid((unsigned)ceil_div(in / 4, NT), (unsigned)ceil_div(out, NR_ROWS));
+    col_sumsq_kernel<<<grid, dim3(NT), 0, s>>>(W, out, in, colsum);
+    KQ_LAUNCHED("col_sumsq_kernel");
+  }
+  if (rowsum) {
+    row_sumsq_kernel<<<dim3((unsigned)out), dim3(NT), 0, s>>>(W, in, rowsum);
+    KQ_LAUNCHED("row_sumsq_kernel");
+  }
+  return KQ_OK;
 }
 
 // d[i] = (H[i,i] / norm[i])^alpha, 1 where either is not positive (in place over norm)
@@ -103,12 +198,6 @@ struct Scale {
   float mul;            // constant factor (1/sqrt(b))
 };
 
-constexpr int OOB = 0x7ffffff0;   // buffer offsets at or past this read 0 / drop the store
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
-  // 0x00020000: the descriptor's data-format word on gfx9
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, OOB, 0x00020000);
-}
-
 // Branch-free (a branch here would let the compiler sink loads issued before it past it):
 // mul * d, mul / d or mul from the raw d word, negated when the sign bit is set.
 __device__ __forceinline__ float factor_of(const Scale& s, unsigned dword, bool neg) {
@@ -118,8 +207,6 @@ __device__ __forceinline__ float factor_of(const Scale& s, unsigned dword, bool 
   const float v = (s.mul * (mul_d ? d : 1.f)) / (div_d ? d : 1.f);
   return hs && neg ? -v : v;
 }
-
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // The factors of the 16 consecutive entries i0 + c .. i0 + c + 15 (c a multiple of 16): four
 // 16-byte loads of d and one of the signs (a missing vector is read out of range, as 0).
@@ -471,6 +558,84 @@ __global__ __launch_bounds__(NT) void col_fwht_kernel(float* __restrict__ M, int
   }
 }
 
+// Column pass for 4096-row blocks in one pass: a workgroup holds a whole block of rows for 8
+// columns (128 KB of LDS) and runs all 12 butterfly stages on it, as three rounds of 4 index
+// bits in registers (16 rows x 4 columns per thread) with two LDS regroupings, the same rounds
+// as the 4096-point row pass:
+//   round A: x = 16 t + i      (a thread's 16 rows are consecutive; global loads)
+//   round B: x = (t & 15) + 16 i + 256 (t >> 4)
+//   round C: x = t + 256 i     (global stores)
+// Thread (t, h) = (tid >> 1, tid & 1) owns columns 4h .. 4h + 3 of the slab, so a lane pair
+// reads or writes the slab's 32 contiguous bytes of a row.  The four slabs that share a
+// 128-byte line of a row run side by side on one XCD (consecutive slabs go to the same XCD),
+// so the line is fetched from memory once.  LDS holds (row, column quad) as 16-byte units,
+// unit 2x + h XOR-swizzled by ((x >> 4) & 7) << 1: every group of 16 lanes of each round
+// touches 16 distinct units modulo 16, i.e. distinct banks.
+constexpr int C4K = 4096;
+constexpr int C4W = 8;         // columns per workgroup
+constexpr int C4T = 512;       // threads
+__device__ __forceinline__ int c4_unit(int x, int h) { return (2 * x + h) ^ (((x >> 4) & 7) << 1); }
+
+__global__ __launch_bounds__(C4T) void col_fwht4096_kernel(float* __restrict__ M, int64_t ncols,
+                                                            int64_t slabs, int64_t total,
+                                                            int64_t per_xcd, int xcds) {
+  __shared__ __attribute__((aligned(16))) float4 sm[C4K * C4W / 4];
+  const int tid = threadIdx.x, h = tid & 1, t = tid >> 1;
+  // workgroup u runs on XCD u mod xcds; XCD x takes items x * per_xcd .. + per_xcd - 1 of the
+  // (block, slab) items (the grid is xcds * per_xcd), so neighbouring slabs run side by side
+  // on one XCD
+  const int64_t u = blockIdx.x;
+  const int64_t item = (u % xcds) * per_xcd + u / xcds;
+  if (item >= total) return;
+  const int64_t blk = item / slabs, slab = item % slabs;
+  const int64_t c = slab * C4W + 4 * h;
+  const bool cok = c < ncols;
+  // descriptor at the block's first row; masked columns read 0 and drop their stores
+  const __amdgpu_buffer_rsrc_t rr = rsrc(M + blk * C4K * ncols);
+  float4 v[16];
+  auto bfly = [&]() {
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if (e & m) continue;
+        const float4 a = v[e], b = v[e | m];
+        v[e] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+        v[e | m] = make_float4(a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w);
+      }
+  };
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int x = 16 * t + i;
+    const int off = cok ? (int)(((int64_t)x * ncols + c) * 4) : OOB;
+    const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, 0);
+    v[i] = make_float4(__uint_as_float(q.x), __uint_as_float(q.y), __uint_as_float(q.z),
+                       __uint_as_float(q.w));
+  }
+  bfly();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sm[c4_unit(16 * t + i, h)] = v[i];
+  __syncthreads();
+  const int xb = (t & 15) + 256 * (t >> 4);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = sm[c4_unit(xb + 16 * i, h)];
+  bfly();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sm[c4_unit(xb + 16 * i, h)] = v[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = sm[c4_unit(t + 256 * i, h)];
+  bfly();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int x = t + 256 * i;
+    const int off = cok ? (int)(((int64_t)x * ncols + c) * 4) : OOB;
+    const u32x4 q = {__float_as_uint(v[i].x), __float_as_uint(v[i].y), __float_as_uint(v[i].z),
+                     __float_as_uint(v[i].w)};
+    __builtin_amdgcn_raw_buffer_store_b128(q, rr, off, 0, 0);
+  }
+}
+
 kq_status launch_col_pass(float* M, int64_t rows, int64_t ncols, int k0, int mb, hipStream_t s) {
   dim3 grid((unsigned)(rows >> mb), (unsigned)ceil_div(ncols, CW));
   switch (mb) {
@@ -485,8 +650,20 @@ kq_status launch_col_pass(float* M, int64_t rows, int64_t ncols, int k0, int mb,
   return KQ_OK;
 }
 
-// FWHT of every column over blocks of b rows (b a power of 2): ceil(log2 b / 8) passes.
+// FWHT of every column over blocks of b rows (b a power of 2): one pass for 4096-row blocks
+// (when a block's byte offsets fit a buffer descriptor), else ceil(log2 b / 8) passes.
 kq_status column_transform(float* M, int64_t rows, int64_t ncols, int64_t b, hipStream_t s) {
+  if (b == C4K && (int64_t)C4K * ncols * 4 < ((int64_t)1 << 31)) {
+    const int64_t slabs = ceil_div(ncols, C4W);
+    const int64_t total = (rows / C4K) * slabs;
+    if (total > 0x7FFFFFFF) return fail(KQ_ESHAPE, "column pass: too many slabs");
+    const int xcds = device_cu_count() % 8 == 0 ? 8 : 1;
+    const int64_t per_xcd = ceil_div(total, xcds);
+    col_fwht4096_kernel<<<dim3((unsigned)(per_xcd * xcds)), dim3(C4T), 0, s>>>(M, ncols, slabs,
+                                                                               total, per_xcd, xcds);
+    KQ_LAUNCHED("col_fwht4096_kernel");
+    return KQ_OK;
+  }
   int m = 0;
   while (((int64_t)1 << m) < b) ++m;
   if (m == 0) return KQ_OK;
@@ -596,19 +773,18 @@ extern "C" kq_status kq_biip_rotate(const float* W_src, float* W_dst, int64_t ou
   hipStream_t s = as_stream(stream);
 
   // 1. rescale vectors (norms of the original W, diagonals of the raw factors)
-  if (rescale && do_in) {
-    KQ_TRY(fill_f32(d_in, in, 0.f, s));
-    dim3 grid((unsigned)ceil_div(in / 4, NT), (unsigned)ceil_div(out, CS_ROWS));
-    col_sumsq_kernel<<<grid, dim3(NT), 0, s>>>(W_src, out, in, d_in);
-    KQ_LAUNCHED("col_sumsq_kernel");
+  // both norm vectors from one read of the original W
+  const bool want_col = rescale && do_in, want_row = rescale && do_out;
+  if (want_col) KQ_TRY(fill_f32(d_in, in, 0.f, s));
+  if (want_col || want_row)
+    KQ_TRY(squared_norms(W_src, out, in, want_col ? d_in : nullptr, want_row ? d_out : nullptr, s));
+  if (want_col) {
     rescale_kernel<<<dim3((unsigned)ceil_div(in, 256)), dim3(256), 0, s>>>(HX_src, in, d_in, alpha);
     KQ_LAUNCHED("rescale_kernel");
   } else {
     KQ_TRY(fill_f32(d_in, in, 1.f, s));
   }
-  if (rescale && do_out) {
-    row_sumsq_kernel<<<dim3((unsigned)out), dim3(NT), 0, s>>>(W_src, in, d_out);
-    KQ_LAUNCHED("row_sumsq_kernel");
+  if (want_row) {
     rescale_kernel<<<dim3((unsigned)ceil_div(out, 256)), dim3(256), 0, s>>>(HG_src, out, d_out, alpha);
     KQ_LAUNCHED("rescale_kernel");
   } else {
