@@ -7,10 +7,13 @@ sides), damping + reverse Cholesky + triangular inverse, blocked GPTQ to
 packed codes with scales and zero points.  The proxy loss is a verification
 output and is not part of the step.
 
-Default workload: Llama-2-7B-shaped q_proj, 4096 x 4096 weights (bf16 values,
-0.1 % outlier input channels x30), 131072 calibration tokens of X and G
-(bf16, log-normal channel scales sigma 1 / 1.5), W4 asymmetric min-max,
-group 128, block 128, 4096-point Hadamard on both sides.
+Default workload: Llama-3-70B-shaped up_proj, 28672 x 8192 weights (bf16 values
+~N(0, 0.01^2), 0.1 % outlier input channels x30), 262144 calibration tokens of X
+(8192 wide) and G (28672 wide: a 28672 x 28672 fp32 H_G on one GPU), bf16 with
+log-normal channel scales (sigma 1 / 1.5), W2 asymmetric min-max, group 128,
+block 128, 8192-point input Hadamard, 7 x 4096 output Hadamard.  Other layer
+workloads: --workload c1|c2|c2r|c3; --workload c4 runs the 32-layer Llama-2-7B
+decoder stack (224 linears, bits allocated to 2.5 per weight).
 
 Prints one JSON line: quantized params/s, the dominant kernel's roofline
 (the SYRK, timed with HIP events on its stream) and the CPU oracle timed on
@@ -37,6 +40,8 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 
 WORKLOADS = {"c1": syn.C1, "c2": syn.C2, "c2r": syn.C2R, "c3": syn.C3, "c5": syn.C5}
+STACK = "c4"   # the decoder stack (not a single layer)
+DEFAULT_WORKLOAD = "c5"
 
 
 def parse():
@@ -44,7 +49,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS) + [STACK],
+                    help=f"default {DEFAULT_WORKLOAD} (c2 with --flipflop / --two-sided)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="approximate CPU budget of the oracle sample")
@@ -61,6 +67,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB fp32 tensor three times (scale for the HBM byte "
                          "counters FETCH_SIZE / WRITE_SIZE) and exit")
+    ap.add_argument("--gemm-calibration", action="store_true",
+                    help="only time the vendor library's dense GEMMs (torch.mm: bf16 and fp32) "
+                         "as a measured achievable MFMA peak, print one JSON line and exit")
     return ap.parse_args()
 
 
@@ -74,6 +83,45 @@ def copy_calibration() -> None:
     torch.cuda.synchronize()
     del y
     print(json.dumps({"copy_calibration_bytes_per_dispatch": 2 ** 30, "dispatches": 3}), flush=True)
+
+
+def gemm_calibration(steps: int) -> None:
+    """The vendor BLAS (torch.mm, hipBLASLt / rocBLAS) on dense products of known size, timed
+    with HIP events: an achievable MFMA rate on this GPU under its clock and power limits, to
+    set beside the datasheet peaks.  Shapes: bf16 8192^3; bf16 A^T A for a 131072 x 4096
+    stream (the full square product over the tokens, the left operand transposed into a
+    contiguous copy first); fp32 8192^3."""
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    res = {}
+
+    def timed(name, fn, flops):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res[name] = {"ms": round(ms, 4), "TFLOP/s": round(flops / (ms / 1e3) / 1e12, 1)}
+
+    a = torch.randn((8192, 8192), device=dev, generator=g).to(torch.bfloat16)
+    b = torch.randn((8192, 8192), device=dev, generator=g).to(torch.bfloat16)
+    timed("bf16_8192^3", lambda: torch.mm(a, b), 2.0 * 8192 ** 3)
+    X = torch.randn((131072, 4096), device=dev, generator=g).to(torch.bfloat16)
+    Xt = X.t().contiguous()
+    timed("bf16_XtX_131072x4096", lambda: torch.mm(Xt, X), 2.0 * 4096 * 4096 * 131072)
+    del X, Xt, a, b
+    a = torch.randn((8192, 8192), device=dev, generator=g)
+    b = torch.randn((8192, 8192), device=dev, generator=g)
+    timed("fp32_8192^3", lambda: torch.mm(a, b), 2.0 * 8192 ** 3)
+    print(json.dumps({"gemm_calibration": res, "steps": steps,
+                      "peaks_TFLOP/s": {"bf16": PEAK_BF16_TFLOPS, "fp32": PEAK_FP32_TFLOPS}}), flush=True)
 
 
 def syrk_flops(n: int, T: int) -> float:
@@ -99,11 +147,15 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_src: str, launch_units: float,
-                         profile: str = "syrk_dma_kernel_c2_hbm_traffic.json"):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", profile)
+def traffic_profile_name(kernel: str, workload: str) -> str:
+    return f"{kernel}_{workload}_hbm_traffic.json"
+
+
+def traffic_from_profile(kernel_src: str, kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload`, from the committed rocprofv3 counter
+    summary of that kernel and workload, if it was taken on the current kernel source;
+    else None."""
+    p = os.path.join(ROOT, "profiles", traffic_profile_name(kernel, workload))
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -136,12 +188,15 @@ def blas_threads() -> int:
         return os.cpu_count() or 1
 
 
-def cpu_baseline(cfg, budget_s: float) -> dict:
-    """The fp64 CPU oracle, as it stands, on a bounded sample of the same workload.
+def oracle_layer_times(cfg, budget_s: float) -> dict:
+    """The fp64 CPU oracle, as it stands, on a bounded sample of one layer workload; returns
+    the full-size time of each part (seconds) and what was sampled.
 
-    Hessians on the first T_s tokens (cost linear in tokens: scaled by T / T_s),
-    BiIP and the damped factorization at full size, GPTQ on R_s rows (rows are
-    independent given U: scaled by out / R_s).  Reported, not a target.
+    Hessians on the first T_s tokens (cost linear in tokens: scaled by T / T_s); BiIP of W
+    and H_X and the damped factorization at full size; H~_G's rescale and rotation at full
+    size when out <= 8192, else on one stripe of 4096 rows, whose row pass stands for every
+    stripe's row pass and column pass alike (x 2 out / 4096); GPTQ on R_s rows (rows are
+    independent given U: scaled by out / R_s).
     """
     import oracle as o
 
@@ -151,20 +206,32 @@ def cpu_baseline(cfg, budget_s: float) -> dict:
     T_s -= T_s % 64
     R_s = int(min(out_n, max(16, 256 * scale * 4096.0 / in_n)))
     t = {}
-    t0 = time.perf_counter()
     X = o.bf16_bits_to_f64(syn.stream(cfg, "x", tokens=T_s))
     G = o.bf16_bits_to_f64(syn.stream(cfg, "g", tokens=T_s))
-    t["prep"] = time.perf_counter() - t0
     t0 = time.perf_counter()
     HX = o.hessian_factor(X)
+    t["hessian_x"] = (time.perf_counter() - t0) * T / T_s
+    t0 = time.perf_counter()
     HG = o.hessian_factor(G)
-    t["hessians_sample"] = time.perf_counter() - t0
+    t["hessian_g"] = (time.perf_counter() - t0) * T / T_s
     del X, G
+    W = syn.weights(cfg).astype(np.float64)
+    s_in, s_out = syn.signs(cfg, "in"), syn.signs(cfg, "out")
+    stripe = 4096
+    full_hg = out_n <= 8192
     t0 = time.perf_counter()
     o.sensitivity(HX, HG)
-    Wt, HXt, HGt, _, _ = o.biip(syn.weights(cfg).astype(np.float64), HX, HG, syn.signs(cfg, "in"),
-                                syn.signs(cfg, "out"), cfg.alpha, o.BIIP_FULL, cfg.had_in, cfg.had_out)
+    Wt, HXt, _, _, d_out = o.biip(W, HX, HG if full_hg else None, s_in, s_out, cfg.alpha,
+                                  o.BIIP_FULL, cfg.had_in, cfg.had_out,
+                                  hg_diag=None if full_hg else np.diag(HG))
     t["sensitivity_biip"] = time.perf_counter() - t0
+    if not full_hg:
+        t0 = time.perf_counter()
+        part = HG[:stripe] / np.outer(d_out[:stripe], d_out)
+        o.rotate_rows(part, s_out, cfg.had_out)
+        t["sensitivity_biip"] += (time.perf_counter() - t0) * 2 * out_n / stripe
+        del part
+    del HG, W
     t0 = time.perf_counter()
     perm = o.act_order_perm(HXt) if cfg.act_order else np.arange(in_n)
     fac = o.damp_and_factor(HXt[np.ix_(perm, perm)] if cfg.act_order else HXt, cfg.damp)
@@ -174,15 +241,26 @@ def cpu_baseline(cfg, budget_s: float) -> dict:
     r = o.quantize_layer(Wt, HXt, None, cfg.bits, cfg.group, cfg.damp, rows=rows, factor=fac,
                          act_order=bool(cfg.act_order), w_clip=bool(cfg.w_clip))
     o.pack_codes(r["gptq"].codes, cfg.bits)
-    t["gptq_pack_sample"] = time.perf_counter() - t0
-    full = (t["hessians_sample"] * T / T_s + t["sensitivity_biip"] + t["factor"]
-            + t["gptq_pack_sample"] * out_n / R_s)
-    return {"value": round(out_n * in_n / full, 1), "unit": "params/s", "cores": blas_threads(),
+    t["gptq_pack"] = (time.perf_counter() - t0) * out_n / R_s
+    sample = (f"Hessians on {T_s} of {T} tokens (x{T / T_s:.1f}), BiIP of W and H_X and the "
+              f"factorization at full size, "
+              + ("H~_G at full size" if full_hg else
+                 f"H~_G's rescale and row pass on {stripe} of {out_n} rows (x{2 * out_n / stripe:.0f} "
+                 f"for every stripe's row and column passes)")
+              + f", GPTQ+pack on {R_s} of {out_n} rows (x{out_n / R_s:.1f})")
+    return {"times_s": t, "sample": sample}
+
+
+def cpu_baseline(cfg, budget_s: float) -> dict:
+    """The oracle's extrapolated full-layer time on the host cores, as params/s.  Reported,
+    not a target."""
+    r = oracle_layer_times(cfg, budget_s)
+    full = sum(r["times_s"].values())
+    return {"value": round(cfg.out * cfg.inp / full, 1), "unit": "params/s", "cores": blas_threads(),
             "kind": "oracle",
-            "sample": (f"Hessians on {T_s} of {T} tokens (x{T / T_s:.1f}), BiIP and factorization at "
-                       f"full size, GPTQ+pack on {R_s} of {out_n} rows (x{out_n / R_s:.1f}); "
-                       f"extrapolated full-layer time {full:.1f} s"),
-            "measured_s": {k: round(v, 2) for k, v in t.items()}}
+            "sample": r["sample"] + f"; extrapolated full-layer time {full:.1f} s",
+            "extrapolated_s": {k: round(v, 2) for k, v in r["times_s"].items()}}
+
 
 # The seven linears of one Llama-2-7B decoder block (out, in) and the block count: the
 # model the pages time decoding on.  32 x 7 = 224 packed layers per token.
@@ -440,8 +518,8 @@ def flipflop_main(a) -> None:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile(
-                         os.path.join(ROOT, "post_quantization_syrk_amd", "csrc", "flipflop.hip"), 1,
-                         "qform_kernel_c2_hbm_traffic.json"),
+                         os.path.join(ROOT, "post_quantization_syrk_amd", "csrc", "flipflop.hip"),
+                         "qform_kernel", a.workload),
                      "kernel": "qform_kernel", "algorithmic_flops_per_launch": flops},
         "cpu_baseline": cpu,
         "phases_ms_per_iteration": {k_: round(v / (iters * a.steps), 3) for k_, v in phases.items()},
@@ -471,6 +549,223 @@ def two_sided_cpu_baseline(cfg) -> dict:
                        f"O(m^2 n^2) work count to {cfg.out} x {cfg.inp}: {full:.3g} s")}
 
 
+def stack_work(bits_of) -> dict:
+    """Algorithmic work of one pass over the decoder stack: SYRK flops (each distinct stream's
+    factor once: per layer 4 activation and 7 gradient factors), fp32 flops (feedback
+    products and factorizations per sublayer) and HBM bytes (rotation and packing per
+    sublayer).  bits_of(layer, k) gives sublayer k's width."""
+    T = syn.STACK_TOKENS
+    syrk = fp32 = hbm = 0.0
+    for layer in range(syn.STACK_LAYERS):
+        seen = set()
+        for k, (_, out_n, in_n, xs, _, _) in enumerate(syn.LLAMA2_7B_SUBLAYERS):
+            if xs not in seen:
+                seen.add(xs)
+                syrk += syrk_flops(in_n, T)
+            syrk += syrk_flops(out_n, T)
+            fp32 += float(out_n) * in_n * (in_n - 128) + 2.0 * float(in_n) ** 3 / 3
+            hbm += (8.0 * (out_n * in_n + in_n * in_n + out_n * out_n)
+                    + out_n * in_n * (1 + bits_of(layer, k) / 8))
+    return {"syrk_flops": syrk, "fp32_flops": fp32, "hbm_bytes": hbm}
+
+
+def stack_cpu_baseline(budget_s: float) -> dict:
+    """The oracle on samples of the stack's three sublayer shapes (4096 x 4096, 11008 x 4096,
+    4096 x 11008 at 32768 tokens), each as oracle_layer_times, combined with the stack's
+    counts: per layer 3 + 1 activation factors (4096 / 11008 wide), 5 + 2 gradient factors
+    (4096 / 11008 wide), and BiIP, factorization and GPTQ for 4 + 2 + 1 sublayers; x 32."""
+    cfgs = syn.stack_sublayer_configs(0)
+    shape = {"sq": cfgs[0], "wide_out": cfgs[4], "wide_in": cfgs[6]}
+    r = {k: oracle_layer_times(c, budget_s / 3.0) for k, c in shape.items()}
+    rest = lambda k: sum(v for n, v in r[k]["times_s"].items() if not n.startswith("hessian"))  # noqa: E731
+    per_layer = (3 * r["sq"]["times_s"]["hessian_x"] + r["wide_in"]["times_s"]["hessian_x"]
+                 + 5 * r["sq"]["times_s"]["hessian_g"] + 2 * r["wide_out"]["times_s"]["hessian_g"]
+                 + 4 * rest("sq") + 2 * rest("wide_out") + rest("wide_in"))
+    full = per_layer * syn.STACK_LAYERS
+    params = syn.STACK_LAYERS * sum(o_ * i_ for _, o_, i_, _, _, _ in syn.LLAMA2_7B_SUBLAYERS)
+    return {"value": round(params / full, 1), "unit": "params/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": ("the three sublayer shapes of layer 0, each: " + r["sq"]["sample"]
+                       + f"; combined per layer and x{syn.STACK_LAYERS}: extrapolated stack time "
+                       f"{full:.0f} s (allocation not counted)"),
+            "extrapolated_s_per_layer": round(per_layer, 2)}
+
+
+def stack_main(a) -> None:
+    """The decoder stack: 32 Llama-2-7B layers x 7 linears (q, k, v, o 4096 x 4096; gate, up
+    11008 x 4096; down 4096 x 11008), 32768 calibration tokens per layer, bits in {2, 3, 4}
+    allocated from tr(H_G) tr(H_X) to 2.5 bits per weight on average.
+
+    One step, inputs resident in HBM (every layer's 4 activation streams, q/k/v and gate/up
+    sharing theirs, 7 gradient streams and 7 weight matrices):
+      pass 1: per layer, H_X of each distinct activation stream and H_G of each sublayer
+              (kq_accumulate_hessian), the 224 sensitivities (kq_sensitivity_async);
+      bits:   one synchronization, the sensitivities to the host, kq_allocate_bits;
+      pass 2: per sublayer, BiIP out of place from the raw factors (q/k/v and gate/up share
+              H_X) and GPTQ to packed codes at the allocated width (kq_quantize_layer).
+    The streams are drawn on the device (torch's generator, seeded per layer and stream) with
+    the stack's recipe: per-channel std exp(sigma N(0, 1)), sigma per layer in U[0.5, 2] as
+    the parity tests' generator gives it, N(0, 1) entries, rounded to bf16; weights
+    N(0, 0.02^2) rounded to bf16.  Drawing 138 GB on the host would dominate the run."""
+    import torch
+    import post_quantization_syrk_amd as kq
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kq.load_library()
+    stream = torch.cuda.current_stream()
+    T, L = syn.STACK_TOKENS, syn.STACK_LAYERS
+    subl = syn.LLAMA2_7B_SUBLAYERS
+    gen = torch.Generator(device=dev)
+
+    def draw(seed, rows, n, sigma):
+        gen.manual_seed(seed)
+        sc = torch.exp(sigma * torch.randn(n, device=dev, generator=gen))
+        out = torch.empty((rows, n), dtype=torch.bfloat16, device=dev)
+        for r0 in range(0, rows, 8192):
+            r1 = min(rows, r0 + 8192)
+            out[r0:r1] = (torch.randn((r1 - r0, n), device=dev, generator=gen) * sc).to(torch.bfloat16)
+        return out
+
+    t0 = time.time()
+    layers = []
+    for layer in range(L):
+        sx, sg = syn.stack_layer_sigmas(layer)
+        base = 1_000_003 * (layer + 1)
+        xs, hx = {}, {}
+        for _, _, in_n, xid, _, _ in subl:
+            if xid not in xs:
+                xs[xid] = draw(base + xid, T, in_n, sx)
+                hx[xid] = torch.empty((in_n, in_n), device=dev)
+        subs = []
+        for k, (_, out_n, in_n, xid, hin, hout) in enumerate(subl):
+            gen.manual_seed(base + 100 + k)
+            W = (torch.randn((out_n, in_n), device=dev, generator=gen) * 0.02).to(torch.bfloat16).float()
+            subs.append(dict(
+                G=draw(base + 10 + k, T, out_n, sg), HG=torch.empty((out_n, out_n), device=dev), W=W,
+                s_in=(torch.randint(0, 2, (in_n,), device=dev, generator=gen, dtype=torch.int8) * 2 - 1),
+                s_out=(torch.randint(0, 2, (out_n,), device=dev, generator=gen, dtype=torch.int8) * 2 - 1),
+                packed=torch.empty(out_n * in_n * 4 // 32, dtype=torch.int32, device=dev),
+                scales=torch.empty((out_n, in_n // 128), device=dev),
+                zeros=torch.empty((out_n, in_n // 128), dtype=torch.uint8, device=dev),
+                out=out_n, inp=in_n, xid=xid, hin=hin, hout=hout))
+        layers.append((xs, hx, subs))
+    nmax = max(max(o_, i_) for _, o_, i_, _, _, _ in subl)
+    HXt = torch.empty(nmax * nmax, device=dev)
+    HGt = torch.empty(nmax * nmax, device=dev)
+    Wt = torch.empty(max(o_ * i_ for _, o_, i_, _, _, _ in subl), device=dev)
+    d_in, d_out = torch.empty(nmax, device=dev), torch.empty(nmax, device=dev)
+    params = {b: kq.make_params(b, 128, 128, 0.01) for b in (2, 3, 4)}
+    ws_bytes = max(kq.kq_quantize_layer_workspace(params[b], o_, i_, False)
+                   for b in (2, 3, 4) for _, o_, i_, _, _, _ in subl)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    sens = torch.empty((L * len(subl), 3), dtype=torch.float64, device=dev)
+    numel = [o_ * i_ for _ in range(L) for _, o_, i_, _, _, _ in subl]
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(record):
+        syrk_ev = []
+        e = [ev() for _ in range(4)] if record else None
+        if record:
+            e[0].record(stream)
+        i = 0
+        for xs, hx, subs in layers:
+            for xid, X in xs.items():
+                if record:
+                    syrk_ev.append((ev(), ev()))
+                    syrk_ev[-1][0].record(stream)
+                kq.kq_accumulate_hessian(X, hx[xid], stream=stream)
+                if record:
+                    syrk_ev[-1][1].record(stream)
+            for sb in subs:
+                if record:
+                    syrk_ev.append((ev(), ev()))
+                    syrk_ev[-1][0].record(stream)
+                kq.kq_accumulate_hessian(sb["G"], sb["HG"], stream=stream)
+                if record:
+                    syrk_ev[-1][1].record(stream)
+                kq.kq_sensitivity_async(hx[sb["xid"]], sb["HG"], sens[i], stream=stream)
+                i += 1
+        if record:
+            e[1].record(stream)
+        s_host = sens[:, 2].cpu().numpy()          # synchronizes the stream
+        bits = kq.kq_allocate_bits(list(s_host), numel, (2, 3, 4), 5, 2)
+        if record:
+            e[2].record(stream)
+        i = 0
+        for xs, hx, subs in layers:
+            for sb in subs:
+                o_, i_ = sb["out"], sb["inp"]
+                hxt, hgt = HXt[:i_ * i_].view(i_, i_), HGt[:o_ * o_].view(o_, o_)
+                wt = Wt[:o_ * i_].view(o_, i_)
+                kq.kq_biip_rotate(sb["W"], wt, hx[sb["xid"]], hxt, sb["HG"], hgt, sb["s_in"],
+                                  sb["s_out"], d_in[:i_], d_out[:o_], 0.25, kq.KQ_BIIP_FULL,
+                                  sb["hin"], sb["hout"], stream=stream)
+                b = bits[i]
+                packed = sb["packed"][:o_ * i_ * b // 32].view(o_, i_ * b // 32)
+                kq.kq_quantize_layer(params[b], wt, hxt, hgt, packed, sb["scales"], sb["zeros"], ws,
+                                     stream=stream)
+                i += 1
+        if record:
+            e[3].record(stream)
+        return e, syrk_ev, bits
+
+    for _ in range(a.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    recs = []
+    t_start = time.perf_counter()
+    for _ in range(a.steps):
+        recs.append(step(True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / a.steps
+    total_params = float(sum(numel))
+    stages = {nm: float(np.mean([r[0][i].elapsed_time(r[0][i + 1]) for r in recs]))
+              for i, nm in enumerate(["pass1_hessians_sensitivities", "allocation", "pass2_biip_quantize"])}
+    syrk_ms = [s0.elapsed_time(s1) for r in recs for s0, s1 in r[1]]
+    bits = recs[-1][2]
+    work = stack_work(lambda layer, k: bits[layer * len(subl) + k])
+    n_syrk = len(syrk_ms) / a.steps
+    flops_per_launch = work["syrk_flops"] / n_syrk
+    achieved = flops_per_launch / (float(np.mean(syrk_ms)) / 1e3) / 1e12
+    lb = {"syrk": work["syrk_flops"] / (PEAK_BF16_TFLOPS * 1e9),
+          "factor_and_feedback": work["fp32_flops"] / (PEAK_FP32_TFLOPS * 1e9),
+          "hbm": work["hbm_bytes"] / (PEAK_HBM_GBS * 1e6)}
+    lb_ms = sum(lb.values())
+    cpu = None if a.no_cpu_baseline else stack_cpu_baseline(a.cpu_seconds)
+    line = {
+        "metric": "quantized params/s per layer incl. Hessian build",
+        "value": round(total_params / (ms_per_step / 1e3), 1), "unit": "params/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 products / f32 accumulate and quantizer",
+        "data": "synthetic (log-normal-channel streams drawn on the device per layer, Llama-shaped)",
+        "config": {"workload": "llama2-7b-decoder-stack-32x7-T32768-mixed-2.5bit", "layers": L,
+                   "sublayers": L * len(subl), "tokens": T, "params": int(total_params),
+                   "bits_allowed": [2, 3, 4], "avg_bits_target": 2.5,
+                   "avg_bits": round(sum(b * n for b, n in zip(bits, numel)) / total_params, 4),
+                   "bits_count": {str(b): bits.count(b) for b in (2, 3, 4)},
+                   "group": 128, "block": 128, "alpha": 0.25, "damp": 0.01},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_profile(
+                         os.path.join(ROOT, "post_quantization_syrk_amd", "csrc", "syrk.hip"),
+                         "syrk_dma_kernel", STACK),
+                     "kernel": "syrk_dma_kernel",
+                     "algorithmic_flops_per_launch": flops_per_launch,
+                     "launches_per_step": int(n_syrk)},
+        "cpu_baseline": cpu,
+        "pipeline_roofline": {"lower_bound_ms": round(lb_ms, 3), "frac": round(lb_ms / ms_per_step, 4),
+                              "terms_ms": {k: round(v, 3) for k, v in lb.items()}},
+        "stages_ms": {k: round(v, 3) for k, v in stages.items()},
+        "syrk_ms_per_step": round(sum(syrk_ms) / a.steps, 3),
+        "input_generation_s": round(gen_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -479,6 +774,18 @@ def main():
         sys.exit(2)
     if a.copy_calibration:
         copy_calibration()
+        return
+    if a.gemm_calibration:
+        gemm_calibration(a.steps)
+        return
+    if a.workload is None:
+        a.workload = "c2" if (a.flipflop is not None or a.two_sided) else DEFAULT_WORKLOAD
+    if a.workload == STACK:
+        if a.flipflop is not None or a.two_sided or a.deploy_bits is not None:
+            print("bench.py: --workload c4 times the GPTQ path of the decoder stack only",
+                  file=sys.stderr)
+            sys.exit(2)
+        stack_main(a)
         return
     if a.deploy_bits is not None:
         deploy_main(a)
@@ -574,7 +881,7 @@ def main():
     flops_per_launch = 0.5 * (syrk_flops(in_n, T) + syrk_flops(out_n, T))
     achieved = flops_per_launch / (syrk_launch_ms / 1e3) / 1e12
     traffic = traffic_from_profile(os.path.join(ROOT, "post_quantization_syrk_amd", "csrc", "syrk.hip"),
-                                   flops_per_launch)
+                                   "syrk_dma_kernel", a.workload)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel": "syrk_dma_kernel",

@@ -39,7 +39,7 @@ def test_pipeline_lower_bound_terms():
     assert all(wide[k] > lb[k] for k in lb)
 
 
-def _profile(tmp_path, src_text, recorded_hash, name="k_hbm_traffic.json"):
+def _profile(tmp_path, src_text, recorded_hash, name="k_w1_hbm_traffic.json"):
     (tmp_path / "profiles").mkdir(exist_ok=True)
     src = tmp_path / "k.hip"
     src.write_text(src_text)
@@ -53,13 +53,15 @@ def test_traffic_taken_only_from_a_profile_of_the_current_source(tmp_path, monke
     src = _profile(tmp_path, "kernel v1", "0" * 16)
     current = bench.source_hash(src)
     _profile(tmp_path, "kernel v1", current)
-    assert bench.traffic_from_profile(src, 1.0, profile="k_hbm_traffic.json") == 123456789
+    assert bench.traffic_from_profile(src, "k", "w1") == 123456789
+    # another workload's counters are not this one's
+    assert bench.traffic_from_profile(src, "k", "w2") is None
     # the kernel changed after the counters were taken: no traffic figure
     with open(src, "w") as f:
         f.write("kernel v2")
-    assert bench.traffic_from_profile(src, 1.0, profile="k_hbm_traffic.json") is None
+    assert bench.traffic_from_profile(src, "k", "w1") is None
     # no profile at all
-    assert bench.traffic_from_profile(src, 1.0, profile="missing.json") is None
+    assert bench.traffic_from_profile(src, "missing", "w1") is None
 
 
 def test_committed_profiles_name_their_kernel_source():
