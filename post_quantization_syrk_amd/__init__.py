@@ -27,7 +27,7 @@ EXPORTED = ("kq_version", "kq_last_error", "kq_accumulate_hessian", "kq_sensitiv
             "kq_biip_rotate", "kq_quantize_layer_workspace", "kq_quantize_layer",
             "kq_allocate_bits", "kq_deploy_linear", "kq_deploy_linear_group",
             "kq_flipflop_workspace", "kq_flipflop", "kq_quantize_two_sided_workspace",
-            "kq_quantize_two_sided")
+            "kq_quantize_two_sided", "kq_testing_select")
 
 
 class KQError(RuntimeError):
@@ -78,7 +78,11 @@ _SIGS = {
                                _sz, _vp, _vp], _int),
     "kq_flipflop": ([_vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _sz,
                      ctypes.POINTER(ctypes.c_double), _vp], _int),
+    "kq_testing_select": ([_int, _i64], _int),
 }
+
+# include/kq_testing.h: implementation selection for tests
+KQ_TESTING_SYRK_KERNEL, KQ_TESTING_FACTOR_PANEL_TILES, KQ_TESTING_ROW_LDS_BYTES = range(3)
 
 _lib = None
 
@@ -99,6 +103,22 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     if path is None:
         _lib = lib
     return lib
+
+
+class testing_select:
+    """Context manager over kq_testing_select: forces one implementation path for the calls
+    made inside the block, then restores the default."""
+
+    def __init__(self, knob: int, value: int):
+        self.knob, self.value = knob, value
+
+    def __enter__(self):
+        _check(load_library().kq_testing_select(self.knob, self.value), "kq_testing_select")
+        return self
+
+    def __exit__(self, *exc):
+        _check(load_library().kq_testing_select(self.knob, -1), "kq_testing_select")
+        return False
 
 
 def _check(status: int, fn: str) -> None:

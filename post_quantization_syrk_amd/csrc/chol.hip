@@ -24,8 +24,6 @@
 // through U_ab = -U_a Z_b[a rows].
 #include "kq_internal.h"
 
-#include <stdlib.h>
-
 namespace kq {
 namespace {
 
@@ -750,9 +748,9 @@ kq_status damp_and_factor(const float* HX, float* F, float* T, uint8_t* dead, do
   // factor once, ahead of the update, instead of in every tile (a third of a tile's products);
   // on the shorter steps the extra launch would cost more than it saves (c3, 11008 wide:
   // quantize 17.5 -> 16.1 ms; c2 is unchanged)
-  // (KQ_ZPRE_TILES overrides the threshold; a tuning knob, both paths give the same factor)
-  int64_t zpre_tiles = 2 * (int64_t)device_cu_count();
-  if (const char* env = getenv("KQ_ZPRE_TILES")) zpre_tiles = atoll(env);
+  // (tests can move the threshold: both paths give the same factor)
+  const int64_t zpre_tiles =
+      testing_value(KQ_TESTING_FACTOR_PANEL_TILES, 2 * (int64_t)device_cu_count());
   for (int64_t s0 = n - NB; s0 >= NB; s0 -= NB) {
     const int64_t m = ceil_div(s0, 128);
     const int64_t tiles = m * (m + 1) / 2;

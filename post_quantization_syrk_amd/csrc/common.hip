@@ -3,6 +3,8 @@
 
 #include <string.h>
 
+#include <atomic>
+
 namespace kq {
 
 static thread_local char g_last_error[512] = "";
@@ -27,6 +29,15 @@ int device_cu_count() {
     cache[dev] = cus;
   }
   return cache[dev];
+}
+
+constexpr int N_TESTING_KNOBS = 3;
+static std::atomic<int64_t> g_testing[N_TESTING_KNOBS] = {{-1}, {-1}, {-1}};
+
+int64_t testing_value(int knob, int64_t dflt) {
+  if (knob < 0 || knob >= N_TESTING_KNOBS) return dflt;
+  const int64_t v = g_testing[knob].load(std::memory_order_relaxed);
+  return v < 0 ? dflt : v;
 }
 
 __global__ void fill_f32_kernel(float* __restrict__ p, int64_t n, float v) {
@@ -64,3 +75,11 @@ kq_status fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
 extern "C" int kq_version(void) { return 200; /* 0.2.0: act_order, w_clip */ }
 
 extern "C" const char* kq_last_error(void) { return kq::g_last_error; }
+
+extern "C" kq_status kq_testing_select(int knob, int64_t value) {
+  if (knob < 0 || knob >= kq::N_TESTING_KNOBS)
+    return kq::fail(KQ_EINVAL, "kq_testing_select: unknown knob %d", knob);
+  if (value < -1) return kq::fail(KQ_EINVAL, "kq_testing_select: value %lld", (long long)value);
+  kq::g_testing[knob].store(value, std::memory_order_relaxed);
+  return KQ_OK;
+}

@@ -524,14 +524,6 @@ __global__ __launch_bounds__(THREADS) void gemm_nn_dma_kernel(DArgs a) {
     }
 }
 
-// 1 = direct-to-LDS kernel for plain row-major products (default), 0 = register-staged kernel
-// for every product (KQ_GEMM_VARIANT; a tuning knob, both compute the same C).
-int gemm_variant() {
-  const char* env = getenv("KQ_GEMM_VARIANT");
-  if (env && atoi(env) == 0) return 0;
-  return 1;
-}
-
 }  // namespace
 
 kq_status gemm_f32(const GemmArgs& g, hipStream_t s) {
@@ -546,8 +538,7 @@ kq_status gemm_f32(const GemmArgs& g, hipStream_t s) {
   const bool aligned = ((uintptr_t)g.A % 16 == 0) && ((uintptr_t)g.B % 16 == 0) &&
                        g.lda % 4 == 0 && g.ldb % 4 == 0 && g.K % 4 == 0 && g.N % 4 == 0;
   if (!g.transA && !g.transB && !g.a_upper && !g.b_upper && !g.upper_only && !g.red &&
-      (g.batch <= 1) && aligned && g.K > 0 && 128 * g.lda + (int64_t)DBK * g.ldb < ((int64_t)1 << 32) &&
-      gemm_variant() == 1) {
+      (g.batch <= 1) && aligned && g.K > 0 && 128 * g.lda + (int64_t)DBK * g.ldb < ((int64_t)1 << 32)) {
     DArgs d;
     d.M = g.M; d.N = g.N; d.K = g.K;
     d.A = g.A; d.lda = g.lda; d.B = g.B; d.ldb = g.ldb; d.C = g.C; d.ldc = g.ldc;

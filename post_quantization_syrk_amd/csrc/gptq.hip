@@ -23,7 +23,6 @@
 #include "kq_internal.h"
 
 #include <math.h>
-#include <stdlib.h>
 
 #include <utility>
 
@@ -639,15 +638,11 @@ __global__ __launch_bounds__(256) void gather_cols_direct_kernel(const T* __rest
   dst[r * n + c] = src[sr * n + idx[c]];
 }
 
-// Largest row staged in LDS by the row kernels (KQ_ROW_LDS_MAX bytes; 0 forces the direct
-// paths, which otherwise serve rows longer than 16384 floats).
+// Largest row staged in LDS by the row kernels (bytes; rows longer than 16384 floats take
+// the direct paths, which tests can force with 0).
 size_t row_lds_max() {
-  const char* env = getenv("KQ_ROW_LDS_MAX");
-  if (env) {
-    const long v = atol(env);
-    if (v >= 0 && v <= 65536) return (size_t)v;
-  }
-  return 65536;
+  const int64_t v = testing_value(KQ_TESTING_ROW_LDS_BYTES, 65536);
+  return (size_t)(v > 65536 ? 65536 : v);
 }
 
 template <typename T>

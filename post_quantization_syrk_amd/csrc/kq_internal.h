@@ -7,6 +7,7 @@
 #include <stdio.h>
 
 #include "../../include/kq.h"
+#include "../../include/kq_testing.h"
 
 namespace kq {
 
@@ -21,6 +22,9 @@ inline bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
+
+// The value a test selected for `knob` with kq_testing_select, or `dflt` when none is set.
+int64_t testing_value(int knob, int64_t dflt);
 
 // fp32 fill kernel launcher (used instead of hipMemsetAsync so captured graphs stay valid).
 kq_status fill_f32(float* p, int64_t n, float v, hipStream_t s);

@@ -28,14 +28,11 @@
 //   * Partial tiles are added to H with fp32 atomics (H is zeroed first unless
 //     accumulating); a final pass mirrors the lower triangle into the upper one.
 //
-// Register-staged kernel (syrk_bf16_kernel, selected by KQ_SYRK_VARIANT=0..3): 64-token
-// stages loaded into registers as 8 tokens x 4 channels per thread, transposed in registers
-// and stored channel-major into two LDS buffers with an XOR-permuted chunk layout; 4 or 8
-// waves; split-major or tile-major order.  It also serves strides too large for the direct
-// kernel's 32-bit per-stage offsets.
+// Register-staged kernel (syrk_bf16_kernel): 64-token stages loaded into registers as 8
+// tokens x 4 channels per thread, transposed in registers and stored channel-major into two
+// LDS buffers with an XOR-permuted chunk layout; 4 or 8 waves; split-major or tile-major
+// order.  It serves strides too large for the direct kernel's 32-bit per-stage offsets.
 #include "kq_internal.h"
-
-#include <stdlib.h>
 
 namespace kq {
 namespace {
@@ -348,40 +345,28 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* p) {
 
 struct DmaArgs {
   SyrkArgs s;
-  int per_xcd;      // tiles per XCD region (region order) / (split, tile) items per XCD
+  int per_xcd;      // tiles per XCD region
   int xcds;
-  int token_major;  // 1: each XCD walks a contiguous range of (split, tile) items
 };
 
-// DNST = stages in the LDS ring (4: 128 KB, 5: 160 KB); each buffer is its own LDS object so
-// that the compiler can tell the reads of one stage from the copies into another.
-template <int DNST>
+// DNST = stages in the LDS ring (128 KB); each buffer is its own LDS object so that the
+// compiler can tell the reads of one stage from the copies into another.
+constexpr int DNST = 4;
 __global__ __launch_bounds__(DWAVES * 64) void syrk_dma_kernel(DmaArgs d) {
-  static_assert(DNST == 4 || DNST == 5, "ring of 4 or 5 stages");
   const SyrkArgs& a = d.s;
   __shared__ __attribute__((aligned(1024))) uint16_t b0[DSTAGE];
   __shared__ __attribute__((aligned(1024))) uint16_t b1[DSTAGE];
   __shared__ __attribute__((aligned(1024))) uint16_t b2[DSTAGE];
   __shared__ __attribute__((aligned(1024))) uint16_t b3[DSTAGE];
-  __shared__ __attribute__((aligned(1024))) uint16_t b4[DNST == 5 ? DSTAGE : 8];
 
   // workgroup u runs on XCD u mod xcds; each XCD walks its own contiguous region of tiles,
   // split by split, so the tiles resident on one XCD share panels in its L2 and all XCDs
   // stream the same token range at the same time
-  // (token-major order: each XCD walks its own range of (split, tile) items in split-major
-  // order, so its resident workgroups share one token range and a compact set of tiles)
   const int u = blockIdx.x;
   const int xcd = u % d.xcds;
   const int q = u / d.xcds;
-  int split, tile;
-  if (d.token_major) {
-    const int item = xcd * d.per_xcd + q;
-    split = item / a.ntiles;
-    tile = item % a.ntiles;
-  } else {
-    split = q / d.per_xcd;
-    tile = xcd * d.per_xcd + q % d.per_xcd;
-  }
+  const int split = q / d.per_xcd;
+  const int tile = xcd * d.per_xcd + q % d.per_xcd;
   if (tile >= a.ntiles || split >= a.splits) return;
   int bi, bj;
   tile_of(tile, a.nb, bi, bj);
@@ -464,7 +449,6 @@ __global__ __launch_bounds__(DWAVES * 64) void syrk_dma_kernel(DmaArgs d) {
   sources(1); issue(b1);
   sources(2); issue(b2);
   sources(3); issue(b3);
-  if constexpr (DNST == 5) { sources(4); issue(b4); }
   __builtin_amdgcn_s_waitcnt(wait_vm(2 * DMA_PER_PANEL * (DNST - 1)));
   lds_barrier();
   read(b0, 0, xa, xb);
@@ -502,18 +486,10 @@ __global__ __launch_bounds__(DWAVES * 64) void syrk_dma_kernel(DmaArgs d) {
     __builtin_amdgcn_sched_barrier(0);                             \
   }
   for (int s0 = 0; s0 < nst; s0 += DNST) {
-    if constexpr (DNST == 4) {
-      KQ_DMA_STEP(0, b0, b1)
-      KQ_DMA_STEP(1, b1, b2)
-      KQ_DMA_STEP(2, b2, b3)
-      KQ_DMA_STEP(3, b3, b0)
-    } else {
-      KQ_DMA_STEP(0, b0, b1)
-      KQ_DMA_STEP(1, b1, b2)
-      KQ_DMA_STEP(2, b2, b3)
-      KQ_DMA_STEP(3, b3, b4)
-      KQ_DMA_STEP(4, b4, b0)
-    }
+    KQ_DMA_STEP(0, b0, b1)
+    KQ_DMA_STEP(1, b1, b2)
+    KQ_DMA_STEP(2, b2, b3)
+    KQ_DMA_STEP(3, b3, b0)
   }
 #undef KQ_DMA_STEP
   // the ring's trailing copies (zeros) must land before the workgroup's LDS is released
@@ -574,65 +550,10 @@ __global__ __launch_bounds__(256) void mirror_lower_to_upper(float* __restrict__
   }
 }
 
-// Kernel variant: 4 = direct-to-LDS kernel (default); 0..3 = register-staged kernel with
-// bit 0 = 8 waves (else 4), bit 1 = split-major order.  KQ_SYRK_VARIANT overrides the default
-// (a tuning knob; every variant computes the same H).
-int syrk_variant() {
-  const char* env = getenv("KQ_SYRK_VARIANT");
-  if (env) {
-    const int v = atoi(env);
-    if (v >= 0 && v <= 4) return v;
-  }
-  return 4;
-}
-
-// Stages in the direct-to-LDS kernel's ring (KQ_SYRK_RING = 4 or 5; a tuning knob).
-int syrk_order() {
-  const char* env = getenv("KQ_SYRK_ORDER");
-  return env && atoi(env) == 1 ? 1 : 0;
-}
-
-// Token splits for the token-major order: the smallest S whose items per XCD
-// (ceil(ntiles S / xcds)) fill whole rounds of the XCD's CUs to within 3 %, at least two
-// workgroups per CU.
-int choose_splits_tm(int ntiles, int cu_per_xcd, int xcds, int64_t T) {
-  const char* env = getenv("KQ_SYRK_SPLITS");
-  if (env) {
-    int v = atoi(env);
-    if (v >= 1) return v;
-  }
-  int64_t max_s = T / (8 * DBK);
-  if (max_s < 1) max_s = 1;
-  if (max_s > 64) max_s = 64;
-  int best = 1;
-  double best_eff = 0.0;
-  for (int s = 1; s <= max_s; ++s) {
-    const int64_t items = ((int64_t)ntiles * s + xcds - 1) / xcds;
-    const int64_t rounds = (items + cu_per_xcd - 1) / cu_per_xcd;
-    const double eff = (double)ntiles * s / (double)(rounds * cu_per_xcd * xcds);
-    if (items < 2LL * cu_per_xcd) continue;
-    if (eff >= 0.97) return s;
-    if (eff > best_eff + 1e-9) { best_eff = eff; best = s; }
-  }
-  return best;
-}
-
-int syrk_ring() {
-  const char* env = getenv("KQ_SYRK_RING");
-  if (env && atoi(env) == 4) return 4;
-  if (env && atoi(env) == 5) return 5;
-  return 4;
-}
-
 // Token splits for the direct-to-LDS kernel: the smallest S (>= 2 stages of work per tile
 // each) whose per-XCD workgroup count fills whole rounds of the XCD's CUs to within 3 %, with
 // at least two workgroups per CU in all.
 int choose_splits_dma(int per_xcd, int cu_per_xcd, int xcds, int64_t T) {
-  const char* env = getenv("KQ_SYRK_SPLITS");
-  if (env) {
-    int v = atoi(env);
-    if (v >= 1) return v;
-  }
   int64_t max_s = T / (8 * DBK);
   if (max_s < 1) max_s = 1;
   if (max_s > 64) max_s = 64;
@@ -649,16 +570,11 @@ int choose_splits_dma(int per_xcd, int cu_per_xcd, int xcds, int64_t T) {
   return best;
 }
 
+// Token splits for the register-staged kernel: at least ~2048 workgroups (8 per CU) for load
+// balance, a multiple of 8, at least 8 stages per split.
 int choose_splits(int ntiles, int64_t T) {
-  const char* env = getenv("KQ_SYRK_SPLITS");
-  if (env) {
-    int v = atoi(env);
-    if (v >= 1) return v;
-  }
-  // at least ~2048 workgroups (8 per CU) for load balance, a multiple of 8, at least 8
   int s = 8;
   while ((int64_t)ntiles * s < 2048 && s < 64) s += 8;
-  // keep at least 8 stages per split
   int64_t max_s = T / (8 * BK);
   if (max_s < 1) max_s = 1;
   if (s > max_s) s = (int)max_s;
@@ -699,25 +615,23 @@ extern "C" kq_status kq_accumulate_hessian(const uint16_t* A_bf16, int64_t T, in
     a.splits = choose_splits(a.ntiles, T);
     a.tok_split = ceil_div(ceil_div(T, a.splits), BK) * BK;
     a.splits = (int)ceil_div(T, a.tok_split);
-    int variant = syrk_variant();
-    // the direct-to-LDS kernel keeps 32-bit per-lane offsets within a 32-token stage
+    // the direct-to-LDS kernel (the default) keeps 32-bit per-lane offsets within a 32-token
+    // stage; larger strides take the register-staged kernel (so may the engine's tests)
+    int variant = (int)testing_value(KQ_TESTING_SYRK_KERNEL, 4);
+    if (variant < 0 || variant > 4) variant = 4;
     if (variant == 4 && (int64_t)DBK * lda + n >= ((int64_t)1 << 32)) variant = 3;
     if (variant == 4) {
       DmaArgs d;
       d.xcds = device_cu_count() % 8 == 0 ? 8 : 1;
       const int cu_per_xcd = device_cu_count() / d.xcds;
-      d.token_major = syrk_order();
       d.per_xcd = (int)ceil_div(a.ntiles, d.xcds);
-      a.splits = d.token_major ? choose_splits_tm(a.ntiles, cu_per_xcd, d.xcds, T)
-                               : choose_splits_dma(d.per_xcd, cu_per_xcd, d.xcds, T);
+      a.splits = choose_splits_dma(d.per_xcd, cu_per_xcd, d.xcds, T);
       a.tok_split = ceil_div(ceil_div(T, a.splits), DBK) * DBK;
       a.splits = (int)ceil_div(T, a.tok_split);
-      if (d.token_major) d.per_xcd = (int)ceil_div((int64_t)a.ntiles * a.splits, d.xcds);
       d.s = a;
-      const int64_t g = (int64_t)d.xcds * d.per_xcd * (d.token_major ? 1 : a.splits);
+      const int64_t g = (int64_t)d.xcds * d.per_xcd * a.splits;
       if (g > 0x7FFFFFFF) return fail(KQ_ESHAPE, "kq_accumulate_hessian: too many tiles");
-      if (syrk_ring() == 5) syrk_dma_kernel<5><<<dim3((unsigned)g), dim3(DWAVES * 64), 0, s>>>(d);
-      else syrk_dma_kernel<4><<<dim3((unsigned)g), dim3(DWAVES * 64), 0, s>>>(d);
+      syrk_dma_kernel<<<dim3((unsigned)g), dim3(DWAVES * 64), 0, s>>>(d);
       KQ_LAUNCHED("syrk_dma_kernel");
     } else {
     const int64_t grid = (int64_t)a.ntiles * a.splits;

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared_symbols():
-    src = open(os.path.join(ROOT, "include", "kq.h")).read()
+    import glob
+    src = "".join(open(f).read() for f in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))))
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(kq_[a-z_0-9]+)\s*\(", src)))
 
@@ -177,3 +178,12 @@ def test_automatic_hadamard_block_beyond_8192_is_refused_on_host():
     L2 = kq.DeployLayer(buf, buf, buf, 4, 128, 16384, None, None, None, None, 0, 0, buf)
     arr2 = (kq.DeployLayer * 1)(L2)
     assert lib.kq_deploy_linear_group(arr2, 1, 256, buf, None) == kq.KQ_ENOTIMPL
+
+
+def test_testing_selector_rejects_bad_arguments():
+    lib = _raw()
+    assert lib.kq_testing_select(99, 0) == kq.KQ_EINVAL
+    assert lib.kq_testing_select(kq.KQ_TESTING_SYRK_KERNEL, -2) == kq.KQ_EINVAL
+    with kq.testing_select(kq.KQ_TESTING_ROW_LDS_BYTES, 0):
+        pass
+    assert lib.kq_testing_select(kq.KQ_TESTING_ROW_LDS_BYTES, -1) == kq.KQ_OK

@@ -117,10 +117,15 @@ def test_quantize_act_order_and_clip(bits, block, act_order, w_clip, with_hg):
         assert np.any(ref["clip_choice"] > 0)
 
 
-def test_quantize_act_order_dead_channel_and_direct_paths(monkeypatch):
+def test_quantize_act_order_dead_channel_and_direct_paths():
     """act_order with a dead channel (its zero diagonal ranks as 1), and the row kernels'
     direct (no LDS staging) paths that rows longer than 16384 floats take."""
-    monkeypatch.setenv("KQ_ROW_LDS_MAX", "0")
+    import post_quantization_syrk_amd as kq
+    with kq.testing_select(kq.KQ_TESTING_ROW_LDS_BYTES, 0):
+        _act_order_dead_channel()
+
+
+def _act_order_dead_channel():
     announce("gptq act_order + w_clip, dead channel, direct row paths")
     rng = np.random.default_rng(41)
     HXt = spd(rng, 192, outliers=2)
@@ -159,7 +164,7 @@ def test_quantize_block_pairs(bits, group, block):
     check_against_oracle(g, Wt, HXt, HGt, bits, group)
 
 
-def test_factor_panel_formed_once_matches_per_tile(monkeypatch):
+def test_factor_panel_formed_once_matches_per_tile():
     """The factorization forms each step's panel factor Z once, ahead of the update, on steps
     with many tiles; forcing that path on every step gives the same bits as forming Z in each
     tile (the same products in the same order)."""
@@ -169,9 +174,10 @@ def test_factor_panel_formed_once_matches_per_tile(monkeypatch):
     Wt = (rng.standard_normal((out_n, in_n)) * 0.05).astype(np.float32).astype(np.float64)
     HXt = spd(rng, in_n, outliers=2).astype(np.float32).astype(np.float64)
     HGt = spd(rng, out_n).astype(np.float32).astype(np.float64)
+    import post_quantization_syrk_amd as kq
     ref = gpu_quantize(Wt, HXt, HGt, 3, 128, 128)
-    monkeypatch.setenv("KQ_ZPRE_TILES", "0")
-    g = gpu_quantize(Wt, HXt, HGt, 3, 128, 128)
+    with kq.testing_select(kq.KQ_TESTING_FACTOR_PANEL_TILES, 0):
+        g = gpu_quantize(Wt, HXt, HGt, 3, 128, 128)
     for key in ("E", "packed", "scales", "zeros", "codes"):
         assert np.array_equal(g[key], ref[key]), key
     check_against_oracle(g, Wt, HXt, HGt, 3, 128)

@@ -50,23 +50,19 @@ def test_ragged_shapes(T, n, lda):
     assert np.array_equal(H, H.T)
 
 
-@pytest.mark.parametrize("variant", ["0", "1", "2", "3", "4", "4/5", "4/tm"])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("T,n,lda", [(20000, 600, 608), (31, 256, 256), (1000, 300, 304)])
-def test_kernel_variants_agree(variant, T, n, lda, monkeypatch):
-    """Every SYRK kernel variant (register-staged 4/8 waves, tile/split-major; direct-to-LDS
-    with a 4- or 5-stage ring, region or token-major workgroup order) against the oracle, on
-    shapes with many token splits, a ragged last stage and a ragged last tile."""
-    v, _, opt = variant.partition("/")
-    monkeypatch.setenv("KQ_SYRK_VARIANT", v)
-    if opt == "tm":
-        monkeypatch.setenv("KQ_SYRK_ORDER", "1")
-    elif opt:
-        monkeypatch.setenv("KQ_SYRK_RING", opt)
+def test_kernel_variants_agree(variant, T, n, lda):
+    """Every SYRK kernel (the register-staged fallback with 4/8 waves, tile/split-major; the
+    direct-to-LDS default) against the oracle, on shapes with many token splits, a ragged
+    last stage and a ragged last tile."""
+    import post_quantization_syrk_amd as kq
     announce(f"hessian variant {variant} T={T} n={n} lda={lda}")
     rng = np.random.default_rng(T + n)
     x = (rng.standard_normal((T, n)) * np.exp(rng.standard_normal(n))).astype(np.float32)
     bits = syn.f32_to_bf16_bits(x)
-    H = gpu_hessian(bits, lda)
+    with kq.testing_select(kq.KQ_TESTING_SYRK_KERNEL, variant):
+        H = gpu_hessian(bits, lda)
     ref = o.hessian_factor(o.bf16_bits_to_f64(bits))
     assert rel_fro(H, ref) <= 1e-5
     assert np.array_equal(H, H.T)
