@@ -362,8 +362,9 @@ kq_status kq_flipflop_workspace(int64_t T, int64_t n, int64_t m, size_t* bytes);
  * fixed-point iteration from the identity).  The 1/m and 1/n are the classical flip-flop's
  * normalization; A (x) B does not depend on it.  Inverses: the reverse Cholesky factor of
  * the current factor without damping (a zero diagonal entry counts as 1); the inverse
- * factor enters the per-token quadratic forms rounded to bf16, as the streams are, with
- * fp32 accumulation, and the scaled streams are rounded to bf16 for the SYRK.
+ * factor enters the per-token quadratic forms as two bf16 terms (its rounding and the
+ * rounding of the remainder, about 16 significant bits) with fp32 accumulation, and so does
+ * each scaled token row in the SYRK (the factor of the two-term stream, folded).
  *
  *   X, G     device bf16 bit patterns, T x n and T x m, token-major, leading dims ldx, ldg
  *            (multiples of 8, >= the widths), 16-byte aligned

@@ -11,11 +11,19 @@
 //      then the explicit U = R^-1 (upper): its diagonal blocks and the panels P = R U_JJ
 //      come from the factorization, the blocks above from U[<J, J] = -U[<J,<J] P[<J, J],
 //      one fp32 MFMA product per block column.  g^T B^-1 g = |U g|^2.
-//   2. w_t = |U g_t|^2 for every token: a bf16 MFMA product of the stream with U (rounded
-//      to bf16, as the streams are), fp32 accumulation, the squares summed per token in the
-//      epilogue; tiles left of the diagonal of U are skipped.
-//   3. The scaled stream sqrt(w_t / (T m)) x_t, rounded to bf16, goes through the SYRK:
-//      A = sum_t (w_t / (T m)) x_t x_t^T.
+//   2. w_t = |U g_t|^2 for every token: bf16 MFMA products of the stream with U, fp32
+//      accumulation, the squares summed per token in the epilogue; tiles left of the
+//      diagonal of U are skipped.  U enters as two bf16 terms, U_hi = bf16(U) and
+//      U_lo = bf16(U - U_hi), multiplied into the same accumulators (the contraction runs
+//      twice), so U carries about 16 significant bits: with U_hi alone its rounding is the
+//      same in every token and its error in the factors does not average out.
+//   3. The scaled stream y_t = sqrt(w_t / (T m)) x_t goes through the SYRK as two bf16
+//      terms, y_hi = bf16(y) and y_lo = bf16(y - y_hi), side by side in one stream of width
+//      2n: its factor H2 = [y_hi y_lo]^T [y_hi y_lo] holds hi.hi, lo.hi and lo.lo, and
+//      A = sum_t y_t y_t^T = hi.hi + lo.hi + (lo.hi)^T + lo.lo, folded in one fixed order
+//      per unordered pair (i, j), so A is exactly symmetric.  With y rounded once the
+//      per-token weights' rounding would not average out (a few heavy tokens dominate the
+//      sum); with two terms each entry of y carries about 16 significant bits.
 //
 // qform_kernel: 256-token x 256-output tiles, 4 waves of 128 x 128 (4 x 4 blocks of
 // v_mfma_f32_32x32x16_bf16); stages of 32 contraction indices: both panels (256 rows x 64
@@ -58,6 +66,12 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+__device__ __forceinline__ unsigned short bf16_rne(float x) {
+  unsigned u = __float_as_uint(x);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
 // Sixteen zero bytes: the source of every copy lane whose row lies outside the matrix, so that
 // each wave issues the same number of copies per stage and the vmcnt waits stay exact.
 __device__ __attribute__((aligned(16))) uint32_t q_zero_chunk[4];
@@ -68,6 +82,7 @@ struct QArgs {
   const uint16_t* S;   // stream, T x k bf16, leading dim lds (elements)
   int64_t lds;
   const uint16_t* U;   // k x k bf16, upper triangular (row j: U[j, j..k)), leading dim k
+  int64_t ulo;         // offset (elements) from U to the k x k low part U_lo
   int64_t T;
   int k;
   float* part;         // T x np partial sums of squares (np = 2 * ceil(k / 256))
@@ -99,8 +114,9 @@ __global__ __launch_bounds__(256) void qform_kernel(QArgs a) {
   const int64_t t0 = (int64_t)tt * QT;
   const int j0 = jt * QT;
   const int i_begin = j0;                       // U[j, i] = 0 for i < j
-  const int nst = (a.k - i_begin) / QK;         // k % 128 == 0
-  const int nst_round = (nst + QNST - 1) / QNST * QNST;
+  const int nst = (a.k - i_begin) / QK;         // k % 128 == 0; stages per pass over U
+  // stages 0 .. nst - 1 multiply by U_hi, nst .. 2 nst - 1 by U_lo (the same stream columns)
+  const int nst_round = (2 * nst + QNST - 1) / QNST * QNST;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -119,11 +135,13 @@ __global__ __launch_bounds__(256) void qform_kernel(QArgs a) {
     srcU[c] = j0 + row < a.k ? a.U + (int64_t)(j0 + row) * a.k + i_begin + 8 * chunk : zero;
   }
   auto issue = [&](int s, uint16_t* buf) {
-    const bool live = s < nst;
+    const bool live = s < 2 * nst;
+    const bool lo = s >= nst;
+    const int sc = lo ? s - nst : s;
 #pragma unroll
     for (int c = 0; c < QCOPIES; ++c) {
-      const uint16_t* ps = live && srcS[c] != zero ? srcS[c] + s * QK : zero;
-      const uint16_t* pu = live && srcU[c] != zero ? srcU[c] + s * QK : zero;
+      const uint16_t* ps = live && srcS[c] != zero ? srcS[c] + sc * QK : zero;
+      const uint16_t* pu = live && srcU[c] != zero ? srcU[c] + (lo ? a.ulo : 0) + sc * QK : zero;
       __builtin_amdgcn_global_load_lds((const void*)ps,
                                        (__attribute__((address_space(3))) void*)(buf + (4 * wave + c) * 512),
                                        16, 0, 0);
@@ -240,8 +258,9 @@ __global__ __launch_bounds__(256) void qform_kernel(QArgs a) {
   }
 }
 
-// out[t, :] = bf16(sqrt(c * sum_p part[t, p]) * S[t, :]) (round to nearest even); one
-// workgroup per token, 8 channels per thread and step.
+// y = sqrt(c * sum_p part[t, p]) * S[t, :]: out[t, 0:k] = bf16(y) and out[t, k:2k] =
+// bf16(y - bf16(y)) (round to nearest even; the remainder is exact in fp32); one workgroup per
+// token, 8 channels per thread and step.
 __global__ __launch_bounds__(256) void ff_scale_kernel(const uint16_t* __restrict__ S, int64_t lds,
                                                        int k, const float* __restrict__ part,
                                                        int np, float c, uint16_t* __restrict__ out,
@@ -260,21 +279,39 @@ __global__ __launch_bounds__(256) void ff_scale_kernel(const uint16_t* __restric
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   for (int i = 8 * threadIdx.x; i < k; i += 8 * 256) {
     const u32x4 v = *(const u32x4*)(S + t * lds + i);
-    u32x4 o;
+    u32x4 oh, ol;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      unsigned r = 0;
+      unsigned rh = 0, rl = 0;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const float x = __uint_as_float(((v[h] >> (16 * e)) & 0xffffu) << 16) * f;
-        unsigned u = __float_as_uint(x);
-        u += 0x7fffu + ((u >> 16) & 1u);
-        r |= (u >> 16) << (16 * e);
+        const unsigned hi = bf16_rne(x);
+        const unsigned lo = bf16_rne(x - __uint_as_float(hi << 16));
+        rh |= hi << (16 * e);
+        rl |= lo << (16 * e);
       }
-      o[h] = r;
+      oh[h] = rh;
+      ol[h] = rl;
     }
-    *(u32x4*)(out + t * ldo + i) = o;
+    *(u32x4*)(out + t * ldo + i) = oh;
+    *(u32x4*)(out + t * ldo + k + i) = ol;
   }
+}
+
+// out (k x k, full symmetric) from the 2k x 2k factor H2 of the two-term stream:
+// out[i][j] = (H2[a][b] + H2[k + a][k + b]) + (H2[k + a][b] + H2[k + b][a]) with
+// (a, b) = (max(i, j), min(i, j)): the same terms in the same order for (i, j) and (j, i).
+// One workgroup per 256 entries of a row (jb row blocks per row).
+__global__ __launch_bounds__(256) void ff_fold_kernel(const float* __restrict__ H2, int64_t k,
+                                                      int64_t jb, float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x / jb;
+  const int64_t j = ((int64_t)blockIdx.x % jb) * 256 + threadIdx.x;
+  if (j >= k) return;
+  const int64_t k2 = 2 * k;
+  const int64_t a = i > j ? i : j, b = i > j ? j : i;
+  out[i * k + j] = (H2[a * k2 + b] + H2[(k + a) * k2 + k + b]) +
+                   (H2[(k + a) * k2 + b] + H2[(k + b) * k2 + a]);
 }
 
 // The diagonal 128-blocks of U: the upper triangles of F's diagonal blocks (U_JJ); below
@@ -288,21 +325,24 @@ __global__ __launch_bounds__(256) void copy_diag_blocks(const float* __restrict_
   }
 }
 
-// bf16 copy of an fp32 matrix (round to nearest even), 4 entries per thread.
-__global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ src,
-                                                      uint16_t* __restrict__ dst, int64_t count) {
+// Two-term bf16 copy of an fp32 matrix (round to nearest even): hi = bf16(v),
+// lo = bf16(v - hi) (v - hi is exact in fp32), 4 entries per thread.
+__global__ __launch_bounds__(256) void to_bf16_pair_kernel(const float* __restrict__ src,
+                                                           uint16_t* __restrict__ hi,
+                                                           uint16_t* __restrict__ lo,
+                                                           int64_t count) {
   const int64_t i = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
   if (i >= count) return;
   const float4 v = *(const float4*)(src + i);
   const float e[4] = {v.x, v.y, v.z, v.w};
-  unsigned short o[4];
+  unsigned short oh[4], ol[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    unsigned u = __float_as_uint(e[j]);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    o[j] = (unsigned short)(u >> 16);
+    oh[j] = bf16_rne(e[j]);
+    ol[j] = bf16_rne(e[j] - __uint_as_float((unsigned)oh[j] << 16));
   }
-  *(ushort4*)(dst + i) = make_ushort4(o[0], o[1], o[2], o[3]);
+  *(ushort4*)(hi + i) = make_ushort4(oh[0], oh[1], oh[2], oh[3]);
+  *(ushort4*)(lo + i) = make_ushort4(ol[0], ol[1], ol[2], ol[3]);
 }
 
 __global__ void identity_kernel(float* __restrict__ M, int64_t k) {
@@ -311,13 +351,14 @@ __global__ void identity_kernel(float* __restrict__ M, int64_t k) {
 }
 
 struct Workspace {
-  uint16_t* Ss;    // scaled stream, T x ldS bf16
+  uint16_t* Ss;    // scaled stream as two bf16 terms, T x ldS (ldS >= 2 kmax)
   int64_t ldS;
+  float* H2;       // its factor, (2 kmax)^2
   float* part;     // T x npmax
   float* F;        // factorization, kmax^2
   float* Tsc;      // factorization scratch, 128 kmax
   float* Uf;       // explicit inverse factor, kmax^2
-  uint16_t* Ub;    // its bf16 copy, kmax^2
+  uint16_t* Ub;    // its two-term bf16 copy: U_hi (kmax^2), then U_lo (kmax^2)
   uint8_t* dead;   // kmax
   double* lam;
   int* flag;
@@ -331,13 +372,14 @@ int64_t layout(int64_t T, int64_t n, int64_t m, char* base, Workspace* w) {
   int64_t off = 0;
   auto take = [&](int64_t bytes) { const int64_t o = off; off += al256(bytes); return base ? base + o : nullptr; };
   Workspace x;
-  x.ldS = (k + 7) / 8 * 8;
+  x.ldS = (2 * k + 7) / 8 * 8;
   x.Ss = (uint16_t*)take(T * x.ldS * 2);
+  x.H2 = (float*)take(4 * k * k * 4);
   x.part = (float*)take(T * np * 4);
   x.F = (float*)take(k * k * 4);
   x.Tsc = (float*)take(128 * k * 4);
   x.Uf = (float*)take(k * k * 4);
-  x.Ub = (uint16_t*)take(k * k * 2);
+  x.Ub = (uint16_t*)take(2 * k * k * 2);
   x.dead = (uint8_t*)take(k);
   x.lam = (double*)take(8);
   x.flag = (int*)take(4);
@@ -345,12 +387,14 @@ int64_t layout(int64_t T, int64_t n, int64_t m, char* base, Workspace* w) {
   return off;
 }
 
-// Ub = bf16(U), U = R^-1 for M = R R^T (no damping; zero diagonals count as 1).
+// Ub = [bf16(U), bf16(U - bf16(U))] (k x k each), U = R^-1 for M = R R^T (no damping; zero
+// diagonals count as 1).
 kq_status inverse_factor(const float* M, int64_t k, const Workspace& w, hipStream_t s) {
   KQ_TRY(explicit_inverse_factor(M, k, 0.0f, w.F, w.Tsc, w.dead, w.lam, w.flag, w.Uf, s));
   const int64_t cnt = k * k;
-  to_bf16_kernel<<<dim3((unsigned)ceil_div(cnt / 4, 256)), dim3(256), 0, s>>>(w.Uf, w.Ub, cnt);
-  KQ_LAUNCHED("to_bf16_kernel");
+  to_bf16_pair_kernel<<<dim3((unsigned)ceil_div(cnt / 4, 256)), dim3(256), 0, s>>>(w.Uf, w.Ub,
+                                                                                  w.Ub + cnt, cnt);
+  KQ_LAUNCHED("to_bf16_pair_kernel");
   return KQ_OK;
 }
 
@@ -358,7 +402,7 @@ kq_status inverse_factor(const float* M, int64_t k, const Workspace& w, hipStrea
 kq_status quadratic_forms(const uint16_t* S, int64_t lds, int64_t T, int64_t k, const Workspace& w,
                           hipStream_t s) {
   QArgs a;
-  a.S = S; a.lds = lds; a.U = w.Ub; a.T = T; a.k = (int)k; a.part = w.part;
+  a.S = S; a.lds = lds; a.U = w.Ub; a.ulo = k * k; a.T = T; a.k = (int)k; a.part = w.part;
   a.njt = (int)((k + QT - 1) / QT);
   a.np = 2 * a.njt;
   a.ntt = (int)((T + QT - 1) / QT);
@@ -413,7 +457,10 @@ kq_status half_step(const float* M, const uint16_t* S2, int64_t ld2, int64_t k2,
   ff_scale_kernel<<<dim3((unsigned)T), dim3(256), 0, s>>>(S1, ld1, (int)k1, w.part, np, c, w.Ss, w.ldS);
   KQ_LAUNCHED("ff_scale_kernel");
   KQ_TRY(pt.mark(s));
-  KQ_TRY(kq_accumulate_hessian(w.Ss, T, k1, w.ldS, out, k1, 0, s));
+  KQ_TRY(kq_accumulate_hessian(w.Ss, T, 2 * k1, w.ldS, w.H2, 2 * k1, 0, s));
+  const int64_t jb = ceil_div(k1, 256);
+  ff_fold_kernel<<<dim3((unsigned)(jb * k1)), dim3(256), 0, s>>>(w.H2, k1, jb, out);
+  KQ_LAUNCHED("ff_fold_kernel");
   return pt.mark(s);
 }
 

@@ -1,13 +1,13 @@
 """GPU parity: the FlipFlop Hessian factors (kq_flipflop) against the oracle's fp64 iteration
 on the same bf16 streams.
 
-Tolerance, from the arithmetic: the GPU rounds the inverse factor U (B^-1 = U^T U) to bf16
-for the per-token quadratic forms (each entry within 2^-9 relative) and rounds each scaled
-token row sqrt(w_t c) x_t to bf16 for the SYRK (each entry within 2^-9, so each term of A
-within about 2^-8).  Both errors are independent across entries and tokens; a coherent
-bound on A's relative Frobenius error is 2^-8 = 3.9e-3 per half step, and the observed
-errors sit far below it.  Iterations feed each other's errors forward through B^-1 and
-A^-1, so the bar is 1e-2 relative Frobenius on every A_k and B_k (k <= 3)."""
+Tolerance: the Hessian factors' 1e-3 relative Frobenius error, on every A_k and B_k (k <= 3).
+The GPU carries the inverse factor U (B^-1 = U^T U) into the per-token quadratic forms, and
+each scaled token row sqrt(w_t c) x_t into the SYRK, as two bf16 terms (about 16
+significant bits, relative error within 2^-17 per entry); the products accumulate in fp32
+and the factorizations run in fp32.  With a single bf16 term the scaled rows alone gave
+2.4e-3 at the first iteration (where U is the identity): a few heavy tokens dominate the
+weighted sums, so their 2^-9 roundings do not average out."""
 import numpy as np
 import pytest
 
@@ -17,7 +17,7 @@ from tests.gpu_util import announce, rel_fro, to_dev_bf16, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
-TOL = 1e-2
+TOL = 1e-3
 
 
 def _gpu(torch, Xb, Gb, iters):
