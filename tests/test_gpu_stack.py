@@ -7,8 +7,8 @@ kq_sensitivity); the oracle takes each trace as the stream's squared norm
 (tr(A^T A) = ||A||_F^2, exact in fp64).  Bits: identical between the library
 allocator on the engine's traces and the oracle allocator on the oracle's traces
 (and on shared inputs); the smallest relative gap between winning and runner-up
-gains is reported as the tie margin.  Two sublayers are then quantized at full
-size with their allocated widths (sampled-row parity)."""
+gains is reported as the tie margin.  One sublayer of each shape is then quantized
+at full size with its allocated width (sampled-row parity and both losses)."""
 import time
 
 import numpy as np
@@ -16,7 +16,7 @@ import pytest
 
 import oracle as o
 import synthetic as syn
-from tests.fullsize_util import check_rows, oracle_hessian, run_engine
+from tests.fullsize_util import check_rows, dequant, oracle_hessian, run_engine
 from tests.gpu_util import announce, rel_fro, torch_cuda
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -82,20 +82,36 @@ def test_decoder_stack_allocation_and_sublayers():
     assert sum(b * n for b, n in zip(bits_ref, numel)) <= (sum(numel) * 5) // 2
     assert set(bits_ref) <= {2, 3, 4}
     torch.cuda.empty_cache()
-    # full-size quantization of two sublayers at their allocated widths
-    for layer, k in ((0, 0), (31, 6)):
+    # full-size quantization of one sublayer of each shape (q 4096 x 4096, gate 11008 x 4096,
+    # down 4096 x 11008) at its allocated width, the widths spread over {2, 3, 4} where the
+    # allocation allows: sampled-row codes, and both losses against the oracle's own factors
+    picks, used = [], set()
+    for k in (0, 4, 6):
+        cands = [layer for layer in range(syn.STACK_LAYERS) if bits_ref[layer * 7 + k] not in used]
+        layer = cands[0] if cands else (0, 15, 31)[(0, 4, 6).index(k)]
+        used.add(bits_ref[layer * 7 + k])
+        picks.append((layer, k))
+    for layer, k in picks:
         cfg = syn.stack_sublayer_configs(layer)[k]
         cfg = cfg.scaled(bits=bits_ref[layer * 7 + k])
         bx, bg, W = syn.stream(cfg, "x"), syn.stream(cfg, "g"), syn.weights(cfg)
         s_in, s_out = syn.signs(cfg, "in"), syn.signs(cfg, "out")
-        g = run_engine(cfg, bx, bg, W, s_in, s_out, want_loss=False)
+        g = run_engine(cfg, bx, bg, W, s_in, s_out, want_loss=True)
         HX, HG = oracle_hessian(bx), oracle_hessian(bg)
         assert rel_fro(g["HX"], HX) <= 1e-5 and rel_fro(g["HG"], HG) <= 1e-5
         Wt, HXt, HGt, _, _ = o.biip(W.astype(np.float64), HX, HG, s_in, s_out, cfg.alpha, o.BIIP_FULL,
                                     cfg.had_in, cfg.had_out)
         assert rel_fro(g["Wt"], Wt) <= 1e-5 and rel_fro(g["HXt"], HXt) <= 1e-5
+        assert rel_fro(g["HGt"], HGt) <= 1e-5
         rows = np.sort(np.random.default_rng(layer).choice(cfg.out, 32, replace=False))
         res = check_rows(g, Wt, HXt, cfg, rows, o.damp_and_factor(HXt, cfg.damp))
-        announce(f"stack: {cfg.name} W{cfg.bits} sampled rows match ({res.accepted_ties} ties adopted)")
+        dW = Wt - dequant(g["codes"], g["scales"], g["zeros"], cfg.group)
+        L_direct = o.proxy_loss(dW, HXt, HGt)
+        L_pred = o.predicted_loss(g["E"], HGt)
+        announce(f"stack: {cfg.name} W{cfg.bits} sampled rows match ({res.accepted_ties} ties adopted); "
+                 f"losses engine {g['loss'][0]:.6e} / {g['loss'][1]:.6e}, oracle {L_direct:.6e} / {L_pred:.6e}")
+        assert g["loss"][0] == pytest.approx(L_direct, rel=1e-3)
+        assert g["loss"][1] == pytest.approx(L_pred, rel=1e-3)
+        assert g["loss"][1] > g["loss"][0]
         del bx, bg, g
         torch.cuda.empty_cache()
