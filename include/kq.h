@@ -228,6 +228,29 @@ kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, const float*
                             float* scales, uint8_t* zeros, uint8_t* codes_opt, double* loss_opt,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* Largest workspace kq_quantize_layer_noalloc serves: a layer is accepted when
+ * kq_quantize_layer_workspace reports at most this many bytes for it (with losses when
+ * losses are requested); e.g. every 2048 x 2048 layer. */
+#define KQ_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/*
+ * kq_quantize_layer_noalloc -- kq_quantize_layer with no workspace argument, for callers that
+ * cannot allocate device memory at the point of the call (tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, steps, outputs and errors as kq_quantize_layer
+ * without ws and ws_bytes; it calls no allocating routine.  Its workspace is a fixed array of
+ * KQ_NOALLOC_WORKSPACE_BYTES in the library's device memory, one per GPU, held until the
+ * process ends; everything in it that must start at zero is cleared by each call.
+ *   KQ_EWORKSPACE (before anything is enqueued) when the layer needs more workspace than the
+ *   array holds.
+ * Calls on one GPU share that GPU's array: calls whose work overlaps on one GPU (different
+ * streams, or host threads) race and give undefined results; calls in one stream are
+ * ordered.  Synchronizes `stream` before returning, as kq_quantize_layer does.
+ */
+kq_status kq_quantize_layer_noalloc(const kq_quant_params* p, float* W_rot, const float* HX_rot,
+                                    const float* HG_rot, int64_t out, int64_t in,
+                                    uint32_t* packed, float* scales, uint8_t* zeros,
+                                    uint8_t* codes_opt, double* loss_opt, void* stream);
+
 /*
  * kq_allocate_bits -- per-sublayer bit widths from sensitivities (host only).
  *

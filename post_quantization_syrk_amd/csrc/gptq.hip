@@ -22,6 +22,8 @@
 //   W0_j - s (q - z) goes to D.
 #include "kq_internal.h"
 
+#include <mutex>
+
 #include <math.h>
 
 #include <utility>
@@ -723,12 +725,13 @@ extern "C" kq_status kq_quantize_layer_workspace(const kq_quant_params* p, int64
   return KQ_OK;
 }
 
-extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, const float* HX_rot,
-                                       const float* HG_rot, int64_t out, int64_t in,
-                                       uint32_t* packed, float* scales, uint8_t* zeros,
-                                       uint8_t* codes_opt, double* loss_opt, void* ws,
-                                       size_t ws_bytes, void* stream) {
-  using namespace kq;
+namespace kq {
+namespace {
+
+kq_status quantize_layer(const kq_quant_params* p, float* W_rot, const float* HX_rot,
+                         const float* HG_rot, int64_t out, int64_t in, uint32_t* packed,
+                         float* scales, uint8_t* zeros, uint8_t* codes_opt, double* loss_opt,
+                         void* ws, size_t ws_bytes, void* stream) {
   KQ_TRY(check_params(p, out, in));
   if (!W_rot || !HX_rot || !packed || !scales || !zeros)
     return fail(KQ_EINVAL, "kq_quantize_layer: NULL argument");
@@ -884,4 +887,61 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
   }
   if (host_flag) return fail(KQ_ENOTSPD, "kq_quantize_layer: damped H_X is not positive definite");
   return KQ_OK;
+}
+
+// Workspace of kq_quantize_layer_noalloc: one copy per GPU, held until the process ends.  Host
+// code never names it directly (its host-side name is no device address): the device address
+// comes from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t NOALLOC_SCRATCH_BYTES = KQ_NOALLOC_WORKSPACE_BYTES;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+kq_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  KQ_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= MAX_DEVICES)
+    return fail(KQ_ENOTIMPL, "kq_quantize_layer_noalloc: device index %d beyond %d", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* a = nullptr;
+    KQ_HIP(hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)));
+    if (!a) return fail(KQ_EHIP, "kq_quantize_layer_noalloc: no device address for the scratch");
+    g_scratch_ptr[dev] = a;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return KQ_OK;
+}
+
+}  // namespace
+}  // namespace kq
+
+extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, const float* HX_rot,
+                                       const float* HG_rot, int64_t out, int64_t in,
+                                       uint32_t* packed, float* scales, uint8_t* zeros,
+                                       uint8_t* codes_opt, double* loss_opt, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  return kq::quantize_layer(p, W_rot, HX_rot, HG_rot, out, in, packed, scales, zeros, codes_opt,
+                            loss_opt, ws, ws_bytes, stream);
+}
+
+extern "C" kq_status kq_quantize_layer_noalloc(const kq_quant_params* p, float* W_rot,
+                                               const float* HX_rot, const float* HG_rot,
+                                               int64_t out, int64_t in, uint32_t* packed,
+                                               float* scales, uint8_t* zeros, uint8_t* codes_opt,
+                                               double* loss_opt, void* stream) {
+  using namespace kq;
+  KQ_TRY(check_params(p, out, in));
+  const size_t need = layout(out, in, p->block, loss_opt != nullptr, p->act_order != 0).total;
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(KQ_EWORKSPACE,
+                "kq_quantize_layer_noalloc: this layer needs %zu bytes of workspace, more than the "
+                "library's fixed %zu; use kq_quantize_layer with a workspace of its own",
+                need, NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  KQ_TRY(scratch_of_current_device(&ws));
+  return quantize_layer(p, W_rot, HX_rot, HG_rot, out, in, packed, scales, zeros, codes_opt,
+                        loss_opt, ws, NOALLOC_SCRATCH_BYTES, stream);
 }
