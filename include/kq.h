@@ -230,7 +230,8 @@ kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, const float*
 
 /* Largest workspace kq_quantize_layer_noalloc serves: a layer is accepted when
  * kq_quantize_layer_workspace reports at most this many bytes for it (with losses when
- * losses are requested); e.g. every 2048 x 2048 layer. */
+ * losses are requested); e.g. a 2048 x 2048 layer without losses (49 MiB) or a 1024 x 1024
+ * layer with them (20.5 MiB). */
 #define KQ_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
 
 /*
