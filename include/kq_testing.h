@@ -24,10 +24,10 @@ enum {
    * register-staged kernel that serves strides too large for the default (bit 0: 8 waves
    * instead of 4; bit 1: split-major workgroup order). */
   KQ_TESTING_SYRK_KERNEL = 0,
-  /* kq_quantize_layer's factorization forms a step's panel factor once, ahead of the
-   * update, when the update has more than this many tiles (default: twice the GPU's compute
-   * units); 0 forces that path on every step.  The same products in the same order. */
-  KQ_TESTING_FACTOR_PANEL_TILES = 1,
+  /* Columns per super-block of kq_quantize_layer's factorization (a multiple of 128,
+   * default 512): each block's update of the columns left of its super-block waits for one
+   * rank-(super-block) update.  The same updates, summed in another order. */
+  KQ_TESTING_FACTOR_SUPERBLOCK = 1,
   /* Longest row (bytes) the quantizer's row kernels stage in LDS (default 65536); 0 forces
    * their direct paths, which longer rows take. */
   KQ_TESTING_ROW_LDS_BYTES = 2

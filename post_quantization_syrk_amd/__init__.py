@@ -85,7 +85,7 @@ _SIGS = {
 }
 
 # include/kq_testing.h: implementation selection for tests
-KQ_TESTING_SYRK_KERNEL, KQ_TESTING_FACTOR_PANEL_TILES, KQ_TESTING_ROW_LDS_BYTES = range(3)
+KQ_TESTING_SYRK_KERNEL, KQ_TESTING_FACTOR_SUPERBLOCK, KQ_TESTING_ROW_LDS_BYTES = range(3)
 
 _lib = None
 

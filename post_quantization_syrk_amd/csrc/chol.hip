@@ -11,11 +11,21 @@
 //
 // Reverse Cholesky, 64-column blocks from the last one up, one launch per block.  With A12
 // the current column block above the diagonal and M = A22^-1 = U22^T U22 (from the previous
-// block's leaf), each 128 x 128 tile forms Z = A12 M (= R12 U22) for its rows and subtracts
-// Z A12^T from A11 (fp32 MFMA, upper tiles); Z^T is kept in the free lower triangle.  One
-// extra workgroup of the same launch updates the next diagonal block privately and factors
-// it: one wave finds R22 R22^T = A22, all four then form U22 = R22^-1 by recursive doubling
-// and M = U22^T U22, so the serial chain of small factorizations overlaps the bulk updates.
+// block's leaf), the block's panel factor is Z = A12 M (= R12 U22), kept transposed in the
+// free lower triangle, and the trailing update is A11 -= Z A12^T.  That update is split in
+// two: the columns are grouped in super-blocks of 1024 (aligned to 0), and a step updates
+// only the columns of its own super-block that are still to come (every row above them:
+// 128 x 128 fp32 MFMA tiles, each forming Z for its rows); the rest of A11, left of the
+// super-block, takes the super-block's whole rank-1024 update at once when the super-block
+// is done, as one plain product A12 Z^T of the super-block's columns with the Z^T rows of the
+// lower triangle (equal to Z A12^T, the update being symmetric).  So the leading matrix is
+// read and written once per super-block rather than once per block (matrices that fit the
+// last-level cache, 64 MB at 4096 wide, are one super-block: there the split only adds to
+// the serial chain).  One extra workgroup of
+// a step's launch updates the next diagonal block privately and factors it: one wave finds
+// R22 R22^T = A22, all four then form U22 = R22^-1 by recursive doubling and
+// M = U22^T U22, so the serial chain of small factorizations overlaps the bulk updates (at a
+// super-block's first block the next diagonal block waits for the deferred update instead).
 // Only the diagonal blocks of U are formed.  GPTQ's feedback into block J needs
 // U[<J, J] = -U[<J,<J] R[<J, J] U_JJ only through E[:, <J] U[<J, J], and
 // E[:, <J] U[<J,<J] = (W - Qhat)[:, <J] (the rounding error so far, in the layer's own
@@ -23,6 +33,8 @@
 // exactly Z; for 128-column blocks [Z_a, Z_b - Z_a Z_b[a rows]], the second half coupled
 // through U_ab = -U_a Z_b[a rows].
 #include "kq_internal.h"
+
+#include <algorithm>
 
 namespace kq {
 namespace {
@@ -381,52 +393,20 @@ __device__ __forceinline__ void store_zt(float* __restrict__ F, int64_t n, int64
   }
 }
 
-// The panel factor of a whole step at once, for steps whose update has many tiles: one
-// workgroup per 128-row block forms Z = A12 M and stores Z^T in the lower triangle, where the
-// update's tiles (and its leaf workgroup) then read it instead of each forming it again.
-// The same products in the same order as the tiles', so the factorization does not change.
-__global__ __launch_bounds__(256) void z_kernel(float* __restrict__ F, int64_t n, int64_t s0,
-                                                const float* __restrict__ Mcur) {
-  __shared__ __attribute__((aligned(16))) float As[128 * 64];
-  __shared__ __attribute__((aligned(16))) float Ms[64 * 64];
-  const int t = threadIdx.x;
-  const int64_t i0 = (int64_t)blockIdx.x * 128;
-  const __amdgpu_buffer_rsrc_t ra = rsrc(F + i0 * n + s0);
-  float4 va[8], mv[4];
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int r = (t >> 4) + 16 * it, off = (r * (int)n + (t & 15) * 4) * 4;
-    va[it] = bload4(ra, i0 + r < s0 ? off : OOB);
-  }
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int q = t + 256 * it, r = q >> 4, c4 = (q & 15) * 4;
-    mv[it] = *(const float4*)(Mcur + r * 64 + c4);
-  }
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int q = t + 256 * it, r = q >> 4, c4 = (q & 15) * 4;
-    Ms[swb(r, c4)] = mv[it].x; Ms[swb(r, c4 + 1)] = mv[it].y; Ms[swb(r, c4 + 2)] = mv[it].z; Ms[swb(r, c4 + 3)] = mv[it].w;
-  }
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int r = (t >> 4) + 16 * it, c4 = (t & 15) * 4;
-    As[sw(r, c4)] = va[it].x; As[sw(r, c4 + 1)] = va[it].y; As[sw(r, c4 + 2)] = va[it].z; As[sw(r, c4 + 3)] = va[it].w;
-  }
-  __syncthreads();
-  panel_z(As, Ms);
-  store_zt(F, n, s0, i0, As);
-}
-
 // Step of the reverse factorization at block [s0, s0 + 64).  With A12 = F[0:s0, s0:s0+64]
 // (the current Schur complement's column block) and M = A22^-1 = U22^T U22 from the previous
-// step's leaf, the block's panel factor is Z = A12 M (= R12 U22 with R12 = A12 U22^T) and the
-// trailing update is A11 -= A12 M A12^T = Z A12^T.  Z is GPTQ's feedback factor P for this
-// 64-column block; it is stored transposed in the free lower triangle, F[s0 + c][r] = Z[r][c].
-// Tiles (upper 128 x 128 of [0, s0)^2): Z for the tile's rows (A12[I] M), then
-// C -= Z[I] A12[K]^T; the diagonal tiles also store Z^T.  The next diagonal block
-// D = [s0-64, s0)^2 is left alone by the tiles: workgroup 0 forms D - Z_D A12[D]^T privately
-// and factors it (leaf), so the next block's factorization overlaps the bulk update.
+// step's leaf, the block's panel factor is Z = A12 M (= R12 U22 with R12 = A12 U22^T), and
+// the trailing update is A11 -= A12 M A12^T = Z A12^T.  Z is GPTQ's feedback factor P for
+// this 64-column block; it is stored transposed in the free lower triangle,
+// F[s0 + c][r] = Z[r][c].  Workgroups, in order:
+//   - with_leaf: workgroup 0 forms the next diagonal block D = [s0-64, s0)^2 privately,
+//     D - Z_D A12[D]^T, and factors it (leaf), so the next step's factorization overlaps
+//     the bulk update;
+//   - zblocks "panel-factor" workgroups: Z for the 128-row blocks of rows [0, 128 zblocks)
+//     (above the super-block), stored as Z^T;
+//   - the tiles (upper 128 x 128 of [0, s0)^2) of the columns [pcol0, s0) that this step
+//     updates now: Z for the tile's rows (A12[I] M), then C -= Z[I] A12[K]^T; the diagonal
+//     tiles also store Z^T of their rows.  D is left to workgroup 0.
 // 4 waves of v_mfma_f32_32x32x2f32; K = 64 in one LDS stage.  80 KB of LDS and at most 256
 // registers per lane let two workgroups share a CU, so one tile's loads overlap another's
 // products.
@@ -434,7 +414,8 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ F, i
                                                      const float* __restrict__ Mcur,
                                                      float* __restrict__ Unext,
                                                      float* __restrict__ Mnext,
-                                                     int* __restrict__ flag, int zpre) {
+                                                     int* __restrict__ flag, int64_t pcol0,
+                                                     int zblocks, int with_leaf) {
   __shared__ __attribute__((aligned(16))) float As[128 * 64];
   __shared__ __attribute__((aligned(16))) float Bs[128 * 64];
   __shared__ __attribute__((aligned(16))) float Ms[64 * 64];
@@ -447,7 +428,8 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ F, i
     const float4 v = *(const float4*)(Mcur + r * 64 + c4);
     Ms[swb(r, c4)] = v.x; Ms[swb(r, c4 + 1)] = v.y; Ms[swb(r, c4 + 2)] = v.z; Ms[swb(r, c4 + 3)] = v.w;
   }
-  if (blockIdx.x == 0) {
+  int b = blockIdx.x;
+  if (with_leaf && b == 0) {
     // A12[D] -> As rows 0..63, D -> Bs as the leaf's X (row stride LB)
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -457,25 +439,16 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ F, i
       *(float4*)(Bs + r * LB + c4) = *(const float4*)(F + (d0 + r) * n + d0 + c4);
     }
     const int wi = w >> 1, wj = w & 1;
-    if (zpre) {
-      // Z_D from the lower triangle, where this step's z_kernel left Z^T
-      for (int q = t; q < 64 * 64; q += 256) {
-        const int c = q >> 6, r = q & 63;
-        As[sw(64 + r, c)] = F[(s0 + c) * n + d0 + r];
-      }
-      __syncthreads();
-    } else {
-      __syncthreads();
-      // Z_D = A12[D] M into As rows 64..127
-      f32x16 acc = f32x16{};
+    __syncthreads();
+    // Z_D = A12[D] M into As rows 64..127
+    f32x16 acc = f32x16{};
 #pragma unroll 8
-      for (int k = 0; k < 64; k += 2)
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[sw(32 * wi + l32, k + kh)],
-                                                   Ms[swb(k + kh, 32 * wj + l32)], acc, 0, 0, 0);
+    for (int k = 0; k < 64; k += 2)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[sw(32 * wi + l32, k + kh)],
+                                                 Ms[swb(k + kh, 32 * wj + l32)], acc, 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) As[sw(64 + 32 * wi + 8 * (r >> 2) + 4 * kh + (r & 3), 32 * wj + l32)] = acc[r];
-      __syncthreads();
-    }
+    for (int r = 0; r < 16; ++r) As[sw(64 + 32 * wi + 8 * (r >> 2) + 4 * kh + (r & 3), 32 * wj + l32)] = acc[r];
+    __syncthreads();
     // D' = D - Z_D A12[D]^T
     f32x16 acc2 = f32x16{};
 #pragma unroll 8
@@ -491,35 +464,44 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ F, i
     leaf(Bs, As, Unext, Mnext, flag);
     return;
   }
-  // upper tile (tm, tn), tm <= tn, enumerated row by row
-  const int m = (int)((s0 + 127) / 128);
-  int idx = blockIdx.x - 1, tm = 0;
-  while (idx >= m - tm) { idx -= m - tm; ++tm; }
-  const int tn = tm + idx;
-  const int64_t i0 = (int64_t)tm * 128, j0 = (int64_t)tn * 128;
-  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
-  // this lane's tile entries: rows rbase + 32 i + 8 (r / 4) + r % 4, columns cbase + 32 j
-  const int64_t rbase = i0 + wm + 4 * kh, cbase = j0 + wn + l32;
-  const int rlim = (int)min((int64_t)128, s0 - rbase), clim = (int)min((int64_t)128, s0 - cbase);
-  // A12[I] (or, with zpre, Z[I] from the lower triangle) and A12[K] (rows past s0 read as 0):
-  // all loads first
-  const __amdgpu_buffer_rsrc_t ra = zpre ? rsrc(F + s0 * n + i0) : rsrc(F + i0 * n + s0);
-  const __amdgpu_buffer_rsrc_t rb = rsrc(F + j0 * n + s0);
-  float4 va[8], vb[8];
-  float vz[32];
-  if (zpre) {
-    // Z[I][r][c] = F[s0 + c][i0 + r]: lanes along r
-#pragma unroll
-    for (int it = 0; it < 32; ++it) {
-      const int c = 2 * it + (t >> 7), r = t & 127;
-      vz[it] = bload(ra, i0 + r < s0 ? (c * (int)n + r) * 4 : OOB);
-    }
-  } else {
+  if (with_leaf) b -= 1;
+  if (b < zblocks) {
+    // panel factor of rows i0 .. i0 + 127 (all below s0): Z = A12[I] M, stored as Z^T
+    const int64_t i0 = (int64_t)b * 128;
+    const __amdgpu_buffer_rsrc_t ra = rsrc(F + i0 * n + s0);
+    float4 va[8];
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int r = (t >> 4) + 16 * it, off = (r * (int)n + (t & 15) * 4) * 4;
       va[it] = bload4(ra, i0 + r < s0 ? off : OOB);
     }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = (t >> 4) + 16 * it, c4 = (t & 15) * 4;
+      As[sw(r, c4)] = va[it].x; As[sw(r, c4 + 1)] = va[it].y; As[sw(r, c4 + 2)] = va[it].z; As[sw(r, c4 + 3)] = va[it].w;
+    }
+    __syncthreads();
+    panel_z(As, Ms);
+    store_zt(F, n, s0, i0, As);
+    return;
+  }
+  b -= zblocks;
+  // tile (tm, tn), tm <= tn, of the columns tn >= pcol0 / 128, enumerated column by column
+  int tn = (int)(pcol0 / 128), tm = b;
+  while (tm > tn) { tm -= tn + 1; ++tn; }
+  const int64_t i0 = (int64_t)tm * 128, j0 = (int64_t)tn * 128;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  // this lane's tile entries: rows rbase + 32 i + 8 (r / 4) + r % 4, columns cbase + 32 j
+  const int64_t rbase = i0 + wm + 4 * kh, cbase = j0 + wn + l32;
+  const int rlim = (int)min((int64_t)128, s0 - rbase), clim = (int)min((int64_t)128, s0 - cbase);
+  // A12[I] and A12[K] (rows past s0 read as 0): all loads first
+  const __amdgpu_buffer_rsrc_t ra = rsrc(F + i0 * n + s0);
+  const __amdgpu_buffer_rsrc_t rb = rsrc(F + j0 * n + s0);
+  float4 va[8], vb[8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int r = (t >> 4) + 16 * it, off = (r * (int)n + (t & 15) * 4) * 4;
+    va[it] = bload4(ra, i0 + r < s0 ? off : OOB);
   }
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
@@ -527,15 +509,10 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ F, i
     vb[it] = bload4(rb, j0 + r < s0 ? off : OOB);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (zpre) {
 #pragma unroll
-    for (int it = 0; it < 32; ++it) As[sw(t & 127, 2 * it + (t >> 7))] = vz[it];
-  } else {
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int r = (t >> 4) + 16 * it, c4 = (t & 15) * 4;
-      As[sw(r, c4)] = va[it].x; As[sw(r, c4 + 1)] = va[it].y; As[sw(r, c4 + 2)] = va[it].z; As[sw(r, c4 + 3)] = va[it].w;
-    }
+  for (int it = 0; it < 8; ++it) {
+    const int r = (t >> 4) + 16 * it, c4 = (t & 15) * 4;
+    As[sw(r, c4)] = va[it].x; As[sw(r, c4 + 1)] = va[it].y; As[sw(r, c4 + 2)] = va[it].z; As[sw(r, c4 + 3)] = va[it].w;
   }
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
@@ -543,12 +520,10 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ F, i
     Bs[sw(r, c4)] = vb[it].x; Bs[sw(r, c4 + 1)] = vb[it].y; Bs[sw(r, c4 + 2)] = vb[it].z; Bs[sw(r, c4 + 3)] = vb[it].w;
   }
   __syncthreads();
-  if (!zpre) {
-    // Z[I] = A12[I] M
-    panel_z(As, Ms);
-    // the diagonal tiles also store Z^T
-    if (tm == tn) store_zt(F, n, s0, i0, As);
-  }
+  // Z[I] = A12[I] M
+  panel_z(As, Ms);
+  // the diagonal tiles also store Z^T
+  if (tm == tn) store_zt(F, n, s0, i0, As);
   // C -= Z[I] A12[K]^T in two halves of 32 k; each half's operands are read before its MFMAs
   f32x16 acc[2][2];
 #pragma unroll
@@ -744,25 +719,46 @@ kq_status damp_and_factor(const float* HX, float* F, float* T, uint8_t* dead, do
   const int64_t nb = n / NB;
   leaf_kernel<<<1, 256, 0, s>>>(F, n, n - NB, Ubuf + (nb - 1) * 4096, Mbuf + (nb - 1) * 4096, flag);
   KQ_LAUNCHED("leaf_kernel");
-  // steps whose update takes more than one round of workgroups (two per CU) form their panel
-  // factor once, ahead of the update, instead of in every tile (a third of a tile's products);
-  // on the shorter steps the extra launch would cost more than it saves (c3, 11008 wide:
-  // quantize 17.5 -> 16.1 ms; c2 is unchanged)
-  // (tests can move the threshold: both paths give the same factor)
-  const int64_t zpre_tiles =
-      testing_value(KQ_TESTING_FACTOR_PANEL_TILES, 2 * (int64_t)device_cu_count());
+  // super-blocks of SB columns (a multiple of 128, aligned to column 0): a step updates the
+  // columns of its own super-block that are still to come; the columns left of it take the
+  // super-block's whole update at its first block.  Worth it once the matrix outgrows the
+  // last-level cache: measured for the quantize stage (factor + GPTQ, out = 4096), 4096 wide
+  // 2.41 ms with no deferral against 2.66 ms at SB = 512; 8192 wide 7.80 ms at 1024 against
+  // 8.89 ms with none; 11008 wide 13.83 ms at 1024, 14.24 at 512, 17.55 with none.  (Tests
+  // can pick other widths: the same updates, summed in another order.)
+  const int64_t n128 = ceil_div(n, 128) * 128;
+  int64_t SB = testing_value(KQ_TESTING_FACTOR_SUPERBLOCK,
+                             n * n * (int64_t)sizeof(float) > ((int64_t)128 << 20) ? 1024 : n128);
+  if (SB < 128 || SB % 128 != 0) SB = 1024;
   for (int64_t s0 = n - NB; s0 >= NB; s0 -= NB) {
-    const int64_t m = ceil_div(s0, 128);
-    const int64_t tiles = m * (m + 1) / 2;
     const int64_t jb = s0 / NB;
-    const int zpre = tiles > zpre_tiles ? 1 : 0;
-    if (zpre) {
-      z_kernel<<<dim3((unsigned)m), dim3(256), 0, s>>>(F, n, s0, Mbuf + jb * 4096);
-      KQ_LAUNCHED("z_kernel");
-    }
-    update_kernel<<<dim3((unsigned)(1 + tiles)), dim3(256), 0, s>>>(
-        F, n, s0, Mbuf + jb * 4096, Ubuf + (jb - 1) * 4096, Mbuf + (jb - 1) * 4096, flag, zpre);
+    const int64_t S0 = (s0 / SB) * SB;          // first column of this block's super-block
+    const bool first = s0 == S0;                 // the super-block's first (leftmost) block
+    const int64_t m = ceil_div(s0, 128);
+    int64_t ptiles = 0;
+    if (!first)
+      for (int64_t tn = S0 / 128; tn < m; ++tn) ptiles += tn + 1;
+    // Z^T for the rows above the super-block (at its first block: for every row above s0)
+    const int64_t zb = first ? m : S0 / 128;
+    const int64_t grid = (first ? 0 : 1) + zb + ptiles;
+    update_kernel<<<dim3((unsigned)grid), dim3(256), 0, s>>>(
+        F, n, s0, Mbuf + jb * 4096, Ubuf + (jb - 1) * 4096, Mbuf + (jb - 1) * 4096, flag, S0,
+        (int)zb, first ? 0 : 1);
     KQ_LAUNCHED("update_kernel");
+    if (first) {
+      // F[0:S0, 0:S0] (upper tiles) -= A12 Z^T over the super-block's columns [S0, S0 + K):
+      // A12 = F[0:S0, S0:S0+K], Z^T = F[S0:S0+K, 0:S0] (the lower triangle)
+      GemmArgs g{};
+      g.M = S0; g.N = S0; g.K = std::min<int64_t>(SB, n - S0);
+      g.A = F + S0; g.lda = n; g.transA = false;
+      g.B = F + S0 * n; g.ldb = n; g.transB = false;
+      g.C = F; g.ldc = n; g.alpha = -1.0f; g.accumulate = true; g.upper_only = true;
+      g.split_k = 1; g.batch = 1;
+      KQ_TRY(gemm_f32(g, s));
+      leaf_kernel<<<1, 256, 0, s>>>(F, n, s0 - NB, Ubuf + (jb - 1) * 4096, Mbuf + (jb - 1) * 4096,
+                                    flag);
+      KQ_LAUNCHED("leaf_kernel");
+    }
   }
   finalize_kernel<<<dim3((unsigned)nb), dim3(256), 0, s>>>(F, n, Ubuf);
   KQ_LAUNCHED("finalize_kernel");

@@ -297,6 +297,7 @@ struct DArgs {
   float* C; int64_t ldc;
   float alpha;
   int accumulate, split_k;
+  int upper_only;     // only tiles with tile row <= tile column
   int64_t k_per_split;
   int64_t partial_stride;
 };
@@ -323,6 +324,7 @@ __global__ __launch_bounds__(THREADS) void gemm_nn_dma_kernel(DArgs a) {
   __shared__ __attribute__((aligned(1024))) float r1[DSTG];
   __shared__ __attribute__((aligned(1024))) float r2[DSTG];
   __shared__ __attribute__((aligned(1024))) float r3[DSTG];
+  if (a.upper_only && blockIdx.x > blockIdx.y) return;
   const int64_t m0 = (int64_t)blockIdx.x * MT, n0 = (int64_t)blockIdx.y * NTL;
   const int64_t kbeg = (int64_t)blockIdx.z * a.k_per_split;
   const int64_t kend = min(a.K, kbeg + a.k_per_split);
@@ -537,12 +539,12 @@ kq_status gemm_f32(const GemmArgs& g, hipStream_t s) {
   // plain row-major products with 16-byte aligned rows take the direct-to-LDS kernel
   const bool aligned = ((uintptr_t)g.A % 16 == 0) && ((uintptr_t)g.B % 16 == 0) &&
                        g.lda % 4 == 0 && g.ldb % 4 == 0 && g.K % 4 == 0 && g.N % 4 == 0;
-  if (!g.transA && !g.transB && !g.a_upper && !g.b_upper && !g.upper_only && !g.red &&
+  if (!g.transA && !g.transB && !g.a_upper && !g.b_upper && !g.red &&
       (g.batch <= 1) && aligned && g.K > 0 && 128 * g.lda + (int64_t)DBK * g.ldb < ((int64_t)1 << 32)) {
     DArgs d;
     d.M = g.M; d.N = g.N; d.K = g.K;
     d.A = g.A; d.lda = g.lda; d.B = g.B; d.ldb = g.ldb; d.C = g.C; d.ldc = g.ldc;
-    d.alpha = g.alpha; d.accumulate = g.accumulate;
+    d.alpha = g.alpha; d.accumulate = g.accumulate; d.upper_only = g.upper_only ? 1 : 0;
     d.k_per_split = ceil_div(ceil_div(g.K, g.split_k), DBK) * DBK;
     d.split_k = (int)ceil_div(g.K, d.k_per_split);
     d.partial_stride = g.partial_stride;

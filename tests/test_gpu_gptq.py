@@ -164,22 +164,20 @@ def test_quantize_block_pairs(bits, group, block):
     check_against_oracle(g, Wt, HXt, HGt, bits, group)
 
 
-def test_factor_panel_formed_once_matches_per_tile():
-    """The factorization forms each step's panel factor Z once, ahead of the update, on steps
-    with many tiles; forcing that path on every step gives the same bits as forming Z in each
-    tile (the same products in the same order)."""
-    announce("gptq factorization with the panel factor formed once")
+@pytest.mark.parametrize("sb", [128, 256, 512, 1024])
+def test_factorization_superblock_widths(sb):
+    """The factorization defers each block's update of the columns left of its super-block to
+    one rank-(super-block) product; every width (one block per super-block boundary at 128,
+    none at 1024 for this 1024-wide layer) gives GPTQ results that match the oracle."""
+    import post_quantization_syrk_amd as kq
+    announce(f"gptq factorization with super-blocks of {sb} columns")
     rng = np.random.default_rng(21)
     out_n, in_n = 72, 1024
     Wt = (rng.standard_normal((out_n, in_n)) * 0.05).astype(np.float32).astype(np.float64)
     HXt = spd(rng, in_n, outliers=2).astype(np.float32).astype(np.float64)
     HGt = spd(rng, out_n).astype(np.float32).astype(np.float64)
-    import post_quantization_syrk_amd as kq
-    ref = gpu_quantize(Wt, HXt, HGt, 3, 128, 128)
-    with kq.testing_select(kq.KQ_TESTING_FACTOR_PANEL_TILES, 0):
+    with kq.testing_select(kq.KQ_TESTING_FACTOR_SUPERBLOCK, sb):
         g = gpu_quantize(Wt, HXt, HGt, 3, 128, 128)
-    for key in ("E", "packed", "scales", "zeros", "codes"):
-        assert np.array_equal(g[key], ref[key]), key
     check_against_oracle(g, Wt, HXt, HGt, 3, 128)
 
 
@@ -301,3 +299,4 @@ def test_engine_damping_read_from_its_losses(dead_ch):
     lam_engine = (g["loss"][1] - g["loss"][0]) / float(np.sum(dW * dW))
     announce(f"damping: engine lambda {lam_engine:.6e}, by hand {lam_hand:.6e}")
     assert lam_engine == pytest.approx(lam_hand, rel=1e-3)
+
