@@ -41,6 +41,7 @@ PEAK_HBM_GBS = 8000.0
 
 WORKLOADS = {"c1": syn.C1, "c2": syn.C2, "c2r": syn.C2R, "c3": syn.C3, "c5": syn.C5}
 STACK = "c4"   # the decoder stack (not a single layer)
+STACK_STREAMS = 4   # streams the stack's sublayer quantizations are dealt to
 DEFAULT_WORKLOAD = "c5"
 
 
@@ -602,7 +603,10 @@ def stack_main(a) -> None:
               (kq_accumulate_hessian), the 224 sensitivities (kq_sensitivity_async);
       bits:   one synchronization, the sensitivities to the host, kq_allocate_bits;
       pass 2: per sublayer, BiIP out of place from the raw factors (q/k/v and gate/up share
-              H_X) and GPTQ to packed codes at the allocated width (kq_quantize_layer).
+              H_X) and GPTQ to packed codes at the allocated width (kq_quantize_layer_async),
+              the sublayers dealt round-robin to STACK_STREAMS streams with a workspace each,
+              so that one sublayer's latency-bound factorization chain overlaps others' work;
+              every status is checked after the timed steps.
     The streams are drawn on the device (torch's generator, seeded per layer and stream) with
     the stack's recipe: per-channel std exp(sigma N(0, 1)), sigma per layer in U[0.5, 2] as
     the parity tests' generator gives it, N(0, 1) entries, rounded to bf16; weights
@@ -650,14 +654,17 @@ def stack_main(a) -> None:
                 out=out_n, inp=in_n, xid=xid, hin=hin, hout=hout))
         layers.append((xs, hx, subs))
     nmax = max(max(o_, i_) for _, o_, i_, _, _, _ in subl)
-    HXt = torch.empty(nmax * nmax, device=dev)
-    HGt = torch.empty(nmax * nmax, device=dev)
-    Wt = torch.empty(max(o_ * i_ for _, o_, i_, _, _, _ in subl), device=dev)
-    d_in, d_out = torch.empty(nmax, device=dev), torch.empty(nmax, device=dev)
     params = {b: kq.make_params(b, 128, 128, 0.01) for b in (2, 3, 4)}
     ws_bytes = max(kq.kq_quantize_layer_workspace(params[b], o_, i_, False)
                    for b in (2, 3, 4) for _, o_, i_, _, _, _ in subl)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    # per pass-2 stream: processed factors, weights, rescale vectors and a workspace
+    lanes = [dict(stream=torch.cuda.Stream(), HXt=torch.empty(nmax * nmax, device=dev),
+                  HGt=torch.empty(nmax * nmax, device=dev),
+                  Wt=torch.empty(max(o_ * i_ for _, o_, i_, _, _, _ in subl), device=dev),
+                  d_in=torch.empty(nmax, device=dev), d_out=torch.empty(nmax, device=dev),
+                  ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev))
+             for _ in range(STACK_STREAMS)]
+    status = torch.full((L * len(subl),), -1, dtype=torch.int32, device=dev)
     sens = torch.empty((L * len(subl), 3), dtype=torch.float64, device=dev)
     numel = [o_ * i_ for _ in range(L) for _, o_, i_, _, _, _ in subl]
     torch.cuda.synchronize()
@@ -693,20 +700,28 @@ def stack_main(a) -> None:
         bits = kq.kq_allocate_bits(list(s_host), numel, (2, 3, 4), 5, 2)
         if record:
             e[2].record(stream)
+        # pass 2 on the lanes' streams, after everything above on the main stream
+        for ln in lanes:
+            ln["stream"].wait_stream(stream)
         i = 0
         for xs, hx, subs in layers:
             for sb in subs:
+                ln = lanes[i % len(lanes)]
+                st = ln["stream"]
                 o_, i_ = sb["out"], sb["inp"]
-                hxt, hgt = HXt[:i_ * i_].view(i_, i_), HGt[:o_ * o_].view(o_, o_)
-                wt = Wt[:o_ * i_].view(o_, i_)
+                hxt, hgt = ln["HXt"][:i_ * i_].view(i_, i_), ln["HGt"][:o_ * o_].view(o_, o_)
+                wt = ln["Wt"][:o_ * i_].view(o_, i_)
                 kq.kq_biip_rotate(sb["W"], wt, hx[sb["xid"]], hxt, sb["HG"], hgt, sb["s_in"],
-                                  sb["s_out"], d_in[:i_], d_out[:o_], 0.25, kq.KQ_BIIP_FULL,
-                                  sb["hin"], sb["hout"], stream=stream)
+                                  sb["s_out"], ln["d_in"][:i_], ln["d_out"][:o_], 0.25,
+                                  kq.KQ_BIIP_FULL, sb["hin"], sb["hout"], stream=st)
                 b = bits[i]
                 packed = sb["packed"][:o_ * i_ * b // 32].view(o_, i_ * b // 32)
-                kq.kq_quantize_layer(params[b], wt, hxt, hgt, packed, sb["scales"], sb["zeros"], ws,
-                                     stream=stream)
+                kq.kq_quantize_layer_async(params[b], wt, hxt, hgt, packed, sb["scales"], sb["zeros"],
+                                           ln["ws"], status[i:i + 1], stream=st)
                 i += 1
+        # the next step's pass 1 overwrites the raw factors pass 2 reads
+        for ln in lanes:
+            stream.wait_stream(ln["stream"])
         if record:
             e[3].record(stream)
         return e, syrk_ev, bits
@@ -721,6 +736,9 @@ def stack_main(a) -> None:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / a.steps
+    bad = int((status != kq.KQ_OK).sum().item())
+    if bad:
+        raise RuntimeError(f"{bad} sublayers did not quantize (status != KQ_OK)")
     total_params = float(sum(numel))
     stages = {nm: float(np.mean([r[0][i].elapsed_time(r[0][i + 1]) for r in recs]))
               for i, nm in enumerate(["pass1_hessians_sensitivities", "allocation", "pass2_biip_quantize"])}
@@ -747,7 +765,8 @@ def stack_main(a) -> None:
                    "bits_allowed": [2, 3, 4], "avg_bits_target": 2.5,
                    "avg_bits": round(sum(b * n for b, n in zip(bits, numel)) / total_params, 4),
                    "bits_count": {str(b): bits.count(b) for b in (2, 3, 4)},
-                   "group": 128, "block": 128, "alpha": 0.25, "damp": 0.01},
+                   "group": 128, "block": 128, "alpha": 0.25, "damp": 0.01,
+                   "pass2_streams": STACK_STREAMS},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile(

@@ -228,6 +228,26 @@ kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, const float*
                             float* scales, uint8_t* zeros, uint8_t* codes_opt, double* loss_opt,
                             void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * kq_quantize_layer_async -- kq_quantize_layer with its status and losses left in device
+ * memory: nothing is waited for, so a caller can quantize many layers in a row, or on
+ * several streams at once, and read every status after its own synchronization.
+ *
+ * Follows: the same passages as kq_quantize_layer, and computes the same results with the
+ * same kernels.  Arguments as kq_quantize_layer, except:
+ *   loss_dev_opt  device, 2 doubles, or NULL: {direct loss, predicted loss} written when the
+ *                 work runs (the workspace must then be sized with losses)
+ *   status_dev    device int (required): KQ_OK, or KQ_ENOTSPD when the damped H~_X has a
+ *                 non-positive pivot, written when the work runs
+ * Argument errors (KQ_EINVAL, KQ_ESHAPE, KQ_ENOTIMPL, KQ_EWORKSPACE) are returned before
+ * anything is enqueued; KQ_EHIP if a launch fails.
+ */
+kq_status kq_quantize_layer_async(const kq_quant_params* p, float* W_rot, const float* HX_rot,
+                                  const float* HG_rot, int64_t out, int64_t in, uint32_t* packed,
+                                  float* scales, uint8_t* zeros, uint8_t* codes_opt,
+                                  double* loss_dev_opt, int* status_dev, void* ws,
+                                  size_t ws_bytes, void* stream);
+
 /* Largest workspace kq_quantize_layer_noalloc serves: a layer is accepted when
  * kq_quantize_layer_workspace reports at most this many bytes for it (with losses when
  * losses are requested); e.g. a 2048 x 2048 layer without losses (49 MiB) or a 1024 x 1024

@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "KQ_OK", 1: "KQ_EINVAL", 2: "KQ_ESHAPE", 3: "KQ_ENOTSPD", 4: 
 EXPORTED = ("kq_version", "kq_last_error", "kq_accumulate_hessian", "kq_sensitivity",
             "kq_sensitivity_async",
             "kq_biip_rotate", "kq_quantize_layer_workspace", "kq_quantize_layer",
-            "kq_quantize_layer_noalloc",
+            "kq_quantize_layer_noalloc", "kq_quantize_layer_async",
             "kq_allocate_bits", "kq_deploy_linear", "kq_deploy_linear_group",
             "kq_flipflop_workspace", "kq_flipflop", "kq_quantize_two_sided_workspace",
             "kq_quantize_two_sided", "kq_testing_select")
@@ -69,6 +69,8 @@ _SIGS = {
                                      ctypes.POINTER(_sz)], _int),
     "kq_quantize_layer": ([ctypes.POINTER(QuantParams), _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp,
                            _vp, _vp, _sz, _vp], _int),
+    "kq_quantize_layer_async": ([ctypes.POINTER(QuantParams), _vp, _vp, _vp, _i64, _i64, _vp, _vp,
+                                 _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "kq_quantize_layer_noalloc": ([ctypes.POINTER(QuantParams), _vp, _vp, _vp, _i64, _i64, _vp, _vp,
                                    _vp, _vp, _vp, _vp], _int),
     "kq_allocate_bits": ([_vp, _vp, _i64, _vp, _int, _i64, _i64, _vp], _int),
@@ -255,6 +257,26 @@ def kq_quantize_layer(p: QuantParams, W_rot, HX_rot, HG_rot, packed, scales, zer
         _dev_ptr(ws, "ws", (torch.uint8,)), ws.numel(), _stream(stream))
     _check(st, "kq_quantize_layer")
     return (loss[0], loss[1]) if want_loss else None
+
+
+def kq_quantize_layer_async(p: QuantParams, W_rot, HX_rot, HG_rot, packed, scales, zeros, ws,
+                            status, codes=None, loss=None, stream=None) -> None:
+    """kq_quantize_layer without waiting: `status` (device int32, 1 entry) receives KQ_OK or
+    KQ_ENOTSPD and `loss` (device float64, 2 entries, optional) the two losses, when the work
+    has run."""
+    torch = _torch()
+    lib = load_library()
+    out_n, in_n = W_rot.shape
+    st = lib.kq_quantize_layer_async(
+        ctypes.byref(p), _dev_ptr(W_rot, "W_rot", (torch.float32,)),
+        _dev_ptr(HX_rot, "HX_rot", (torch.float32,)),
+        _dev_ptr(HG_rot, "HG_rot", (torch.float32,), True), out_n, in_n,
+        _dev_ptr(packed, "packed", (torch.int32, torch.uint32)),
+        _dev_ptr(scales, "scales", (torch.float32,)), _dev_ptr(zeros, "zeros", (torch.uint8,)),
+        _dev_ptr(codes, "codes", (torch.uint8,), True), _dev_ptr(loss, "loss", (torch.float64,), True),
+        _dev_ptr(status, "status", (torch.int32,)), _dev_ptr(ws, "ws", (torch.uint8,)), ws.numel(),
+        _stream(stream))
+    _check(st, "kq_quantize_layer_async")
 
 
 KQ_NOALLOC_WORKSPACE_BYTES = 64 << 20

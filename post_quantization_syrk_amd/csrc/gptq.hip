@@ -728,14 +728,30 @@ extern "C" kq_status kq_quantize_layer_workspace(const kq_quant_params* p, int64
 namespace kq {
 namespace {
 
+// Status and losses of an asynchronous call, written when its work has run.
+__global__ void quantize_finish_kernel(const double* __restrict__ scal, const int* __restrict__ flag,
+                                       double* __restrict__ loss_dev, int* __restrict__ status_dev) {
+  if (threadIdx.x == 0) {
+    if (loss_dev) {
+      loss_dev[0] = scal[1];
+      loss_dev[1] = scal[2];
+    }
+    *status_dev = flag[0] ? (int)KQ_ENOTSPD : (int)KQ_OK;
+  }
+}
+
+// The quantizer.  Synchronous (status_dev == NULL): losses to the host loss_opt, the status
+// returned after a stream synchronization.  Asynchronous: losses to the device loss_dev, the
+// status to the device status_dev, nothing waited for.
 kq_status quantize_layer(const kq_quant_params* p, float* W_rot, const float* HX_rot,
                          const float* HG_rot, int64_t out, int64_t in, uint32_t* packed,
                          float* scales, uint8_t* zeros, uint8_t* codes_opt, double* loss_opt,
-                         void* ws, size_t ws_bytes, void* stream) {
+                         void* ws, size_t ws_bytes, void* stream, double* loss_dev = nullptr,
+                         int* status_dev = nullptr) {
   KQ_TRY(check_params(p, out, in));
   if (!W_rot || !HX_rot || !packed || !scales || !zeros)
     return fail(KQ_EINVAL, "kq_quantize_layer: NULL argument");
-  const bool with_loss = loss_opt != nullptr;
+  const bool with_loss = loss_opt != nullptr || loss_dev != nullptr;
   const int B = p->block;
   const bool ao = p->act_order != 0, clip = p->w_clip != 0;
   // a group spanning the whole row (group == in > block, or any row grid with act_order or
@@ -876,6 +892,11 @@ kq_status quantize_layer(const kq_quant_params* p, float* W_rot, const float* HX
       KQ_LAUNCHED("dot_kernel");
     }
   }
+  if (status_dev) {
+    quantize_finish_kernel<<<dim3(1), dim3(64), 0, s>>>(scal, flag, loss_dev, status_dev);
+    KQ_LAUNCHED("quantize_finish_kernel");
+    return KQ_OK;
+  }
   double host_scal[3] = {0, 0, 0};
   int host_flag = 0;
   KQ_HIP(hipMemcpyAsync(host_scal, scal, sizeof(host_scal), hipMemcpyDeviceToHost, s));
@@ -925,6 +946,17 @@ extern "C" kq_status kq_quantize_layer(const kq_quant_params* p, float* W_rot, c
                                        size_t ws_bytes, void* stream) {
   return kq::quantize_layer(p, W_rot, HX_rot, HG_rot, out, in, packed, scales, zeros, codes_opt,
                             loss_opt, ws, ws_bytes, stream);
+}
+
+extern "C" kq_status kq_quantize_layer_async(const kq_quant_params* p, float* W_rot,
+                                             const float* HX_rot, const float* HG_rot,
+                                             int64_t out, int64_t in, uint32_t* packed,
+                                             float* scales, uint8_t* zeros, uint8_t* codes_opt,
+                                             double* loss_dev_opt, int* status_dev, void* ws,
+                                             size_t ws_bytes, void* stream) {
+  if (!status_dev) return kq::fail(KQ_EINVAL, "kq_quantize_layer_async: status_dev is NULL");
+  return kq::quantize_layer(p, W_rot, HX_rot, HG_rot, out, in, packed, scales, zeros, codes_opt,
+                            nullptr, ws, ws_bytes, stream, loss_dev_opt, status_dev);
 }
 
 extern "C" kq_status kq_quantize_layer_noalloc(const kq_quant_params* p, float* W_rot,

@@ -300,3 +300,62 @@ def test_engine_damping_read_from_its_losses(dead_ch):
     announce(f"damping: engine lambda {lam_engine:.6e}, by hand {lam_hand:.6e}")
     assert lam_engine == pytest.approx(lam_hand, rel=1e-3)
 
+
+def test_quantize_async_matches_sync_and_reports_status():
+    """kq_quantize_layer_async leaves the status and losses in device memory: on several
+    streams at once its outputs equal the synchronous call's bit for bit, its losses match
+    the synchronous ones, and a non-positive pivot is reported as KQ_ENOTSPD in the status."""
+    torch = torch_cuda()
+    import post_quantization_syrk_amd as kq
+    announce("gptq async calls on three streams")
+    rng = np.random.default_rng(31)
+    cases = []
+    for out_n, in_n, bits, group in ((96, 512, 3, 128), (64, 384, 4, 128), (130, 256, 2, 64)):
+        Wt = (rng.standard_normal((out_n, in_n)) * 0.05).astype(np.float32)
+        HXt = spd(rng, in_n, outliers=2).astype(np.float32)
+        HGt = spd(rng, out_n).astype(np.float32)
+        cases.append((Wt, HXt, HGt, bits, group))
+    streams = [torch.cuda.Stream() for _ in cases]
+    outs = []
+    for (Wt, HXt, HGt, bits, group), st in zip(cases, streams):
+        out_n, in_n = Wt.shape
+        p = kq.make_params(bits, group, 128 if in_n % 128 == 0 else 64, 0.01)
+        with torch.cuda.stream(st):
+            W = torch.from_numpy(Wt).cuda()
+            HX, HG = torch.from_numpy(HXt).cuda(), torch.from_numpy(HGt).cuda()
+            ws = torch.empty(kq.kq_quantize_layer_workspace(p, out_n, in_n, True), dtype=torch.uint8,
+                             device="cuda")
+            o = dict(W=W, packed=torch.zeros((out_n, in_n * bits // 32), dtype=torch.int32, device="cuda"),
+                     scales=torch.zeros((out_n, in_n // group), device="cuda"),
+                     zeros=torch.zeros((out_n, in_n // group), dtype=torch.uint8, device="cuda"),
+                     codes=torch.zeros((out_n, in_n), dtype=torch.uint8, device="cuda"),
+                     loss=torch.zeros(2, dtype=torch.float64, device="cuda"),
+                     status=torch.full((1,), -1, dtype=torch.int32, device="cuda"), ws=ws, HX=HX, HG=HG)
+            kq.kq_quantize_layer_async(p, W, HX, HG, o["packed"], o["scales"], o["zeros"], ws, o["status"],
+                                       codes=o["codes"], loss=o["loss"], stream=st)
+        outs.append((o, p))
+    torch.cuda.synchronize()
+    for (Wt, HXt, HGt, bits, group), (o, p) in zip(cases, outs):
+        assert int(o["status"].item()) == kq.KQ_OK
+        ref = gpu_quantize(Wt.astype(np.float64), HXt.astype(np.float64), HGt.astype(np.float64), bits,
+                           group, p.block)
+        assert np.array_equal(o["codes"].cpu().numpy().astype(np.int64), ref["codes"])
+        assert np.array_equal(o["packed"].cpu().numpy().view(np.uint32), ref["packed"])
+        assert np.array_equal(o["scales"].cpu().numpy(), ref["scales"])
+        assert np.array_equal(o["W"].cpu().numpy(), ref["E"])
+        lo = o["loss"].cpu().numpy()
+        assert lo[0] == pytest.approx(ref["loss"][0], rel=1e-9)
+        assert lo[1] == pytest.approx(ref["loss"][1], rel=1e-9)
+    # a non-positive pivot: no exception, the status says so
+    H = spd(rng, 64)
+    H[10, 10] = -50.0 * H[10, 10]
+    p = kq.make_params(2, 64, 64, 0.01)
+    W = torch.from_numpy(rng.standard_normal((16, 64)).astype(np.float32)).cuda()
+    status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(kq.kq_quantize_layer_workspace(p, 16, 64, False), dtype=torch.uint8, device="cuda")
+    kq.kq_quantize_layer_async(p, W, torch.from_numpy(H.astype(np.float32)).cuda(), None,
+                               torch.zeros((16, 4), dtype=torch.int32, device="cuda"),
+                               torch.zeros((16, 1), device="cuda"),
+                               torch.zeros((16, 1), dtype=torch.uint8, device="cuda"), ws, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == kq.KQ_ENOTSPD
