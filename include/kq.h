@@ -407,8 +407,10 @@ kq_status kq_flipflop_workspace(int64_t T, int64_t n, int64_t m, size_t* bytes);
  * normalization; A (x) B does not depend on it.  Inverses: the reverse Cholesky factor of
  * the current factor without damping (a zero diagonal entry counts as 1); the inverse
  * factor enters the per-token quadratic forms as two bf16 terms (its rounding and the
- * rounding of the remainder, about 16 significant bits) with fp32 accumulation, and so does
- * each scaled token row in the SYRK (the factor of the two-term stream, folded).
+ * rounding of the remainder, about 16 significant bits) with fp32 accumulation.  Each factor
+ * is formed as sum_t a_t s_t^T, the per-token weight applied to one side only: a_t (the
+ * weighted token row) as two bf16 terms against the exact bf16 stream s_t, the lower
+ * triangle computed and mirrored (exactly symmetric).
  *
  *   X, G     device bf16 bit patterns, T x n and T x m, token-major, leading dims ldx, ldg
  *            (multiples of 8, >= the widths), 16-byte aligned

@@ -24,9 +24,10 @@ enum {
    * register-staged kernel that serves strides too large for the default (bit 0: 8 waves
    * instead of 4; bit 1: split-major workgroup order). */
   KQ_TESTING_SYRK_KERNEL = 0,
-  /* Columns per super-block of kq_quantize_layer's factorization (a multiple of 128,
-   * default 512): each block's update of the columns left of its super-block waits for one
-   * rank-(super-block) update.  The same updates, summed in another order. */
+  /* Columns per super-block of kq_quantize_layer's factorization (a multiple of 128;
+   * default 1024 for factors larger than 128 MB, else the whole width): each block's update
+   * of the columns left of its super-block waits for one rank-(super-block) update.  The
+   * same updates, summed in another order. */
   KQ_TESTING_FACTOR_SUPERBLOCK = 1,
   /* Longest row (bytes) the quantizer's row kernels stage in LDS (default 65536); 0 forces
    * their direct paths, which longer rows take. */

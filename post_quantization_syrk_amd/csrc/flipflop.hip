@@ -17,13 +17,14 @@
 //      U_lo = bf16(U - U_hi), multiplied into the same accumulators (the contraction runs
 //      twice), so U carries about 16 significant bits: with U_hi alone its rounding is the
 //      same in every token and its error in the factors does not average out.
-//   3. The scaled stream y_t = sqrt(w_t / (T m)) x_t goes through the SYRK as two bf16
-//      terms, y_hi = bf16(y) and y_lo = bf16(y - y_hi), side by side in one stream of width
-//      2n: its factor H2 = [y_hi y_lo]^T [y_hi y_lo] holds hi.hi, lo.hi and lo.lo, and
-//      A = sum_t y_t y_t^T = hi.hi + lo.hi + (lo.hi)^T + lo.lo, folded in one fixed order
-//      per unordered pair (i, j), so A is exactly symmetric.  With y rounded once the
-//      per-token weights' rounding would not average out (a few heavy tokens dominate the
-//      sum); with two terms each entry of y carries about 16 significant bits.
+//   3. A = sum_t a_t x_t^T with a_t = (w_t / (T m)) x_t: the weight goes on one side only,
+//      so the other operand is the exact bf16 stream x.  a enters as two bf16 terms,
+//      a_hi = bf16(a) and a_lo = bf16(a - a_hi) (about 16 significant bits; with a rounded
+//      once the per-token weights' rounding would not average out, a few heavy tokens
+//      dominating the sum), through the SYRK's kernel with a second stream for the column
+//      channels: the lower tiles of a_hi x^T, then of a_lo x^T added to them, then the lower
+//      triangle mirrored, so A is exactly symmetric.  Two products of width n, half the
+//      work of a SYRK of the stream [y_hi y_lo] of width 2n.
 //
 // qform_kernel: 256-token x 256-output tiles, 4 waves of 128 x 128 (4 x 4 blocks of
 // v_mfma_f32_32x32x16_bf16); stages of 32 contraction indices: both panels (256 rows x 64
@@ -258,8 +259,8 @@ __global__ __launch_bounds__(256) void qform_kernel(QArgs a) {
   }
 }
 
-// y = sqrt(c * sum_p part[t, p]) * S[t, :]: out[t, 0:k] = bf16(y) and out[t, k:2k] =
-// bf16(y - bf16(y)) (round to nearest even; the remainder is exact in fp32); one workgroup per
+// a = c * sum_p part[t, p] * S[t, :]: out[t, 0:k] = bf16(a) and out[t, k:2k] =
+// bf16(a - bf16(a)) (round to nearest even; the remainder is exact in fp32); one workgroup per
 // token, 8 channels per thread and step.
 __global__ __launch_bounds__(256) void ff_scale_kernel(const uint16_t* __restrict__ S, int64_t lds,
                                                        int k, const float* __restrict__ part,
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(256) void ff_scale_kernel(const uint16_t* __restric
     for (int p = threadIdx.x; p < np; p += 64) w += part[t * np + p];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) w += __shfl_xor(w, o);
-    if (threadIdx.x == 0) sf = sqrtf(c * w);
+    if (threadIdx.x == 0) sf = c * w;
   }
   __syncthreads();
   const float f = sf;
@@ -297,21 +298,6 @@ __global__ __launch_bounds__(256) void ff_scale_kernel(const uint16_t* __restric
     *(u32x4*)(out + t * ldo + i) = oh;
     *(u32x4*)(out + t * ldo + k + i) = ol;
   }
-}
-
-// out (k x k, full symmetric) from the 2k x 2k factor H2 of the two-term stream:
-// out[i][j] = (H2[a][b] + H2[k + a][k + b]) + (H2[k + a][b] + H2[k + b][a]) with
-// (a, b) = (max(i, j), min(i, j)): the same terms in the same order for (i, j) and (j, i).
-// One workgroup per 256 entries of a row (jb row blocks per row).
-__global__ __launch_bounds__(256) void ff_fold_kernel(const float* __restrict__ H2, int64_t k,
-                                                      int64_t jb, float* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x / jb;
-  const int64_t j = ((int64_t)blockIdx.x % jb) * 256 + threadIdx.x;
-  if (j >= k) return;
-  const int64_t k2 = 2 * k;
-  const int64_t a = i > j ? i : j, b = i > j ? j : i;
-  out[i * k + j] = (H2[a * k2 + b] + H2[(k + a) * k2 + k + b]) +
-                   (H2[(k + a) * k2 + b] + H2[(k + b) * k2 + a]);
 }
 
 // The diagonal 128-blocks of U: the upper triangles of F's diagonal blocks (U_JJ); below
@@ -351,9 +337,8 @@ __global__ void identity_kernel(float* __restrict__ M, int64_t k) {
 }
 
 struct Workspace {
-  uint16_t* Ss;    // scaled stream as two bf16 terms, T x ldS (ldS >= 2 kmax)
+  uint16_t* Ss;    // weighted stream as two bf16 terms side by side, T x ldS (ldS >= 2 kmax)
   int64_t ldS;
-  float* H2;       // its factor, (2 kmax)^2
   float* part;     // T x npmax
   float* F;        // factorization, kmax^2
   float* Tsc;      // factorization scratch, 128 kmax
@@ -374,7 +359,6 @@ int64_t layout(int64_t T, int64_t n, int64_t m, char* base, Workspace* w) {
   Workspace x;
   x.ldS = (2 * k + 7) / 8 * 8;
   x.Ss = (uint16_t*)take(T * x.ldS * 2);
-  x.H2 = (float*)take(4 * k * k * 4);
   x.part = (float*)take(T * np * 4);
   x.F = (float*)take(k * k * 4);
   x.Tsc = (float*)take(128 * k * 4);
@@ -457,10 +441,8 @@ kq_status half_step(const float* M, const uint16_t* S2, int64_t ld2, int64_t k2,
   ff_scale_kernel<<<dim3((unsigned)T), dim3(256), 0, s>>>(S1, ld1, (int)k1, w.part, np, c, w.Ss, w.ldS);
   KQ_LAUNCHED("ff_scale_kernel");
   KQ_TRY(pt.mark(s));
-  KQ_TRY(kq_accumulate_hessian(w.Ss, T, 2 * k1, w.ldS, w.H2, 2 * k1, 0, s));
-  const int64_t jb = ceil_div(k1, 256);
-  ff_fold_kernel<<<dim3((unsigned)(jb * k1)), dim3(256), 0, s>>>(w.H2, k1, jb, out);
-  KQ_LAUNCHED("ff_fold_kernel");
+  KQ_TRY(gram_lower(w.Ss, w.ldS, S1, ld1, T, k1, out, k1, false, false, s));
+  KQ_TRY(gram_lower(w.Ss + k1, w.ldS, S1, ld1, T, k1, out, k1, true, true, s));
   return pt.mark(s);
 }
 

@@ -64,6 +64,12 @@ kq_status gemm_f32(const GemmArgs& g, hipStream_t s);
 kq_status explicit_inverse_factor(const float* M, int64_t k, float damp, float* F, float* Tsc,
                                   uint8_t* dead, double* lam, int* flag, float* U, hipStream_t s);
 
+// H's lower block triangle (+)= sum_t A[t, i] B[t, j] over T tokens of two bf16 streams of n
+// channels (16-byte aligned, strides multiples of 8), then optionally the lower triangle
+// mirrored into the upper one; B == A forms the Hessian A^T A (syrk.hip).
+kq_status gram_lower(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t T,
+                     int64_t n, float* H, int64_t ldh, bool accumulate, bool mirror, hipStream_t s);
+
 }  // namespace kq
 
 #define KQ_HIP(expr)                                                                  \

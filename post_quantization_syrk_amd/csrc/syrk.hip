@@ -46,8 +46,10 @@ constexpr int PANEL = TILE * BK;   // bf16 elements of one panel in LDS (no padd
 constexpr int BAND = 4;            // tile rows per band in the visiting order
 
 struct SyrkArgs {
-  const uint16_t* A;
+  const uint16_t* A;   // the tiles' row channels
   int64_t lda;
+  const uint16_t* B;   // the tiles' column channels (B == A for a Hessian; only the
+  int64_t ldb;         // direct-to-LDS kernel reads B)
   int64_t T;
   int n;
   float* H;
@@ -387,7 +389,7 @@ __global__ __launch_bounds__(DWAVES * 64) void syrk_dma_kernel(DmaArgs d) {
     const int row = 2 * (DMA_PER_PANEL * wave + r) + (lane >> 5);
     const int k8 = 8 * ((lane & 31) ^ dswz(row & 3));
     offi[r] = (uint32_t)(row * a.lda) + (uint32_t)(ci + k8 < a.n ? ci + k8 : 0);
-    offj[r] = (uint32_t)(row * a.lda) + (uint32_t)(cj + k8 < a.n ? cj + k8 : 0);
+    offj[r] = (uint32_t)(row * a.ldb) + (uint32_t)(cj + k8 < a.n ? cj + k8 : 0);
   }
 
   // per-lane element offsets of the operand reads inside a panel (first token half, kk = 0)
@@ -412,9 +414,8 @@ __global__ __launch_bounds__(DWAVES * 64) void syrk_dma_kernel(DmaArgs d) {
   const uint16_t* srcj[DMA_PER_PANEL];
   auto sources = [&](int s) {
     const int64_t t0 = tbeg + (int64_t)s * DBK;
-    const uint16_t* base = a.A + min(t0, tend) * a.lda;
-    dma_sources(base, t0, tend, offi, wave, lane, srci);
-    dma_sources(base, t0, tend, offj, wave, lane, srcj);
+    dma_sources(a.A + min(t0, tend) * a.lda, t0, tend, offi, wave, lane, srci);
+    dma_sources(a.B + min(t0, tend) * a.ldb, t0, tend, offj, wave, lane, srcj);
   };
   auto issue = [&](uint16_t* buf) {
     dma_copy(srci, buf, wave);
@@ -582,6 +583,71 @@ int choose_splits(int ntiles, int64_t T) {
 }
 
 }  // namespace
+
+// H's lower block triangle (+)= sum_t A[t, i] B[t, j] (bf16 streams, T tokens, n channels), then
+// optionally the mirror of the lower triangle into the upper one.  B == A is the Hessian
+// A^T A; a second stream B takes the direct-to-LDS kernel, whose 32-bit stage offsets it
+// needs (KQ_ENOTIMPL otherwise).
+kq_status gram_lower(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t T,
+                     int64_t n, float* H, int64_t ldh, bool accumulate, bool mirror, hipStream_t s) {
+  const int ni = (int)n;
+  if (!accumulate) {
+    zero_lower_tiles<<<dim3(ni), dim3(256), 0, s>>>(H, ldh, ni);
+    KQ_LAUNCHED("zero_lower_tiles");
+  }
+  if (T > 0) {
+    SyrkArgs a;
+    a.A = A; a.lda = lda; a.B = B; a.ldb = ldb; a.T = T; a.n = ni; a.H = H; a.ldh = ldh;
+    a.nb = (int)ceil_div(n, TILE);
+    a.ntiles = a.nb * (a.nb + 1) / 2;
+    a.splits = choose_splits(a.ntiles, T);
+    a.tok_split = ceil_div(ceil_div(T, a.splits), BK) * BK;
+    a.splits = (int)ceil_div(T, a.tok_split);
+    // the direct-to-LDS kernel (the default) keeps 32-bit per-lane offsets within a 32-token
+    // stage; larger strides take the register-staged kernel (so may the engine's tests)
+    const bool dma_fits = (int64_t)DBK * std::max(lda, ldb) + n < ((int64_t)1 << 32);
+    int variant = B == A ? (int)testing_value(KQ_TESTING_SYRK_KERNEL, 4) : 4;
+    if (variant < 0 || variant > 4) variant = 4;
+    if (variant == 4 && !dma_fits) {
+      if (B != A) return fail(KQ_ENOTIMPL, "two-stream Gram product: stream stride too large");
+      variant = 3;
+    }
+    if (variant == 4) {
+      DmaArgs d;
+      d.xcds = device_cu_count() % 8 == 0 ? 8 : 1;
+      const int cu_per_xcd = device_cu_count() / d.xcds;
+      d.per_xcd = (int)ceil_div(a.ntiles, d.xcds);
+      a.splits = choose_splits_dma(d.per_xcd, cu_per_xcd, d.xcds, T);
+      a.tok_split = ceil_div(ceil_div(T, a.splits), DBK) * DBK;
+      a.splits = (int)ceil_div(T, a.tok_split);
+      d.s = a;
+      const int64_t g = (int64_t)d.xcds * d.per_xcd * a.splits;
+      if (g > 0x7FFFFFFF) return fail(KQ_ESHAPE, "kq_accumulate_hessian: too many tiles");
+      syrk_dma_kernel<<<dim3((unsigned)g), dim3(DWAVES * 64), 0, s>>>(d);
+      KQ_LAUNCHED("syrk_dma_kernel");
+    } else {
+      const int64_t grid = (int64_t)a.ntiles * a.splits;
+      if (grid > 0x7FFFFFFF) return fail(KQ_ESHAPE, "kq_accumulate_hessian: too many tiles");
+      const bool split_major = (variant & 2) != 0;
+      if (variant & 1) {
+        if (split_major) syrk_bf16_kernel<8, true><<<dim3((unsigned)grid), dim3(512), 0, s>>>(a);
+        else syrk_bf16_kernel<8, false><<<dim3((unsigned)grid), dim3(512), 0, s>>>(a);
+      } else {
+        if (split_major) syrk_bf16_kernel<4, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
+        else syrk_bf16_kernel<4, false><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
+      }
+      KQ_LAUNCHED("syrk_bf16_kernel");
+    }
+  }
+  if (mirror) {
+    const int m = (int)ceil_div(n, 64);
+    const int64_t mt = (int64_t)m * (m + 1) / 2;
+    mirror_lower_to_upper<<<dim3((unsigned)mt), dim3(256), 0, s>>>(H, ldh, ni, m);
+    KQ_LAUNCHED("mirror_lower_to_upper");
+  }
+  return KQ_OK;
+}
+
 }  // namespace kq
 
 extern "C" kq_status kq_accumulate_hessian(const uint16_t* A_bf16, int64_t T, int64_t n,
@@ -601,55 +667,6 @@ extern "C" kq_status kq_accumulate_hessian(const uint16_t* A_bf16, int64_t T, in
     return fail(KQ_EINVAL, "kq_accumulate_hessian: A must be 16-byte aligned");
   if (accumulate != 0 && accumulate != 1)
     return fail(KQ_EINVAL, "kq_accumulate_hessian: accumulate must be 0 or 1");
-  hipStream_t s = as_stream(stream);
-  const int ni = (int)n;
-  if (!accumulate) {
-    zero_lower_tiles<<<dim3(ni), dim3(256), 0, s>>>(H, ldh, ni);
-    KQ_LAUNCHED("zero_lower_tiles");
-  }
-  if (T > 0) {
-    SyrkArgs a;
-    a.A = A_bf16; a.lda = lda; a.T = T; a.n = ni; a.H = H; a.ldh = ldh;
-    a.nb = (int)ceil_div(n, TILE);
-    a.ntiles = a.nb * (a.nb + 1) / 2;
-    a.splits = choose_splits(a.ntiles, T);
-    a.tok_split = ceil_div(ceil_div(T, a.splits), BK) * BK;
-    a.splits = (int)ceil_div(T, a.tok_split);
-    // the direct-to-LDS kernel (the default) keeps 32-bit per-lane offsets within a 32-token
-    // stage; larger strides take the register-staged kernel (so may the engine's tests)
-    int variant = (int)testing_value(KQ_TESTING_SYRK_KERNEL, 4);
-    if (variant < 0 || variant > 4) variant = 4;
-    if (variant == 4 && (int64_t)DBK * lda + n >= ((int64_t)1 << 32)) variant = 3;
-    if (variant == 4) {
-      DmaArgs d;
-      d.xcds = device_cu_count() % 8 == 0 ? 8 : 1;
-      const int cu_per_xcd = device_cu_count() / d.xcds;
-      d.per_xcd = (int)ceil_div(a.ntiles, d.xcds);
-      a.splits = choose_splits_dma(d.per_xcd, cu_per_xcd, d.xcds, T);
-      a.tok_split = ceil_div(ceil_div(T, a.splits), DBK) * DBK;
-      a.splits = (int)ceil_div(T, a.tok_split);
-      d.s = a;
-      const int64_t g = (int64_t)d.xcds * d.per_xcd * a.splits;
-      if (g > 0x7FFFFFFF) return fail(KQ_ESHAPE, "kq_accumulate_hessian: too many tiles");
-      syrk_dma_kernel<<<dim3((unsigned)g), dim3(DWAVES * 64), 0, s>>>(d);
-      KQ_LAUNCHED("syrk_dma_kernel");
-    } else {
-    const int64_t grid = (int64_t)a.ntiles * a.splits;
-    if (grid > 0x7FFFFFFF) return fail(KQ_ESHAPE, "kq_accumulate_hessian: too many tiles");
-    const bool split_major = (variant & 2) != 0;
-    if (variant & 1) {
-      if (split_major) syrk_bf16_kernel<8, true><<<dim3((unsigned)grid), dim3(512), 0, s>>>(a);
-      else syrk_bf16_kernel<8, false><<<dim3((unsigned)grid), dim3(512), 0, s>>>(a);
-    } else {
-      if (split_major) syrk_bf16_kernel<4, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
-      else syrk_bf16_kernel<4, false><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
-    }
-    KQ_LAUNCHED("syrk_bf16_kernel");
-    }
-  }
-  const int m = (int)ceil_div(n, 64);
-  const int64_t mt = (int64_t)m * (m + 1) / 2;
-  mirror_lower_to_upper<<<dim3((unsigned)mt), dim3(256), 0, s>>>(H, ldh, ni, m);
-  KQ_LAUNCHED("mirror_lower_to_upper");
-  return KQ_OK;
+  return gram_lower(A_bf16, lda, A_bf16, lda, T, n, H, ldh, accumulate != 0, true,
+                    as_stream(stream));
 }

@@ -2,10 +2,11 @@
 on the same bf16 streams.
 
 Tolerance: the Hessian factors' 1e-3 relative Frobenius error, on every A_k and B_k (k <= 3).
-The GPU carries the inverse factor U (B^-1 = U^T U) into the per-token quadratic forms, and
-each scaled token row sqrt(w_t c) x_t into the SYRK, as two bf16 terms (about 16
-significant bits, relative error within 2^-17 per entry); the products accumulate in fp32
-and the factorizations run in fp32.  With a single bf16 term the scaled rows alone gave
+The GPU carries the inverse factor U (B^-1 = U^T U) into the per-token quadratic forms as
+two bf16 terms (about 16 significant bits, relative error within 2^-17 per entry), and forms
+each factor one-sided, sum_t a_t x_t^T with the weighted row a_t = w_t c x_t as two bf16
+terms against the exact bf16 stream x_t; the products accumulate in fp32 and the
+factorizations run in fp32.  With the weighted rows rounded to one bf16 term the error was
 2.4e-3 at the first iteration (where U is the identity): a few heavy tokens dominate the
 weighted sums, so their 2^-9 roundings do not average out."""
 import numpy as np
