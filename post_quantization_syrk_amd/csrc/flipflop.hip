@@ -89,8 +89,11 @@ struct QArgs {
   float* part;         // T x np partial sums of squares (np = 2 * ceil(k / 256))
   int np;
   int ntt, njt;        // token tiles, output tiles
-  int per_xcd;         // tiles per XCD
+  int ntt_x;           // token tiles per XCD
+  int per_xcd;         // tiles per XCD: ntt_x * njt
 };
+
+constexpr int QBAND = 8;                // token tiles per band of an XCD's walk
 
 // part[t, 2 jt + wc] = sum over the 128 outputs j of wave column wc of tile jt of
 // (sum_i U[j, i] S[t, i])^2.
@@ -105,13 +108,20 @@ __global__ __launch_bounds__(256) void qform_kernel(QArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t b1[QSTAGE];
   __shared__ __attribute__((aligned(1024))) uint16_t b2[QSTAGE];
   __shared__ __attribute__((aligned(1024))) uint16_t b3[QSTAGE];
-  // workgroup u runs on XCD u mod 8; each XCD takes a contiguous range of tiles in
-  // token-major order, so the 256 x k panel of one token tile stays in that XCD's L2 while
-  // its output tiles pass
+  // workgroup u runs on XCD u mod 8; each XCD takes its own range of ntt_x token tiles, in
+  // bands of QBAND token tiles walked output tile by output tile, so the 32 tiles an XCD
+  // runs at once span 8 token panels and 4 panels of U (rather than 2 and 16) and share
+  // their stage windows in its L2
   const int u = blockIdx.x;
-  const int q = (u & 7) * a.per_xcd + (u >> 3);
-  if (q >= a.ntt * a.njt) return;
-  const int tt = q / a.njt, jt = q % a.njt;
+  const int l = u >> 3;
+  const int band = l / (QBAND * a.njt);
+  const int tb0 = band * QBAND;
+  const int bt = min(QBAND, a.ntt_x - tb0);
+  if (bt <= 0) return;
+  const int w = l - band * QBAND * a.njt;
+  const int jt = w / bt;
+  const int tt = (u & 7) * a.ntt_x + tb0 + w % bt;
+  if (tt >= a.ntt || jt >= a.njt) return;
   const int64_t t0 = (int64_t)tt * QT;
   const int j0 = jt * QT;
   const int i_begin = j0;                       // U[j, i] = 0 for i < j
@@ -390,8 +400,8 @@ kq_status quadratic_forms(const uint16_t* S, int64_t lds, int64_t T, int64_t k, 
   a.njt = (int)((k + QT - 1) / QT);
   a.np = 2 * a.njt;
   a.ntt = (int)((T + QT - 1) / QT);
-  const int64_t tiles = (int64_t)a.ntt * a.njt;
-  a.per_xcd = (int)ceil_div(tiles, 8);
+  a.ntt_x = (int)ceil_div(a.ntt, 8);
+  a.per_xcd = a.ntt_x * a.njt;
   const int64_t grid = 8 * (int64_t)a.per_xcd;
   if (grid > 0x7fffffff) return fail(KQ_ESHAPE, "kq_flipflop: too many tiles");
   qform_kernel<<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
