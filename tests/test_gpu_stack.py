@@ -34,41 +34,62 @@ def _sq_norm(bits: np.ndarray, chunk: int = 8192) -> float:
         return float(np.sum(list(ex.map(part, range(0, bits.shape[0], chunk)))))
 
 
+def _gen(c, which):
+    """One stream of a sublayer and its squared norm (host, fp64)."""
+    bits = syn.stream(c, which)
+    return bits, _sq_norm(bits)
+
+
+def _submit_layer(pool, layer):
+    """Queue a layer's distinct streams: its activation streams (q/k/v share one, gate/up
+    share one) and its seven gradient streams."""
+    cfgs = syn.stack_sublayer_configs(layer)
+    xs = {}
+    for c in cfgs:
+        xs.setdefault(c.x_stream, c)
+    fx = {k: pool.submit(_gen, c, "x") for k, c in xs.items()}
+    fg = [pool.submit(_gen, c, "g") for c in cfgs]
+    return cfgs, fx, fg
+
+
 def test_decoder_stack_allocation_and_sublayers():
+    from concurrent.futures import ThreadPoolExecutor
     torch = torch_cuda()
     import post_quantization_syrk_amd as kq
     t_all = time.time()
     sens_gpu, sens_ref, numel, names = [], [], [], []
-    for layer in range(syn.STACK_LAYERS):
-        cfgs = syn.stack_sublayer_configs(layer)
-        # the four activation streams of the layer (q/k/v share one, gate/up share one)
-        hx, nx = {}, {}
-        for c in cfgs:
-            if c.x_stream in hx:
-                continue
-            bits = syn.stream(c, "x")
-            nx[c.x_stream] = _sq_norm(bits)
-            X = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
-            H = torch.empty((c.inp, c.inp), device="cuda")
-            kq.kq_accumulate_hessian(X, H)
-            hx[c.x_stream] = H
-            del X, bits
-        for c in cfgs:
-            bits = syn.stream(c, "g")
-            ng = _sq_norm(bits)
-            G = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
-            HG = torch.empty((c.out, c.out), device="cuda")
-            kq.kq_accumulate_hessian(G, HG)
-            tx, tg, s = kq.kq_sensitivity(hx[c.x_stream], HG)
-            assert tx == pytest.approx(nx[c.x_stream], rel=1e-5)
-            assert tg == pytest.approx(ng, rel=1e-5)
-            sens_gpu.append(s)
-            sens_ref.append(nx[c.x_stream] * ng)
-            numel.append(c.params)
-            names.append(c.name)
-            del G, HG, bits
-        del hx
-        announce(f"stack layer {layer}: traces done ({time.time() - t_all:.0f} s)")
+    # streams are drawn on the host a layer ahead of the GPU work, four at a time (each
+    # stream's generator is itself threaded over its token chunks)
+    with ThreadPoolExecutor(4) as pool:
+        nxt = _submit_layer(pool, 0)
+        for layer in range(syn.STACK_LAYERS):
+            cfgs, fx, fg = nxt
+            if layer + 1 < syn.STACK_LAYERS:
+                nxt = _submit_layer(pool, layer + 1)
+            hx, nx = {}, {}
+            for k, f in fx.items():
+                bits, nx[k] = f.result()
+                c = next(c for c in cfgs if c.x_stream == k)
+                X = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+                H = torch.empty((c.inp, c.inp), device="cuda")
+                kq.kq_accumulate_hessian(X, H)
+                hx[k] = H
+                del X, bits
+            for c, f in zip(cfgs, fg):
+                bits, ng = f.result()
+                G = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+                HG = torch.empty((c.out, c.out), device="cuda")
+                kq.kq_accumulate_hessian(G, HG)
+                tx, tg, s = kq.kq_sensitivity(hx[c.x_stream], HG)
+                assert tx == pytest.approx(nx[c.x_stream], rel=1e-5)
+                assert tg == pytest.approx(ng, rel=1e-5)
+                sens_gpu.append(s)
+                sens_ref.append(nx[c.x_stream] * ng)
+                numel.append(c.params)
+                names.append(c.name)
+                del G, HG, bits
+            del hx, fx, fg
+            announce(f"stack layer {layer}: traces done ({time.time() - t_all:.0f} s)")
     assert len(sens_gpu) == 224
     bits_ref, margin = o.allocate_bits(sens_ref, numel, (2, 3, 4), 5, 2, report_margin=True)
     bits_lib_shared = kq.kq_allocate_bits(sens_ref, numel, (2, 3, 4), 5, 2)
