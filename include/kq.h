@@ -105,8 +105,8 @@ kq_status kq_accumulate_hessian(const uint16_t* A_bf16, int64_t T, int64_t n, in
 /*
  * kq_sensitivity -- traces and the sensitivity s = tr(H_G) * tr(H_X).
  *
- * Follows: KronQ README, opening section ("inter-layer mixed precision ...
- * guided by tr(H_G) tr(H_X) sensitivity"); KronQ arXiv abstract, point 2.
+ * Follows: KronQ README, opening section (the per-sublayer bit widths are chosen from
+ * the product of the two factors' traces); KronQ arXiv abstract, point 2.
  * Meant for the raw factors (before BiIP).
  *
  *   HX   device fp32, n_in x n_in (leading dim ldx); only the diagonal is read
@@ -138,8 +138,8 @@ kq_status kq_sensitivity_async(const float* HX, int64_t n_in, int64_t ldx, const
 /*
  * kq_biip_rotate -- bidirectional incoherence processing of one layer.
  *
- * Follows: KronQ README, opening section ("incoherence rotation + rescaling on
- * both the input and output sides") and flags table (--incoh_kernel had,
+ * Follows: KronQ README, opening section (the incoherence rotation and the rescale
+ * are applied on the input side and on the output side) and flags table (--incoh_kernel had,
  * --alpha 0.25); KronQ arXiv abstract, point 1.
  * With D_in = diag(d_in), D_out = diag(d_out) and P = blockdiag(Had_b) diag(S) / sqrt(b)
  * (Sylvester Hadamard of order b in natural order, S the +-1 signs):

@@ -80,8 +80,8 @@ def trace(H: np.ndarray) -> float:
 def sensitivity(HX: np.ndarray, HG: np.ndarray) -> tuple[float, float, float]:
     """Per-sublayer sensitivity s = tr(H_G) * tr(H_X).
 
-    [KronQ-README] opening section ("inter-layer mixed precision ... guided by
-    tr(H_G) tr(H_X) sensitivity"); [KronQ-abstract] point (2).  READING: taken
+    [KronQ-README] opening section (bit widths across sublayers are chosen from
+    the product of the two factors' traces); [KronQ-abstract] point (2).  READING: taken
     on the raw factors, before incoherence processing (rotation keeps the
     trace, rescaling does not; the raw value is the layer's own property).
     Returns (tr H_X, tr H_G, product).
@@ -159,8 +159,8 @@ def rescale_vectors(W: np.ndarray, HX: np.ndarray, HG: np.ndarray | None, alpha:
                     ) -> tuple[np.ndarray, np.ndarray]:
     """Diagonal rescale factors of BiIP, input side d_in and output side d_out.
 
-    [KronQ-README] opening section: BiIP applies "rotation + rescaling on both
-    the input and output sides"; the flags table gives alpha = 0.25 for
+    [KronQ-README] opening section: BiIP rotates and rescales on the input side
+    and on the output side; the flags table gives alpha = 0.25 for
     weight-only runs.  The formula is not on the pages.  READING:
         d_in[i]  = (H_X[i,i] / sum_r W[r,i]^2) ** alpha
         d_out[k] = (H_G[k,k] / sum_i W[k,i]^2) ** alpha
@@ -194,7 +194,8 @@ def biip(W: np.ndarray, HX: np.ndarray, HG: np.ndarray | None, sign_in: np.ndarr
     [KronQ-abstract] point (1) and [KronQ-README] opening section: the
     input-side random rotation is extended to the output dimension using the
     gradient covariance; both sides get a randomized Hadamard rotation plus a
-    rescale.  [KronQ-news] "rotation extended to the output side".
+    rescale.  [KronQ-news] also describes the rotation as carried over to the
+    output side.
     READING (order and form):
       1. rescale   W <- D_out W D_in,  H_X <- D_in^-1 H_X D_in^-1,
                    H_G <- D_out^-1 H_G D_out^-1          (rescale_vectors)
@@ -817,8 +818,8 @@ def allocate_bits(sens, numel, allowed=(2, 3, 4), target_num: int = 5, target_de
                   report_margin: bool = False):
     """Per-sublayer bit widths from the tr(H_G) tr(H_X) sensitivities.
 
-    [KronQ-README] opening section and flags table ("inter-layer mixed
-    precision", `--inter_layer_mp`); [KronQ-abstract] point (2).  The rule is
+    [KronQ-README] opening section and flags table (mixed precision across
+    sublayers, `--inter_layer_mp`); [KronQ-abstract] point (2).  The rule is
     not on the pages.  READING: a sublayer's expected loss is modelled as
     s_l * 4^-b_l (uniform-noise model: E tr(H_G dW H_X dW^T) = sigma^2 tr(H_G)
     tr(H_X), sigma^2 ~ 4^-b).  Start every sublayer at the lowest width; while

@@ -1,7 +1,7 @@
 // Inter-layer bit allocation from tr(H_G) * tr(H_X) sensitivities (host code).
 //
-// KronQ README, opening section ("inter-layer mixed precision: per-sublayer
-// bit allocation guided by tr(H_G) tr(H_X) sensitivity") and flags table
+// KronQ README, opening section (the bit width of each sublayer is set from the
+// product of its two factors' traces) and flags table
 // (--inter_layer_mp); KronQ arXiv abstract, point 2.  The pages do not give
 // the rule.  This engine's rule: a sublayer's expected loss behaves like
 // s_l * 4^-b_l (uniform quantization noise of variance ~ 4^-b gives

@@ -1,8 +1,8 @@
 // Bidirectional incoherence processing (BiIP): rescale + randomized Hadamard
 // rotation of W, H_X and H_G on the input and the output side.
 //
-// KronQ README, opening section: "incoherence rotation + rescaling on both the
-// input and output sides"; flags table: --incoh_kernel had, --alpha 0.25;
+// KronQ README, opening section: the incoherence rotation and the rescale act on the
+// input side and on the output side; flags table: --incoh_kernel had, --alpha 0.25;
 // KronQ arXiv abstract, point 1: the input-side random rotation is extended
 // to the output dimension using the gradient covariance.
 //

@@ -1,8 +1,8 @@
 // Trace reductions and the per-sublayer sensitivity tr(H_G) * tr(H_X).
 //
 // KronQ README, opening section: inter-layer mixed precision is guided by the
-// tr(H_G) tr(H_X) sensitivity; KronQ arXiv abstract, point 2: the metric is
-// driven by the gradient and activation Hessian traces.
+// tr(H_G) tr(H_X) sensitivity; KronQ arXiv abstract, point 2: the metric comes from
+// the traces of the gradient and the activation factor.
 #include "kq_internal.h"
 
 #include <mutex>

@@ -366,8 +366,8 @@ def test_dead_channel_rule():
 
 # ---------------------------------------------------------------------------
 # Damping: lambda = damp * mean(diag H~_X) on the processed factor, after a dead channel's
-# diagonal is set to 1 (the single-layer workload's "damping 1% of mean diag(H_X)", read as
-# GPTQ's relative damping of the factor it factors)
+# diagonal is set to 1 (the single-layer workload's damping of one percent of the mean
+# diagonal, read as GPTQ's relative damping of the factor it factors)
 # ---------------------------------------------------------------------------
 def test_damping_hand_example_with_dead_channel():
     """H = diag(4, 0, 8, 12), damp 0.01.  The dead channel counts as 1, so the mean diagonal
