@@ -8,17 +8,21 @@
 // i' >= i and r' >= r, so a coordinate depends only on those above and to its left, and all
 // coordinates of one anti-diagonal r + i can be rounded together.
 //
-// Schedule: 32 x 32 tiles and, per anti-diagonal of tiles, three launches.  F = E U_X (E
-// the scaled errors, zero until a tile has run) collects each finished tile's errors
-// pushed to the right.  For every tile (R, I) of the diagonal:
+// Schedule: 32 x 32 tiles and, per anti-diagonal of tiles, two launches.  F = E U_X (E the
+// scaled errors, zero until a tile has run) collects each finished tile's errors pushed to
+// the right.  For every tile (R, I) of the diagonal:
 //   1. pull: the pending feedback sum_{R'' <= R} U_G[R'', R]^T F[R'', I] (every tile above
 //      or to the left is done), split over slices of 256 contraction indices, one workgroup
 //      each (fp32 MFMA), partial sums kept per slice and added in a fixed order;
 //   2. round: one workgroup per tile rounds its 63 anti-diagonals; each step's errors e_k
 //      (one per row) feed the whole tile through U_G[k, r'] U_X[d - k, i'], a 32 x 32 x 32
 //      product of which each wave forms and applies one 16 x 16 quadrant (LDS float atomics,
-//      or partials summed across waves, cost several times the whole loop here);
-//   3. push: F[R, I..] += E_tile U_X[I, I..], split over chunks of 256 columns (fp32 MFMA).
+//      or partials summed across waves, cost several times the whole loop here).  The
+//      workgroup then pushes its errors into its own and the next column block,
+//      F[R, I..I+1] += E_tile U_X[I, I..I+1], with operands loaded before the rounding;
+//   3. push: the rest, F[R, I+2..] += E_tile U_X[I, I+2..], split over chunks of 256
+//      columns (fp32 MFMA).  Nothing before diagonal d + 2 reads those columns, so these
+//      workgroups share a launch with the pull of the next diagonal.
 // Pulls cost O(m^2 n) and pushes O(m n^2) in all, as in the BaKron bound.
 //
 // Grids: per (row, group) asymmetric min-max from W~ before rounding (a static grid; every
@@ -64,9 +68,8 @@ __device__ __forceinline__ int acc_row(int r, int kh) { return 8 * (r >> 2) + 4 
 // 1. pull, slice s of tile (R, I): sum over k in [s KS, min(32 (R + 1), (s + 1) KS)) of
 //    U_G[k][r0 + r'] F[k][c0 + i'].  The four waves take interleaved k pairs, 16 pairs' loads
 //    in flight before their products.
-__global__ __launch_bounds__(256) void ts_pull_kernel(TSArgs a) {
-  __shared__ float red[4][TS * TS];
-  const int tix = blockIdx.x / a.nslice, sl = blockIdx.x % a.nslice;
+__device__ __forceinline__ void ts_pull(const TSArgs& a, int b, float (*red)[TS * TS]) {
+  const int tix = b / a.nslice, sl = b % a.nslice;
   const int R = a.r_lo + tix, I = a.d - R;
   const int r0 = TS * R, c0 = TS * I;
   const int K = r0 + TS, kb = sl * KS, ke = min(K, kb + KS);
@@ -97,9 +100,9 @@ __global__ __launch_bounds__(256) void ts_pull_kernel(TSArgs a) {
 }
 
 // 2. round tile (R, I): W~ (dead rows / columns zero) minus the pulled feedback, then the
-//    tile's own anti-diagonals.
+//    tile's own anti-diagonals; then its errors pushed into its own and the next column block.
 __global__ __launch_bounds__(256) void ts_round_kernel(TSArgs a) {
-  __shared__ float wt[TS][TS + 1];    // the tile's weights, updated
+  __shared__ float wt[TS][TS + 1];    // the tile's weights minus the pulled feedback
   __shared__ float ugd[TS][TS + 1];   // U_G diagonal block [k][r']
   __shared__ float uxd[TS][TS + 1];   // U_X diagonal block [i][i']
   __shared__ float et[TS][TS + 1];    // scaled errors
@@ -159,6 +162,18 @@ __global__ __launch_bounds__(256) void ts_round_kernel(TSArgs a) {
   }
   __syncthreads();
 
+  // operands of the near push (F[R, I..I+1] and U_X[I, I+1]), loaded now so that their
+  // latency passes under the rounding: no other workgroup of this launch writes them
+  const bool near = wave == 0 || (wave == 1 && c0 + TS < a.n);
+  const int cbn = c0 + TS * (wave & 1);
+  float nbv[16], nfo[16];
+  if (near) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) nbv[j] = a.UX[(int64_t)(c0 + 2 * j + kh) * n + cbn + l32];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) nfo[r] = a.F[(int64_t)(r0 + acc_row(r, kh)) * n + cbn + l32];
+  }
+
   // Wave w owns the 16 x 16 quadrant (rows 16 (w >> 1), columns 16 (w & 1)) of each step's
   // feedback Delta[r'][i'] = sum_k U_G[k][r'] e_k U_X[dd - k][i'] (v_mfma_f32_16x16x4f32, k in
   // fours): A[r'][kk] = U_G[k][r'] is fixed, B[kk][i'] = e_k U_X[dd - k][i'].
@@ -199,6 +214,16 @@ __global__ __launch_bounds__(256) void ts_round_kernel(TSArgs a) {
     }
     __syncthreads();
   }
+  // near push: F[R, I] += E_tile U_X[I, I] (wave 0) and F[R, I + 1] += E_tile U_X[I, I + 1]
+  // (wave 1), the products in the order the far push takes for the other blocks
+  if (near) {
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(et[l32][2 * j + kh], nbv[j], acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) a.F[(int64_t)(r0 + acc_row(r, kh)) * n + cbn + l32] = nfo[r] + acc[r];
+  }
   // errors and codes out once the tile is done (a global store inside the loop would make
   // every barrier wait for it)
   for (int e = t; e < TS * TS; e += 256) {
@@ -208,13 +233,13 @@ __global__ __launch_bounds__(256) void ts_round_kernel(TSArgs a) {
   }
 }
 
-// 3. push, chunk c of tile (R, I): F[r0 + r][col] += sum_k E[r0 + r][c0 + k] U_X[c0 + k][col]
-//    for the chunk's columns (at or right of c0), 32 per wave block.
-__global__ __launch_bounds__(256) void ts_push_kernel(TSArgs a, int nchunk) {
-  const int tix = blockIdx.x / nchunk, ch = blockIdx.x % nchunk;
+// 3. far push, chunk c of tile (R, I): F[r0 + r][col] += sum_k E[r0 + r][c0 + k] U_X[c0 + k][col]
+//    for the chunk's columns (at or right of c0 + 64), 32 per wave block.
+__device__ __forceinline__ void ts_push_far(const TSArgs& a, int b, int nchunk) {
+  const int tix = b / nchunk, ch = b % nchunk;
   const int R = a.r_lo + tix, I = a.d - R;
   const int r0 = TS * R, c0 = TS * I;
-  const int cb0 = c0 + ch * PS;
+  const int cb0 = c0 + 2 * TS + ch * PS;
   if (cb0 >= a.n) return;
   const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, kh = lane >> 5;
   const int wave = t >> 6;
@@ -223,8 +248,8 @@ __global__ __launch_bounds__(256) void ts_push_kernel(TSArgs a, int nchunk) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) eop[j] = a.E[(int64_t)(r0 + l32) * n + c0 + 2 * j + kh];
   const int nblk = min(PS, a.n - cb0) / TS;
-  for (int b = wave; b < nblk; b += 4) {
-    const int cb = cb0 + TS * b;
+  for (int blk = wave; blk < nblk; blk += 4) {
+    const int cb = cb0 + TS * blk;
     float bv[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) bv[j] = a.UX[(int64_t)(c0 + 2 * j + kh) * n + cb + l32];
@@ -237,6 +262,16 @@ __global__ __launch_bounds__(256) void ts_push_kernel(TSArgs a, int nchunk) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) a.F[(int64_t)(r0 + acc_row(r, kh)) * n + cb + l32] = fo[r] + acc[r];
   }
+}
+
+// One launch: the pull workgroups of diagonal d + 1 (ap, npull of them) and the far-push
+// workgroups of diagonal d (aq, nchunk per tile).  The two sets touch disjoint data: the pull
+// reads F's column blocks I of its tiles, which the far push of diagonal d does not write.
+__global__ __launch_bounds__(256) void ts_pull_push_kernel(TSArgs ap, int npull, TSArgs aq, int nchunk) {
+  __shared__ float red[4][TS * TS];
+  const int b = blockIdx.x;
+  if (b < npull) ts_pull(ap, b, red);
+  else ts_push_far(aq, b - npull, nchunk);
 }
 
 // Static grid per (row, group) from W~ with dead rows and columns zeroed: one wave each.
@@ -383,21 +418,37 @@ extern "C" kq_status kq_quantize_two_sided(const kq_quant_params* p, const float
   a.W = W; a.UX = w.UX; a.UG = w.UG; a.scale = scales; a.zero = zeros;
   a.deadX = w.deadX; a.deadG = w.deadG; a.F = w.F; a.E = w.E; a.part = w.part; a.codes = codes;
   a.m = (int)m; a.n = (int)n; a.ng = (int)(n / p->group); a.group = p->group; a.maxq = maxq;
-  const int NR = (int)(m / TS), NI = (int)(n / TS);
-  for (int d = 0; d < NR + NI - 1; ++d) {
-    a.d = d;
-    a.r_lo = std::max(0, d - (NI - 1));
+  const int NR = (int)(m / TS), NI = (int)(n / TS), ND = NR + NI - 1;
+  // the tiles of diagonal d: rows r_lo .. r_hi; the lowest one pulls the most slices
+  auto diagonal = [&](int d, TSArgs& x) {
+    x = a;
+    x.d = d;
+    x.r_lo = std::max(0, d - (NI - 1));
     const int r_hi = std::min(d, NR - 1);
-    const int tiles = r_hi - a.r_lo + 1;
-    a.nslice = (TS * (r_hi + 1) + KS - 1) / KS;           // the lowest tile pulls the most
-    ts_pull_kernel<<<dim3((unsigned)(tiles * a.nslice)), dim3(256), 0, s>>>(a);
-    KQ_LAUNCHED("ts_pull_kernel");
-    ts_round_kernel<<<dim3((unsigned)tiles), dim3(256), 0, s>>>(a);
+    x.nslice = (TS * (r_hi + 1) + KS - 1) / KS;
+    return r_hi - x.r_lo + 1;
+  };
+  TSArgs ap;
+  const int t0 = diagonal(0, ap);
+  ts_pull_push_kernel<<<dim3((unsigned)(t0 * ap.nslice)), dim3(256), 0, s>>>(ap, t0 * ap.nslice, ap, 0);
+  KQ_LAUNCHED("ts_pull_push_kernel");
+  for (int d = 0; d < ND; ++d) {
+    TSArgs ar;
+    const int tiles = diagonal(d, ar);
+    ts_round_kernel<<<dim3((unsigned)tiles), dim3(256), 0, s>>>(ar);
     KQ_LAUNCHED("ts_round_kernel");
-    const int I_lo = d - r_hi;                              // the leftmost tile pushes the most
-    const int nchunk = (int)ceil_div(n - (int64_t)TS * I_lo, PS);
-    ts_push_kernel<<<dim3((unsigned)(tiles * nchunk)), dim3(256), 0, s>>>(a, nchunk);
-    KQ_LAUNCHED("ts_push_kernel");
+    // the pulls of diagonal d + 1 and the far pushes of diagonal d in one launch; the
+    // leftmost tile of d pushes the most columns
+    TSArgs an = ar;
+    const int npull = d + 1 < ND ? diagonal(d + 1, an) * an.nslice : 0;
+    const int I_lo = d - (ar.r_lo + tiles - 1);
+    const int64_t far_cols = n - (int64_t)TS * (I_lo + 2);
+    const int nchunk = far_cols > 0 ? (int)ceil_div(far_cols, PS) : 0;
+    const int64_t total = (int64_t)npull + (int64_t)tiles * nchunk;
+    if (total > 0) {
+      ts_pull_push_kernel<<<dim3((unsigned)total), dim3(256), 0, s>>>(an, npull, ar, nchunk);
+      KQ_LAUNCHED("ts_pull_push_kernel");
+    }
   }
   const int64_t words = m * (n * p->bits / 32);
   ts_pack_kernel<<<dim3((unsigned)ceil_div(words, 256)), dim3(256), 0, s>>>(codes, m, n, p->bits, packed);

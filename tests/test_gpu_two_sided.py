@@ -57,6 +57,7 @@ def _check(gpu, ref, bits):
     (128, 128, 3, 64, 0.01),    # 4 x 4 tiles, 3-bit codes across word boundaries
     (256, 128, 2, 128, 0.02),   # more rows than columns
     (128, 256, 4, 32, 0.01),    # more columns; a group per tile
+    (384, 384, 3, 64, 0.01),    # pulls over two slices, far pushes over two chunks
 ])
 def test_two_sided_matches_oracle(m, n, bits, group, damp):
     torch = torch_cuda()
