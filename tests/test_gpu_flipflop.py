@@ -31,7 +31,7 @@ def _gpu(torch, Xb, Gb, iters):
     return A.cpu().numpy().astype(np.float64), B.cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("T,n,m", [(1000, 256, 384), (3000, 384, 128)])
+@pytest.mark.parametrize("T,n,m", [(1000, 256, 384), (3000, 384, 128), (480, 256, 128)])
 def test_flipflop_matches_oracle(T, n, m):
     torch = torch_cuda()
     announce(f"flipflop T={T} n={n} m={m}")

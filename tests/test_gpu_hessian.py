@@ -68,6 +68,24 @@ def test_kernel_variants_agree(variant, T, n, lda):
     assert np.array_equal(H, H.T)
 
 
+@pytest.mark.parametrize("T,n,lda", [(200, 600, 600), (100, 257, 264), (480, 1024, 1032)])
+def test_single_token_split_several_tiles(T, n, lda):
+    """Fewer than 512 tokens make one token split over several (ragged) tiles; H starts as
+    NaN, so an entry left unwritten fails.  A second chunk is then accumulated on top."""
+    announce(f"hessian single split T={T} n={n} lda={lda}")
+    rng = np.random.default_rng(T * n)
+    x = (rng.standard_normal((2 * T, n)) * np.exp(rng.standard_normal(n))).astype(np.float32)
+    bits = syn.f32_to_bf16_bits(x)
+    H = gpu_hessian(bits[:T], lda)
+    ref = o.hessian_factor(o.bf16_bits_to_f64(bits[:T]))
+    assert rel_fro(H, ref) <= 1e-5
+    assert np.array_equal(H, H.T)
+    H2 = gpu_hessian(bits[T:], lda, accumulate_from=H)
+    ref2 = o.hessian_factor(o.bf16_bits_to_f64(bits))
+    assert rel_fro(H2, ref2) <= 1e-5
+    assert np.array_equal(H2, H2.T)
+
+
 def test_empty_stream_gives_zero_and_accumulate_keeps():
     torch = torch_cuda()
     import post_quantization_syrk_amd as kq
