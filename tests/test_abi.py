@@ -187,3 +187,23 @@ def test_testing_selector_rejects_bad_arguments():
     with kq.testing_select(kq.KQ_TESTING_ROW_LDS_BYTES, 0):
         pass
     assert lib.kq_testing_select(kq.KQ_TESTING_ROW_LDS_BYTES, -1) == kq.KQ_OK
+
+
+def test_async_and_noalloc_quantizers_reject_bad_arguments_on_host():
+    """The asynchronous quantizer needs a device status word; the allocation-free one refuses a
+    layer whose workspace exceeds its fixed array before any device call."""
+    lib = _raw()
+    buf = ctypes.c_void_p(0x1000)
+    p = kq.make_params(2, 128, 128, 0.01)
+    need = kq.kq_quantize_layer_workspace(p, 256, 256, False)
+    args = (ctypes.byref(p), buf, buf, None, 256, 256, buf, buf, buf, None, None)
+    assert lib.kq_quantize_layer_async(*args, None, buf, need, None) == kq.KQ_EINVAL
+    assert b"status" in lib.kq_last_error()
+    assert lib.kq_quantize_layer_async(*args, buf, buf, need - 1, None) == kq.KQ_EWORKSPACE
+    bad = kq.make_params(5, 128, 128, 0.01)
+    assert lib.kq_quantize_layer_async(ctypes.byref(bad), *args[1:], buf, buf, need, None) == kq.KQ_EINVAL
+    # 4096 x 8192 needs far more than the fixed 64 MiB
+    assert lib.kq_quantize_layer_noalloc(ctypes.byref(p), buf, buf, None, 4096, 8192, buf, buf, buf,
+                                         None, None, None) == kq.KQ_EWORKSPACE
+    assert lib.kq_quantize_layer_noalloc(ctypes.byref(bad), buf, buf, None, 256, 256, buf, buf, buf,
+                                         None, None, None) == kq.KQ_EINVAL
