@@ -32,6 +32,7 @@
 // basis), so the factor kept for block J is P[<J, J] = R[<J, J] U_JJ: for 64-column blocks
 // exactly Z; for 128-column blocks [Z_a, Z_b - Z_a Z_b[a rows]], the second half coupled
 // through U_ab = -U_a Z_b[a rows].
+#include "device_util.h"
 #include "kq_internal.h"
 
 #include <algorithm>
@@ -260,27 +261,6 @@ __device__ __forceinline__ void leaf_inverse(const float* Rl, const float* rsq, 
 __device__ __forceinline__ int sw(int r, int k) { return r * 64 + (k ^ ((2 * r) & 62)); }
 // A 64 x 64 matrix read with lanes along columns (B operand): odd rows shifted by 32 columns.
 __device__ __forceinline__ int swb(int k, int c) { return k * 64 + (c ^ ((k & 1) << 5)); }
-
-// Raw buffer access with per-lane masking: a lane whose byte offset is OOB (at or past the
-// descriptor's record count) reads 0 and its store is dropped, so the masked loads and stores
-// of a tile's edge need no branches (a branch per access would make each one wait for every
-// earlier memory operation).  0x00020000 is the descriptor's data-format word on gfx9.
-constexpr int OOB = 0x7ffffff0;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const float* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, OOB, 0x00020000);
-}
-__device__ __forceinline__ float4 bload4(__amdgpu_buffer_rsrc_t r, int off) {
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
-                     __uint_as_float(v.w));
-}
-__device__ __forceinline__ float bload(__amdgpu_buffer_rsrc_t r, int off) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-__device__ __forceinline__ void bstore(float v, __amdgpu_buffer_rsrc_t r, int off) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
-}
 
 // LDS for a leaf: X (64 x LB: A', the factor's scratch, then U) and Y (64 x LB for R, 64 for
 // 1 / R_jj, 32 x LB scratch).

@@ -17,6 +17,7 @@
 //     block).  The kernel boundary orders the two: no device-wide fence inside a kernel, which
 //     on this chip writes back and invalidates the whole L2 of the workgroup's XCD.
 // At full rate the layer is HBM-bound: out * in * bits / 8 bytes of packed words per call.
+#include "device_util.h"
 #include "kq_internal.h"
 
 #include <math.h>
@@ -65,16 +66,6 @@ __device__ __forceinline__ int layer_of(const GroupArgs& a, int wg, bool outrot)
   for (int k = 1; k < a.nl; ++k)
     if (wg >= (outrot ? a.L[k].sg0 : a.L[k].wg0)) l = k;
   return l;
-}
-
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor over `bytes` bytes at base: loads at or past the end read 0, so that
-// masked lanes need no branch (a branch around a load makes the compiler wait for every
-// load in flight where the paths join).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
-  // 0x00020000: the descriptor's data-format word on gfx9
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
 // LDS index of entry i: 16 floats of padding after every 256 entries, so that the strided

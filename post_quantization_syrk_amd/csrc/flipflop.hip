@@ -32,6 +32,7 @@
 // ring of four stages, operands read with ds_read_b128 (8 consecutive contraction indices of
 // one row per lane, as the MFMA takes them); the 16-byte chunks of row r sit in slot
 // c ^ ((r >> 2) & 3), which spreads the rows read together over the banks.
+#include "device_util.h"
 #include "kq_internal.h"
 
 #include <math.h>
@@ -55,17 +56,6 @@ constexpr int QPANEL = QT * QK;         // bf16 elements of one panel (16 KB)
 constexpr int QSTAGE = 2 * QPANEL;      // both panels of a stage (32 KB)
 constexpr int QNST = 4;                 // stages in the ring (128 KB)
 constexpr int QCOPIES = QPANEL * 2 / 1024 / 4;   // 1 KB wave copies per panel and wave (4)
-
-// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
-constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
 
 __device__ __forceinline__ unsigned short bf16_rne(float x) {
   unsigned u = __float_as_uint(x);
@@ -287,7 +277,6 @@ __global__ __launch_bounds__(256) void ff_scale_kernel(const uint16_t* __restric
   }
   __syncthreads();
   const float f = sf;
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   for (int i = 8 * threadIdx.x; i < k; i += 8 * 256) {
     const u32x4 v = *(const u32x4*)(S + t * lds + i);
     u32x4 oh, ol;

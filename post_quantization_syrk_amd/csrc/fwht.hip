@@ -24,6 +24,7 @@
 // Column pass: a tile of R = 2^mb rows (stride 2^k0) x 64 columns; each
 // thread holds 4 columns x R/16 rows, butterflies the register bits, then
 // one LDS transpose brings the remaining row bits into registers.
+#include "device_util.h"
 #include "kq_internal.h"
 
 #include <math.h>
@@ -40,14 +41,6 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
-}
-
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int OOB = 0x7ffffff0;   // buffer offsets at or past this read 0 / drop the store
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
-  // 0x00020000: the descriptor's data-format word on gfx9
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, OOB, 0x00020000);
 }
 
 // Both squared-norm vectors of W from one read of it.  A workgroup takes NR_ROWS whole rows;

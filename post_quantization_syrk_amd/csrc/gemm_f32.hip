@@ -7,6 +7,7 @@
 // floats.  Optional split-K (fp32 atomics into C, or one partial product per split
 // stored to its own slice), upper-triangle-only tile sets, and a reduction epilogue
 // sum(alpha * AB .* D) into an fp64 accumulator.
+#include "device_util.h"
 #include "kq_internal.h"
 
 #include <stdlib.h>
@@ -302,18 +303,6 @@ struct DArgs {
   int64_t partial_stride;
 };
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
-constexpr int gwait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-constexpr int GWAIT_LGKM0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
-
-__device__ __forceinline__ void gbarrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 __device__ __forceinline__ void gcopy(const float* src, float* dst) {
   __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst,
                                    16, 0, 0);
@@ -420,11 +409,11 @@ __global__ __launch_bounds__(THREADS) void gemm_nn_dma_kernel(DArgs a) {
   issue(1, r1);
   issue(2, r2);
   issue(3, r3);
-  __builtin_amdgcn_s_waitcnt(gwait_vm(16));   // stages 0 and 1 of this wave
-  gbarrier();
+  __builtin_amdgcn_s_waitcnt(wait_vm(16));   // stages 0 and 1 of this wave
+  lds_barrier();
   read(r0, xa, xb);
-  __builtin_amdgcn_s_waitcnt(GWAIT_LGKM0);
-  gbarrier();
+  __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+  lds_barrier();
 
   // Step s (operands of stage s in registers, stage s+1 visible): refill stage s's buffer
   // with stage s + 4, multiply stage s while reading stage s+1, wait for this wave's copies of
@@ -441,9 +430,9 @@ __global__ __launch_bounds__(THREADS) void gemm_nn_dma_kernel(DArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           \
     }                                                              \
     __builtin_amdgcn_sched_barrier(0);                             \
-    __builtin_amdgcn_s_waitcnt(gwait_vm(16));                      \
-    __builtin_amdgcn_s_waitcnt(GWAIT_LGKM0);                       \
-    gbarrier();                                                    \
+    __builtin_amdgcn_s_waitcnt(wait_vm(16));                      \
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);                       \
+    lds_barrier();                                                    \
   }
   for (int s0 = 0; s0 < nfull; s0 += DRING) {
     KQ_G_STEP(0, r0, r1, xa, xb, ya, yb)
@@ -459,7 +448,7 @@ __global__ __launch_bounds__(THREADS) void gemm_nn_dma_kernel(DArgs a) {
     if (nst > s0 + 2) KQ_G_STEP(2, r2, r3, xa, xb, ya, yb)
   }
 #undef KQ_G_STEP
-  __builtin_amdgcn_s_waitcnt(gwait_vm(0));
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
 
   const int kh = h, rh = kh * 4;
   if (a.partial_stride > 0) {

@@ -20,6 +20,7 @@
 //     q = clamp(rint(w/s) + z), e_j = (w_j - s (q - z)) / U_jj, w_k -= e_j U_jk (k in J)
 //   the codes are packed into the output words in the same kernel; e_j replaces W0_j and
 //   W0_j - s (q - z) goes to D.
+#include "device_util.h"
 #include "kq_internal.h"
 
 #include <mutex>
@@ -39,19 +40,6 @@ constexpr int LPR = 16;             // lanes per matrix row in the column kernel
 constexpr int CTHREADS = 256;       // threads per workgroup in the column kernel
 constexpr int RPW = CTHREADS / LPR; // matrix rows per workgroup
 constexpr int YSLOTS = 8;           // most K splits of the feedback product
-
-// Raw buffer loads with per-lane masking: a byte offset at or past OOB reads 0 (no branch).
-// 0x00020000 is the descriptor's data-format word on gfx9.
-constexpr int OOB = 0x7ffffff0;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const float* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, OOB, 0x00020000);
-}
-__device__ __forceinline__ float4 bload4(__amdgpu_buffer_rsrc_t r, int off) {
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
-                     __uint_as_float(v.w));
-}
 
 // Slices of the feedback product's workspace: enough K splits to give every CU of a 256-CU
 // device one 128-row tile, at most YSLOTS.

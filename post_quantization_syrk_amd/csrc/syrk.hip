@@ -32,6 +32,7 @@
 // tokens x 4 channels per thread, transposed in registers and stored channel-major into two
 // LDS buffers with an XOR-permuted chunk layout; 4 or 8 waves; split-major or tile-major
 // order.  It serves strides too large for the direct kernel's 32-bit per-stage offsets.
+#include "device_util.h"
 #include "kq_internal.h"
 
 namespace kq {
@@ -290,19 +291,6 @@ constexpr int DWAVES = 4;
 constexpr int DMA_PER_PANEL = DPANEL * 2 / 1024 / DWAVES;   // 1 KB wave instructions per wave
 
 __device__ __forceinline__ int dswz(int e) { return (0xC6A0 >> (4 * e)) & 15; }
-
-// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
-constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-constexpr int WAIT_LGKM0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
-
-// Workgroup barrier for LDS hand-off; also a hard boundary for the instruction scheduler.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
 
 // Sixteen zero bytes in device memory: the source of every copy lane whose token lies outside
 // the split, so that each wave issues the same number of copies in every stage and the
