@@ -6,7 +6,9 @@
 // through LDS stored k-major so every MFMA operand read is 32 consecutive
 // floats.  Optional split-K (fp32 atomics into C, or one partial product per split
 // stored to its own slice), upper-triangle-only tile sets, and a reduction epilogue
-// sum(alpha * AB .* D) into an fp64 accumulator.
+// sum(alpha * AB .* D) into an fp64 accumulator.  The direct-to-LDS kernel for plain
+// row-major products hands each XCD a contiguous run of tiles in groups of four tile
+// columns, so the workgroups that share an L2 also share their operand panels.
 #include "device_util.h"
 #include "kq_internal.h"
 
@@ -301,7 +303,47 @@ struct DArgs {
   int upper_only;     // only tiles with tile row <= tile column
   int64_t k_per_split;
   int64_t partial_stride;
+  int tm, tn, gn;      // tile rows, tile columns, tile columns per group
+  int xcds;
+  int64_t per_split, total, per_xcd;
 };
+
+// Tile o of one split's list.  Tiles come in groups of gn tile columns; inside a group, tile
+// rows in order with the group's columns adjacent, so the workgroups an XCD runs at once cover
+// a compact block of C and share their A and B panels in its L2.  Upper sets (tile row <= tile
+// column, tm >= tn) keep in each group the rows up to the group's last column.
+__device__ __forceinline__ void dma_tile(const DArgs& a, int64_t o, int& ti, int& tj) {
+  if (!a.upper_only) {
+    const int64_t gsz = (int64_t)a.gn * a.tm;
+    const int g = (int)(o / gsz);
+    const int c0 = g * a.gn, w = min(a.gn, a.tn - c0);
+    const int r = (int)(o - g * gsz);
+    ti = r / w;
+    tj = c0 + r % w;
+    return;
+  }
+  int64_t base = 0;
+  for (int g = 0;; ++g) {
+    const int c0 = g * a.gn, w = min(a.gn, a.tn - c0);
+    const int64_t full = (int64_t)w * (c0 + 1);
+    const int64_t cnt = full + w * (w - 1) / 2;
+    if (o < base + cnt) {
+      int r = (int)(o - base);
+      if (r < full) {
+        ti = r / w;
+        tj = c0 + r % w;
+      } else {
+        r -= (int)full;
+        int k = 1;
+        while (r >= w - k) { r -= w - k; ++k; }
+        ti = c0 + k;
+        tj = c0 + k + r;
+      }
+      return;
+    }
+    base += cnt;
+  }
+}
 
 __device__ __forceinline__ void gcopy(const float* src, float* dst) {
   __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst,
@@ -313,9 +355,15 @@ __global__ __launch_bounds__(THREADS) void gemm_nn_dma_kernel(DArgs a) {
   __shared__ __attribute__((aligned(1024))) float r1[DSTG];
   __shared__ __attribute__((aligned(1024))) float r2[DSTG];
   __shared__ __attribute__((aligned(1024))) float r3[DSTG];
-  if (a.upper_only && blockIdx.x > blockIdx.y) return;
-  const int64_t m0 = (int64_t)blockIdx.x * MT, n0 = (int64_t)blockIdx.y * NTL;
-  const int64_t kbeg = (int64_t)blockIdx.z * a.k_per_split;
+  // workgroup u runs on XCD u mod xcds, which takes the items xcd * per_xcd .. + per_xcd - 1
+  const int64_t u = blockIdx.x;
+  const int64_t item = (u % a.xcds) * a.per_xcd + u / a.xcds;
+  if (item >= a.total) return;
+  const int split = (int)(item / a.per_split);
+  int ti, tj;
+  dma_tile(a, item - split * a.per_split, ti, tj);
+  const int64_t m0 = (int64_t)ti * MT, n0 = (int64_t)tj * NTL;
+  const int64_t kbeg = (int64_t)split * a.k_per_split;
   const int64_t kend = min(a.K, kbeg + a.k_per_split);
   if (kbeg >= kend) return;
   const int nst = (int)((kend - kbeg + DBK - 1) / DBK);   // stages of this split
@@ -452,7 +500,7 @@ __global__ __launch_bounds__(THREADS) void gemm_nn_dma_kernel(DArgs a) {
 
   const int kh = h, rh = kh * 4;
   if (a.partial_stride > 0) {
-    float* Cp = a.C + (int64_t)blockIdx.z * a.partial_stride;
+    float* Cp = a.C + (int64_t)split * a.partial_stride;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -528,8 +576,10 @@ kq_status gemm_f32(const GemmArgs& g, hipStream_t s) {
   // plain row-major products with 16-byte aligned rows take the direct-to-LDS kernel
   const bool aligned = ((uintptr_t)g.A % 16 == 0) && ((uintptr_t)g.B % 16 == 0) &&
                        g.lda % 4 == 0 && g.ldb % 4 == 0 && g.K % 4 == 0 && g.N % 4 == 0;
+  // (upper tile sets there need at least as many tile rows as tile columns)
   if (!g.transA && !g.transB && !g.a_upper && !g.b_upper && !g.red &&
-      (g.batch <= 1) && aligned && g.K > 0 && 128 * g.lda + (int64_t)DBK * g.ldb < ((int64_t)1 << 32)) {
+      (g.batch <= 1) && aligned && g.K > 0 && 128 * g.lda + (int64_t)DBK * g.ldb < ((int64_t)1 << 32) &&
+      (!g.upper_only || g.M >= g.N)) {
     DArgs d;
     d.M = g.M; d.N = g.N; d.K = g.K;
     d.A = g.A; d.lda = g.lda; d.B = g.B; d.ldb = g.ldb; d.C = g.C; d.ldc = g.ldc;
@@ -538,8 +588,15 @@ kq_status gemm_f32(const GemmArgs& g, hipStream_t s) {
     d.split_k = (int)ceil_div(g.K, d.k_per_split);
     d.partial_stride = g.partial_stride;
     if (g.splits_used) *g.splits_used = d.split_k;
-    dim3 grid((unsigned)ceil_div(g.M, MT), (unsigned)ceil_div(g.N, NTL), (unsigned)d.split_k);
-    gemm_nn_dma_kernel<<<grid, dim3(THREADS), 0, s>>>(d);
+    d.tm = (int)ceil_div(g.M, MT);
+    d.tn = (int)ceil_div(g.N, NTL);
+    d.gn = 4;
+    d.per_split = g.upper_only ? (int64_t)d.tn * (d.tn + 1) / 2 : (int64_t)d.tm * d.tn;
+    d.total = d.per_split * d.split_k;
+    d.xcds = device_cu_count() % 8 == 0 ? 8 : 1;
+    d.per_xcd = ceil_div(d.total, d.xcds);
+    if (d.per_xcd * d.xcds > 0x7fffffff) return fail(KQ_ESHAPE, "gemm_f32: too many tiles");
+    gemm_nn_dma_kernel<<<dim3((unsigned)(d.per_xcd * d.xcds)), dim3(THREADS), 0, s>>>(d);
     KQ_LAUNCHED("gemm_nn_dma_kernel");
     return KQ_OK;
   }
