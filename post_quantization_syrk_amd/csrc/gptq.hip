@@ -41,13 +41,29 @@ constexpr int CTHREADS = 256;       // threads per workgroup in the column kerne
 constexpr int RPW = CTHREADS / LPR; // matrix rows per workgroup
 constexpr int YSLOTS = 8;           // most K splits of the feedback product
 
-// Slices of the feedback product's workspace: enough K splits to give every CU of a 256-CU
-// device one 128-row tile, at most YSLOTS.
-inline int64_t y_slots(int64_t out) {
-  const int64_t tiles = (out + 127) / 128;
-  const int64_t s = 256 / tiles;
-  return s < 1 ? 1 : (s > YSLOTS ? YSLOTS : s);
+// K splits of one feedback product (out x N, K = 32 * stages), at most cap: the count with
+// the least modelled time.  Workgroups run in whole rounds of one 128 x 128 tile per CU; a
+// split's tile costs its stages plus about three stages of fill and epilogue; every slice
+// after the first adds its store here and its read in the column kernel, 8 out N bytes, at
+// about 12.8 MB per stage time.
+inline int64_t feedback_splits(int64_t out, int64_t N, int64_t stages, int64_t cap, int cus) {
+  const int64_t tiles = ceil_div(out, 128) * ceil_div(N, 128);
+  const double slice = 8.0 * (double)out * (double)N / 12.8e6;
+  int64_t best = 1;
+  double best_t = -1.0;
+  for (int64_t s = 1; s <= cap && s <= stages; ++s) {
+    const double t = (double)(ceil_div(tiles * s, cus) * (ceil_div(stages, s) + 3)) + (s - 1) * slice;
+    if (best_t < 0.0 || t < best_t) {
+      best_t = t;
+      best = s;
+    }
+  }
+  return best;
 }
+
+// Slices of the feedback product's workspace, for a pair of B-column blocks: the split count
+// the model above takes at K = 8192 on a 256-CU device (larger K runs with that many).
+inline int64_t y_slots(int64_t out, int B) { return feedback_splits(out, 2 * B, 256, YSLOTS, 256); }
 
 struct ColArgs {
   float* W;            // out x in: W0 (unprocessed columns) / errors e (processed columns)
@@ -661,7 +677,7 @@ Layout layout(int64_t out, int64_t in, int B, bool with_loss, bool act_order) {
   size_t o = 0;
   L.f = o;    o = align256(o + (size_t)in * in * sizeof(float));
   L.t = o;    o = align256(o + (size_t)in * 128 * sizeof(float));
-  L.y = o;    o = align256(o + (size_t)y_slots(out) * out * 2 * B * sizeof(float));
+  L.y = o;    o = align256(o + (size_t)y_slots(out, B) * out * 2 * B * sizeof(float));
   L.d = o;    o = align256(o + (size_t)out * in * sizeof(float));
   L.dead = o; o = align256(o + (size_t)in);
   L.scal = o; o = align256(o + 8 * sizeof(double));
@@ -813,17 +829,12 @@ kq_status quantize_layer(const kq_quant_params* p, float* W_rot, const float* HX
       g.A = Dm; g.lda = in; g.transA = false;
       g.B = F + j0; g.ldb = in; g.transB = false;
       g.C = Y; g.ldc = N; g.alpha = 1.0f; g.accumulate = false; g.upper_only = false;
-      // one workgroup per CU (the product keeps a 128 KB LDS ring): split K so that one round
-      // of workgroups covers the GPU, down to one 32-deep stage per split; each split stores
-      // its own slice (out x N, as many as the workspace holds), which the column kernel sums
-      const int64_t tiles = ceil_div(out, 128) * ceil_div(N, 128);
-      int64_t split = cus / tiles;
-      const int64_t max_split = ceil_div(j0, 32);
-      if (split > max_split) split = max_split;
-      const int64_t cap = std::min<int64_t>(YSLOTS, 2 * y_slots(out) / a.nblk);
-      if (split > cap) split = cap;
-      if (split < 1) split = 1;
-      g.split_k = (int)split;
+      // one workgroup per CU (the product keeps a 128 KB LDS ring): split K where whole
+      // rounds of workgroups then cover the GPU better, down to one 32-deep stage per split;
+      // each split stores its own slice (out x N, as many as the workspace holds), which the
+      // column kernel sums
+      const int64_t cap = std::min<int64_t>(YSLOTS, 2 * y_slots(out, B) / a.nblk);
+      g.split_k = (int)feedback_splits(out, N, ceil_div(j0, 32), cap, cus);
       g.partial_stride = out * N;
       g.splits_used = &a.nsplit;
       KQ_TRY(gemm_f32(g, s));
