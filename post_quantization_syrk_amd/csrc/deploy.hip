@@ -31,7 +31,6 @@ namespace {
 
 constexpr int DT = 256;     // threads per workgroup
 constexpr int DR = 16;      // output blocks up to this many rows are rotated in the matvec kernel
-constexpr int MAXC = 8;     // 16-byte chunks per lane and row kept in flight
 constexpr int SEG = 4096;   // entries per workgroup of the output rotation (or one block)
 
 constexpr int MAXL = 8;     // layers per grouped call
@@ -471,8 +470,10 @@ kq_status deploy_group(const kq_deploy_layer* layers, int nl, int64_t in, const 
     return fail(KQ_ESHAPE, "%s: in = %lld too large for the LDS copy of x", fn, (long long)in);
   a.xlen = (int)xlen;
   hipStream_t s = as_stream(stream);
-  // 16-byte chunks per lane and row: all of them in flight when they fit in MAXC
-  const int mc = nck <= 2 ? 2 : nck <= 4 ? 4 : MAXC;
+  // 16-byte chunks per lane and row in flight: all of them up to four, else batches of four
+  // (six in flight for the 11008-wide W4 rows took 289 registers, one wave per SIMD; batches
+  // of four leave room for two and ran that call 3 % faster)
+  const int mc = nck <= 2 ? 2 : 4;
   // 8 rows per wave when the 16-row tiles outnumber what the device holds at once (about
   // four workgroups per CU) and the weights of 8 rows fit in registers
   const int rpw = (tiles16 > 4 * (int64_t)device_cu_count() && mc <= 4) ? 8 : 4;
@@ -491,7 +492,7 @@ kq_status deploy_group(const kq_deploy_layer* layers, int nl, int64_t in, const 
       : launch_with_lds(deploy_matvec_kernel<W, M, 2, 8>, grid, lds, s, a, nm))
 #define KQ_MV(W)                                                                             \
   (rpw == 8 ? (mc == 2 ? KQ_MV8(W, 2) : KQ_MV8(W, 4))                                        \
-            : (mc == 2 ? KQ_MV4(W, 2) : mc == 4 ? KQ_MV4(W, 4) : KQ_MV4(W, MAXC)))
+            : (mc == 2 ? KQ_MV4(W, 2) : KQ_MV4(W, 4)))
   st = wmask == 1 ? KQ_MV(4) : wmask == 2 ? KQ_MV(2) : KQ_MV(0);
 #undef KQ_MV
 #undef KQ_MV8
