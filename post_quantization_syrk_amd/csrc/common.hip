@@ -18,17 +18,18 @@ kq_status fail(kq_status s, const char* fmt, ...) {
 }
 
 int device_cu_count() {
-  static int cache[64] = {0};
+  // per device; threads that race to fill an entry store the same value
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int cus = 0;
+  int cus = cache[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    cache[dev] = cus;
+    cache[dev].store(cus, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return cus;
 }
 
 constexpr int N_TESTING_KNOBS = 3;
