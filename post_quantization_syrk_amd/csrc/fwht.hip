@@ -15,7 +15,8 @@
 // tiled column passes.  Every pass reads and writes each element once.
 //
 // Row pass, 4096-element blocks: three rounds of 4 index bits in registers with two LDS
-// regroupings (row_fwht4096_kernel).
+// regroupings (row_fwht4096_kernel); 8192-element blocks likewise with rounds of 5, 5 and 3
+// bits (row_fwht8192_kernel).
 // Row pass, other blocks (wavefront-shuffle FWHT): a Hadamard block of b contiguous
 // elements is spread over b/EPT threads with EPT values each (16-byte
 // vectors).  Butterflies over the in-register index bits run in registers,
@@ -466,6 +467,107 @@ __global__ __launch_bounds__(NT) void row_fwht4096_kernel(const float* __restric
   }
 }
 
+// Row pass for 8192-element blocks, the same scheme with 32 values per thread: the 13 stages
+// as rounds of 5, 5 and 3 index bits in registers with two LDS regroupings,
+//   round A: x = 32 t + i                              (bits 0-4; contiguous 128-byte loads)
+//   round B: x = (t & 31) + 32 i + 1024 (t >> 5)       (bits 5-9)
+//   round C: x = t + 256 i, stages of i's bits 2-4 only (bits 10-12; bits 8-9 are done)
+// LDS index x + (x >> 5): the lanes of round A's writes and round B's accesses sit on
+// distinct banks (round C's reads put two lanes of a wave on one bank).
+constexpr int RB8 = 8192;
+template <int R>
+__global__ __launch_bounds__(NT) void row_fwht8192_kernel(const float* __restrict__ src,
+                                                          float* __restrict__ dst, int64_t rows,
+                                                          int64_t n, Scale rs, Scale cs) {
+  __shared__ float sm[RB8 + RB8 / 32];
+  const int t = threadIdx.x;
+  const int64_t nb = n / RB8;
+  const int64_t cb = blockIdx.x % nb, r0 = (int64_t)(blockIdx.x / nb) * R;
+  const int64_t c0 = cb * RB8;
+  float csc[32], rsv[R];
+  ScaleLoads16 lc0, lc1;
+  RowLoads<R> lr;
+  scales16_issue(cs, c0, 32 * t, lc0);
+  scales16_issue(cs, c0, 32 * t + 16, lc1);
+  rows_issue<R>(rs, r0, rows, lr);
+  // every row's loads (rows past the end read 0), then the factors
+  u32x4 in[R][8];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int64_t r = r0 + k;
+    const __amdgpu_buffer_rsrc_t rr = rsrc(src + (r < rows ? r : 0) * n + c0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      in[k][j] = __builtin_amdgcn_raw_buffer_load_b128(rr, r < rows ? (32 * t + 4 * j) * 4 : OOB, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    float c16[16];
+    scales16_form(cs, lc0, c16);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) csc[i] = c16[i];
+    scales16_form(cs, lc1, c16);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) csc[16 + i] = c16[i];
+  }
+  rows_form<R>(rs, r0, lr, rsv);
+  float v[32];
+  // butterfly stages over the register index bits in [m0, 32)
+  auto bfly = [&](int m0) {
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) {
+      if (m < m0) continue;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        if (e & m) continue;
+        const float a = v[e], c = v[e | m];
+        v[e] = a + c;
+        v[e | m] = a - c;
+      }
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int64_t r = r0 + k;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[4 * j] = __uint_as_float(in[k][j].x); v[4 * j + 1] = __uint_as_float(in[k][j].y);
+      v[4 * j + 2] = __uint_as_float(in[k][j].z); v[4 * j + 3] = __uint_as_float(in[k][j].w);
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] *= rsv[k] * csc[i];
+    bfly(1);
+    if (k > 0) __syncthreads();   // the previous row's round C reads of sm are done
+#pragma unroll
+    for (int i = 0; i < 32; ++i) sm[33 * t + i] = v[i];   // x = 32 t + i
+    __syncthreads();
+    const int xb = (t & 31) + 1024 * (t >> 5);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int x = xb + 32 * i;
+      v[i] = sm[x + (x >> 5)];
+    }
+    bfly(1);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int x = xb + 32 * i;
+      sm[x + (x >> 5)] = v[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int x = t + 256 * i;
+      v[i] = sm[x + (x >> 5)];
+    }
+    bfly(4);
+    const __amdgpu_buffer_rsrc_t rd = rsrc(dst + (r < rows ? r : 0) * n + c0);
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[i]), rd,
+                                            r < rows ? (t + 256 * i) * 4 : OOB, 0, 0);
+  }
+}
+
 // Pure scaling (no transform on this side): dst[r][c] = src[r][c] * rs(r) * cs(c)
 __global__ __launch_bounds__(NT) void scale_kernel(const float* __restrict__ src,
                                                    float* __restrict__ dst, int64_t rows,
@@ -693,6 +795,17 @@ kq_status row_transform(const float* src, float* dst, int64_t rows, int64_t n, i
 #undef KQ_R4096
     }
     KQ_LAUNCHED("row_fwht4096_kernel");
+    return KQ_OK;
+  }
+  if (b == RB8) {
+    // two rows per workgroup when that still leaves about four workgroups per CU (four rows
+    // per workgroup, two workgroups per CU, ran 3 % slower)
+    const int64_t nb = n / RB8;
+    const int R = (rows * nb) / 2048 >= 1 ? 2 : 1;
+    const dim3 grid((unsigned)(nb * ceil_div(rows, R)));
+    if (R == 2) row_fwht8192_kernel<2><<<grid, dim3(NT), 0, s>>>(src, dst, rows, n, rs, cs);
+    else row_fwht8192_kernel<1><<<grid, dim3(NT), 0, s>>>(src, dst, rows, n, rs, cs);
+    KQ_LAUNCHED("row_fwht8192_kernel");
     return KQ_OK;
   }
   // 16 values per thread up to 1024-point blocks (at most 64 threads, one wave, per block)
