@@ -515,10 +515,16 @@ __global__ void zero_lower_tiles(float* __restrict__ H, int64_t ldh, int n) {
 __global__ __launch_bounds__(256) void mirror_lower_to_upper(float* __restrict__ H, int64_t ldh,
                                                              int n, int m) {
   __shared__ float t[64][65];
-  // upper-triangle tile (ti, tj), ti <= tj, enumerated row by row
-  int idx = blockIdx.x, ti = 0;
-  while (idx >= m - ti) { idx -= m - ti; ++ti; }
-  const int tj = ti + idx;
+  // upper-triangle tile (ti, tj), ti <= tj, enumerated row by row: rows before ti hold
+  // S(ti) = ti (2m - ti + 1) / 2 tiles; ti from the quadratic's root, corrected for rounding
+  const int idx = blockIdx.x;
+  auto before = [&](int r) { return (int64_t)r * (2 * m - r + 1) / 2; };
+  const float bq = 2.0f * (float)m + 1.0f;
+  int ti = (int)((bq - sqrtf(fmaxf(bq * bq - 8.0f * (float)idx, 0.0f))) * 0.5f);
+  ti = max(0, min(ti, m - 1));
+  while (ti > 0 && before(ti) > idx) --ti;
+  while (ti + 1 < m && before(ti + 1) <= idx) ++ti;
+  const int tj = ti + (int)(idx - before(ti));
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   // source tile (tj, ti) of the lower part: rows tj*64.., cols ti*64..
   float v[16];
